@@ -1,0 +1,175 @@
+"""Exact jagged softmax attention in float64 -- oracle (test infrastructure only).
+
+What is computed. The pages say the kernel applies the FlashAttention algorithm
+directly to packed Q/K/V tensors whose sequence boundaries sit in an offsets
+array, never materialising a padded token ([bites] section "Why attention in
+GEM needed a rewrite"; [clarity] third paragraph). FlashAttention is an exact
+reformulation of softmax attention, so the oracle is softmax attention itself,
+written per sequence and head with dense fp64 matrix products:
+
+  s_ij  = scale * <q_i, k_j>                  for the keys j visible to row i
+  LSE_i = ln sum_{j visible} exp(s_ij)         (natural log of scaled scores)
+  P_ij  = exp(s_ij - LSE_i)
+  o_i   = sum_j P_ij v_j
+
+Backward, for the loss L = sum(dO * O):
+  delta_i = <dO_i, o_i>
+  dV_j    = sum_i P_ij dO_i
+  dP_ij   = <dO_i, v_j>
+  dS_ij   = P_ij (dP_ij - delta_i)
+  dq_i    = scale * sum_j dS_ij k_j
+  dk_j    = scale * sum_i dS_ij q_i
+
+Broadcast-Q: one dense Q is shared by every sequence and its gradient is the
+sum over the whole batch ([clarity] second paragraph; [bites] section
+"Optimizations layered on top"). Output rows of sequence b are b*Lq + i.
+
+Visibility. All keys of the row's own sequence; with ``causal`` only keys
+j <= i (local indices, Q and KV share offsets); with a block mask only keys
+whose 128-key block is kept for the row's 128-row Q tile ([radar] section "The
+turning point": the block-sparse variant iterates only over selected blocks).
+A row with no visible key has O = 0, LSE = -inf and contributes no gradient.
+
+Inputs are float64 arrays holding bf16-representable values:
+q [Lq|T_q, H, D], k/v [T_k, H, D], dO [T_q, H, D]; offsets int [B+1].
+LSE and delta are returned as [H, T_q].
+"""
+from __future__ import annotations
+
+import numpy as np
+
+MASK_BLOCK = 128
+
+
+def _q_rows(b, kv_offsets, q_offsets, lq, broadcast_q):
+    """(slice into q, slice into the output rows) of sequence b."""
+    if broadcast_q:
+        return slice(0, lq), slice(b * lq, (b + 1) * lq)
+    lo, hi = int(q_offsets[b]), int(q_offsets[b + 1])
+    return slice(lo, hi), slice(lo, hi)
+
+
+def visibility(n_rows, n_keys, *, causal=False, mask_b=None, rows=None):
+    """bool [len(rows), n_keys]: key j visible to local query row i."""
+    i = np.arange(n_rows) if rows is None else np.asarray(rows)
+    j = np.arange(n_keys)
+    vis = np.ones((len(i), n_keys), dtype=bool)
+    if causal:
+        vis &= j[None, :] <= i[:, None]
+    if mask_b is not None:
+        vis &= mask_b[(i // MASK_BLOCK)[:, None], (j // MASK_BLOCK)[None, :]].astype(bool)
+    return vis
+
+
+def _softmax_stats(s, vis):
+    """LSE per row and P, for scores s with invisible entries excluded."""
+    s = np.where(vis, s, -np.inf)
+    row_max = s.max(axis=1, initial=-np.inf)
+    finite = np.isfinite(row_max)
+    shift = np.where(finite, row_max, 0.0)
+    e = np.exp(s - shift[:, None])          # exp(-inf) = 0 for invisible keys
+    tot = e.sum(axis=1)
+    with np.errstate(divide="ignore"):
+        lse = np.where(finite, shift + np.log(tot), -np.inf)
+    p = np.where(finite[:, None], e / np.where(finite, tot, 1.0)[:, None], 0.0)
+    return lse, p
+
+
+def _problem(q, kv_offsets, q_offsets, broadcast_q):
+    B = len(kv_offsets) - 1
+    if broadcast_q:
+        lq = q.shape[0]
+        t_q = B * lq
+    else:
+        lq = 0
+        t_q = int(q_offsets[-1])
+    return B, lq, t_q
+
+
+def forward(q, k, v, kv_offsets, *, scale, broadcast_q, q_offsets=None, causal=False,
+            block_mask=None, seqs=None, heads=None):
+    """O [T_q,H,D] and LSE [H,T_q] (float64). Rows of sequences not in ``seqs``
+    (default: all) stay 0 / -inf."""
+    B, lq, t_q = _problem(q, kv_offsets, q_offsets, broadcast_q)
+    H, D = k.shape[1], k.shape[2]
+    o = np.zeros((t_q, H, D))
+    lse = np.full((H, t_q), -np.inf)
+    for b in (range(B) if seqs is None else seqs):
+        qs, os_ = _q_rows(b, kv_offsets, q_offsets, lq, broadcast_q)
+        ks = slice(int(kv_offsets[b]), int(kv_offsets[b + 1]))
+        n_rows, n_keys = qs.stop - qs.start, ks.stop - ks.start
+        vis = visibility(n_rows, n_keys, causal=causal,
+                         mask_b=None if block_mask is None else block_mask[b])
+        for h in (range(H) if heads is None else heads):
+            s = scale * (q[qs, h, :] @ k[ks, h, :].T)
+            l, p = _softmax_stats(s, vis)
+            o[os_, h, :] = p @ v[ks, h, :]
+            lse[h, os_] = l
+    return o, lse
+
+
+def forward_rows(q, k, v, kv_offsets, b, h, rows, *, scale, broadcast_q, q_offsets=None,
+                 causal=False, block_mask=None):
+    """O [len(rows), D] and LSE [len(rows)] for local query rows of (b, h) only."""
+    B, lq, _ = _problem(q, kv_offsets, q_offsets, broadcast_q)
+    qs, _ = _q_rows(b, kv_offsets, q_offsets, lq, broadcast_q)
+    ks = slice(int(kv_offsets[b]), int(kv_offsets[b + 1]))
+    rows = np.asarray(rows)
+    vis = visibility(qs.stop - qs.start, ks.stop - ks.start, causal=causal,
+                     mask_b=None if block_mask is None else block_mask[b], rows=rows)
+    s = scale * (q[qs.start + rows, h, :] @ k[ks, h, :].T)
+    l, p = _softmax_stats(s, vis)
+    return p @ v[ks, h, :], l
+
+
+def backward(q, k, v, do, kv_offsets, *, scale, broadcast_q, q_offsets=None, causal=False,
+             block_mask=None, seqs=None, heads=None):
+    """dQ (shape of q), dK, dV [T_k,H,D] and delta [H,T_q], all float64.
+
+    With ``seqs`` given, only those sequences contribute (their dK/dV rows are
+    exact; a broadcast dQ is then the partial sum over ``seqs``)."""
+    B, lq, t_q = _problem(q, kv_offsets, q_offsets, broadcast_q)
+    H, D = k.shape[1], k.shape[2]
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    delta = np.zeros((H, t_q))
+    for b in (range(B) if seqs is None else seqs):
+        qs, os_ = _q_rows(b, kv_offsets, q_offsets, lq, broadcast_q)
+        ks = slice(int(kv_offsets[b]), int(kv_offsets[b + 1]))
+        n_rows, n_keys = qs.stop - qs.start, ks.stop - ks.start
+        vis = visibility(n_rows, n_keys, causal=causal,
+                         mask_b=None if block_mask is None else block_mask[b])
+        for h in (range(H) if heads is None else heads):
+            qb, kb, vb, dob = q[qs, h, :], k[ks, h, :], v[ks, h, :], do[os_, h, :]
+            _, p = _softmax_stats(scale * (qb @ kb.T), vis)
+            ob = p @ vb
+            dl = np.sum(dob * ob, axis=1)
+            dp = dob @ vb.T
+            ds = p * (dp - dl[:, None])
+            dq[qs, h, :] += scale * (ds @ kb)
+            dk[ks, h, :] = scale * (ds.T @ qb)
+            dv[ks, h, :] = p.T @ dob
+            delta[h, os_] = dl
+    return dq, dk, dv, delta
+
+
+def broadcast_dq_rows(q, k, v, do, kv_offsets, h, rows, *, scale, block_mask=None):
+    """Rows of the batch-summed broadcast dQ for head h: sum over every sequence
+    b of scale * sum_j dS_b[i, j] k_j. Each row needs only its own row of the
+    scores of every sequence, so this stays cheap at full size."""
+    B = len(kv_offsets) - 1
+    lq = q.shape[0]
+    rows = np.asarray(rows)
+    out = np.zeros((len(rows), q.shape[2]))
+    for b in range(B):
+        ks = slice(int(kv_offsets[b]), int(kv_offsets[b + 1]))
+        vis = visibility(lq, ks.stop - ks.start,
+                         mask_b=None if block_mask is None else block_mask[b], rows=rows)
+        kb, vb = k[ks, h, :], v[ks, h, :]
+        _, p = _softmax_stats(scale * (q[rows, h, :] @ kb.T), vis)
+        dob = do[b * lq + rows, h, :]
+        dl = np.sum(dob * (p @ vb), axis=1)
+        ds = p * (dob @ vb.T - dl[:, None])
+        out += scale * (ds @ kb)
+    return out

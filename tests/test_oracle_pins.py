@@ -1,0 +1,351 @@
+"""Pins of the fp64 oracle against what the mathematics fixes (CPU only).
+
+Each test checks the oracle against something other than itself: a worked
+example derived by hand, closed forms, a pure-Python brute force over padded
+tensors, torch's float64 attention and autograd, finite differences, and
+invariants of softmax attention. A dropped term, a wrong sign or index, a
+missing scale or a transposed operand in the oracle fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import attention as A
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _expr(x):
+    if isinstance(x, list):
+        return [_expr(e) for e in x]
+    return eval(x, {"__builtins__": {}}, {"log": math.log, "sqrt": math.sqrt})
+
+
+def test_hand_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "two_key_example.json")))
+    q, k, v, do = (np.array(_expr(g[n]), dtype=np.float64) for n in ("q", "k", "v", "do"))
+    off = W.offsets_of(np.array(g["lengths"]))
+    scale = _expr(g["scale"])
+    o, lse = A.forward(q, k, v, off, scale=scale, broadcast_q=True)
+    dq, dk, dv, delta = A.backward(q, k, v, do, off, scale=scale, broadcast_q=True)
+    ex = g["expect"]
+    np.testing.assert_allclose(o, _expr(ex["o"]), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, _expr(ex["lse"]), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dq, _expr(ex["dq"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, _expr(ex["dk"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, _expr(ex["dv"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(delta, [[11.0, 2.0]], rtol=0, atol=1e-12)
+
+
+def _small(broadcast, causal=False, lengths=(5, 1, 9, 3), lq=6, H=2, D=8, seed=0, mask=None):
+    rng = np.random.default_rng(seed)
+    lengths = np.array(lengths)
+    off = W.offsets_of(lengths)
+    tk = int(off[-1])
+    if broadcast:
+        q = rng.standard_normal((lq, H, D))
+        tq = len(lengths) * lq
+        qoff = None
+    else:
+        qoff = off
+        tq = tk
+        q = rng.standard_normal((tq, H, D))
+    k = rng.standard_normal((tk, H, D))
+    v = rng.standard_normal((tk, H, D))
+    do = rng.standard_normal((tq, H, D))
+    kw = dict(scale=1 / math.sqrt(D), broadcast_q=broadcast, q_offsets=qoff, causal=causal,
+              block_mask=mask)
+    return q, k, v, do, off, kw
+
+
+def _seq_iter(off, qoff, lq, broadcast):
+    for b in range(len(off) - 1):
+        if broadcast:
+            yield b, 0, lq, b * lq, off[b], off[b + 1]
+        else:
+            yield b, qoff[b], qoff[b + 1], qoff[b], off[b], off[b + 1]
+
+
+@pytest.mark.parametrize("broadcast,causal", [(True, False), (False, False), (False, True)])
+def test_zero_q_gives_mean_of_visible_values(broadcast, causal):
+    q, k, v, do, off, kw = _small(broadcast, causal)
+    q[:] = 0.0
+    o, lse = A.forward(q, k, v, off, **kw)
+    lq = q.shape[0]
+    for b, q0, q1, o0, k0, k1 in _seq_iter(off, kw["q_offsets"], lq, broadcast):
+        for i in range(q1 - q0):
+            n = (i + 1) if causal else (k1 - k0)
+            np.testing.assert_allclose(o[o0 + i], v[k0:k0 + n].mean(axis=0), atol=1e-14)
+            np.testing.assert_allclose(lse[:, o0 + i], math.log(n), atol=1e-14)
+
+
+def test_one_key_sequence():
+    q, k, v, do, off, kw = _small(True, lengths=(1, 4))
+    o, lse = A.forward(q, k, v, off, **kw)
+    dq, dk, dv, _ = A.backward(q, k, v, do, off, **kw)
+    lq = q.shape[0]
+    np.testing.assert_array_equal(o[:lq], np.broadcast_to(v[0], (lq,) + v.shape[1:]))
+    np.testing.assert_allclose(lse[:, :lq].T, kw["scale"] * np.einsum("ihd,hd->ih", q, k[0]),
+                               atol=1e-14)
+    np.testing.assert_allclose(dk[0], 0.0, atol=1e-14)
+    np.testing.assert_allclose(dv[0], do[:lq].sum(axis=0), atol=1e-13)
+    # the one-key sequence contributes nothing to the batch-summed dQ
+    dq_rest, _, _, _ = A.backward(q, k, v, do, off, seqs=[1], **kw)
+    np.testing.assert_allclose(dq, dq_rest, atol=1e-14)
+
+
+def _brute_force_padded(q, k, v, off, kw):
+    """Independent path: pad every sequence to the longest, mask the padding and
+    the invisible keys with -inf, and evaluate softmax with scalar Python loops."""
+    B = len(off) - 1
+    H, D = k.shape[1], k.shape[2]
+    lens = [int(off[b + 1] - off[b]) for b in range(B)]
+    lk = max(lens)
+    if kw["broadcast_q"]:
+        lq = q.shape[0]
+        qlens = [lq] * B
+        qpad = np.zeros((B, lq, H, D))
+        for b in range(B):
+            qpad[b] = q
+    else:
+        qlens = lens
+        lq = lk
+        qpad = np.zeros((B, lq, H, D))
+        for b in range(B):
+            qpad[b, :lens[b]] = q[off[b]:off[b + 1]]
+    kpad = np.zeros((B, lk, H, D))
+    vpad = np.zeros((B, lk, H, D))
+    for b in range(B):
+        kpad[b, :lens[b]] = k[off[b]:off[b + 1]]
+        vpad[b, :lens[b]] = v[off[b]:off[b + 1]]
+    o = np.zeros((B, lq, H, D))
+    lse = np.full((B, lq, H), -math.inf)
+    mask = kw.get("block_mask")
+    for b in range(B):
+        for h in range(H):
+            for i in range(qlens[b]):
+                scores = []
+                for j in range(lk):
+                    ok = j < lens[b]
+                    if kw["causal"] and j > i:
+                        ok = False
+                    if mask is not None and not mask[b, i // 128, j // 128]:
+                        ok = False
+                    if ok:
+                        s = kw["scale"] * sum(qpad[b, i, h, d] * kpad[b, j, h, d] for d in range(D))
+                        scores.append((j, s))
+                if not scores:
+                    continue
+                mx = max(s for _, s in scores)
+                z = sum(math.exp(s - mx) for _, s in scores)
+                lse[b, i, h] = mx + math.log(z)
+                for j, s in scores:
+                    p = math.exp(s - mx) / z
+                    for d in range(D):
+                        o[b, i, h, d] += p * vpad[b, j, h, d]
+    return o, lse, qlens
+
+
+@pytest.mark.parametrize("broadcast,causal", [(True, False), (False, False), (False, True)])
+def test_matches_padded_brute_force(broadcast, causal):
+    q, k, v, do, off, kw = _small(broadcast, causal, lengths=(5, 1, 9, 3), lq=4, D=4)
+    o, lse = A.forward(q, k, v, off, **kw)
+    ob, lseb, qlens = _brute_force_padded(q, k, v, off, kw)
+    lq = q.shape[0]
+    for b, q0, q1, o0, _, _ in _seq_iter(off, kw["q_offsets"], lq, broadcast):
+        n = q1 - q0
+        np.testing.assert_allclose(o[o0:o0 + n], ob[b, :n], atol=1e-13)
+        np.testing.assert_allclose(lse[:, o0:o0 + n].T, lseb[b, :n], atol=1e-13)
+
+
+def test_block_sparse_matches_brute_force():
+    rng = np.random.default_rng(7)
+    lengths = (300, 130, 17)
+    mask = (rng.random((3, 2, 3)) < 0.5).astype(np.uint8)
+    mask[:, :, 0] = 1
+    mask[0, 1, 2] = 0
+    mask[0, 0, 1] = 1
+    q, k, v, do, off, kw = _small(True, lengths=lengths, lq=200, H=1, D=2, seed=3, mask=mask)
+    o, lse = A.forward(q, k, v, off, **kw)
+    ob, lseb, _ = _brute_force_padded(q, k, v, off, kw)
+    for b in range(3):
+        np.testing.assert_allclose(o[b * 200:(b + 1) * 200], ob[b], atol=1e-13)
+        np.testing.assert_allclose(lse[:, b * 200:(b + 1) * 200].T, lseb[b], atol=1e-13)
+
+
+def _torch_reference(q, k, v, do, off, kw):
+    """torch float64 SDPA + autograd per sequence (a library special case)."""
+    B = len(off) - 1
+    lq = q.shape[0]
+    tq = q.shape[0] * B if kw["broadcast_q"] else q.shape[0]
+    qt = torch.tensor(q, requires_grad=True)
+    kt = torch.tensor(k, requires_grad=True)
+    vt = torch.tensor(v, requires_grad=True)
+    outs = torch.zeros((tq,) + q.shape[1:], dtype=torch.float64)
+    outs_list = []
+    for b, q0, q1, o0, k0, k1 in _seq_iter(off, kw["q_offsets"], lq, kw["broadcast_q"]):
+        qb = qt[q0:q1].transpose(0, 1)          # [H, n, D]
+        kb = kt[k0:k1].transpose(0, 1)
+        vb = vt[k0:k1].transpose(0, 1)
+        vis = torch.tensor(A.visibility(q1 - q0, k1 - k0, causal=kw["causal"],
+                                        mask_b=None if kw["block_mask"] is None
+                                        else kw["block_mask"][b]))
+        ob = torch.nn.functional.scaled_dot_product_attention(
+            qb, kb, vb, attn_mask=vis, scale=kw["scale"])
+        outs_list.append((o0, ob.transpose(0, 1)))
+    o = torch.cat([x for _, x in outs_list], dim=0) if outs_list else outs
+    loss = (o * torch.tensor(do)).sum()
+    loss.backward()
+    return o.detach().numpy(), qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+@pytest.mark.parametrize("broadcast,causal", [(True, False), (False, False), (False, True)])
+def test_matches_torch_float64_and_autograd(broadcast, causal):
+    q, k, v, do, off, kw = _small(broadcast, causal, lengths=(17, 1, 40, 33, 8), lq=24, H=3, D=16)
+    o, _ = A.forward(q, k, v, off, **kw)
+    dq, dk, dv, _ = A.backward(q, k, v, do, off, **kw)
+    ot, dqt, dkt, dvt = _torch_reference(q, k, v, do, off, kw)
+    np.testing.assert_allclose(o, ot, atol=1e-12)
+    np.testing.assert_allclose(dq, dqt, atol=1e-11)
+    np.testing.assert_allclose(dk, dkt, atol=1e-11)
+    np.testing.assert_allclose(dv, dvt, atol=1e-11)
+
+
+def test_block_sparse_matches_torch_masked():
+    x = W.make_inputs(5, batch=6, lq=256, heads=2, head_dim=16)
+    q, k, v, do = (x.as_f64(n) for n in ("q", "k", "v", "do"))
+    kw = dict(scale=0.25, broadcast_q=True, q_offsets=None, causal=False, block_mask=x.block_mask)
+    o, _ = A.forward(q, k, v, x.kv_offsets, **kw)
+    dq, dk, dv, _ = A.backward(q, k, v, do, x.kv_offsets, **kw)
+    ot, dqt, dkt, dvt = _torch_reference(q, k, v, do, x.kv_offsets, kw)
+    np.testing.assert_allclose(o, ot, atol=1e-12)
+    np.testing.assert_allclose(dq, dqt, atol=1e-10)
+    np.testing.assert_allclose(dk, dkt, atol=1e-11)
+    np.testing.assert_allclose(dv, dvt, atol=1e-11)
+    # an all-ones mask is the dense problem
+    ones = np.ones_like(x.block_mask)
+    o1, l1 = A.forward(q, k, v, x.kv_offsets, **dict(kw, block_mask=ones))
+    o2, l2 = A.forward(q, k, v, x.kv_offsets, **dict(kw, block_mask=None))
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def _loss(q, k, v, do, off, kw):
+    o, _ = A.forward(q, k, v, off, **kw)
+    return float(np.sum(do * o))
+
+
+@pytest.mark.parametrize("case", ["broadcast", "per_seq", "causal", "sparse"])
+def test_finite_differences(case):
+    if case == "sparse":
+        mask = np.array([[[1, 0, 1], [1, 1, 0]], [[1, 1, 1], [1, 0, 1]]], dtype=np.uint8)
+        q, k, v, do, off, kw = _small(True, lengths=(300, 260), lq=140, H=1, D=2, seed=5,
+                                      mask=mask)
+        n_probe = 12
+    else:
+        q, k, v, do, off, kw = _small(case == "broadcast", case == "causal",
+                                      lengths=(1, 4), lq=3, H=1, D=4, seed=11)
+        n_probe = None
+    grads = dict(zip(("q", "k", "v"), A.backward(q, k, v, do, off, **kw)[:3]))
+    arrs = {"q": q, "k": k, "v": v}
+    rng = np.random.default_rng(1)
+    eps = 1e-6
+    for name, arr in arrs.items():
+        flat = arr.reshape(-1)
+        idx = range(flat.size) if n_probe is None else rng.choice(flat.size, n_probe, replace=False)
+        g = grads[name].reshape(-1)
+        scale = max(1.0, np.abs(g).max())
+        for t in idx:
+            keep = flat[t]
+            flat[t] = keep + eps
+            lp = _loss(q, k, v, do, off, kw)
+            flat[t] = keep - eps
+            lm = _loss(q, k, v, do, off, kw)
+            flat[t] = keep
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - g[t]) <= 1e-6 * scale, (name, t, fd, g[t])
+
+
+@pytest.mark.parametrize("broadcast,causal", [(True, False), (False, True)])
+def test_gradient_invariants(broadcast, causal):
+    q, k, v, do, off, kw = _small(broadcast, causal, lengths=(7, 1, 12), lq=5, H=2, D=8)
+    dq, dk, dv, _ = A.backward(q, k, v, do, off, **kw)
+    lq = q.shape[0]
+    for b, q0, q1, o0, k0, k1 in _seq_iter(off, kw["q_offsets"], lq, broadcast):
+        # every row's softmax sums to one, so sum_j dS_ij = 0 and sum_j P_ij = 1
+        np.testing.assert_allclose(dk[k0:k1].sum(axis=0), 0.0, atol=1e-12)
+        np.testing.assert_allclose(dv[k0:k1].sum(axis=0), do[o0:o0 + (q1 - q0)].sum(axis=0),
+                                   atol=1e-12)
+
+
+def test_broadcast_dq_is_sum_of_per_sequence_dq():
+    q, k, v, do, off, kw = _small(True, lengths=(7, 1, 12, 5), lq=5, H=2, D=8)
+    dq, dk, dv, _ = A.backward(q, k, v, do, off, **kw)
+    B, lq = len(off) - 1, q.shape[0]
+    qrep = np.concatenate([q] * B, axis=0)
+    qoff = np.arange(B + 1, dtype=np.int32) * lq
+    dq_s, dk_s, dv_s, _ = A.backward(qrep, k, v, do, off, **dict(kw, broadcast_q=False,
+                                                                   q_offsets=qoff))
+    np.testing.assert_allclose(dq, dq_s.reshape(B, lq, *q.shape[1:]).sum(axis=0), atol=1e-12)
+    np.testing.assert_allclose(dk, dk_s, atol=1e-13)
+    np.testing.assert_allclose(dv, dv_s, atol=1e-13)
+
+
+def test_key_shift_and_value_shift():
+    q, k, v, do, off, kw = _small(False, False, lengths=(6, 9), H=1, D=8)
+    o, lse = A.forward(q, k, v, off, **kw)
+    u = np.random.default_rng(2).standard_normal(8)
+    o2, lse2 = A.forward(q, k + u, v, off, **kw)
+    np.testing.assert_allclose(o2, o, atol=1e-12)
+    np.testing.assert_allclose(lse2[0], lse[0] + kw["scale"] * (q[:, 0, :] @ u), atol=1e-12)
+    c = np.arange(8.0)
+    o3, _ = A.forward(q, k, v + c, off, **kw)
+    np.testing.assert_allclose(o3, o + c, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_output_and_lse_bounds(causal):
+    q, k, v, do, off, kw = _small(False, causal, lengths=(6, 9, 2), H=2, D=8, seed=4)
+    o, lse = A.forward(q, k, v, off, **kw)
+    for b in range(3):
+        k0, k1 = off[b], off[b + 1]
+        for i in range(k1 - k0):
+            n = i + 1 if causal else k1 - k0
+            for h in range(2):
+                s = kw["scale"] * (k[k0:k0 + n, h] @ q[k0 + i, h])
+                assert s.max() - 1e-12 <= lse[h, k0 + i] <= s.max() + math.log(n) + 1e-12
+                vv = v[k0:k0 + n, h]
+                assert np.all(o[k0 + i, h] >= vv.min(axis=0) - 1e-12)
+                assert np.all(o[k0 + i, h] <= vv.max(axis=0) + 1e-12)
+
+
+def test_row_samplers_agree_with_full_pass():
+    x = W.make_inputs(5, batch=5, lq=256, heads=2, head_dim=16)
+    q, k, v, do = (x.as_f64(n) for n in ("q", "k", "v", "do"))
+    kw = dict(scale=0.25, broadcast_q=True, block_mask=x.block_mask)
+    o, lse = A.forward(q, k, v, x.kv_offsets, **kw)
+    dq, _, _, _ = A.backward(q, k, v, do, x.kv_offsets, **kw)
+    rows = np.array([0, 7, 128, 255])
+    for b in (0, 3):
+        orow, lrow = A.forward_rows(q, k, v, x.kv_offsets, b, 1, rows, **kw)
+        np.testing.assert_allclose(orow, o[b * 256 + rows, 1], atol=1e-13)
+        np.testing.assert_allclose(lrow, lse[1, b * 256 + rows], atol=1e-13)
+    dqr = A.broadcast_dq_rows(q, k, v, do, x.kv_offsets, 1, rows, scale=0.25,
+                              block_mask=x.block_mask)
+    np.testing.assert_allclose(dqr, dq[rows, 1], atol=1e-12)
+
+
+def test_empty_row_reading():
+    """A sequence with no key: O = 0, LSE = -inf, no gradient (reading of a case
+    the pages never mention)."""
+    q, k, v, do, off, kw = _small(True, lengths=(0, 3), lq=2, H=1, D=4)
+    o, lse = A.forward(q, k, v, off, **kw)
+    assert np.all(o[:2] == 0) and np.all(np.isneginf(lse[:, :2]))
+    dq, dk, dv, _ = A.backward(q, k, v, do, off, **kw)
+    dq1, _, _, _ = A.backward(q, k, v, do, off, seqs=[1], **kw)
+    np.testing.assert_array_equal(dq, dq1)

@@ -1,0 +1,109 @@
+"""Pins of the oracle tile planner by brute force on small inputs (CPU only).
+
+The work of a tile is re-derived from the visibility rule itself (count the
+KV blocks / Q blocks holding at least one visible (query, key) pair), and the
+deal is checked for its defining properties: every tile exactly once, work
+non-increasing along the deal order, snake assignment over the workers.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention as A
+from oracle import planner as P
+
+
+def _brute_work(pass_, b, t, lq_b, lk_b, bm, bn, causal, mask):
+    mask_b = None if mask is None else mask[b]
+    if pass_ == P.FWD:
+        rows = np.arange(t * bm, min((t + 1) * bm, lq_b))
+        vis = A.visibility(lq_b, lk_b, causal=causal, mask_b=mask_b, rows=rows)
+        cols = np.nonzero(vis.any(axis=0))[0]
+        return len(set(int(j) // bn for j in cols))
+    keys = np.arange(t * bn, min((t + 1) * bn, lk_b))
+    vis = A.visibility(lq_b, lk_b, causal=causal, mask_b=mask_b)[:, keys]
+    rows = np.nonzero(vis.any(axis=1))[0]
+    return len(set(int(i) // bm for i in rows))
+
+
+def _cases():
+    rng = np.random.default_rng(0)
+    lens = rng.integers(1, 700, size=9)
+    mask = (rng.random((9, 3, 6)) < 0.5).astype(np.uint8)
+    mask[:, :, 0] = 1
+    return [
+        ("bcast", [300] * 9, lens, False, None),
+        ("perseq", lens, lens, False, None),
+        ("causal", lens, lens, True, None),
+        ("sparse", [300] * 9, lens, False, mask),
+    ]
+
+
+@pytest.mark.parametrize("name,qlens,kvlens,causal,mask", _cases())
+@pytest.mark.parametrize("pass_,bm,bn", [(P.FWD, 128, 64), (P.BWD, 64, 128)])
+@pytest.mark.parametrize("workers", [1, 7, 16, 255])
+def test_plan_properties(name, qlens, kvlens, causal, mask, pass_, bm, bn, workers):
+    H = 3
+    wp, tiles = P.plan(qlens, kvlens, H, workers, pass_, block_m=bm, block_n=bn,
+                       causal=causal, block_mask=mask)
+    assert wp[0] == 0 and wp[-1] == len(tiles) and np.all(np.diff(wp) >= 0)
+    # every tile of the enumeration exactly once, with its brute-force work
+    expect = set()
+    for b in range(len(kvlens)):
+        n_t = P.cdiv(qlens[b], bm) if pass_ == P.FWD else P.cdiv(kvlens[b], bn)
+        for h in range(H):
+            for t in range(n_t):
+                expect.add((b, h, t, _brute_work(pass_, b, t, qlens[b], kvlens[b], bm, bn,
+                                                 causal, mask)))
+    got = [tuple(int(x) for x in r) for r in tiles]
+    assert len(got) == len(set(got)) == len(expect)
+    assert set(got) == expect
+    # rebuild the deal order: position i lives on worker snake(i), in increasing i
+    n = len(tiles)
+    cursor = wp[:-1].copy()
+    order = []
+    for i in range(n):
+        p = i % workers
+        w = p if (i // workers) % 2 == 0 else workers - 1 - p
+        order.append(got[cursor[w]])
+        cursor[w] += 1
+    assert np.all(cursor == wp[1:])
+    works = [r[3] for r in order]
+    assert all(works[i] >= works[i + 1] for i in range(n - 1))
+    # stable: equal work keeps (b, h, t) enumeration order
+    for i in range(n - 1):
+        if works[i] == works[i + 1]:
+            assert order[i][:3] < order[i + 1][:3]
+    # balance: no worker exceeds the mean by more than one largest tile
+    loads = [sum(r[3] for r in got[wp[w]:wp[w + 1]]) for w in range(workers)]
+    assert max(loads) <= sum(works) / workers + (max(works) if works else 0)
+
+
+def test_sparse_lists_by_scan():
+    rng = np.random.default_rng(3)
+    lens = np.array([5, 129, 256, 900, 1])
+    mask = (rng.random((5, 2, 8)) < 0.5).astype(np.uint8)
+    qlens = [200] * 5
+    ptr, idx = P.sparse_lists(mask, qlens, lens, P.FWD)
+    assert len(ptr) == 5 * 2 + 1
+    for b in range(5):
+        for m in range(2):
+            r = b * 2 + m
+            want = [c for c in range(8) if mask[b, m, c] and 128 * c < lens[b]]
+            assert list(idx[ptr[r]:ptr[r + 1]]) == want
+    ptr, idx = P.sparse_lists(mask, qlens, lens, P.BWD)
+    assert len(ptr) == 5 * 8 + 1
+    for b in range(5):
+        for c in range(8):
+            r = b * 8 + c
+            want = [m for m in range(2) if mask[b, m, c] and 128 * m < qlens[b]]
+            assert list(idx[ptr[r]:ptr[r + 1]]) == want
+
+
+def test_offsets_from_lengths():
+    assert list(P.offsets_from_lengths([3, 0, 5])) == [0, 3, 3, 8]
+    assert list(P.offsets_from_lengths([])) == [0]
+    with pytest.raises(ValueError):
+        P.offsets_from_lengths([1, -1])
+    x = W.make_inputs(1)
+    assert list(P.offsets_from_lengths(x.lengths)) == list(x.kv_offsets)
