@@ -1,0 +1,196 @@
+/*
+ * jfa.h -- C ABI of the jagged FlashAttention library for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * What it computes. Exact softmax attention run directly on packed ("jagged")
+ * Q/K/V tensors whose sequence boundaries are given by an int32 offsets array,
+ * with no padded token ("Meta's TLX Jagged Flash Attention Beats FA4 on
+ * Blackwell With 3x Less Code" (ainewsbites.com), section "Why attention in GEM
+ * needed a rewrite"; "Meta's 3.2K-line Triton kernel outruns FlashAttention-4
+ * on jagged Blackwell attention" (theclarity.today), third paragraph).
+ * In broadcast-Q mode one dense Q is shared by every sequence and its gradient
+ * is summed over the whole batch (theclarity.today, second paragraph).
+ * For sequence b, query row i and a visible key j:
+ *     s_ij = scale * <q_i, k_j>,  LSE_i = ln sum_j exp(s_ij),
+ *     O_i  = sum_j exp(s_ij - LSE_i) v_j.
+ * Visible keys: every key of the row's own sequence; with causal=1 only keys
+ * j <= i (local indices); with a block mask only keys whose 128-key block is
+ * kept for the row's 128-row Q tile ("TLX porta l'attenzione jagged su
+ * Blackwell" (ai-radar.it), section "The turning point").
+ *
+ * Layouts (all row-major, contiguous):
+ *   q        bf16 [lq, H, D] when broadcast_q, else [T_q, H, D]
+ *   k, v     bf16 [T_k, H, D],   T_k = kv_offsets[B]
+ *   o, dO    bf16 [T_q, H, D],   T_q = B*lq (row b*lq+i) when broadcast_q,
+ *                                else q_offsets[B]
+ *   lse      fp32 [H, T_q]       natural log of the scaled scores; -inf for a
+ *                                row with no visible key (its O row is 0)
+ *   delta    fp32 [H, T_q]       rowsum(dO * O)
+ *   dq       bf16, shape of q;   dq_accum fp32, shape of q (the fp32 sum the
+ *                                bf16 dq is rounded from)
+ *   dk, dv   bf16 [T_k, H, D]
+ *   offsets  int32 [B+1], offsets[0] = 0, non-decreasing
+ *   mask     uint8 [B, mask_q_blocks, mask_kv_blocks], nonzero = kept
+ * Device tensors must be 16-byte aligned. H*D*2 bytes is the row stride.
+ *
+ * Conventions for every function:
+ *   - returns JFA_OK (0) or a negative JFA_ERR_* status; never throws, never
+ *     aborts, never allocates device memory and never synchronises;
+ *   - GPU work is enqueued on the caller's stream (a hipStream_t passed as
+ *     void*; NULL is the default stream);
+ *   - the caller owns every buffer; host pointers (h_*) are read during the
+ *     call only; device pointers (d_* and tensors) must stay valid until the
+ *     enqueued work completes;
+ *   - arguments are validated on the host before anything is launched; a bad
+ *     argument returns an error and launches nothing.
+ */
+#ifndef JFA_H
+#define JFA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define JFA_ABI_VERSION 1
+
+/* status codes */
+#define JFA_OK                 0
+#define JFA_ERR_INVALID_ARG   -1  /* null/misaligned pointer, bad size or flag */
+#define JFA_ERR_BAD_OFFSETS   -2  /* offsets[0] != 0, decreasing, or overflow   */
+#define JFA_ERR_UNSUPPORTED   -3  /* head_dim not 64/128, causal with broadcast
+                                     Q or with unequal Q/KV lengths, mask with
+                                     causal                                   */
+#define JFA_ERR_PLAN_MISMATCH -4  /* plan built for another pass/problem      */
+#define JFA_ERR_WORKSPACE     -5  /* workspace too small                       */
+#define JFA_ERR_HIP           -6  /* a HIP call failed: see jfa_last_hip_error */
+#define JFA_ERR_BAD_MASK      -7  /* block mask missing or too small           */
+
+/* planner passes */
+#define JFA_PASS_FWD 0
+#define JFA_PASS_BWD 1
+
+/* Problem description shared by the planner, jfa_fwd and jfa_bwd. */
+typedef struct jfa_problem {
+    int32_t batch;          /* B >= 0 sequences                                */
+    int32_t num_heads;      /* H >= 1                                          */
+    int32_t head_dim;       /* D, 64 or 128                                    */
+    int32_t broadcast_q;    /* 1: one dense Q [lq,H,D] shared by all sequences */
+    int32_t lq;             /* rows of the shared Q (broadcast_q only), >= 0   */
+    int32_t causal;         /* 1: key j visible to row i iff j <= i; needs
+                               per-sequence Q with the same lengths as KV      */
+    int32_t mask_q_blocks;  /* block-sparse mask dims; both 0 = dense          */
+    int32_t mask_kv_blocks;
+    float   softmax_scale;  /* finite; usually 1/sqrt(D)                       */
+} jfa_problem;
+
+/* Sizes of a plan, filled by jfa_plan_query / jfa_plan_build. */
+typedef struct jfa_plan_info {
+    int32_t pass;           /* JFA_PASS_FWD or JFA_PASS_BWD                    */
+    int32_t num_workers;    /* W persistent workgroups the plan is dealt to    */
+    int32_t num_tiles;      /* N tiles                                         */
+    int32_t block_m;        /* rows of a Q tile (fwd) / Q block (bwd)          */
+    int32_t block_n;        /* keys of a KV block (fwd) / KV tile (bwd)        */
+    int32_t total_q;        /* T_q                                             */
+    int32_t total_kv;       /* T_k                                             */
+    int32_t sparse_rows;    /* rows of the block-sparse CSR (fwd) / columns of
+                               the CSC (bwd); 0 when dense                     */
+    int32_t sparse_nnz;     /* entries of its index array                      */
+    int32_t max_work;       /* largest tile work                               */
+    int64_t total_work;     /* sum of tile work                                */
+} jfa_plan_info;
+
+int32_t jfa_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* jfa_status_string(int32_t status);
+
+/* The hipError_t of the last failed HIP call made by this thread. */
+int32_t jfa_last_hip_error(void);
+
+/* Compute units of HIP device `device` (the natural worker count unit). */
+int32_t jfa_device_workers(int32_t device, int32_t* num_cus);
+
+/* offsets[0] = 0, offsets[b+1] = offsets[b] + lengths[b]. h_offsets has B+1
+ * entries. Lengths must be >= 0 and the total must fit int32. */
+int32_t jfa_offsets_from_lengths(const int32_t* h_lengths, int32_t batch, int32_t* h_offsets);
+
+/*
+ * Host tile planner ("Meta's TLX Jagged Flash Attention Beats FA4 on
+ * Blackwell" (ainewsbites.com), section "Optimizations layered on top": tiles
+ * sorted on the host by KV workload, largest first, dealt to the processors
+ * in a zigzag pattern; software load balancing across length skew).
+ *
+ * Tiles are enumerated in (b, h, t) order. FWD: t is a Q tile of block_m=128
+ * rows, work = KV blocks of block_n=64 keys visited (dense: ceil(Lk/64);
+ * causal: ceil(min(128(t+1), L)/64); block-sparse: the 64-key blocks of the
+ * kept 128-key mask blocks inside the sequence). BWD: t is a KV tile of
+ * block_n=128 keys, work = Q blocks of block_m=64 rows visited (dense:
+ * ceil(Lq/64); causal: ceil(L/64) - 2t; block-sparse: the 64-row blocks of the
+ * kept 128-row mask tiles). Tiles are stably sorted by work, descending, and
+ * sorted tile i goes to worker i mod W when floor(i/W) is even, else to
+ * W-1-(i mod W).
+ *
+ * h_q_offsets: int32 [B+1], NULL in broadcast mode. h_kv_offsets: int32 [B+1].
+ * h_block_mask: NULL when mask_q_blocks = mask_kv_blocks = 0.
+ * jfa_plan_query fills *info only (sizes). jfa_plan_build also writes
+ *   h_worker_ptr  int32 [W+1]      tiles of worker w are [ptr[w], ptr[w+1])
+ *   h_tiles       int32 [N*4]      (b, h, t, work) per tile
+ *   h_sparse_ptr  int32 [sparse_rows+1], h_sparse_idx int32 [sparse_nnz]
+ *                 (block-sparse only, else may be NULL): FWD = CSR over rows
+ *                 b*mask_q_blocks+m of the kept 128-key blocks inside the
+ *                 sequence; BWD = CSC over columns b*mask_kv_blocks+c of the
+ *                 kept 128-row Q tiles inside the sequence; ascending.
+ * The caller copies these arrays to the device for jfa_fwd / jfa_bwd.
+ */
+int32_t jfa_plan_query(const jfa_problem* prob, const int32_t* h_q_offsets,
+                       const int32_t* h_kv_offsets, const uint8_t* h_block_mask,
+                       int32_t pass, int32_t num_workers, jfa_plan_info* info);
+int32_t jfa_plan_build(const jfa_problem* prob, const int32_t* h_q_offsets,
+                       const int32_t* h_kv_offsets, const uint8_t* h_block_mask,
+                       int32_t pass, int32_t num_workers, jfa_plan_info* info,
+                       int32_t* h_worker_ptr, int32_t* h_tiles,
+                       int32_t* h_sparse_ptr, int32_t* h_sparse_idx);
+
+/*
+ * Forward pass: O and LSE. One persistent launch of info->num_workers
+ * workgroups walking a FWD plan (d_worker_ptr, d_tiles and, for a block mask,
+ * d_sparse_ptr/d_sparse_idx, all device copies of jfa_plan_build's output).
+ * d_q_offsets is NULL in broadcast mode. Every O/LSE row is written.
+ */
+int32_t jfa_fwd(const jfa_problem* prob, const jfa_plan_info* info,
+                const int32_t* d_worker_ptr, const int32_t* d_tiles,
+                const int32_t* d_sparse_ptr, const int32_t* d_sparse_idx,
+                const int32_t* d_q_offsets, const int32_t* d_kv_offsets,
+                const void* q, const void* k, const void* v,
+                void* o, float* lse, void* stream);
+
+/* Bytes of scratch jfa_bwd needs for this BWD plan (may be 0). */
+int32_t jfa_bwd_workspace_bytes(const jfa_problem* prob, const jfa_plan_info* info,
+                                int64_t* bytes);
+
+/*
+ * Backward pass: dQ, dK, dV for the loss sum(dO * O), given the forward's O
+ * and LSE. Enqueues, in stream order: a preprocess kernel (delta =
+ * rowsum(dO*O) in fp32, dq_accum cleared), the persistent main kernel walking
+ * a BWD plan (dK, dV accumulated per KV tile in registers; per-workgroup dQ
+ * partials staged through LDS and added into dq_accum in fp32), and a kernel
+ * rounding dq_accum to bf16 dq. In broadcast mode dq is the sum over all
+ * sequences (theclarity.today, second paragraph). dq_accum and delta are
+ * outputs too. workspace may be NULL when jfa_bwd_workspace_bytes gives 0.
+ */
+int32_t jfa_bwd(const jfa_problem* prob, const jfa_plan_info* info,
+                const int32_t* d_worker_ptr, const int32_t* d_tiles,
+                const int32_t* d_sparse_ptr, const int32_t* d_sparse_idx,
+                const int32_t* d_q_offsets, const int32_t* d_kv_offsets,
+                const void* q, const void* k, const void* v,
+                const void* o, const float* lse, const void* d_o,
+                void* dq, void* dk, void* dv, float* dq_accum, float* delta,
+                void* workspace, int64_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JFA_H */

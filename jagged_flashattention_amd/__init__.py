@@ -1,0 +1,311 @@
+"""Python binding of libjfa.so, the jagged FlashAttention library for MI355X.
+
+Argument marshalling only: every step of forward and backward runs in the HIP
+kernels behind the C ABI (include/jfa.h). The functions keep the C names;
+torch is used for device memory and the current HIP stream. If the library is
+not built, every call raises -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libjfa.so")
+
+JFA_OK = 0
+JFA_ERR_INVALID_ARG = -1
+JFA_ERR_BAD_OFFSETS = -2
+JFA_ERR_UNSUPPORTED = -3
+JFA_ERR_PLAN_MISMATCH = -4
+JFA_ERR_WORKSPACE = -5
+JFA_ERR_HIP = -6
+JFA_ERR_BAD_MASK = -7
+JFA_PASS_FWD = 0
+JFA_PASS_BWD = 1
+
+EXPORTS = (
+    "jfa_abi_version", "jfa_status_string", "jfa_last_hip_error", "jfa_device_workers",
+    "jfa_offsets_from_lengths", "jfa_plan_query", "jfa_plan_build", "jfa_fwd",
+    "jfa_bwd_workspace_bytes", "jfa_bwd",
+)
+
+
+class JfaProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("broadcast_q", ctypes.c_int32),
+                ("lq", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("mask_q_blocks", ctypes.c_int32), ("mask_kv_blocks", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
+
+
+class JfaPlanInfo(ctypes.Structure):
+    _fields_ = [("pass_", ctypes.c_int32), ("num_workers", ctypes.c_int32),
+                ("num_tiles", ctypes.c_int32), ("block_m", ctypes.c_int32),
+                ("block_n", ctypes.c_int32), ("total_q", ctypes.c_int32),
+                ("total_kv", ctypes.c_int32), ("sparse_rows", ctypes.c_int32),
+                ("sparse_nnz", ctypes.c_int32), ("max_work", ctypes.c_int32),
+                ("total_work", ctypes.c_int64)]
+
+
+class JfaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = "%s failed: %s (%d)" % (where, jfa_status_string(status), status)
+        if status == JFA_ERR_HIP:
+            msg += ", hipError %d" % _lib().jfa_last_hip_error()
+        super().__init__(msg)
+        self.status = status
+
+
+_LIB = None
+
+_P = ctypes.c_void_p
+_I32P = ctypes.POINTER(ctypes.c_int32)
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libjfa.so is not built (run jagged_flashattention_amd/build.py); "
+                               "there is no fallback implementation")
+        lib = ctypes.CDLL(LIB_PATH)
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
+        prob, info = ctypes.POINTER(JfaProblem), ctypes.POINTER(JfaPlanInfo)
+        sig = {
+            "jfa_abi_version": (i32, []),
+            "jfa_status_string": (ctypes.c_char_p, [i32]),
+            "jfa_last_hip_error": (i32, []),
+            "jfa_device_workers": (i32, [i32, _I32P]),
+            "jfa_offsets_from_lengths": (i32, [_P, i32, _P]),
+            "jfa_plan_query": (i32, [prob, _P, _P, _P, i32, i32, info]),
+            "jfa_plan_build": (i32, [prob, _P, _P, _P, i32, i32, info, _P, _P, _P, _P]),
+            "jfa_fwd": (i32, [prob, info] + [_P] * 12),
+            "jfa_bwd_workspace_bytes": (i32, [prob, info, ctypes.POINTER(i64)]),
+            "jfa_bwd": (i32, [prob, info] + [_P] * 18 + [i64, _P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def _check(status: int, where: str):
+    if status != JFA_OK:
+        raise JfaError(status, where)
+
+
+def _np_ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(_P)
+
+
+def _dev_ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ---------------------------------------------------------------- C functions
+
+def jfa_abi_version() -> int:
+    return _lib().jfa_abi_version()
+
+
+def jfa_status_string(status: int) -> str:
+    return _lib().jfa_status_string(status).decode()
+
+
+def jfa_device_workers(device: int = 0) -> int:
+    n = ctypes.c_int32(0)
+    _check(_lib().jfa_device_workers(device, ctypes.byref(n)), "jfa_device_workers")
+    return n.value
+
+
+def jfa_offsets_from_lengths(lengths) -> np.ndarray:
+    ln = np.ascontiguousarray(lengths, dtype=np.int32)
+    out = np.zeros(len(ln) + 1, dtype=np.int32)
+    _check(_lib().jfa_offsets_from_lengths(_np_ptr(ln), len(ln), _np_ptr(out)),
+           "jfa_offsets_from_lengths")
+    return out
+
+
+@dataclasses.dataclass
+class Problem:
+    batch: int
+    num_heads: int
+    head_dim: int
+    broadcast_q: bool
+    lq: int = 0
+    causal: bool = False
+    mask_q_blocks: int = 0
+    mask_kv_blocks: int = 0
+    softmax_scale: float = 0.0
+
+    def c(self) -> JfaProblem:
+        return JfaProblem(self.batch, self.num_heads, self.head_dim, int(self.broadcast_q),
+                          self.lq, int(self.causal), self.mask_q_blocks, self.mask_kv_blocks,
+                          self.softmax_scale)
+
+
+def _i32(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.int32)
+
+
+def jfa_plan_query(prob: Problem, q_offsets, kv_offsets, block_mask, pass_: int,
+                   num_workers: int) -> JfaPlanInfo:
+    info = JfaPlanInfo()
+    qo, ko = _i32(q_offsets), _i32(kv_offsets)
+    m = None if block_mask is None else np.ascontiguousarray(block_mask, dtype=np.uint8)
+    cp = prob.c()
+    _check(_lib().jfa_plan_query(ctypes.byref(cp), _np_ptr(qo), _np_ptr(ko), _np_ptr(m), pass_,
+                                 num_workers, ctypes.byref(info)), "jfa_plan_query")
+    return info
+
+
+@dataclasses.dataclass
+class HostPlan:
+    info: JfaPlanInfo
+    worker_ptr: np.ndarray
+    tiles: np.ndarray          # [N, 4] int32 (b, h, t, work)
+    sparse_ptr: Optional[np.ndarray]
+    sparse_idx: Optional[np.ndarray]
+
+
+def jfa_plan_build(prob: Problem, q_offsets, kv_offsets, block_mask, pass_: int,
+                   num_workers: int) -> HostPlan:
+    info = jfa_plan_query(prob, q_offsets, kv_offsets, block_mask, pass_, num_workers)
+    qo, ko = _i32(q_offsets), _i32(kv_offsets)
+    m = None if block_mask is None else np.ascontiguousarray(block_mask, dtype=np.uint8)
+    wp = np.zeros(info.num_workers + 1, dtype=np.int32)
+    tiles = np.zeros((info.num_tiles, 4), dtype=np.int32)
+    sparse = prob.mask_q_blocks != 0
+    sp = np.zeros(info.sparse_rows + 1, dtype=np.int32) if sparse else None
+    si = np.zeros(max(info.sparse_nnz, 1), dtype=np.int32) if sparse else None
+    info2 = JfaPlanInfo()
+    cp = prob.c()
+    _check(_lib().jfa_plan_build(ctypes.byref(cp), _np_ptr(qo), _np_ptr(ko), _np_ptr(m), pass_,
+                                 num_workers, ctypes.byref(info2), _np_ptr(wp), _np_ptr(tiles),
+                                 _np_ptr(sp), _np_ptr(si)), "jfa_plan_build")
+    if sparse:
+        si = si[:info2.sparse_nnz]
+    return HostPlan(info2, wp, tiles, sp, si)
+
+
+@dataclasses.dataclass
+class DevicePlan:
+    """A host plan copied to the device (torch int32 tensors)."""
+    info: JfaPlanInfo
+    worker_ptr: object
+    tiles: object
+    sparse_ptr: object
+    sparse_idx: object
+
+
+def to_device(plan: HostPlan, device="cuda") -> DevicePlan:
+    import torch
+    f = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    return DevicePlan(plan.info, f(plan.worker_ptr), f(plan.tiles.reshape(-1)),
+                      f(plan.sparse_ptr), f(plan.sparse_idx))
+
+
+def jfa_fwd(prob: Problem, plan: DevicePlan, q_offsets, kv_offsets, q, k, v, o, lse,
+            stream=None) -> None:
+    """Enqueue the forward on ``stream`` (default: torch's current stream).
+    q_offsets / kv_offsets are device int32 tensors (q_offsets None when
+    broadcast); q, k, v, o bf16 and lse fp32 device tensors (see jfa.h)."""
+    cp = prob.c()
+    _check(_lib().jfa_fwd(ctypes.byref(cp), ctypes.byref(plan.info), _dev_ptr(plan.worker_ptr),
+                          _dev_ptr(plan.tiles), _dev_ptr(plan.sparse_ptr),
+                          _dev_ptr(plan.sparse_idx), _dev_ptr(q_offsets), _dev_ptr(kv_offsets),
+                          _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(o), _dev_ptr(lse),
+                          _stream(stream)), "jfa_fwd")
+
+
+def jfa_bwd_workspace_bytes(prob: Problem, info: JfaPlanInfo) -> int:
+    n = ctypes.c_int64(0)
+    cp = prob.c()
+    _check(_lib().jfa_bwd_workspace_bytes(ctypes.byref(cp), ctypes.byref(info), ctypes.byref(n)),
+           "jfa_bwd_workspace_bytes")
+    return n.value
+
+
+def jfa_bwd(prob: Problem, plan: DevicePlan, q_offsets, kv_offsets, q, k, v, o, lse, d_o,
+            dq, dk, dv, dq_accum, delta, workspace=None, workspace_bytes: int = 0,
+            stream=None) -> None:
+    """Enqueue the backward (preprocess, main, dQ convert) on ``stream``."""
+    cp = prob.c()
+    _check(_lib().jfa_bwd(ctypes.byref(cp), ctypes.byref(plan.info), _dev_ptr(plan.worker_ptr),
+                          _dev_ptr(plan.tiles), _dev_ptr(plan.sparse_ptr),
+                          _dev_ptr(plan.sparse_idx), _dev_ptr(q_offsets), _dev_ptr(kv_offsets),
+                          _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(o), _dev_ptr(lse),
+                          _dev_ptr(d_o), _dev_ptr(dq), _dev_ptr(dk), _dev_ptr(dv),
+                          _dev_ptr(dq_accum), _dev_ptr(delta), _dev_ptr(workspace),
+                          int(workspace_bytes), _stream(stream)), "jfa_bwd")
+
+
+# ------------------------------------------------------- convenience wrappers
+
+def default_workers(device: int = 0, per_cu: int = 1) -> int:
+    return jfa_device_workers(device) * per_cu
+
+
+class JaggedAttention:
+    """Plans once for fixed offsets and runs forward/backward on torch tensors.
+
+    q: [lq,H,D] (broadcast) or [T_q,H,D]; k, v: [T_k,H,D]; bf16 on the GPU.
+    Host copies of the offsets are needed for planning (the planner runs on
+    the CPU); device copies are made here.
+    """
+
+    def __init__(self, prob: Problem, kv_offsets, q_offsets=None, block_mask=None,
+                 fwd_workers: Optional[int] = None, bwd_workers: Optional[int] = None,
+                 device="cuda"):
+        import torch
+        self.prob = prob
+        self.device = device
+        cus = jfa_device_workers(torch.device(device).index or 0)
+        self.fwd_plan_host = jfa_plan_build(prob, q_offsets, kv_offsets, block_mask,
+                                            JFA_PASS_FWD, fwd_workers or 2 * cus)
+        self.bwd_plan_host = jfa_plan_build(prob, q_offsets, kv_offsets, block_mask,
+                                            JFA_PASS_BWD, bwd_workers or cus)
+        self.fwd_plan = to_device(self.fwd_plan_host, device)
+        self.bwd_plan = to_device(self.bwd_plan_host, device)
+        self.kv_offsets = torch.from_numpy(_i32(kv_offsets)).to(device)
+        self.q_offsets = None if q_offsets is None else torch.from_numpy(_i32(q_offsets)).to(device)
+        self.total_q = self.fwd_plan.info.total_q
+        self.total_kv = self.fwd_plan.info.total_kv
+        self.ws_bytes = jfa_bwd_workspace_bytes(prob, self.bwd_plan.info)
+        self.workspace = (torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+                          if self.ws_bytes else None)
+
+    def forward(self, q, k, v, o=None, lse=None):
+        import torch
+        H, D = self.prob.num_heads, self.prob.head_dim
+        if o is None:
+            o = torch.empty((self.total_q, H, D), dtype=torch.bfloat16, device=self.device)
+        if lse is None:
+            lse = torch.empty((H, self.total_q), dtype=torch.float32, device=self.device)
+        jfa_fwd(self.prob, self.fwd_plan, self.q_offsets, self.kv_offsets, q, k, v, o, lse)
+        return o, lse
+
+    def backward(self, q, k, v, o, lse, d_o, out=None):
+        import torch
+        if out is None:
+            out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+                       dq_accum=torch.empty(q.shape, dtype=torch.float32, device=self.device),
+                       delta=torch.empty((self.prob.num_heads, self.total_q), dtype=torch.float32,
+                                         device=self.device))
+        jfa_bwd(self.prob, self.bwd_plan, self.q_offsets, self.kv_offsets, q, k, v, o, lse, d_o,
+                out["dq"], out["dk"], out["dv"], out["dq_accum"], out["delta"], self.workspace,
+                self.ws_bytes)
+        return out

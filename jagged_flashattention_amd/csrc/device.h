@@ -1,0 +1,72 @@
+// Device-side helpers for gfx950 (CDNA4): MFMA wrappers, transposed LDS
+// reads, cross-half-wave exchange and bf16 packing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jfa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// D[32x32] += A[32x16] * B[16x32], bf16 in, fp32 accumulate.
+// Lane l holds A row l%32, k = 8*(l/32)..+7; B column l%32, same k;
+// accumulator register r holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposed LDS read of 4 bf16. Inside each group of 16 lanes, let lane
+// 4e+c load the 4 consecutive values at its address; lane i of the group then
+// receives element (i % 4) of the loads of lanes i/4, 4+i/4, 8+i/4, 12+i/4,
+// i.e. lane i gets column i of the 4x16 matrix whose row e is the 16 values
+// loaded by lanes 4e..4e+3.
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t* p) {
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 concat(bf16x4 lo, bf16x4 hi) {
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Value of x in lane l^32 combined with x: both halves end up with the pair.
+__device__ __forceinline__ float pair_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(f32x8 x) { return __builtin_convertvector(x, bf16x8); }
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
+    return __builtin_bit_cast(bf16x8, *(const u32x4*)p);
+}
+
+// Persistent worker of this workgroup. Workgroup ids are dealt round-robin to
+// the 8 XCDs; mapping consecutive workers to the same XCD puts tiles dealt
+// next to each other (e.g. the Q tiles of one sequence and head, which read
+// the same K/V) behind the same L2.
+__device__ __forceinline__ int worker_id(int num_workers) {
+    const int bid = blockIdx.x;
+    if ((num_workers & 7) == 0) return (bid & 7) * (num_workers >> 3) + (bid >> 3);
+    return bid;
+}
+
+}  // namespace jfa

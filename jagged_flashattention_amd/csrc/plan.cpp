@@ -1,0 +1,284 @@
+// Host tile planner and problem validation (plain C++17, no HIP calls).
+//
+// The planner follows the scheduling the pages describe for the forward
+// kernel: tiles sorted on the host by KV workload, largest first, and handed
+// to the processors in a zigzag pattern, plus software load balancing across
+// length skew ("Meta's TLX Jagged Flash Attention Beats FA4 on Blackwell With
+// 3x Less Code" (ainewsbites.com), section "Optimizations layered on top").
+// The backward pass reuses it with KV tiles. The pages fix no tile size, work
+// measure, tie order or meaning of "zigzag"; the readings used here are:
+// work = inner-loop trip count of the tile, stable sort (ties keep (b,h,t)
+// order), snake deal (round r goes left-to-right when r is even, else
+// right-to-left).
+#include "internal.h"
+
+#include <algorithm>
+#include <cstring>
+#include <numeric>
+#include <vector>
+
+namespace jfa {
+
+static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int32_t check_offsets(const int32_t* off, int32_t batch) {
+    if (off == nullptr) return JFA_ERR_INVALID_ARG;
+    if (off[0] != 0) return JFA_ERR_BAD_OFFSETS;
+    for (int32_t b = 0; b < batch; ++b)
+        if (off[b + 1] < off[b]) return JFA_ERR_BAD_OFFSETS;
+    return JFA_OK;
+}
+
+int32_t check_problem(const jfa_problem* p) {
+    if (p == nullptr) return JFA_ERR_INVALID_ARG;
+    if (p->batch < 0 || p->num_heads < 1 || p->lq < 0) return JFA_ERR_INVALID_ARG;
+    if (p->broadcast_q != 0 && p->broadcast_q != 1) return JFA_ERR_INVALID_ARG;
+    if (p->causal != 0 && p->causal != 1) return JFA_ERR_INVALID_ARG;
+    if (p->head_dim != 64 && p->head_dim != 128) return JFA_ERR_UNSUPPORTED;
+    if (!(p->softmax_scale == p->softmax_scale) || p->softmax_scale > 3.0e38f ||
+        p->softmax_scale < -3.0e38f)
+        return JFA_ERR_INVALID_ARG;
+    if (p->causal && p->broadcast_q) return JFA_ERR_UNSUPPORTED;
+    const bool sparse = p->mask_q_blocks != 0 || p->mask_kv_blocks != 0;
+    if (sparse && (p->mask_q_blocks < 1 || p->mask_kv_blocks < 1)) return JFA_ERR_BAD_MASK;
+    if (sparse && p->causal) return JFA_ERR_UNSUPPORTED;
+    // rows of the packed tensors are addressed as int32 * H * D elements in 64 bits;
+    // keep H*D within int32
+    if ((int64_t)p->num_heads * p->head_dim > (1 << 24)) return JFA_ERR_INVALID_ARG;
+    return JFA_OK;
+}
+
+namespace {
+
+struct Tile { int32_t b, h, t, work; };
+
+struct Lens {
+    std::vector<int32_t> q, kv;
+    int64_t total_q = 0, total_kv = 0;
+};
+
+int32_t lengths_of(const jfa_problem* p, const int32_t* qo, const int32_t* ko, Lens& L) {
+    int32_t st = check_offsets(ko, p->batch);
+    if (st) return st;
+    L.kv.resize(p->batch);
+    L.q.resize(p->batch);
+    for (int32_t b = 0; b < p->batch; ++b) L.kv[b] = ko[b + 1] - ko[b];
+    L.total_kv = ko[p->batch];
+    if (p->broadcast_q) {
+        for (int32_t b = 0; b < p->batch; ++b) L.q[b] = p->lq;
+        L.total_q = (int64_t)p->batch * p->lq;
+        if (L.total_q > INT32_MAX) return JFA_ERR_INVALID_ARG;
+    } else {
+        st = check_offsets(qo, p->batch);
+        if (st) return st;
+        for (int32_t b = 0; b < p->batch; ++b) L.q[b] = qo[b + 1] - qo[b];
+        L.total_q = qo[p->batch];
+        if (p->causal)
+            for (int32_t b = 0; b < p->batch; ++b)
+                if (L.q[b] != L.kv[b]) return JFA_ERR_UNSUPPORTED;
+    }
+    const bool sparse = p->mask_q_blocks != 0;
+    if (sparse)
+        for (int32_t b = 0; b < p->batch; ++b)
+            if (cdiv(L.q[b], kMaskBlock) > p->mask_q_blocks ||
+                cdiv(L.kv[b], kMaskBlock) > p->mask_kv_blocks)
+                return JFA_ERR_BAD_MASK;
+    return JFA_OK;
+}
+
+inline bool kept(const jfa_problem* p, const uint8_t* mask, int32_t b, int32_t m, int32_t c) {
+    return mask[((int64_t)b * p->mask_q_blocks + m) * p->mask_kv_blocks + c] != 0;
+}
+
+int32_t tile_work(const jfa_problem* p, const uint8_t* mask, int32_t pass, int32_t b, int32_t t,
+                  int32_t lq, int32_t lk) {
+    const bool sparse = p->mask_q_blocks != 0;
+    if (pass == JFA_PASS_FWD) {
+        if (sparse) {
+            int64_t w = 0;
+            const int32_t m = t * kFwdBlockM / kMaskBlock;
+            for (int32_t c = 0; c < cdiv(lk, kMaskBlock); ++c)
+                if (kept(p, mask, b, m, c))
+                    w += cdiv(std::min<int64_t>((int64_t)kMaskBlock * (c + 1), lk) -
+                                  (int64_t)kMaskBlock * c,
+                              kFwdBlockN);
+            return (int32_t)w;
+        }
+        if (p->causal)
+            return (int32_t)cdiv(std::min<int64_t>((int64_t)(t + 1) * kFwdBlockM, lk), kFwdBlockN);
+        return (int32_t)cdiv(lk, kFwdBlockN);
+    }
+    const int32_t nqb = (int32_t)cdiv(lq, kBwdBlockM);
+    if (sparse) {
+        const int32_t c = t * kBwdBlockN / kMaskBlock;
+        int32_t w = 0;
+        for (int32_t r = 0; r < nqb; ++r)
+            if (kept(p, mask, b, r * kBwdBlockM / kMaskBlock, c)) ++w;
+        return w;
+    }
+    if (p->causal) return nqb - (int32_t)(((int64_t)t * kBwdBlockN) / kBwdBlockM);
+    return nqb;
+}
+
+int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, const uint8_t* mask,
+                  int32_t pass, int32_t W, jfa_plan_info* info, int32_t* worker_ptr,
+                  int32_t* tiles_out, int32_t* sp_ptr, int32_t* sp_idx, bool build) {
+    if (info == nullptr) return JFA_ERR_INVALID_ARG;
+    int32_t st = check_problem(p);
+    if (st) return st;
+    if (pass != JFA_PASS_FWD && pass != JFA_PASS_BWD) return JFA_ERR_INVALID_ARG;
+    if (W < 1) return JFA_ERR_INVALID_ARG;
+    const bool sparse = p->mask_q_blocks != 0;
+    if (sparse && mask == nullptr) return JFA_ERR_BAD_MASK;
+    Lens L;
+    st = lengths_of(p, qo, ko, L);
+    if (st) return st;
+
+    const int32_t bm = pass == JFA_PASS_FWD ? kFwdBlockM : kBwdBlockM;
+    const int32_t bn = pass == JFA_PASS_FWD ? kFwdBlockN : kBwdBlockN;
+
+    // 1-2. enumerate tiles with their work
+    std::vector<Tile> tiles;
+    int64_t n_total = 0;
+    for (int32_t b = 0; b < p->batch; ++b)
+        n_total += (int64_t)p->num_heads *
+                   (pass == JFA_PASS_FWD ? cdiv(L.q[b], bm) : cdiv(L.kv[b], bn));
+    if (n_total > INT32_MAX / 4) return JFA_ERR_INVALID_ARG;
+    tiles.reserve((size_t)n_total);
+    int64_t total_work = 0;
+    int32_t max_work = 0;
+    for (int32_t b = 0; b < p->batch; ++b) {
+        const int32_t nt =
+            (int32_t)(pass == JFA_PASS_FWD ? cdiv(L.q[b], bm) : cdiv(L.kv[b], bn));
+        for (int32_t h = 0; h < p->num_heads; ++h)
+            for (int32_t t = 0; t < nt; ++t) {
+                const int32_t w = tile_work(p, mask, pass, b, t, L.q[b], L.kv[b]);
+                tiles.push_back({b, h, t, w});
+                total_work += w;
+                max_work = std::max(max_work, w);
+            }
+    }
+
+    // block-sparse lists
+    int64_t sp_rows = 0, sp_nnz = 0;
+    if (sparse) {
+        if (pass == JFA_PASS_FWD) {
+            sp_rows = (int64_t)p->batch * p->mask_q_blocks;
+            for (int32_t b = 0; b < p->batch; ++b)
+                for (int32_t m = 0; m < p->mask_q_blocks; ++m)
+                    for (int32_t c = 0; c < cdiv(L.kv[b], kMaskBlock); ++c)
+                        sp_nnz += kept(p, mask, b, m, c);
+        } else {
+            sp_rows = (int64_t)p->batch * p->mask_kv_blocks;
+            for (int32_t b = 0; b < p->batch; ++b)
+                for (int32_t c = 0; c < p->mask_kv_blocks; ++c)
+                    for (int32_t m = 0; m < cdiv(L.q[b], kMaskBlock); ++m)
+                        sp_nnz += kept(p, mask, b, m, c);
+        }
+        if (sp_rows > INT32_MAX - 1 || sp_nnz > INT32_MAX) return JFA_ERR_INVALID_ARG;
+    }
+
+    info->pass = pass;
+    info->num_workers = W;
+    info->num_tiles = (int32_t)tiles.size();
+    info->block_m = bm;
+    info->block_n = bn;
+    info->total_q = (int32_t)L.total_q;
+    info->total_kv = (int32_t)L.total_kv;
+    info->sparse_rows = (int32_t)sp_rows;
+    info->sparse_nnz = (int32_t)sp_nnz;
+    info->max_work = max_work;
+    info->total_work = total_work;
+    if (!build) return JFA_OK;
+    if (worker_ptr == nullptr || (tiles_out == nullptr && !tiles.empty()))
+        return JFA_ERR_INVALID_ARG;
+    if (sparse && (sp_ptr == nullptr || (sp_idx == nullptr && sp_nnz > 0)))
+        return JFA_ERR_INVALID_ARG;
+
+    // 3. stable sort by work, descending
+    std::vector<int32_t> order(tiles.size());
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int32_t a, int32_t c) { return tiles[a].work > tiles[c].work; });
+    // 4. snake deal; 5. emit per worker in increasing deal position
+    std::vector<int32_t> count(W, 0), owner(order.size());
+    for (size_t i = 0; i < order.size(); ++i) {
+        const int32_t pos = (int32_t)(i % W);
+        const int32_t w = ((i / W) % 2 == 0) ? pos : W - 1 - pos;
+        owner[i] = w;
+        ++count[w];
+    }
+    worker_ptr[0] = 0;
+    for (int32_t w = 0; w < W; ++w) worker_ptr[w + 1] = worker_ptr[w] + count[w];
+    std::vector<int32_t> cursor(worker_ptr, worker_ptr + W);
+    for (size_t i = 0; i < order.size(); ++i) {
+        const Tile& t = tiles[order[i]];
+        int32_t* dst = tiles_out + 4 * (int64_t)cursor[owner[i]]++;
+        dst[0] = t.b;
+        dst[1] = t.h;
+        dst[2] = t.t;
+        dst[3] = t.work;
+    }
+
+    if (sparse) {
+        int32_t n = 0;
+        sp_ptr[0] = 0;
+        int32_t r = 0;
+        if (pass == JFA_PASS_FWD) {
+            for (int32_t b = 0; b < p->batch; ++b)
+                for (int32_t m = 0; m < p->mask_q_blocks; ++m) {
+                    for (int32_t c = 0; c < cdiv(L.kv[b], kMaskBlock); ++c)
+                        if (kept(p, mask, b, m, c)) sp_idx[n++] = c;
+                    sp_ptr[++r] = n;
+                }
+        } else {
+            for (int32_t b = 0; b < p->batch; ++b)
+                for (int32_t c = 0; c < p->mask_kv_blocks; ++c) {
+                    for (int32_t m = 0; m < cdiv(L.q[b], kMaskBlock); ++m)
+                        if (kept(p, mask, b, m, c)) sp_idx[n++] = m;
+                    sp_ptr[++r] = n;
+                }
+        }
+    }
+    return JFA_OK;
+}
+
+}  // namespace
+}  // namespace jfa
+
+extern "C" {
+
+int32_t jfa_offsets_from_lengths(const int32_t* h_lengths, int32_t batch, int32_t* h_offsets) {
+    if (batch < 0 || h_offsets == nullptr || (batch > 0 && h_lengths == nullptr))
+        return JFA_ERR_INVALID_ARG;
+    int64_t acc = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+        if (h_lengths[b] < 0) return JFA_ERR_BAD_OFFSETS;
+        acc += h_lengths[b];
+        if (acc > INT32_MAX) return JFA_ERR_BAD_OFFSETS;
+    }
+    acc = 0;
+    h_offsets[0] = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+        acc += h_lengths[b];
+        h_offsets[b + 1] = (int32_t)acc;
+    }
+    return JFA_OK;
+}
+
+int32_t jfa_plan_query(const jfa_problem* prob, const int32_t* h_q_offsets,
+                       const int32_t* h_kv_offsets, const uint8_t* h_block_mask, int32_t pass,
+                       int32_t num_workers, jfa_plan_info* info) {
+    return jfa::plan_impl(prob, h_q_offsets, h_kv_offsets, h_block_mask, pass, num_workers, info,
+                          nullptr, nullptr, nullptr, nullptr, false);
+}
+
+int32_t jfa_plan_build(const jfa_problem* prob, const int32_t* h_q_offsets,
+                       const int32_t* h_kv_offsets, const uint8_t* h_block_mask, int32_t pass,
+                       int32_t num_workers, jfa_plan_info* info, int32_t* h_worker_ptr,
+                       int32_t* h_tiles, int32_t* h_sparse_ptr, int32_t* h_sparse_idx) {
+    return jfa::plan_impl(prob, h_q_offsets, h_kv_offsets, h_block_mask, pass, num_workers, info,
+                          h_worker_ptr, h_tiles, h_sparse_ptr, h_sparse_idx, true);
+}
+
+}  // extern "C"

@@ -1,0 +1,141 @@
+"""The C ABI library on the CPU: it loads, exports every symbol the header
+declares, and its host-side logic (offsets, planner, argument validation)
+behaves as documented. No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import jagged_flashattention_amd as J
+import workloads as W
+from oracle import planner as OP
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "jfa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(jfa_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _header_functions()
+    assert len(names) >= 10
+    lib = ctypes.CDLL(J.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(J.EXPORTS)
+
+
+def test_version_and_status_strings():
+    assert J.jfa_abi_version() == 1
+    for st in range(-7, 1):
+        assert J.jfa_status_string(st) not in ("", "unknown status")
+    assert J.jfa_status_string(-99) == "unknown status"
+
+
+def test_offsets_from_lengths_matches_oracle():
+    x = W.make_inputs(2)
+    assert np.array_equal(J.jfa_offsets_from_lengths(x.lengths),
+                          OP.offsets_from_lengths(x.lengths))
+    assert list(J.jfa_offsets_from_lengths([])) == [0]
+    with pytest.raises(J.JfaError) as e:
+        J.jfa_offsets_from_lengths([3, -1])
+    assert e.value.status == J.JFA_ERR_BAD_OFFSETS
+    with pytest.raises(J.JfaError):
+        J.jfa_offsets_from_lengths([2**30, 2**30, 2**30])
+
+
+def _prob(**kw):
+    base = dict(batch=2, num_heads=1, head_dim=64, broadcast_q=True, lq=8, softmax_scale=0.125)
+    base.update(kw)
+    return J.Problem(**base)
+
+
+@pytest.mark.parametrize("kw,qoff,kvoff,mask,status", [
+    (dict(head_dim=96), None, [0, 3, 5], None, J.JFA_ERR_UNSUPPORTED),
+    (dict(causal=True), None, [0, 3, 5], None, J.JFA_ERR_UNSUPPORTED),
+    (dict(), None, [1, 3, 5], None, J.JFA_ERR_BAD_OFFSETS),
+    (dict(), None, [0, 3, 2], None, J.JFA_ERR_BAD_OFFSETS),
+    (dict(broadcast_q=False, causal=True), [0, 3, 6], [0, 3, 5], None, J.JFA_ERR_UNSUPPORTED),
+    (dict(broadcast_q=False), None, [0, 3, 5], None, J.JFA_ERR_INVALID_ARG),
+    (dict(num_heads=0), None, [0, 3, 5], None, J.JFA_ERR_INVALID_ARG),
+    (dict(batch=-1), None, [0], None, J.JFA_ERR_INVALID_ARG),
+    (dict(mask_q_blocks=1, mask_kv_blocks=1), None, [0, 3, 5], None, J.JFA_ERR_BAD_MASK),
+    (dict(mask_q_blocks=1, mask_kv_blocks=1), None, [0, 300, 305],
+     np.ones((2, 1, 1), np.uint8), J.JFA_ERR_BAD_MASK),
+    (dict(mask_q_blocks=1, mask_kv_blocks=0), None, [0, 3, 5], None, J.JFA_ERR_BAD_MASK),
+    (dict(broadcast_q=False, causal=True, mask_q_blocks=1, mask_kv_blocks=1), [0, 3, 5],
+     [0, 3, 5], np.ones((2, 1, 1), np.uint8), J.JFA_ERR_UNSUPPORTED),
+    (dict(softmax_scale=float("nan")), None, [0, 3, 5], None, J.JFA_ERR_INVALID_ARG),
+])
+def test_planner_rejects_bad_problems(kw, qoff, kvoff, mask, status):
+    with pytest.raises(J.JfaError) as e:
+        J.jfa_plan_build(_prob(**kw), qoff, kvoff, mask, J.JFA_PASS_FWD, 4)
+    assert e.value.status == status
+
+
+def test_planner_rejects_zero_workers_and_bad_pass():
+    with pytest.raises(J.JfaError) as e:
+        J.jfa_plan_query(_prob(), None, [0, 3, 5], None, J.JFA_PASS_FWD, 0)
+    assert e.value.status == J.JFA_ERR_INVALID_ARG
+    with pytest.raises(J.JfaError) as e:
+        J.jfa_plan_query(_prob(), None, [0, 3, 5], None, 7, 4)
+    assert e.value.status == J.JFA_ERR_INVALID_ARG
+
+
+def test_empty_batch_plan():
+    p = J.jfa_plan_build(_prob(batch=0), None, [0], None, J.JFA_PASS_FWD, 8)
+    assert p.info.num_tiles == 0 and list(p.worker_ptr) == [0] * 9
+
+
+class _FakeTensor:
+    def __init__(self, addr):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+def _call_fwd(prob, info, **over):
+    t = _FakeTensor(0x1000)
+    args = dict(worker_ptr=t, tiles=t, sparse_ptr=None, sparse_idx=None, q_off=None, kv_off=t,
+                q=t, k=t, v=t, o=t, lse=t)
+    args.update(over)
+    cp = prob.c()
+    f = lambda x: None if x is None else ctypes.c_void_p(x.data_ptr())
+    return J._lib().jfa_fwd(ctypes.byref(cp), ctypes.byref(info), f(args["worker_ptr"]),
+                            f(args["tiles"]), f(args["sparse_ptr"]), f(args["sparse_idx"]),
+                            f(args["q_off"]), f(args["kv_off"]), f(args["q"]), f(args["k"]),
+                            f(args["v"]), f(args["o"]), f(args["lse"]), None)
+
+
+def test_fwd_validation_returns_before_launch():
+    prob = _prob()
+    fwd = J.jfa_plan_build(prob, None, [0, 3, 5], None, J.JFA_PASS_FWD, 4)
+    bwd = J.jfa_plan_build(prob, None, [0, 3, 5], None, J.JFA_PASS_BWD, 4)
+    assert _call_fwd(prob, bwd.info) == J.JFA_ERR_PLAN_MISMATCH          # wrong pass
+    assert _call_fwd(prob, fwd.info, q=_FakeTensor(0x1008)) == J.JFA_ERR_INVALID_ARG  # misaligned
+    assert _call_fwd(prob, fwd.info, o=None) == J.JFA_ERR_INVALID_ARG
+    assert _call_fwd(prob, fwd.info, tiles=None) == J.JFA_ERR_INVALID_ARG
+    assert _call_fwd(_prob(lq=9), fwd.info) == J.JFA_ERR_PLAN_MISMATCH   # T_q != B*lq
+    assert _call_fwd(_prob(head_dim=32), fwd.info) == J.JFA_ERR_UNSUPPORTED
+    sp = _prob(mask_q_blocks=1, mask_kv_blocks=1)
+    assert _call_fwd(sp, fwd.info) == J.JFA_ERR_PLAN_MISMATCH            # dense plan, sparse prob
+    # an empty problem is a no-op that launches nothing
+    e = J.jfa_plan_build(_prob(batch=0), None, [0], None, J.JFA_PASS_FWD, 4)
+    assert _call_fwd(_prob(batch=0), e.info, worker_ptr=None, tiles=None, q=None, k=None, v=None,
+                     o=None, lse=None, kv_off=None) == J.JFA_OK
+
+
+def test_bwd_workspace_query():
+    prob = _prob()
+    bwd = J.jfa_plan_build(prob, None, [0, 3, 5], None, J.JFA_PASS_BWD, 4)
+    assert J.jfa_bwd_workspace_bytes(prob, bwd.info) >= 0
+    fwd = J.jfa_plan_build(prob, None, [0, 3, 5], None, J.JFA_PASS_FWD, 4)
+    with pytest.raises(J.JfaError) as e:
+        J.jfa_bwd_workspace_bytes(prob, fwd.info)
+    assert e.value.status == J.JFA_ERR_PLAN_MISMATCH

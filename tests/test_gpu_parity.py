@@ -1,0 +1,263 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Small cases: the oracle evaluates every output; they span several tiles and
+ragged tails of every mode (broadcast Q, per-sequence Q, causal, block-sparse,
+D = 64 and 128, empty and one-key sequences, Lq not a multiple of the tile).
+Full sizes: the five workloads run in the launch configuration the benchmark
+times, and sampled outputs are compared with the oracle row by row.
+
+Tolerances (stated for this path): O and LSE max |gpu - oracle| <= 1e-2;
+dQ, dK, dV max |gpu - oracle| / max |oracle| <= 2e-2.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention as A
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import jagged_flashattention_amd as J  # noqa: E402
+
+TOL_O = 1e-2
+TOL_GRAD = 2e-2
+
+
+def dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def host_f64(t):
+    u = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return W.bf16_bits_to_f32(u).astype(np.float64)
+
+
+def problem_of(x):
+    w = x.workload
+    mq, mk = (x.block_mask.shape[1], x.block_mask.shape[2]) if x.block_mask is not None else (0, 0)
+    return J.Problem(batch=x.batch, num_heads=w.heads, head_dim=w.head_dim,
+                     broadcast_q=w.broadcast_q, lq=w.lq if w.broadcast_q else 0,
+                     causal=w.causal, mask_q_blocks=mq, mask_kv_blocks=mk,
+                     softmax_scale=w.scale)
+
+
+@dataclasses.dataclass
+class GpuRun:
+    o: object
+    lse: object
+    dq: object
+    dk: object
+    dv: object
+    dq_accum: object
+    delta: object
+
+
+def run_gpu(x, fwd_workers=None, bwd_workers=None, canary=True):
+    prob = problem_of(x)
+    att = J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask,
+                            fwd_workers=fwd_workers, bwd_workers=bwd_workers)
+    q, k, v, do = dev(x.q), dev(x.k), dev(x.v), dev(x.do)
+    H, D = prob.num_heads, prob.head_dim
+    o = torch.empty((att.total_q, H, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((H, att.total_q), dtype=torch.float32, device="cuda")
+    if canary:
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+    att.forward(q, k, v, o, lse)
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               dq_accum=torch.empty(q.shape, dtype=torch.float32, device="cuda"),
+               delta=torch.empty((H, att.total_q), dtype=torch.float32, device="cuda"))
+    if canary:
+        for t in out.values():
+            t.fill_(float("nan"))
+    att.backward(q, k, v, o, lse, do, out)
+    torch.cuda.synchronize()
+    return GpuRun(o, lse, **out)
+
+
+def oracle_full(x):
+    q, k, v, do = (x.as_f64(n) for n in ("q", "k", "v", "do"))
+    w = x.workload
+    kw = dict(scale=w.scale, broadcast_q=w.broadcast_q, q_offsets=x.q_offsets, causal=w.causal,
+              block_mask=x.block_mask)
+    o, lse = A.forward(q, k, v, x.kv_offsets, **kw)
+    dq, dk, dv, delta = A.backward(q, k, v, do, x.kv_offsets, **kw)
+    return o, lse, dq, dk, dv, delta
+
+
+def rel_err(got, ref):
+    scale = np.abs(ref).max()
+    return np.abs(got - ref).max() / (scale if scale > 0 else 1.0)
+
+
+def check_all(x, g):
+    o, lse, dq, dk, dv, delta = oracle_full(x)
+    go, glse = host_f64(g.o), g.lse.cpu().numpy().astype(np.float64)
+    assert not np.isnan(go).any() and not np.isnan(glse).any()
+    fin = np.isfinite(lse)
+    assert np.array_equal(fin, np.isfinite(glse)), "rows without keys must give LSE=-inf"
+    assert np.abs(go - o).max() <= TOL_O
+    if fin.any():
+        assert np.abs(glse[fin] - lse[fin]).max() <= TOL_O
+    gdq, gdk, gdv = host_f64(g.dq), host_f64(g.dk), host_f64(g.dv)
+    for name, got, ref in (("dq", gdq, dq), ("dk", gdk, dk), ("dv", gdv, dv)):
+        assert not np.isnan(got).any(), name
+        assert rel_err(got, ref) <= TOL_GRAD, (name, rel_err(got, ref))
+    assert rel_err(g.dq_accum.cpu().numpy().astype(np.float64), dq) <= TOL_GRAD
+    gdelta = g.delta.cpu().numpy()
+    assert np.abs(gdelta - delta).max() <= 2e-2 * max(1.0, np.abs(delta).max())
+
+
+def _custom(name, *, broadcast, H, D, lengths, lq=0, causal=False, mask_seed=None, seed=11,
+            q_lengths=None):
+    w = W.Workload(name, len(lengths), H, D, broadcast, lq, causal, "const:1", seed=seed,
+                   mask_seed=mask_seed)
+    x = W.make_inputs(w, lengths=np.array(lengths))
+    if q_lengths is not None:
+        # per-sequence Q with its own lengths: redraw Q / dO rows for them
+        rng = np.random.default_rng(seed + 1000)
+        q_off = W.offsets_of(np.array(q_lengths))
+        tq = int(q_off[-1])
+        x = dataclasses.replace(
+            x, q_offsets=q_off,
+            q=W.f32_to_bf16_bits(rng.standard_normal((tq, H, D), dtype=np.float32)),
+            do=W.f32_to_bf16_bits(rng.standard_normal((tq, H, D), dtype=np.float32)))
+    return x
+
+
+RAGGED = [0, 1, 15, 16, 63, 64, 65, 127, 128, 129, 200, 300]
+CAUSAL = [1, 63, 64, 65, 128, 129, 257, 400]
+
+SMALL_CASES = {
+    "cfg1": lambda: W.make_inputs(1),
+    "bcast_ragged_d128": lambda: _custom("b128", broadcast=True, H=2, D=128, lengths=RAGGED, lq=100),
+    "bcast_ragged_d64": lambda: _custom("b64", broadcast=True, H=3, D=64, lengths=RAGGED, lq=200),
+    "perseq_d128": lambda: _custom("p128", broadcast=False, H=2, D=128,
+                                   lengths=[70, 3, 200, 129, 0], q_lengths=[5, 130, 64, 1, 7]),
+    "causal_d128": lambda: _custom("c128", broadcast=False, H=2, D=128, lengths=CAUSAL, causal=True),
+    "causal_d64": lambda: _custom("c64", broadcast=False, H=2, D=64, lengths=CAUSAL, causal=True),
+    "sparse_d128": lambda: _custom("s128", broadcast=True, H=2, D=128, lq=256, mask_seed=5,
+                                   lengths=[1, 64, 65, 127, 128, 129, 300, 513, 640]),
+    "sparse_d64": lambda: _custom("s64", broadcast=True, H=2, D=64, lq=200, mask_seed=7,
+                                  lengths=[1, 64, 65, 127, 128, 129, 300, 513]),
+    "cfg2_small": lambda: W.make_inputs(2, batch=16, heads=2),
+    "cfg3_small": lambda: W.make_inputs(3, batch=3, heads=2),
+    "cfg4_small": lambda: W.make_inputs(4, batch=2, heads=2),
+    "cfg5_small": lambda: W.make_inputs(5, batch=12, heads=2),
+}
+
+
+@pytest.mark.parametrize("case", list(SMALL_CASES))
+def test_small_parity(case):
+    print("case", case, flush=True)
+    x = SMALL_CASES[case]()
+    check_all(x, run_gpu(x))
+
+
+def test_one_key_sequence_is_bitwise_v_row():
+    x = _custom("onekey", broadcast=True, H=2, D=128, lengths=[1, 5, 1], lq=70)
+    g = run_gpu(x)
+    o = g.o.view(torch.int16).cpu().numpy().view(np.uint16)
+    for b, row in ((0, 0), (2, 6)):
+        for h in range(2):
+            assert np.array_equal(o[b * 70:(b + 1) * 70, h], np.broadcast_to(x.v[row, h], (70, 128)))
+
+
+def test_zero_q_gives_mean_of_v():
+    x = _custom("zeroq", broadcast=True, H=1, D=64, lengths=[7, 300], lq=40)
+    x = dataclasses.replace(x, q=np.zeros_like(x.q))
+    g = run_gpu(x)
+    o = host_f64(g.o)
+    v = W.bf16_bits_to_f32(x.v).astype(np.float64)
+    assert np.abs(o[:40] - v[0:7].mean(axis=0)).max() <= TOL_O
+    assert np.abs(o[40:] - v[7:307].mean(axis=0)).max() <= TOL_O
+    lse = g.lse.cpu().numpy()
+    np.testing.assert_allclose(lse[0, :40], np.log(7), atol=1e-5)
+    np.testing.assert_allclose(lse[0, 40:], np.log(300), atol=1e-5)
+
+
+@pytest.mark.parametrize("case", ["bcast_ragged_d128", "causal_d128", "sparse_d128"])
+def test_deterministic_across_plans_and_runs(case):
+    """O, LSE, dK, dV are bitwise identical for any worker count (each tile is
+    computed by one workgroup in a fixed order); dQ sums in fp32 atomics, so
+    it only agrees to reassociation."""
+    x = SMALL_CASES[case]()
+    runs = [run_gpu(x, fwd_workers=fw, bwd_workers=bw) for fw, bw in ((None, None), (1, 1), (7, 13),
+                                                                      (None, None))]
+    ref = runs[0]
+    for r in runs[1:]:
+        for name in ("o", "lse", "dk", "dv", "delta"):
+            a, b = getattr(ref, name), getattr(r, name)
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), name
+        d = (ref.dq_accum - r.dq_accum).abs().max().item()
+        assert d <= 1e-4 * max(1.0, ref.dq_accum.abs().max().item())
+
+
+# ----------------------------------------------------------------- full sizes
+
+def _head_f64(bits, h, rows=None):
+    sl = bits[:, h, :] if rows is None else bits[rows, h, :]
+    return W.bf16_bits_to_f32(sl).astype(np.float64)[:, None, :]
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_size_sampled_parity(cfg):
+    print("full-size workload", cfg, flush=True)
+    x = W.make_inputs(cfg)
+    g = run_gpu(x, canary=True)
+    w = x.workload
+    rng = np.random.default_rng(100 + cfg)
+    lens = x.lengths
+    seqs = sorted(set([int(np.argmax(lens)), int(np.argmin(lens)), int(rng.integers(0, x.batch))]))
+    go = g.o.view(torch.int16).cpu().numpy().view(np.uint16)
+    glse = g.lse.cpu().numpy()
+    gdk = g.dk.view(torch.int16).cpu().numpy().view(np.uint16)
+    gdv = g.dv.view(torch.int16).cpu().numpy().view(np.uint16)
+    gdq = g.dq_accum.cpu().numpy()
+    assert not np.isnan(glse).any()
+    heads = [int(rng.integers(0, w.heads))]
+    for b in seqs:
+        k0, k1 = int(x.kv_offsets[b]), int(x.kv_offsets[b + 1])
+        if w.broadcast_q:
+            qs, os_ = slice(0, w.lq), slice(b * w.lq, (b + 1) * w.lq)
+        else:
+            qs = os_ = slice(int(x.q_offsets[b]), int(x.q_offsets[b + 1]))
+        for h in heads:
+            q1 = _head_f64(x.q, h, qs)
+            k1_ = _head_f64(x.k, h, slice(k0, k1))
+            v1 = _head_f64(x.v, h, slice(k0, k1))
+            do1 = _head_f64(x.do, h, os_)
+            off = np.array([0, k1 - k0], dtype=np.int32)
+            qoff = None if w.broadcast_q else np.array([0, qs.stop - qs.start], dtype=np.int32)
+            mask = None if x.block_mask is None else x.block_mask[b:b + 1]
+            kw = dict(scale=w.scale, broadcast_q=w.broadcast_q, q_offsets=qoff, causal=w.causal,
+                      block_mask=mask)
+            o, lse = A.forward(q1, k1_, v1, off, **kw)
+            dq, dk, dv, _ = A.backward(q1, k1_, v1, do1, off, **kw)
+            assert np.abs(W.bf16_bits_to_f32(go[os_, h]) - o[:, 0]).max() <= TOL_O, (b, h)
+            assert np.abs(glse[h, os_] - lse[0]).max() <= TOL_O, (b, h)
+            assert rel_err(W.bf16_bits_to_f32(gdk[k0:k1, h]), dk[:, 0]) <= TOL_GRAD, (b, h)
+            assert rel_err(W.bf16_bits_to_f32(gdv[k0:k1, h]), dv[:, 0]) <= TOL_GRAD, (b, h)
+            if not w.broadcast_q:
+                assert rel_err(gdq[qs, h], dq[:, 0]) <= TOL_GRAD, (b, h)
+    if w.broadcast_q:
+        # rows of the batch-summed dQ need one row of every sequence's scores
+        rows = np.array(sorted(set([0, w.lq - 1] + list(rng.integers(0, w.lq, size=4)))))
+        h = heads[0]
+        q_h = _head_f64(x.q, h)
+        k_h = _head_f64(x.k, h)
+        v_h = _head_f64(x.v, h)
+        do_h = _head_f64(x.do, h)
+        ref = A.broadcast_dq_rows(q_h, k_h, v_h, do_h, x.kv_offsets, 0, rows, scale=w.scale,
+                                  block_mask=x.block_mask)
+        assert rel_err(gdq[rows, h], ref) <= TOL_GRAD
+        # and the bf16 dq is the rounding of the fp32 sum
+        gdq16 = host_f64(g.dq)
+        assert np.abs(gdq16 - gdq).max() <= 2 ** -8 * np.abs(gdq).max()
