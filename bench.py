@@ -1,0 +1,274 @@
+"""Benchmark: jagged FlashAttention forward + backward on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input: jfa_fwd
+(O, LSE) then the backward stages (delta preprocess, main dK/dV/dQ kernel,
+dQ convert). Inputs are resident in HBM before timing starts. The default
+workload is the GEM-shaped broadcast-Q one (B=256 sequences with lognormal
+lengths, H=4, D=128, one shared Q of 256 rows).
+
+Prints ONE JSON line with the throughput (algorithmic fwd+bwd TFLOP/s), the
+roofline of the dominant kernel (timed with HIP events on the launch stream)
+and the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+METRIC = "JFA fwd+bwd TFLOP/s (bf16) and % of MFMA peak, jagged broadcast-Q"
+
+
+def work_model(x):
+    """Algorithmic FLOPs and bytes of one step (see the design notes)."""
+    import numpy as np
+    w = x.workload
+    H, D = w.heads, w.head_dim
+    lens = x.lengths.astype(np.int64)
+    B = len(lens)
+    t_k = int(lens.sum())
+    if w.broadcast_q:
+        q_rows, t_q = w.lq, B * w.lq
+        q_lens = np.full(B, w.lq, dtype=np.int64)
+    else:
+        q_lens = np.diff(x.q_offsets.astype(np.int64))
+        q_rows = t_q = int(q_lens.sum())
+    kv_read_rows = t_k
+    if x.block_mask is not None:
+        pairs = 0
+        kv_read_rows = 0
+        mask = x.block_mask
+        for b in range(B):
+            nk = -(-int(lens[b]) // 128)
+            nq = -(-int(q_lens[b]) // 128)
+            rows = np.minimum(128, q_lens[b] - 128 * np.arange(nq))
+            keys = np.minimum(128, lens[b] - 128 * np.arange(nk))
+            m = mask[b, :nq, :nk].astype(np.int64)
+            pairs += int(rows @ m @ keys)
+            kv_read_rows += int(keys[m.any(axis=0)].sum())
+    elif w.causal:
+        pairs = int((lens * (lens + 1) // 2).sum())
+    else:
+        pairs = int((q_lens * lens).sum())
+    e = H * D * 2   # bytes of one bf16 row of all heads
+    fwd_bytes = q_rows * e + 2 * kv_read_rows * e + t_q * e + t_q * H * 4
+    pre_bytes = 2 * t_q * e + t_q * H * 4 + q_rows * H * D * 4
+    main_bytes = (q_rows * e + 2 * kv_read_rows * e + t_q * e + 2 * t_q * H * 4 + 2 * t_k * e
+                  + q_rows * H * D * 4)
+    fin_bytes = q_rows * H * D * 4 + q_rows * e
+    return dict(pairs=pairs, fwd_flop=4 * H * D * pairs, bwd_flop=10 * H * D * pairs,
+                fwd_bytes=fwd_bytes, pre_bytes=pre_bytes, main_bytes=main_bytes,
+                fin_bytes=fin_bytes, t_q=t_q, t_k=t_k, q_rows=q_rows)
+
+
+def cpu_baseline(x, budget_s: float):
+    """The fp64 oracle (as it stands) on the first sequences of the same
+    workload until ``budget_s`` seconds of CPU work are spent."""
+    from threadpoolctl import threadpool_info
+    import numpy as np
+    from oracle import attention as A
+    import workloads as W
+    w = x.workload
+    q = x.as_f64("q") if w.broadcast_q else None
+    done, flop, t_used = 0, 0.0, 0.0
+    kw = dict(scale=w.scale, broadcast_q=w.broadcast_q, causal=w.causal)
+    for b in range(x.batch):
+        k0, k1 = int(x.kv_offsets[b]), int(x.kv_offsets[b + 1])
+        k = W.bf16_bits_to_f32(x.k[k0:k1]).astype(np.float64)
+        v = W.bf16_bits_to_f32(x.v[k0:k1]).astype(np.float64)
+        off = np.array([0, k1 - k0], dtype=np.int32)
+        if w.broadcast_q:
+            qb, os_ = q, slice(b * w.lq, (b + 1) * w.lq)
+            qoff = None
+            n_rows = w.lq
+        else:
+            q0, q1 = int(x.q_offsets[b]), int(x.q_offsets[b + 1])
+            qb = W.bf16_bits_to_f32(x.q[q0:q1]).astype(np.float64)
+            os_ = slice(q0, q1)
+            qoff = np.array([0, q1 - q0], dtype=np.int32)
+            n_rows = q1 - q0
+        do = W.bf16_bits_to_f32(x.do[os_]).astype(np.float64)
+        mask = None if x.block_mask is None else x.block_mask[b:b + 1]
+        t0 = time.perf_counter()
+        A.forward(qb, k, v, off, q_offsets=qoff, block_mask=mask, **kw)
+        A.backward(qb, k, v, do, off, q_offsets=qoff, block_mask=mask, **kw)
+        t_used += time.perf_counter() - t0
+        L = k1 - k0
+        if mask is not None:
+            vis = A.visibility(n_rows, L, mask_b=mask[0])
+            pairs = int(vis.sum())
+        elif w.causal:
+            pairs = L * (L + 1) // 2
+        else:
+            pairs = n_rows * L
+        flop += 14.0 * w.heads * w.head_dim * pairs
+        done += 1
+        if t_used >= budget_s:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                   if p.get("internal_api") in ("openblas", "mkl", "blis")] or [1])
+    return {"value": flop / t_used / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "fp64 oracle fwd+bwd of the first %d of %d sequences (all %d heads) of the "
+                      "same workload, %.1f s" % (done, x.batch, w.heads, t_used)}
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if
+    they were taken on the current kernel source; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "%s.%s.traffic.txt" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            a, b = line.split("=", 1)
+            kv[a.strip()] = b.strip()
+    src = os.path.join(ROOT, "jagged_flashattention_amd", "csrc", kv.get("source", ""))
+    if not os.path.exists(src):
+        return None
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if digest != kv.get("source_sha256_16"):
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, help="1..5 (2: GEM-shaped broadcast-Q)")
+    ap.add_argument("--fwd-workers-per-cu", type=int, default=2)
+    ap.add_argument("--bwd-workers-per-cu", type=int, default=1)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle CPU work for the baseline (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+              "(the multi-GPU sharding is described in the design notes, not built)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import jagged_flashattention_amd as J
+    import workloads as W
+
+    x = W.make_inputs(args.workload)
+    w = x.workload
+    model = work_model(x)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v, do = dev(x.q), dev(x.k), dev(x.v), dev(x.do)
+    mq, mk = (x.block_mask.shape[1], x.block_mask.shape[2]) if x.block_mask is not None else (0, 0)
+    prob = J.Problem(batch=x.batch, num_heads=w.heads, head_dim=w.head_dim,
+                     broadcast_q=w.broadcast_q, lq=w.lq if w.broadcast_q else 0, causal=w.causal,
+                     mask_q_blocks=mq, mask_kv_blocks=mk, softmax_scale=w.scale)
+    cus = J.jfa_device_workers(0)
+    t0 = time.perf_counter()
+    att = J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask,
+                            fwd_workers=cus * args.fwd_workers_per_cu,
+                            bwd_workers=cus * args.bwd_workers_per_cu)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    H, D = w.heads, w.head_dim
+    o = torch.empty((att.total_q, H, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((H, att.total_q), dtype=torch.float32, device="cuda")
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               dq_accum=torch.empty(q.shape, dtype=torch.float32, device="cuda"),
+               delta=torch.empty((H, att.total_q), dtype=torch.float32, device="cuda"))
+    stages = (J.JFA_BWD_PREPROCESS, J.JFA_BWD_MAIN, J.JFA_BWD_FINISH)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        att.forward(q, k, v, o, lse)
+        for i, s in enumerate(stages):
+            if ev is not None:
+                ev[1 + i].record()
+            att.backward(q, k, v, o, lse, do, out, stages=s)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    names = ("fwd", "bwd_pre", "bwd_main", "bwd_finish")
+    per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in events])) for j, n in enumerate(names)}
+
+    flop = model["fwd_flop"] + model["bwd_flop"]
+    value = flop / (ms_step * 1e-3) / 1e12
+    wl_name = w.name
+    fwd_tf = model["fwd_flop"] / (per["fwd"] * 1e-3) / 1e12
+    bwd_ms = per["bwd_pre"] + per["bwd_main"] + per["bwd_finish"]
+    bwd_tf = model["bwd_flop"] / (bwd_ms * 1e-3) / 1e12
+
+    kernels = {
+        "fwd": ("fwd.hip", model["fwd_flop"], model["fwd_bytes"]),
+        "bwd_main": ("bwd.hip", model["bwd_flop"], model["main_bytes"]),
+    }
+    dom = max(kernels, key=lambda n: per[n])
+    _, kflop, kbytes = kernels[dom]
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    t_s = per[dom] * 1e-3
+    if kflop / kbytes >= ridge:
+        roof = {"bound": "mfma", "achieved": kflop / t_s / 1e12, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": kbytes / t_s / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_for(dom, wl_name)
+    roof["kernel"] = dom
+    roof["avg_ms"] = per[dom]
+    roof["algorithmic_flop"] = kflop
+    roof["algorithmic_bytes"] = kbytes
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl_name, "batch": x.batch, "heads": H, "head_dim": D,
+                   "broadcast_q": w.broadcast_q, "lq": w.lq if w.broadcast_q else None,
+                   "causal": w.causal, "block_sparse": x.block_mask is not None,
+                   "lengths": w.lengths, "seed": w.seed, "total_kv": model["t_k"],
+                   "total_q": model["t_q"],
+                   "fwd_workers": att.fwd_plan.info.num_workers,
+                   "bwd_workers": att.bwd_plan.info.num_workers},
+        "pct_mfma_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "fwd_tflops": fwd_tf,
+        "bwd_tflops": bwd_tf,
+        "kernel_ms": per,
+        "plan_host_ms": plan_ms,
+        "roofline": roof,
+    }
+    if args.cpu_budget > 0:
+        res["cpu_baseline"] = cpu_baseline(x, args.cpu_budget)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

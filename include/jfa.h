@@ -189,6 +189,27 @@ int32_t jfa_bwd(const jfa_problem* prob, const jfa_plan_info* info,
                 void* dq, void* dk, void* dv, float* dq_accum, float* delta,
                 void* workspace, int64_t workspace_bytes, void* stream);
 
+/*
+ * The same backward, one stage at a time, for callers that interleave other
+ * work or time each launch: `stages` is a bitwise OR of the JFA_BWD_* flags;
+ * the selected launches are enqueued in stage order. Each stage expects the
+ * outputs of the stages before it to be in place (delta and a cleared
+ * dq_accum for MAIN, the summed dq_accum for FINISH). Arguments are the same
+ * as jfa_bwd and are validated the same way whatever the stages.
+ */
+#define JFA_BWD_PREPROCESS 1   /* delta = rowsum(dO*O); dq_accum = 0        */
+#define JFA_BWD_MAIN       2   /* dK, dV written; dQ partials into dq_accum */
+#define JFA_BWD_FINISH     4   /* dq = bf16(dq_accum)                       */
+#define JFA_BWD_ALL        7
+int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_plan_info* info,
+                       const int32_t* d_worker_ptr, const int32_t* d_tiles,
+                       const int32_t* d_sparse_ptr, const int32_t* d_sparse_idx,
+                       const int32_t* d_q_offsets, const int32_t* d_kv_offsets,
+                       const void* q, const void* k, const void* v,
+                       const void* o, const float* lse, const void* d_o,
+                       void* dq, void* dk, void* dv, float* dq_accum, float* delta,
+                       void* workspace, int64_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,8 +31,12 @@ JFA_PASS_BWD = 1
 EXPORTS = (
     "jfa_abi_version", "jfa_status_string", "jfa_last_hip_error", "jfa_device_workers",
     "jfa_offsets_from_lengths", "jfa_plan_query", "jfa_plan_build", "jfa_fwd",
-    "jfa_bwd_workspace_bytes", "jfa_bwd",
+    "jfa_bwd_workspace_bytes", "jfa_bwd", "jfa_bwd_stages",
 )
+JFA_BWD_PREPROCESS = 1
+JFA_BWD_MAIN = 2
+JFA_BWD_FINISH = 4
+JFA_BWD_ALL = 7
 
 
 class JfaProblem(ctypes.Structure):
@@ -87,6 +91,7 @@ def _lib():
             "jfa_fwd": (i32, [prob, info] + [_P] * 12),
             "jfa_bwd_workspace_bytes": (i32, [prob, info, ctypes.POINTER(i64)]),
             "jfa_bwd": (i32, [prob, info] + [_P] * 18 + [i64, _P]),
+            "jfa_bwd_stages": (i32, [i32, prob, info] + [_P] * 18 + [i64, _P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -243,14 +248,23 @@ def jfa_bwd(prob: Problem, plan: DevicePlan, q_offsets, kv_offsets, q, k, v, o, 
             dq, dk, dv, dq_accum, delta, workspace=None, workspace_bytes: int = 0,
             stream=None) -> None:
     """Enqueue the backward (preprocess, main, dQ convert) on ``stream``."""
+    jfa_bwd_stages(JFA_BWD_ALL, prob, plan, q_offsets, kv_offsets, q, k, v, o, lse, d_o, dq, dk,
+                   dv, dq_accum, delta, workspace, workspace_bytes, stream)
+
+
+def jfa_bwd_stages(stages: int, prob: Problem, plan: DevicePlan, q_offsets, kv_offsets, q, k, v,
+                   o, lse, d_o, dq, dk, dv, dq_accum, delta, workspace=None,
+                   workspace_bytes: int = 0, stream=None) -> None:
+    """Enqueue the selected backward stages (JFA_BWD_* flags) on ``stream``."""
     cp = prob.c()
-    _check(_lib().jfa_bwd(ctypes.byref(cp), ctypes.byref(plan.info), _dev_ptr(plan.worker_ptr),
+    _check(_lib().jfa_bwd_stages(stages, ctypes.byref(cp), ctypes.byref(plan.info),
+                                 _dev_ptr(plan.worker_ptr),
                           _dev_ptr(plan.tiles), _dev_ptr(plan.sparse_ptr),
                           _dev_ptr(plan.sparse_idx), _dev_ptr(q_offsets), _dev_ptr(kv_offsets),
                           _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(o), _dev_ptr(lse),
                           _dev_ptr(d_o), _dev_ptr(dq), _dev_ptr(dk), _dev_ptr(dv),
                           _dev_ptr(dq_accum), _dev_ptr(delta), _dev_ptr(workspace),
-                          int(workspace_bytes), _stream(stream)), "jfa_bwd")
+                          int(workspace_bytes), _stream(stream)), "jfa_bwd_stages")
 
 
 # ------------------------------------------------------- convenience wrappers
@@ -298,14 +312,14 @@ class JaggedAttention:
         jfa_fwd(self.prob, self.fwd_plan, self.q_offsets, self.kv_offsets, q, k, v, o, lse)
         return o, lse
 
-    def backward(self, q, k, v, o, lse, d_o, out=None):
+    def backward(self, q, k, v, o, lse, d_o, out=None, stages=JFA_BWD_ALL):
         import torch
         if out is None:
             out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
                        dq_accum=torch.empty(q.shape, dtype=torch.float32, device=self.device),
                        delta=torch.empty((self.prob.num_heads, self.total_q), dtype=torch.float32,
                                          device=self.device))
-        jfa_bwd(self.prob, self.bwd_plan, self.q_offsets, self.kv_offsets, q, k, v, o, lse, d_o,
-                out["dq"], out["dk"], out["dv"], out["dq_accum"], out["delta"], self.workspace,
-                self.ws_bytes)
+        jfa_bwd_stages(stages, self.prob, self.bwd_plan, self.q_offsets, self.kv_offsets, q, k, v,
+                       o, lse, d_o, out["dq"], out["dk"], out["dv"], out["dq_accum"],
+                       out["delta"], self.workspace, self.ws_bytes)
         return out

@@ -145,12 +145,14 @@ int32_t jfa_bwd_workspace_bytes(const jfa_problem* prob, const jfa_plan_info* in
     return JFA_OK;
 }
 
-int32_t jfa_bwd(const jfa_problem* prob, const jfa_plan_info* info, const int32_t* d_worker_ptr,
-                const int32_t* d_tiles, const int32_t* d_sparse_ptr, const int32_t* d_sparse_idx,
-                const int32_t* d_q_offsets, const int32_t* d_kv_offsets, const void* q,
-                const void* k, const void* v, const void* o, const float* lse, const void* d_o,
-                void* dq, void* dk, void* dv, float* dq_accum, float* delta, void* workspace,
-                int64_t workspace_bytes, void* stream) {
+int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_plan_info* info,
+                       const int32_t* d_worker_ptr, const int32_t* d_tiles,
+                       const int32_t* d_sparse_ptr, const int32_t* d_sparse_idx,
+                       const int32_t* d_q_offsets, const int32_t* d_kv_offsets, const void* q,
+                       const void* k, const void* v, const void* o, const float* lse,
+                       const void* d_o, void* dq, void* dk, void* dv, float* dq_accum,
+                       float* delta, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (stages < 0 || stages > JFA_BWD_ALL) return JFA_ERR_INVALID_ARG;
     int32_t st = check_common(prob, info, JFA_PASS_BWD, d_worker_ptr, d_tiles, d_sparse_ptr,
                               d_sparse_idx, d_q_offsets, d_kv_offsets);
     if (st) return st;
@@ -196,7 +198,18 @@ int32_t jfa_bwd(const jfa_problem* prob, const jfa_plan_info* info, const int32_
     a.scale = prob->softmax_scale;
     a.scale_log2 = prob->softmax_scale * 1.4426950408889634f;
     return hip_status(jfa::launch_bwd(a, prob->head_dim, mode_of(prob), prob->broadcast_q != 0,
-                                      stream));
+                                      stages, stream));
+}
+
+int32_t jfa_bwd(const jfa_problem* prob, const jfa_plan_info* info, const int32_t* d_worker_ptr,
+                const int32_t* d_tiles, const int32_t* d_sparse_ptr, const int32_t* d_sparse_idx,
+                const int32_t* d_q_offsets, const int32_t* d_kv_offsets, const void* q,
+                const void* k, const void* v, const void* o, const float* lse, const void* d_o,
+                void* dq, void* dk, void* dv, float* dq_accum, float* delta, void* workspace,
+                int64_t workspace_bytes, void* stream) {
+    return jfa_bwd_stages(JFA_BWD_ALL, prob, info, d_worker_ptr, d_tiles, d_sparse_ptr,
+                          d_sparse_idx, d_q_offsets, d_kv_offsets, q, k, v, o, lse, d_o, dq, dk,
+                          dv, dq_accum, delta, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

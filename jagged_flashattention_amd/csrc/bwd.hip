@@ -377,10 +377,10 @@ int32_t launch_main(const BwdArgs& a, hipStream_t s) {
 }
 
 template <int D>
-int32_t launch_d(const BwdArgs& a, Mode mode, bool bcast, hipStream_t s) {
+int32_t launch_d(const BwdArgs& a, Mode mode, bool bcast, int32_t stages, hipStream_t s) {
     const int64_t rows_h = (int64_t)a.total_q * a.num_heads;
     const int64_t accum_n = (int64_t)a.q_rows * a.num_heads * D;
-    {
+    if (stages & JFA_BWD_PREPROCESS) {
         const int64_t want = (rows_h * (D / 8) + 255) / 256;
         const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(want, 4096));
         hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(grid), dim3(256), 0, s, a.o, a.d_o, a.delta,
@@ -388,28 +388,31 @@ int32_t launch_d(const BwdArgs& a, Mode mode, bool bcast, hipStream_t s) {
         const int32_t e = (int32_t)hipGetLastError();
         if (e) return e;
     }
-    int32_t e = 0;
-    if (a.num_workers == 0) e = 0;
-    else if (mode == kCausal) e = launch_main<D, kCausal, false>(a, s);
-    else if (mode == kSparse)
-        e = bcast ? launch_main<D, kSparse, true>(a, s) : launch_main<D, kSparse, false>(a, s);
-    else
-        e = bcast ? launch_main<D, kDense, true>(a, s) : launch_main<D, kDense, false>(a, s);
-    if (e) return e;
-    {
+    if ((stages & JFA_BWD_MAIN) && a.num_workers > 0) {
+        int32_t e;
+        if (mode == kCausal) e = launch_main<D, kCausal, false>(a, s);
+        else if (mode == kSparse)
+            e = bcast ? launch_main<D, kSparse, true>(a, s) : launch_main<D, kSparse, false>(a, s);
+        else
+            e = bcast ? launch_main<D, kDense, true>(a, s) : launch_main<D, kDense, false>(a, s);
+        if (e) return e;
+    }
+    if (stages & JFA_BWD_FINISH) {
         const int64_t n8 = accum_n / 8;
         const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((n8 + 255) / 256, 4096));
         hipLaunchKernelGGL(dq_convert_kernel, dim3(grid), dim3(256), 0, s, a.dq_accum, a.dq, n8);
         return (int32_t)hipGetLastError();
     }
+    return 0;
 }
 
 }  // namespace
 
-int32_t launch_bwd(const BwdArgs& a, int32_t head_dim, Mode mode, bool broadcast, void* stream) {
+int32_t launch_bwd(const BwdArgs& a, int32_t head_dim, Mode mode, bool broadcast, int32_t stages,
+                   void* stream) {
     hipStream_t s = (hipStream_t)stream;
-    if (head_dim == 64) return launch_d<64>(a, mode, broadcast, s);
-    return launch_d<128>(a, mode, broadcast, s);
+    if (head_dim == 64) return launch_d<64>(a, mode, broadcast, stages, s);
+    return launch_d<128>(a, mode, broadcast, stages, s);
 }
 
 }  // namespace jfa

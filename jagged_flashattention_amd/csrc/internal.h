@@ -72,6 +72,7 @@ struct BwdArgs {
 
 // Launchers (return a hipError_t value as int32).
 int32_t launch_fwd(const FwdArgs& a, int32_t head_dim, Mode mode, bool broadcast, void* stream);
-int32_t launch_bwd(const BwdArgs& a, int32_t head_dim, Mode mode, bool broadcast, void* stream);
+int32_t launch_bwd(const BwdArgs& a, int32_t head_dim, Mode mode, bool broadcast, int32_t stages,
+                   void* stream);
 
 }  // namespace jfa
