@@ -150,6 +150,9 @@ def main():
     ap.add_argument("--bwd-workers-per-cu", type=int, default=1)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle CPU work for the baseline (0: skip)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run one device copy of this many MiB (a known-size kernel "
+                         "that scales the FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
@@ -196,6 +199,14 @@ def main():
         if ev is not None:
             ev[4].record()
 
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

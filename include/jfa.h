@@ -82,7 +82,7 @@ typedef struct jfa_problem {
                                per-sequence Q with the same lengths as KV      */
     int32_t mask_q_blocks;  /* block-sparse mask dims; both 0 = dense          */
     int32_t mask_kv_blocks;
-    float   softmax_scale;  /* finite; usually 1/sqrt(D)                       */
+    float   softmax_scale;  /* finite and > 0; usually 1/sqrt(D)               */
 } jfa_problem;
 
 /* Sizes of a plan, filled by jfa_plan_query / jfa_plan_build. */

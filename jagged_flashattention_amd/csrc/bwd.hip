@@ -24,7 +24,7 @@
 //   dS  = P * (dP - delta)
 //   dV^T += dO^T P       A = dO^T via transposed LDS reads, B = P
 //   dK^T += Q^T dS       A = Q^T via transposed LDS reads,  B = dS
-//   dQ   = dS K          A = dS via transposed reads of the staged dS^T,
+//   dQ   = dS K          A = scale*dS via transposed reads of the staged dS^T,
 //                        B = K via transposed reads of the K tile
 #include <type_traits>
 
@@ -37,36 +37,131 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kPad = 8;
 
+// LDS layout. Tiles whose rows are read as MFMA operands by 16 lanes at a
+// time are laid out so that those 16 rows hit distinct banks:
+//  - natural [row][D] tiles (Q, dO, and at tile start K, V; at tile end the
+//    dK/dV staging): 16-byte chunk c of row r is stored at chunk c ^ swz(r),
+//    swz(r) = (r + r/CH) mod CH, CH = D/8 chunks per row;
+//  - Q^T, dO^T: [d][64 rows] padded by 16 bytes per row;
+//  - K^T: [d][128 keys], 256-byte rows, chunk c of row d stored at
+//    c ^ ((d/8 ^ d) mod 16);
+//  - rows of Q^T/dO^T and keys of K^T are stored in the "sigma" order of each
+//    16-group (0-3, 8-11, 4-7, 12-15), so that the 8 values one lane feeds to
+//    a 32x32x16 MFMA (rows 16c + sigma(8h..8h+7)) are one 16-byte read and
+//    match the accumulator registers they are multiplied with.
+// Region R holds the Q-block tiles during the loop, the natural K tile during
+// the tile prologue, and the dK/dV staging in the tile epilogue. The natural
+// V tile stays in its own region for the whole tile (its rows are the B
+// operand of dP = dO V^T).
 template <int D>
-struct BwdSmem {
-    uint16_t k[kBwdBlockN][D + kPad];            // K tile, row-major
-    uint16_t q[2][kBwdBlockM][D + kPad];         // Q block, double-buffered
-    uint16_t dout[2][kBwdBlockM][D + kPad];      // dO block, double-buffered
-    uint16_t dst[kBwdBlockN][kBwdBlockM + kPad]; // dS^T of the tile (bf16)
-    float lse[2][kBwdBlockM];                    // LSE*log2(e); +inf = no row
-    float delta[2][kBwdBlockM];
+struct BwdLds {
+    static constexpr int KT = 0;                                   // K^T
+    static constexpr int KT_BYTES = D * kBwdBlockN * 2;
+    static constexpr int R = KT + KT_BYTES;
+    static constexpr int QN = R;                                    // [64][D]
+    static constexpr int DN = QN + kBwdBlockM * D * 2;              // [64][D]
+    static constexpr int QT = DN + kBwdBlockM * D * 2;              // [D][72]
+    static constexpr int DT = QT + D * (kBwdBlockM + 8) * 2;        // [D][72]
+    static constexpr int KN = R;                                    // [128][D]
+    static constexpr int DKS = R;                                   // [128][D] (epilogue)
+    static constexpr int DVS = R + kBwdBlockN * D * 2;              // [128][D] (epilogue)
+    static constexpr int R_BYTES = (DT + D * (kBwdBlockM + 8) * 2 - R) > 2 * kBwdBlockN * D * 2
+                                       ? (DT + D * (kBwdBlockM + 8) * 2 - R)
+                                       : 2 * kBwdBlockN * D * 2;
+    static constexpr int VN = R + R_BYTES;                          // [128][D]
+    static constexpr int DST = VN + kBwdBlockN * D * 2;             // [128][68]
+    static constexpr int LSE = DST + kBwdBlockN * (kBwdBlockM + 4) * 2;
+    static constexpr int DELTA = LSE + kBwdBlockM * 4;
+    static constexpr int BYTES = DELTA + kBwdBlockM * 4;
 };
+
+// position of row q (within its group of 16) in sigma order
+__device__ __forceinline__ int sigma_pos(int q) {
+    const int g = (q >> 2) & 3;
+    return (q & ~15) | (((g >> 1) | ((g & 1) << 1)) << 2) | (q & 3);
+}
+
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    constexpr int CH = D / 8;
+    constexpr int SH = (D == 128) ? 4 : 3;
+    return (r + (r >> SH)) & (CH - 1);
+}
+
+__device__ __forceinline__ int kt_swz(int d) { return ((d >> 3) ^ d) & 15; }
+
+// byte offset of element (row r, element c8*8 + e) of a natural [row][D] tile
+template <int D>
+__device__ __forceinline__ int nat_off(int r, int chunk) {
+    return r * D * 2 + ((chunk ^ swz<D>(r)) << 4);
+}
+__device__ __forceinline__ int kt_off(int d, int pos) {
+    return d * (kBwdBlockN * 2) + (((pos >> 3) ^ kt_swz(d)) << 4) + ((pos & 7) << 1);
+}
+
+// 4 rows x 8 bf16 (one 16-byte chunk per row) -> 8 columns x 4 rows
+__device__ __forceinline__ void transpose4x8(const u32x4 (&x)[4], u32x2 (&y)[8]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        y[2 * k][0] = (x[0][k] & 0xffffu) | (x[1][k] << 16);
+        y[2 * k][1] = (x[2][k] & 0xffffu) | (x[3][k] << 16);
+        y[2 * k + 1][0] = (x[0][k] >> 16) | (x[1][k] & 0xffff0000u);
+        y[2 * k + 1][1] = (x[2][k] >> 16) | (x[3][k] & 0xffff0000u);
+    }
+}
 
 template <int D, int MODE, bool BCAST>
 __global__ void __launch_bounds__(kThreads) bwd_kernel(BwdArgs a) {
-    __shared__ BwdSmem<D> sm;
+    using LY = BwdLds<D>;
+    __shared__ __attribute__((aligned(16))) char smem[LY::BYTES];
     constexpr int KC = D / 16;
     constexpr int MD = D / 32;
-    constexpr int CPR = D / 8;
-    constexpr int RPP = kThreads / CPR;       // rows per load pass
-    constexpr int NPQ = kBwdBlockM / RPP;     // passes for a 64-row block
-    constexpr int NPK = kBwdBlockN / RPP;     // passes for the 128-key tile
-    constexpr int QS = D + kPad;              // LDS row strides (elements)
-    constexpr int SS = kBwdBlockM + kPad;
+    constexpr int CH = D / 8;
+    constexpr int KPP = 4 * (kThreads / CH);       // keys per pass of the tile loader
+    constexpr int KPASS = kBwdBlockN / KPP;        // 2 (D=128) or 1 (D=64)
+    auto lds = [&](int byte_off) -> char* { return smem + byte_off; };
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int lr = lane & 31, hf = lane >> 5;
     const int H = a.num_heads;
     const int64_t rs = (int64_t)H * D;
     const int g16 = lane >> 4, n16 = lane & 15;
     const int tr_row = 4 * (g16 >> 1) + (n16 >> 2);
     const int tr_col = (g16 & 1) * 16 + 4 * (n16 & 3);
-    const int ld_row = tid / CPR, ld_col = (tid % CPR) * 8;
+    // Q/dO block loader: 4 rows (4qg..4qg+3) x one 16-byte chunk dc per thread
+    const int ld_qg = tid & 15, ld_dc = tid >> 4;
+    const bool ld_on = ld_dc < CH;
+    // K/V tile loader: chunk tdc of keys 4tkg..4tkg+3 (+KPP per pass); a load
+    // instruction covers whole 16*CH-byte rows
+    const int tdc = tid % CH, tkg = tid / CH;
+
+    // per-lane pieces of the swizzled addresses of natural rows 32mb + lr
+    int nat_base[2], nat_x[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        const int row = 32 * mb + lr;
+        const int sw = swz<D>(row);
+        nat_base[mb] = row * D * 2 + 16 * (hf ^ (sw & 1));
+        nat_x[mb] = sw >> 1;
+    }
+    // natural K/V tile rows of this lane's key (row 32*wave + lr)
+    int kv_base, kv_x;
+    {
+        const int row = 32 * wave + lr;
+        const int sw = swz<D>(row);
+        kv_base = row * D * 2 + 16 * (hf ^ (sw & 1));
+        kv_x = sw >> 1;
+    }
+    // K^T rows read as the dQ B operand by this lane (d = 32nd + lr)
+    int kt_base[2], kt_x[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int d = 32 * (2 * (wave & 1) + j) + lr;
+        const int sw = kt_swz(d);
+        kt_base[j] = LY::KT + d * (kBwdBlockN * 2) + 16 * (hf ^ (sw & 1));
+        kt_x[j] = sw >> 1;
+    }
 
     const int w = worker_id(a.num_workers);
     const int t_begin = a.worker_ptr[w], t_end = a.worker_ptr[w + 1];
@@ -96,160 +191,189 @@ __global__ void __launch_bounds__(kThreads) bwd_kernel(BwdArgs a) {
             return r0 + i;
         };
         const int nmasked = (MODE == kCausal) ? min(2, work) : 0;
-
-        // K tile into LDS; this wave's K and V rows into registers
         const int key = n * kBwdBlockN + wave * 32 + lr;   // local key of this lane
+        const int64_t kvrow0 = (int64_t)kv0 * rs + (int64_t)hd * D;
+
+        // Q / dO / LSE / delta of a block: global -> registers (raw values only:
+        // any arithmetic on a loaded value here would make the wave wait for
+        // the whole prefetch right away) -> LDS at the end of the iteration
+        u32x4 qv[4], dv[4];
+        float rowv = 0.f;
+        int ld_r = 0;   // Q block of the registers, for the zero fill at store time
+        auto gload = [&](int r) {
+            // unconditional loads from a row clamped into the sequence (Lq >= 1
+            // whenever a block exists); rows past the end are zeroed in sstore
+            ld_r = r;
 #pragma unroll
-        for (int p = 0; p < NPK; ++p) {
-            const int kk = n * kBwdBlockN + ld_row + p * RPP;
-            u32x4 x = u32x4{};
-            if (kk < L) x = *(const u32x4*)(a.k + (int64_t)(kv0 + kk) * rs + (int64_t)hd * D + ld_col);
-            *(u32x4*)&sm.k[ld_row + p * RPP][ld_col] = x;
-        }
-        bf16x8 kf[KC], vf[KC];
-        if (key < L) {
-            const int64_t off = (int64_t)(kv0 + key) * rs + (int64_t)hd * D + 8 * hf;
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                kf[kc] = load_bf16x8(a.k + off + 16 * kc);
-                vf[kc] = load_bf16x8(a.v + off + 16 * kc);
+            for (int p = 0; p < 4; ++p) {
+                const int qi = min(r * kBwdBlockM + 4 * ld_qg + p, Lq - 1);
+                qv[p] = *(const u32x4*)(a.q + (int64_t)(q0 + qi) * rs + (int64_t)hd * D + 8 * (ld_dc & (CH - 1)));
+                dv[p] = *(const u32x4*)(a.d_o + (int64_t)(orow0 + qi) * rs + (int64_t)hd * D + 8 * (ld_dc & (CH - 1)));
             }
-        } else {
+            {
+                // wave 0 loads LSE, wave 1 delta (a wave-uniform choice keeps the
+                // base pointers scalar)
+                const int qi = min(r * kBwdBlockM + lane, Lq - 1);
+                const int64_t idx = (int64_t)hd * a.total_q + orow0 + qi;
+                if (wave == 0) rowv = a.lse[idx];
+                else if (wave == 1) rowv = a.delta[idx];
+            }
+        };
+        auto sstore = [&]() {
+            if (ld_on) {
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                kf[kc] = bf16x8{};
-                vf[kc] = bf16x8{};
+                for (int p = 0; p < 4; ++p) {
+                    if (ld_r * kBwdBlockM + 4 * ld_qg + p >= Lq) {
+                        qv[p] = u32x4{};
+                        dv[p] = u32x4{};
+                    }
+                }
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const int o = nat_off<D>(4 * ld_qg + p, ld_dc);
+                    *(u32x4*)lds(LY::QN + o) = qv[p];
+                    *(u32x4*)lds(LY::DN + o) = dv[p];
+                }
+                u32x2 y[8];
+                const int pos2 = 2 * sigma_pos(4 * ld_qg);
+                transpose4x8(qv, y);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    *(u32x2*)lds(LY::QT + (8 * ld_dc + e) * (kBwdBlockM + 8) * 2 + pos2) = y[e];
+                transpose4x8(dv, y);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    *(u32x2*)lds(LY::DT + (8 * ld_dc + e) * (kBwdBlockM + 8) * 2 + pos2) = y[e];
+            }
+            // LSE in the exp2 domain; a row without keys (LSE = -inf) or outside
+            // the sequence gets +inf so that its P is 0
+            const bool in_seq = ld_r * kBwdBlockM + lane < Lq;
+            if (wave == 0)
+                ((float*)lds(LY::LSE))[lane] = (!in_seq || rowv == -INFINITY) ? INFINITY : rowv * kLog2e;
+            else if (wave == 1)
+                ((float*)lds(LY::DELTA))[lane] = in_seq ? rowv : 0.f;
+        };
+
+        // ---- tile prologue: the K and V tiles are loaded as whole rows, stored
+        // to LDS (natural K and V, and K^T), then each wave reads its K/V
+        // fragments; block 0 is loaded meanwhile
+        {
+            u32x4 kx[KPASS][4], vx[KPASS][4];
+#pragma unroll
+            for (int pass = 0; pass < KPASS; ++pass)
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const int kk = min(n * kBwdBlockN + KPP * pass + 4 * tkg + p, L - 1);
+                    kx[pass][p] = *(const u32x4*)(a.k + kvrow0 + (int64_t)kk * rs + 8 * tdc);
+                    vx[pass][p] = *(const u32x4*)(a.v + kvrow0 + (int64_t)kk * rs + 8 * tdc);
+                }
+#pragma unroll
+            for (int pass = 0; pass < KPASS; ++pass) {
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const int kl = KPP * pass + 4 * tkg + p;   // key within the tile
+                    if (n * kBwdBlockN + kl >= L) {
+                        kx[pass][p] = u32x4{};
+                        vx[pass][p] = u32x4{};
+                    }
+                    const int o = nat_off<D>(kl, tdc);
+                    *(u32x4*)lds(LY::KN + o) = kx[pass][p];
+                    *(u32x4*)lds(LY::VN + o) = vx[pass][p];
+                }
+                u32x2 y[8];
+                transpose4x8(kx[pass], y);
+                const int pos = sigma_pos(KPP * pass + 4 * tkg);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) *(u32x2*)lds(LY::KT + kt_off(8 * tdc + e, pos)) = y[e];
             }
         }
+        __syncthreads();
+        if (work > 0) gload(qblk(0));
+        // this wave's K rows as MFMA B operands (keys on lanes); its V rows are
+        // read from LDS where they are used
+        bf16x8 kf[KC];
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+            kf[kc] = __builtin_bit_cast(bf16x8, *(const u32x4*)lds(LY::KN + kv_base + 32 * (kc ^ kv_x)));
         f32x16 dk_acc[MD], dv_acc[MD];
 #pragma unroll
         for (int md = 0; md < MD; ++md) {
             dk_acc[md] = f32x16{};
             dv_acc[md] = f32x16{};
         }
-
-        // Q / dO / LSE / delta block loader (registers, then LDS)
-        u32x4 qr[NPQ], dr[NPQ];
-        float rowv = 0.f;
-        auto gload = [&](int r) {
-#pragma unroll
-            for (int p = 0; p < NPQ; ++p) {
-                const int qi = r * kBwdBlockM + ld_row + p * RPP;
-                if (qi < Lq) {
-                    qr[p] = *(const u32x4*)(a.q + (int64_t)(q0 + qi) * rs + (int64_t)hd * D + ld_col);
-                    dr[p] = *(const u32x4*)(a.d_o + (int64_t)(orow0 + qi) * rs + (int64_t)hd * D + ld_col);
-                } else {
-                    qr[p] = u32x4{};
-                    dr[p] = u32x4{};
-                }
-            }
-            if (tid < 2 * kBwdBlockM) {
-                const int qi = r * kBwdBlockM + (tid & (kBwdBlockM - 1));
-                const bool is_lse = tid < kBwdBlockM;
-                if (qi < Lq) {
-                    const int64_t idx = (int64_t)hd * a.total_q + orow0 + qi;
-                    if (is_lse) {
-                        const float l = a.lse[idx];
-                        rowv = (l == -INFINITY) ? INFINITY : l * kLog2e;
-                    } else {
-                        rowv = a.delta[idx];
-                    }
-                } else {
-                    rowv = is_lse ? INFINITY : 0.f;
-                }
-            }
-        };
-        auto sstore = [&](int buf) {
-#pragma unroll
-            for (int p = 0; p < NPQ; ++p) {
-                *(u32x4*)&sm.q[buf][ld_row + p * RPP][ld_col] = qr[p];
-                *(u32x4*)&sm.dout[buf][ld_row + p * RPP][ld_col] = dr[p];
-            }
-            if (tid < kBwdBlockM) sm.lse[buf][tid] = rowv;
-            else if (tid < 2 * kBwdBlockM) sm.delta[buf][tid - kBwdBlockM] = rowv;
-        };
-
-        if (work > 0) {
-            gload(qblk(0));
-            sstore(0);
-        }
+        __syncthreads();   // region R changes from K/V to the Q-block tiles
+        if (work > 0) sstore();
+        // block 0 landed; nothing left in flight (see wait_vmem)
+        wait_vmem();
         __syncthreads();
 
         auto body = [&](int i, auto masked_tag) {
             constexpr bool MASKED = decltype(masked_tag)::value;
-            const int buf = i & 1;
             const int r = qblk(i);
             if (i + 1 < work) gload(qblk(i + 1));
 
-            f32x16 s[2], dp[2];
+            // the block in two halves of 32 query rows (mb), to keep the live
+            // register set small
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
-                s[mb] = f32x16{};
-                dp[mb] = f32x16{};
+                f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
                 for (int kc = 0; kc < KC; ++kc) {
-                    const bf16x8 qa = load_bf16x8(&sm.q[buf][32 * mb + lr][16 * kc + 8 * hf]);
-                    s[mb] = mfma32(qa, kf[kc], s[mb]);
+                    const int off = nat_base[mb] + 32 * (kc ^ nat_x[mb]);
+                    const bf16x8 qa = __builtin_bit_cast(bf16x8, *(const u32x4*)lds(LY::QN + off));
+                    s = mfma32(qa, kf[kc], s);
+                    const bf16x8 da = __builtin_bit_cast(bf16x8, *(const u32x4*)lds(LY::DN + off));
+                    const bf16x8 vb =
+                        __builtin_bit_cast(bf16x8, *(const u32x4*)lds(LY::VN + kv_base + 32 * (kc ^ kv_x)));
+                    dp = mfma32(da, vb, dp);
                 }
-#pragma unroll
-                for (int kc = 0; kc < KC; ++kc) {
-                    const bf16x8 da = load_bf16x8(&sm.dout[buf][32 * mb + lr][16 * kc + 8 * hf]);
-                    dp[mb] = mfma32(da, vf[kc], dp[mb]);
-                }
-            }
-            // P and dS; register r of block mb is query row 32mb + 8(r/4) + 4hf + r%4
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+                // P and dS; register r is query row 32mb + 8(r/4) + 4hf + r%4
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int row = 32 * mb + 8 * g + 4 * hf;
-                    const f32x4 l4 = *(const f32x4*)&sm.lse[buf][row];
-                    const f32x4 d4 = *(const f32x4*)&sm.delta[buf][row];
+                    const f32x4 l4 = *(const f32x4*)lds(LY::LSE + 4 * row);
+                    const f32x4 d4 = *(const f32x4*)lds(LY::DELTA + 4 * row);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        float p = __builtin_amdgcn_exp2f(s[mb][4 * g + j] * a.scale_log2 - l4[j]);
+                        float p = __builtin_amdgcn_exp2f(s[4 * g + j] * a.scale_log2 - l4[j]);
                         if (MASKED) {
                             if (key > r * kBwdBlockM + row + j) p = 0.f;
                         }
-                        s[mb][4 * g + j] = p;
-                        dp[mb][4 * g + j] = p * (dp[mb][4 * g + j] - d4[j]);
+                        s[4 * g + j] = p;
+                        dp[4 * g + j] = p * (dp[4 * g + j] - d4[j]);
                     }
                 }
-            bf16x8 pb[4], sb[4];
+                // dV^T += dO^T P ; dK^T += Q^T dS over this half's 32 query rows
+                // (16-row chunks c = 2mb, 2mb + 1)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                f32x8 x, y;
+                for (int cc = 0; cc < 2; ++cc) {
+                    const int c = 2 * mb + cc;
+                    f32x8 x, y;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    x[j] = s[c >> 1][8 * (c & 1) + j];
-                    y[j] = dp[c >> 1][8 * (c & 1) + j];
+                    for (int j = 0; j < 8; ++j) {
+                        x[j] = s[8 * cc + j];
+                        y[j] = dp[8 * cc + j];
+                    }
+                    const bf16x8 pb = to_bf16x8(x), sb = to_bf16x8(y);
+#pragma unroll
+                    for (int md = 0; md < MD; ++md) {
+                        const int o = (32 * md + lr) * (kBwdBlockM + 8) * 2 + (16 * c + 8 * hf) * 2;
+                        const bf16x8 da = __builtin_bit_cast(bf16x8, *(const u32x4*)lds(LY::DT + o));
+                        dv_acc[md] = mfma32(da, pb, dv_acc[md]);
+                        const bf16x8 qa = __builtin_bit_cast(bf16x8, *(const u32x4*)lds(LY::QT + o));
+                        dk_acc[md] = mfma32(qa, sb, dk_acc[md]);
+                    }
                 }
-                pb[c] = to_bf16x8(x);
-                sb[c] = to_bf16x8(y);
-            }
-            // dV^T += dO^T P ; dK^T += Q^T dS   (reduction over the 64 query rows)
-#pragma unroll
-            for (int md = 0; md < MD; ++md)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const uint16_t* dp_ = &sm.dout[buf][16 * c + tr_row][32 * md + tr_col];
-                    const bf16x8 da = concat(lds_read_tr(dp_), lds_read_tr(dp_ + 8 * QS));
-                    dv_acc[md] = mfma32(da, pb[c], dv_acc[md]);
-                    const uint16_t* qp_ = &sm.q[buf][16 * c + tr_row][32 * md + tr_col];
-                    const bf16x8 qa = concat(lds_read_tr(qp_), lds_read_tr(qp_ + 8 * QS));
-                    dk_acc[md] = mfma32(qa, sb[c], dk_acc[md]);
-                }
-            // stage dS^T[key][row] of the whole tile
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+                // stage scale * dS^T[key][row] of the whole tile (the dQ operand)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     f32x4 x;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) x[j] = dp[mb][4 * g + j];
-                    *(u32x2*)&sm.dst[wave * 32 + lr][32 * mb + 8 * g + 4 * hf] =
-                        __builtin_bit_cast(u32x2, to_bf16x4(x));
+                    for (int j = 0; j < 4; ++j) x[j] = dp[4 * g + j] * a.scale;
+                    *(u32x2*)lds(LY::DST + (wave * 32 + lr) * (kBwdBlockM + 4) * 2 +
+                                 (32 * mb + 8 * g + 4 * hf) * 2) = __builtin_bit_cast(u32x2, to_bf16x4(x));
                 }
+            }
             __syncthreads();
             // dQ[row, d] = sum over the tile's 128 keys of dS[row, key] K[key, d]:
             // this wave computes rows 32*(wave/2).. and d blocks 2*(wave%2), +1
@@ -258,35 +382,38 @@ __global__ void __launch_bounds__(kThreads) bwd_kernel(BwdArgs a) {
                 f32x16 dq[2] = {f32x16{}, f32x16{}};
 #pragma unroll
                 for (int c = 0; c < kBwdBlockN / 16; ++c) {
-                    const uint16_t* sp_ = &sm.dst[16 * c + tr_row][32 * mq + tr_col];
-                    const bf16x8 sa = concat(lds_read_tr(sp_), lds_read_tr(sp_ + 8 * SS));
+                    const uint16_t* sp_ = (const uint16_t*)lds(LY::DST + (16 * c + tr_row) * (kBwdBlockM + 4) * 2 +
+                                                               (32 * mq + tr_col) * 2);
+                    const bf16x8 sa = concat(lds_read_tr(sp_), lds_read_tr(sp_ + 8 * (kBwdBlockM + 4)));
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
                         const int nd = 2 * (wave & 1) + j;
                         if (nd < MD) {
-                            const uint16_t* kp_ = &sm.k[16 * c + tr_row][32 * nd + tr_col];
-                            const bf16x8 kb = concat(lds_read_tr(kp_), lds_read_tr(kp_ + 8 * QS));
+                            const bf16x8 kb = __builtin_bit_cast(
+                                bf16x8, *(const u32x4*)lds(kt_base[j] + 32 * (c ^ kt_x[j])));
                             dq[j] = mfma32(sa, kb, dq[j]);
                         }
                     }
                 }
                 // register rr is query row 32mq + 8(rr/4) + 4hf + rr%4, column d = 32nd + lr
+                const int row0 = r * kBwdBlockM + 32 * mq;
+                const bool full = row0 + 32 <= Lq;   // wave-uniform
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const int nd = 2 * (wave & 1) + j;
                     if (nd < MD) {
+                        float* dqp = a.dq_accum + (int64_t)(q0 + row0 + 4 * hf) * rs + (int64_t)hd * D +
+                                     32 * nd + lr;
 #pragma unroll
                         for (int rr = 0; rr < 16; ++rr) {
-                            const int qi = r * kBwdBlockM + 32 * mq + 8 * (rr >> 2) + 4 * hf + (rr & 3);
-                            if (qi < Lq)
-                                unsafeAtomicAdd(a.dq_accum + (int64_t)(q0 + qi) * rs + (int64_t)hd * D +
-                                                    32 * nd + lr,
-                                                dq[j][rr] * a.scale);
+                            const int qi = row0 + 8 * (rr >> 2) + 4 * hf + (rr & 3);
+                            if (full || qi < Lq)
+                                unsafeAtomicAdd(dqp + (int64_t)(8 * (rr >> 2) + (rr & 3)) * rs, dq[j][rr]);
                         }
                     }
                 }
             }
-            if (i + 1 < work) sstore(buf ^ 1);
+            if (i + 1 < work) sstore();
             __syncthreads();
         };
 
@@ -294,9 +421,10 @@ __global__ void __launch_bounds__(kThreads) bwd_kernel(BwdArgs a) {
         for (; i < nmasked; ++i) body(i, std::true_type{});
         for (; i < work; ++i) body(i, std::false_type{});
 
-        // dK = scale * (dK^T)^T, dV: lane = key, register = d
-        if (key < L) {
-            const int64_t base = (int64_t)(kv0 + key) * rs + (int64_t)hd * D + 4 * hf;
+        // ---- tile epilogue: stage dK = scale * (dK^T)^T and dV (bf16) in region
+        // R as natural rows, then write whole rows to global memory
+        {
+            const int row = wave * 32 + lr;
 #pragma unroll
             for (int md = 0; md < MD; ++md)
 #pragma unroll
@@ -307,11 +435,27 @@ __global__ void __launch_bounds__(kThreads) bwd_kernel(BwdArgs a) {
                         x[j] = dk_acc[md][4 * g + j] * a.scale;
                         y[j] = dv_acc[md][4 * g + j];
                     }
-                    *(u32x2*)(a.dk + base + 32 * md + 8 * g) = __builtin_bit_cast(u32x2, to_bf16x4(x));
-                    *(u32x2*)(a.dv + base + 32 * md + 8 * g) = __builtin_bit_cast(u32x2, to_bf16x4(y));
+                    const int o = nat_off<D>(row, 4 * md + g) + 8 * hf;
+                    *(u32x2*)lds(LY::DKS + o) = __builtin_bit_cast(u32x2, to_bf16x4(x));
+                    *(u32x2*)lds(LY::DVS + o) = __builtin_bit_cast(u32x2, to_bf16x4(y));
                 }
         }
-        // the K tile in LDS is rewritten by the next tile
+        __syncthreads();
+#pragma unroll
+        for (int pass = 0; pass < KPASS; ++pass)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int kl = KPP * pass + 4 * tkg + p;
+                const int o = nat_off<D>(kl, tdc);
+                const u32x4 xk = *(const u32x4*)lds(LY::DKS + o);
+                const u32x4 xv = *(const u32x4*)lds(LY::DVS + o);
+                if (n * kBwdBlockN + kl < L) {
+                    const int64_t g = kvrow0 + (int64_t)(n * kBwdBlockN + kl) * rs + 8 * tdc;
+                    *(u32x4*)(a.dk + g) = xk;
+                    *(u32x4*)(a.dv + g) = xv;
+                }
+            }
+        // LDS is rewritten by the next tile
         __syncthreads();
     }
 }

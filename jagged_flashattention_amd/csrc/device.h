@@ -59,6 +59,13 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
     return __builtin_bit_cast(bf16x8, *(const u32x4*)p);
 }
 
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima): wait for all
+// vector memory operations of this wave. Placed before a loop whose body
+// issues prefetch loads, it keeps the compiler from conservatively waiting on
+// those prefetches inside the loop (its per-register wait tracking is merged
+// over the back edge).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Persistent worker of this workgroup. Workgroup ids are dealt round-robin to
 // the 8 XCDs; mapping consecutive workers to the same XCD puts tiles dealt
 // next to each other (e.g. the Q tiles of one sequence and head, which read

@@ -14,9 +14,11 @@
 //     held in VGPRs as the B operand of S^T = K Q^T (32x32x16 bf16 MFMA) so a
 //     lane owns one query row: row max / row sum stay in-lane and need one
 //     cross-half exchange;
-//   - K and V of a 64-key block double-buffered in LDS from coalesced 16-byte
-//     global loads issued one block ahead; V stays row-major and is fed to
-//     O^T += V^T P^T through ds_read_tr16_b64 transposed reads;
+//   - K and V of a 64-key block double-buffered in LDS from 16-byte global
+//     loads issued one block ahead; K rows are stored with a chunk swizzle and
+//     V is transposed on its way into LDS (keys in the order the P^T
+//     accumulator registers hold them), so every MFMA operand is one
+//     conflict-free 16-byte LDS read;
 //   - fp32 running max and sum in the exp2 domain, rescaling of the O
 //     accumulator skipped when no row max moved;
 //   - a bulk loop without any mask arithmetic and a tail loop (last partial
@@ -30,34 +32,61 @@ namespace jfa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPad = 8;  // bf16 elements of padding per LDS row
 
 template <int D>
 struct FwdSmem {
-    uint16_t k[2][kFwdBlockN][D + kPad];
-    uint16_t v[2][kFwdBlockN][D + kPad];
+    uint16_t k[2][kFwdBlockN][D];            // K rows, 16-byte chunks swizzled
+    uint16_t vt[2][D][kFwdBlockN + 8];       // V^T, keys in sigma order
 };
+
+// position of key q (within its group of 16) in sigma order 0-3, 8-11, 4-7, 12-15
+__device__ __forceinline__ int sigma_pos(int q) {
+    const int g = (q >> 2) & 3;
+    return (q & ~15) | (((g >> 1) | ((g & 1) << 1)) << 2) | (q & 3);
+}
+
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    constexpr int CH = D / 8;
+    constexpr int SH = (D == 128) ? 4 : 3;
+    return (r + (r >> SH)) & (CH - 1);
+}
+
+__device__ __forceinline__ void transpose4x8(const u32x4 (&x)[4], u32x2 (&y)[8]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        y[2 * k][0] = (x[0][k] & 0xffffu) | (x[1][k] << 16);
+        y[2 * k][1] = (x[2][k] & 0xffffu) | (x[3][k] << 16);
+        y[2 * k + 1][0] = (x[0][k] >> 16) | (x[1][k] & 0xffff0000u);
+        y[2 * k + 1][1] = (x[2][k] >> 16) | (x[3][k] & 0xffff0000u);
+    }
+}
 
 template <int D, int MODE, bool BCAST>
 __global__ void __launch_bounds__(kThreads, 2) fwd_kernel(FwdArgs a) {
     __shared__ FwdSmem<D> sm;
     constexpr int KC = D / 16;              // 16-wide d chunks of S^T = K Q^T
     constexpr int MD = D / 32;              // 32-row d blocks of O^T
-    constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
-    constexpr int RPP = kThreads / CPR;     // rows per load pass
-    constexpr int NP = kFwdBlockN / RPP;    // load passes per block
-    constexpr int VSTRIDE = D + kPad;
+    constexpr int CH = D / 8;               // 16-byte chunks per K/V row
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int lr = lane & 31, hf = lane >> 5;
     const int H = a.num_heads;
     const int64_t rs = (int64_t)H * D;
-
-    // lane constants of the transposed V read (see lds_read_tr)
-    const int g16 = lane >> 4, n16 = lane & 15;
-    const int tr_row = 4 * (g16 >> 1) + (n16 >> 2);
-    const int tr_col = (g16 & 1) * 16 + 4 * (n16 & 3);
-    const int ld_row = tid / CPR, ld_col = (tid % CPR) * 8;
+    // loader: keys 4kg..4kg+3 x one 16-byte chunk dc per thread
+    const int ld_kg = tid & 15, ld_dc = tid >> 4;
+    const bool ld_on = ld_dc < CH;
+    const int ld_pos = sigma_pos(4 * ld_kg);
+    // swizzled K-row addresses of this lane (rows 32mb + lr)
+    int nat_base[2], nat_x[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        const int row = 32 * mb + lr;
+        const int s = swz<D>(row);
+        nat_base[mb] = row * D + 8 * (hf ^ (s & 1));
+        nat_x[mb] = s >> 1;
+    }
 
     const int w = worker_id(a.num_workers);
     const int t_begin = a.worker_ptr[w], t_end = a.worker_ptr[w + 1];
@@ -112,26 +141,40 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_kernel(FwdArgs a) {
         for (int md = 0; md < MD; ++md) oacc[md] = f32x16{};
         float m_run = -1e30f, l_run = 0.f;
 
-        u32x4 kr[NP], vr[NP];
+        // (threads past the row width load a valid chunk and never store it)
+        const uint16_t* kbase = a.k + (int64_t)kv0 * rs + (int64_t)hd * D + 8 * (ld_dc & (CH - 1));
+        const uint16_t* vbase = a.v + (int64_t)kv0 * rs + (int64_t)hd * D + 8 * (ld_dc & (CH - 1));
+        u32x4 kr[4], vr[4];
+        int ld_n = 0;   // KV block held in the registers, for the zero fill at store time
         auto gload = [&](int n) {
+            // unconditional loads from a key clamped into the sequence (L >= 1
+            // whenever a block exists); keys past the end are zeroed in sstore
+            ld_n = n;
 #pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                const int key = kFwdBlockN * n + ld_row + p * RPP;
-                if (key < L) {
-                    const int64_t off = (int64_t)(kv0 + key) * rs + (int64_t)hd * D + ld_col;
-                    kr[p] = *(const u32x4*)(a.k + off);
-                    vr[p] = *(const u32x4*)(a.v + off);
-                } else {
-                    kr[p] = u32x4{};
-                    vr[p] = u32x4{};
-                }
+            for (int p = 0; p < 4; ++p) {
+                const int key = min(kFwdBlockN * n + 4 * ld_kg + p, L - 1);
+                kr[p] = *(const u32x4*)(kbase + (int64_t)key * rs);
+                vr[p] = *(const u32x4*)(vbase + (int64_t)key * rs);
             }
         };
         auto sstore = [&](int buf) {
+            if (ld_on) {
 #pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                *(u32x4*)&sm.k[buf][ld_row + p * RPP][ld_col] = kr[p];
-                *(u32x4*)&sm.v[buf][ld_row + p * RPP][ld_col] = vr[p];
+                for (int p = 0; p < 4; ++p) {
+                    if (kFwdBlockN * ld_n + 4 * ld_kg + p >= L) {
+                        kr[p] = u32x4{};
+                        vr[p] = u32x4{};
+                    }
+                }
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const int row = 4 * ld_kg + p;
+                    *(u32x4*)&sm.k[buf][row][8 * (ld_dc ^ swz<D>(row))] = kr[p];
+                }
+                u32x2 y[8];
+                transpose4x8(vr, y);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) *(u32x2*)&sm.vt[buf][8 * ld_dc + e][ld_pos] = y[e];
             }
         };
 
@@ -139,6 +182,10 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_kernel(FwdArgs a) {
             gload(blk(0));
             sstore(0);
         }
+        // Nothing may be left in flight here: otherwise the compiler's wait
+        // counters, merged over the loop back edge, make the first MFMAs of
+        // every iteration wait for that iteration's prefetch loads.
+        wait_vmem();
         __syncthreads();
 
         auto body = [&](int i, auto masked_tag) {
@@ -154,7 +201,8 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_kernel(FwdArgs a) {
                 s[mb] = f32x16{};
 #pragma unroll
                 for (int kc = 0; kc < KC; ++kc) {
-                    const bf16x8 kf = load_bf16x8(&sm.k[buf][32 * mb + lr][16 * kc + 8 * hf]);
+                    const bf16x8 kf =
+                        load_bf16x8(&sm.k[buf][0][0] + nat_base[mb] + 16 * (kc ^ nat_x[mb]));
                     s[mb] = mfma32(kf, qf[kc], s[mb]);
                 }
             }
@@ -163,7 +211,7 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_kernel(FwdArgs a) {
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float x = s[mb][r] * a.scale_log2;
+                    float x = s[mb][r];
                     if (MASKED) {
                         const int kk = kFwdBlockN * n + 32 * mb + 8 * (r >> 2) + 4 * hf + (r & 3);
                         bool ok = kk < L;
@@ -173,7 +221,8 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_kernel(FwdArgs a) {
                     s[mb][r] = x;
                     mx = fmaxf(mx, x);
                 }
-            mx = pair_max(mx);
+            // running max in the exp2 domain of the scaled scores
+            mx = pair_max(mx) * a.scale_log2;
             const float m_new = fmaxf(m_run, mx);
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             float ls = 0.f;
@@ -181,7 +230,7 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_kernel(FwdArgs a) {
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(s[mb][r] - m_new);
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][r], a.scale_log2, -m_new));
                     s[mb][r] = p;
                     ls += p;
                 }
@@ -205,8 +254,7 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_kernel(FwdArgs a) {
             for (int md = 0; md < MD; ++md)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    const uint16_t* vp = &sm.v[buf][16 * c + tr_row][32 * md + tr_col];
-                    const bf16x8 vf = concat(lds_read_tr(vp), lds_read_tr(vp + 8 * VSTRIDE));
+                    const bf16x8 vf = load_bf16x8(&sm.vt[buf][32 * md + lr][16 * c + 8 * hf]);
                     oacc[md] = mfma32(vf, pb[c], oacc[md]);
                 }
             if (i + 1 < work) sstore(buf ^ 1);

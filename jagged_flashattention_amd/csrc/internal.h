@@ -3,7 +3,7 @@
 
 #include <stdint.h>
 
-#include "../../include/jfa.h"
+#include "jfa.h"
 
 namespace jfa {
 

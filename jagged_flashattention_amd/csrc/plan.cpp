@@ -35,9 +35,8 @@ int32_t check_problem(const jfa_problem* p) {
     if (p->broadcast_q != 0 && p->broadcast_q != 1) return JFA_ERR_INVALID_ARG;
     if (p->causal != 0 && p->causal != 1) return JFA_ERR_INVALID_ARG;
     if (p->head_dim != 64 && p->head_dim != 128) return JFA_ERR_UNSUPPORTED;
-    if (!(p->softmax_scale == p->softmax_scale) || p->softmax_scale > 3.0e38f ||
-        p->softmax_scale < -3.0e38f)
-        return JFA_ERR_INVALID_ARG;
+    // finite and positive (the kernels take the row max before scaling)
+    if (!(p->softmax_scale > 0.0f) || p->softmax_scale > 3.0e38f) return JFA_ERR_INVALID_ARG;
     if (p->causal && p->broadcast_q) return JFA_ERR_UNSUPPORTED;
     const bool sparse = p->mask_q_blocks != 0 || p->mask_kv_blocks != 0;
     if (sparse && (p->mask_q_blocks < 1 || p->mask_kv_blocks < 1)) return JFA_ERR_BAD_MASK;

@@ -71,6 +71,9 @@ def _prob(**kw):
     (dict(broadcast_q=False, causal=True, mask_q_blocks=1, mask_kv_blocks=1), [0, 3, 5],
      [0, 3, 5], np.ones((2, 1, 1), np.uint8), J.JFA_ERR_UNSUPPORTED),
     (dict(softmax_scale=float("nan")), None, [0, 3, 5], None, J.JFA_ERR_INVALID_ARG),
+    (dict(softmax_scale=-0.5), None, [0, 3, 5], None, J.JFA_ERR_INVALID_ARG),
+    (dict(softmax_scale=0.0), None, [0, 3, 5], None, J.JFA_ERR_INVALID_ARG),
+    (dict(softmax_scale=float("inf")), None, [0, 3, 5], None, J.JFA_ERR_INVALID_ARG),
 ])
 def test_planner_rejects_bad_problems(kw, qoff, kvoff, mask, status):
     with pytest.raises(J.JfaError) as e:
