@@ -146,7 +146,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2, help="1..5 (2: GEM-shaped broadcast-Q)")
-    ap.add_argument("--fwd-workers-per-cu", type=int, default=2)
+    ap.add_argument("--fwd-workers-per-cu", type=int, default=1)
     ap.add_argument("--bwd-workers-per-cu", type=int, default=1)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle CPU work for the baseline (0: skip)")

@@ -70,6 +70,7 @@ extern "C" {
 /* planner passes */
 #define JFA_PASS_FWD 0
 #define JFA_PASS_BWD 1
+#define JFA_PASS_DQ 2   /* Q-stationary dQ pass of the backward */
 
 /* Problem description shared by the planner, jfa_fwd and jfa_bwd. */
 typedef struct jfa_problem {
@@ -87,8 +88,9 @@ typedef struct jfa_problem {
 
 /* Sizes of a plan, filled by jfa_plan_query / jfa_plan_build. */
 typedef struct jfa_plan_info {
-    int32_t pass;           /* JFA_PASS_FWD or JFA_PASS_BWD                    */
-    int32_t num_workers;    /* W persistent workgroups the plan is dealt to    */
+    int32_t pass;           /* JFA_PASS_FWD, JFA_PASS_BWD or JFA_PASS_DQ       */
+    int32_t num_workers;    /* W persistent workgroups the plan is dealt to
+                               (DQ with broadcast Q: max(requested, G))       */
     int32_t num_tiles;      /* N tiles                                         */
     int32_t block_m;        /* rows of a Q tile (fwd) / Q block (bwd)          */
     int32_t block_n;        /* keys of a KV block (fwd) / KV tile (bwd)        */
@@ -122,15 +124,21 @@ int32_t jfa_offsets_from_lengths(const int32_t* h_lengths, int32_t batch, int32_
  * sorted on the host by KV workload, largest first, dealt to the processors
  * in a zigzag pattern; software load balancing across length skew).
  *
- * Tiles are enumerated in (b, h, t) order. FWD: t is a Q tile of block_m=128
+ * Tiles are enumerated in (b, h, t) order. FWD: t is a Q tile of block_m=256
  * rows, work = KV blocks of block_n=64 keys visited (dense: ceil(Lk/64);
- * causal: ceil(min(128(t+1), L)/64); block-sparse: the 64-key blocks of the
- * kept 128-key mask blocks inside the sequence). BWD: t is a KV tile of
- * block_n=128 keys, work = Q blocks of block_m=64 rows visited (dense:
- * ceil(Lq/64); causal: ceil(L/64) - 2t; block-sparse: the 64-row blocks of the
- * kept 128-row mask tiles). Tiles are stably sorted by work, descending, and
- * sorted tile i goes to worker i mod W when floor(i/W) is even, else to
- * W-1-(i mod W).
+ * causal: ceil(min(256(t+1), L)/64); block-sparse: the 64-key blocks of the
+ * 128-key mask blocks inside the sequence kept by either of the tile's two
+ * 128-row mask rows). BWD: t is a KV tile of block_n=128 keys, work = Q
+ * blocks of block_m=64 rows visited (dense: ceil(Lq/64); causal:
+ * ceil(L/64) - 2t; block-sparse: the 64-row blocks of the kept 128-row mask
+ * tiles). Tiles are stably sorted by work, descending, and sorted tile i goes
+ * to worker i mod W when floor(i/W) is even, else to W-1-(i mod W).
+ * DQ: the FWD tiles and work. With per-sequence Q the deal is the FWD deal.
+ * With broadcast Q (every tile (b, h, t) adds into the same dQ rows of head
+ * h), the G = H * ceil(lq/256) groups g = h * ceil(lq/256) + t get disjoint
+ * worker ranges [g W'/G, (g+1) W'/G) of W' = max(W, G) workers, and each
+ * group's tiles are sorted and snake-dealt over its own range, so that every
+ * worker sums one group only (one partial per worker).
  *
  * h_q_offsets: int32 [B+1], NULL in broadcast mode. h_kv_offsets: int32 [B+1].
  * h_block_mask: NULL when mask_q_blocks = mask_kv_blocks = 0.
@@ -138,10 +146,13 @@ int32_t jfa_offsets_from_lengths(const int32_t* h_lengths, int32_t batch, int32_
  *   h_worker_ptr  int32 [W+1]      tiles of worker w are [ptr[w], ptr[w+1])
  *   h_tiles       int32 [N*4]      (b, h, t, work) per tile
  *   h_sparse_ptr  int32 [sparse_rows+1], h_sparse_idx int32 [sparse_nnz]
- *                 (block-sparse only, else may be NULL): FWD = CSR over rows
- *                 b*mask_q_blocks+m of the kept 128-key blocks inside the
- *                 sequence; BWD = CSC over columns b*mask_kv_blocks+c of the
- *                 kept 128-row Q tiles inside the sequence; ascending.
+ *                 (block-sparse only, else may be NULL): FWD and DQ = CSR
+ *                 over Q tiles b*ceil(mask_q_blocks/2)+t of the 128-key
+ *                 blocks c inside the sequence kept by a mask row of the
+ *                 tile, stored as 4c + bits (bit k: row 2t+k keeps c; rows
+ *                 past the mask or the sequence keep nothing); BWD = CSC over
+ *                 columns b*mask_kv_blocks+c of the kept 128-row Q tiles
+ *                 inside the sequence; ascending.
  * The caller copies these arrays to the device for jfa_fwd / jfa_bwd.
  */
 int32_t jfa_plan_query(const jfa_problem* prob, const int32_t* h_q_offsets,

@@ -27,6 +27,7 @@ JFA_ERR_HIP = -6
 JFA_ERR_BAD_MASK = -7
 JFA_PASS_FWD = 0
 JFA_PASS_BWD = 1
+JFA_PASS_DQ = 2
 
 EXPORTS = (
     "jfa_abi_version", "jfa_status_string", "jfa_last_hip_error", "jfa_device_workers",
@@ -289,7 +290,7 @@ class JaggedAttention:
         self.device = device
         cus = jfa_device_workers(torch.device(device).index or 0)
         self.fwd_plan_host = jfa_plan_build(prob, q_offsets, kv_offsets, block_mask,
-                                            JFA_PASS_FWD, fwd_workers or 2 * cus)
+                                            JFA_PASS_FWD, fwd_workers or cus)
         self.bwd_plan_host = jfa_plan_build(prob, q_offsets, kv_offsets, block_mask,
                                             JFA_PASS_BWD, bwd_workers or cus)
         self.fwd_plan = to_device(self.fwd_plan_host, device)

@@ -42,8 +42,11 @@ int32_t check_common(const jfa_problem* p, const jfa_plan_info* info, int32_t pa
     if (p->broadcast_q && info->total_q != (int64_t)p->batch * p->lq) return JFA_ERR_PLAN_MISMATCH;
     const bool sparse = p->mask_q_blocks != 0;
     if (sparse) {
-        const int64_t rows = (int64_t)p->batch *
-                             (pass == JFA_PASS_FWD ? p->mask_q_blocks : p->mask_kv_blocks);
+        const int64_t rows =
+            (int64_t)p->batch * (pass == JFA_PASS_FWD
+                                     ? (p->mask_q_blocks + jfa::kFwdBlockM / jfa::kMaskBlock - 1) /
+                                           (jfa::kFwdBlockM / jfa::kMaskBlock)
+                                     : p->mask_kv_blocks);
         if (info->sparse_rows != rows) return JFA_ERR_PLAN_MISMATCH;
         if (d_sparse_ptr == nullptr || (info->sparse_nnz > 0 && d_sparse_idx == nullptr))
             return JFA_ERR_INVALID_ARG;

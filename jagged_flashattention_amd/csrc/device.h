@@ -65,6 +65,39 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
 // those prefetches inside the loop (its per-register wait tracking is merged
 // over the back edge).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N): all but this wave's N most recent vector memory
+// operations have completed (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_keep() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Scheduling hint for a run of N LDS operand reads each feeding one MFMA:
+// issue the first A reads, then alternate one MFMA with one more read, then
+// the last A MFMAs. Without it the scheduler keeps a single read in flight
+// and every MFMA waits out a full LDS latency. Only orders the reads and
+// MFMAs of the current scheduling region; other instructions move freely.
+template <int N, int A>
+__device__ __forceinline__ void pipeline_reads_mfma() {
+    constexpr int kMfma = 0x008, kDsRead = 0x100;
+    __builtin_amdgcn_sched_group_barrier(kDsRead, A, 0);
+#pragma unroll
+    for (int j = 0; j < N - A; ++j) {
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kMfma, A, 0);
+}
+
+// Load of a wave-uniform value from memory the kernel never writes (plans,
+// offsets), through the constant address space so that it becomes a scalar
+// load: a vector load would need a vmcnt wait, which also waits for every
+// copy in flight.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* p) {
+    return *(const __attribute__((address_space(4))) T*)p;
+}
 
 // Persistent worker of this workgroup. Workgroup ids are dealt round-robin to
 // the 8 XCDs; mapping consecutive workers to the same XCD puts tiles dealt

@@ -8,36 +8,68 @@
 // sections "What TLX changes" and "Optimizations layered on top"). The
 // warp-specialised Blackwell machinery is not reproduced; on CDNA4 the same
 // goals map to:
-//   - a persistent grid that walks a host-built tile list (sorted by KV work,
-//     dealt in zigzag order), with an XCD-aware workgroup -> worker map;
-//   - 4 waves per workgroup, each owning 32 query rows of a 128-row tile, Q
-//     held in VGPRs as the B operand of S^T = K Q^T (32x32x16 bf16 MFMA) so a
-//     lane owns one query row: row max / row sum stay in-lane and need one
-//     cross-half exchange;
-//   - K and V of a 64-key block double-buffered in LDS from 16-byte global
-//     loads issued one block ahead; K rows are stored with a chunk swizzle and
-//     V is transposed on its way into LDS (keys in the order the P^T
-//     accumulator registers hold them), so every MFMA operand is one
-//     conflict-free 16-byte LDS read;
-//   - fp32 running max and sum in the exp2 domain, rescaling of the O
-//     accumulator skipped when no row max moved;
-//   - a bulk loop without any mask arithmetic and a tail loop (last partial
-//     block, causal diagonal) with it.
-#include <type_traits>
-
+//   - one persistent workgroup of 8 waves per CU walking a host-built tile
+//     list (sorted by KV work, dealt in zigzag order). A tile is 256 query
+//     rows, 32 per wave, so a 64-key K/V block brought into LDS serves 256
+//     rows (for a broadcast Q of 256 rows: every K/V row is read once);
+//   - the worker's blocks form one stream across its tiles: K and V of block
+//     j+3 are copied global -> LDS with direct-to-LDS loads while block j is
+//     computed (4-slot K ring, 3-slot V ring; a block's copies get two
+//     iterations to land), so the copy costs no VGPRs and no LDS store
+//     instructions, and tile boundaries do not drain the pipe;
+//   - V of block j+1 is transposed LDS -> LDS with transposed LDS reads
+//     (ds_read_b64_tr_b16) into V^T with keys in the order the P^T
+//     accumulator registers hold them, once per block for all 8 waves;
+//   - per wave: S^T = K Q^T (32x32x16 bf16 MFMA, Q in VGPRs as the B operand,
+//     so a lane owns one query row and row max / row sum stay in-lane), fp32
+//     online softmax in the exp2 domain (rescale skipped while no row max
+//     moves), O^T += V^T P^T with P^T straight from the accumulators;
+//   - a bulk path without mask arithmetic and a masked tail (partial last
+//     block, causal diagonal); blocks a wave's rows cannot see (causal, or
+//     dropped by its block-sparse mask row) are skipped by that wave;
+//   - O leaves through a per-wave LDS staging area (in the K slot and V^T
+//     buffer the tile's last block has released) as whole 16-byte-per-lane
+//     rows, so each store instruction writes 4 full rows.
+// Every LDS tile is XOR-swizzled at 16-byte granularity so that the MFMA
+// operand reads, the transposed reads and the V^T writes are free of bank
+// conflicts (64 banks x 4 bytes).
 #include "device.h"
 #include "internal.h"
 
 namespace jfa {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kAhead = 3;        // block j+kAhead is copied while block j is computed
+constexpr int kKSlots = kAhead + 1;   // K ring: blocks j .. j+kAhead
+constexpr int kVSlots = kAhead;       // V ring: blocks j+1 .. j+kAhead (j+1 is transposed at j)
+constexpr int kReadAhead = 4;    // LDS operand reads kept in flight ahead of the MFMAs
+constexpr int kStageRows = 16;   // O rows per wave per epilogue round
+
+static_assert(kFwdBlockM == 32 * kWaves && kFwdBlockN == 64, "forward tile geometry");
 
 template <int D>
-struct FwdSmem {
-    uint16_t k[2][kFwdBlockN][D];            // K rows, 16-byte chunks swizzled
-    uint16_t vt[2][D][kFwdBlockN + 8];       // V^T, keys in sigma order
+struct FwdLds {
+    static constexpr int BLK = kFwdBlockN * D * 2;            // one K or V block
+    static constexpr int K = 0;                                // kKSlots natural K blocks
+    static constexpr int V = K + kKSlots * BLK;                // kVSlots natural V blocks
+    static constexpr int VT = V + kVSlots * BLK;               // 2 V^T blocks [D][64]
+    static constexpr int BYTES = VT + 2 * BLK;
+    static constexpr int OST_WAVE = kStageRows * D * 2;        // O staging of one wave
+    static_assert(4 * OST_WAVE == BLK, "staging: 4 waves per released block");
 };
+
+// 16-byte chunk swizzles (chunk index XOR f(row)).
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {   // K rows: S^T operand reads
+    return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {   // V rows: transposed reads
+    return D == 128 ? 2 * ((r & 3) + 4 * ((r >> 3) & 1)) : 2 * (((r >> 1) & 1) + 2 * ((r >> 3) & 1));
+}
+__device__ __forceinline__ int swz_vt(int d) { return (d >> 1) & 7; }   // V^T rows (64 keys)
 
 // position of key q (within its group of 16) in sigma order 0-3, 8-11, 4-7, 12-15
 __device__ __forceinline__ int sigma_pos(int q) {
@@ -45,242 +77,341 @@ __device__ __forceinline__ int sigma_pos(int q) {
     return (q & ~15) | (((g >> 1) | ((g & 1) << 1)) << 2) | (q & 3);
 }
 
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-    constexpr int CH = D / 8;
-    constexpr int SH = (D == 128) ? 4 : 3;
-    return (r + (r >> SH)) & (CH - 1);
-}
-
-__device__ __forceinline__ void transpose4x8(const u32x4 (&x)[4], u32x2 (&y)[8]) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        y[2 * k][0] = (x[0][k] & 0xffffu) | (x[1][k] << 16);
-        y[2 * k][1] = (x[2][k] & 0xffffu) | (x[3][k] << 16);
-        y[2 * k + 1][0] = (x[0][k] >> 16) | (x[1][k] & 0xffff0000u);
-        y[2 * k + 1][1] = (x[2][k] >> 16) | (x[3][k] & 0xffff0000u);
-    }
+// Direct-to-LDS copy of 16 bytes per lane: lane l's bytes at g land at
+// lds_wave_base + 16 l (lds_wave_base wave-uniform). Issued as inline
+// assembly so that the compiler does not treat every later LDS read as
+// possibly overlapping the copy (it would wait for all copies in flight
+// before each of them); completion is awaited explicitly with wait_vmem()
+// followed by a workgroup barrier.
+__device__ __forceinline__ void load_lds16(const uint16_t* g, char* lds_wave_base) {
+    const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_wave_base;
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(g), "s"(lds)
+        : "memory");
 }
 
 template <int D, int MODE, bool BCAST>
-__global__ void __launch_bounds__(kThreads, 2) fwd_kernel(FwdArgs a) {
-    __shared__ FwdSmem<D> sm;
+__global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
+    using LY = FwdLds<D>;
+    __shared__ __attribute__((aligned(1024))) char smem[LY::BYTES];
     constexpr int KC = D / 16;              // 16-wide d chunks of S^T = K Q^T
     constexpr int MD = D / 32;              // 32-row d blocks of O^T
     constexpr int CH = D / 8;               // 16-byte chunks per K/V row
+    constexpr int LPW = (kFwdBlockN * CH) / (64 * kWaves);   // K (and V) loads per wave per block
+    constexpr int TPW = (kFwdBlockN * D) / (256 * kWaves);   // transposed reads per wave per block
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int lr = lane & 31, hf = lane >> 5;
     const int H = a.num_heads;
     const int64_t rs = (int64_t)H * D;
-    // loader: keys 4kg..4kg+3 x one 16-byte chunk dc per thread
-    const int ld_kg = tid & 15, ld_dc = tid >> 4;
-    const bool ld_on = ld_dc < CH;
-    const int ld_pos = sigma_pos(4 * ld_kg);
-    // swizzled K-row addresses of this lane (rows 32mb + lr)
-    int nat_base[2], nat_x[2];
+
+    // direct-to-LDS copy: load u of this wave fills chunk positions 64u'+lane
+    // (u' = LPW*wave + u) of a block, i.e. key r, stored chunk cp
+    int ld_row[LPW], ld_gk[LPW], ld_gv[LPW];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-        const int row = 32 * mb + lr;
-        const int s = swz<D>(row);
-        nat_base[mb] = row * D + 8 * (hf ^ (s & 1));
-        nat_x[mb] = s >> 1;
+    for (int u = 0; u < LPW; ++u) {
+        const int p = 64 * (LPW * wave + u) + lane;
+        const int r = p / CH, cp = p % CH;
+        ld_row[u] = r;
+        ld_gk[u] = 8 * (cp ^ swz_k<D>(r));
+        ld_gv[u] = 8 * (cp ^ swz_v<D>(r));
     }
+    // transposition V -> V^T: this lane's read and write addresses per read u
+    int tr_src[TPW], tr_dst[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int P = 2 * (TPW * wave + u) + (lane >> 5);
+        const int dg = P >> 3, s = (P >> 1) & 3, z = P & 1;
+        const int kq = 4 * s + z + 2 * ((lane >> 4) & 1);   // key quad of this 16-lane group
+        const int n16 = lane & 15, e = n16 >> 2, c = n16 & 3;
+        const int r = 4 * kq + e;
+        tr_src[u] = r * D * 2 + (((2 * dg + (c >> 1)) ^ swz_v<D>(r)) << 4) + 8 * (c & 1);
+        const int d = 16 * dg + n16, pos = sigma_pos(4 * kq);
+        tr_dst[u] = d * 128 + (((pos >> 3) ^ swz_vt(d)) << 4) + 2 * (pos & 7);
+    }
+    // S^T operand: K row 32mb + lr, chunk 2kc + hf (swz_k(32mb + lr) == swz_k(lr))
+    int k_off[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) k_off[kc] = lr * D * 2 + (((2 * kc + hf) ^ swz_k<D>(lr)) << 4);
+    // O^T operand: V^T row 32md + lr, 16-key chunk c -> stored chunk 2c + hf
+    // (swz_vt(32md + lr) == swz_vt(lr))
+    int vt_off[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vt_off[c] = lr * 128 + (((2 * c + hf) ^ swz_vt(lr)) << 4);
 
     const int w = worker_id(a.num_workers);
-    const int t_begin = a.worker_ptr[w], t_end = a.worker_ptr[w + 1];
+    const int t_begin = ld_uniform(a.worker_ptr + w), t_end = ld_uniform(a.worker_ptr + w + 1);
 
+    // ---- the block stream of this worker: (tile, block) in plan order
+    struct TileInfo {
+        int b, h, t, work, kv0, L;
+        const int* sp;
+    };
+    auto tile_info = [&](int ti) -> TileInfo {
+        TileInfo ti_;
+        ti_.b = ld_uniform(a.tiles + 4 * ti + 0);
+        ti_.h = ld_uniform(a.tiles + 4 * ti + 1);
+        ti_.t = ld_uniform(a.tiles + 4 * ti + 2);
+        ti_.work = ld_uniform(a.tiles + 4 * ti + 3);
+        ti_.kv0 = ld_uniform(a.kv_off + ti_.b);
+        ti_.L = ld_uniform(a.kv_off + ti_.b + 1) - ti_.kv0;
+        ti_.sp = nullptr;
+        if (MODE == kSparse)
+            ti_.sp = a.sp_idx + ld_uniform(a.sp_ptr + ti_.b * ((a.mask_q_blocks + 1) >> 1) + ti_.t);
+        return ti_;
+    };
+    // 64-key block of the sequence visited at position i of a tile
+    auto seq_block = [&](const TileInfo& T, int i) -> int {
+        if (MODE == kSparse) return 2 * (ld_uniform(T.sp + (i >> 1)) >> 2) + (i & 1);
+        return i;
+    };
+
+    // loader cursor
+    int l_ti = t_begin, l_i = 0, l_slot = 0;
+    TileInfo LT;
+    LT.work = 0;
+    auto l_settle = [&]() {   // skip to the next tile with blocks (LT is l_ti's)
+        while (l_i >= LT.work) {
+            ++l_ti;
+            l_i = 0;
+            if (l_ti >= t_end) return;
+            LT = tile_info(l_ti);
+        }
+    };
+    // issue the copies of the loader's block into ring slots (K: s % 3, V: s % 2)
+    // and advance; keys past the sequence are clamped to its last row (always
+    // finite data, masked out of the softmax by the tail path)
+    auto l_issue = [&]() {
+        if (l_ti >= t_end) return;
+        const int n = seq_block(LT, l_i);
+        const int64_t base = (int64_t)LT.kv0 * rs + (int64_t)LT.h * D;
+        char* kdst = smem + LY::K + (l_slot % kKSlots) * LY::BLK;
+        char* vdst = smem + LY::V + (l_slot % kVSlots) * LY::BLK;
+#pragma unroll
+        for (int u = 0; u < LPW; ++u) {
+            const int key = min(kFwdBlockN * n + ld_row[u], LT.L - 1);
+            const int64_t row = base + (int64_t)key * rs;
+            load_lds16(a.k + row + ld_gk[u], kdst + 1024 * (LPW * wave + u));
+            load_lds16(a.v + row + ld_gv[u], vdst + 1024 * (LPW * wave + u));
+        }
+        ++l_slot;
+        ++l_i;
+        l_settle();
+    };
+    // V (natural, slot s % kVSlots) -> V^T (buffer s % 2), in two halves so
+    // that the transposed reads can be issued well before their writes
+    auto tr_read = [&](int s, bf16x4 (&x)[TPW]) {
+        const char* src = smem + LY::V + (s % kVSlots) * LY::BLK;
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) x[u] = lds_read_tr((const uint16_t*)(src + tr_src[u]));
+    };
+    auto tr_write = [&](int s, const bf16x4 (&x)[TPW]) {
+        char* dst = smem + LY::VT + (s & 1) * LY::BLK;
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) *(bf16x4*)(dst + tr_dst[u]) = x[u];
+    };
+    auto transpose_v = [&](int s) {
+        bf16x4 x[TPW];
+        tr_read(s, x);
+        tr_write(s, x);
+    };
+
+    if (t_begin < t_end) {
+        LT = tile_info(t_begin);
+        l_settle();
+    }
+    int total = 0;   // stream length, to know whether block s+1 exists
+    for (int ti = t_begin; ti < t_end; ++ti) total += ld_uniform(a.tiles + 4 * ti + 3);
+
+    // prologue: block 0 landed and transposed, blocks 1 .. kAhead-1 in flight
+    if (total > 0) {
+        l_issue();
+        wait_vmem();
+        __syncthreads();
+        transpose_v(0);
+#pragma unroll
+        for (int k = 1; k < kAhead; ++k) l_issue();
+    }
+
+    int s = 0;   // stream position of the consumer
     for (int ti = t_begin; ti < t_end; ++ti) {
-        const int b = a.tiles[4 * ti + 0];
-        const int hd = a.tiles[4 * ti + 1];
-        const int t = a.tiles[4 * ti + 2];
-        const int work = a.tiles[4 * ti + 3];
-        const int kv0 = a.kv_off[b];
-        const int L = a.kv_off[b + 1] - kv0;
+        const TileInfo T = tile_info(ti);
         int q0, Lq, orow0;
         if (BCAST) {
             q0 = 0;
             Lq = a.lq;
-            orow0 = b * a.lq;
+            orow0 = T.b * a.lq;
         } else {
-            q0 = a.q_off[b];
-            Lq = a.q_off[b + 1] - q0;
+            q0 = ld_uniform(a.q_off + T.b);
+            Lq = ld_uniform(a.q_off + T.b + 1) - q0;
             orow0 = q0;
         }
-        const int qrow = t * kFwdBlockM + wave * 32 + lr;
-        const int* sp = nullptr;
-        if (MODE == kSparse) sp = a.sp_idx + a.sp_ptr[b * a.mask_q_blocks + t];
-        auto blk = [&](int i) -> int {
-            if (MODE == kSparse) return 2 * sp[i >> 1] + (i & 1);
-            return i;
-        };
-        int nbulk;
-        if (MODE == kDense) {
-            nbulk = L / kFwdBlockN;
-        } else if (MODE == kCausal) {
-            nbulk = min(2 * t, L / kFwdBlockN);
-        } else {
-            nbulk = work;
-            if (work > 0 && kFwdBlockN * (blk(work - 1) + 1) > L) nbulk = work - 1;
-        }
-        nbulk = min(nbulk, work);
-
+        const int row0 = T.t * kFwdBlockM + 32 * wave;   // first row of this wave
+        const int qrow = row0 + lr;
+        const bool wave_rows = row0 < Lq;                // wave-uniform
+        // Q^T fragments of this lane's row (rows past the sequence read its last
+        // row; a tile exists only when Lq >= 1, and a wave without rows skips
+        // every block)
         bf16x8 qf[KC];
-        if (qrow < Lq) {
-            const uint16_t* qp = a.q + (int64_t)(q0 + qrow) * rs + (int64_t)hd * D + 8 * hf;
+        {
+            const int qr = min(qrow, Lq - 1);
+            const uint16_t* qp = a.q + (int64_t)(q0 + qr) * rs + (int64_t)T.h * D + 8 * hf;
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) qf[kc] = load_bf16x8(qp + 16 * kc);
-        } else {
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc) qf[kc] = bf16x8{};
         }
-
         f32x16 oacc[MD];
 #pragma unroll
         for (int md = 0; md < MD; ++md) oacc[md] = f32x16{};
         float m_run = -1e30f, l_run = 0.f;
 
-        // (threads past the row width load a valid chunk and never store it)
-        const uint16_t* kbase = a.k + (int64_t)kv0 * rs + (int64_t)hd * D + 8 * (ld_dc & (CH - 1));
-        const uint16_t* vbase = a.v + (int64_t)kv0 * rs + (int64_t)hd * D + 8 * (ld_dc & (CH - 1));
-        u32x4 kr[4], vr[4];
-        int ld_n = 0;   // KV block held in the registers, for the zero fill at store time
-        auto gload = [&](int n) {
-            // unconditional loads from a key clamped into the sequence (L >= 1
-            // whenever a block exists); keys past the end are zeroed in sstore
-            ld_n = n;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int key = min(kFwdBlockN * n + 4 * ld_kg + p, L - 1);
-                kr[p] = *(const u32x4*)(kbase + (int64_t)key * rs);
-                vr[p] = *(const u32x4*)(vbase + (int64_t)key * rs);
-            }
-        };
-        auto sstore = [&](int buf) {
-            if (ld_on) {
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    if (kFwdBlockN * ld_n + 4 * ld_kg + p >= L) {
-                        kr[p] = u32x4{};
-                        vr[p] = u32x4{};
-                    }
-                }
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const int row = 4 * ld_kg + p;
-                    *(u32x4*)&sm.k[buf][row][8 * (ld_dc ^ swz<D>(row))] = kr[p];
-                }
-                u32x2 y[8];
-                transpose4x8(vr, y);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) *(u32x2*)&sm.vt[buf][8 * ld_dc + e][ld_pos] = y[e];
-            }
-        };
-
-        if (work > 0) {
-            gload(blk(0));
-            sstore(0);
-        }
-        // Nothing may be left in flight here: otherwise the compiler's wait
-        // counters, merged over the loop back edge, make the first MFMAs of
-        // every iteration wait for that iteration's prefetch loads.
+        // The tile's Q rows and the previous tile's stores are younger than
+        // the copies in flight: wait for everything once here, so that no
+        // load the compiler tracks is pending inside the block loop.
         wait_vmem();
-        __syncthreads();
-
-        auto body = [&](int i, auto masked_tag) {
-            constexpr bool MASKED = decltype(masked_tag)::value;
-            const int buf = i & 1;
-            const int n = blk(i);
-            if (i + 1 < work) gload(blk(i + 1));
-
-            // S^T[key, qrow] for the 64 keys of the block: two 32-key halves
-            f32x16 s[2];
+        // S^T of a landed block (K slot of stream position p) into acc
+        auto compute_s = [&](f32x16 (&acc)[2], int p) {
+            const char* kb = smem + LY::K + (p % kKSlots) * LY::BLK;
+            acc[0] = f32x16{};
+            acc[1] = f32x16{};
+            bf16x8 kf[2 * KC];
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                s[mb] = f32x16{};
+            for (int j = 0; j < 2 * KC; ++j)
+                kf[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(kb + 32 * D * 2 * (j & 1) + k_off[j >> 1]));
 #pragma unroll
-                for (int kc = 0; kc < KC; ++kc) {
-                    const bf16x8 kf =
-                        load_bf16x8(&sm.k[buf][0][0] + nat_base[mb] + 16 * (kc ^ nat_x[mb]));
-                    s[mb] = mfma32(kf, qf[kc], s[mb]);
-                }
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float x = s[mb][r];
-                    if (MASKED) {
-                        const int kk = kFwdBlockN * n + 32 * mb + 8 * (r >> 2) + 4 * hf + (r & 3);
-                        bool ok = kk < L;
-                        if (MODE == kCausal) ok = ok && kk <= qrow;
-                        x = ok ? x : -INFINITY;
-                    }
-                    s[mb][r] = x;
-                    mx = fmaxf(mx, x);
-                }
-            // running max in the exp2 domain of the scaled scores
-            mx = pair_max(mx) * a.scale_log2;
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            float ls = 0.f;
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][r], a.scale_log2, -m_new));
-                    s[mb][r] = p;
-                    ls += p;
-                }
-            l_run = l_run * alpha + ls;
-            m_run = m_new;
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-                for (int md = 0; md < MD; ++md) oacc[md] *= alpha;
-            }
-            // P^T as the B operand: chunk c holds keys 16c..16c+15 of the block
-            bf16x8 pb[4];
+            for (int j = 0; j < 2 * KC; ++j) acc[j & 1] = mfma32(kf[j], qf[j >> 1], acc[j & 1]);
+        };
+        // exp2 of the scaled scores against the new running max, their row
+        // sum, and P^T as bf16 B operands (chunk c: keys 16c..16c+15)
+        auto exp_pack = [&](f32x16 (&sc)[2], float m_new, float& ls, bf16x8 (&pb)[4]) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 f32x8 x;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] = s[c >> 1][8 * (c & 1) + j];
+                for (int j = 0; j < 8; ++j) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(sc[c >> 1][8 * (c & 1) + j], a.scale_log2, -m_new));
+                    ls += p;
+                    x[j] = p;
+                }
                 pb[c] = to_bf16x8(x);
             }
-            // O^T[d, qrow] += V^T[d, key] P^T[key, qrow]
+        };
+        // O^T[d, qrow] += V^T[d, key] P^T[key, qrow] (V^T buffer of stream position p)
+        auto pv = [&](const bf16x8 (&pb)[4], int p) {
+            const char* vtb = smem + LY::VT + (p & 1) * LY::BLK;
+            bf16x8 vf[4 * MD];
 #pragma unroll
-            for (int md = 0; md < MD; ++md)
+            for (int j = 0; j < 4 * MD; ++j)
+                vf[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(vtb + 32 * 128 * (j >> 2) + vt_off[j & 3]));
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const bf16x8 vf = load_bf16x8(&sm.vt[buf][32 * md + lr][16 * c + 8 * hf]);
-                    oacc[md] = mfma32(vf, pb[c], oacc[md]);
-                }
-            if (i + 1 < work) sstore(buf ^ 1);
-            __syncthreads();
+            for (int j = 0; j < 4 * MD; ++j) oacc[j >> 2] = mfma32(vf[j], pb[j & 3], oacc[j >> 2]);
+            pipeline_reads_mfma<4 * MD, kReadAhead>();
         };
 
-        int i = 0;
-        for (; i < nbulk; ++i) body(i, std::false_type{});
-        for (; i < work; ++i) body(i, std::true_type{});
+        for (int i = 0; i < T.work; ++i, ++s) {
+            // Block s+1 landed; in steady state the copies of block s+2 (the
+            // wave's 2*LPW most recent vector memory operations) stay in flight.
+            if (i > 0) {
+                if (s + 2 < total) wait_vmem_keep<2 * LPW>();
+                else wait_vmem();
+            }
+            // every wave is past block s-1: its K slot and V^T buffer are free
+            __syncthreads();
+            l_issue();                              // block s+kAhead
+            if (s + 1 < total) transpose_v(s + 1);  // V^T of block s+1
 
-        const float l_tot = pair_sum(l_run);
-        if (qrow < Lq) {
-            const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-            const int orow = orow0 + qrow;
-            uint16_t* op = a.o + (int64_t)orow * rs + (int64_t)hd * D + 4 * hf;
+            const int n = seq_block(T, i);
+            bool skip = !wave_rows, masked;
+            if (MODE == kCausal) {
+                skip = skip || kFwdBlockN * n > row0 + 31;
+                masked = kFwdBlockN * n + kFwdBlockN - 1 > row0 || kFwdBlockN * (n + 1) > T.L;
+            } else {
+                masked = kFwdBlockN * (n + 1) > T.L;
+                if (MODE == kSparse) skip = skip || !((ld_uniform(T.sp + (i >> 1)) >> (wave >> 2)) & 1);
+            }
+            if (!skip) {
+                f32x16 sc[2];
+                compute_s(sc, s);
+                pipeline_reads_mfma<2 * KC, kReadAhead>();
+                // masked tail: keys past the sequence (and, causal, past the row) -> -inf
+                if (masked) {
+                    const int lim = MODE == kCausal ? min(T.L - 1, qrow) : T.L - 1;
 #pragma unroll
-            for (int md = 0; md < MD; ++md)
+                    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    f32x4 x;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) x[j] = oacc[md][4 * g + j] * inv;
-                    *(u32x2*)(op + 32 * md + 8 * g) = __builtin_bit_cast(u32x2, to_bf16x4(x));
+                        for (int r = 0; r < 16; ++r) {
+                            const int kk = kFwdBlockN * n + 32 * mb + 8 * (r >> 2) + 4 * hf + (r & 3);
+                            sc[mb][r] = kk <= lim ? sc[mb][r] : -INFINITY;
+                        }
                 }
-            if (hf == 0)
-                a.lse[(int64_t)hd * a.total_q + orow] =
+                float mx = -INFINITY;
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[mb][r]);
+                // running max in the exp2 domain of the scaled scores
+                mx = pair_max(mx) * a.scale_log2;
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                m_run = m_new;
+                if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+                    for (int md = 0; md < MD; ++md) oacc[md] *= alpha;
+                }
+                float ls = 0.f;
+                bf16x8 pb[4];
+                exp_pack(sc, m_new, ls, pb);
+                l_run = l_run * alpha + ls;
+                pv(pb, s);
+            }
+        }
+
+        // ---- epilogue: O = O^T / l through this wave's staging area, LSE.
+        // The staging areas are the K slot of block s-1 (no copy in flight
+        // targets it: those are blocks s .. s+kAhead-1) for waves 0-3 and the
+        // V^T buffer of block s-1 for waves 4-7, free once every wave is past
+        // block s-1; both are next written after the next iteration's barrier.
+        const float l_tot = pair_sum(l_run);
+        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+        __syncthreads();
+        if (wave_rows) {
+            char* st = wave < 4 ? smem + LY::K + ((s + kKSlots - 1) % kKSlots) * LY::BLK + wave * LY::OST_WAVE
+                                : smem + LY::VT + ((s + 1) & 1) * LY::BLK + (wave - 4) * LY::OST_WAVE;
+#pragma unroll
+            for (int rd = 0; rd < 32 / kStageRows; ++rd) {
+                if ((lr >> 4) == rd) {
+                    const int r = lr & 15;
+#pragma unroll
+                    for (int md = 0; md < MD; ++md)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            f32x4 x;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) x[j] = oacc[md][4 * g + j] * inv;
+                            const int chunk = 4 * md + g;
+                            *(bf16x4*)(st + r * D * 2 + ((chunk ^ (r & (CH - 1))) << 4) + 8 * hf) =
+                                to_bf16x4(x);
+                        }
+                }
+#pragma unroll
+                for (int v = 0; v < kStageRows * CH / 64; ++v) {
+                    const int k = lane + 64 * v;
+                    const int r = k / CH, chunk = k % CH;
+                    const u32x4 x = *(const u32x4*)(st + r * D * 2 + ((chunk ^ (r & (CH - 1))) << 4));
+                    const int orow = row0 + kStageRows * rd + r;
+                    if (orow < Lq)
+                        *(u32x4*)(a.o + (int64_t)(orow0 + orow) * rs + (int64_t)T.h * D + 8 * chunk) = x;
+                }
+            }
+            if (hf == 0 && qrow < Lq)
+                a.lse[(int64_t)T.h * a.total_q + orow0 + qrow] =
                     l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
         }
     }

@@ -89,15 +89,32 @@ inline bool kept(const jfa_problem* p, const uint8_t* mask, int32_t b, int32_t m
     return mask[((int64_t)b * p->mask_q_blocks + m) * p->mask_kv_blocks + c] != 0;
 }
 
+// Mask rows per forward tile.
+constexpr int32_t kRowsPerTile = kFwdBlockM / kMaskBlock;
+static_assert(kRowsPerTile * kMaskBlock == kFwdBlockM && kRowsPerTile <= 2, "tile/mask geometry");
+
+// Bits of the mask rows of forward tile (b, t) that keep 128-key block c (bit
+// k: row kRowsPerTile*t + k; rows past the mask or the sequence count as not
+// keeping it).
+inline int32_t fwd_bits(const jfa_problem* p, const uint8_t* mask, int32_t b, int32_t t, int32_t c,
+                        int32_t lq) {
+    int32_t bits = 0;
+    for (int32_t k = 0; k < kRowsPerTile; ++k) {
+        const int32_t m = kRowsPerTile * t + k;
+        if (m < p->mask_q_blocks && (int64_t)kMaskBlock * m < lq && kept(p, mask, b, m, c))
+            bits |= 1 << k;
+    }
+    return bits;
+}
+
 int32_t tile_work(const jfa_problem* p, const uint8_t* mask, int32_t pass, int32_t b, int32_t t,
                   int32_t lq, int32_t lk) {
     const bool sparse = p->mask_q_blocks != 0;
-    if (pass == JFA_PASS_FWD) {
+    if (pass != JFA_PASS_BWD) {
         if (sparse) {
             int64_t w = 0;
-            const int32_t m = t * kFwdBlockM / kMaskBlock;
             for (int32_t c = 0; c < cdiv(lk, kMaskBlock); ++c)
-                if (kept(p, mask, b, m, c))
+                if (fwd_bits(p, mask, b, t, c, lq))
                     w += cdiv(std::min<int64_t>((int64_t)kMaskBlock * (c + 1), lk) -
                                   (int64_t)kMaskBlock * c,
                               kFwdBlockN);
@@ -125,30 +142,31 @@ int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, co
     if (info == nullptr) return JFA_ERR_INVALID_ARG;
     int32_t st = check_problem(p);
     if (st) return st;
-    if (pass != JFA_PASS_FWD && pass != JFA_PASS_BWD) return JFA_ERR_INVALID_ARG;
+    if (pass != JFA_PASS_FWD && pass != JFA_PASS_BWD && pass != JFA_PASS_DQ)
+        return JFA_ERR_INVALID_ARG;
     if (W < 1) return JFA_ERR_INVALID_ARG;
+    // Q-tile passes (forward, dQ) enumerate Q tiles; the backward KV tiles
+    const bool qtiles = pass != JFA_PASS_BWD;
     const bool sparse = p->mask_q_blocks != 0;
     if (sparse && mask == nullptr) return JFA_ERR_BAD_MASK;
     Lens L;
     st = lengths_of(p, qo, ko, L);
     if (st) return st;
 
-    const int32_t bm = pass == JFA_PASS_FWD ? kFwdBlockM : kBwdBlockM;
-    const int32_t bn = pass == JFA_PASS_FWD ? kFwdBlockN : kBwdBlockN;
+    const int32_t bm = qtiles ? kFwdBlockM : kBwdBlockM;
+    const int32_t bn = qtiles ? kFwdBlockN : kBwdBlockN;
 
     // 1-2. enumerate tiles with their work
     std::vector<Tile> tiles;
     int64_t n_total = 0;
     for (int32_t b = 0; b < p->batch; ++b)
-        n_total += (int64_t)p->num_heads *
-                   (pass == JFA_PASS_FWD ? cdiv(L.q[b], bm) : cdiv(L.kv[b], bn));
+        n_total += (int64_t)p->num_heads * (qtiles ? cdiv(L.q[b], bm) : cdiv(L.kv[b], bn));
     if (n_total > INT32_MAX / 4) return JFA_ERR_INVALID_ARG;
     tiles.reserve((size_t)n_total);
     int64_t total_work = 0;
     int32_t max_work = 0;
     for (int32_t b = 0; b < p->batch; ++b) {
-        const int32_t nt =
-            (int32_t)(pass == JFA_PASS_FWD ? cdiv(L.q[b], bm) : cdiv(L.kv[b], bn));
+        const int32_t nt = (int32_t)(qtiles ? cdiv(L.q[b], bm) : cdiv(L.kv[b], bn));
         for (int32_t h = 0; h < p->num_heads; ++h)
             for (int32_t t = 0; t < nt; ++t) {
                 const int32_t w = tile_work(p, mask, pass, b, t, L.q[b], L.kv[b]);
@@ -160,13 +178,14 @@ int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, co
 
     // block-sparse lists
     int64_t sp_rows = 0, sp_nnz = 0;
+    const int32_t fwd_rows = (int32_t)cdiv(p->mask_q_blocks, kRowsPerTile);
     if (sparse) {
-        if (pass == JFA_PASS_FWD) {
-            sp_rows = (int64_t)p->batch * p->mask_q_blocks;
+        if (qtiles) {
+            sp_rows = (int64_t)p->batch * fwd_rows;
             for (int32_t b = 0; b < p->batch; ++b)
-                for (int32_t m = 0; m < p->mask_q_blocks; ++m)
+                for (int32_t t = 0; t < fwd_rows; ++t)
                     for (int32_t c = 0; c < cdiv(L.kv[b], kMaskBlock); ++c)
-                        sp_nnz += kept(p, mask, b, m, c);
+                        sp_nnz += fwd_bits(p, mask, b, t, c, L.q[b]) != 0;
         } else {
             sp_rows = (int64_t)p->batch * p->mask_kv_blocks;
             for (int32_t b = 0; b < p->batch; ++b)
@@ -177,6 +196,15 @@ int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, co
         if (sp_rows > INT32_MAX - 1 || sp_nnz > INT32_MAX) return JFA_ERR_INVALID_ARG;
     }
 
+    // dQ pass with broadcast Q: tiles grouped by (head, Q tile); group g owns
+    // the workers [g W' / G, (g+1) W' / G) of W' = max(W, G) workers
+    const bool grouped = pass == JFA_PASS_DQ && p->broadcast_q;
+    const int32_t nqt = (int32_t)cdiv(p->lq, bm);
+    const int64_t G = grouped ? (int64_t)p->num_heads * nqt : 0;
+    if (grouped) {
+        if (G > INT32_MAX / 2) return JFA_ERR_INVALID_ARG;
+        W = (int32_t)std::max<int64_t>(W, G);
+    }
     info->pass = pass;
     info->num_workers = W;
     info->num_tiles = (int32_t)tiles.size();
@@ -194,18 +222,34 @@ int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, co
     if (sparse && (sp_ptr == nullptr || (sp_idx == nullptr && sp_nnz > 0)))
         return JFA_ERR_INVALID_ARG;
 
-    // 3. stable sort by work, descending
+    // 3. stable sort by work, descending (within each group when grouped)
     std::vector<int32_t> order(tiles.size());
     std::iota(order.begin(), order.end(), 0);
-    std::stable_sort(order.begin(), order.end(),
-                     [&](int32_t a, int32_t c) { return tiles[a].work > tiles[c].work; });
-    // 4. snake deal; 5. emit per worker in increasing deal position
+    auto group_of = [&](const Tile& t) -> int64_t {
+        return grouped ? (int64_t)t.h * nqt + t.t : 0;
+    };
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t c) {
+        const int64_t ga = group_of(tiles[a]), gc = group_of(tiles[c]);
+        if (ga != gc) return ga < gc;
+        return tiles[a].work > tiles[c].work;
+    });
+    // 4. snake deal over the group's workers; 5. emit per worker in increasing
+    // deal position
     std::vector<int32_t> count(W, 0), owner(order.size());
-    for (size_t i = 0; i < order.size(); ++i) {
-        const int32_t pos = (int32_t)(i % W);
-        const int32_t w = ((i / W) % 2 == 0) ? pos : W - 1 - pos;
-        owner[i] = w;
-        ++count[w];
+    for (size_t i = 0; i < order.size();) {
+        const int64_t g = group_of(tiles[order[i]]);
+        size_t e = i;
+        while (e < order.size() && group_of(tiles[order[e]]) == g) ++e;
+        const int32_t w0 = grouped ? (int32_t)(g * W / G) : 0;
+        const int32_t nw = grouped ? (int32_t)((g + 1) * W / G) - w0 : W;
+        for (size_t k = i; k < e; ++k) {
+            const size_t j = k - i;
+            const int32_t pos = (int32_t)(j % nw);
+            const int32_t w = w0 + (((j / nw) % 2 == 0) ? pos : nw - 1 - pos);
+            owner[k] = w;
+            ++count[w];
+        }
+        i = e;
     }
     worker_ptr[0] = 0;
     for (int32_t w = 0; w < W; ++w) worker_ptr[w + 1] = worker_ptr[w] + count[w];
@@ -223,11 +267,13 @@ int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, co
         int32_t n = 0;
         sp_ptr[0] = 0;
         int32_t r = 0;
-        if (pass == JFA_PASS_FWD) {
+        if (qtiles) {
             for (int32_t b = 0; b < p->batch; ++b)
-                for (int32_t m = 0; m < p->mask_q_blocks; ++m) {
-                    for (int32_t c = 0; c < cdiv(L.kv[b], kMaskBlock); ++c)
-                        if (kept(p, mask, b, m, c)) sp_idx[n++] = c;
+                for (int32_t t = 0; t < fwd_rows; ++t) {
+                    for (int32_t c = 0; c < cdiv(L.kv[b], kMaskBlock); ++c) {
+                        const int32_t bits = fwd_bits(p, mask, b, t, c, L.q[b]);
+                        if (bits) sp_idx[n++] = 4 * c + bits;
+                    }
                     sp_ptr[++r] = n;
                 }
         } else {

@@ -15,8 +15,8 @@ plainest readings, written out step by step here, are:
     forward (KV blocks of ``block_n`` keys visited):
       dense        ceil(Lk_b / block_n)
       causal       ceil(min((t+1)*block_m, Lk_b) / block_n)
-      block-sparse sum over the kept 128-key mask blocks c of the row of
-                   ceil((min(128(c+1), Lk_b) - 128c) / block_n)
+      block-sparse sum over the 128-key mask blocks c kept by any mask row of
+                   the tile of ceil((min(128(c+1), Lk_b) - 128c) / block_n)
     backward (Q blocks of ``block_m`` rows visited):
       dense        ceil(Lq_b / block_m)
       causal       ceil(Lq_b / block_m) - floor(t*block_n / block_m)
@@ -28,10 +28,26 @@ plainest readings, written out step by step here, are:
  5. Emit worker_ptr[W+1] and, per worker in increasing i, tiles[.,4] =
     (b, h, t, work), all int32.
 
+dQ pass (the backward's Q-stationary dQ kernel). Tiles are the forward
+tiles: (b, h, t) with the forward work.
+ * per-sequence Q: the forward plan itself;
+ * broadcast Q: every Q tile t of head h gets the contributions of all
+   sequences, summed over the batch ([clarity] second paragraph). Tiles are
+   grouped by g = h * ceil(Lq / block_m) + t (G groups). The plan uses
+   W' = max(W, G) workers; group g owns the contiguous workers
+   [floor(g W' / G), floor((g+1) W' / G)), and its tiles (b = 0..B-1) are
+   stably sorted by work, descending, and dealt in snake order over them.
+   Every worker thus sums one group only, into one per-worker partial.
+
 Block-sparse lists ([radar] section "The turning point": the block-sparse
 variant only adds iteration over the selected blocks). The mask is uint8
 [B, NQ, NK] over 128-row Q tiles x 128-key blocks, shared by all heads.
-  forward  CSR over rows (b, m), m < NQ: kept c < ceil(Lk_b/128), ascending
+  forward  CSR over the Q tiles (b, t) of block_m = R * 128 rows,
+           t < ceil(NQ / R): the 128-key blocks c < ceil(Lk_b/128) kept by at
+           least one of the tile's mask rows m = R t + k (m < NQ, 128 m < Lq_b),
+           ascending, each stored as 4 c + sum_k 2^k [row R t + k keeps c]
+           (R <= 2). A tile visits the union of its rows' blocks; each row
+           skips the blocks its own mask row drops.
   backward CSC over columns (b, c), c < NK: kept m < ceil(Lq_b/128), ascending
 """
 from __future__ import annotations
@@ -39,7 +55,7 @@ from __future__ import annotations
 import numpy as np
 
 MASK_BLOCK = 128
-FWD, BWD = 0, 1
+FWD, BWD, DQ = 0, 1, 2
 
 
 def cdiv(a: int, b: int) -> int:
@@ -58,17 +74,31 @@ def offsets_from_lengths(lengths):
     return np.array(out, dtype=np.int32)
 
 
-def sparse_lists(block_mask, q_lens, kv_lens, pass_):
-    """(ptr, idx) int32: forward CSR over (b, m) or backward CSC over (b, c)."""
+def _fwd_row_entries(block_mask, b, t, lq_b, lk_b, block_m):
+    """Forward list of Q tile (b, t): [(c, bits)] for the kept union, ascending c."""
+    _, NQ, NK = block_mask.shape
+    R = block_m // MASK_BLOCK
+    rows = [m for m in range(R * t, R * t + R) if m < NQ and MASK_BLOCK * m < lq_b]
+    out = []
+    for c in range(min(cdiv(lk_b, MASK_BLOCK), NK)):
+        bits = sum(1 << (m - R * t) for m in rows if block_mask[b, m, c])
+        if bits:
+            out.append((c, bits))
+    return out
+
+
+def sparse_lists(block_mask, q_lens, kv_lens, pass_, *, block_m=MASK_BLOCK):
+    """(ptr, idx) int32: forward CSR over Q tiles (b, t) or backward CSC over (b, c)."""
     B, NQ, NK = block_mask.shape
     ptr, idx = [0], []
     if pass_ == FWD:
+        R = block_m // MASK_BLOCK
+        assert R * MASK_BLOCK == block_m and 1 <= R <= 2
         for b in range(B):
-            nk = cdiv(int(kv_lens[b]), MASK_BLOCK)
-            for m in range(NQ):
-                for c in range(min(nk, NK)):
-                    if block_mask[b, m, c]:
-                        idx.append(c)
+            for t in range(cdiv(NQ, R)):
+                for c, bits in _fwd_row_entries(block_mask, b, t, int(q_lens[b]),
+                                                int(kv_lens[b]), block_m):
+                    idx.append(4 * c + bits)
                 ptr.append(len(idx))
     else:
         for b in range(B):
@@ -84,11 +114,8 @@ def sparse_lists(block_mask, q_lens, kv_lens, pass_):
 def _tile_work(pass_, b, t, lq_b, lk_b, *, block_m, block_n, causal, block_mask):
     if pass_ == FWD:
         if block_mask is not None:
-            w = 0
-            for c in range(min(cdiv(lk_b, MASK_BLOCK), block_mask.shape[2])):
-                if block_mask[b, t * block_m // MASK_BLOCK, c]:
-                    w += cdiv(min(MASK_BLOCK * (c + 1), lk_b) - MASK_BLOCK * c, block_n)
-            return w
+            return sum(cdiv(min(MASK_BLOCK * (c + 1), lk_b) - MASK_BLOCK * c, block_n)
+                       for c, _ in _fwd_row_entries(block_mask, b, t, lq_b, lk_b, block_m))
         if causal:
             return cdiv(min((t + 1) * block_m, lk_b), block_n)
         return cdiv(lk_b, block_n)
@@ -99,6 +126,47 @@ def _tile_work(pass_, b, t, lq_b, lk_b, *, block_m, block_n, causal, block_mask)
     if causal:
         return nqb - (t * block_n) // block_m
     return nqb
+
+
+def _snake(order_len, W):
+    """Worker (0..W-1) of each position of a sorted list under the snake deal."""
+    out = []
+    for i in range(order_len):
+        p = i % W
+        out.append(p if (i // W) % 2 == 0 else W - 1 - p)
+    return out
+
+
+def plan_dq(q_lens, kv_lens, num_heads, num_workers, *, broadcast_q, lq=0, block_m, block_n,
+            causal=False, block_mask=None):
+    """dQ pass. Returns (worker_ptr int32 [W'+1], tiles int32 [N, 4])."""
+    if not broadcast_q:
+        return plan(q_lens, kv_lens, num_heads, num_workers, FWD, block_m=block_m,
+                    block_n=block_n, causal=causal, block_mask=block_mask)
+    B = len(kv_lens)
+    nqt = cdiv(int(lq), block_m)
+    G = num_heads * nqt
+    if int(num_workers) < 1:
+        raise ValueError("need at least one worker")
+    W = max(int(num_workers), G)
+    per_worker = [[] for _ in range(W)]
+    for g in range(G):
+        h, t = divmod(g, nqt)
+        w0, w1 = (g * W) // G, ((g + 1) * W) // G
+        tiles = [(b, h, t, _tile_work(FWD, b, t, int(lq), int(kv_lens[b]), block_m=block_m,
+                                       block_n=block_n, causal=causal, block_mask=block_mask))
+                 for b in range(B)]
+        order = sorted(range(len(tiles)), key=lambda i: -tiles[i][3])   # stable
+        owner = _snake(len(order), w1 - w0)
+        for i, ti in enumerate(order):
+            per_worker[w0 + owner[i]].append(tiles[ti])
+    worker_ptr = [0]
+    flat = []
+    for lst in per_worker:
+        flat.extend(lst)
+        worker_ptr.append(len(flat))
+    return (np.array(worker_ptr, dtype=np.int32),
+            np.array(flat, dtype=np.int32).reshape(-1, 4))
 
 
 def plan(q_lens, kv_lens, num_heads, num_workers, pass_, *, block_m, block_n,
@@ -118,10 +186,7 @@ def plan(q_lens, kv_lens, num_heads, num_workers, pass_, *, block_m, block_n,
                                causal=causal, block_mask=block_mask)
                 tiles.append((b, h, t, w))
     order = sorted(range(len(tiles)), key=lambda i: -tiles[i][3])   # stable
-    owner = []
-    for i in range(len(order)):
-        p = i % W
-        owner.append(p if (i // W) % 2 == 0 else W - 1 - p)
+    owner = _snake(len(order), W)
     per_worker = [[] for _ in range(W)]
     for i, ti in enumerate(order):
         per_worker[owner[i]].append(tiles[ti])

@@ -6,7 +6,7 @@ import jagged_flashattention_amd as J
 import workloads as W
 from oracle import planner as OP
 
-FWD_BM, FWD_BN, BWD_BM, BWD_BN = 128, 64, 64, 128
+FWD_BM, FWD_BN, BWD_BM, BWD_BN = 256, 64, 64, 128
 
 
 def _problem_of(x):
@@ -52,11 +52,35 @@ def test_cpp_plan_equals_oracle_plan(cfg, workers, pass_):
     assert hp.info.block_m == bm and hp.info.block_n == bn
     assert hp.info.total_kv == int(kv_off[-1])
     if mask is not None:
-        sp, si = OP.sparse_lists(mask, q_lens, lens, pass_)
+        sp, si = OP.sparse_lists(mask, q_lens, lens, pass_, block_m=bm)
         assert np.array_equal(hp.sparse_ptr, sp)
         assert np.array_equal(hp.sparse_idx, si)
     else:
         assert hp.sparse_ptr is None and hp.info.sparse_rows == 0
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+@pytest.mark.parametrize("workers", [1, 3, 7, 255, 256, 512])
+def test_cpp_dq_plan_equals_oracle(cfg, workers):
+    w, lens, mask = _lengths_only(cfg)
+    kv_off = W.offsets_of(lens)
+    q_off = None if w.broadcast_q else kv_off
+    mq, mk = (mask.shape[1], mask.shape[2]) if mask is not None else (0, 0)
+    prob = J.Problem(batch=w.batch, num_heads=w.heads, head_dim=w.head_dim,
+                     broadcast_q=w.broadcast_q, lq=w.lq if w.broadcast_q else 0, causal=w.causal,
+                     mask_q_blocks=mq, mask_kv_blocks=mk, softmax_scale=w.scale)
+    hp = J.jfa_plan_build(prob, q_off, kv_off, mask, J.JFA_PASS_DQ, workers)
+    q_lens = [w.lq] * w.batch if w.broadcast_q else lens
+    wp, tiles = OP.plan_dq(q_lens, lens, w.heads, workers, broadcast_q=w.broadcast_q,
+                           lq=w.lq if w.broadcast_q else 0, block_m=FWD_BM, block_n=FWD_BN,
+                           causal=w.causal, block_mask=mask)
+    assert hp.info.block_m == FWD_BM and hp.info.block_n == FWD_BN
+    assert hp.info.num_workers == len(wp) - 1
+    assert np.array_equal(hp.worker_ptr, wp)
+    assert np.array_equal(hp.tiles, tiles)
+    if mask is not None:
+        sp, si = OP.sparse_lists(mask, q_lens, lens, OP.FWD, block_m=FWD_BM)
+        assert np.array_equal(hp.sparse_ptr, sp) and np.array_equal(hp.sparse_idx, si)
 
 
 def test_cpp_plan_random_small_problems():
@@ -94,5 +118,11 @@ def test_cpp_plan_random_small_problems():
             assert np.array_equal(hp.worker_ptr, wp), (trial, pass_)
             assert np.array_equal(hp.tiles, tiles), (trial, pass_)
             if mask is not None:
-                sp, si = OP.sparse_lists(mask, q_lens, lens, pass_)
+                sp, si = OP.sparse_lists(mask, q_lens, lens, pass_, block_m=bm)
                 assert np.array_equal(hp.sparse_ptr, sp) and np.array_equal(hp.sparse_idx, si)
+        hp = J.jfa_plan_build(prob, q_off, kv_off, mask, J.JFA_PASS_DQ, W_)
+        wp, tiles = OP.plan_dq(q_lens, lens, H, W_, broadcast_q=bool(prob.broadcast_q),
+                               lq=prob.lq, block_m=FWD_BM, block_n=FWD_BN, causal=causal,
+                               block_mask=mask)
+        assert np.array_equal(hp.worker_ptr, wp), (trial, "dq")
+        assert np.array_equal(hp.tiles, tiles), (trial, "dq")

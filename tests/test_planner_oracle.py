@@ -40,7 +40,7 @@ def _cases():
 
 
 @pytest.mark.parametrize("name,qlens,kvlens,causal,mask", _cases())
-@pytest.mark.parametrize("pass_,bm,bn", [(P.FWD, 128, 64), (P.BWD, 64, 128)])
+@pytest.mark.parametrize("pass_,bm,bn", [(P.FWD, 256, 64), (P.FWD, 128, 64), (P.BWD, 64, 128)])
 @pytest.mark.parametrize("workers", [1, 7, 16, 255])
 def test_plan_properties(name, qlens, kvlens, causal, mask, pass_, bm, bn, workers):
     H = 3
@@ -89,8 +89,23 @@ def test_sparse_lists_by_scan():
     for b in range(5):
         for m in range(2):
             r = b * 2 + m
-            want = [c for c in range(8) if mask[b, m, c] and 128 * c < lens[b]]
+            want = [4 * c + 1 for c in range(8) if mask[b, m, c] and 128 * c < lens[b]]
             assert list(idx[ptr[r]:ptr[r + 1]]) == want
+    # 256-row tiles: the union of the two rows' kept blocks, one bit per row;
+    # with 200 query rows both mask rows hold rows of the sequence, with 100
+    # only the first does
+    for ql in (200, 100):
+        ptr, idx = P.sparse_lists(mask, [ql] * 5, lens, P.FWD, block_m=256)
+        assert len(ptr) == 5 + 1
+        for b in range(5):
+            want = []
+            for c in range(8):
+                if 128 * c >= lens[b]:
+                    continue
+                bits = int(mask[b, 0, c]) | ((int(mask[b, 1, c]) << 1) if ql > 128 else 0)
+                if bits:
+                    want.append(4 * c + bits)
+            assert list(idx[ptr[b]:ptr[b + 1]]) == want
     ptr, idx = P.sparse_lists(mask, qlens, lens, P.BWD)
     assert len(ptr) == 5 * 8 + 1
     for b in range(5):
@@ -107,3 +122,48 @@ def test_offsets_from_lengths():
         P.offsets_from_lengths([1, -1])
     x = W.make_inputs(1)
     assert list(P.offsets_from_lengths(x.lengths)) == list(x.kv_offsets)
+
+
+@pytest.mark.parametrize("workers", [1, 3, 4, 5, 64])
+@pytest.mark.parametrize("lq", [0, 100, 256, 600])
+def test_dq_plan_grouped(workers, lq):
+    """Broadcast-Q dQ plan: every (b, h, t) tile once, each worker inside one
+    (h, t) group, groups on contiguous disjoint worker ranges, snake deal with
+    non-increasing work inside each group."""
+    rng = np.random.default_rng(lq + workers)
+    lens = rng.integers(0, 900, size=11)
+    H, bm, bn = 3, 256, 64
+    wp, tiles = P.plan_dq([lq] * 11, lens, H, workers, broadcast_q=True, lq=lq,
+                          block_m=bm, block_n=bn)
+    nqt = P.cdiv(lq, bm)
+    G = H * nqt
+    Wp = max(workers, G)
+    assert len(wp) == Wp + 1
+    got = [tuple(int(x) for x in r) for r in tiles]
+    expect = {(b, h, t, _brute_work(P.FWD, b, t, lq, int(lens[b]), bm, bn, False, None))
+              for b in range(11) for h in range(H) for t in range(nqt)}
+    assert len(got) == len(set(got)) and set(got) == expect
+    for g in range(G):
+        h, t = divmod(g, nqt)
+        w0, w1 = g * Wp // G, (g + 1) * Wp // G
+        assert w1 > w0
+        grp = [r for w in range(w0, w1) for r in got[wp[w]:wp[w + 1]]]
+        assert all(r[1] == h and r[2] == t for r in grp) and len(grp) == 11
+        nw = w1 - w0
+        cursor = [wp[w] for w in range(w0, w1)]
+        order = []
+        for i in range(len(grp)):
+            p = i % nw
+            w = p if (i // nw) % 2 == 0 else nw - 1 - p
+            order.append(got[cursor[w]])
+            cursor[w] += 1
+        assert cursor == [wp[w + 1] for w in range(w0, w1)]
+        works = [r[3] for r in order]
+        assert all(works[i] >= works[i + 1] for i in range(len(works) - 1))
+
+
+def test_dq_plan_per_sequence_is_forward_plan():
+    lens = np.array([5, 300, 0, 1000, 257])
+    a = P.plan_dq(lens, lens, 2, 3, broadcast_q=False, block_m=256, block_n=64, causal=True)
+    b = P.plan(lens, lens, 2, 3, P.FWD, block_m=256, block_n=64, causal=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
