@@ -1,8 +1,8 @@
 """Benchmark: jagged FlashAttention forward + backward on one MI355X.
 
 One step = the whole hot path over one batch of synthetic input: jfa_fwd
-(O, LSE) then the backward stages (delta preprocess, main dK/dV/dQ kernel,
-dQ convert). Inputs are resident in HBM before timing starts. The default
+(O, LSE) then the backward stages (delta preprocess, dK/dV kernel, dQ kernel,
+dQ reduce). Inputs are resident in HBM before timing starts. The default
 workload is the GEM-shaped broadcast-Q one (B=256 sequences with lognormal
 lengths, H=4, D=128, one shared Q of 256 rows).
 
@@ -58,14 +58,20 @@ def work_model(x):
     else:
         pairs = int((q_lens * lens).sum())
     e = H * D * 2   # bytes of one bf16 row of all heads
+    # each kernel: its inputs read once, its outputs written once
     fwd_bytes = q_rows * e + 2 * kv_read_rows * e + t_q * e + t_q * H * 4
-    pre_bytes = 2 * t_q * e + t_q * H * 4 + q_rows * H * D * 4
-    main_bytes = (q_rows * e + 2 * kv_read_rows * e + t_q * e + 2 * t_q * H * 4 + 2 * t_k * e
-                  + q_rows * H * D * 4)
-    fin_bytes = q_rows * H * D * 4 + q_rows * e
+    pre_bytes = 2 * t_q * e + t_q * H * 4
+    dkdv_bytes = q_rows * e + 2 * kv_read_rows * e + t_q * e + 2 * t_q * H * 4 + 2 * t_k * e
+    dq_bytes = (q_rows * e + 2 * kv_read_rows * e + t_q * e + 2 * t_q * H * 4
+                + q_rows * H * D * 4 + q_rows * e)
+    reduce_bytes = q_rows * H * D * 4 + q_rows * e
+    # FLOPs: the forward's two GEMMs; the backward's five (S, dP, dV, dK in the
+    # dK/dV kernel, dQ in the dQ kernel; the dQ kernel's recomputation of S
+    # and dP is not counted)
     return dict(pairs=pairs, fwd_flop=4 * H * D * pairs, bwd_flop=10 * H * D * pairs,
-                fwd_bytes=fwd_bytes, pre_bytes=pre_bytes, main_bytes=main_bytes,
-                fin_bytes=fin_bytes, t_q=t_q, t_k=t_k, q_rows=q_rows)
+                dkdv_flop=8 * H * D * pairs, dq_flop=2 * H * D * pairs,
+                fwd_bytes=fwd_bytes, pre_bytes=pre_bytes, dkdv_bytes=dkdv_bytes,
+                dq_bytes=dq_bytes, reduce_bytes=reduce_bytes, t_q=t_q, t_k=t_k, q_rows=q_rows)
 
 
 def cpu_baseline(x, budget_s: float):
@@ -186,7 +192,8 @@ def main():
     out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
                dq_accum=torch.empty(q.shape, dtype=torch.float32, device="cuda"),
                delta=torch.empty((H, att.total_q), dtype=torch.float32, device="cuda"))
-    stages = (J.JFA_BWD_PREPROCESS, J.JFA_BWD_MAIN, J.JFA_BWD_FINISH)
+    stages = (J.JFA_BWD_PREPROCESS, J.JFA_BWD_DKDV, J.JFA_BWD_DQ, J.JFA_BWD_DQ_REDUCE)
+    nev = len(stages) + 2
 
     def step(ev=None):
         if ev is not None:
@@ -197,7 +204,7 @@ def main():
                 ev[1 + i].record()
             att.backward(q, k, v, o, lse, do, out, stages=s)
         if ev is not None:
-            ev[4].record()
+            ev[-1].record()
 
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib << 20
@@ -210,7 +217,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -218,19 +225,20 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    names = ("fwd", "bwd_pre", "bwd_main", "bwd_finish")
+    names = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq", "bwd_dq_reduce")
     per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in events])) for j, n in enumerate(names)}
 
     flop = model["fwd_flop"] + model["bwd_flop"]
     value = flop / (ms_step * 1e-3) / 1e12
     wl_name = w.name
     fwd_tf = model["fwd_flop"] / (per["fwd"] * 1e-3) / 1e12
-    bwd_ms = per["bwd_pre"] + per["bwd_main"] + per["bwd_finish"]
+    bwd_ms = per["bwd_pre"] + per["bwd_dkdv"] + per["bwd_dq"] + per["bwd_dq_reduce"]
     bwd_tf = model["bwd_flop"] / (bwd_ms * 1e-3) / 1e12
 
     kernels = {
         "fwd": ("fwd.hip", model["fwd_flop"], model["fwd_bytes"]),
-        "bwd_main": ("bwd.hip", model["bwd_flop"], model["main_bytes"]),
+        "bwd_dkdv": ("bwd.hip", model["dkdv_flop"], model["dkdv_bytes"]),
+        "bwd_dq": ("dq.hip", model["dq_flop"], model["dq_bytes"]),
     }
     dom = max(kernels, key=lambda n: per[n])
     _, kflop, kbytes = kernels[dom]
@@ -268,7 +276,8 @@ def main():
                    "lengths": w.lengths, "seed": w.seed, "total_kv": model["t_k"],
                    "total_q": model["t_q"],
                    "fwd_workers": att.fwd_plan.info.num_workers,
-                   "bwd_workers": att.bwd_plan.info.num_workers},
+                   "bwd_workers": att.bwd_plan.info.num_workers,
+                   "dq_workers": att.dq_plan.info.num_workers},
         "pct_mfma_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "fwd_tflops": fwd_tf,
         "bwd_tflops": bwd_tf,

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define JFA_ABI_VERSION 1
+#define JFA_ABI_VERSION 2
 
 /* status codes */
 #define JFA_OK                 0
@@ -177,25 +177,45 @@ int32_t jfa_fwd(const jfa_problem* prob, const jfa_plan_info* info,
                 const void* q, const void* k, const void* v,
                 void* o, float* lse, void* stream);
 
-/* Bytes of scratch jfa_bwd needs for this BWD plan (may be 0). */
-int32_t jfa_bwd_workspace_bytes(const jfa_problem* prob, const jfa_plan_info* info,
+/* A plan on the device: the sizes of jfa_plan_build's output and device
+ * copies of its arrays (sparse_ptr / sparse_idx NULL when dense). The caller
+ * owns everything it points to. */
+typedef struct jfa_device_plan {
+    const jfa_plan_info* info;
+    const int32_t* worker_ptr;
+    const int32_t* tiles;
+    const int32_t* sparse_ptr;
+    const int32_t* sparse_idx;
+} jfa_device_plan;
+
+/* Bytes of device scratch jfa_bwd needs for this DQ plan: with broadcast Q,
+ * one fp32 [256][head_dim] partial per dQ worker (dq_info->num_workers of
+ * them); 0 with per-sequence Q. */
+int32_t jfa_bwd_workspace_bytes(const jfa_problem* prob, const jfa_plan_info* dq_info,
                                 int64_t* bytes);
 
 /*
  * Backward pass: dQ, dK, dV for the loss sum(dO * O), given the forward's O
- * and LSE. Enqueues, in stream order: a preprocess kernel (delta =
- * rowsum(dO*O) in fp32, dq_accum cleared), the persistent main kernel walking
- * a BWD plan (dK, dV accumulated per KV tile in registers; per-workgroup dQ
- * partials staged through LDS and added into dq_accum in fp32), and a kernel
- * rounding dq_accum to bf16 dq. In broadcast mode dq is the sum over all
- * sequences (theclarity.today, second paragraph). dq_accum and delta are
- * outputs too. workspace may be NULL when jfa_bwd_workspace_bytes gives 0.
+ * and LSE. kv_plan is a BWD plan (KV tiles), dq_plan a DQ plan (Q tiles), both
+ * for this problem and these offsets. Enqueues, in stream order:
+ *   1. preprocess: delta = rowsum(dO * O), fp32 [H, T_q];
+ *   2. dK/dV: KV-stationary persistent kernel over kv_plan, dK and dV
+ *      accumulated per KV tile in registers and written as bf16;
+ *   3. dQ: Q-stationary persistent kernel over dq_plan (the forward's tiles),
+ *      dQ accumulated in registers while the K/V blocks stream past. With
+ *      per-sequence Q each tile writes its rows of dq_accum (fp32) and dq
+ *      (bf16). With broadcast Q, dQ sums over all sequences (theclarity.today,
+ *      second paragraph): each dQ worker adds up its tiles, which all belong
+ *      to one (head, Q tile) group, into one fp32 partial in the workspace;
+ *   4. dQ reduce (broadcast Q only): the partials of each group are added in
+ *      worker order into dq_accum (fp32 [lq, H, D]) and dq (bf16). The result
+ *      does not depend on timing; no atomics are used anywhere.
+ * dq_accum and delta are outputs too. workspace: jfa_bwd_workspace_bytes
+ * bytes, 16-byte aligned (may be NULL when that is 0).
  */
-int32_t jfa_bwd(const jfa_problem* prob, const jfa_plan_info* info,
-                const int32_t* d_worker_ptr, const int32_t* d_tiles,
-                const int32_t* d_sparse_ptr, const int32_t* d_sparse_idx,
-                const int32_t* d_q_offsets, const int32_t* d_kv_offsets,
-                const void* q, const void* k, const void* v,
+int32_t jfa_bwd(const jfa_problem* prob, const jfa_device_plan* kv_plan,
+                const jfa_device_plan* dq_plan, const int32_t* d_q_offsets,
+                const int32_t* d_kv_offsets, const void* q, const void* k, const void* v,
                 const void* o, const float* lse, const void* d_o,
                 void* dq, void* dk, void* dv, float* dq_accum, float* delta,
                 void* workspace, int64_t workspace_bytes, void* stream);
@@ -204,19 +224,18 @@ int32_t jfa_bwd(const jfa_problem* prob, const jfa_plan_info* info,
  * The same backward, one stage at a time, for callers that interleave other
  * work or time each launch: `stages` is a bitwise OR of the JFA_BWD_* flags;
  * the selected launches are enqueued in stage order. Each stage expects the
- * outputs of the stages before it to be in place (delta and a cleared
- * dq_accum for MAIN, the summed dq_accum for FINISH). Arguments are the same
- * as jfa_bwd and are validated the same way whatever the stages.
+ * outputs of the stages before it to be in place (delta for DKDV and DQ, the
+ * dQ partials for DQ_REDUCE). Arguments are the same as jfa_bwd and are
+ * validated the same way whatever the stages.
  */
-#define JFA_BWD_PREPROCESS 1   /* delta = rowsum(dO*O); dq_accum = 0        */
-#define JFA_BWD_MAIN       2   /* dK, dV written; dQ partials into dq_accum */
-#define JFA_BWD_FINISH     4   /* dq = bf16(dq_accum)                       */
-#define JFA_BWD_ALL        7
-int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_plan_info* info,
-                       const int32_t* d_worker_ptr, const int32_t* d_tiles,
-                       const int32_t* d_sparse_ptr, const int32_t* d_sparse_idx,
-                       const int32_t* d_q_offsets, const int32_t* d_kv_offsets,
-                       const void* q, const void* k, const void* v,
+#define JFA_BWD_PREPROCESS 1   /* delta = rowsum(dO*O)                         */
+#define JFA_BWD_DKDV       2   /* dK, dV                                       */
+#define JFA_BWD_DQ         4   /* dQ (per-sequence Q) or dQ partials (broadcast) */
+#define JFA_BWD_DQ_REDUCE  8   /* broadcast Q: dq_accum, dq from the partials  */
+#define JFA_BWD_ALL        15
+int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device_plan* kv_plan,
+                       const jfa_device_plan* dq_plan, const int32_t* d_q_offsets,
+                       const int32_t* d_kv_offsets, const void* q, const void* k, const void* v,
                        const void* o, const float* lse, const void* d_o,
                        void* dq, void* dk, void* dv, float* dq_accum, float* delta,
                        void* workspace, int64_t workspace_bytes, void* stream);

@@ -35,9 +35,10 @@ EXPORTS = (
     "jfa_bwd_workspace_bytes", "jfa_bwd", "jfa_bwd_stages",
 )
 JFA_BWD_PREPROCESS = 1
-JFA_BWD_MAIN = 2
-JFA_BWD_FINISH = 4
-JFA_BWD_ALL = 7
+JFA_BWD_DKDV = 2
+JFA_BWD_DQ = 4
+JFA_BWD_DQ_REDUCE = 8
+JFA_BWD_ALL = 15
 
 
 class JfaProblem(ctypes.Structure):
@@ -55,6 +56,12 @@ class JfaPlanInfo(ctypes.Structure):
                 ("total_kv", ctypes.c_int32), ("sparse_rows", ctypes.c_int32),
                 ("sparse_nnz", ctypes.c_int32), ("max_work", ctypes.c_int32),
                 ("total_work", ctypes.c_int64)]
+
+
+class JfaDevicePlan(ctypes.Structure):
+    _fields_ = [("info", ctypes.POINTER(JfaPlanInfo)), ("worker_ptr", ctypes.c_void_p),
+                ("tiles", ctypes.c_void_p), ("sparse_ptr", ctypes.c_void_p),
+                ("sparse_idx", ctypes.c_void_p)]
 
 
 class JfaError(RuntimeError):
@@ -81,6 +88,7 @@ def _lib():
         lib = ctypes.CDLL(LIB_PATH)
         i32, i64 = ctypes.c_int32, ctypes.c_int64
         prob, info = ctypes.POINTER(JfaProblem), ctypes.POINTER(JfaPlanInfo)
+        dplan = ctypes.POINTER(JfaDevicePlan)
         sig = {
             "jfa_abi_version": (i32, []),
             "jfa_status_string": (ctypes.c_char_p, [i32]),
@@ -91,8 +99,8 @@ def _lib():
             "jfa_plan_build": (i32, [prob, _P, _P, _P, i32, i32, info, _P, _P, _P, _P]),
             "jfa_fwd": (i32, [prob, info] + [_P] * 12),
             "jfa_bwd_workspace_bytes": (i32, [prob, info, ctypes.POINTER(i64)]),
-            "jfa_bwd": (i32, [prob, info] + [_P] * 18 + [i64, _P]),
-            "jfa_bwd_stages": (i32, [i32, prob, info] + [_P] * 18 + [i64, _P]),
+            "jfa_bwd": (i32, [prob, dplan, dplan] + [_P] * 14 + [i64, _P]),
+            "jfa_bwd_stages": (i32, [i32, prob, dplan, dplan] + [_P] * 14 + [i64, _P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -237,35 +245,40 @@ def jfa_fwd(prob: Problem, plan: DevicePlan, q_offsets, kv_offsets, q, k, v, o, 
                           _stream(stream)), "jfa_fwd")
 
 
-def jfa_bwd_workspace_bytes(prob: Problem, info: JfaPlanInfo) -> int:
+def jfa_bwd_workspace_bytes(prob: Problem, dq_info: JfaPlanInfo) -> int:
+    """Device scratch bytes jfa_bwd needs for a DQ plan."""
     n = ctypes.c_int64(0)
     cp = prob.c()
-    _check(_lib().jfa_bwd_workspace_bytes(ctypes.byref(cp), ctypes.byref(info), ctypes.byref(n)),
-           "jfa_bwd_workspace_bytes")
+    _check(_lib().jfa_bwd_workspace_bytes(ctypes.byref(cp), ctypes.byref(dq_info),
+                                          ctypes.byref(n)), "jfa_bwd_workspace_bytes")
     return n.value
 
 
-def jfa_bwd(prob: Problem, plan: DevicePlan, q_offsets, kv_offsets, q, k, v, o, lse, d_o,
-            dq, dk, dv, dq_accum, delta, workspace=None, workspace_bytes: int = 0,
-            stream=None) -> None:
-    """Enqueue the backward (preprocess, main, dQ convert) on ``stream``."""
-    jfa_bwd_stages(JFA_BWD_ALL, prob, plan, q_offsets, kv_offsets, q, k, v, o, lse, d_o, dq, dk,
-                   dv, dq_accum, delta, workspace, workspace_bytes, stream)
+def _c_plan(plan: DevicePlan) -> JfaDevicePlan:
+    return JfaDevicePlan(ctypes.pointer(plan.info), _dev_ptr(plan.worker_ptr), _dev_ptr(plan.tiles),
+                         _dev_ptr(plan.sparse_ptr), _dev_ptr(plan.sparse_idx))
 
 
-def jfa_bwd_stages(stages: int, prob: Problem, plan: DevicePlan, q_offsets, kv_offsets, q, k, v,
-                   o, lse, d_o, dq, dk, dv, dq_accum, delta, workspace=None,
-                   workspace_bytes: int = 0, stream=None) -> None:
+def jfa_bwd(prob: Problem, kv_plan: DevicePlan, dq_plan: DevicePlan, q_offsets, kv_offsets, q, k,
+            v, o, lse, d_o, dq, dk, dv, dq_accum, delta, workspace=None,
+            workspace_bytes: int = 0, stream=None) -> None:
+    """Enqueue the whole backward (preprocess, dK/dV, dQ, dQ reduce) on ``stream``."""
+    jfa_bwd_stages(JFA_BWD_ALL, prob, kv_plan, dq_plan, q_offsets, kv_offsets, q, k, v, o, lse,
+                   d_o, dq, dk, dv, dq_accum, delta, workspace, workspace_bytes, stream)
+
+
+def jfa_bwd_stages(stages: int, prob: Problem, kv_plan: DevicePlan, dq_plan: DevicePlan,
+                   q_offsets, kv_offsets, q, k, v, o, lse, d_o, dq, dk, dv, dq_accum, delta,
+                   workspace=None, workspace_bytes: int = 0, stream=None) -> None:
     """Enqueue the selected backward stages (JFA_BWD_* flags) on ``stream``."""
     cp = prob.c()
-    _check(_lib().jfa_bwd_stages(stages, ctypes.byref(cp), ctypes.byref(plan.info),
-                                 _dev_ptr(plan.worker_ptr),
-                          _dev_ptr(plan.tiles), _dev_ptr(plan.sparse_ptr),
-                          _dev_ptr(plan.sparse_idx), _dev_ptr(q_offsets), _dev_ptr(kv_offsets),
-                          _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(o), _dev_ptr(lse),
-                          _dev_ptr(d_o), _dev_ptr(dq), _dev_ptr(dk), _dev_ptr(dv),
-                          _dev_ptr(dq_accum), _dev_ptr(delta), _dev_ptr(workspace),
-                          int(workspace_bytes), _stream(stream)), "jfa_bwd_stages")
+    kp, qp = _c_plan(kv_plan), _c_plan(dq_plan)
+    _check(_lib().jfa_bwd_stages(stages, ctypes.byref(cp), ctypes.byref(kp), ctypes.byref(qp),
+                                 _dev_ptr(q_offsets), _dev_ptr(kv_offsets), _dev_ptr(q),
+                                 _dev_ptr(k), _dev_ptr(v), _dev_ptr(o), _dev_ptr(lse),
+                                 _dev_ptr(d_o), _dev_ptr(dq), _dev_ptr(dk), _dev_ptr(dv),
+                                 _dev_ptr(dq_accum), _dev_ptr(delta), _dev_ptr(workspace),
+                                 int(workspace_bytes), _stream(stream)), "jfa_bwd_stages")
 
 
 # ------------------------------------------------------- convenience wrappers
@@ -284,7 +297,7 @@ class JaggedAttention:
 
     def __init__(self, prob: Problem, kv_offsets, q_offsets=None, block_mask=None,
                  fwd_workers: Optional[int] = None, bwd_workers: Optional[int] = None,
-                 device="cuda"):
+                 dq_workers: Optional[int] = None, device="cuda"):
         import torch
         self.prob = prob
         self.device = device
@@ -293,13 +306,16 @@ class JaggedAttention:
                                             JFA_PASS_FWD, fwd_workers or cus)
         self.bwd_plan_host = jfa_plan_build(prob, q_offsets, kv_offsets, block_mask,
                                             JFA_PASS_BWD, bwd_workers or cus)
+        self.dq_plan_host = jfa_plan_build(prob, q_offsets, kv_offsets, block_mask,
+                                           JFA_PASS_DQ, dq_workers or cus)
         self.fwd_plan = to_device(self.fwd_plan_host, device)
         self.bwd_plan = to_device(self.bwd_plan_host, device)
+        self.dq_plan = to_device(self.dq_plan_host, device)
         self.kv_offsets = torch.from_numpy(_i32(kv_offsets)).to(device)
         self.q_offsets = None if q_offsets is None else torch.from_numpy(_i32(q_offsets)).to(device)
         self.total_q = self.fwd_plan.info.total_q
         self.total_kv = self.fwd_plan.info.total_kv
-        self.ws_bytes = jfa_bwd_workspace_bytes(prob, self.bwd_plan.info)
+        self.ws_bytes = jfa_bwd_workspace_bytes(prob, self.dq_plan.info)
         self.workspace = (torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
                           if self.ws_bytes else None)
 
@@ -320,7 +336,7 @@ class JaggedAttention:
                        dq_accum=torch.empty(q.shape, dtype=torch.float32, device=self.device),
                        delta=torch.empty((self.prob.num_heads, self.total_q), dtype=torch.float32,
                                          device=self.device))
-        jfa_bwd_stages(stages, self.prob, self.bwd_plan, self.q_offsets, self.kv_offsets, q, k, v,
-                       o, lse, d_o, out["dq"], out["dk"], out["dv"], out["dq_accum"],
-                       out["delta"], self.workspace, self.ws_bytes)
+        jfa_bwd_stages(stages, self.prob, self.bwd_plan, self.dq_plan, self.q_offsets,
+                       self.kv_offsets, q, k, v, o, lse, d_o, out["dq"], out["dk"], out["dv"],
+                       out["dq_accum"], out["delta"], self.workspace, self.ws_bytes)
         return out

@@ -34,8 +34,9 @@ int32_t check_common(const jfa_problem* p, const jfa_plan_info* info, int32_t pa
     if (st) return st;
     if (info == nullptr) return JFA_ERR_INVALID_ARG;
     if (info->pass != pass) return JFA_ERR_PLAN_MISMATCH;
-    const int32_t bm = pass == JFA_PASS_FWD ? jfa::kFwdBlockM : jfa::kBwdBlockM;
-    const int32_t bn = pass == JFA_PASS_FWD ? jfa::kFwdBlockN : jfa::kBwdBlockN;
+    const bool qtiles = pass != JFA_PASS_BWD;
+    const int32_t bm = qtiles ? jfa::kFwdBlockM : jfa::kBwdBlockM;
+    const int32_t bn = qtiles ? jfa::kFwdBlockN : jfa::kBwdBlockN;
     if (info->block_m != bm || info->block_n != bn) return JFA_ERR_PLAN_MISMATCH;
     if (info->num_workers < 1 || info->num_tiles < 0 || info->total_q < 0 || info->total_kv < 0)
         return JFA_ERR_PLAN_MISMATCH;
@@ -43,10 +44,9 @@ int32_t check_common(const jfa_problem* p, const jfa_plan_info* info, int32_t pa
     const bool sparse = p->mask_q_blocks != 0;
     if (sparse) {
         const int64_t rows =
-            (int64_t)p->batch * (pass == JFA_PASS_FWD
-                                     ? (p->mask_q_blocks + jfa::kFwdBlockM / jfa::kMaskBlock - 1) /
-                                           (jfa::kFwdBlockM / jfa::kMaskBlock)
-                                     : p->mask_kv_blocks);
+            (int64_t)p->batch * (qtiles ? (p->mask_q_blocks + jfa::kFwdBlockM / jfa::kMaskBlock - 1) /
+                                              (jfa::kFwdBlockM / jfa::kMaskBlock)
+                                        : p->mask_kv_blocks);
         if (info->sparse_rows != rows) return JFA_ERR_PLAN_MISMATCH;
         if (d_sparse_ptr == nullptr || (info->sparse_nnz > 0 && d_sparse_idx == nullptr))
             return JFA_ERR_INVALID_ARG;
@@ -138,34 +138,48 @@ int32_t jfa_fwd(const jfa_problem* prob, const jfa_plan_info* info, const int32_
                                       stream));
 }
 
-int32_t jfa_bwd_workspace_bytes(const jfa_problem* prob, const jfa_plan_info* info,
+int32_t jfa_bwd_workspace_bytes(const jfa_problem* prob, const jfa_plan_info* dq_info,
                                 int64_t* bytes) {
-    if (bytes == nullptr || info == nullptr) return JFA_ERR_INVALID_ARG;
+    if (bytes == nullptr || dq_info == nullptr) return JFA_ERR_INVALID_ARG;
     int32_t st = jfa::check_problem(prob);
     if (st) return st;
-    if (info->pass != JFA_PASS_BWD) return JFA_ERR_PLAN_MISMATCH;
-    *bytes = 0;
+    if (dq_info->pass != JFA_PASS_DQ || dq_info->num_workers < 1) return JFA_ERR_PLAN_MISMATCH;
+    // broadcast Q: one fp32 [256][D] partial per dQ worker
+    *bytes = prob->broadcast_q
+                 ? (int64_t)dq_info->num_workers * jfa::kFwdBlockM * prob->head_dim * 4
+                 : 0;
     return JFA_OK;
 }
 
-int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_plan_info* info,
-                       const int32_t* d_worker_ptr, const int32_t* d_tiles,
-                       const int32_t* d_sparse_ptr, const int32_t* d_sparse_idx,
-                       const int32_t* d_q_offsets, const int32_t* d_kv_offsets, const void* q,
-                       const void* k, const void* v, const void* o, const float* lse,
-                       const void* d_o, void* dq, void* dk, void* dv, float* dq_accum,
-                       float* delta, void* workspace, int64_t workspace_bytes, void* stream) {
+static int32_t check_plan(const jfa_problem* prob, const jfa_device_plan* plan, int32_t pass,
+                          const int32_t* d_q_offsets, const int32_t* d_kv_offsets) {
+    if (plan == nullptr) return JFA_ERR_INVALID_ARG;
+    return check_common(prob, plan->info, pass, plan->worker_ptr, plan->tiles, plan->sparse_ptr,
+                        plan->sparse_idx, d_q_offsets, d_kv_offsets);
+}
+
+int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device_plan* kv_plan,
+                       const jfa_device_plan* dq_plan, const int32_t* d_q_offsets,
+                       const int32_t* d_kv_offsets, const void* q, const void* k, const void* v,
+                       const void* o, const float* lse, const void* d_o, void* dq, void* dk,
+                       void* dv, float* dq_accum, float* delta, void* workspace,
+                       int64_t workspace_bytes, void* stream) {
     if (stages < 0 || stages > JFA_BWD_ALL) return JFA_ERR_INVALID_ARG;
-    int32_t st = check_common(prob, info, JFA_PASS_BWD, d_worker_ptr, d_tiles, d_sparse_ptr,
-                              d_sparse_idx, d_q_offsets, d_kv_offsets);
+    int32_t st = check_plan(prob, kv_plan, JFA_PASS_BWD, d_q_offsets, d_kv_offsets);
     if (st) return st;
+    st = check_plan(prob, dq_plan, JFA_PASS_DQ, d_q_offsets, d_kv_offsets);
+    if (st) return st;
+    const jfa_plan_info* ki = kv_plan->info;
+    const jfa_plan_info* qi = dq_plan->info;
+    if (ki->total_q != qi->total_q || ki->total_kv != qi->total_kv) return JFA_ERR_PLAN_MISMATCH;
     int64_t need = 0;
-    st = jfa_bwd_workspace_bytes(prob, info, &need);
+    st = jfa_bwd_workspace_bytes(prob, qi, &need);
     if (st) return st;
-    if (workspace_bytes < need || (need > 0 && workspace == nullptr)) return JFA_ERR_WORKSPACE;
+    if (workspace_bytes < need || (need > 0 && (workspace == nullptr || !aligned16(workspace))))
+        return JFA_ERR_WORKSPACE;
     const int64_t hd = (int64_t)prob->num_heads * prob->head_dim;
-    const int64_t q_rows = prob->broadcast_q ? prob->lq : info->total_q;
-    const int64_t tq = info->total_q, tk = info->total_kv;
+    const int64_t q_rows = prob->broadcast_q ? prob->lq : ki->total_q;
+    const int64_t tq = ki->total_q, tk = ki->total_kv;
     if (!tensor_ok(q, q_rows * hd) || !tensor_ok(k, tk * hd) || !tensor_ok(v, tk * hd) ||
         !tensor_ok(o, tq * hd) || !tensor_ok(d_o, tq * hd) || !tensor_ok(dq, q_rows * hd) ||
         !tensor_ok(dk, tk * hd) || !tensor_ok(dv, tk * hd) || !tensor_ok(dq_accum, q_rows * hd))
@@ -173,13 +187,15 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_plan_i
     if (tq > 0 && (lse == nullptr || delta == nullptr || !aligned4(lse) || !aligned4(delta)))
         return JFA_ERR_INVALID_ARG;
     if (tq == 0 && q_rows == 0 && tk == 0) return JFA_OK;
+    const jfa::Mode mode = mode_of(prob);
+    const bool bcast = prob->broadcast_q != 0;
 
     jfa::BwdArgs a;
-    a.worker_ptr = d_worker_ptr;
-    a.tiles = d_tiles;
-    a.sp_ptr = d_sparse_ptr;
-    a.sp_idx = d_sparse_idx;
-    a.q_off = prob->broadcast_q ? nullptr : d_q_offsets;
+    a.worker_ptr = kv_plan->worker_ptr;
+    a.tiles = kv_plan->tiles;
+    a.sp_ptr = kv_plan->sparse_ptr;
+    a.sp_idx = kv_plan->sparse_idx;
+    a.q_off = bcast ? nullptr : d_q_offsets;
     a.kv_off = d_kv_offsets;
     a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint16_t*>(k);
@@ -187,32 +203,73 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_plan_i
     a.o = static_cast<const uint16_t*>(o);
     a.lse = lse;
     a.d_o = static_cast<const uint16_t*>(d_o);
-    a.dq = static_cast<uint16_t*>(dq);
     a.dk = static_cast<uint16_t*>(dk);
     a.dv = static_cast<uint16_t*>(dv);
-    a.dq_accum = dq_accum;
     a.delta = delta;
     a.num_heads = prob->num_heads;
     a.lq = prob->lq;
-    a.total_q = info->total_q;
-    a.q_rows = (int32_t)q_rows;
+    a.total_q = ki->total_q;
     a.mask_kv_blocks = prob->mask_kv_blocks;
-    a.num_workers = info->num_tiles > 0 ? info->num_workers : 0;  // 0: no main launch
+    a.num_workers = ki->num_tiles > 0 ? ki->num_workers : 0;  // 0: no dK/dV launch
     a.scale = prob->softmax_scale;
     a.scale_log2 = prob->softmax_scale * 1.4426950408889634f;
-    return hip_status(jfa::launch_bwd(a, prob->head_dim, mode_of(prob), prob->broadcast_q != 0,
-                                      stages, stream));
+    st = hip_status(jfa::launch_bwd(a, prob->head_dim, mode, bcast,
+                                    stages & (JFA_BWD_PREPROCESS | JFA_BWD_DKDV), stream));
+    if (st) return st;
+
+    if ((stages & JFA_BWD_DQ) && qi->num_tiles > 0) {
+        jfa::DqArgs d;
+        d.worker_ptr = dq_plan->worker_ptr;
+        d.tiles = dq_plan->tiles;
+        d.sp_ptr = dq_plan->sparse_ptr;
+        d.sp_idx = dq_plan->sparse_idx;
+        d.q_off = bcast ? nullptr : d_q_offsets;
+        d.kv_off = d_kv_offsets;
+        d.q = a.q;
+        d.k = a.k;
+        d.v = a.v;
+        d.d_o = a.d_o;
+        d.lse = lse;
+        d.delta = delta;
+        d.dq = static_cast<uint16_t*>(dq);
+        d.dq_accum = dq_accum;
+        d.partial = static_cast<float*>(workspace);
+        d.num_heads = prob->num_heads;
+        d.lq = prob->lq;
+        d.total_q = qi->total_q;
+        d.mask_q_blocks = prob->mask_q_blocks;
+        d.num_workers = qi->num_workers;
+        d.scale = prob->softmax_scale;
+        d.scale_log2 = a.scale_log2;
+        st = hip_status(jfa::launch_dq(d, prob->head_dim, mode, bcast, stream));
+        if (st) return st;
+    }
+    if ((stages & JFA_BWD_DQ_REDUCE) && bcast) {
+        jfa::DqReduceArgs r;
+        r.worker_ptr = dq_plan->worker_ptr;
+        r.partial = static_cast<const float*>(workspace);
+        r.dq_accum = dq_accum;
+        r.dq = static_cast<uint16_t*>(dq);
+        r.num_heads = prob->num_heads;
+        r.lq = prob->lq;
+        r.num_workers = qi->num_workers;
+        if (qi->num_tiles > 0 && r.worker_ptr == nullptr) return JFA_ERR_INVALID_ARG;
+        if (qi->num_tiles == 0) r.worker_ptr = nullptr;
+        st = hip_status(jfa::launch_dq_reduce(r, prob->head_dim, stream));
+        if (st) return st;
+    }
+    return JFA_OK;
 }
 
-int32_t jfa_bwd(const jfa_problem* prob, const jfa_plan_info* info, const int32_t* d_worker_ptr,
-                const int32_t* d_tiles, const int32_t* d_sparse_ptr, const int32_t* d_sparse_idx,
-                const int32_t* d_q_offsets, const int32_t* d_kv_offsets, const void* q,
-                const void* k, const void* v, const void* o, const float* lse, const void* d_o,
-                void* dq, void* dk, void* dv, float* dq_accum, float* delta, void* workspace,
-                int64_t workspace_bytes, void* stream) {
-    return jfa_bwd_stages(JFA_BWD_ALL, prob, info, d_worker_ptr, d_tiles, d_sparse_ptr,
-                          d_sparse_idx, d_q_offsets, d_kv_offsets, q, k, v, o, lse, d_o, dq, dk,
-                          dv, dq_accum, delta, workspace, workspace_bytes, stream);
+int32_t jfa_bwd(const jfa_problem* prob, const jfa_device_plan* kv_plan,
+                const jfa_device_plan* dq_plan, const int32_t* d_q_offsets,
+                const int32_t* d_kv_offsets, const void* q, const void* k, const void* v,
+                const void* o, const float* lse, const void* d_o, void* dq, void* dk, void* dv,
+                float* dq_accum, float* delta, void* workspace, int64_t workspace_bytes,
+                void* stream) {
+    return jfa_bwd_stages(JFA_BWD_ALL, prob, kv_plan, dq_plan, d_q_offsets, d_kv_offsets, q, k, v,
+                          o, lse, d_o, dq, dk, dv, dq_accum, delta, workspace, workspace_bytes,
+                          stream);
 }
 
 }  // extern "C"

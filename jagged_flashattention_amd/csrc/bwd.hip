@@ -1,31 +1,22 @@
-// Jagged FlashAttention backward for gfx950.
+// Jagged FlashAttention backward for gfx950: preprocess and the KV-stationary
+// dK/dV pass (the dQ pass is Q-stationary, in its own kernel).
 //
-// Three launches in stream order:
-//   1. preprocess: delta = rowsum(dO * O) in fp32, dq_accum cleared;
-//   2. main: one persistent workgroup per worker walking a KV-tile plan.
-//      A workgroup owns a 128-key KV tile (32 keys per wave) and streams the
-//      64-row Q/dO blocks that see it. dK and dV are accumulated per KV tile
-//      in registers. dS of the whole tile is staged through LDS and the
-//      workgroup's dQ partial for the Q block (all 128 keys reduced inside
-//      the MFMA) is added into the fp32 dq_accum;
-//   3. convert: dq = bf16(dq_accum).
-// In broadcast-Q mode every KV tile of every sequence adds into the same
-// [lq, H, D] dQ: the contended cross-program reduction the pages single out
-// as the main backward bottleneck ("Meta's 3.2K-line Triton kernel outruns
-// FlashAttention-4 on jagged Blackwell attention" (theclarity.today), second
-// paragraph; "Meta's TLX Jagged Flash Attention Beats FA4 on Blackwell"
-// (ainewsbites.com), section "Optimizations layered on top", multi-stage dQ
-// staging).
+//   1. preprocess: delta = rowsum(dO * O) in fp32 (the standard FlashAttention
+//      backward step; the pages only name the backward's persistent, tiled
+//      structure: "Meta's TLX Jagged Flash Attention Beats FA4 on Blackwell"
+//      (ainewsbites.com), section "Optimizations layered on top");
+//   2. dK/dV: one persistent workgroup per worker walking a KV-tile plan. A
+//      workgroup owns a 128-key KV tile (32 keys per wave) and streams the
+//      64-row Q/dO blocks that see it; dK and dV are accumulated per KV tile
+//      in registers and written once, as whole rows through LDS.
 //
 // Per Q block and wave (keys on lanes, query rows in registers):
 //   S   = Q K^T          A = Q rows from LDS,    B = K (registers)
 //   P   = exp2(S*scale*log2e - LSE*log2e)
-//   dP  = dO V^T         A = dO rows from LDS,   B = V (registers)
+//   dP  = dO V^T         A = dO rows from LDS,   B = V rows from LDS
 //   dS  = P * (dP - delta)
-//   dV^T += dO^T P       A = dO^T via transposed LDS reads, B = P
-//   dK^T += Q^T dS       A = Q^T via transposed LDS reads,  B = dS
-//   dQ   = dS K          A = scale*dS via transposed reads of the staged dS^T,
-//                        B = K via transposed reads of the K tile
+//   dV^T += dO^T P       A = dO^T from LDS (rows in sigma order), B = P
+//   dK^T += Q^T dS       A = Q^T from LDS (rows in sigma order),  B = dS
 #include <type_traits>
 
 #include "device.h"
@@ -43,21 +34,17 @@ constexpr int kPad = 8;
 //    dK/dV staging): 16-byte chunk c of row r is stored at chunk c ^ swz(r),
 //    swz(r) = (r + r/CH) mod CH, CH = D/8 chunks per row;
 //  - Q^T, dO^T: [d][64 rows] padded by 16 bytes per row;
-//  - K^T: [d][128 keys], 256-byte rows, chunk c of row d stored at
-//    c ^ ((d/8 ^ d) mod 16);
-//  - rows of Q^T/dO^T and keys of K^T are stored in the "sigma" order of each
-//    16-group (0-3, 8-11, 4-7, 12-15), so that the 8 values one lane feeds to
-//    a 32x32x16 MFMA (rows 16c + sigma(8h..8h+7)) are one 16-byte read and
-//    match the accumulator registers they are multiplied with.
+//  - rows of Q^T/dO^T are stored in the "sigma" order of each 16-group (0-3,
+//    8-11, 4-7, 12-15), so that the 8 values one lane feeds to a 32x32x16
+//    MFMA (rows 16c + sigma(8h..8h+7)) are one 16-byte read and match the
+//    accumulator registers they are multiplied with.
 // Region R holds the Q-block tiles during the loop, the natural K tile during
 // the tile prologue, and the dK/dV staging in the tile epilogue. The natural
 // V tile stays in its own region for the whole tile (its rows are the B
 // operand of dP = dO V^T).
 template <int D>
 struct BwdLds {
-    static constexpr int KT = 0;                                   // K^T
-    static constexpr int KT_BYTES = D * kBwdBlockN * 2;
-    static constexpr int R = KT + KT_BYTES;
+    static constexpr int R = 0;
     static constexpr int QN = R;                                    // [64][D]
     static constexpr int DN = QN + kBwdBlockM * D * 2;              // [64][D]
     static constexpr int QT = DN + kBwdBlockM * D * 2;              // [D][72]
@@ -69,8 +56,7 @@ struct BwdLds {
                                        ? (DT + D * (kBwdBlockM + 8) * 2 - R)
                                        : 2 * kBwdBlockN * D * 2;
     static constexpr int VN = R + R_BYTES;                          // [128][D]
-    static constexpr int DST = VN + kBwdBlockN * D * 2;             // [128][68]
-    static constexpr int LSE = DST + kBwdBlockN * (kBwdBlockM + 4) * 2;
+    static constexpr int LSE = VN + kBwdBlockN * D * 2;
     static constexpr int DELTA = LSE + kBwdBlockM * 4;
     static constexpr int BYTES = DELTA + kBwdBlockM * 4;
 };
@@ -88,15 +74,10 @@ __device__ __forceinline__ int swz(int r) {
     return (r + (r >> SH)) & (CH - 1);
 }
 
-__device__ __forceinline__ int kt_swz(int d) { return ((d >> 3) ^ d) & 15; }
-
 // byte offset of element (row r, element c8*8 + e) of a natural [row][D] tile
 template <int D>
 __device__ __forceinline__ int nat_off(int r, int chunk) {
     return r * D * 2 + ((chunk ^ swz<D>(r)) << 4);
-}
-__device__ __forceinline__ int kt_off(int d, int pos) {
-    return d * (kBwdBlockN * 2) + (((pos >> 3) ^ kt_swz(d)) << 4) + ((pos & 7) << 1);
 }
 
 // 4 rows x 8 bf16 (one 16-byte chunk per row) -> 8 columns x 4 rows
@@ -111,7 +92,7 @@ __device__ __forceinline__ void transpose4x8(const u32x4 (&x)[4], u32x2 (&y)[8])
 }
 
 template <int D, int MODE, bool BCAST>
-__global__ void __launch_bounds__(kThreads) bwd_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(kThreads) dkdv_kernel(BwdArgs a) {
     using LY = BwdLds<D>;
     __shared__ __attribute__((aligned(16))) char smem[LY::BYTES];
     constexpr int KC = D / 16;
@@ -126,9 +107,6 @@ __global__ void __launch_bounds__(kThreads) bwd_kernel(BwdArgs a) {
     const int lr = lane & 31, hf = lane >> 5;
     const int H = a.num_heads;
     const int64_t rs = (int64_t)H * D;
-    const int g16 = lane >> 4, n16 = lane & 15;
-    const int tr_row = 4 * (g16 >> 1) + (n16 >> 2);
-    const int tr_col = (g16 & 1) * 16 + 4 * (n16 & 3);
     // Q/dO block loader: 4 rows (4qg..4qg+3) x one 16-byte chunk dc per thread
     const int ld_qg = tid & 15, ld_dc = tid >> 4;
     const bool ld_on = ld_dc < CH;
@@ -153,41 +131,32 @@ __global__ void __launch_bounds__(kThreads) bwd_kernel(BwdArgs a) {
         kv_base = row * D * 2 + 16 * (hf ^ (sw & 1));
         kv_x = sw >> 1;
     }
-    // K^T rows read as the dQ B operand by this lane (d = 32nd + lr)
-    int kt_base[2], kt_x[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int d = 32 * (2 * (wave & 1) + j) + lr;
-        const int sw = kt_swz(d);
-        kt_base[j] = LY::KT + d * (kBwdBlockN * 2) + 16 * (hf ^ (sw & 1));
-        kt_x[j] = sw >> 1;
-    }
 
     const int w = worker_id(a.num_workers);
-    const int t_begin = a.worker_ptr[w], t_end = a.worker_ptr[w + 1];
+    const int t_begin = ld_uniform(a.worker_ptr + w), t_end = ld_uniform(a.worker_ptr + w + 1);
 
     for (int ti = t_begin; ti < t_end; ++ti) {
-        const int b = a.tiles[4 * ti + 0];
-        const int hd = a.tiles[4 * ti + 1];
-        const int n = a.tiles[4 * ti + 2];
-        const int work = a.tiles[4 * ti + 3];
-        const int kv0 = a.kv_off[b];
-        const int L = a.kv_off[b + 1] - kv0;
+        const int b = ld_uniform(a.tiles + 4 * ti + 0);
+        const int hd = ld_uniform(a.tiles + 4 * ti + 1);
+        const int n = ld_uniform(a.tiles + 4 * ti + 2);
+        const int work = ld_uniform(a.tiles + 4 * ti + 3);
+        const int kv0 = ld_uniform(a.kv_off + b);
+        const int L = ld_uniform(a.kv_off + b + 1) - kv0;
         int q0, Lq, orow0;
         if (BCAST) {
             q0 = 0;
             Lq = a.lq;
             orow0 = b * a.lq;
         } else {
-            q0 = a.q_off[b];
-            Lq = a.q_off[b + 1] - q0;
+            q0 = ld_uniform(a.q_off + b);
+            Lq = ld_uniform(a.q_off + b + 1) - q0;
             orow0 = q0;
         }
         const int* sp = nullptr;
-        if (MODE == kSparse) sp = a.sp_idx + a.sp_ptr[b * a.mask_kv_blocks + n];
+        if (MODE == kSparse) sp = a.sp_idx + ld_uniform(a.sp_ptr + b * a.mask_kv_blocks + n);
         const int r0 = (MODE == kCausal) ? (n * kBwdBlockN) / kBwdBlockM : 0;
         auto qblk = [&](int i) -> int {
-            if (MODE == kSparse) return 2 * sp[i >> 1] + (i & 1);
+            if (MODE == kSparse) return 2 * ld_uniform(sp + (i >> 1)) + (i & 1);
             return r0 + i;
         };
         const int nmasked = (MODE == kCausal) ? min(2, work) : 0;
@@ -255,8 +224,8 @@ __global__ void __launch_bounds__(kThreads) bwd_kernel(BwdArgs a) {
         };
 
         // ---- tile prologue: the K and V tiles are loaded as whole rows, stored
-        // to LDS (natural K and V, and K^T), then each wave reads its K/V
-        // fragments; block 0 is loaded meanwhile
+        // to LDS, then each wave reads its K fragments; block 0 is loaded
+        // meanwhile
         {
             u32x4 kx[KPASS][4], vx[KPASS][4];
 #pragma unroll
@@ -280,11 +249,6 @@ __global__ void __launch_bounds__(kThreads) bwd_kernel(BwdArgs a) {
                     *(u32x4*)lds(LY::KN + o) = kx[pass][p];
                     *(u32x4*)lds(LY::VN + o) = vx[pass][p];
                 }
-                u32x2 y[8];
-                transpose4x8(kx[pass], y);
-                const int pos = sigma_pos(KPP * pass + 4 * tkg);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) *(u32x2*)lds(LY::KT + kt_off(8 * tdc + e, pos)) = y[e];
             }
         }
         __syncthreads();
@@ -364,55 +328,9 @@ __global__ void __launch_bounds__(kThreads) bwd_kernel(BwdArgs a) {
                         dk_acc[md] = mfma32(qa, sb, dk_acc[md]);
                     }
                 }
-                // stage scale * dS^T[key][row] of the whole tile (the dQ operand)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    f32x4 x;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) x[j] = dp[4 * g + j] * a.scale;
-                    *(u32x2*)lds(LY::DST + (wave * 32 + lr) * (kBwdBlockM + 4) * 2 +
-                                 (32 * mb + 8 * g + 4 * hf) * 2) = __builtin_bit_cast(u32x2, to_bf16x4(x));
-                }
             }
+            // every wave is done with this block's tiles before they are replaced
             __syncthreads();
-            // dQ[row, d] = sum over the tile's 128 keys of dS[row, key] K[key, d]:
-            // this wave computes rows 32*(wave/2).. and d blocks 2*(wave%2), +1
-            {
-                const int mq = wave >> 1;
-                f32x16 dq[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-                for (int c = 0; c < kBwdBlockN / 16; ++c) {
-                    const uint16_t* sp_ = (const uint16_t*)lds(LY::DST + (16 * c + tr_row) * (kBwdBlockM + 4) * 2 +
-                                                               (32 * mq + tr_col) * 2);
-                    const bf16x8 sa = concat(lds_read_tr(sp_), lds_read_tr(sp_ + 8 * (kBwdBlockM + 4)));
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int nd = 2 * (wave & 1) + j;
-                        if (nd < MD) {
-                            const bf16x8 kb = __builtin_bit_cast(
-                                bf16x8, *(const u32x4*)lds(kt_base[j] + 32 * (c ^ kt_x[j])));
-                            dq[j] = mfma32(sa, kb, dq[j]);
-                        }
-                    }
-                }
-                // register rr is query row 32mq + 8(rr/4) + 4hf + rr%4, column d = 32nd + lr
-                const int row0 = r * kBwdBlockM + 32 * mq;
-                const bool full = row0 + 32 <= Lq;   // wave-uniform
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int nd = 2 * (wave & 1) + j;
-                    if (nd < MD) {
-                        float* dqp = a.dq_accum + (int64_t)(q0 + row0 + 4 * hf) * rs + (int64_t)hd * D +
-                                     32 * nd + lr;
-#pragma unroll
-                        for (int rr = 0; rr < 16; ++rr) {
-                            const int qi = row0 + 8 * (rr >> 2) + 4 * hf + (rr & 3);
-                            if (full || qi < Lq)
-                                unsafeAtomicAdd(dqp + (int64_t)(8 * (rr >> 2) + (rr & 3)) * rs, dq[j][rr]);
-                        }
-                    }
-                }
-            }
             if (i + 1 < work) sstore();
             __syncthreads();
         };
@@ -460,18 +378,15 @@ __global__ void __launch_bounds__(kThreads) bwd_kernel(BwdArgs a) {
     }
 }
 
-// delta[h, row] = sum_d dO[row,h,d] * O[row,h,d]; also clears dq_accum.
+// delta[h, row] = sum_d dO[row,h,d] * O[row,h,d] in fp32.
 template <int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(const uint16_t* __restrict__ o,
                                                       const uint16_t* __restrict__ d_o,
-                                                      float* __restrict__ delta,
-                                                      float* __restrict__ dq_accum,
-                                                      int64_t rows_h, int32_t H, int32_t total_q,
-                                                      int64_t accum_n4) {
+                                                      float* __restrict__ delta, int64_t rows_h,
+                                                      int32_t H, int32_t total_q) {
     constexpr int LPR = D / 8;  // lanes per (row, head)
     const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = gtid; i < accum_n4; i += nthreads) ((f32x4*)dq_accum)[i] = f32x4{};
     const int64_t groups = nthreads / LPR;
     const int sub = threadIdx.x % LPR;
     // every lane runs the same trip count so the shuffles see a full wave
@@ -497,42 +412,24 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const uint16_t* __restrict
     }
 }
 
-__global__ void __launch_bounds__(256) dq_convert_kernel(const float* __restrict__ src,
-                                                         uint16_t* __restrict__ dst, int64_t n8) {
-    const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = gtid; i < n8; i += nthreads) {
-        const f32x4 a = ((const f32x4*)src)[2 * i];
-        const f32x4 b = ((const f32x4*)src)[2 * i + 1];
-        f32x8 x;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            x[j] = a[j];
-            x[4 + j] = b[j];
-        }
-        ((u32x4*)dst)[i] = __builtin_bit_cast(u32x4, to_bf16x8(x));
-    }
-}
-
 template <int D, int MODE, bool BCAST>
 int32_t launch_main(const BwdArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((bwd_kernel<D, MODE, BCAST>), dim3(a.num_workers), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((dkdv_kernel<D, MODE, BCAST>), dim3(a.num_workers), dim3(kThreads), 0, s, a);
     return (int32_t)hipGetLastError();
 }
 
 template <int D>
 int32_t launch_d(const BwdArgs& a, Mode mode, bool bcast, int32_t stages, hipStream_t s) {
     const int64_t rows_h = (int64_t)a.total_q * a.num_heads;
-    const int64_t accum_n = (int64_t)a.q_rows * a.num_heads * D;
-    if (stages & JFA_BWD_PREPROCESS) {
+    if ((stages & JFA_BWD_PREPROCESS) && rows_h > 0) {
         const int64_t want = (rows_h * (D / 8) + 255) / 256;
         const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(want, 4096));
         hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(grid), dim3(256), 0, s, a.o, a.d_o, a.delta,
-                           a.dq_accum, rows_h, a.num_heads, a.total_q, accum_n / 4);
+                           rows_h, a.num_heads, a.total_q);
         const int32_t e = (int32_t)hipGetLastError();
         if (e) return e;
     }
-    if ((stages & JFA_BWD_MAIN) && a.num_workers > 0) {
+    if ((stages & JFA_BWD_DKDV) && a.num_workers > 0) {
         int32_t e;
         if (mode == kCausal) e = launch_main<D, kCausal, false>(a, s);
         else if (mode == kSparse)
@@ -540,12 +437,6 @@ int32_t launch_d(const BwdArgs& a, Mode mode, bool bcast, int32_t stages, hipStr
         else
             e = bcast ? launch_main<D, kDense, true>(a, s) : launch_main<D, kDense, false>(a, s);
         if (e) return e;
-    }
-    if (stages & JFA_BWD_FINISH) {
-        const int64_t n8 = accum_n / 8;
-        const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((n8 + 255) / 256, 4096));
-        hipLaunchKernelGGL(dq_convert_kernel, dim3(grid), dim3(256), 0, s, a.dq_accum, a.dq, n8);
-        return (int32_t)hipGetLastError();
     }
     return 0;
 }

@@ -90,6 +90,16 @@ __device__ __forceinline__ void pipeline_reads_mfma() {
     __builtin_amdgcn_sched_group_barrier(kMfma, A, 0);
 }
 
+// Orders a wave's LDS writes before its following LDS reads of what other
+// lanes of the same wave wrote (and the reads before later overwrites).
+// Without it such cross-lane traffic is a data race to the compiler, which
+// may then move the reads, e.g. into a branch only some lanes take.
+__device__ __forceinline__ void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Load of a wave-uniform value from memory the kernel never writes (plans,
 // offsets), through the constant address space so that it becomes a scalar
 // load: a vector load would need a vmcnt wait, which also waits for every

@@ -33,21 +33,18 @@
 // Every LDS tile is XOR-swizzled at 16-byte granularity so that the MFMA
 // operand reads, the transposed reads and the V^T writes are free of bank
 // conflicts (64 banks x 4 bytes).
-#include "device.h"
-#include "internal.h"
+#include "qtile.h"
 
 namespace jfa {
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
+using namespace qtile;
 constexpr int kAhead = 3;        // block j+kAhead is copied while block j is computed
 constexpr int kKSlots = kAhead + 1;   // K ring: blocks j .. j+kAhead
 constexpr int kVSlots = kAhead;       // V ring: blocks j+1 .. j+kAhead (j+1 is transposed at j)
 constexpr int kReadAhead = 4;    // LDS operand reads kept in flight ahead of the MFMAs
 constexpr int kStageRows = 16;   // O rows per wave per epilogue round
 
-static_assert(kFwdBlockM == 32 * kWaves && kFwdBlockN == 64, "forward tile geometry");
 
 template <int D>
 struct FwdLds {
@@ -59,43 +56,6 @@ struct FwdLds {
     static constexpr int OST_WAVE = kStageRows * D * 2;        // O staging of one wave
     static_assert(4 * OST_WAVE == BLK, "staging: 4 waves per released block");
 };
-
-// 16-byte chunk swizzles (chunk index XOR f(row)).
-template <int D>
-__device__ __forceinline__ int swz_k(int r) {   // K rows: S^T operand reads
-    return D == 128 ? (r & 15) : ((r >> 1) & 7);
-}
-template <int D>
-__device__ __forceinline__ int swz_v(int r) {   // V rows: transposed reads
-    return D == 128 ? 2 * ((r & 3) + 4 * ((r >> 3) & 1)) : 2 * (((r >> 1) & 1) + 2 * ((r >> 3) & 1));
-}
-__device__ __forceinline__ int swz_vt(int d) { return (d >> 1) & 7; }   // V^T rows (64 keys)
-
-// position of key q (within its group of 16) in sigma order 0-3, 8-11, 4-7, 12-15
-__device__ __forceinline__ int sigma_pos(int q) {
-    const int g = (q >> 2) & 3;
-    return (q & ~15) | (((g >> 1) | ((g & 1) << 1)) << 2) | (q & 3);
-}
-
-// Direct-to-LDS copy of 16 bytes per lane: lane l's bytes at g land at
-// lds_wave_base + 16 l (lds_wave_base wave-uniform). Issued as inline
-// assembly so that the compiler does not treat every later LDS read as
-// possibly overlapping the copy (it would wait for all copies in flight
-// before each of them); completion is awaited explicitly with wait_vmem()
-// followed by a workgroup barrier.
-__device__ __forceinline__ void load_lds16(const uint16_t* g, char* lds_wave_base) {
-    const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_wave_base;
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(g), "s"(lds)
-        : "memory");
-}
 
 template <int D, int MODE, bool BCAST>
 __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
@@ -126,53 +86,25 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
     }
     // transposition V -> V^T: this lane's read and write addresses per read u
     int tr_src[TPW], tr_dst[TPW];
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-        const int P = 2 * (TPW * wave + u) + (lane >> 5);
-        const int dg = P >> 3, s = (P >> 1) & 3, z = P & 1;
-        const int kq = 4 * s + z + 2 * ((lane >> 4) & 1);   // key quad of this 16-lane group
-        const int n16 = lane & 15, e = n16 >> 2, c = n16 & 3;
-        const int r = 4 * kq + e;
-        tr_src[u] = r * D * 2 + (((2 * dg + (c >> 1)) ^ swz_v<D>(r)) << 4) + 8 * (c & 1);
-        const int d = 16 * dg + n16, pos = sigma_pos(4 * kq);
-        tr_dst[u] = d * 128 + (((pos >> 3) ^ swz_vt(d)) << 4) + 2 * (pos & 7);
-    }
+    transpose_offsets<D, TPW>(wave, lane, [](int r) { return swz_v<D>(r); }, tr_src, tr_dst);
     // S^T operand: K row 32mb + lr, chunk 2kc + hf (swz_k(32mb + lr) == swz_k(lr))
     int k_off[KC];
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) k_off[kc] = lr * D * 2 + (((2 * kc + hf) ^ swz_k<D>(lr)) << 4);
     // O^T operand: V^T row 32md + lr, 16-key chunk c -> stored chunk 2c + hf
-    // (swz_vt(32md + lr) == swz_vt(lr))
+    // (swz_t(32md + lr) == swz_t(lr))
     int vt_off[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) vt_off[c] = lr * 128 + (((2 * c + hf) ^ swz_vt(lr)) << 4);
+    for (int c = 0; c < 4; ++c) vt_off[c] = lr * 128 + (((2 * c + hf) ^ swz_t(lr)) << 4);
 
     const int w = worker_id(a.num_workers);
     const int t_begin = ld_uniform(a.worker_ptr + w), t_end = ld_uniform(a.worker_ptr + w + 1);
 
     // ---- the block stream of this worker: (tile, block) in plan order
-    struct TileInfo {
-        int b, h, t, work, kv0, L;
-        const int* sp;
+    auto tile_info = [&](int ti) {
+        return qtile::tile_info<MODE>(a.tiles, a.kv_off, a.sp_ptr, a.sp_idx, a.mask_q_blocks, ti);
     };
-    auto tile_info = [&](int ti) -> TileInfo {
-        TileInfo ti_;
-        ti_.b = ld_uniform(a.tiles + 4 * ti + 0);
-        ti_.h = ld_uniform(a.tiles + 4 * ti + 1);
-        ti_.t = ld_uniform(a.tiles + 4 * ti + 2);
-        ti_.work = ld_uniform(a.tiles + 4 * ti + 3);
-        ti_.kv0 = ld_uniform(a.kv_off + ti_.b);
-        ti_.L = ld_uniform(a.kv_off + ti_.b + 1) - ti_.kv0;
-        ti_.sp = nullptr;
-        if (MODE == kSparse)
-            ti_.sp = a.sp_idx + ld_uniform(a.sp_ptr + ti_.b * ((a.mask_q_blocks + 1) >> 1) + ti_.t);
-        return ti_;
-    };
-    // 64-key block of the sequence visited at position i of a tile
-    auto seq_block = [&](const TileInfo& T, int i) -> int {
-        if (MODE == kSparse) return 2 * (ld_uniform(T.sp + (i >> 1)) >> 2) + (i & 1);
-        return i;
-    };
+    auto seq_block = [&](const TileInfo& T, int i) { return qtile::seq_block<MODE>(T, i); };
 
     // loader cursor
     int l_ti = t_begin, l_i = 0, l_slot = 0;
@@ -186,8 +118,8 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
             LT = tile_info(l_ti);
         }
     };
-    // issue the copies of the loader's block into ring slots (K: s % 3, V: s % 2)
-    // and advance; keys past the sequence are clamped to its last row (always
+    // issue the copies of the loader's block into ring slots (K: s % kKSlots,
+    // V: s % kVSlots) and advance; keys past the sequence are clamped to its last row (always
     // finite data, masked out of the softmax by the tail path)
     auto l_issue = [&]() {
         if (l_ti >= t_end) return;
@@ -206,8 +138,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
         ++l_i;
         l_settle();
     };
-    // V (natural, slot s % kVSlots) -> V^T (buffer s % 2), in two halves so
-    // that the transposed reads can be issued well before their writes
+    // V (natural, slot s % kVSlots) -> V^T (buffer s % 2)
     auto tr_read = [&](int s, bf16x4 (&x)[TPW]) {
         const char* src = smem + LY::V + (s % kVSlots) * LY::BLK;
 #pragma unroll
@@ -328,14 +259,8 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
             if (s + 1 < total) transpose_v(s + 1);  // V^T of block s+1
 
             const int n = seq_block(T, i);
-            bool skip = !wave_rows, masked;
-            if (MODE == kCausal) {
-                skip = skip || kFwdBlockN * n > row0 + 31;
-                masked = kFwdBlockN * n + kFwdBlockN - 1 > row0 || kFwdBlockN * (n + 1) > T.L;
-            } else {
-                masked = kFwdBlockN * (n + 1) > T.L;
-                if (MODE == kSparse) skip = skip || !((ld_uniform(T.sp + (i >> 1)) >> (wave >> 2)) & 1);
-            }
+            bool skip, masked;
+            block_flags<MODE>(T, i, n, row0, wave_rows, wave, skip, masked);
             if (!skip) {
                 f32x16 sc[2];
                 compute_s(sc, s);
@@ -400,6 +325,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
                                 to_bf16x4(x);
                         }
                 }
+                wave_sync_lds();
 #pragma unroll
                 for (int v = 0; v < kStageRows * CH / 64; ++v) {
                     const int k = lane + 64 * v;
@@ -409,6 +335,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
                     if (orow < Lq)
                         *(u32x4*)(a.o + (int64_t)(orow0 + orow) * rs + (int64_t)T.h * D + 8 * chunk) = x;
                 }
+                wave_sync_lds();
             }
             if (hf == 0 && qrow < Lq)
                 a.lse[(int64_t)T.h * a.total_q + orow0 + qrow] =

@@ -42,6 +42,8 @@ struct FwdArgs {
     float scale_log2;       // softmax_scale * log2(e)
 };
 
+// KV-stationary dK/dV pass of the backward (JFA_PASS_BWD plan) and the
+// delta preprocess.
 struct BwdArgs {
     const int32_t* worker_ptr;
     const int32_t* tiles;
@@ -55,24 +57,61 @@ struct BwdArgs {
     const uint16_t* o;
     const float* lse;
     const uint16_t* d_o;
-    uint16_t* dq;
     uint16_t* dk;
     uint16_t* dv;
-    float* dq_accum;
     float* delta;
     int32_t num_heads;
     int32_t lq;
     int32_t total_q;
-    int32_t q_rows;          // rows of q / dq (lq in broadcast mode, else T_q)
     int32_t mask_kv_blocks;
     int32_t num_workers;
     float scale;
     float scale_log2;
 };
 
+// Q-stationary dQ pass of the backward (JFA_PASS_DQ plan).
+struct DqArgs {
+    const int32_t* worker_ptr;
+    const int32_t* tiles;
+    const int32_t* sp_ptr;
+    const int32_t* sp_idx;
+    const int32_t* q_off;    // null in broadcast mode
+    const int32_t* kv_off;
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* d_o;
+    const float* lse;
+    const float* delta;
+    uint16_t* dq;            // per-sequence Q: bf16 [T_q, H, D]
+    float* dq_accum;         // per-sequence Q: fp32 [T_q, H, D]
+    float* partial;          // broadcast Q: fp32 [W][256][D] per-worker partial sums
+    int32_t num_heads;
+    int32_t lq;
+    int32_t total_q;
+    int32_t mask_q_blocks;
+    int32_t num_workers;
+    float scale;
+    float scale_log2;
+};
+
+// Deterministic sum of the broadcast-Q dQ partials of each (head, Q tile)
+// group in worker order, into dq_accum (fp32) and dq (bf16), both [lq, H, D].
+struct DqReduceArgs {
+    const int32_t* worker_ptr;   // the DQ plan's (to skip workers without tiles)
+    const float* partial;
+    float* dq_accum;
+    uint16_t* dq;
+    int32_t num_heads;
+    int32_t lq;
+    int32_t num_workers;         // W' of the DQ plan
+};
+
 // Launchers (return a hipError_t value as int32).
 int32_t launch_fwd(const FwdArgs& a, int32_t head_dim, Mode mode, bool broadcast, void* stream);
 int32_t launch_bwd(const BwdArgs& a, int32_t head_dim, Mode mode, bool broadcast, int32_t stages,
                    void* stream);
+int32_t launch_dq(const DqArgs& a, int32_t head_dim, Mode mode, bool broadcast, void* stream);
+int32_t launch_dq_reduce(const DqReduceArgs& a, int32_t head_dim, void* stream);
 
 }  // namespace jfa

@@ -1,0 +1,136 @@
+// Pieces shared by the Q-stationary kernels (forward and the backward's dQ
+// pass): a workgroup of 8 waves owns a tile of 256 query rows, 32 per wave,
+// and streams 64-key K/V blocks of its sequence through LDS with
+// direct-to-LDS copies. Each tile's rows meet the keys in the order the host
+// plan gives ("Meta's TLX Jagged Flash Attention Beats FA4 on Blackwell With
+// 3x Less Code" (ainewsbites.com), sections "What TLX changes" and
+// "Optimizations layered on top": persistent programs, multi-buffered K/V).
+#pragma once
+
+#include "device.h"
+#include "internal.h"
+
+namespace jfa {
+namespace qtile {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+static_assert(kFwdBlockM == 32 * kWaves && kFwdBlockN == 64, "Q-tile geometry");
+
+// 16-byte chunk swizzles of LDS tiles (stored chunk = chunk XOR f(row)),
+// chosen for 64 banks x 4 bytes:
+//  - swz_k: rows read as 32x32x16 MFMA A operands (16 lanes = 16 rows, one
+//    16-byte chunk each);
+//  - swz_v: rows read by transposed reads (a 16-lane group reads 4 rows x 32
+//    bytes; the two groups of a half wave read rows r and r + 8);
+//  - swz_kv: both uses at once (swz_v plus bit 2 of the row);
+//  - swz_t: [d][64 keys] transposed tiles (128-byte rows) read as A operands.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+    return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+    return D == 128 ? 2 * ((r & 3) + 4 * ((r >> 3) & 1)) : 2 * (((r >> 1) & 1) + 2 * ((r >> 3) & 1));
+}
+template <int D>
+__device__ __forceinline__ int swz_kv(int r) {
+    return swz_v<D>(r) + ((r >> 2) & 1);
+}
+__device__ __forceinline__ int swz_t(int d) { return (d >> 1) & 7; }
+
+// position of key q (within its group of 16) in sigma order 0-3, 8-11, 4-7,
+// 12-15: the order in which a 32x32 accumulator column holds its 16 rows
+// once they are fed back as a B operand (register r of lane half h holds row
+// 8(r/4) + 4h + r%4)
+__device__ __forceinline__ int sigma_pos(int q) {
+    const int g = (q >> 2) & 3;
+    return (q & ~15) | (((g >> 1) | ((g & 1) << 1)) << 2) | (q & 3);
+}
+
+// Direct-to-LDS copy of 16 bytes per lane: lane l's bytes at g land at
+// lds_wave_base + 16 l (lds_wave_base wave-uniform). Issued as inline
+// assembly so that the compiler does not treat every later LDS read as
+// possibly overlapping the copy (it would wait for all copies in flight
+// before each of them); completion is awaited explicitly with wait_vmem()
+// or wait_vmem_keep() followed by a workgroup barrier.
+__device__ __forceinline__ void load_lds16(const uint16_t* g, char* lds_wave_base) {
+    const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_wave_base;
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(g), "s"(lds)
+        : "memory");
+}
+
+// One tile of a Q-tile plan (wave-uniform).
+struct TileInfo {
+    int b, h, t, work, kv0, L;
+    const int* sp;   // block-sparse list of the tile (4c + keep bits), else null
+};
+
+template <int MODE>
+__device__ __forceinline__ TileInfo tile_info(const int32_t* tiles, const int32_t* kv_off,
+                                              const int32_t* sp_ptr, const int32_t* sp_idx,
+                                              int32_t mask_q_blocks, int ti) {
+    TileInfo T;
+    T.b = ld_uniform(tiles + 4 * ti + 0);
+    T.h = ld_uniform(tiles + 4 * ti + 1);
+    T.t = ld_uniform(tiles + 4 * ti + 2);
+    T.work = ld_uniform(tiles + 4 * ti + 3);
+    T.kv0 = ld_uniform(kv_off + T.b);
+    T.L = ld_uniform(kv_off + T.b + 1) - T.kv0;
+    T.sp = nullptr;
+    if (MODE == kSparse) T.sp = sp_idx + ld_uniform(sp_ptr + T.b * ((mask_q_blocks + 1) >> 1) + T.t);
+    return T;
+}
+
+// 64-key block of the sequence visited at position i of a tile
+template <int MODE>
+__device__ __forceinline__ int seq_block(const TileInfo& T, int i) {
+    if (MODE == kSparse) return 2 * (ld_uniform(T.sp + (i >> 1)) >> 2) + (i & 1);
+    return i;
+}
+
+// Which blocks a wave takes and which need the tail masks: rows row0 ..
+// row0+31 of the wave, block n of the sequence (position i of the tile).
+template <int MODE>
+__device__ __forceinline__ void block_flags(const TileInfo& T, int i, int n, int row0, bool wave_rows,
+                                            int wave, bool& skip, bool& masked) {
+    skip = !wave_rows;
+    if (MODE == kCausal) {
+        skip = skip || kFwdBlockN * n > row0 + 31;
+        masked = kFwdBlockN * n + kFwdBlockN - 1 > row0 || kFwdBlockN * (n + 1) > T.L;
+    } else {
+        masked = kFwdBlockN * (n + 1) > T.L;
+        if (MODE == kSparse) skip = skip || !((ld_uniform(T.sp + (i >> 1)) >> (wave >> 2)) & 1);
+    }
+}
+
+// Addresses of the transposition of a natural [64 keys][D] tile into a
+// [D][64] tile with keys in sigma order, by 16-lane transposed reads: per read
+// u of this wave, the source offset (rows swizzled by SWZ) and the
+// destination offset (rows swizzled by swz_t).
+template <int D, int TPW, typename SWZ>
+__device__ __forceinline__ void transpose_offsets(int wave, int lane, SWZ swz, int (&src)[TPW],
+                                                  int (&dst)[TPW]) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int P = 2 * (TPW * wave + u) + (lane >> 5);
+        const int dg = P >> 3, s = (P >> 1) & 3, z = P & 1;
+        const int kq = 4 * s + z + 2 * ((lane >> 4) & 1);   // key quad of this 16-lane group
+        const int n16 = lane & 15, e = n16 >> 2, c = n16 & 3;
+        const int r = 4 * kq + e;
+        src[u] = r * D * 2 + (((2 * dg + (c >> 1)) ^ swz(r)) << 4) + 8 * (c & 1);
+        const int d = 16 * dg + n16, pos = sigma_pos(4 * kq);
+        dst[u] = d * 128 + (((pos >> 3) ^ swz_t(d)) << 4) + 2 * (pos & 7);
+    }
+}
+
+}  // namespace qtile
+}  // namespace jfa

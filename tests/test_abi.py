@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert J.jfa_abi_version() == 1
+    assert J.jfa_abi_version() == 2
     for st in range(-7, 1):
         assert J.jfa_status_string(st) not in ("", "unknown status")
     assert J.jfa_status_string(-99) == "unknown status"
@@ -136,9 +136,41 @@ def test_fwd_validation_returns_before_launch():
 
 def test_bwd_workspace_query():
     prob = _prob()
-    bwd = J.jfa_plan_build(prob, None, [0, 3, 5], None, J.JFA_PASS_BWD, 4)
-    assert J.jfa_bwd_workspace_bytes(prob, bwd.info) >= 0
+    dq = J.jfa_plan_build(prob, None, [0, 3, 5], None, J.JFA_PASS_DQ, 4)
+    # broadcast Q: one fp32 [256][D] partial per dQ worker
+    assert J.jfa_bwd_workspace_bytes(prob, dq.info) == dq.info.num_workers * 256 * prob.head_dim * 4
+    per_seq = _prob(broadcast_q=False, lq=0)
+    dq2 = J.jfa_plan_build(per_seq, [0, 2, 4], [0, 3, 5], None, J.JFA_PASS_DQ, 4)
+    assert J.jfa_bwd_workspace_bytes(per_seq, dq2.info) == 0
+    for p in (J.JFA_PASS_FWD, J.JFA_PASS_BWD):
+        other = J.jfa_plan_build(prob, None, [0, 3, 5], None, p, 4)
+        with pytest.raises(J.JfaError) as e:
+            J.jfa_bwd_workspace_bytes(prob, other.info)
+        assert e.value.status == J.JFA_ERR_PLAN_MISMATCH
+
+
+def _call_bwd(prob, kv, dq, ws_bytes, **over):
+    t = _FakeTensor(0x1000)
+    f = lambda x: None if x is None else ctypes.c_void_p(x.data_ptr())
+    args = dict(q=t, k=t, v=t, o=t, lse=t, d_o=t, dq=t, dk=t, dv=t, dq_accum=t, delta=t, ws=t)
+    args.update(over)
+    plans = [J.JfaDevicePlan(ctypes.pointer(p.info), 0x1000, 0x1000, None, None) for p in (kv, dq)]
+    cp = prob.c()
+    return J._lib().jfa_bwd(ctypes.byref(cp), ctypes.byref(plans[0]), ctypes.byref(plans[1]),
+                            None, ctypes.c_void_p(0x1000), *[f(args[k]) for k in
+                            ("q", "k", "v", "o", "lse", "d_o", "dq", "dk", "dv", "dq_accum",
+                             "delta", "ws")], ws_bytes, None)
+
+
+def test_bwd_validation_returns_before_launch():
+    prob = _prob()
+    kv = J.jfa_plan_build(prob, None, [0, 3, 5], None, J.JFA_PASS_BWD, 4)
+    dq = J.jfa_plan_build(prob, None, [0, 3, 5], None, J.JFA_PASS_DQ, 4)
     fwd = J.jfa_plan_build(prob, None, [0, 3, 5], None, J.JFA_PASS_FWD, 4)
-    with pytest.raises(J.JfaError) as e:
-        J.jfa_bwd_workspace_bytes(prob, fwd.info)
-    assert e.value.status == J.JFA_ERR_PLAN_MISMATCH
+    need = J.jfa_bwd_workspace_bytes(prob, dq.info)
+    assert _call_bwd(prob, dq, dq, need) == J.JFA_ERR_PLAN_MISMATCH      # KV plan of the wrong pass
+    assert _call_bwd(prob, kv, fwd, need) == J.JFA_ERR_PLAN_MISMATCH     # dQ plan of the wrong pass
+    assert _call_bwd(prob, kv, dq, need - 1) == J.JFA_ERR_WORKSPACE
+    assert _call_bwd(prob, kv, dq, need, ws=None) == J.JFA_ERR_WORKSPACE
+    assert _call_bwd(prob, kv, dq, need, dk=_FakeTensor(0x1004)) == J.JFA_ERR_INVALID_ARG
+    assert _call_bwd(_prob(lq=9), kv, dq, need) == J.JFA_ERR_PLAN_MISMATCH

@@ -58,10 +58,11 @@ class GpuRun:
     delta: object
 
 
-def run_gpu(x, fwd_workers=None, bwd_workers=None, canary=True):
+def run_gpu(x, fwd_workers=None, bwd_workers=None, dq_workers=None, canary=True):
     prob = problem_of(x)
     att = J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask,
-                            fwd_workers=fwd_workers, bwd_workers=bwd_workers)
+                            fwd_workers=fwd_workers, bwd_workers=bwd_workers,
+                            dq_workers=dq_workers)
     q, k, v, do = dev(x.q), dev(x.k), dev(x.v), dev(x.do)
     H, D = prob.num_heads, prob.head_dim
     o = torch.empty((att.total_q, H, D), dtype=torch.bfloat16, device="cuda")
@@ -185,12 +186,18 @@ def test_zero_q_gives_mean_of_v():
 @pytest.mark.parametrize("case", ["bcast_ragged_d128", "causal_d128", "sparse_d128"])
 def test_deterministic_across_plans_and_runs(case):
     """O, LSE, dK, dV are bitwise identical for any worker count (each tile is
-    computed by one workgroup in a fixed order); dQ sums in fp32 atomics, so
-    it only agrees to reassociation."""
+    computed by one workgroup in a fixed order). dQ is bitwise identical from
+    run to run of the same plans (no atomics; broadcast partials are summed in
+    worker order); across dQ plans with other worker counts only the grouping
+    of the fp32 sum changes."""
     x = SMALL_CASES[case]()
-    runs = [run_gpu(x, fwd_workers=fw, bwd_workers=bw) for fw, bw in ((None, None), (1, 1), (7, 13),
-                                                                      (None, None))]
+    runs = [run_gpu(x, fwd_workers=fw, bwd_workers=bw, dq_workers=qw)
+            for fw, bw, qw in ((None, None, None), (1, 1, 1), (7, 13, 5), (None, None, None))]
     ref = runs[0]
+    for name in ("dq_accum", "dq"):
+        a, b = getattr(ref, name), getattr(runs[3], name)
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), name
     for r in runs[1:]:
         for name in ("o", "lse", "dk", "dv", "delta"):
             a, b = getattr(ref, name), getattr(r, name)
