@@ -128,10 +128,11 @@ int32_t jfa_offsets_from_lengths(const int32_t* h_lengths, int32_t batch, int32_
  * rows, work = KV blocks of block_n=64 keys visited (dense: ceil(Lk/64);
  * causal: ceil(min(256(t+1), L)/64); block-sparse: the 64-key blocks of the
  * 128-key mask blocks inside the sequence kept by either of the tile's two
- * 128-row mask rows). BWD: t is a KV tile of block_n=128 keys, work = Q
- * blocks of block_m=64 rows visited (dense: ceil(Lq/64); causal:
- * ceil(L/64) - 2t; block-sparse: the 64-row blocks of the kept 128-row mask
- * tiles). Tiles are stably sorted by work, descending, and sorted tile i goes
+ * 128-row mask rows). BWD: t is a KV tile of block_n=256 keys, work = Q
+ * blocks of block_m=32 rows visited (dense: ceil(Lq/32); causal:
+ * ceil(L/32) - 8t; block-sparse: the 32-row blocks of the 128-row mask rows
+ * kept by either of the tile's two 128-key mask columns inside the
+ * sequence). Tiles are stably sorted by work, descending, and sorted tile i goes
  * to worker i mod W when floor(i/W) is even, else to W-1-(i mod W).
  * DQ: the FWD tiles and work. With per-sequence Q the deal is the FWD deal.
  * With broadcast Q (every tile (b, h, t) adds into the same dQ rows of head
@@ -150,9 +151,11 @@ int32_t jfa_offsets_from_lengths(const int32_t* h_lengths, int32_t batch, int32_
  *                 over Q tiles b*ceil(mask_q_blocks/2)+t of the 128-key
  *                 blocks c inside the sequence kept by a mask row of the
  *                 tile, stored as 4c + bits (bit k: row 2t+k keeps c; rows
- *                 past the mask or the sequence keep nothing); BWD = CSC over
- *                 columns b*mask_kv_blocks+c of the kept 128-row Q tiles
- *                 inside the sequence; ascending.
+ *                 past the mask or the sequence keep nothing); BWD = CSC
+ *                 over KV tiles b*ceil(mask_kv_blocks/2)+t of the 128-row
+ *                 mask rows m inside the sequence kept by a mask column of
+ *                 the tile, stored as 4m + bits (bit k: column 2t+k keeps
+ *                 m); ascending.
  * The caller copies these arrays to the device for jfa_fwd / jfa_bwd.
  */
 int32_t jfa_plan_query(const jfa_problem* prob, const int32_t* h_q_offsets,

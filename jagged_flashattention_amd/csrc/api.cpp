@@ -46,7 +46,8 @@ int32_t check_common(const jfa_problem* p, const jfa_plan_info* info, int32_t pa
         const int64_t rows =
             (int64_t)p->batch * (qtiles ? (p->mask_q_blocks + jfa::kFwdBlockM / jfa::kMaskBlock - 1) /
                                               (jfa::kFwdBlockM / jfa::kMaskBlock)
-                                        : p->mask_kv_blocks);
+                                        : (p->mask_kv_blocks + jfa::kBwdBlockN / jfa::kMaskBlock - 1) /
+                                              (jfa::kBwdBlockN / jfa::kMaskBlock));
         if (info->sparse_rows != rows) return JFA_ERR_PLAN_MISMATCH;
         if (d_sparse_ptr == nullptr || (info->sparse_nnz > 0 && d_sparse_idx == nullptr))
             return JFA_ERR_INVALID_ARG;

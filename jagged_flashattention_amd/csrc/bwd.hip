@@ -5,376 +5,384 @@
 //      backward step; the pages only name the backward's persistent, tiled
 //      structure: "Meta's TLX Jagged Flash Attention Beats FA4 on Blackwell"
 //      (ainewsbites.com), section "Optimizations layered on top");
-//   2. dK/dV: one persistent workgroup per worker walking a KV-tile plan. A
-//      workgroup owns a 128-key KV tile (32 keys per wave) and streams the
-//      64-row Q/dO blocks that see it; dK and dV are accumulated per KV tile
-//      in registers and written once, as whole rows through LDS.
+//   2. dK/dV: one persistent workgroup of 8 waves per CU walking a KV-tile
+//      plan. A workgroup owns a 256-key KV tile (32 keys per wave, K in VGPRs
+//      as a B operand, V in LDS) and streams the 32-row Q/dO blocks that see
+//      it. The worker's blocks form one stream across its tiles: Q and dO of
+//      block j+2 are copied global -> LDS with direct-to-LDS loads while block
+//      j is computed, and Q^T, dO^T of block j+1 are made LDS -> LDS with
+//      transposed reads. dK and dV stay in registers for the whole tile and
+//      leave as whole rows through LDS.
 //
 // Per Q block and wave (keys on lanes, query rows in registers):
-//   S   = Q K^T          A = Q rows from LDS,    B = K (registers)
+//   S   = Q K^T          A = Q rows from LDS,    B = K (VGPRs)
 //   P   = exp2(S*scale*log2e - LSE*log2e)
 //   dP  = dO V^T         A = dO rows from LDS,   B = V rows from LDS
 //   dS  = P * (dP - delta)
 //   dV^T += dO^T P       A = dO^T from LDS (rows in sigma order), B = P
 //   dK^T += Q^T dS       A = Q^T from LDS (rows in sigma order),  B = dS
-#include <type_traits>
-
-#include "device.h"
-#include "internal.h"
+#include "qtile.h"
 
 namespace jfa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kPad = 8;
+using namespace qtile;
 
-// LDS layout. Tiles whose rows are read as MFMA operands by 16 lanes at a
-// time are laid out so that those 16 rows hit distinct banks:
-//  - natural [row][D] tiles (Q, dO, and at tile start K, V; at tile end the
-//    dK/dV staging): 16-byte chunk c of row r is stored at chunk c ^ swz(r),
-//    swz(r) = (r + r/CH) mod CH, CH = D/8 chunks per row;
-//  - Q^T, dO^T: [d][64 rows] padded by 16 bytes per row;
-//  - rows of Q^T/dO^T are stored in the "sigma" order of each 16-group (0-3,
-//    8-11, 4-7, 12-15), so that the 8 values one lane feeds to a 32x32x16
-//    MFMA (rows 16c + sigma(8h..8h+7)) are one 16-byte read and match the
-//    accumulator registers they are multiplied with.
-// Region R holds the Q-block tiles during the loop, the natural K tile during
-// the tile prologue, and the dK/dV staging in the tile epilogue. The natural
-// V tile stays in its own region for the whole tile (its rows are the B
-// operand of dP = dO V^T).
+constexpr int kAhead = 2;            // block j+2 is copied while block j is computed
+constexpr int kSlots = kAhead + 1;   // Q/dO ring: blocks j .. j+kAhead
+constexpr int kReadAhead = 4;        // LDS operand reads kept in flight ahead of the MFMAs
+static_assert(kBwdBlockN == 32 * kWaves && kBwdBlockM == 32, "dK/dV tile geometry");
+
 template <int D>
-struct BwdLds {
-    static constexpr int R = 0;
-    static constexpr int QN = R;                                    // [64][D]
-    static constexpr int DN = QN + kBwdBlockM * D * 2;              // [64][D]
-    static constexpr int QT = DN + kBwdBlockM * D * 2;              // [D][72]
-    static constexpr int DT = QT + D * (kBwdBlockM + 8) * 2;        // [D][72]
-    static constexpr int KN = R;                                    // [128][D]
-    static constexpr int DKS = R;                                   // [128][D] (epilogue)
-    static constexpr int DVS = R + kBwdBlockN * D * 2;              // [128][D] (epilogue)
-    static constexpr int R_BYTES = (DT + D * (kBwdBlockM + 8) * 2 - R) > 2 * kBwdBlockN * D * 2
-                                       ? (DT + D * (kBwdBlockM + 8) * 2 - R)
-                                       : 2 * kBwdBlockN * D * 2;
-    static constexpr int VN = R + R_BYTES;                          // [128][D]
-    static constexpr int LSE = VN + kBwdBlockN * D * 2;
-    static constexpr int DELTA = LSE + kBwdBlockM * 4;
-    static constexpr int BYTES = DELTA + kBwdBlockM * 4;
+struct DkdvLds {
+    static constexpr int QB = kBwdBlockM * D * 2;            // a Q or dO block [32][D] bf16
+    static constexpr int ROWV = 2 * QB;                       // LSE*log2e [32], delta [32] fp32
+    static constexpr int SLOT = 2 * QB + 512;                 // Q, dO, row values
+    static constexpr int RING = 0;                            // kSlots slots
+    static constexpr int T = RING + kSlots * SLOT;            // 2 x (Q^T, dO^T) [D][32]
+    static constexpr int TBUF = 2 * QB;
+    static constexpr int V = T + 2 * TBUF;                    // V tile [256][D] (epilogue staging)
+    static constexpr int BYTES = V + kBwdBlockN * D * 2;
+    static constexpr int ST_WAVE = 32 * D * 2;                // staging of one wave: 32 rows
+    static_assert(kWaves * ST_WAVE == kBwdBlockN * D * 2, "staging fits the V tile");
 };
 
-// position of row q (within its group of 16) in sigma order
-__device__ __forceinline__ int sigma_pos(int q) {
-    const int g = (q >> 2) & 3;
-    return (q & ~15) | (((g >> 1) | ((g & 1) << 1)) << 2) | (q & 3);
-}
-
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-    constexpr int CH = D / 8;
-    constexpr int SH = (D == 128) ? 4 : 3;
-    return (r + (r >> SH)) & (CH - 1);
-}
-
-// byte offset of element (row r, element c8*8 + e) of a natural [row][D] tile
-template <int D>
-__device__ __forceinline__ int nat_off(int r, int chunk) {
-    return r * D * 2 + ((chunk ^ swz<D>(r)) << 4);
-}
-
-// 4 rows x 8 bf16 (one 16-byte chunk per row) -> 8 columns x 4 rows
-__device__ __forceinline__ void transpose4x8(const u32x4 (&x)[4], u32x2 (&y)[8]) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        y[2 * k][0] = (x[0][k] & 0xffffu) | (x[1][k] << 16);
-        y[2 * k][1] = (x[2][k] & 0xffffu) | (x[3][k] << 16);
-        y[2 * k + 1][0] = (x[0][k] >> 16) | (x[1][k] & 0xffff0000u);
-        y[2 * k + 1][1] = (x[2][k] >> 16) | (x[3][k] & 0xffff0000u);
-    }
-}
+// [D][32] transposed tiles (64-byte rows): stored chunk = chunk ^ ((d >> 2) & 3)
+__device__ __forceinline__ int swz_t32(int d) { return (d >> 2) & 3; }
 
 template <int D, int MODE, bool BCAST>
-__global__ void __launch_bounds__(kThreads) dkdv_kernel(BwdArgs a) {
-    using LY = BwdLds<D>;
-    __shared__ __attribute__((aligned(16))) char smem[LY::BYTES];
-    constexpr int KC = D / 16;
-    constexpr int MD = D / 32;
-    constexpr int CH = D / 8;
-    constexpr int KPP = 4 * (kThreads / CH);       // keys per pass of the tile loader
-    constexpr int KPASS = kBwdBlockN / KPP;        // 2 (D=128) or 1 (D=64)
-    auto lds = [&](int byte_off) -> char* { return smem + byte_off; };
+__global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
+    using LY = DkdvLds<D>;
+    __shared__ __attribute__((aligned(1024))) char smem[LY::BYTES];
+    constexpr int KC = D / 16;              // 16-wide d chunks of S and dP
+    constexpr int MD = D / 32;              // 32-row d blocks of dK^T, dV^T
+    constexpr int CH = D / 8;               // 16-byte chunks per row
+    constexpr int QPW = (2 * kBwdBlockM * CH) / (64 * kWaves);   // Q + dO copies per wave per block
+    constexpr int VPW = (kBwdBlockN * CH) / (64 * kWaves);       // V copies per wave per tile
+    constexpr int TPW = (kBwdBlockM * D) / (256 * kWaves);       // transposed reads per wave per tensor
+    static_assert(QPW >= 1 && TPW >= 1, "copy split");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int lr = lane & 31, hf = lane >> 5;
     const int H = a.num_heads;
     const int64_t rs = (int64_t)H * D;
-    // Q/dO block loader: 4 rows (4qg..4qg+3) x one 16-byte chunk dc per thread
-    const int ld_qg = tid & 15, ld_dc = tid >> 4;
-    const bool ld_on = ld_dc < CH;
-    // K/V tile loader: chunk tdc of keys 4tkg..4tkg+3 (+KPP per pass); a load
-    // instruction covers whole 16*CH-byte rows
-    const int tdc = tid % CH, tkg = tid / CH;
 
-    // per-lane pieces of the swizzled addresses of natural rows 32mb + lr
-    int nat_base[2], nat_x[2];
+    constexpr int QH = (kBwdBlockM * CH) / 64;   // copies per tensor (Q or dO) per block
+    // transposition [32 rows][D] -> [D][32] with rows in sigma order: per
+    // read u, a 16-lane group reads 4 rows x 16 d; the two groups of a half
+    // wave read row quads kq and kq + 2
+    int tr_src[TPW], tr_dst[TPW];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-        const int row = 32 * mb + lr;
-        const int sw = swz<D>(row);
-        nat_base[mb] = row * D * 2 + 16 * (hf ^ (sw & 1));
-        nat_x[mb] = sw >> 1;
+    for (int u = 0; u < TPW; ++u) {
+        const int P = 2 * (TPW * wave + u) + (lane >> 5);
+        const int dg = P >> 2, sq = (P >> 1) & 1, z = P & 1;
+        const int kq = 4 * sq + z + 2 * ((lane >> 4) & 1);
+        const int n16 = lane & 15, e = n16 >> 2, c = n16 & 3;
+        const int r = 4 * kq + e;
+        tr_src[u] = r * D * 2 + (((2 * dg + (c >> 1)) ^ swz_kv<D>(r)) << 4) + 8 * (c & 1);
+        const int d = 16 * dg + n16, pos = sigma_pos(4 * kq);
+        tr_dst[u] = d * 64 + (((pos >> 3) ^ swz_t32(d)) << 4) + 2 * (pos & 7);
     }
-    // natural K/V tile rows of this lane's key (row 32*wave + lr)
-    int kv_base, kv_x;
-    {
-        const int row = 32 * wave + lr;
-        const int sw = swz<D>(row);
-        kv_base = row * D * 2 + 16 * (hf ^ (sw & 1));
-        kv_x = sw >> 1;
-    }
+    // A operands: Q / dO row lr, chunk 2kc + hf; the V rows (B operand) of
+    // this wave's keys use the same pattern 32 rows further per wave
+    // (2kc + hf) ^ x = 2 (kc ^ x/2) + ((hf ^ x) & 1): one base and one XOR mask
+    const int ro_x = swz_kv<D>(lr);
+    const int ro_base = lr * D * 2 + (((hf ^ ro_x) & 1) << 4), ro_xh = ro_x >> 1;
+    auto row_off = [&](int kc) { return ro_base + ((kc ^ ro_xh) << 5); };
+    // Q^T / dO^T row 32md + lr, 16-row chunk c (stored chunk 2c + hf)
+    int t_off[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) t_off[c] = lr * 64 + (((2 * c + hf) ^ swz_t32(lr)) << 4);
 
     const int w = worker_id(a.num_workers);
     const int t_begin = ld_uniform(a.worker_ptr + w), t_end = ld_uniform(a.worker_ptr + w + 1);
+    const int kv_tiles_per_row = (a.mask_kv_blocks + 1) >> 1;
 
-    for (int ti = t_begin; ti < t_end; ++ti) {
-        const int b = ld_uniform(a.tiles + 4 * ti + 0);
-        const int hd = ld_uniform(a.tiles + 4 * ti + 1);
-        const int n = ld_uniform(a.tiles + 4 * ti + 2);
-        const int work = ld_uniform(a.tiles + 4 * ti + 3);
-        const int kv0 = ld_uniform(a.kv_off + b);
-        const int L = ld_uniform(a.kv_off + b + 1) - kv0;
-        int q0, Lq, orow0;
+    struct KvTile {
+        int b, h, n, work, kv0, L, q0, Lq, orow0, r0;
+        const int* sp;
+    };
+    auto tile_info = [&](int ti) {
+        KvTile T;
+        T.b = ld_uniform(a.tiles + 4 * ti + 0);
+        T.h = ld_uniform(a.tiles + 4 * ti + 1);
+        T.n = ld_uniform(a.tiles + 4 * ti + 2);
+        T.work = ld_uniform(a.tiles + 4 * ti + 3);
+        T.kv0 = ld_uniform(a.kv_off + T.b);
+        T.L = ld_uniform(a.kv_off + T.b + 1) - T.kv0;
         if (BCAST) {
-            q0 = 0;
-            Lq = a.lq;
-            orow0 = b * a.lq;
+            T.q0 = 0;
+            T.Lq = a.lq;
+            T.orow0 = T.b * a.lq;
         } else {
-            q0 = ld_uniform(a.q_off + b);
-            Lq = ld_uniform(a.q_off + b + 1) - q0;
-            orow0 = q0;
+            T.q0 = ld_uniform(a.q_off + T.b);
+            T.Lq = ld_uniform(a.q_off + T.b + 1) - T.q0;
+            T.orow0 = T.q0;
         }
-        const int* sp = nullptr;
-        if (MODE == kSparse) sp = a.sp_idx + ld_uniform(a.sp_ptr + b * a.mask_kv_blocks + n);
-        const int r0 = (MODE == kCausal) ? (n * kBwdBlockN) / kBwdBlockM : 0;
-        auto qblk = [&](int i) -> int {
-            if (MODE == kSparse) return 2 * ld_uniform(sp + (i >> 1)) + (i & 1);
-            return r0 + i;
-        };
-        const int nmasked = (MODE == kCausal) ? min(2, work) : 0;
-        const int key = n * kBwdBlockN + wave * 32 + lr;   // local key of this lane
-        const int64_t kvrow0 = (int64_t)kv0 * rs + (int64_t)hd * D;
+        T.r0 = MODE == kCausal ? (T.n * kBwdBlockN) / kBwdBlockM : 0;
+        T.sp = nullptr;
+        if (MODE == kSparse) T.sp = a.sp_idx + ld_uniform(a.sp_ptr + T.b * kv_tiles_per_row + T.n);
+        return T;
+    };
+    // Q block (32-row block index in the sequence) at position i of a tile
+    auto q_block = [&](const KvTile& T, int i) -> int {
+        if (MODE == kSparse) return 4 * (ld_uniform(T.sp + (i >> 2)) >> 2) + (i & 3);
+        return T.r0 + i;
+    };
 
-        // Q / dO / LSE / delta of a block: global -> registers (raw values only:
-        // any arithmetic on a loaded value here would make the wave wait for
-        // the whole prefetch right away) -> LDS at the end of the iteration
-        u32x4 qv[4], dv[4];
-        float rowv = 0.f;
-        int ld_r = 0;   // Q block of the registers, for the zero fill at store time
-        auto gload = [&](int r) {
-            // unconditional loads from a row clamped into the sequence (Lq >= 1
-            // whenever a block exists); rows past the end are zeroed in sstore
-            ld_r = r;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int qi = min(r * kBwdBlockM + 4 * ld_qg + p, Lq - 1);
-                qv[p] = *(const u32x4*)(a.q + (int64_t)(q0 + qi) * rs + (int64_t)hd * D + 8 * (ld_dc & (CH - 1)));
-                dv[p] = *(const u32x4*)(a.d_o + (int64_t)(orow0 + qi) * rs + (int64_t)hd * D + 8 * (ld_dc & (CH - 1)));
-            }
-            {
-                // wave 0 loads LSE, wave 1 delta (a wave-uniform choice keeps the
-                // base pointers scalar)
-                const int qi = min(r * kBwdBlockM + lane, Lq - 1);
-                const int64_t idx = (int64_t)hd * a.total_q + orow0 + qi;
-                if (wave == 0) rowv = a.lse[idx];
-                else if (wave == 1) rowv = a.delta[idx];
-            }
-        };
-        auto sstore = [&]() {
-            if (ld_on) {
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    if (ld_r * kBwdBlockM + 4 * ld_qg + p >= Lq) {
-                        qv[p] = u32x4{};
-                        dv[p] = u32x4{};
-                    }
-                }
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const int o = nat_off<D>(4 * ld_qg + p, ld_dc);
-                    *(u32x4*)lds(LY::QN + o) = qv[p];
-                    *(u32x4*)lds(LY::DN + o) = dv[p];
-                }
-                u32x2 y[8];
-                const int pos2 = 2 * sigma_pos(4 * ld_qg);
-                transpose4x8(qv, y);
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    *(u32x2*)lds(LY::QT + (8 * ld_dc + e) * (kBwdBlockM + 8) * 2 + pos2) = y[e];
-                transpose4x8(dv, y);
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    *(u32x2*)lds(LY::DT + (8 * ld_dc + e) * (kBwdBlockM + 8) * 2 + pos2) = y[e];
-            }
-            // LSE in the exp2 domain; a row without keys (LSE = -inf) or outside
-            // the sequence gets +inf so that its P is 0
-            const bool in_seq = ld_r * kBwdBlockM + lane < Lq;
-            if (wave == 0)
-                ((float*)lds(LY::LSE))[lane] = (!in_seq || rowv == -INFINITY) ? INFINITY : rowv * kLog2e;
-            else if (wave == 1)
-                ((float*)lds(LY::DELTA))[lane] = in_seq ? rowv : 0.f;
-        };
-
-        // ---- tile prologue: the K and V tiles are loaded as whole rows, stored
-        // to LDS, then each wave reads its K fragments; block 0 is loaded
-        // meanwhile
-        {
-            u32x4 kx[KPASS][4], vx[KPASS][4];
-#pragma unroll
-            for (int pass = 0; pass < KPASS; ++pass)
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const int kk = min(n * kBwdBlockN + KPP * pass + 4 * tkg + p, L - 1);
-                    kx[pass][p] = *(const u32x4*)(a.k + kvrow0 + (int64_t)kk * rs + 8 * tdc);
-                    vx[pass][p] = *(const u32x4*)(a.v + kvrow0 + (int64_t)kk * rs + 8 * tdc);
-                }
-#pragma unroll
-            for (int pass = 0; pass < KPASS; ++pass) {
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const int kl = KPP * pass + 4 * tkg + p;   // key within the tile
-                    if (n * kBwdBlockN + kl >= L) {
-                        kx[pass][p] = u32x4{};
-                        vx[pass][p] = u32x4{};
-                    }
-                    const int o = nat_off<D>(kl, tdc);
-                    *(u32x4*)lds(LY::KN + o) = kx[pass][p];
-                    *(u32x4*)lds(LY::VN + o) = vx[pass][p];
-                }
-            }
+    // ---- loader: the worker's Q/dO blocks in plan order, kAhead blocks ahead
+    int l_ti = t_begin, l_i = 0, l_slot = 0;
+    KvTile LT;
+    LT.work = 0;
+    auto l_settle = [&]() {
+        while (l_i >= LT.work) {
+            ++l_ti;
+            l_i = 0;
+            if (l_ti >= t_end) return;
+            LT = tile_info(l_ti);
         }
+    };
+    // row values of the loader's latest block: wave 0 lanes 0-31 LSE, 32-63
+    // delta of rows 0..31 (raw, with a flag for rows inside the sequence; made
+    // into exp2-domain values when written to LDS one iteration later)
+    float pend_v = 0.f;
+    bool pend_in = false;
+    // rows past the sequence are clamped to its last row (finite data; their
+    // LSE is set to +inf so that P = 0)
+    auto l_issue = [&]() {
+        if (l_ti >= t_end) return;
+        const int rb = q_block(LT, l_i);
+        char* dst = smem + LY::RING + (l_slot % kSlots) * LY::SLOT;
+        const int64_t hq = (int64_t)LT.h * D;
+        // copy u of this wave is copy g = QPW*wave + u of the block (first
+        // half Q, second half dO) and fills chunk positions 64 (g mod QH) +
+        // lane: row r, stored chunk cp (g and the tensor are wave-uniform)
+#pragma unroll
+        for (int u = 0; u < QPW; ++u) {
+            const int g = QPW * wave + u;
+            const bool is_do = g >= QH;
+            const int p = 64 * (g % QH) + lane;
+            const int r = p / CH, cp = p % CH;
+            const int qi = min(kBwdBlockM * rb + r, LT.Lq - 1);
+            const int64_t off = hq + 8 * (cp ^ swz_kv<D>(r));
+            const uint16_t* src = is_do ? a.d_o + (int64_t)(LT.orow0 + qi) * rs + off
+                                        : a.q + (int64_t)(LT.q0 + qi) * rs + off;
+            load_lds16(src, dst + (is_do ? LY::QB : 0) + 1024 * (g % QH));
+        }
+        if (wave == 0) {
+            const int row = kBwdBlockM * rb + lr;
+            const int qi = min(row, LT.Lq - 1);
+            const int64_t idx = (int64_t)LT.h * a.total_q + LT.orow0 + qi;
+            pend_v = hf ? a.delta[idx] : a.lse[idx];
+            pend_in = row < LT.Lq;
+        }
+        ++l_slot;
+        ++l_i;
+        l_settle();
+    };
+    auto put_rowvals = [&](int s) {   // row values of block s (loaded one step earlier)
+        if (wave == 0) {
+            float* rv = (float*)(smem + LY::RING + (s % kSlots) * LY::SLOT + LY::ROWV);
+            float x;
+            if (hf == 0) x = (!pend_in || pend_v == -INFINITY) ? INFINITY : pend_v * kLog2e;
+            else x = pend_in ? pend_v : 0.f;
+            rv[lane] = x;
+        }
+    };
+    // Q and dO of block s (slot s % kSlots) -> Q^T, dO^T (buffer s % 2)
+    auto transpose_q = [&](int s) {
+        const char* src = smem + LY::RING + (s % kSlots) * LY::SLOT;
+        char* dst = smem + LY::T + (s & 1) * LY::TBUF;
+        bf16x4 x[2 * TPW];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int u = 0; u < TPW; ++u)
+                x[TPW * t + u] = lds_read_tr((const uint16_t*)(src + t * LY::QB + tr_src[u]));
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int u = 0; u < TPW; ++u) *(bf16x4*)(dst + t * LY::QB + tr_dst[u]) = x[TPW * t + u];
+    };
+
+    if (t_begin < t_end) {
+        LT = tile_info(t_begin);
+        l_settle();
+    }
+    int total = 0;   // stream length
+    for (int ti = t_begin; ti < t_end; ++ti) total += ld_uniform(a.tiles + 4 * ti + 3);
+    if (total > 0) {   // block 0 landed and prepared, block 1 in flight
+        l_issue();
+        wait_vmem();
         __syncthreads();
-        if (work > 0) gload(qblk(0));
-        // this wave's K rows as MFMA B operands (keys on lanes); its V rows are
-        // read from LDS where they are used
-        bf16x8 kf[KC];
+        put_rowvals(0);
+        transpose_q(0);
+        l_issue();
+    }
+
+    int s = 0;   // stream position of the consumer
+    for (int ti = t_begin; ti < t_end; ++ti) {
+        const KvTile T = tile_info(ti);
+        const int key0 = T.n * kBwdBlockN + 32 * wave;   // first key of this wave (tile-local)
+        const bool wave_keys = key0 < T.L;               // wave-uniform
+        const int64_t kvrow0 = (int64_t)T.kv0 * rs + (int64_t)T.h * D;
+        // ---- tile start: V tile to LDS, this wave's K rows to VGPRs (keys
+        // past the sequence are clamped to its last row; their dK/dV are not
+        // stored). Every wave is past the previous tile's epilogue staging.
+        __syncthreads();
+        // V tile copies: copy u fills chunk positions 64 (VPW wave + u) + lane
+        // (addresses recomputed per tile rather than kept live across it)
+        const int lane_t = opaque(lane);
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-            kf[kc] = __builtin_bit_cast(bf16x8, *(const u32x4*)lds(LY::KN + kv_base + 32 * (kc ^ kv_x)));
+        for (int u = 0; u < VPW; ++u) {
+            const int p = 64 * (VPW * wave + u) + lane_t;
+            const int r = p / CH, cp = p % CH;
+            const int key = min(T.n * kBwdBlockN + r, T.L - 1);
+            load_lds16(a.v + kvrow0 + (int64_t)key * rs + 8 * (cp ^ swz_kv<D>(r)),
+                       smem + LY::V + 1024 * (VPW * wave + u));
+        }
+        bf16x8 kf[KC];
+        {
+            const int key = min(key0 + lr, T.L - 1);
+            const uint16_t* kp = a.k + kvrow0 + (int64_t)key * rs + 8 * hf;
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) kf[kc] = load_bf16x8(kp + 16 * kc);
+        }
+        wait_vmem();
+        __syncthreads();
         f32x16 dk_acc[MD], dv_acc[MD];
 #pragma unroll
         for (int md = 0; md < MD; ++md) {
             dk_acc[md] = f32x16{};
             dv_acc[md] = f32x16{};
         }
-        __syncthreads();   // region R changes from K/V to the Q-block tiles
-        if (work > 0) sstore();
-        // block 0 landed; nothing left in flight (see wait_vmem)
-        wait_vmem();
-        __syncthreads();
+        const char* vb = smem + LY::V + 32 * wave * D * 2;   // this wave's V rows
 
-        auto body = [&](int i, auto masked_tag) {
-            constexpr bool MASKED = decltype(masked_tag)::value;
-            const int r = qblk(i);
-            if (i + 1 < work) gload(qblk(i + 1));
+        for (int i = 0; i < T.work; ++i, ++s) {
+            if (i > 0) wait_vmem();   // block s+1 landed (the only copies in flight)
+            // every wave is past block s-1: its slot and transposed buffer are free
+            __syncthreads();
+            if (s + 1 < total) put_rowvals(s + 1);
+            l_issue();                               // block s+kAhead
+            if (s + 1 < total) transpose_q(s + 1);   // Q^T, dO^T of block s+1
 
-            // the block in two halves of 32 query rows (mb), to keep the live
-            // register set small
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                f32x16 s = f32x16{}, dp = f32x16{};
+            const int rb = q_block(T, i);
+            bool skip = !wave_keys, masked = false;
+            if (MODE == kCausal) {
+                skip = skip || kBwdBlockM * rb + kBwdBlockM - 1 < key0;
+                masked = kBwdBlockM * rb < key0 + 31;
+            } else if (MODE == kSparse) {
+                skip = skip || !((ld_uniform(T.sp + (i >> 2)) >> (wave >> 2)) & 1);
+            }
+            if (skip) continue;
+            const char* qb = smem + LY::RING + (s % kSlots) * LY::SLOT;
+            const char* db = qb + LY::QB;
+            const float* rv = (const float*)(qb + LY::ROWV);
+            const char* qt = smem + LY::T + (s & 1) * LY::TBUF;
+            const char* dt = qt + LY::QB;
+
+            f32x16 sc = f32x16{}, dp = f32x16{};
+            {
+                bf16x8 qa[KC], da[KC], vf[KC];
 #pragma unroll
                 for (int kc = 0; kc < KC; ++kc) {
-                    const int off = nat_base[mb] + 32 * (kc ^ nat_x[mb]);
-                    const bf16x8 qa = __builtin_bit_cast(bf16x8, *(const u32x4*)lds(LY::QN + off));
-                    s = mfma32(qa, kf[kc], s);
-                    const bf16x8 da = __builtin_bit_cast(bf16x8, *(const u32x4*)lds(LY::DN + off));
-                    const bf16x8 vb =
-                        __builtin_bit_cast(bf16x8, *(const u32x4*)lds(LY::VN + kv_base + 32 * (kc ^ kv_x)));
-                    dp = mfma32(da, vb, dp);
+                    qa[kc] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qb + row_off(kc)));
+                    da[kc] = __builtin_bit_cast(bf16x8, *(const u32x4*)(db + row_off(kc)));
+                    vf[kc] = __builtin_bit_cast(bf16x8, *(const u32x4*)(vb + row_off(kc)));
                 }
-                // P and dS; register r is query row 32mb + 8(r/4) + 4hf + r%4
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int row = 32 * mb + 8 * g + 4 * hf;
-                    const f32x4 l4 = *(const f32x4*)lds(LY::LSE + 4 * row);
-                    const f32x4 d4 = *(const f32x4*)lds(LY::DELTA + 4 * row);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        float p = __builtin_amdgcn_exp2f(s[4 * g + j] * a.scale_log2 - l4[j]);
-                        if (MASKED) {
-                            if (key > r * kBwdBlockM + row + j) p = 0.f;
-                        }
-                        s[4 * g + j] = p;
-                        dp[4 * g + j] = p * (dp[4 * g + j] - d4[j]);
-                    }
+                for (int kc = 0; kc < KC; ++kc) {
+                    sc = mfma32(qa[kc], kf[kc], sc);
+                    dp = mfma32(da[kc], vf[kc], dp);
                 }
-                // dV^T += dO^T P ; dK^T += Q^T dS over this half's 32 query rows
-                // (16-row chunks c = 2mb, 2mb + 1)
+                // two d chunks of reads ahead, then 2 MFMAs per 3 reads
+                __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
-                for (int cc = 0; cc < 2; ++cc) {
-                    const int c = 2 * mb + cc;
-                    f32x8 x, y;
+                for (int kc = 2; kc < KC; ++kc) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            }
+            // P and dS; register r is query row 32rb + 8(r/4) + 4hf + r%4, the
+            // column this lane's key 32wave + lr (tile-local)
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        x[j] = s[8 * cc + j];
-                        y[j] = dp[8 * cc + j];
+            for (int g = 0; g < 4; ++g) {
+                const int row = 8 * g + 4 * hf;
+                const f32x4 l4 = *(const f32x4*)(rv + row);
+                const f32x4 d4 = *(const f32x4*)(rv + 32 + row);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float p = __builtin_amdgcn_exp2f(fmaf(sc[4 * g + j], a.scale_log2, -l4[j]));
+                    if (MODE == kCausal && masked) {
+                        if (key0 + lr > kBwdBlockM * rb + row + j) p = 0.f;
                     }
-                    const bf16x8 pb = to_bf16x8(x), sb = to_bf16x8(y);
-#pragma unroll
-                    for (int md = 0; md < MD; ++md) {
-                        const int o = (32 * md + lr) * (kBwdBlockM + 8) * 2 + (16 * c + 8 * hf) * 2;
-                        const bf16x8 da = __builtin_bit_cast(bf16x8, *(const u32x4*)lds(LY::DT + o));
-                        dv_acc[md] = mfma32(da, pb, dv_acc[md]);
-                        const bf16x8 qa = __builtin_bit_cast(bf16x8, *(const u32x4*)lds(LY::QT + o));
-                        dk_acc[md] = mfma32(qa, sb, dk_acc[md]);
-                    }
+                    sc[4 * g + j] = p;
+                    dp[4 * g + j] = p * (dp[4 * g + j] - d4[j]);
                 }
             }
-            // every wave is done with this block's tiles before they are replaced
-            __syncthreads();
-            if (i + 1 < work) sstore();
-            __syncthreads();
-        };
+            bf16x8 pb[2], sb[2];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                f32x8 x, y;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    x[j] = sc[8 * c + j];
+                    y[j] = dp[8 * c + j];
+                }
+                pb[c] = to_bf16x8(x);
+                sb[c] = to_bf16x8(y);
+            }
+            // dV^T += dO^T P ; dK^T += Q^T dS over the block's 32 rows
+            {
+                bf16x8 dta[2 * MD], qta[2 * MD];
+#pragma unroll
+                for (int j = 0; j < 2 * MD; ++j) {
+                    const int o = 32 * 64 * (j >> 1) + t_off[j & 1];
+                    dta[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(dt + o));
+                    qta[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qt + o));
+                }
+#pragma unroll
+                for (int j = 0; j < 2 * MD; ++j) {
+                    dv_acc[j >> 1] = mfma32(dta[j], pb[j & 1], dv_acc[j >> 1]);
+                    dk_acc[j >> 1] = mfma32(qta[j], sb[j & 1], dk_acc[j >> 1]);
+                }
+                pipeline_reads_mfma<4 * MD, kReadAhead>();
+            }
+        }
 
-        int i = 0;
-        for (; i < nmasked; ++i) body(i, std::true_type{});
-        for (; i < work; ++i) body(i, std::false_type{});
-
-        // ---- tile epilogue: stage dK = scale * (dK^T)^T and dV (bf16) in region
-        // R as natural rows, then write whole rows to global memory
-        {
-            const int row = wave * 32 + lr;
+        // ---- tile epilogue: dK = scale * (dK^T)^T and dV as bf16 rows, through
+        // this wave's part of the V tile (free once every wave is done with V)
+        __syncthreads();
+        char* st = smem + LY::V + wave * LY::ST_WAVE;
+        const int lane_e = opaque(lane), lr_e = lane_e & 31, hf_e = lane_e >> 5;
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
             for (int md = 0; md < MD; ++md)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    f32x4 x, y;
+                    f32x4 x;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        x[j] = dk_acc[md][4 * g + j] * a.scale;
-                        y[j] = dv_acc[md][4 * g + j];
-                    }
-                    const int o = nat_off<D>(row, 4 * md + g) + 8 * hf;
-                    *(u32x2*)lds(LY::DKS + o) = __builtin_bit_cast(u32x2, to_bf16x4(x));
-                    *(u32x2*)lds(LY::DVS + o) = __builtin_bit_cast(u32x2, to_bf16x4(y));
+                    for (int j = 0; j < 4; ++j)
+                        x[j] = pass == 0 ? dk_acc[md][4 * g + j] * a.scale : dv_acc[md][4 * g + j];
+                    const int chunk = 4 * md + g;
+                    *(bf16x4*)(st + lr_e * D * 2 + ((chunk ^ (lr_e & (CH - 1))) << 4) + 8 * hf_e) =
+                        to_bf16x4(x);
                 }
-        }
-        __syncthreads();
+            wave_sync_lds();
+            uint16_t* out = pass == 0 ? a.dk : a.dv;
 #pragma unroll
-        for (int pass = 0; pass < KPASS; ++pass)
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int kl = KPP * pass + 4 * tkg + p;
-                const int o = nat_off<D>(kl, tdc);
-                const u32x4 xk = *(const u32x4*)lds(LY::DKS + o);
-                const u32x4 xv = *(const u32x4*)lds(LY::DVS + o);
-                if (n * kBwdBlockN + kl < L) {
-                    const int64_t g = kvrow0 + (int64_t)(n * kBwdBlockN + kl) * rs + 8 * tdc;
-                    *(u32x4*)(a.dk + g) = xk;
-                    *(u32x4*)(a.dv + g) = xv;
-                }
+            for (int v = 0; v < 32 * CH / 64; ++v) {
+                const int k = lane_e + 64 * v;
+                const int r = k / CH, chunk = k % CH;
+                const u32x4 x = *(const u32x4*)(st + r * D * 2 + ((chunk ^ (r & (CH - 1))) << 4));
+                if (key0 + r < T.L)
+                    *(u32x4*)(out + kvrow0 + (int64_t)(key0 + r) * rs + 8 * chunk) = x;
             }
-        // LDS is rewritten by the next tile
-        __syncthreads();
+            wave_sync_lds();
+        }
     }
 }
 

@@ -100,6 +100,14 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// The value of x, opaque to the optimiser: values derived from it are
+// recomputed where they are used instead of being hoisted out of loops (and
+// then spilled when registers are short).
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // Load of a wave-uniform value from memory the kernel never writes (plans,
 // offsets), through the constant address space so that it becomes a scalar
 // load: a vector load would need a vmcnt wait, which also waits for every

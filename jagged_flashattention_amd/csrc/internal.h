@@ -9,12 +9,13 @@ namespace jfa {
 
 // Tile geometry. Forward (and the Q-stationary dQ pass): a workgroup of 8
 // waves owns 256 query rows (32 per wave) and streams 64-key K/V blocks.
-// Backward: a workgroup owns a 128-key KV tile (32 keys per wave) and streams
-// 64-row Q/dO blocks. The block-sparse mask has 128-row x 128-key granularity.
+// dK/dV pass: a workgroup of 8 waves owns a 256-key KV tile (32 keys per
+// wave) and streams 32-row Q/dO blocks. The block-sparse mask has 128-row x
+// 128-key granularity.
 constexpr int32_t kFwdBlockM = 256;
 constexpr int32_t kFwdBlockN = 64;
-constexpr int32_t kBwdBlockM = 64;
-constexpr int32_t kBwdBlockN = 128;
+constexpr int32_t kBwdBlockM = 32;
+constexpr int32_t kBwdBlockN = 256;
 constexpr int32_t kMaskBlock = 128;
 
 int32_t check_problem(const jfa_problem* p);

@@ -107,6 +107,24 @@ inline int32_t fwd_bits(const jfa_problem* p, const uint8_t* mask, int32_t b, in
     return bits;
 }
 
+// Mask columns per backward KV tile.
+constexpr int32_t kColsPerTile = kBwdBlockN / kMaskBlock;
+static_assert(kColsPerTile * kMaskBlock == kBwdBlockN && kColsPerTile <= 2, "tile/mask geometry");
+
+// Bits of the mask columns of backward KV tile (b, t) that keep 128-row mask
+// row m (bit k: column kColsPerTile*t + k; columns past the mask or the
+// sequence count as not keeping it).
+inline int32_t bwd_bits(const jfa_problem* p, const uint8_t* mask, int32_t b, int32_t t, int32_t m,
+                        int32_t lk) {
+    int32_t bits = 0;
+    for (int32_t k = 0; k < kColsPerTile; ++k) {
+        const int32_t c = kColsPerTile * t + k;
+        if (c < p->mask_kv_blocks && (int64_t)kMaskBlock * c < lk && kept(p, mask, b, m, c))
+            bits |= 1 << k;
+    }
+    return bits;
+}
+
 int32_t tile_work(const jfa_problem* p, const uint8_t* mask, int32_t pass, int32_t b, int32_t t,
                   int32_t lq, int32_t lk) {
     const bool sparse = p->mask_q_blocks != 0;
@@ -126,11 +144,12 @@ int32_t tile_work(const jfa_problem* p, const uint8_t* mask, int32_t pass, int32
     }
     const int32_t nqb = (int32_t)cdiv(lq, kBwdBlockM);
     if (sparse) {
-        const int32_t c = t * kBwdBlockN / kMaskBlock;
-        int32_t w = 0;
-        for (int32_t r = 0; r < nqb; ++r)
-            if (kept(p, mask, b, r * kBwdBlockM / kMaskBlock, c)) ++w;
-        return w;
+        int64_t w = 0;
+        for (int32_t m = 0; m < cdiv(lq, kMaskBlock); ++m)
+            if (bwd_bits(p, mask, b, t, m, lk))
+                w += cdiv(std::min<int64_t>((int64_t)kMaskBlock * (m + 1), lq) - (int64_t)kMaskBlock * m,
+                          kBwdBlockM);
+        return (int32_t)w;
     }
     if (p->causal) return nqb - (int32_t)(((int64_t)t * kBwdBlockN) / kBwdBlockM);
     return nqb;
@@ -179,6 +198,7 @@ int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, co
     // block-sparse lists
     int64_t sp_rows = 0, sp_nnz = 0;
     const int32_t fwd_rows = (int32_t)cdiv(p->mask_q_blocks, kRowsPerTile);
+    const int32_t bwd_cols = (int32_t)cdiv(p->mask_kv_blocks, kColsPerTile);
     if (sparse) {
         if (qtiles) {
             sp_rows = (int64_t)p->batch * fwd_rows;
@@ -187,11 +207,11 @@ int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, co
                     for (int32_t c = 0; c < cdiv(L.kv[b], kMaskBlock); ++c)
                         sp_nnz += fwd_bits(p, mask, b, t, c, L.q[b]) != 0;
         } else {
-            sp_rows = (int64_t)p->batch * p->mask_kv_blocks;
+            sp_rows = (int64_t)p->batch * bwd_cols;
             for (int32_t b = 0; b < p->batch; ++b)
-                for (int32_t c = 0; c < p->mask_kv_blocks; ++c)
+                for (int32_t t = 0; t < bwd_cols; ++t)
                     for (int32_t m = 0; m < cdiv(L.q[b], kMaskBlock); ++m)
-                        sp_nnz += kept(p, mask, b, m, c);
+                        sp_nnz += bwd_bits(p, mask, b, t, m, L.kv[b]) != 0;
         }
         if (sp_rows > INT32_MAX - 1 || sp_nnz > INT32_MAX) return JFA_ERR_INVALID_ARG;
     }
@@ -278,9 +298,11 @@ int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, co
                 }
         } else {
             for (int32_t b = 0; b < p->batch; ++b)
-                for (int32_t c = 0; c < p->mask_kv_blocks; ++c) {
-                    for (int32_t m = 0; m < cdiv(L.q[b], kMaskBlock); ++m)
-                        if (kept(p, mask, b, m, c)) sp_idx[n++] = m;
+                for (int32_t t = 0; t < bwd_cols; ++t) {
+                    for (int32_t m = 0; m < cdiv(L.q[b], kMaskBlock); ++m) {
+                        const int32_t bits = bwd_bits(p, mask, b, t, m, L.kv[b]);
+                        if (bits) sp_idx[n++] = 4 * m + bits;
+                    }
                     sp_ptr[++r] = n;
                 }
         }

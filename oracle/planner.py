@@ -20,8 +20,8 @@ plainest readings, written out step by step here, are:
     backward (Q blocks of ``block_m`` rows visited):
       dense        ceil(Lq_b / block_m)
       causal       ceil(Lq_b / block_m) - floor(t*block_n / block_m)
-      block-sparse number of Q blocks r < ceil(Lq_b / block_m) whose 128-row
-                   mask row keeps the tile's 128-key mask column
+      block-sparse sum over the 128-row mask rows m kept by any mask column
+                   of the tile of ceil((min(128(m+1), Lq_b) - 128m) / block_m)
  3. Stable sort by work, descending (ties keep enumeration order).
  4. Deal in snake order over W workers: sorted tile i goes to worker i mod W
     when floor(i / W) is even, else to W - 1 - (i mod W).
@@ -48,7 +48,11 @@ variant only adds iteration over the selected blocks). The mask is uint8
            ascending, each stored as 4 c + sum_k 2^k [row R t + k keeps c]
            (R <= 2). A tile visits the union of its rows' blocks; each row
            skips the blocks its own mask row drops.
-  backward CSC over columns (b, c), c < NK: kept m < ceil(Lq_b/128), ascending
+  backward CSC over the KV tiles (b, t) of block_n = C * 128 keys,
+           t < ceil(NK / C): the 128-row mask rows m < ceil(Lq_b/128) kept by
+           at least one of the tile's mask columns c = C t + k (c < NK,
+           128 c < Lk_b), ascending, each stored as 4 m + sum_k 2^k [column
+           C t + k keeps m] (C <= 2).
 """
 from __future__ import annotations
 
@@ -87,8 +91,21 @@ def _fwd_row_entries(block_mask, b, t, lq_b, lk_b, block_m):
     return out
 
 
-def sparse_lists(block_mask, q_lens, kv_lens, pass_, *, block_m=MASK_BLOCK):
-    """(ptr, idx) int32: forward CSR over Q tiles (b, t) or backward CSC over (b, c)."""
+def _bwd_col_entries(block_mask, b, t, lq_b, lk_b, block_n):
+    """Backward list of KV tile (b, t): [(m, bits)] for the kept union, ascending m."""
+    _, NQ, NK = block_mask.shape
+    C = block_n // MASK_BLOCK
+    cols = [c for c in range(C * t, C * t + C) if c < NK and MASK_BLOCK * c < lk_b]
+    out = []
+    for m in range(min(cdiv(lq_b, MASK_BLOCK), NQ)):
+        bits = sum(1 << (c - C * t) for c in cols if block_mask[b, m, c])
+        if bits:
+            out.append((m, bits))
+    return out
+
+
+def sparse_lists(block_mask, q_lens, kv_lens, pass_, *, block_m=MASK_BLOCK, block_n=MASK_BLOCK):
+    """(ptr, idx) int32: forward CSR over Q tiles (b, t) or backward CSC over KV tiles (b, t)."""
     B, NQ, NK = block_mask.shape
     ptr, idx = [0], []
     if pass_ == FWD:
@@ -101,12 +118,13 @@ def sparse_lists(block_mask, q_lens, kv_lens, pass_, *, block_m=MASK_BLOCK):
                     idx.append(4 * c + bits)
                 ptr.append(len(idx))
     else:
+        C = block_n // MASK_BLOCK
+        assert C * MASK_BLOCK == block_n and 1 <= C <= 2
         for b in range(B):
-            nq = cdiv(int(q_lens[b]), MASK_BLOCK)
-            for c in range(NK):
-                for m in range(min(nq, NQ)):
-                    if block_mask[b, m, c]:
-                        idx.append(m)
+            for t in range(cdiv(NK, C)):
+                for m, bits in _bwd_col_entries(block_mask, b, t, int(q_lens[b]),
+                                                int(kv_lens[b]), block_n):
+                    idx.append(4 * m + bits)
                 ptr.append(len(idx))
     return np.array(ptr, dtype=np.int32), np.array(idx, dtype=np.int32)
 
@@ -121,8 +139,8 @@ def _tile_work(pass_, b, t, lq_b, lk_b, *, block_m, block_n, causal, block_mask)
         return cdiv(lk_b, block_n)
     nqb = cdiv(lq_b, block_m)
     if block_mask is not None:
-        c = t * block_n // MASK_BLOCK
-        return sum(1 for r in range(nqb) if block_mask[b, r * block_m // MASK_BLOCK, c])
+        return sum(cdiv(min(MASK_BLOCK * (m + 1), lq_b) - MASK_BLOCK * m, block_m)
+                   for m, _ in _bwd_col_entries(block_mask, b, t, lq_b, lk_b, block_n))
     if causal:
         return nqb - (t * block_n) // block_m
     return nqb

@@ -6,7 +6,7 @@ import jagged_flashattention_amd as J
 import workloads as W
 from oracle import planner as OP
 
-FWD_BM, FWD_BN, BWD_BM, BWD_BN = 256, 64, 64, 128
+FWD_BM, FWD_BN, BWD_BM, BWD_BN = 256, 64, 32, 256
 
 
 def _problem_of(x):
@@ -52,7 +52,7 @@ def test_cpp_plan_equals_oracle_plan(cfg, workers, pass_):
     assert hp.info.block_m == bm and hp.info.block_n == bn
     assert hp.info.total_kv == int(kv_off[-1])
     if mask is not None:
-        sp, si = OP.sparse_lists(mask, q_lens, lens, pass_, block_m=bm)
+        sp, si = OP.sparse_lists(mask, q_lens, lens, pass_, block_m=bm, block_n=bn)
         assert np.array_equal(hp.sparse_ptr, sp)
         assert np.array_equal(hp.sparse_idx, si)
     else:
@@ -118,7 +118,7 @@ def test_cpp_plan_random_small_problems():
             assert np.array_equal(hp.worker_ptr, wp), (trial, pass_)
             assert np.array_equal(hp.tiles, tiles), (trial, pass_)
             if mask is not None:
-                sp, si = OP.sparse_lists(mask, q_lens, lens, pass_, block_m=bm)
+                sp, si = OP.sparse_lists(mask, q_lens, lens, pass_, block_m=bm, block_n=bn)
                 assert np.array_equal(hp.sparse_ptr, sp) and np.array_equal(hp.sparse_idx, si)
         hp = J.jfa_plan_build(prob, q_off, kv_off, mask, J.JFA_PASS_DQ, W_)
         wp, tiles = OP.plan_dq(q_lens, lens, H, W_, broadcast_q=bool(prob.broadcast_q),

@@ -40,7 +40,8 @@ def _cases():
 
 
 @pytest.mark.parametrize("name,qlens,kvlens,causal,mask", _cases())
-@pytest.mark.parametrize("pass_,bm,bn", [(P.FWD, 256, 64), (P.FWD, 128, 64), (P.BWD, 64, 128)])
+@pytest.mark.parametrize("pass_,bm,bn", [(P.FWD, 256, 64), (P.FWD, 128, 64), (P.BWD, 32, 256),
+                                         (P.BWD, 64, 128)])
 @pytest.mark.parametrize("workers", [1, 7, 16, 255])
 def test_plan_properties(name, qlens, kvlens, causal, mask, pass_, bm, bn, workers):
     H = 3
@@ -111,8 +112,24 @@ def test_sparse_lists_by_scan():
     for b in range(5):
         for c in range(8):
             r = b * 8 + c
-            want = [m for m in range(2) if mask[b, m, c] and 128 * m < qlens[b]]
+            want = [4 * m + 1 for m in range(2) if mask[b, m, c] and 128 * m < qlens[b]
+                    and 128 * c < lens[b]]
             assert list(idx[ptr[r]:ptr[r + 1]]) == want
+    # 256-key tiles: the union of the two columns' kept rows, one bit per
+    # column; a column past the sequence keeps nothing
+    ptr, idx = P.sparse_lists(mask, qlens, lens, P.BWD, block_n=256)
+    assert len(ptr) == 5 * 4 + 1
+    for b in range(5):
+        for t in range(4):
+            want = []
+            for m in range(2):
+                if 128 * m >= qlens[b]:
+                    continue
+                bits = sum(1 << k for k in range(2)
+                           if mask[b, m, 2 * t + k] and 128 * (2 * t + k) < lens[b])
+                if bits:
+                    want.append(4 * m + bits)
+            assert list(idx[ptr[b * 4 + t]:ptr[b * 4 + t + 1]]) == want
 
 
 def test_offsets_from_lengths():
