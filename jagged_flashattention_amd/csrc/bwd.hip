@@ -221,36 +221,35 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
         l_issue();
     }
 
-    int s = 0;   // stream position of the consumer
-    for (int ti = t_begin; ti < t_end; ++ti) {
-        const KvTile T = tile_info(ti);
-        const int key0 = T.n * kBwdBlockN + 32 * wave;   // first key of this wave (tile-local)
-        const bool wave_keys = key0 < T.L;               // wave-uniform
+    // V tile of T to LDS and this wave's K rows of T to VGPRs (keys past the
+    // sequence are clamped to its last row; their dK/dV are not stored). The
+    // addresses are recomputed per tile rather than kept live across it.
+    bf16x8 kf[KC];
+    auto load_kv = [&](const KvTile& T) {
         const int64_t kvrow0 = (int64_t)T.kv0 * rs + (int64_t)T.h * D;
-        // ---- tile start: V tile to LDS, this wave's K rows to VGPRs (keys
-        // past the sequence are clamped to its last row; their dK/dV are not
-        // stored). Every wave is past the previous tile's epilogue staging.
-        __syncthreads();
-        // V tile copies: copy u fills chunk positions 64 (VPW wave + u) + lane
-        // (addresses recomputed per tile rather than kept live across it)
         const int lane_t = opaque(lane);
 #pragma unroll
-        for (int u = 0; u < VPW; ++u) {
+        for (int u = 0; u < VPW; ++u) {   // copy u fills chunk positions 64 (VPW wave + u) + lane
             const int p = 64 * (VPW * wave + u) + lane_t;
             const int r = p / CH, cp = p % CH;
             const int key = min(T.n * kBwdBlockN + r, T.L - 1);
             load_lds16(a.v + kvrow0 + (int64_t)key * rs + 8 * (cp ^ swz_kv<D>(r)),
                        smem + LY::V + 1024 * (VPW * wave + u));
         }
-        bf16x8 kf[KC];
-        {
-            const int key = min(key0 + lr, T.L - 1);
-            const uint16_t* kp = a.k + kvrow0 + (int64_t)key * rs + 8 * hf;
+        const int key = min(T.n * kBwdBlockN + 32 * wave + (lane_t & 31), T.L - 1);
+        const uint16_t* kp = a.k + kvrow0 + (int64_t)key * rs + 8 * (lane_t >> 5);
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) kf[kc] = load_bf16x8(kp + 16 * kc);
-        }
-        wait_vmem();
-        __syncthreads();
+        for (int kc = 0; kc < KC; ++kc) kf[kc] = load_bf16x8(kp + 16 * kc);
+    };
+    if (t_begin < t_end) load_kv(tile_info(t_begin));
+    wait_vmem();
+    __syncthreads();
+
+    int s = 0;   // stream position of the consumer
+    for (int ti = t_begin; ti < t_end; ++ti) {
+        const KvTile T = tile_info(ti);
+        const int key0 = T.n * kBwdBlockN + 32 * wave;   // first key of this wave (tile-local)
+        const bool wave_keys = key0 < T.L;               // wave-uniform
         f32x16 dk_acc[MD], dv_acc[MD];
 #pragma unroll
         for (int md = 0; md < MD; ++md) {
@@ -263,9 +262,13 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
             if (i > 0) wait_vmem();   // block s+1 landed (the only copies in flight)
             // every wave is past block s-1: its slot and transposed buffer are free
             __syncthreads();
-            if (s + 1 < total) put_rowvals(s + 1);
+            // (past the end of the stream these two work on stale, unread data)
+            put_rowvals(s + 1);
             l_issue();                               // block s+kAhead
-            if (s + 1 < total) transpose_q(s + 1);   // Q^T, dO^T of block s+1
+            // Q^T, dO^T of block s+1: here, or (dense) behind the S/dP MFMAs,
+            // where the extra live registers still fit
+            constexpr bool kLateTranspose = MODE == kDense;
+            if (!kLateTranspose) transpose_q(s + 1);
 
             const int rb = q_block(T, i);
             bool skip = !wave_keys, masked = false;
@@ -275,7 +278,10 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
             } else if (MODE == kSparse) {
                 skip = skip || !((ld_uniform(T.sp + (i >> 2)) >> (wave >> 2)) & 1);
             }
-            if (skip) continue;
+            if (skip) {
+                if (kLateTranspose) transpose_q(s + 1);
+                continue;
+            }
             const char* qb = smem + LY::RING + (s % kSlots) * LY::SLOT;
             const char* db = qb + LY::QB;
             const float* rv = (const float*)(qb + LY::ROWV);
@@ -305,6 +311,7 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             }
+            if (kLateTranspose) transpose_q(s + 1);
             // P and dS; register r is query row 32rb + 8(r/4) + 4hf + r%4, the
             // column this lane's key 32wave + lr (tile-local)
 #pragma unroll
@@ -352,37 +359,52 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
             }
         }
 
-        // ---- tile epilogue: dK = scale * (dK^T)^T and dV as bf16 rows, through
-        // this wave's part of the V tile (free once every wave is done with V)
+        // ---- tile end. Every wave is done with V, with block s-1's ring slot
+        // and with its transposed buffer: the next tile's V tile and K rows are
+        // fetched right away, and dK = scale * (dK^T)^T and dV leave as bf16
+        // rows through the free slot (waves 4-7) and transposed buffer (waves
+        // 0-3), 16 keys per wave at a time, meanwhile.
         __syncthreads();
-        char* st = smem + LY::V + wave * LY::ST_WAVE;
-        const int lane_e = opaque(lane), lr_e = lane_e & 31, hf_e = lane_e >> 5;
+        if (ti + 1 < t_end) load_kv(tile_info(ti + 1));
+        {
+            const int64_t kvrow0 = (int64_t)T.kv0 * rs + (int64_t)T.h * D;
+            char* st = wave < 4 ? smem + LY::T + ((s + 1) & 1) * LY::TBUF + wave * (16 * D * 2)
+                                : smem + LY::RING + ((s + kSlots - 1) % kSlots) * LY::SLOT + (wave - 4) * (16 * D * 2);
+            const int lane_e = opaque(lane), lr_e = lane_e & 31, hf_e = lane_e >> 5;
 #pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
+            for (int pass = 0; pass < 4; ++pass) {   // dK keys 0-15, 16-31, then dV
+                const int rd = pass & 1;
+                if ((lr_e >> 4) == rd) {
+                    const int r = lr_e & 15;
 #pragma unroll
-            for (int md = 0; md < MD; ++md)
+                    for (int md = 0; md < MD; ++md)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    f32x4 x;
+                        for (int g = 0; g < 4; ++g) {
+                            f32x4 x;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        x[j] = pass == 0 ? dk_acc[md][4 * g + j] * a.scale : dv_acc[md][4 * g + j];
-                    const int chunk = 4 * md + g;
-                    *(bf16x4*)(st + lr_e * D * 2 + ((chunk ^ (lr_e & (CH - 1))) << 4) + 8 * hf_e) =
-                        to_bf16x4(x);
+                            for (int j = 0; j < 4; ++j)
+                                x[j] = pass < 2 ? dk_acc[md][4 * g + j] * a.scale : dv_acc[md][4 * g + j];
+                            const int chunk = 4 * md + g;
+                            *(bf16x4*)(st + r * D * 2 + ((chunk ^ (r & (CH - 1))) << 4) + 8 * hf_e) =
+                                to_bf16x4(x);
+                        }
                 }
-            wave_sync_lds();
-            uint16_t* out = pass == 0 ? a.dk : a.dv;
+                wave_sync_lds();
+                uint16_t* out = pass < 2 ? a.dk : a.dv;
 #pragma unroll
-            for (int v = 0; v < 32 * CH / 64; ++v) {
-                const int k = lane_e + 64 * v;
-                const int r = k / CH, chunk = k % CH;
-                const u32x4 x = *(const u32x4*)(st + r * D * 2 + ((chunk ^ (r & (CH - 1))) << 4));
-                if (key0 + r < T.L)
-                    *(u32x4*)(out + kvrow0 + (int64_t)(key0 + r) * rs + 8 * chunk) = x;
+                for (int v = 0; v < 16 * CH / 64; ++v) {
+                    const int k = lane_e + 64 * v;
+                    const int r = k / CH, chunk = k % CH;
+                    const u32x4 x = *(const u32x4*)(st + r * D * 2 + ((chunk ^ (r & (CH - 1))) << 4));
+                    const int key = key0 + 16 * rd + r;
+                    if (key < T.L) *(u32x4*)(out + kvrow0 + (int64_t)key * rs + 8 * chunk) = x;
+                }
+                wave_sync_lds();
             }
-            wave_sync_lds();
         }
+        // the next tile's V and K landed (and this tile's stores are done)
+        wait_vmem();
+        __syncthreads();
     }
 }
 
