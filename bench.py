@@ -154,6 +154,9 @@ def main():
     ap.add_argument("--workload", type=int, default=2, help="1..5 (2: GEM-shaped broadcast-Q)")
     ap.add_argument("--fwd-workers-per-cu", type=int, default=1)
     ap.add_argument("--bwd-workers-per-cu", type=int, default=1)
+    ap.add_argument("--fwd-plan", choices=("dynamic", "static"), default="dynamic",
+                    help="forward tiles claimed at run time from the sorted list, or the "
+                         "static snake deal")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle CPU work for the baseline (0: skip)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -184,7 +187,8 @@ def main():
     t0 = time.perf_counter()
     att = J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask,
                             fwd_workers=cus * args.fwd_workers_per_cu,
-                            bwd_workers=cus * args.bwd_workers_per_cu)
+                            bwd_workers=cus * args.bwd_workers_per_cu,
+                            fwd_dynamic=args.fwd_plan == "dynamic")
     plan_ms = (time.perf_counter() - t0) * 1e3
     H, D = w.heads, w.head_dim
     o = torch.empty((att.total_q, H, D), dtype=torch.bfloat16, device="cuda")
@@ -276,6 +280,7 @@ def main():
                    "lengths": w.lengths, "seed": w.seed, "total_kv": model["t_k"],
                    "total_q": model["t_q"],
                    "fwd_workers": att.fwd_plan.info.num_workers,
+                   "fwd_plan": args.fwd_plan,
                    "bwd_workers": att.bwd_plan.info.num_workers,
                    "dq_workers": att.dq_plan.info.num_workers},
         "pct_mfma_peak": 100.0 * value / PEAK_BF16_TFLOPS,

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define JFA_ABI_VERSION 2
+#define JFA_ABI_VERSION 3
 
 /* status codes */
 #define JFA_OK                 0
@@ -71,6 +71,8 @@ extern "C" {
 #define JFA_PASS_FWD 0
 #define JFA_PASS_BWD 1
 #define JFA_PASS_DQ 2   /* Q-stationary dQ pass of the backward */
+/* OR'ed into a FWD pass: a plan for dynamic tile fetch (see the planner) */
+#define JFA_PLAN_DYNAMIC 16
 
 /* Problem description shared by the planner, jfa_fwd and jfa_bwd. */
 typedef struct jfa_problem {
@@ -88,7 +90,8 @@ typedef struct jfa_problem {
 
 /* Sizes of a plan, filled by jfa_plan_query / jfa_plan_build. */
 typedef struct jfa_plan_info {
-    int32_t pass;           /* JFA_PASS_FWD, JFA_PASS_BWD or JFA_PASS_DQ       */
+    int32_t pass;           /* JFA_PASS_FWD, JFA_PASS_BWD or JFA_PASS_DQ, with
+                               JFA_PLAN_DYNAMIC for a dynamic FWD plan         */
     int32_t num_workers;    /* W persistent workgroups the plan is dealt to
                                (DQ with broadcast Q: max(requested, G))       */
     int32_t num_tiles;      /* N tiles                                         */
@@ -141,6 +144,15 @@ int32_t jfa_offsets_from_lengths(const int32_t* h_lengths, int32_t batch, int32_
  * group's tiles are sorted and snake-dealt over its own range, so that every
  * worker sums one group only (one partial per worker).
  *
+ * JFA_PASS_FWD | JFA_PLAN_DYNAMIC: the same FWD tiles for dynamic fetch (the
+ * role the pages give the hardware's cluster launch control next to the host
+ * sort: a running workgroup claims the next tile when it needs one; bites,
+ * sections "What TLX changes" and "Optimizations layered on top"). h_tiles
+ * holds the whole stably sorted list (largest work first) and
+ * h_worker_ptr[w] = min(w, N): worker w starts with sorted tile w, and later
+ * tiles W, W+1, ... go, one at a time and in order, to whichever worker asks
+ * first (a device counter, see jfa_fwd). Only the forward has this mode.
+ *
  * h_q_offsets: int32 [B+1], NULL in broadcast mode. h_kv_offsets: int32 [B+1].
  * h_block_mask: NULL when mask_q_blocks = mask_kv_blocks = 0.
  * jfa_plan_query fills *info only (sizes). jfa_plan_build also writes
@@ -167,18 +179,28 @@ int32_t jfa_plan_build(const jfa_problem* prob, const int32_t* h_q_offsets,
                        int32_t* h_worker_ptr, int32_t* h_tiles,
                        int32_t* h_sparse_ptr, int32_t* h_sparse_idx);
 
+/* Bytes of device scratch jfa_fwd needs for this FWD plan: 256 for a
+ * dynamic plan (the tile counter), else 0. */
+int32_t jfa_fwd_workspace_bytes(const jfa_problem* prob, const jfa_plan_info* info,
+                                int64_t* bytes);
+
 /*
  * Forward pass: O and LSE. One persistent launch of info->num_workers
  * workgroups walking a FWD plan (d_worker_ptr, d_tiles and, for a block mask,
  * d_sparse_ptr/d_sparse_idx, all device copies of jfa_plan_build's output).
  * d_q_offsets is NULL in broadcast mode. Every O/LSE row is written.
+ * workspace: jfa_fwd_workspace_bytes bytes, 16-byte aligned (may be NULL when
+ * that is 0). For a dynamic plan it holds the tile counter: it must be all
+ * zero before the first launch that uses it (e.g. allocated zeroed), every
+ * launch leaves it zero again, and launches that share one workspace must
+ * not overlap in time (same stream, or ordered by events).
  */
 int32_t jfa_fwd(const jfa_problem* prob, const jfa_plan_info* info,
                 const int32_t* d_worker_ptr, const int32_t* d_tiles,
                 const int32_t* d_sparse_ptr, const int32_t* d_sparse_idx,
                 const int32_t* d_q_offsets, const int32_t* d_kv_offsets,
                 const void* q, const void* k, const void* v,
-                void* o, float* lse, void* stream);
+                void* o, float* lse, void* workspace, int64_t workspace_bytes, void* stream);
 
 /* A plan on the device: the sizes of jfa_plan_build's output and device
  * copies of its arrays (sparse_ptr / sparse_idx NULL when dense). The caller

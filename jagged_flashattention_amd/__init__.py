@@ -28,11 +28,12 @@ JFA_ERR_BAD_MASK = -7
 JFA_PASS_FWD = 0
 JFA_PASS_BWD = 1
 JFA_PASS_DQ = 2
+JFA_PLAN_DYNAMIC = 16
 
 EXPORTS = (
     "jfa_abi_version", "jfa_status_string", "jfa_last_hip_error", "jfa_device_workers",
-    "jfa_offsets_from_lengths", "jfa_plan_query", "jfa_plan_build", "jfa_fwd",
-    "jfa_bwd_workspace_bytes", "jfa_bwd", "jfa_bwd_stages",
+    "jfa_offsets_from_lengths", "jfa_plan_query", "jfa_plan_build", "jfa_fwd_workspace_bytes",
+    "jfa_fwd", "jfa_bwd_workspace_bytes", "jfa_bwd", "jfa_bwd_stages",
 )
 JFA_BWD_PREPROCESS = 1
 JFA_BWD_DKDV = 2
@@ -97,7 +98,8 @@ def _lib():
             "jfa_offsets_from_lengths": (i32, [_P, i32, _P]),
             "jfa_plan_query": (i32, [prob, _P, _P, _P, i32, i32, info]),
             "jfa_plan_build": (i32, [prob, _P, _P, _P, i32, i32, info, _P, _P, _P, _P]),
-            "jfa_fwd": (i32, [prob, info] + [_P] * 12),
+            "jfa_fwd_workspace_bytes": (i32, [prob, info, ctypes.POINTER(i64)]),
+            "jfa_fwd": (i32, [prob, info] + [_P] * 12 + [i64, _P]),
             "jfa_bwd_workspace_bytes": (i32, [prob, info, ctypes.POINTER(i64)]),
             "jfa_bwd": (i32, [prob, dplan, dplan] + [_P] * 14 + [i64, _P]),
             "jfa_bwd_stages": (i32, [i32, prob, dplan, dplan] + [_P] * 14 + [i64, _P]),
@@ -232,17 +234,29 @@ def to_device(plan: HostPlan, device="cuda") -> DevicePlan:
                       f(plan.sparse_ptr), f(plan.sparse_idx))
 
 
+def jfa_fwd_workspace_bytes(prob: Problem, info: JfaPlanInfo) -> int:
+    """Device scratch bytes jfa_fwd needs for a FWD plan (the counter of a
+    dynamic plan)."""
+    n = ctypes.c_int64(0)
+    cp = prob.c()
+    _check(_lib().jfa_fwd_workspace_bytes(ctypes.byref(cp), ctypes.byref(info), ctypes.byref(n)),
+           "jfa_fwd_workspace_bytes")
+    return n.value
+
+
 def jfa_fwd(prob: Problem, plan: DevicePlan, q_offsets, kv_offsets, q, k, v, o, lse,
-            stream=None) -> None:
+            workspace=None, workspace_bytes: int = 0, stream=None) -> None:
     """Enqueue the forward on ``stream`` (default: torch's current stream).
     q_offsets / kv_offsets are device int32 tensors (q_offsets None when
-    broadcast); q, k, v, o bf16 and lse fp32 device tensors (see jfa.h)."""
+    broadcast); q, k, v, o bf16 and lse fp32 device tensors (see jfa.h). A
+    dynamic plan needs a zero-initialised workspace (each launch leaves it
+    zero again)."""
     cp = prob.c()
     _check(_lib().jfa_fwd(ctypes.byref(cp), ctypes.byref(plan.info), _dev_ptr(plan.worker_ptr),
                           _dev_ptr(plan.tiles), _dev_ptr(plan.sparse_ptr),
                           _dev_ptr(plan.sparse_idx), _dev_ptr(q_offsets), _dev_ptr(kv_offsets),
                           _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(o), _dev_ptr(lse),
-                          _stream(stream)), "jfa_fwd")
+                          _dev_ptr(workspace), int(workspace_bytes), _stream(stream)), "jfa_fwd")
 
 
 def jfa_bwd_workspace_bytes(prob: Problem, dq_info: JfaPlanInfo) -> int:
@@ -297,13 +311,14 @@ class JaggedAttention:
 
     def __init__(self, prob: Problem, kv_offsets, q_offsets=None, block_mask=None,
                  fwd_workers: Optional[int] = None, bwd_workers: Optional[int] = None,
-                 dq_workers: Optional[int] = None, device="cuda"):
+                 dq_workers: Optional[int] = None, fwd_dynamic: bool = True, device="cuda"):
         import torch
         self.prob = prob
         self.device = device
         cus = jfa_device_workers(torch.device(device).index or 0)
+        fwd_pass = JFA_PASS_FWD | (JFA_PLAN_DYNAMIC if fwd_dynamic else 0)
         self.fwd_plan_host = jfa_plan_build(prob, q_offsets, kv_offsets, block_mask,
-                                            JFA_PASS_FWD, fwd_workers or cus)
+                                            fwd_pass, fwd_workers or cus)
         self.bwd_plan_host = jfa_plan_build(prob, q_offsets, kv_offsets, block_mask,
                                             JFA_PASS_BWD, bwd_workers or cus)
         self.dq_plan_host = jfa_plan_build(prob, q_offsets, kv_offsets, block_mask,
@@ -318,6 +333,11 @@ class JaggedAttention:
         self.ws_bytes = jfa_bwd_workspace_bytes(prob, self.dq_plan.info)
         self.workspace = (torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
                           if self.ws_bytes else None)
+        # the dynamic forward's tile counter starts at zero and every launch
+        # leaves it zero
+        self.fwd_ws_bytes = jfa_fwd_workspace_bytes(prob, self.fwd_plan.info)
+        self.fwd_workspace = (torch.zeros(self.fwd_ws_bytes, dtype=torch.uint8, device=device)
+                              if self.fwd_ws_bytes else None)
 
     def forward(self, q, k, v, o=None, lse=None):
         import torch
@@ -326,7 +346,8 @@ class JaggedAttention:
             o = torch.empty((self.total_q, H, D), dtype=torch.bfloat16, device=self.device)
         if lse is None:
             lse = torch.empty((H, self.total_q), dtype=torch.float32, device=self.device)
-        jfa_fwd(self.prob, self.fwd_plan, self.q_offsets, self.kv_offsets, q, k, v, o, lse)
+        jfa_fwd(self.prob, self.fwd_plan, self.q_offsets, self.kv_offsets, q, k, v, o, lse,
+                self.fwd_workspace, self.fwd_ws_bytes)
         return o, lse
 
     def backward(self, q, k, v, o, lse, d_o, out=None, stages=JFA_BWD_ALL):

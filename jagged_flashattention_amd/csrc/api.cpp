@@ -33,7 +33,9 @@ int32_t check_common(const jfa_problem* p, const jfa_plan_info* info, int32_t pa
     int32_t st = jfa::check_problem(p);
     if (st) return st;
     if (info == nullptr) return JFA_ERR_INVALID_ARG;
-    if (info->pass != pass) return JFA_ERR_PLAN_MISMATCH;
+    // a dynamic plan is a FWD plan with its own deal
+    const int32_t ipass = info->pass == (JFA_PASS_FWD | JFA_PLAN_DYNAMIC) ? JFA_PASS_FWD : info->pass;
+    if (ipass != pass) return JFA_ERR_PLAN_MISMATCH;
     const bool qtiles = pass != JFA_PASS_BWD;
     const int32_t bm = qtiles ? jfa::kFwdBlockM : jfa::kBwdBlockM;
     const int32_t bn = qtiles ? jfa::kFwdBlockN : jfa::kBwdBlockN;
@@ -102,13 +104,30 @@ int32_t jfa_device_workers(int32_t device, int32_t* num_cus) {
     return JFA_OK;
 }
 
+int32_t jfa_fwd_workspace_bytes(const jfa_problem* prob, const jfa_plan_info* info,
+                                int64_t* bytes) {
+    if (bytes == nullptr || info == nullptr) return JFA_ERR_INVALID_ARG;
+    int32_t st = jfa::check_problem(prob);
+    if (st) return st;
+    if (info->pass == JFA_PASS_FWD) *bytes = 0;
+    else if (info->pass == (JFA_PASS_FWD | JFA_PLAN_DYNAMIC)) *bytes = jfa::kFwdCounterBytes;
+    else return JFA_ERR_PLAN_MISMATCH;
+    return JFA_OK;
+}
+
 int32_t jfa_fwd(const jfa_problem* prob, const jfa_plan_info* info, const int32_t* d_worker_ptr,
                 const int32_t* d_tiles, const int32_t* d_sparse_ptr, const int32_t* d_sparse_idx,
                 const int32_t* d_q_offsets, const int32_t* d_kv_offsets, const void* q,
-                const void* k, const void* v, void* o, float* lse, void* stream) {
+                const void* k, const void* v, void* o, float* lse, void* workspace,
+                int64_t workspace_bytes, void* stream) {
     int32_t st = check_common(prob, info, JFA_PASS_FWD, d_worker_ptr, d_tiles, d_sparse_ptr,
                               d_sparse_idx, d_q_offsets, d_kv_offsets);
     if (st) return st;
+    int64_t need = 0;
+    st = jfa_fwd_workspace_bytes(prob, info, &need);
+    if (st) return st;
+    if (workspace_bytes < need || (need > 0 && (workspace == nullptr || !aligned16(workspace))))
+        return JFA_ERR_WORKSPACE;
     if (info->num_tiles == 0) return JFA_OK;  // no output row exists
     const int64_t hd = (int64_t)prob->num_heads * prob->head_dim;
     const int64_t q_rows = prob->broadcast_q ? prob->lq : info->total_q;
@@ -134,6 +153,8 @@ int32_t jfa_fwd(const jfa_problem* prob, const jfa_plan_info* info, const int32_
     a.total_q = info->total_q;
     a.mask_q_blocks = prob->mask_q_blocks;
     a.num_workers = info->num_workers;
+    a.num_tiles = info->num_tiles;
+    a.counter = need > 0 ? static_cast<int32_t*>(workspace) : nullptr;
     a.scale_log2 = prob->softmax_scale * 1.4426950408889634f;
     return hip_status(jfa::launch_fwd(a, prob->head_dim, mode_of(prob), prob->broadcast_q != 0,
                                       stream));

@@ -52,7 +52,9 @@ struct FwdLds {
     static constexpr int K = 0;                                // kKSlots natural K blocks
     static constexpr int V = K + kKSlots * BLK;                // kVSlots natural V blocks
     static constexpr int VT = V + kVSlots * BLK;               // 2 V^T blocks [D][64]
-    static constexpr int BYTES = VT + 2 * BLK;
+    static constexpr int CLAIM = VT + 2 * BLK;                 // int [2][64]: claimed tiles
+    static constexpr int QUEUE = CLAIM + 2 * 64 * 4;           // int [kWaves][8]: tile queues
+    static constexpr int BYTES = QUEUE + kWaves * 8 * 4;
     static constexpr int OST_WAVE = kStageRows * D * 2;        // O staging of one wave
     static_assert(4 * OST_WAVE == BLK, "staging: 4 waves per released block");
 };
@@ -99,30 +101,127 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
 
     const int w = worker_id(a.num_workers);
     const int t_begin = ld_uniform(a.worker_ptr + w), t_end = ld_uniform(a.worker_ptr + w + 1);
+    const bool dynamic = a.counter != nullptr;
 
-    // ---- the block stream of this worker: (tile, block) in plan order
     auto tile_info = [&](int ti) {
         return qtile::tile_info<MODE>(a.tiles, a.kv_off, a.sp_ptr, a.sp_idx, a.mask_q_blocks, ti);
     };
     auto seq_block = [&](const TileInfo& T, int i) { return qtile::seq_block<MODE>(T, i); };
-
-    // loader cursor
-    int l_ti = t_begin, l_i = 0, l_slot = 0;
-    TileInfo LT;
-    LT.work = 0;
-    auto l_settle = [&]() {   // skip to the next tile with blocks (LT is l_ti's)
-        while (l_i >= LT.work) {
-            ++l_ti;
-            l_i = 0;
-            if (l_ti >= t_end) return;
-            LT = tile_info(l_ti);
+    // Q / O rows of a tile's sequence: first Q row, row count, first O row
+    auto rows_of = [&](const TileInfo& T, int& q0, int& Lq, int& orow0) {
+        if (BCAST) {
+            q0 = 0;
+            Lq = a.lq;
+            orow0 = T.b * a.lq;
+        } else {
+            q0 = ld_uniform(a.q_off + T.b);
+            Lq = ld_uniform(a.q_off + T.b + 1) - q0;
+            orow0 = q0;
         }
     };
-    // issue the copies of the loader's block into ring slots (K: s % kKSlots,
-    // V: s % kVSlots) and advance; keys past the sequence are clamped to its last row (always
-    // finite data, masked out of the softmax by the tail path)
+
+    // ---- the worker's tiles. Static plan: t_begin .. t_end-1. Dynamic plan:
+    // tile t_begin (= w), then tiles claimed one at a time from the counter
+    // (num_workers + its old value) until a claim falls past the list. A claim
+    // is made (lane 0 of wave 0) when the loader starts on the last block of
+    // its tile, a few blocks before this workgroup needs the next tile, so the
+    // next tile goes to a workgroup that is about to be free; its value
+    // reaches the other waves through LDS after the next barrier, when the
+    // loader needs it. The loader hands each tile with blocks to the consumer
+    // through a per-wave queue in LDS (it is at most kAhead blocks ahead, so
+    // at most kAhead + 1 tiles are queued); a tile without blocks (an empty
+    // sequence, or no kept block) gets O = 0, LSE = -inf from the loader.
+    int* const claim_lds = (int*)(smem + LY::CLAIM);
+    int* const queue_lds = (int*)(smem + LY::QUEUE) + 8 * wave;
+    int q_head = 0, q_tail = 0;          // consumer queue cursors (wave-uniform)
+    int l_next = dynamic && t_begin < t_end ? t_begin : -1;   // tile after the loader's
+    bool l_have = dynamic;               // l_next is known
+    bool l_claiming = false;             // a claim is in flight
+    int n_claims = 0;                    // claims received (parity picks the LDS slot)
+    int claim_ret = 0;                   // wave 0, lane 0: the counter's old value
+    auto claim = [&]() {
+        // One atomic, by lane 0 of wave 0, whose value is first read after
+        // the next wait for the copies issued after it (see publish), so its
+        // latency hides behind the iteration's work.
+        if (wave == 0) claim_ret = atomic_inc_lane0_async(a.counter);
+        l_claiming = true;
+    };
+    // wave 0 puts a claimed value in LDS before a barrier; every wave reads it
+    // (lane 0's) after that barrier. Two slots: a slot is rewritten only after
+    // the barrier that follows its read.
+    auto publish = [&]() {
+        if (l_claiming && wave == 0) {
+            async_value_ready(claim_ret);
+            claim_lds[64 * (n_claims & 1) + lane] = claim_ret;
+        }
+    };
+    auto receive = [&]() {
+        if (l_claiming) {
+            const int v = __builtin_amdgcn_readfirstlane(claim_lds[64 * (n_claims & 1)]) + a.num_workers;
+            ++n_claims;
+            l_claiming = false;
+            l_next = (unsigned)v < (unsigned)a.num_tiles ? v : -1;   // past the list: done
+            l_have = true;
+        }
+    };
+    auto claim_now = [&]() {   // the next tile is needed before the next barrier
+        if (!l_claiming) claim();
+        if (wave == 0) wait_vmem();
+        publish();
+        __syncthreads();
+        receive();
+    };
+    auto zero_rows = [&](const TileInfo& Z) {   // O = 0, LSE = -inf for the tile's rows
+        int q0, Lq, orow0;
+        rows_of(Z, q0, Lq, orow0);
+        const int r0 = Z.t * kFwdBlockM, r1 = min(Lq, r0 + kFwdBlockM);
+        for (int k = tid; k < (r1 - r0) * CH; k += kThreads) {
+            const int r = r0 + k / CH, c = k % CH;
+            *(u32x4*)(a.o + (int64_t)(orow0 + r) * rs + (int64_t)Z.h * D + 8 * c) = u32x4{0, 0, 0, 0};
+        }
+        for (int r = r0 + tid; r < r1; r += kThreads) a.lse[(int64_t)Z.h * a.total_q + orow0 + r] = -INFINITY;
+    };
+
+    // loader cursor: tile l_ti (info LT), next block l_i, blocks issued l_slot
+    int l_ti = t_begin - 1, l_i = 0, l_slot = 0;
+    bool l_end = false;
+    TileInfo LT;
+    LT.work = 0;
+    auto advance = [&]() {   // to the next tile with blocks, or the end
+        while (!l_end && l_i >= LT.work) {
+            int nt;
+            if (dynamic) {
+                if (!l_have) claim_now();
+                nt = l_next;
+                l_have = false;
+            } else {
+                nt = l_ti + 1 < t_end ? l_ti + 1 : -1;
+            }
+            if (nt < 0) {
+                l_end = true;
+                break;
+            }
+            l_ti = nt;
+            l_i = 0;
+            LT = tile_info(nt);
+            if (LT.work == 0) {
+                zero_rows(LT);
+            } else {
+                queue_lds[q_tail & 7] = nt;
+                ++q_tail;
+            }
+        }
+    };
+    // issue the copies of the loader's next block into ring slots (K: slot
+    // l_slot % kKSlots, V: l_slot % kVSlots); keys past the sequence are
+    // clamped to its last row (always finite data, masked out of the softmax
+    // by the tail path)
     auto l_issue = [&]() {
-        if (l_ti >= t_end) return;
+        if (l_i >= LT.work) advance();
+        if (l_end) return;
+        // the last block of the loader's tile: claim the tile after it now,
+        // ahead of the copies (a later wait for the copies covers the claim)
+        if (dynamic && l_i == LT.work - 1 && !l_have && !l_claiming) claim();
         const int n = seq_block(LT, l_i);
         const int64_t base = (int64_t)LT.kv0 * rs + (int64_t)LT.h * D;
         char* kdst = smem + LY::K + (l_slot % kKSlots) * LY::BLK;
@@ -136,7 +235,6 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
         }
         ++l_slot;
         ++l_i;
-        l_settle();
     };
     // V (natural, slot s % kVSlots) -> V^T (buffer s % 2)
     auto tr_read = [&](int s, bf16x4 (&x)[TPW]) {
@@ -155,16 +253,9 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
         tr_write(s, x);
     };
 
-    if (t_begin < t_end) {
-        LT = tile_info(t_begin);
-        l_settle();
-    }
-    int total = 0;   // stream length, to know whether block s+1 exists
-    for (int ti = t_begin; ti < t_end; ++ti) total += ld_uniform(a.tiles + 4 * ti + 3);
-
     // prologue: block 0 landed and transposed, blocks 1 .. kAhead-1 in flight
-    if (total > 0) {
-        l_issue();
+    l_issue();
+    if (l_slot > 0) {
         wait_vmem();
         __syncthreads();
         transpose_v(0);
@@ -173,18 +264,14 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
     }
 
     int s = 0;   // stream position of the consumer
-    for (int ti = t_begin; ti < t_end; ++ti) {
+    // the loader queues a tile no later than the iteration that consumes the
+    // previous tile's last block, so an empty queue means the end
+    while (q_head != q_tail) {
+        const int ti = __builtin_amdgcn_readfirstlane(queue_lds[q_head & 7]);
+        ++q_head;
         const TileInfo T = tile_info(ti);
         int q0, Lq, orow0;
-        if (BCAST) {
-            q0 = 0;
-            Lq = a.lq;
-            orow0 = T.b * a.lq;
-        } else {
-            q0 = ld_uniform(a.q_off + T.b);
-            Lq = ld_uniform(a.q_off + T.b + 1) - q0;
-            orow0 = q0;
-        }
+        rows_of(T, q0, Lq, orow0);
         const int row0 = T.t * kFwdBlockM + 32 * wave;   // first row of this wave
         const int qrow = row0 + lr;
         const bool wave_rows = row0 < Lq;                // wave-uniform
@@ -250,13 +337,15 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
             // Block s+1 landed; in steady state the copies of block s+2 (the
             // wave's 2*LPW most recent vector memory operations) stay in flight.
             if (i > 0) {
-                if (s + 2 < total) wait_vmem_keep<2 * LPW>();
+                if (l_slot == s + kAhead) wait_vmem_keep<2 * LPW>();
                 else wait_vmem();
             }
+            publish();
             // every wave is past block s-1: its K slot and V^T buffer are free
             __syncthreads();
-            l_issue();                              // block s+kAhead
-            if (s + 1 < total) transpose_v(s + 1);  // V^T of block s+1
+            receive();
+            l_issue();                                // block s+kAhead
+            if (l_slot > s + 1) transpose_v(s + 1);   // V^T of block s+1
 
             const int n = seq_block(T, i);
             bool skip, masked;
@@ -340,6 +429,16 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
             if (hf == 0 && qrow < Lq)
                 a.lse[(int64_t)T.h * a.total_q + orow0 + qrow] =
                     l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+        }
+    }
+    // Dynamic plan: every claim of this workgroup has returned (the last one
+    // ended its stream). The last workgroup to get here sees all the others'
+    // claims done and leaves the counters zero for the next launch.
+    if (dynamic && tid == 0) {
+        __threadfence();
+        if (atomicAdd(a.counter + 1, 1) == (int)gridDim.x - 1) {
+            atomicExch(a.counter, 0);
+            atomicExch(a.counter + 1, 0);
         }
     }
 }

@@ -40,8 +40,13 @@ struct FwdArgs {
     int32_t total_q;
     int32_t mask_q_blocks;
     int32_t num_workers;
+    int32_t num_tiles;
+    int32_t* counter;       // dynamic plan: [0] tiles claimed, [1] workgroups done; else null
     float scale_log2;       // softmax_scale * log2(e)
 };
+
+// Workspace of a dynamic forward plan (two int32 counters, padded).
+constexpr int64_t kFwdCounterBytes = 256;
 
 // KV-stationary dK/dV pass of the backward (JFA_PASS_BWD plan) and the
 // delta preprocess.

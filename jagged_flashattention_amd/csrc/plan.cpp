@@ -10,6 +10,11 @@
 // work = inner-loop trip count of the tile, stable sort (ties keep (b,h,t)
 // order), snake deal (round r goes left-to-right when r is even, else
 // right-to-left).
+// A dynamic forward plan keeps the same sort but deals only the first W
+// tiles (one per worker); the rest are claimed at run time, in sorted order,
+// through a device counter: the counterpart of the cluster launch control the
+// pages pair with the host sort (same page, sections "What TLX changes" and
+// "Optimizations layered on top").
 #include "internal.h"
 
 #include <algorithm>
@@ -156,13 +161,16 @@ int32_t tile_work(const jfa_problem* p, const uint8_t* mask, int32_t pass, int32
 }
 
 int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, const uint8_t* mask,
-                  int32_t pass, int32_t W, jfa_plan_info* info, int32_t* worker_ptr,
+                  int32_t pass_flags, int32_t W, jfa_plan_info* info, int32_t* worker_ptr,
                   int32_t* tiles_out, int32_t* sp_ptr, int32_t* sp_idx, bool build) {
     if (info == nullptr) return JFA_ERR_INVALID_ARG;
     int32_t st = check_problem(p);
     if (st) return st;
+    const bool dynamic = (pass_flags & JFA_PLAN_DYNAMIC) != 0;
+    const int32_t pass = pass_flags & ~JFA_PLAN_DYNAMIC;
     if (pass != JFA_PASS_FWD && pass != JFA_PASS_BWD && pass != JFA_PASS_DQ)
         return JFA_ERR_INVALID_ARG;
+    if (dynamic && pass != JFA_PASS_FWD) return JFA_ERR_INVALID_ARG;
     if (W < 1) return JFA_ERR_INVALID_ARG;
     // Q-tile passes (forward, dQ) enumerate Q tiles; the backward KV tiles
     const bool qtiles = pass != JFA_PASS_BWD;
@@ -225,7 +233,7 @@ int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, co
         if (G > INT32_MAX / 2) return JFA_ERR_INVALID_ARG;
         W = (int32_t)std::max<int64_t>(W, G);
     }
-    info->pass = pass;
+    info->pass = pass_flags;
     info->num_workers = W;
     info->num_tiles = (int32_t)tiles.size();
     info->block_m = bm;
@@ -253,10 +261,21 @@ int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, co
         if (ga != gc) return ga < gc;
         return tiles[a].work > tiles[c].work;
     });
+    if (dynamic) {   // the sorted list itself; worker w starts with tile w
+        for (int32_t w = 0; w <= W; ++w) worker_ptr[w] = (int32_t)std::min<size_t>(w, order.size());
+        for (size_t i = 0; i < order.size(); ++i) {
+            const Tile& t = tiles[order[i]];
+            int32_t* dst = tiles_out + 4 * (int64_t)i;
+            dst[0] = t.b;
+            dst[1] = t.h;
+            dst[2] = t.t;
+            dst[3] = t.work;
+        }
+    }
     // 4. snake deal over the group's workers; 5. emit per worker in increasing
     // deal position
-    std::vector<int32_t> count(W, 0), owner(order.size());
-    for (size_t i = 0; i < order.size();) {
+    std::vector<int32_t> count(dynamic ? 0 : W, 0), owner(dynamic ? 0 : order.size());
+    for (size_t i = 0; i < owner.size();) {
         const int64_t g = group_of(tiles[order[i]]);
         size_t e = i;
         while (e < order.size() && group_of(tiles[order[e]]) == g) ++e;
@@ -271,10 +290,12 @@ int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, co
         }
         i = e;
     }
-    worker_ptr[0] = 0;
-    for (int32_t w = 0; w < W; ++w) worker_ptr[w + 1] = worker_ptr[w] + count[w];
-    std::vector<int32_t> cursor(worker_ptr, worker_ptr + W);
-    for (size_t i = 0; i < order.size(); ++i) {
+    if (!dynamic) {
+        worker_ptr[0] = 0;
+        for (int32_t w = 0; w < W; ++w) worker_ptr[w + 1] = worker_ptr[w] + count[w];
+    }
+    std::vector<int32_t> cursor(worker_ptr, worker_ptr + (dynamic ? 0 : W));
+    for (size_t i = 0; i < owner.size(); ++i) {
         const Tile& t = tiles[order[i]];
         int32_t* dst = tiles_out + 4 * (int64_t)cursor[owner[i]]++;
         dst[0] = t.b;

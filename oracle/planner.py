@@ -28,6 +28,14 @@ plainest readings, written out step by step here, are:
  5. Emit worker_ptr[W+1] and, per worker in increasing i, tiles[.,4] =
     (b, h, t, work), all int32.
 
+Dynamic forward plan. The pages pair the host sort with the hardware's
+cluster launch control, which lets a running program claim its next tile
+([bites] sections "What TLX changes" and "Optimizations layered on top",
+item on scheduling jagged tiles). Reading: steps 1-3 as above; the plan is
+the sorted list itself, worker w starts with sorted tile w (worker_ptr[w] =
+min(w, N)), and tiles W, W+1, ... are claimed at run time, in order, by
+whichever worker asks first.
+
 dQ pass (the backward's Q-stationary dQ kernel). Tiles are the forward
 tiles: (b, h, t) with the forward work.
  * per-sequence Q: the forward plan itself;
@@ -188,7 +196,7 @@ def plan_dq(q_lens, kv_lens, num_heads, num_workers, *, broadcast_q, lq=0, block
 
 
 def plan(q_lens, kv_lens, num_heads, num_workers, pass_, *, block_m, block_n,
-         causal=False, block_mask=None):
+         causal=False, block_mask=None, dynamic=False):
     """Returns (worker_ptr int32 [W+1], tiles int32 [N, 4])."""
     B = len(kv_lens)
     W = int(num_workers)
@@ -204,6 +212,11 @@ def plan(q_lens, kv_lens, num_heads, num_workers, pass_, *, block_m, block_n,
                                causal=causal, block_mask=block_mask)
                 tiles.append((b, h, t, w))
     order = sorted(range(len(tiles)), key=lambda i: -tiles[i][3])   # stable
+    if dynamic:
+        if pass_ != FWD:
+            raise ValueError("dynamic plans are forward plans")
+        worker_ptr = np.array([min(w, len(order)) for w in range(W + 1)], dtype=np.int32)
+        return worker_ptr, np.array([tiles[i] for i in order], dtype=np.int32).reshape(-1, 4)
     owner = _snake(len(order), W)
     per_worker = [[] for _ in range(W)]
     for i, ti in enumerate(order):

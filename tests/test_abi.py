@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert J.jfa_abi_version() == 2
+    assert J.jfa_abi_version() == 3
     for st in range(-7, 1):
         assert J.jfa_status_string(st) not in ("", "unknown status")
     assert J.jfa_status_string(-99) == "unknown status"
@@ -103,17 +103,18 @@ class _FakeTensor:
         return self.addr
 
 
-def _call_fwd(prob, info, **over):
+def _call_fwd(prob, info, ws_bytes=0, **over):
     t = _FakeTensor(0x1000)
     args = dict(worker_ptr=t, tiles=t, sparse_ptr=None, sparse_idx=None, q_off=None, kv_off=t,
-                q=t, k=t, v=t, o=t, lse=t)
+                q=t, k=t, v=t, o=t, lse=t, ws=None)
     args.update(over)
     cp = prob.c()
     f = lambda x: None if x is None else ctypes.c_void_p(x.data_ptr())
     return J._lib().jfa_fwd(ctypes.byref(cp), ctypes.byref(info), f(args["worker_ptr"]),
                             f(args["tiles"]), f(args["sparse_ptr"]), f(args["sparse_idx"]),
                             f(args["q_off"]), f(args["kv_off"]), f(args["q"]), f(args["k"]),
-                            f(args["v"]), f(args["o"]), f(args["lse"]), None)
+                            f(args["v"]), f(args["o"]), f(args["lse"]), f(args["ws"]), ws_bytes,
+                            None)
 
 
 def test_fwd_validation_returns_before_launch():
@@ -132,6 +133,22 @@ def test_fwd_validation_returns_before_launch():
     e = J.jfa_plan_build(_prob(batch=0), None, [0], None, J.JFA_PASS_FWD, 4)
     assert _call_fwd(_prob(batch=0), e.info, worker_ptr=None, tiles=None, q=None, k=None, v=None,
                      o=None, lse=None, kv_off=None) == J.JFA_OK
+
+
+def test_fwd_workspace_query_and_validation():
+    prob = _prob()
+    static = J.jfa_plan_build(prob, None, [0, 3, 5], None, J.JFA_PASS_FWD, 4)
+    dyn = J.jfa_plan_build(prob, None, [0, 3, 5], None, J.JFA_PASS_FWD | J.JFA_PLAN_DYNAMIC, 4)
+    assert J.jfa_fwd_workspace_bytes(prob, static.info) == 0
+    need = J.jfa_fwd_workspace_bytes(prob, dyn.info)
+    assert need == 256
+    assert _call_fwd(prob, dyn.info) == J.JFA_ERR_WORKSPACE                    # no counter
+    assert _call_fwd(prob, dyn.info, need - 4, ws=_FakeTensor(0x2000)) == J.JFA_ERR_WORKSPACE
+    assert _call_fwd(prob, dyn.info, need, ws=_FakeTensor(0x2008)) == J.JFA_ERR_WORKSPACE
+    bwd = J.jfa_plan_build(prob, None, [0, 3, 5], None, J.JFA_PASS_BWD, 4)
+    with pytest.raises(J.JfaError) as e:
+        J.jfa_fwd_workspace_bytes(prob, bwd.info)
+    assert e.value.status == J.JFA_ERR_PLAN_MISMATCH
 
 
 def test_bwd_workspace_query():

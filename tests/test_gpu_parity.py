@@ -58,11 +58,12 @@ class GpuRun:
     delta: object
 
 
-def run_gpu(x, fwd_workers=None, bwd_workers=None, dq_workers=None, canary=True):
+def run_gpu(x, fwd_workers=None, bwd_workers=None, dq_workers=None, canary=True,
+            fwd_dynamic=True):
     prob = problem_of(x)
     att = J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask,
                             fwd_workers=fwd_workers, bwd_workers=bwd_workers,
-                            dq_workers=dq_workers)
+                            dq_workers=dq_workers, fwd_dynamic=fwd_dynamic)
     q, k, v, do = dev(x.q), dev(x.k), dev(x.v), dev(x.do)
     H, D = prob.num_heads, prob.head_dim
     o = torch.empty((att.total_q, H, D), dtype=torch.bfloat16, device="cuda")
@@ -205,6 +206,37 @@ def test_deterministic_across_plans_and_runs(case):
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), name
         d = (ref.dq_accum - r.dq_accum).abs().max().item()
         assert d <= 1e-4 * max(1.0, ref.dq_accum.abs().max().item())
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("case", ["bcast_ragged_d128", "perseq_d128", "causal_d64", "sparse_d128",
+                                  "cfg2_small"])
+def test_dynamic_forward_equals_static(case):
+    """The dynamic plan (tiles claimed at run time) gives O and LSE bitwise
+    equal to the static plan's, for any worker count (more workers than
+    tiles, one worker), and back-to-back launches on one workspace (the
+    counter resets itself) agree."""
+    print("case", case, flush=True)
+    x = SMALL_CASES[case]()
+    ref = run_gpu(x, fwd_dynamic=False)
+    prob = problem_of(x)
+    q, k, v = dev(x.q), dev(x.k), dev(x.v)
+    H, D = prob.num_heads, prob.head_dim
+    for fw in (None, 1, 3, 4096):
+        att = J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask, fwd_workers=fw,
+                                fwd_dynamic=True)
+        assert att.fwd_ws_bytes > 0
+        for rep_ in range(3):
+            o = torch.full((att.total_q, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+            lse = torch.full((H, att.total_q), float("nan"), dtype=torch.float32, device="cuda")
+            att.forward(q, k, v, o, lse)
+            torch.cuda.synchronize()
+            assert torch.equal(_bits(o), _bits(ref.o)), (fw, rep_)
+            assert torch.equal(_bits(lse), _bits(ref.lse)), (fw, rep_)
+        assert int(att.fwd_workspace.view(torch.int32)[:2].abs().sum().item()) == 0
 
 
 # ----------------------------------------------------------------- full sizes

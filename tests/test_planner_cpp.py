@@ -126,3 +126,31 @@ def test_cpp_plan_random_small_problems():
                                block_mask=mask)
         assert np.array_equal(hp.worker_ptr, wp), (trial, "dq")
         assert np.array_equal(hp.tiles, tiles), (trial, "dq")
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("workers", [1, 7, 256, 5000])
+def test_cpp_dynamic_plan_equals_oracle(cfg, workers):
+    w, lens, mask = _lengths_only(cfg)
+    kv_off = W.offsets_of(lens)
+    q_off = None if w.broadcast_q else kv_off
+    mq, mk = (mask.shape[1], mask.shape[2]) if mask is not None else (0, 0)
+    prob = J.Problem(batch=w.batch, num_heads=w.heads, head_dim=w.head_dim,
+                     broadcast_q=w.broadcast_q, lq=w.lq if w.broadcast_q else 0, causal=w.causal,
+                     mask_q_blocks=mq, mask_kv_blocks=mk, softmax_scale=w.scale)
+    hp = J.jfa_plan_build(prob, q_off, kv_off, mask, J.JFA_PASS_FWD | J.JFA_PLAN_DYNAMIC, workers)
+    q_lens = [w.lq] * w.batch if w.broadcast_q else lens
+    wp, tiles = OP.plan(q_lens, lens, w.heads, workers, OP.FWD, block_m=FWD_BM, block_n=FWD_BN,
+                        causal=w.causal, block_mask=mask, dynamic=True)
+    assert hp.info.pass_ == J.JFA_PASS_FWD | J.JFA_PLAN_DYNAMIC
+    assert hp.info.num_workers == workers
+    assert np.array_equal(hp.worker_ptr, wp)
+    assert np.array_equal(hp.tiles, tiles)
+
+
+def test_cpp_dynamic_plan_only_for_forward():
+    prob = J.Problem(2, 1, 64, True, lq=8, softmax_scale=0.1)
+    for p in (J.JFA_PASS_BWD, J.JFA_PASS_DQ):
+        with pytest.raises(J.JfaError) as e:
+            J.jfa_plan_build(prob, None, [0, 3, 5], None, p | J.JFA_PLAN_DYNAMIC, 4)
+        assert e.value.status == J.JFA_ERR_INVALID_ARG

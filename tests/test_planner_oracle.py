@@ -80,6 +80,41 @@ def test_plan_properties(name, qlens, kvlens, causal, mask, pass_, bm, bn, worke
     assert max(loads) <= sum(works) / workers + (max(works) if works else 0)
 
 
+@pytest.mark.parametrize("name,qlens,kvlens,causal,mask", _cases())
+@pytest.mark.parametrize("workers", [1, 7, 16, 255])
+def test_dynamic_plan_properties(name, qlens, kvlens, causal, mask, workers):
+    """The dynamic forward plan: every tile once, with its brute-force work,
+    in non-increasing work with ties in (b, h, t) order; worker w starts with
+    tile w. List scheduling of that order (each tile to the first worker to
+    be free, as the device counter hands them out) stays within one largest
+    tile of the mean load."""
+    H = 2
+    bm, bn = 256, 64
+    wp, tiles = P.plan(qlens, kvlens, H, workers, P.FWD, block_m=bm, block_n=bn,
+                       causal=causal, block_mask=mask, dynamic=True)
+    n = len(tiles)
+    assert list(wp) == [min(w, n) for w in range(workers + 1)]
+    expect = set()
+    for b in range(len(kvlens)):
+        for h in range(H):
+            for t in range(P.cdiv(qlens[b], bm)):
+                expect.add((b, h, t, _brute_work(P.FWD, b, t, qlens[b], kvlens[b], bm, bn,
+                                                 causal, mask)))
+    got = [tuple(int(x) for x in r) for r in tiles]
+    assert len(got) == len(set(got)) == len(expect) and set(got) == expect
+    works = [r[3] for r in got]
+    assert all(works[i] >= works[i + 1] for i in range(n - 1))
+    for i in range(n - 1):
+        if works[i] == works[i + 1]:
+            assert got[i][:3] < got[i + 1][:3]
+    free = [0] * workers
+    for i, wk in enumerate(works):
+        w = i if i < workers else min(range(workers), key=lambda x: free[x])
+        free[w] += wk
+    if works:
+        assert max(free) <= sum(works) / workers + max(works)
+
+
 def test_sparse_lists_by_scan():
     rng = np.random.default_rng(3)
     lens = np.array([5, 129, 256, 900, 1])
