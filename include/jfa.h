@@ -142,7 +142,12 @@ int32_t jfa_offsets_from_lengths(const int32_t* h_lengths, int32_t batch, int32_
  * h), the G = H * ceil(lq/256) groups g = h * ceil(lq/256) + t get disjoint
  * worker ranges [g W'/G, (g+1) W'/G) of W' = max(W, G) workers, and each
  * group's tiles are sorted and snake-dealt over its own range, so that every
- * worker sums one group only (one partial per worker).
+ * worker sums one group only (one partial per worker). Since those partials
+ * are summed anyway, a broadcast-Q DQ tile of more than 16 blocks is first
+ * split into n = ceil(work/16) chunks of consecutive positions of its block
+ * list (the first work mod n of them one block longer), listed in (b, h, t,
+ * chunk) order; a chunk starting at position k0 is stored as
+ * (b, h, t + ceil(lq/256) * k0, its length).
  *
  * JFA_PASS_FWD | JFA_PLAN_DYNAMIC: the same FWD tiles for dynamic fetch (the
  * role the pages give the hardware's cluster launch control next to the host

@@ -256,6 +256,7 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device
         d.dq = static_cast<uint16_t*>(dq);
         d.dq_accum = dq_accum;
         d.partial = static_cast<float*>(workspace);
+        d.chunk_div = bcast ? (prob->lq + jfa::kFwdBlockM - 1) / jfa::kFwdBlockM : 0;
         d.num_heads = prob->num_heads;
         d.lq = prob->lq;
         d.total_q = qi->total_q;

@@ -89,7 +89,8 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
     const int w = worker_id(a.num_workers);
     const int t_begin = ld_uniform(a.worker_ptr + w), t_end = ld_uniform(a.worker_ptr + w + 1);
     auto tile_info = [&](int ti) {
-        return qtile::tile_info<MODE>(a.tiles, a.kv_off, a.sp_ptr, a.sp_idx, a.mask_q_blocks, ti);
+        return qtile::tile_info<MODE>(a.tiles, a.kv_off, a.sp_ptr, a.sp_idx, a.mask_q_blocks,
+                                      a.chunk_div, ti);
     };
 
     // ---- loader: the worker's blocks in plan order, kAhead blocks ahead
@@ -108,7 +109,7 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
     // probabilities the tail path zeroes)
     auto l_issue = [&]() {
         if (l_ti >= t_end) return;
-        const int n = seq_block<MODE>(LT, l_i);
+        const int n = seq_block<MODE>(LT, LT.k0 + l_i);
         const int64_t base = (int64_t)LT.kv0 * rs + (int64_t)LT.h * D;
         char* kdst = smem + LY::K + (l_slot % kSlots) * LY::BLK;
         char* vdst = smem + LY::V + (l_slot % kSlots) * LY::BLK;
@@ -236,9 +237,9 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
             l_issue();                              // block s+kAhead
             if (s + 1 < total) transpose_k(s + 1);  // K^T of block s+1
 
-            const int n = seq_block<MODE>(T, i);
+            const int n = seq_block<MODE>(T, T.k0 + i);
             bool skip, masked;
-            block_flags<MODE>(T, i, n, row0, wave_rows, wave, skip, masked);
+            block_flags<MODE>(T, T.k0 + i, n, row0, wave_rows, wave, skip, masked);
             if (skip) continue;
             const char* kb = smem + LY::K + (s % kSlots) * LY::BLK;
             const char* vb = smem + LY::V + (s % kSlots) * LY::BLK;

@@ -104,7 +104,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
     const bool dynamic = a.counter != nullptr;
 
     auto tile_info = [&](int ti) {
-        return qtile::tile_info<MODE>(a.tiles, a.kv_off, a.sp_ptr, a.sp_idx, a.mask_q_blocks, ti);
+        return qtile::tile_info<MODE>(a.tiles, a.kv_off, a.sp_ptr, a.sp_idx, a.mask_q_blocks, 0, ti);
     };
     auto seq_block = [&](const TileInfo& T, int i) { return qtile::seq_block<MODE>(T, i); };
     // Q / O rows of a tile's sequence: first Q row, row count, first O row

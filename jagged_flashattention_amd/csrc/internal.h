@@ -17,6 +17,9 @@ constexpr int32_t kFwdBlockN = 64;
 constexpr int32_t kBwdBlockM = 32;
 constexpr int32_t kBwdBlockN = 256;
 constexpr int32_t kMaskBlock = 128;
+// Broadcast-Q dQ plans split a tile of more than this many 64-key blocks into
+// chunks of at most this many.
+constexpr int32_t kDqChunkBlocks = 16;
 
 int32_t check_problem(const jfa_problem* p);
 int32_t check_offsets(const int32_t* off, int32_t batch);
@@ -92,6 +95,7 @@ struct DqArgs {
     uint16_t* dq;            // per-sequence Q: bf16 [T_q, H, D]
     float* dq_accum;         // per-sequence Q: fp32 [T_q, H, D]
     float* partial;          // broadcast Q: fp32 [W][256][D] per-worker partial sums
+    int32_t chunk_div;       // broadcast Q: Q tiles per sequence (chunked tile records), else 0
     int32_t num_heads;
     int32_t lq;
     int32_t total_q;

@@ -225,13 +225,34 @@ int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, co
     }
 
     // dQ pass with broadcast Q: tiles grouped by (head, Q tile); group g owns
-    // the workers [g W' / G, (g+1) W' / G) of W' = max(W, G) workers
+    // the workers [g W' / G, (g+1) W' / G) of W' = max(W, G) workers. A tile
+    // of w > kDqChunkBlocks blocks is split into n = ceil(w / kDqChunkBlocks)
+    // chunks of consecutive list positions, the first (w mod n) one block
+    // longer; a chunk starting at position k0 is stored with t + nqt * k0 in
+    // place of t (every chunk adds into the same partial sum).
     const bool grouped = pass == JFA_PASS_DQ && p->broadcast_q;
     const int32_t nqt = (int32_t)cdiv(p->lq, bm);
     const int64_t G = grouped ? (int64_t)p->num_heads * nqt : 0;
     if (grouped) {
         if (G > INT32_MAX / 2) return JFA_ERR_INVALID_ARG;
+        if ((int64_t)nqt * max_work > INT32_MAX) return JFA_ERR_INVALID_ARG;
         W = (int32_t)std::max<int64_t>(W, G);
+        std::vector<Tile> chunks;
+        chunks.reserve(tiles.size());
+        max_work = 0;
+        for (const Tile& t : tiles) {
+            const int32_t n = std::max<int32_t>(1, (int32_t)cdiv(t.work, kDqChunkBlocks));
+            const int32_t q = t.work / n, r = t.work % n;
+            int32_t k0 = 0;
+            for (int32_t c = 0; c < n; ++c) {
+                const int32_t len = q + (c < r ? 1 : 0);
+                chunks.push_back({t.b, t.h, t.t + nqt * k0, len});
+                max_work = std::max(max_work, len);
+                k0 += len;
+            }
+        }
+        if (chunks.size() > (size_t)(INT32_MAX / 4)) return JFA_ERR_INVALID_ARG;
+        tiles.swap(chunks);
     }
     info->pass = pass_flags;
     info->num_workers = W;
@@ -254,7 +275,7 @@ int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, co
     std::vector<int32_t> order(tiles.size());
     std::iota(order.begin(), order.end(), 0);
     auto group_of = [&](const Tile& t) -> int64_t {
-        return grouped ? (int64_t)t.h * nqt + t.t : 0;
+        return grouped ? (int64_t)t.h * nqt + t.t % nqt : 0;
     };
     std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t c) {
         const int64_t ga = group_of(tiles[a]), gc = group_of(tiles[c]);

@@ -68,20 +68,26 @@ __device__ __forceinline__ void load_lds16(const uint16_t* g, char* lds_wave_bas
         : "memory");
 }
 
-// One tile of a Q-tile plan (wave-uniform).
+// One tile of a Q-tile plan (wave-uniform): Q tile t of sequence b, head h,
+// visiting positions k0 .. k0+work-1 of the tile's block list (k0 > 0 only
+// for a chunk of a split broadcast-Q dQ tile).
 struct TileInfo {
-    int b, h, t, work, kv0, L;
+    int b, h, t, k0, work, kv0, L;
     const int* sp;   // block-sparse list of the tile (4c + keep bits), else null
 };
 
+// chunk_div: 0, or for a chunked plan the number of Q tiles per sequence,
+// the record's third field being t + chunk_div * k0
 template <int MODE>
 __device__ __forceinline__ TileInfo tile_info(const int32_t* tiles, const int32_t* kv_off,
                                               const int32_t* sp_ptr, const int32_t* sp_idx,
-                                              int32_t mask_q_blocks, int ti) {
+                                              int32_t mask_q_blocks, int chunk_div, int ti) {
     TileInfo T;
     T.b = ld_uniform(tiles + 4 * ti + 0);
     T.h = ld_uniform(tiles + 4 * ti + 1);
-    T.t = ld_uniform(tiles + 4 * ti + 2);
+    const int f2 = ld_uniform(tiles + 4 * ti + 2);
+    T.t = chunk_div > 0 ? f2 % chunk_div : f2;
+    T.k0 = chunk_div > 0 ? f2 / chunk_div : 0;
     T.work = ld_uniform(tiles + 4 * ti + 3);
     T.kv0 = ld_uniform(kv_off + T.b);
     T.L = ld_uniform(kv_off + T.b + 1) - T.kv0;

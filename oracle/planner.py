@@ -46,6 +46,12 @@ tiles: (b, h, t) with the forward work.
    [floor(g W' / G), floor((g+1) W' / G)), and its tiles (b = 0..B-1) are
    stably sorted by work, descending, and dealt in snake order over them.
    Every worker thus sums one group only, into one per-worker partial.
+   Because those partials are summed anyway, a long tile can be split at no
+   cost: a tile of work w > DQ_CHUNK is cut into n = ceil(w / DQ_CHUNK)
+   chunks of consecutive positions of its block list, the first (w mod n)
+   of them one block longer, listed in (b, h, t, chunk) order before the
+   sort; a chunk starting at position k0 is stored as (b, h, t + nqt * k0,
+   length) with nqt = ceil(Lq / block_m).
 
 Block-sparse lists ([radar] section "The turning point": the block-sparse
 variant only adds iteration over the selected blocks). The mask is uint8
@@ -68,6 +74,7 @@ import numpy as np
 
 MASK_BLOCK = 128
 FWD, BWD, DQ = 0, 1, 2
+DQ_CHUNK = 16   # longest broadcast-Q dQ chunk, in KV blocks
 
 
 def cdiv(a: int, b: int) -> int:
@@ -179,9 +186,16 @@ def plan_dq(q_lens, kv_lens, num_heads, num_workers, *, broadcast_q, lq=0, block
     for g in range(G):
         h, t = divmod(g, nqt)
         w0, w1 = (g * W) // G, ((g + 1) * W) // G
-        tiles = [(b, h, t, _tile_work(FWD, b, t, int(lq), int(kv_lens[b]), block_m=block_m,
-                                       block_n=block_n, causal=causal, block_mask=block_mask))
-                 for b in range(B)]
+        tiles = []
+        for b in range(B):
+            w = _tile_work(FWD, b, t, int(lq), int(kv_lens[b]), block_m=block_m,
+                           block_n=block_n, causal=causal, block_mask=block_mask)
+            n = max(1, cdiv(w, DQ_CHUNK))
+            k0 = 0
+            for c in range(n):
+                length = w // n + (1 if c < w % n else 0)
+                tiles.append((b, h, t + nqt * k0, length))
+                k0 += length
         order = sorted(range(len(tiles)), key=lambda i: -tiles[i][3])   # stable
         owner = _snake(len(order), w1 - w0)
         for i, ti in enumerate(order):

@@ -148,6 +148,12 @@ SMALL_CASES = {
                                    lengths=[1, 64, 65, 127, 128, 129, 300, 513, 640]),
     "sparse_d64": lambda: _custom("s64", broadcast=True, H=2, D=64, lq=200, mask_seed=7,
                                   lengths=[1, 64, 65, 127, 128, 129, 300, 513]),
+    # long sequences: broadcast dQ tiles split into chunks (odd chunk starts
+    # inside the block-sparse lists too)
+    "bcast_long_d64": lambda: _custom("bl64", broadcast=True, H=2, D=64, lq=300,
+                                      lengths=[1500, 33, 2100, 1025]),
+    "sparse_long_d128": lambda: _custom("sl128", broadcast=True, H=2, D=128, lq=256, mask_seed=9,
+                                        lengths=[2500, 1100, 64, 3000]),
     "cfg2_small": lambda: W.make_inputs(2, batch=16, heads=2),
     "cfg3_small": lambda: W.make_inputs(3, batch=3, heads=2),
     "cfg4_small": lambda: W.make_inputs(4, batch=2, heads=2),

@@ -179,11 +179,14 @@ def test_offsets_from_lengths():
 @pytest.mark.parametrize("workers", [1, 3, 4, 5, 64])
 @pytest.mark.parametrize("lq", [0, 100, 256, 600])
 def test_dq_plan_grouped(workers, lq):
-    """Broadcast-Q dQ plan: every (b, h, t) tile once, each worker inside one
+    """Broadcast-Q dQ plan: every (b, h, t) tile covered once by its chunks
+    (consecutive block ranges that partition the tile's brute-force work,
+    at most DQ_CHUNK long, the first ones one longer), each worker inside one
     (h, t) group, groups on contiguous disjoint worker ranges, snake deal with
     non-increasing work inside each group."""
     rng = np.random.default_rng(lq + workers)
-    lens = rng.integers(0, 900, size=11)
+    lens = rng.integers(0, 3000, size=11)
+    lens[3] = 0
     H, bm, bn = 3, 256, 64
     wp, tiles = P.plan_dq([lq] * 11, lens, H, workers, broadcast_q=True, lq=lq,
                           block_m=bm, block_n=bn)
@@ -192,15 +195,36 @@ def test_dq_plan_grouped(workers, lq):
     Wp = max(workers, G)
     assert len(wp) == Wp + 1
     got = [tuple(int(x) for x in r) for r in tiles]
-    expect = {(b, h, t, _brute_work(P.FWD, b, t, lq, int(lens[b]), bm, bn, False, None))
+    assert len(got) == len(set(got))
+    chunks = {}
+    for b, h, f2, n in got:
+        t, k0 = f2 % max(nqt, 1), f2 // max(nqt, 1)
+        chunks.setdefault((b, h, t), []).append((k0, n))
+    expect = {(b, h, t): _brute_work(P.FWD, b, t, lq, int(lens[b]), bm, bn, False, None)
               for b in range(11) for h in range(H) for t in range(nqt)}
-    assert len(got) == len(set(got)) and set(got) == expect
+    assert set(chunks) == set(expect)
+    n_split = 0
+    for key, parts in chunks.items():
+        w = expect[key]
+        parts.sort()
+        n = max(1, P.cdiv(w, P.DQ_CHUNK))
+        assert len(parts) == n
+        n_split += n > 1
+        assert parts[0][0] == 0 and sum(p[1] for p in parts) == w
+        for (k0, ln), (k1, _) in zip(parts, parts[1:]):
+            assert k1 == k0 + ln
+        lens_ = [p[1] for p in parts]
+        assert max(lens_) <= P.DQ_CHUNK and max(lens_) - min(lens_) <= 1
+        assert lens_ == sorted(lens_, reverse=True)
+    if lq > 0:
+        assert n_split > 0
     for g in range(G):
         h, t = divmod(g, nqt)
         w0, w1 = g * Wp // G, (g + 1) * Wp // G
         assert w1 > w0
         grp = [r for w in range(w0, w1) for r in got[wp[w]:wp[w + 1]]]
-        assert all(r[1] == h and r[2] == t for r in grp) and len(grp) == 11
+        assert all(r[1] == h and r[2] % nqt == t for r in grp)
+        assert len(grp) == sum(len(chunks[(b, h, t)]) for b in range(11))
         nw = w1 - w0
         cursor = [wp[w] for w in range(w0, w1)]
         order = []
