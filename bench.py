@@ -53,8 +53,16 @@ def work_model(x):
             m = mask[b, :nq, :nk].astype(np.int64)
             pairs += int(rows @ m @ keys)
             kv_read_rows += int(keys[m.any(axis=0)].sum())
-    elif w.causal:
-        pairs = int((lens * (lens + 1) // 2).sum())
+    elif w.causal or w.window is not None:
+        # visible pairs of the band j in [i - left, i + right] (causal: right = 0)
+        left = None if w.window is None else w.window[0]
+        right = 0 if w.causal else (None if w.window is None else w.window[1])
+        pairs = 0
+        for L in lens:
+            i = np.arange(int(L), dtype=np.int64)
+            lo = np.zeros_like(i) if left is None else np.maximum(0, i - left)
+            hi = np.full_like(i, L - 1) if right is None else np.minimum(L - 1, i + right)
+            pairs += int(np.maximum(0, hi - lo + 1).sum())
     else:
         pairs = int((q_lens * lens).sum())
     e = H * D * 2   # bytes of one bf16 row of all heads
@@ -84,7 +92,7 @@ def cpu_baseline(x, budget_s: float):
     w = x.workload
     q = x.as_f64("q") if w.broadcast_q else None
     done, flop, t_used = 0, 0.0, 0.0
-    kw = dict(scale=w.scale, broadcast_q=w.broadcast_q, causal=w.causal)
+    kw = dict(scale=w.scale, broadcast_q=w.broadcast_q, causal=w.causal, window=w.window)
     for b in range(x.batch):
         k0, k1 = int(x.kv_offsets[b]), int(x.kv_offsets[b + 1])
         k = W.bf16_bits_to_f32(x.k[k0:k1]).astype(np.float64)
@@ -110,6 +118,8 @@ def cpu_baseline(x, budget_s: float):
         if mask is not None:
             vis = A.visibility(n_rows, L, mask_b=mask[0])
             pairs = int(vis.sum())
+        elif w.window is not None:
+            pairs = int(A.visibility(n_rows, L, causal=w.causal, window=w.window).sum())
         elif w.causal:
             pairs = L * (L + 1) // 2
         else:
@@ -151,7 +161,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, help="1..5 (2: GEM-shaped broadcast-Q)")
+    ap.add_argument("--workload", type=int, default=2, help="1..6 (2: GEM-shaped broadcast-Q; 6: sliding window)")
     ap.add_argument("--fwd-workers-per-cu", type=int, default=1)
     ap.add_argument("--bwd-workers-per-cu", type=int, default=1)
     ap.add_argument("--fwd-plan", choices=("dynamic", "static"), default="dynamic",
@@ -182,7 +192,9 @@ def main():
     mq, mk = (x.block_mask.shape[1], x.block_mask.shape[2]) if x.block_mask is not None else (0, 0)
     prob = J.Problem(batch=x.batch, num_heads=w.heads, head_dim=w.head_dim,
                      broadcast_q=w.broadcast_q, lq=w.lq if w.broadcast_q else 0, causal=w.causal,
-                     mask_q_blocks=mq, mask_kv_blocks=mk, softmax_scale=w.scale)
+                     mask_q_blocks=mq, mask_kv_blocks=mk, softmax_scale=w.scale,
+                     window_left=-1 if w.window is None or w.window[0] is None else w.window[0],
+                     window_right=-1 if w.window is None or w.window[1] is None else w.window[1])
     cus = J.jfa_device_workers(0)
     t0 = time.perf_counter()
     att = J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask,
@@ -277,6 +289,7 @@ def main():
         "config": {"workload": wl_name, "batch": x.batch, "heads": H, "head_dim": D,
                    "broadcast_q": w.broadcast_q, "lq": w.lq if w.broadcast_q else None,
                    "causal": w.causal, "block_sparse": x.block_mask is not None,
+                   "window": w.window,
                    "lengths": w.lengths, "seed": w.seed, "total_kv": model["t_k"],
                    "total_q": model["t_q"],
                    "fwd_workers": att.fwd_plan.info.num_workers,

@@ -14,9 +14,14 @@
  *     s_ij = scale * <q_i, k_j>,  LSE_i = ln sum_j exp(s_ij),
  *     O_i  = sum_j exp(s_ij - LSE_i) v_j.
  * Visible keys: every key of the row's own sequence; with causal=1 only keys
- * j <= i (local indices); with a block mask only keys whose 128-key block is
- * kept for the row's 128-row Q tile ("TLX porta l'attenzione jagged su
- * Blackwell" (ai-radar.it), section "The turning point").
+ * j <= i (local indices); with a sliding window only keys
+ * i - window_left <= j <= i + window_right (the pages name sliding-window
+ * attention among the variants the kernel serves, theclarity.today second
+ * paragraph, without defining it: this band is the usual meaning; causal is
+ * the band with no left bound and right bound 0); with a block mask only keys
+ * whose 128-key block is kept for the row's 128-row Q tile ("TLX porta
+ * l'attenzione jagged su Blackwell" (ai-radar.it), section "The turning
+ * point").
  *
  * Layouts (all row-major, contiguous):
  *   q        bf16 [lq, H, D] when broadcast_q, else [T_q, H, D]
@@ -53,15 +58,15 @@
 extern "C" {
 #endif
 
-#define JFA_ABI_VERSION 3
+#define JFA_ABI_VERSION 4
 
 /* status codes */
 #define JFA_OK                 0
 #define JFA_ERR_INVALID_ARG   -1  /* null/misaligned pointer, bad size or flag */
 #define JFA_ERR_BAD_OFFSETS   -2  /* offsets[0] != 0, decreasing, or overflow   */
-#define JFA_ERR_UNSUPPORTED   -3  /* head_dim not 64/128, causal with broadcast
-                                     Q or with unequal Q/KV lengths, mask with
-                                     causal                                   */
+#define JFA_ERR_UNSUPPORTED   -3  /* head_dim not 64/128, causal or window with
+                                     broadcast Q or with unequal Q/KV lengths,
+                                     mask with causal or window               */
 #define JFA_ERR_PLAN_MISMATCH -4  /* plan built for another pass/problem      */
 #define JFA_ERR_WORKSPACE     -5  /* workspace too small                       */
 #define JFA_ERR_HIP           -6  /* a HIP call failed: see jfa_last_hip_error */
@@ -86,6 +91,11 @@ typedef struct jfa_problem {
     int32_t mask_q_blocks;  /* block-sparse mask dims; both 0 = dense          */
     int32_t mask_kv_blocks;
     float   softmax_scale;  /* finite and > 0; usually 1/sqrt(D)               */
+    int32_t window_left;    /* sliding window: key j visible to row i only if
+                               j >= i - window_left; -1 = no bound             */
+    int32_t window_right;   /* ... and only if j <= i + window_right; -1 = no
+                               bound (causal=1 makes it 0). Either bound needs
+                               per-sequence Q with the same lengths as KV      */
 } jfa_problem;
 
 /* Sizes of a plan, filled by jfa_plan_query / jfa_plan_build. */
@@ -129,7 +139,10 @@ int32_t jfa_offsets_from_lengths(const int32_t* h_lengths, int32_t batch, int32_
  *
  * Tiles are enumerated in (b, h, t) order. FWD: t is a Q tile of block_m=256
  * rows, work = KV blocks of block_n=64 keys visited (dense: ceil(Lk/64);
- * causal: ceil(min(256(t+1), L)/64); block-sparse: the 64-key blocks of the
+ * causal: ceil(min(256(t+1), L)/64); band (window, causal): the blocks from
+ * jmin/64 to jmax/64 with jmin = max(0, 256t - left), jmax = min(L - 1,
+ * 256t + 255 + right) (rows past L excluded), 0 if jmax < jmin; block-sparse:
+ * the 64-key blocks of the
  * 128-key mask blocks inside the sequence kept by either of the tile's two
  * 128-row mask rows). BWD: t is a KV tile of block_n=256 keys, work = Q
  * blocks of block_m=32 rows visited (dense: ceil(Lq/32); causal:

@@ -47,7 +47,8 @@ class JfaProblem(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("broadcast_q", ctypes.c_int32),
                 ("lq", ctypes.c_int32), ("causal", ctypes.c_int32),
                 ("mask_q_blocks", ctypes.c_int32), ("mask_kv_blocks", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("window_left", ctypes.c_int32),
+                ("window_right", ctypes.c_int32)]
 
 
 class JfaPlanInfo(ctypes.Structure):
@@ -166,11 +167,13 @@ class Problem:
     mask_q_blocks: int = 0
     mask_kv_blocks: int = 0
     softmax_scale: float = 0.0
+    window_left: int = -1     # sliding window bounds (-1: none)
+    window_right: int = -1
 
     def c(self) -> JfaProblem:
         return JfaProblem(self.batch, self.num_heads, self.head_dim, int(self.broadcast_q),
                           self.lq, int(self.causal), self.mask_q_blocks, self.mask_kv_blocks,
-                          self.softmax_scale)
+                          self.softmax_scale, self.window_left, self.window_right)
 
 
 def _i32(a):

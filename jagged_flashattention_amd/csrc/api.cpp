@@ -21,7 +21,7 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 jfa::Mode mode_of(const jfa_problem* p) {
     if (p->mask_q_blocks != 0) return jfa::kSparse;
-    if (p->causal) return jfa::kCausal;
+    if (jfa::band_of(p).on) return jfa::kCausal;   // banded: causal or sliding window
     return jfa::kDense;
 }
 
@@ -80,7 +80,7 @@ const char* jfa_status_string(int32_t status) {
         case JFA_OK: return "ok";
         case JFA_ERR_INVALID_ARG: return "invalid argument";
         case JFA_ERR_BAD_OFFSETS: return "bad offsets (offsets[0] != 0, decreasing, or overflow)";
-        case JFA_ERR_UNSUPPORTED: return "unsupported problem (head_dim, causal mode or mask)";
+        case JFA_ERR_UNSUPPORTED: return "unsupported problem (head_dim, causal/window mode or mask)";
         case JFA_ERR_PLAN_MISMATCH: return "plan does not match the problem or pass";
         case JFA_ERR_WORKSPACE: return "workspace too small";
         case JFA_ERR_HIP: return "HIP call failed";
@@ -154,6 +154,9 @@ int32_t jfa_fwd(const jfa_problem* prob, const jfa_plan_info* info, const int32_
     a.mask_q_blocks = prob->mask_q_blocks;
     a.num_workers = info->num_workers;
     a.num_tiles = info->num_tiles;
+    const jfa::Band bd = jfa::band_of(prob);
+    a.win_left = bd.left;
+    a.win_right = bd.right;
     a.counter = need > 0 ? static_cast<int32_t*>(workspace) : nullptr;
     a.scale_log2 = prob->softmax_scale * 1.4426950408889634f;
     return hip_status(jfa::launch_fwd(a, prob->head_dim, mode_of(prob), prob->broadcast_q != 0,
@@ -233,6 +236,9 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device
     a.total_q = ki->total_q;
     a.mask_kv_blocks = prob->mask_kv_blocks;
     a.num_workers = ki->num_tiles > 0 ? ki->num_workers : 0;  // 0: no dK/dV launch
+    const jfa::Band bd = jfa::band_of(prob);
+    a.win_left = bd.left;
+    a.win_right = bd.right;
     a.scale = prob->softmax_scale;
     a.scale_log2 = prob->softmax_scale * 1.4426950408889634f;
     st = hip_status(jfa::launch_bwd(a, prob->head_dim, mode, bcast,
@@ -257,6 +263,8 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device
         d.dq_accum = dq_accum;
         d.partial = static_cast<float*>(workspace);
         d.chunk_div = bcast ? (prob->lq + jfa::kFwdBlockM - 1) / jfa::kFwdBlockM : 0;
+        d.win_left = bd.left;
+        d.win_right = bd.right;
         d.num_heads = prob->num_heads;
         d.lq = prob->lq;
         d.total_q = qi->total_q;

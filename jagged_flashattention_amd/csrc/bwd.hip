@@ -21,6 +21,8 @@
 //   dS  = P * (dP - delta)
 //   dV^T += dO^T P       A = dO^T from LDS (rows in sigma order), B = P
 //   dK^T += Q^T dS       A = Q^T from LDS (rows in sigma order),  B = dS
+#include <climits>
+
 #include "qtile.h"
 
 namespace jfa {
@@ -120,7 +122,9 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
             T.Lq = ld_uniform(a.q_off + T.b + 1) - T.q0;
             T.orow0 = T.q0;
         }
-        T.r0 = MODE == kCausal ? (T.n * kBwdBlockN) / kBwdBlockM : 0;
+        // banded: the first Q block whose rows see the tile's keys (rows
+        // i >= j - right for key j)
+        T.r0 = MODE == kCausal && a.win_right >= 0 ? max(0, T.n * kBwdBlockN - a.win_right) / kBwdBlockM : 0;
         T.sp = nullptr;
         if (MODE == kSparse) T.sp = a.sp_idx + ld_uniform(a.sp_ptr + T.b * kv_tiles_per_row + T.n);
         return T;
@@ -273,8 +277,14 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
             const int rb = q_block(T, i);
             bool skip = !wave_keys, masked = false;
             if (MODE == kCausal) {
-                skip = skip || kBwdBlockM * rb + kBwdBlockM - 1 < key0;
-                masked = kBwdBlockM * rb < key0 + 31;
+                // row i sees key j iff j - wr <= i <= j + wl: rows R0..R1 and
+                // this wave's keys K0..K1 meet iff R1 >= K0 - wr and R0 <=
+                // K1 + wl; every pair is visible iff R0 >= K1 - wr and R1 <= K0 + wl
+                const int64_t R0 = kBwdBlockM * rb, R1 = R0 + kBwdBlockM - 1, K0 = key0, K1 = key0 + 31;
+                skip = skip || (a.win_right >= 0 && R1 < K0 - a.win_right) ||
+                       (a.win_left >= 0 && R0 > K1 + a.win_left);
+                masked = (a.win_right >= 0 && R0 < K1 - a.win_right) ||
+                         (a.win_left >= 0 && R1 > K0 + a.win_left);
             } else if (MODE == kSparse) {
                 skip = skip || !((ld_uniform(T.sp + (i >> 2)) >> (wave >> 2)) & 1);
             }
@@ -313,7 +323,15 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
             }
             if (kLateTranspose) transpose_q(s + 1);
             // P and dS; register r is query row 32rb + 8(r/4) + 4hf + r%4, the
-            // column this lane's key 32wave + lr (tile-local)
+            // column this lane's key 32wave + lr (tile-local). Banded: with
+            // c = 8(r/4) + r%4, key - row = base - c, visible iff
+            // c_lo <= c <= c_hi
+            int c_lo = INT_MIN, c_hi = INT_MAX;
+            if (MODE == kCausal && masked) {
+                const int base = key0 + lr - kBwdBlockM * rb - 4 * hf;
+                if (a.win_right >= 0) c_lo = base - a.win_right;
+                if (a.win_left >= 0) c_hi = base + a.win_left;
+            }
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int row = 8 * g + 4 * hf;
@@ -323,7 +341,8 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
                 for (int j = 0; j < 4; ++j) {
                     float p = __builtin_amdgcn_exp2f(fmaf(sc[4 * g + j], a.scale_log2, -l4[j]));
                     if (MODE == kCausal && masked) {
-                        if (key0 + lr > kBwdBlockM * rb + row + j) p = 0.f;
+                        const int c = 8 * g + j;
+                        if (c < c_lo || c > c_hi) p = 0.f;
                     }
                     sc[4 * g + j] = p;
                     dp[4 * g + j] = p * (dp[4 * g + j] - d4[j]);

@@ -90,7 +90,7 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
     const int t_begin = ld_uniform(a.worker_ptr + w), t_end = ld_uniform(a.worker_ptr + w + 1);
     auto tile_info = [&](int ti) {
         return qtile::tile_info<MODE>(a.tiles, a.kv_off, a.sp_ptr, a.sp_idx, a.mask_q_blocks,
-                                      a.chunk_div, ti);
+                                      a.chunk_div, a.win_left, a.win_right, ti);
     };
 
     // ---- loader: the worker's blocks in plan order, kAhead blocks ahead
@@ -263,12 +263,16 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
                     pipeline_reads_mfma<2 * KC, kReadAhead>();
                 }
                 // register r is key 64n + 32hb + 8(r/4) + 4hf + r%4
-                if (masked) {
-                    const int lim = MODE == kCausal ? min(T.L - 1, qrow) : T.L - 1;
+                if (masked) {   // keys past the sequence or (banded) outside [lo, lim]
+                    int lim = T.L - 1, lo = 0;
+                    if (MODE == kCausal) {
+                        if (T.wr >= 0 && qrow <= T.L - 1 - T.wr) lim = qrow + T.wr;
+                        if (T.wl >= 0) lo = qrow - T.wl;
+                    }
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int kk = kFwdBlockN * n + 32 * hb + 8 * (r >> 2) + 4 * hf + (r & 3);
-                        sc[r] = kk <= lim ? sc[r] : -INFINITY;
+                        sc[r] = (kk <= lim && kk >= lo) ? sc[r] : -INFINITY;
                     }
                 }
                 bf16x8 db[2];

@@ -104,7 +104,8 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
     const bool dynamic = a.counter != nullptr;
 
     auto tile_info = [&](int ti) {
-        return qtile::tile_info<MODE>(a.tiles, a.kv_off, a.sp_ptr, a.sp_idx, a.mask_q_blocks, 0, ti);
+        return qtile::tile_info<MODE>(a.tiles, a.kv_off, a.sp_ptr, a.sp_idx, a.mask_q_blocks, 0,
+                                      a.win_left, a.win_right, ti);
     };
     auto seq_block = [&](const TileInfo& T, int i) { return qtile::seq_block<MODE>(T, i); };
     // Q / O rows of a tile's sequence: first Q row, row count, first O row
@@ -354,15 +355,20 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
                 f32x16 sc[2];
                 compute_s(sc, s);
                 pipeline_reads_mfma<2 * KC, kReadAhead>();
-                // masked tail: keys past the sequence (and, causal, past the row) -> -inf
+                // masked tail: keys past the sequence (and, banded, outside the
+                // row's window [lo, lim]) -> -inf
                 if (masked) {
-                    const int lim = MODE == kCausal ? min(T.L - 1, qrow) : T.L - 1;
+                    int lim = T.L - 1, lo = 0;
+                    if (MODE == kCausal) {
+                        if (T.wr >= 0 && qrow <= T.L - 1 - T.wr) lim = qrow + T.wr;
+                        if (T.wl >= 0) lo = qrow - T.wl;
+                    }
 #pragma unroll
                     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int kk = kFwdBlockN * n + 32 * mb + 8 * (r >> 2) + 4 * hf + (r & 3);
-                            sc[mb][r] = kk <= lim ? sc[mb][r] : -INFINITY;
+                            sc[mb][r] = (kk <= lim && kk >= lo) ? sc[mb][r] : -INFINITY;
                         }
                 }
                 float mx = -INFINITY;

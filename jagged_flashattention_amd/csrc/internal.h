@@ -24,7 +24,21 @@ constexpr int32_t kDqChunkBlocks = 16;
 int32_t check_problem(const jfa_problem* p);
 int32_t check_offsets(const int32_t* off, int32_t batch);
 
+// kCausal is the banded mode: causal and sliding-window attention (a key
+// window [i - left, i + right] per query row i, a bound < 0 meaning none).
 enum Mode : int32_t { kDense = 0, kCausal = 1, kSparse = 2 };
+
+struct Band {
+    bool on;
+    int32_t left, right;   // -1: unbounded
+};
+inline Band band_of(const jfa_problem* p) {
+    Band b;
+    b.left = p->window_left;
+    b.right = p->causal ? 0 : p->window_right;
+    b.on = p->causal || p->window_left >= 0 || p->window_right >= 0;
+    return b;
+}
 
 struct FwdArgs {
     const int32_t* worker_ptr;
@@ -44,6 +58,7 @@ struct FwdArgs {
     int32_t mask_q_blocks;
     int32_t num_workers;
     int32_t num_tiles;
+    int32_t win_left, win_right;   // banded mode: window bounds (-1: none)
     int32_t* counter;       // dynamic plan: [0] tiles claimed, [1] workgroups done; else null
     float scale_log2;       // softmax_scale * log2(e)
 };
@@ -74,6 +89,7 @@ struct BwdArgs {
     int32_t total_q;
     int32_t mask_kv_blocks;
     int32_t num_workers;
+    int32_t win_left, win_right;   // banded mode: window bounds (-1: none)
     float scale;
     float scale_log2;
 };
@@ -96,6 +112,7 @@ struct DqArgs {
     float* dq_accum;         // per-sequence Q: fp32 [T_q, H, D]
     float* partial;          // broadcast Q: fp32 [W][256][D] per-worker partial sums
     int32_t chunk_div;       // broadcast Q: Q tiles per sequence (chunked tile records), else 0
+    int32_t win_left, win_right;   // banded mode: window bounds (-1: none)
     int32_t num_heads;
     int32_t lq;
     int32_t total_q;

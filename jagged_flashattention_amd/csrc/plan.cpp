@@ -42,10 +42,12 @@ int32_t check_problem(const jfa_problem* p) {
     if (p->head_dim != 64 && p->head_dim != 128) return JFA_ERR_UNSUPPORTED;
     // finite and positive (the kernels take the row max before scaling)
     if (!(p->softmax_scale > 0.0f) || p->softmax_scale > 3.0e38f) return JFA_ERR_INVALID_ARG;
-    if (p->causal && p->broadcast_q) return JFA_ERR_UNSUPPORTED;
+    if (p->window_left < -1 || p->window_right < -1) return JFA_ERR_INVALID_ARG;
+    const bool banded = p->causal || p->window_left >= 0 || p->window_right >= 0;
+    if (banded && p->broadcast_q) return JFA_ERR_UNSUPPORTED;
     const bool sparse = p->mask_q_blocks != 0 || p->mask_kv_blocks != 0;
     if (sparse && (p->mask_q_blocks < 1 || p->mask_kv_blocks < 1)) return JFA_ERR_BAD_MASK;
-    if (sparse && p->causal) return JFA_ERR_UNSUPPORTED;
+    if (sparse && banded) return JFA_ERR_UNSUPPORTED;
     // rows of the packed tensors are addressed as int32 * H * D elements in 64 bits;
     // keep H*D within int32
     if ((int64_t)p->num_heads * p->head_dim > (1 << 24)) return JFA_ERR_INVALID_ARG;
@@ -77,7 +79,7 @@ int32_t lengths_of(const jfa_problem* p, const int32_t* qo, const int32_t* ko, L
         if (st) return st;
         for (int32_t b = 0; b < p->batch; ++b) L.q[b] = qo[b + 1] - qo[b];
         L.total_q = qo[p->batch];
-        if (p->causal)
+        if (band_of(p).on)
             for (int32_t b = 0; b < p->batch; ++b)
                 if (L.q[b] != L.kv[b]) return JFA_ERR_UNSUPPORTED;
     }
@@ -143,8 +145,13 @@ int32_t tile_work(const jfa_problem* p, const uint8_t* mask, int32_t pass, int32
                               kFwdBlockN);
             return (int32_t)w;
         }
-        if (p->causal)
-            return (int32_t)cdiv(std::min<int64_t>((int64_t)(t + 1) * kFwdBlockM, lk), kFwdBlockN);
+        const Band bd = band_of(p);
+        if (bd.on) {   // the tile's rows see the contiguous key range j0..j1
+            const int64_t r0 = (int64_t)t * kFwdBlockM, r1 = std::min<int64_t>(r0 + kFwdBlockM, lq) - 1;
+            const int64_t j0 = bd.left < 0 ? 0 : std::max<int64_t>(0, r0 - bd.left);
+            const int64_t j1 = bd.right < 0 ? lk - 1 : std::min<int64_t>(lk - 1, r1 + bd.right);
+            return j1 < j0 ? 0 : (int32_t)(j1 / kFwdBlockN - j0 / kFwdBlockN + 1);
+        }
         return (int32_t)cdiv(lk, kFwdBlockN);
     }
     const int32_t nqb = (int32_t)cdiv(lq, kBwdBlockM);
@@ -156,7 +163,13 @@ int32_t tile_work(const jfa_problem* p, const uint8_t* mask, int32_t pass, int32
                           kBwdBlockM);
         return (int32_t)w;
     }
-    if (p->causal) return nqb - (int32_t)(((int64_t)t * kBwdBlockN) / kBwdBlockM);
+    const Band bd = band_of(p);
+    if (bd.on) {   // rows i see key j iff j - right <= i <= j + left
+        const int64_t k0 = (int64_t)t * kBwdBlockN, k1 = std::min<int64_t>(k0 + kBwdBlockN, lk) - 1;
+        const int64_t i0 = bd.right < 0 ? 0 : std::max<int64_t>(0, k0 - bd.right);
+        const int64_t i1 = bd.left < 0 ? lq - 1 : std::min<int64_t>(lq - 1, k1 + bd.left);
+        return i1 < i0 ? 0 : (int32_t)(i1 / kBwdBlockM - i0 / kBwdBlockM + 1);
+    }
     return nqb;
 }
 

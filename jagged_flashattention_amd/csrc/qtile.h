@@ -70,9 +70,10 @@ __device__ __forceinline__ void load_lds16(const uint16_t* g, char* lds_wave_bas
 
 // One tile of a Q-tile plan (wave-uniform): Q tile t of sequence b, head h,
 // visiting positions k0 .. k0+work-1 of the tile's block list (k0 > 0 only
-// for a chunk of a split broadcast-Q dQ tile).
+// for a chunk of a split broadcast-Q dQ tile). Banded mode: the list is the
+// KV blocks c0, c0+1, ... and wl, wr are the window bounds (-1: none).
 struct TileInfo {
-    int b, h, t, k0, work, kv0, L;
+    int b, h, t, k0, work, kv0, L, c0, wl, wr;
     const int* sp;   // block-sparse list of the tile (4c + keep bits), else null
 };
 
@@ -81,7 +82,8 @@ struct TileInfo {
 template <int MODE>
 __device__ __forceinline__ TileInfo tile_info(const int32_t* tiles, const int32_t* kv_off,
                                               const int32_t* sp_ptr, const int32_t* sp_idx,
-                                              int32_t mask_q_blocks, int chunk_div, int ti) {
+                                              int32_t mask_q_blocks, int chunk_div, int win_left,
+                                              int win_right, int ti) {
     TileInfo T;
     T.b = ld_uniform(tiles + 4 * ti + 0);
     T.h = ld_uniform(tiles + 4 * ti + 1);
@@ -93,6 +95,10 @@ __device__ __forceinline__ TileInfo tile_info(const int32_t* tiles, const int32_
     T.L = ld_uniform(kv_off + T.b + 1) - T.kv0;
     T.sp = nullptr;
     if (MODE == kSparse) T.sp = sp_idx + ld_uniform(sp_ptr + T.b * ((mask_q_blocks + 1) >> 1) + T.t);
+    T.wl = win_left;
+    T.wr = win_right;
+    T.c0 = 0;   // the first key the tile's rows see, in blocks
+    if (MODE == kCausal && win_left >= 0) T.c0 = max(0, T.t * kFwdBlockM - win_left) / kFwdBlockN;
     return T;
 }
 
@@ -100,6 +106,7 @@ __device__ __forceinline__ TileInfo tile_info(const int32_t* tiles, const int32_
 template <int MODE>
 __device__ __forceinline__ int seq_block(const TileInfo& T, int i) {
     if (MODE == kSparse) return 2 * (ld_uniform(T.sp + (i >> 1)) >> 2) + (i & 1);
+    if (MODE == kCausal) return T.c0 + i;
     return i;
 }
 
@@ -110,8 +117,12 @@ __device__ __forceinline__ void block_flags(const TileInfo& T, int i, int n, int
                                             int wave, bool& skip, bool& masked) {
     skip = !wave_rows;
     if (MODE == kCausal) {
-        skip = skip || kFwdBlockN * n > row0 + 31;
-        masked = kFwdBlockN * n + kFwdBlockN - 1 > row0 || kFwdBlockN * (n + 1) > T.L;
+        // rows R0..R1 see keys [R0 - wl, R1 + wr]; every row sees the whole
+        // block [K0, K1] iff K0 >= R1 - wl and K1 <= R0 + wr
+        const int64_t R0 = row0, R1 = row0 + 31, K0 = (int64_t)kFwdBlockN * n, K1 = K0 + kFwdBlockN - 1;
+        skip = skip || (T.wr >= 0 && K0 > R1 + T.wr) || (T.wl >= 0 && K1 < R0 - T.wl);
+        masked = (T.wr >= 0 && K1 > R0 + T.wr) || (T.wl >= 0 && K0 < R1 - T.wl) ||
+                 kFwdBlockN * (n + 1) > T.L;
     } else {
         masked = kFwdBlockN * (n + 1) > T.L;
         if (MODE == kSparse) skip = skip || !((ld_uniform(T.sp + (i >> 1)) >> (wave >> 2)) & 1);

@@ -27,7 +27,12 @@ sum over the whole batch ([clarity] second paragraph; [bites] section
 Visibility. All keys of the row's own sequence; with ``causal`` only keys
 j <= i (local indices, Q and KV share offsets); with a block mask only keys
 whose 128-key block is kept for the row's 128-row Q tile ([radar] section "The
-turning point": the block-sparse variant iterates only over selected blocks).
+turning point": the block-sparse variant iterates only over selected blocks);
+with a sliding window (left, right) only keys i - left <= j <= i + right, a
+bound being None when absent (the pages name sliding-window attention as one
+of the variants the kernel serves -- [clarity] second paragraph, [bites] "Why
+attention in GEM needed a rewrite" -- without defining it; this band of local
+indices is the usual meaning, and causal is the band (None, 0)).
 A row with no visible key has O = 0, LSE = -inf and contributes no gradient.
 
 Inputs are float64 arrays holding bf16-representable values:
@@ -49,13 +54,19 @@ def _q_rows(b, kv_offsets, q_offsets, lq, broadcast_q):
     return slice(lo, hi), slice(lo, hi)
 
 
-def visibility(n_rows, n_keys, *, causal=False, mask_b=None, rows=None):
+def visibility(n_rows, n_keys, *, causal=False, window=None, mask_b=None, rows=None):
     """bool [len(rows), n_keys]: key j visible to local query row i."""
     i = np.arange(n_rows) if rows is None else np.asarray(rows)
     j = np.arange(n_keys)
     vis = np.ones((len(i), n_keys), dtype=bool)
     if causal:
         vis &= j[None, :] <= i[:, None]
+    if window is not None:
+        left, right = window
+        if left is not None:
+            vis &= j[None, :] >= i[:, None] - left
+        if right is not None:
+            vis &= j[None, :] <= i[:, None] + right
     if mask_b is not None:
         vis &= mask_b[(i // MASK_BLOCK)[:, None], (j // MASK_BLOCK)[None, :]].astype(bool)
     return vis
@@ -87,7 +98,7 @@ def _problem(q, kv_offsets, q_offsets, broadcast_q):
 
 
 def forward(q, k, v, kv_offsets, *, scale, broadcast_q, q_offsets=None, causal=False,
-            block_mask=None, seqs=None, heads=None):
+            block_mask=None, seqs=None, heads=None, window=None):
     """O [T_q,H,D] and LSE [H,T_q] (float64). Rows of sequences not in ``seqs``
     (default: all) stay 0 / -inf."""
     B, lq, t_q = _problem(q, kv_offsets, q_offsets, broadcast_q)
@@ -98,7 +109,7 @@ def forward(q, k, v, kv_offsets, *, scale, broadcast_q, q_offsets=None, causal=F
         qs, os_ = _q_rows(b, kv_offsets, q_offsets, lq, broadcast_q)
         ks = slice(int(kv_offsets[b]), int(kv_offsets[b + 1]))
         n_rows, n_keys = qs.stop - qs.start, ks.stop - ks.start
-        vis = visibility(n_rows, n_keys, causal=causal,
+        vis = visibility(n_rows, n_keys, causal=causal, window=window,
                          mask_b=None if block_mask is None else block_mask[b])
         for h in (range(H) if heads is None else heads):
             s = scale * (q[qs, h, :] @ k[ks, h, :].T)
@@ -109,13 +120,13 @@ def forward(q, k, v, kv_offsets, *, scale, broadcast_q, q_offsets=None, causal=F
 
 
 def forward_rows(q, k, v, kv_offsets, b, h, rows, *, scale, broadcast_q, q_offsets=None,
-                 causal=False, block_mask=None):
+                 causal=False, block_mask=None, window=None):
     """O [len(rows), D] and LSE [len(rows)] for local query rows of (b, h) only."""
     B, lq, _ = _problem(q, kv_offsets, q_offsets, broadcast_q)
     qs, _ = _q_rows(b, kv_offsets, q_offsets, lq, broadcast_q)
     ks = slice(int(kv_offsets[b]), int(kv_offsets[b + 1]))
     rows = np.asarray(rows)
-    vis = visibility(qs.stop - qs.start, ks.stop - ks.start, causal=causal,
+    vis = visibility(qs.stop - qs.start, ks.stop - ks.start, causal=causal, window=window,
                      mask_b=None if block_mask is None else block_mask[b], rows=rows)
     s = scale * (q[qs.start + rows, h, :] @ k[ks, h, :].T)
     l, p = _softmax_stats(s, vis)
@@ -123,7 +134,7 @@ def forward_rows(q, k, v, kv_offsets, b, h, rows, *, scale, broadcast_q, q_offse
 
 
 def backward(q, k, v, do, kv_offsets, *, scale, broadcast_q, q_offsets=None, causal=False,
-             block_mask=None, seqs=None, heads=None):
+             block_mask=None, seqs=None, heads=None, window=None):
     """dQ (shape of q), dK, dV [T_k,H,D] and delta [H,T_q], all float64.
 
     With ``seqs`` given, only those sequences contribute (their dK/dV rows are
@@ -138,7 +149,7 @@ def backward(q, k, v, do, kv_offsets, *, scale, broadcast_q, q_offsets=None, cau
         qs, os_ = _q_rows(b, kv_offsets, q_offsets, lq, broadcast_q)
         ks = slice(int(kv_offsets[b]), int(kv_offsets[b + 1]))
         n_rows, n_keys = qs.stop - qs.start, ks.stop - ks.start
-        vis = visibility(n_rows, n_keys, causal=causal,
+        vis = visibility(n_rows, n_keys, causal=causal, window=window,
                          mask_b=None if block_mask is None else block_mask[b])
         for h in (range(H) if heads is None else heads):
             qb, kb, vb, dob = q[qs, h, :], k[ks, h, :], v[ks, h, :], do[os_, h, :]

@@ -15,11 +15,21 @@ plainest readings, written out step by step here, are:
     forward (KV blocks of ``block_n`` keys visited):
       dense        ceil(Lk_b / block_n)
       causal       ceil(min((t+1)*block_m, Lk_b) / block_n)
+      band         (sliding window (left, right), causal = (none, 0); Q and KV
+                   share lengths): the keys the tile's rows r0..r1 see span
+                   jmin = max(0, r0 - left) .. jmax = min(Lk_b - 1, r1 + right),
+                   a contiguous range, so work = jmax // block_n - jmin // block_n
+                   + 1 (0 if jmax < jmin) and the tile starts at block
+                   jmin // block_n
       block-sparse sum over the 128-key mask blocks c kept by any mask row of
                    the tile of ceil((min(128(c+1), Lk_b) - 128c) / block_n)
     backward (Q blocks of ``block_m`` rows visited):
       dense        ceil(Lq_b / block_m)
       causal       ceil(Lq_b / block_m) - floor(t*block_n / block_m)
+      band         the rows that see keys k0..k1 span imin = max(0, k0 - right)
+                   .. imax = min(Lq_b - 1, k1 + left): work = imax // block_m
+                   - imin // block_m + 1 (0 if imax < imin), starting at Q
+                   block imin // block_m
       block-sparse sum over the 128-row mask rows m kept by any mask column
                    of the tile of ceil((min(128(m+1), Lq_b) - 128m) / block_m)
  3. Stable sort by work, descending (ties keep enumeration order).
@@ -144,20 +154,44 @@ def sparse_lists(block_mask, q_lens, kv_lens, pass_, *, block_m=MASK_BLOCK, bloc
     return np.array(ptr, dtype=np.int32), np.array(idx, dtype=np.int32)
 
 
-def _tile_work(pass_, b, t, lq_b, lk_b, *, block_m, block_n, causal, block_mask):
+def band(causal, window):
+    """(left, right) bounds of the visible band (None: unbounded), or None."""
+    left, right = (None, None) if window is None else window
+    if causal:
+        right = 0 if right is None else min(right, 0)
+    if left is None and right is None:
+        return None
+    return left, right
+
+
+def band_range(lo, hi, n, left, right):
+    """Rows lo..hi see keys (or keys lo..hi are seen by rows) in
+    [max(0, lo - left), min(n - 1, hi + right)]: that range as (first, last)."""
+    first = 0 if left is None else max(0, lo - left)
+    last = n - 1 if right is None else min(n - 1, hi + right)
+    return first, last
+
+
+def _tile_work(pass_, b, t, lq_b, lk_b, *, block_m, block_n, causal, block_mask, window=None):
+    bd = band(causal, window)
     if pass_ == FWD:
         if block_mask is not None:
             return sum(cdiv(min(MASK_BLOCK * (c + 1), lk_b) - MASK_BLOCK * c, block_n)
                        for c, _ in _fwd_row_entries(block_mask, b, t, lq_b, lk_b, block_m))
-        if causal:
-            return cdiv(min((t + 1) * block_m, lk_b), block_n)
+        if bd is not None:
+            r0, r1 = t * block_m, min((t + 1) * block_m, lq_b) - 1
+            j0, j1 = band_range(r0, r1, lk_b, *bd)
+            return 0 if j1 < j0 else j1 // block_n - j0 // block_n + 1
         return cdiv(lk_b, block_n)
     nqb = cdiv(lq_b, block_m)
     if block_mask is not None:
         return sum(cdiv(min(MASK_BLOCK * (m + 1), lq_b) - MASK_BLOCK * m, block_m)
                    for m, _ in _bwd_col_entries(block_mask, b, t, lq_b, lk_b, block_n))
-    if causal:
-        return nqb - (t * block_n) // block_m
+    if bd is not None:
+        k0, k1 = t * block_n, min((t + 1) * block_n, lk_b) - 1
+        # rows i see key j iff j - right <= i <= j + left
+        i0, i1 = band_range(k0, k1, lq_b, bd[1], bd[0])
+        return 0 if i1 < i0 else i1 // block_m - i0 // block_m + 1
     return nqb
 
 
@@ -171,11 +205,11 @@ def _snake(order_len, W):
 
 
 def plan_dq(q_lens, kv_lens, num_heads, num_workers, *, broadcast_q, lq=0, block_m, block_n,
-            causal=False, block_mask=None):
+            causal=False, block_mask=None, window=None):
     """dQ pass. Returns (worker_ptr int32 [W'+1], tiles int32 [N, 4])."""
     if not broadcast_q:
         return plan(q_lens, kv_lens, num_heads, num_workers, FWD, block_m=block_m,
-                    block_n=block_n, causal=causal, block_mask=block_mask)
+                    block_n=block_n, causal=causal, block_mask=block_mask, window=window)
     B = len(kv_lens)
     nqt = cdiv(int(lq), block_m)
     G = num_heads * nqt
@@ -210,7 +244,7 @@ def plan_dq(q_lens, kv_lens, num_heads, num_workers, *, broadcast_q, lq=0, block
 
 
 def plan(q_lens, kv_lens, num_heads, num_workers, pass_, *, block_m, block_n,
-         causal=False, block_mask=None, dynamic=False):
+         causal=False, block_mask=None, dynamic=False, window=None):
     """Returns (worker_ptr int32 [W+1], tiles int32 [N, 4])."""
     B = len(kv_lens)
     W = int(num_workers)
@@ -223,7 +257,7 @@ def plan(q_lens, kv_lens, num_heads, num_workers, pass_, *, block_m, block_n,
         for h in range(num_heads):
             for t in range(n_t):
                 w = _tile_work(pass_, b, t, lq_b, lk_b, block_m=block_m, block_n=block_n,
-                               causal=causal, block_mask=block_mask)
+                               causal=causal, block_mask=block_mask, window=window)
                 tiles.append((b, h, t, w))
     order = sorted(range(len(tiles)), key=lambda i: -tiles[i][3])   # stable
     if dynamic:

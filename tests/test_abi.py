@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert J.jfa_abi_version() == 3
+    assert J.jfa_abi_version() == 4
     for st in range(-7, 1):
         assert J.jfa_status_string(st) not in ("", "unknown status")
     assert J.jfa_status_string(-99) == "unknown status"
@@ -74,6 +74,11 @@ def _prob(**kw):
     (dict(softmax_scale=-0.5), None, [0, 3, 5], None, J.JFA_ERR_INVALID_ARG),
     (dict(softmax_scale=0.0), None, [0, 3, 5], None, J.JFA_ERR_INVALID_ARG),
     (dict(softmax_scale=float("inf")), None, [0, 3, 5], None, J.JFA_ERR_INVALID_ARG),
+    (dict(window_left=4), None, [0, 3, 5], None, J.JFA_ERR_UNSUPPORTED),       # window, broadcast
+    (dict(broadcast_q=False, window_right=-2), [0, 3, 5], [0, 3, 5], None, J.JFA_ERR_INVALID_ARG),
+    (dict(broadcast_q=False, window_left=3), [0, 3, 6], [0, 3, 5], None, J.JFA_ERR_UNSUPPORTED),
+    (dict(broadcast_q=False, window_left=3, mask_q_blocks=1, mask_kv_blocks=1), [0, 3, 5],
+     [0, 3, 5], np.ones((2, 1, 1), np.uint8), J.JFA_ERR_UNSUPPORTED),
 ])
 def test_planner_rejects_bad_problems(kw, qoff, kvoff, mask, status):
     with pytest.raises(J.JfaError) as e:

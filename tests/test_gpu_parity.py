@@ -1,7 +1,7 @@
 """Parity of the HIP path (through the C ABI) with the fp64 oracle.
 
 Small cases: the oracle evaluates every output; they span several tiles and
-ragged tails of every mode (broadcast Q, per-sequence Q, causal, block-sparse,
+ragged tails of every mode (broadcast Q, per-sequence Q, causal, sliding window, block-sparse,
 D = 64 and 128, empty and one-key sequences, Lq not a multiple of the tile).
 Full sizes: the five workloads run in the launch configuration the benchmark
 times, and sampled outputs are compared with the oracle row by row.
@@ -44,7 +44,13 @@ def problem_of(x):
     return J.Problem(batch=x.batch, num_heads=w.heads, head_dim=w.head_dim,
                      broadcast_q=w.broadcast_q, lq=w.lq if w.broadcast_q else 0,
                      causal=w.causal, mask_q_blocks=mq, mask_kv_blocks=mk,
-                     softmax_scale=w.scale)
+                     softmax_scale=w.scale, window_left=_bound(w.window, 0),
+                     window_right=_bound(w.window, 1))
+
+
+def _bound(window, k):
+    """ABI encoding of one side of a sliding window (-1: none)."""
+    return -1 if window is None or window[k] is None else int(window[k])
 
 
 @dataclasses.dataclass
@@ -87,7 +93,7 @@ def oracle_full(x):
     q, k, v, do = (x.as_f64(n) for n in ("q", "k", "v", "do"))
     w = x.workload
     kw = dict(scale=w.scale, broadcast_q=w.broadcast_q, q_offsets=x.q_offsets, causal=w.causal,
-              block_mask=x.block_mask)
+              block_mask=x.block_mask, window=w.window)
     o, lse = A.forward(q, k, v, x.kv_offsets, **kw)
     dq, dk, dv, delta = A.backward(q, k, v, do, x.kv_offsets, **kw)
     return o, lse, dq, dk, dv, delta
@@ -117,9 +123,9 @@ def check_all(x, g):
 
 
 def _custom(name, *, broadcast, H, D, lengths, lq=0, causal=False, mask_seed=None, seed=11,
-            q_lengths=None):
+            q_lengths=None, window=None):
     w = W.Workload(name, len(lengths), H, D, broadcast, lq, causal, "const:1", seed=seed,
-                   mask_seed=mask_seed)
+                   mask_seed=mask_seed, window=window)
     x = W.make_inputs(w, lengths=np.array(lengths))
     if q_lengths is not None:
         # per-sequence Q with its own lengths: redraw Q / dO rows for them
@@ -135,6 +141,7 @@ def _custom(name, *, broadcast, H, D, lengths, lq=0, causal=False, mask_seed=Non
 
 RAGGED = [0, 1, 15, 16, 63, 64, 65, 127, 128, 129, 200, 300]
 CAUSAL = [1, 63, 64, 65, 128, 129, 257, 400]
+WINDOWED = [1, 5, 64, 129, 300, 600, 0]
 
 SMALL_CASES = {
     "cfg1": lambda: W.make_inputs(1),
@@ -144,6 +151,17 @@ SMALL_CASES = {
                                    lengths=[70, 3, 200, 129, 0], q_lengths=[5, 130, 64, 1, 7]),
     "causal_d128": lambda: _custom("c128", broadcast=False, H=2, D=128, lengths=CAUSAL, causal=True),
     "causal_d64": lambda: _custom("c64", broadcast=False, H=2, D=64, lengths=CAUSAL, causal=True),
+    # sliding windows: causal with a left bound, two-sided, one-sided, zero width
+    "window_causal_d128": lambda: _custom("w1", broadcast=False, H=2, D=128, lengths=WINDOWED,
+                                          causal=True, window=(100, None)),
+    "window_band_d128": lambda: _custom("w2", broadcast=False, H=2, D=128, lengths=WINDOWED,
+                                        window=(300, 40)),
+    "window_right_d64": lambda: _custom("w3", broadcast=False, H=2, D=64, lengths=WINDOWED,
+                                        window=(None, 70)),
+    "window_zero_d64": lambda: _custom("w4", broadcast=False, H=2, D=64, lengths=WINDOWED,
+                                       window=(0, 0)),
+    "window_wide_d128": lambda: _custom("w5", broadcast=False, H=1, D=128, lengths=[1200, 700, 1],
+                                        causal=True, window=(513, None)),
     "sparse_d128": lambda: _custom("s128", broadcast=True, H=2, D=128, lq=256, mask_seed=5,
                                    lengths=[1, 64, 65, 127, 128, 129, 300, 513, 640]),
     "sparse_d64": lambda: _custom("s64", broadcast=True, H=2, D=64, lq=200, mask_seed=7,
@@ -175,6 +193,19 @@ def test_one_key_sequence_is_bitwise_v_row():
     for b, row in ((0, 0), (2, 6)):
         for h in range(2):
             assert np.array_equal(o[b * 70:(b + 1) * 70, h], np.broadcast_to(x.v[row, h], (70, 128)))
+
+
+def test_zero_width_window_is_bitwise_v():
+    """Window (0, 0): each row sees its own key alone, so P = 1 exactly: O is
+    bitwise the bf16 V row and dV bitwise dO. dK = scale (dP - delta) q is
+    zero up to the rounding of dP - delta (two fp32 sums of the same
+    products in different orders)."""
+    x = SMALL_CASES["window_zero_d64"]()
+    g = run_gpu(x)
+    o = g.o.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(o, x.v)
+    assert np.array_equal(g.dv.view(torch.int16).cpu().numpy().view(np.uint16), x.do)
+    assert g.dk.float().abs().max().item() <= 1e-5
 
 
 def test_zero_q_gives_mean_of_v():
@@ -219,6 +250,7 @@ def _bits(t):
 
 
 @pytest.mark.parametrize("case", ["bcast_ragged_d128", "perseq_d128", "causal_d64", "sparse_d128",
+                                  "window_band_d128",
                                   "cfg2_small"])
 def test_dynamic_forward_equals_static(case):
     """The dynamic plan (tiles claimed at run time) gives O and LSE bitwise
@@ -252,7 +284,7 @@ def _head_f64(bits, h, rows=None):
     return W.bf16_bits_to_f32(sl).astype(np.float64)[:, None, :]
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5, 6])
 def test_full_size_sampled_parity(cfg):
     print("full-size workload", cfg, flush=True)
     x = W.make_inputs(cfg)
@@ -283,7 +315,7 @@ def test_full_size_sampled_parity(cfg):
             qoff = None if w.broadcast_q else np.array([0, qs.stop - qs.start], dtype=np.int32)
             mask = None if x.block_mask is None else x.block_mask[b:b + 1]
             kw = dict(scale=w.scale, broadcast_q=w.broadcast_q, q_offsets=qoff, causal=w.causal,
-                      block_mask=mask)
+                      block_mask=mask, window=w.window)
             o, lse = A.forward(q1, k1_, v1, off, **kw)
             dq, dk, dv, _ = A.backward(q1, k1_, v1, do1, off, **kw)
             assert np.abs(W.bf16_bits_to_f32(go[os_, h]) - o[:, 0]).max() <= TOL_O, (b, h)

@@ -42,7 +42,8 @@ def test_hand_worked_example():
     np.testing.assert_allclose(delta, [[11.0, 2.0]], rtol=0, atol=1e-12)
 
 
-def _small(broadcast, causal=False, lengths=(5, 1, 9, 3), lq=6, H=2, D=8, seed=0, mask=None):
+def _small(broadcast, causal=False, lengths=(5, 1, 9, 3), lq=6, H=2, D=8, seed=0, mask=None,
+           window=None):
     rng = np.random.default_rng(seed)
     lengths = np.array(lengths)
     off = W.offsets_of(lengths)
@@ -60,7 +61,15 @@ def _small(broadcast, causal=False, lengths=(5, 1, 9, 3), lq=6, H=2, D=8, seed=0
     do = rng.standard_normal((tq, H, D))
     kw = dict(scale=1 / math.sqrt(D), broadcast_q=broadcast, q_offsets=qoff, causal=causal,
               block_mask=mask)
+    if window is not None:
+        kw["window"] = window
     return q, k, v, do, off, kw
+
+
+def _in_band(i, j, window):
+    """Key j inside row i's sliding window (left, right), None = unbounded."""
+    left, right = window
+    return (left is None or j >= i - left) and (right is None or j <= i + right)
 
 
 def _seq_iter(off, qoff, lq, broadcast):
@@ -135,6 +144,8 @@ def _brute_force_padded(q, k, v, off, kw):
                     if kw["causal"] and j > i:
                         ok = False
                     if mask is not None and not mask[b, i // 128, j // 128]:
+                        ok = False
+                    if kw.get("window") is not None and not _in_band(i, j, kw["window"]):
                         ok = False
                     if ok:
                         s = kw["scale"] * sum(qpad[b, i, h, d] * kpad[b, j, h, d] for d in range(D))
@@ -349,3 +360,106 @@ def test_empty_row_reading():
     dq, dk, dv, _ = A.backward(q, k, v, do, off, **kw)
     dq1, _, _, _ = A.backward(q, k, v, do, off, seqs=[1], **kw)
     np.testing.assert_array_equal(dq, dq1)
+
+
+# ---------------------------------------------------------------- sliding window
+
+WINDOWS = [(2, 1), (3, 0), (0, 0), (None, 2), (4, None), (0, 5)]
+
+
+@pytest.mark.parametrize("window", WINDOWS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_matches_padded_brute_force(window, causal):
+    q, k, v, do, off, kw = _small(False, causal, lengths=(5, 1, 9, 3, 0), D=4, window=window)
+    o, lse = A.forward(q, k, v, off, **kw)
+    ob, lseb, _ = _brute_force_padded(q, k, v, off, kw)
+    for b, q0, q1, o0, _, _ in _seq_iter(off, kw["q_offsets"], q.shape[0], False):
+        n = q1 - q0
+        np.testing.assert_allclose(o[o0:o0 + n], ob[b, :n], atol=1e-13)
+        np.testing.assert_allclose(lse[:, o0:o0 + n].T, lseb[b, :n], atol=1e-13)
+
+
+def test_window_zero_width_is_the_diagonal():
+    """Window (0, 0): row i sees key i alone, so O_i = v_i and LSE_i = s_ii
+    exactly, and dV_i = dO_i, dK_i = 0."""
+    q, k, v, do, off, kw = _small(False, lengths=(4, 7, 1), H=2, D=8, window=(0, 0))
+    o, lse = A.forward(q, k, v, off, **kw)
+    np.testing.assert_array_equal(o, v)
+    np.testing.assert_allclose(lse.T, kw["scale"] * np.einsum("ihd,ihd->ih", q, k), atol=1e-14)
+    dq, dk, dv, _ = A.backward(q, k, v, do, off, **kw)
+    np.testing.assert_allclose(dv, do, atol=1e-14)
+    np.testing.assert_allclose(dk, 0.0, atol=1e-14)
+    np.testing.assert_allclose(dq, 0.0, atol=1e-14)
+
+
+def test_window_limits_reduce_to_dense_and_causal():
+    q, k, v, do, off, kw = _small(False, lengths=(6, 9, 2), H=1, D=8, seed=3)
+    dense = A.forward(q, k, v, off, **kw)
+    causal = A.forward(q, k, v, off, **dict(kw, causal=True))
+    for win, ref in (((None, None), dense), ((100, 100), dense), ((None, 0), causal),
+                     ((100, 0), causal)):
+        got = A.forward(q, k, v, off, **dict(kw, window=win))
+        np.testing.assert_array_equal(got[0], ref[0])
+        np.testing.assert_array_equal(got[1], ref[1])
+
+
+@pytest.mark.parametrize("window", [(3, 1), (5, 0)])
+def test_window_zero_q_gives_band_mean(window):
+    q, k, v, do, off, kw = _small(False, lengths=(7, 2, 10), window=window)
+    q[:] = 0.0
+    o, lse = A.forward(q, k, v, off, **kw)
+    left, right = window
+    for b in range(3):
+        k0, k1 = off[b], off[b + 1]
+        for i in range(k1 - k0):
+            lo, hi = max(0, i - left), min(k1 - k0 - 1, i + right)
+            np.testing.assert_allclose(o[k0 + i], v[k0 + lo:k0 + hi + 1].mean(axis=0), atol=1e-14)
+            np.testing.assert_allclose(lse[:, k0 + i], math.log(hi - lo + 1), atol=1e-14)
+
+
+def test_window_matches_torch_float64_and_autograd():
+    """Band mask built here from index arithmetic, fed to torch SDPA."""
+    window = (6, 2)
+    q, k, v, do, off, kw = _small(False, lengths=(17, 1, 40, 33, 8), H=3, D=16, window=window)
+    o, _ = A.forward(q, k, v, off, **kw)
+    dq, dk, dv, _ = A.backward(q, k, v, do, off, **kw)
+    qt = torch.tensor(q, requires_grad=True)
+    kt = torch.tensor(k, requires_grad=True)
+    vt = torch.tensor(v, requires_grad=True)
+    outs = []
+    for b in range(len(off) - 1):
+        s0, s1 = int(off[b]), int(off[b + 1])
+        n = s1 - s0
+        i = torch.arange(n)[:, None]
+        j = torch.arange(n)[None, :]
+        band = (j >= i - window[0]) & (j <= i + window[1])
+        ob = torch.nn.functional.scaled_dot_product_attention(
+            qt[s0:s1].transpose(0, 1), kt[s0:s1].transpose(0, 1), vt[s0:s1].transpose(0, 1),
+            attn_mask=band, scale=kw["scale"])
+        outs.append(ob.transpose(0, 1))
+    ot = torch.cat(outs, dim=0)
+    (ot * torch.tensor(do)).sum().backward()
+    np.testing.assert_allclose(o, ot.detach().numpy(), atol=1e-12)
+    np.testing.assert_allclose(dq, qt.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(dv, vt.grad.numpy(), atol=1e-11)
+
+
+@pytest.mark.parametrize("window,causal", [((2, 1), False), ((1, None), True)])
+def test_window_finite_differences(window, causal):
+    q, k, v, do, off, kw = _small(False, causal, lengths=(3, 6), H=1, D=4, seed=13,
+                                  window=window)
+    grads = dict(zip(("q", "k", "v"), A.backward(q, k, v, do, off, **kw)[:3]))
+    eps = 1e-6
+    for name, arr in (("q", q), ("k", k), ("v", v)):
+        flat = arr.reshape(-1)
+        g = grads[name].reshape(-1)
+        scale = max(1.0, np.abs(g).max())
+        for t in range(flat.size):
+            keep = flat[t]
+            flat[t] = keep + eps
+            lp = _loss(q, k, v, do, off, kw)
+            flat[t] = keep - eps
+            lm = _loss(q, k, v, do, off, kw)
+            flat[t] = keep
+            assert abs((lp - lm) / (2 * eps) - g[t]) <= 1e-6 * scale, (name, t)

@@ -154,3 +154,31 @@ def test_cpp_dynamic_plan_only_for_forward():
         with pytest.raises(J.JfaError) as e:
             J.jfa_plan_build(prob, None, [0, 3, 5], None, p | J.JFA_PLAN_DYNAMIC, 4)
         assert e.value.status == J.JFA_ERR_INVALID_ARG
+
+
+def test_cpp_band_plans_equal_oracle():
+    """Sliding-window problems: C++ FWD, BWD and DQ plans equal the oracle's."""
+    rng = np.random.default_rng(7)
+    for trial in range(30):
+        B = int(rng.integers(1, 6))
+        lens = rng.integers(0, 1500, size=B).astype(np.int32)
+        off = W.offsets_of(lens)
+        causal = bool(trial % 3 == 0)
+        wl = int(rng.integers(-1, 700))
+        wr = -1 if causal else int(rng.integers(-1, 400))
+        if wl < 0 and wr < 0 and not causal:
+            wl = 5
+        prob = J.Problem(B, 2, 128, False, causal=causal, softmax_scale=0.1,
+                         window_left=wl, window_right=wr)
+        window = (None if wl < 0 else wl, None if wr < 0 else wr)
+        W_ = int(rng.integers(1, 40))
+        for pass_, bm, bn in ((0, FWD_BM, FWD_BN), (1, BWD_BM, BWD_BN)):
+            hp = J.jfa_plan_build(prob, off, off, None, pass_, W_)
+            wp, tiles = OP.plan(lens, lens, 2, W_, pass_, block_m=bm, block_n=bn, causal=causal,
+                                window=window)
+            assert np.array_equal(hp.worker_ptr, wp), (trial, pass_)
+            assert np.array_equal(hp.tiles, tiles), (trial, pass_)
+        hp = J.jfa_plan_build(prob, off, off, None, J.JFA_PASS_DQ, W_)
+        wp, tiles = OP.plan_dq(lens, lens, 2, W_, broadcast_q=False, block_m=FWD_BM,
+                               block_n=FWD_BN, causal=causal, window=window)
+        assert np.array_equal(hp.tiles, tiles), (trial, "dq")

@@ -13,15 +13,15 @@ from oracle import attention as A
 from oracle import planner as P
 
 
-def _brute_work(pass_, b, t, lq_b, lk_b, bm, bn, causal, mask):
+def _brute_work(pass_, b, t, lq_b, lk_b, bm, bn, causal, mask, window=None):
     mask_b = None if mask is None else mask[b]
     if pass_ == P.FWD:
         rows = np.arange(t * bm, min((t + 1) * bm, lq_b))
-        vis = A.visibility(lq_b, lk_b, causal=causal, mask_b=mask_b, rows=rows)
+        vis = A.visibility(lq_b, lk_b, causal=causal, mask_b=mask_b, rows=rows, window=window)
         cols = np.nonzero(vis.any(axis=0))[0]
         return len(set(int(j) // bn for j in cols))
     keys = np.arange(t * bn, min((t + 1) * bn, lk_b))
-    vis = A.visibility(lq_b, lk_b, causal=causal, mask_b=mask_b)[:, keys]
+    vis = A.visibility(lq_b, lk_b, causal=causal, mask_b=mask_b, window=window)[:, keys]
     rows = np.nonzero(vis.any(axis=1))[0]
     return len(set(int(i) // bm for i in rows))
 
@@ -243,3 +243,22 @@ def test_dq_plan_per_sequence_is_forward_plan():
     a = P.plan_dq(lens, lens, 2, 3, broadcast_q=False, block_m=256, block_n=64, causal=True)
     b = P.plan(lens, lens, 2, 3, P.FWD, block_m=256, block_n=64, causal=True)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("window,causal", [((100, 30), False), ((0, 0), False), ((700, None), False),
+                                           ((None, 300), False), ((257, None), True),
+                                           ((31, 33), False)])
+@pytest.mark.parametrize("pass_,bm,bn", [(P.FWD, 256, 64), (P.BWD, 32, 256)])
+def test_band_plan_work_by_brute_force(window, causal, pass_, bm, bn):
+    """Sliding-window (band) work: the blocks holding a visible pair, counted
+    from the visibility rule itself, for every tile."""
+    rng = np.random.default_rng(3)
+    lens = list(rng.integers(1, 900, size=7)) + [1, 256, 257]
+    wp, tiles = P.plan(lens, lens, 2, 5, pass_, block_m=bm, block_n=bn, causal=causal,
+                       window=window)
+    got = {(int(r[0]), int(r[1]), int(r[2])): int(r[3]) for r in tiles}
+    for b, L in enumerate(lens):
+        n_t = P.cdiv(L, bm) if pass_ == P.FWD else P.cdiv(L, bn)
+        for t in range(n_t):
+            w = _brute_work(pass_, b, t, L, L, bm, bn, causal, None, window=window)
+            assert got[(b, 0, t)] == w, (b, t)

@@ -48,6 +48,7 @@ class Workload:
     seed: int
     mask_seed: Optional[int] = None   # block-sparse when not None
     input_seed: Optional[int] = None  # draw Q/K/V/dO from another workload's seed
+    window: Optional[tuple] = None    # sliding window (left, right), None = unbounded side
 
     @property
     def scale(self) -> float:
@@ -62,6 +63,10 @@ WORKLOADS = {
     4: Workload("dense-causal-4096", 8, 16, 128, False, 0, True, "const:4096", seed=4),
     5: Workload("block-sparse-broadcast-q", 256, 4, 128, True, 256, False,
                 "lognormal:%r:1.0:16:4096" % math.log(512.0), seed=2, mask_seed=5),
+    # sliding-window variant of the jagged self-attention shape: causal with a
+    # 1024-key window (row i sees keys i-1023 .. i)
+    6: Workload("jagged-sliding-window", 64, 8, 128, False, 0, True, "uniform:128:8192", seed=6,
+                window=(1023, None)),
 }
 
 
