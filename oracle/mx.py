@@ -1,0 +1,150 @@
+"""MXFP8 (microscaling FP8) encoding -- oracle (test infrastructure only).
+
+The pages describe an MXFP8 version of the kernel: its matrix products run in
+microscaling precision, with P quantised to FP8 on the fly ([radar] section
+"The turning point"). They give no block size, element or scale format. The
+plainest reading is the OCP Microscaling (MX) format MXFP8: FP8 E4M3 elements
+(OCP encoding: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+infinities, 0x7F / 0xFF are NaN, largest finite 448) sharing one E8M0 scale
+(a power of two 2^(c-127), code c in 0..254) per block of 32 consecutive
+elements along the contraction dimension of each product. A block x_1..x_32
+is encoded as
+
+  e     = floor(log2(max_i |x_i|)) - 8      (8: exponent of E4M3's largest
+                                             power of two; clamped to
+                                             [-127, 127]; an all-zero block
+                                             takes -127)
+  q_i   = E4M3(x_i / 2^e)                    (round to nearest, ties to even,
+                                             magnitudes above 448 clamped)
+
+and decodes to q_i * 2^e. The blocks run along d for Q and K (the d of
+S = Q K^T), and along the keys of each sequence for V (the keys of O = P V):
+32 consecutive keys of one sequence, the last block of a sequence possibly
+shorter, never spanning two sequences.
+
+Layouts (uint8): Q codes [rows, H, D], Q scales [H, rows, D/32]; K likewise;
+V codes [T_k, H, D], V scales [H, NB, D] with NB = sum_b ceil(L_b / 32), the
+blocks of sequence b starting at mx_block_offsets(kv_offsets)[b].
+
+The attention the MXFP8 variant computes is then softmax attention on the
+decoded Q, K, V (``oracle.attention`` on the decoded tensors). P's own FP8
+quantisation happens inside the kernel, in whichever order its online softmax
+visits the keys; the oracle keeps P exact and the tests bound the difference
+(every P element is rounded to E4M3 with a relative error of at most 2^-4,
+or, below E4M3's normal range, an absolute error of at most 2^-18).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 32
+E4M3_MAX = 448.0
+E4M3_EMAX = 8        # exponent of the largest power of two E4M3 holds
+E8M0_BIAS = 127
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """float64 values of E4M3 codes (NaN for 0x7F and 0xFF)."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    out = sign * mag
+    return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+def e4m3_encode(y) -> np.ndarray:
+    """E4M3 codes of float64 values: magnitudes above 448 are clamped to 448,
+    the rest rounded to the nearest E4M3 value, ties to the even mantissa."""
+    y = np.asarray(y, dtype=np.float64)
+    neg = np.signbit(y)
+    a = np.minimum(np.abs(y), E4M3_MAX)
+    # spacing of E4M3 values around a: 2^(e-3) for a in [2^e, 2^(e+1)), e >= -6;
+    # 2^-9 in the subnormal range below 2^-6
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))          # a = f * 2^ex, f in [0.5, 1)
+    e = np.maximum(ex - 1, -6)
+    step = np.ldexp(1.0, e - 3)
+    q = np.rint(a / step) * step                        # exact: a is a short binary fraction
+    q = np.where(a > 0, q, 0.0)
+    # back to fields: q is on the E4M3 grid (rounding up may reach 2^(e+1))
+    _, qx = np.frexp(np.where(q > 0, q, 1.0))
+    qe = qx - 1
+    normal = (q >= 2.0 ** -6)
+    exp_field = np.where(normal, qe + 7, 0)
+    man = np.where(normal, q / np.ldexp(1.0, qe) - 1.0, q / 2.0 ** -6) * 8.0
+    man = np.rint(man).astype(np.int64)
+    code = (exp_field.astype(np.int64) << 3) | man
+    code = np.where(q > 0, code, 0)
+    return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def block_exponent(amax) -> np.ndarray:
+    """Shared exponent e of a block with largest magnitude amax (see above)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))   # floor(log2(amax)) = ex - 1
+    e = np.where(amax > 0, ex - 1 - E4M3_EMAX, -E8M0_BIAS)
+    return np.clip(e, -E8M0_BIAS, E8M0_BIAS).astype(np.int64)
+
+
+def _encode_blocks(x):
+    """x [..., 32] -> (codes [..., 32], scale codes [...])."""
+    e = block_exponent(np.abs(x).max(axis=-1))
+    codes = e4m3_encode(np.ldexp(x, -e[..., None]))
+    return codes, (e + E8M0_BIAS).astype(np.uint8)
+
+
+def quantize_rows(x):
+    """Q or K [rows, H, D] (D a multiple of 32) -> codes [rows, H, D], scales
+    [H, rows, D/32]: one block per 32 consecutive d of a (row, head)."""
+    x = np.asarray(x, dtype=np.float64)
+    rows, H, D = x.shape
+    codes, sc = _encode_blocks(x.reshape(rows, H, D // BLOCK, BLOCK))
+    return codes.reshape(rows, H, D), np.ascontiguousarray(sc.transpose(1, 0, 2))
+
+
+def dequantize_rows(codes, scales):
+    rows, H, D = codes.shape
+    s = np.ldexp(1.0, scales.astype(np.int64) - E8M0_BIAS)             # [H, rows, D/32]
+    s = np.repeat(s.transpose(1, 0, 2), BLOCK, axis=2)                  # [rows, H, D]
+    return e4m3_decode(codes) * s
+
+
+def mx_block_offsets(kv_offsets) -> np.ndarray:
+    """First V scale block of each sequence: prefix sums of ceil(L_b / 32)."""
+    lens = np.diff(np.asarray(kv_offsets, dtype=np.int64))
+    out = np.zeros(len(lens) + 1, dtype=np.int64)
+    out[1:] = np.cumsum(-(-lens // BLOCK))
+    return out.astype(np.int32)
+
+
+def quantize_v(v, kv_offsets):
+    """V [T_k, H, D] -> codes [T_k, H, D], scales [H, NB, D]: one block per 32
+    consecutive keys of a sequence (the last one possibly shorter) per (head, d)."""
+    v = np.asarray(v, dtype=np.float64)
+    T, H, D = v.shape
+    boff = mx_block_offsets(kv_offsets)
+    codes = np.zeros((T, H, D), dtype=np.uint8)
+    scales = np.zeros((H, int(boff[-1]), D), dtype=np.uint8)
+    for b in range(len(kv_offsets) - 1):
+        k0, k1 = int(kv_offsets[b]), int(kv_offsets[b + 1])
+        for j, s0 in enumerate(range(k0, k1, BLOCK)):
+            s1 = min(s0 + BLOCK, k1)
+            blk = v[s0:s1]                                   # [n, H, D]
+            e = block_exponent(np.abs(blk).max(axis=0))      # [H, D]
+            codes[s0:s1] = e4m3_encode(np.ldexp(blk, -e[None]))
+            scales[:, boff[b] + j, :] = (e + E8M0_BIAS).astype(np.uint8)
+    return codes, scales
+
+
+def dequantize_v(codes, scales, kv_offsets):
+    T, H, D = codes.shape
+    boff = mx_block_offsets(kv_offsets)
+    out = e4m3_decode(codes)
+    for b in range(len(kv_offsets) - 1):
+        k0, k1 = int(kv_offsets[b]), int(kv_offsets[b + 1])
+        for j, s0 in enumerate(range(k0, k1, BLOCK)):
+            s1 = min(s0 + BLOCK, k1)
+            s = np.ldexp(1.0, scales[:, boff[b] + j, :].astype(np.int64) - E8M0_BIAS)   # [H, D]
+            out[s0:s1] *= s[None]
+    return out
