@@ -23,6 +23,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 METRIC = "JFA fwd+bwd TFLOP/s (bf16) and % of MFMA peak, jagged broadcast-Q"
 
 
@@ -164,6 +165,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2, help="1..6 (2: GEM-shaped broadcast-Q; 6: sliding window)")
     ap.add_argument("--fwd-workers-per-cu", type=int, default=1)
     ap.add_argument("--bwd-workers-per-cu", type=int, default=1)
+    ap.add_argument("--mx", type=int, default=1,
+                    help="also time the MXFP8 forward on the same inputs (head_dim 128; 0: skip)")
     ap.add_argument("--fwd-plan", choices=("dynamic", "static"), default="dynamic",
                     help="forward tiles claimed at run time from the sorted list, or the "
                          "static snake deal")
@@ -244,6 +247,25 @@ def main():
     names = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq", "bwd_dq_reduce")
     per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in events])) for j, n in enumerate(names)}
 
+    # the MXFP8 forward of the same problem (inputs encoded once, outside the
+    # timed loop; same plan), timed alone with HIP events
+    mx = None
+    if args.mx and D == 128:
+        mxq = att.quantize_mx(q, k, v)
+        for _ in range(args.warmup):
+            att.forward_mx(mxq, o, lse)
+        torch.cuda.synchronize()
+        mev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for e0, e1 in mev:
+            e0.record()
+            att.forward_mx(mxq, o, lse)
+            e1.record()
+        torch.cuda.synchronize()
+        mx_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in mev]))
+        mx = {"fwd_ms": mx_ms, "fwd_tflops": model["fwd_flop"] / (mx_ms * 1e-3) / 1e12,
+              "pct_fp8_peak": 100.0 * model["fwd_flop"] / (mx_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS}
+
     flop = model["fwd_flop"] + model["bwd_flop"]
     value = flop / (ms_step * 1e-3) / 1e12
     wl_name = w.name
@@ -303,6 +325,8 @@ def main():
         "plan_host_ms": plan_ms,
         "roofline": roof,
     }
+    if mx is not None:
+        res["mxfp8_forward"] = mx
     if args.cpu_budget > 0:
         res["cpu_baseline"] = cpu_baseline(x, args.cpu_budget)
     print(json.dumps(res))

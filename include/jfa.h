@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define JFA_ABI_VERSION 4
+#define JFA_ABI_VERSION 5
 
 /* status codes */
 #define JFA_OK                 0
@@ -219,6 +219,50 @@ int32_t jfa_fwd(const jfa_problem* prob, const jfa_plan_info* info,
                 const int32_t* d_q_offsets, const int32_t* d_kv_offsets,
                 const void* q, const void* k, const void* v,
                 void* o, float* lse, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * MXFP8 variant ("TLX porta l'attenzione jagged su Blackwell" (ai-radar.it),
+ * section "The turning point": products in microscaling precision, P
+ * quantised to FP8 on the fly). Format: OCP MXFP8 -- E4M3 element codes
+ * (uint8) sharing one E8M0 scale code c (value 2^(c-127), uint8) per block of
+ * 32 elements along the contraction dimension of each product: d for Q and
+ * K, 32 consecutive keys of one sequence for V (a sequence's last block may
+ * be shorter; blocks never span two sequences). A block's exponent is
+ * floor(log2(max |x|)) - 8 (clamped to [-127, 127]; 0 blocks: -127); its
+ * elements are x / 2^e rounded to nearest even, magnitudes above 448
+ * clamped. Layouts: Q codes [q rows, H, D] with scales [H, q rows, D/32]
+ * (q rows = lq when broadcast, else T_q); K codes [T_k, H, D] with scales
+ * [H, T_k, D/32]; V codes [T_k, H, D] with scales [H, NB, D], the blocks of
+ * sequence b starting at block_offsets[b] and NB = block_offsets[B].
+ */
+/* block_offsets[0] = 0, block_offsets[b+1] = block_offsets[b] + ceil(L_b/32)
+ * for the lengths given by h_kv_offsets [B+1] (host arrays). */
+int32_t jfa_mx_block_offsets(const int32_t* h_kv_offsets, int32_t batch, int32_t* h_block_offsets);
+/* Encode a bf16 [rows, num_heads, head_dim] tensor (Q or K; head_dim a
+ * multiple of 32) into codes [rows, H, D] and scales [H, rows, D/32]. */
+int32_t jfa_mx_quantize_rows(const void* src, int64_t rows, int32_t num_heads, int32_t head_dim,
+                             void* codes, void* scales, void* stream);
+/* Encode bf16 V [T_k, H, D] into codes [T_k, H, D] and scales [H, NB, D];
+ * d_kv_offsets / d_block_offsets are device copies ([B+1]). */
+int32_t jfa_mx_quantize_v(const void* v, const int32_t* d_kv_offsets,
+                          const int32_t* d_block_offsets, int32_t batch, int32_t num_heads,
+                          int32_t head_dim, int32_t num_blocks, void* codes, void* scales,
+                          void* stream);
+/*
+ * MXFP8 forward: O (bf16) and LSE (fp32) as jfa_fwd, from MXFP8 Q, K, V
+ * (head_dim 128; same plans, modes and workspace as jfa_fwd). S = Q K^T and
+ * O = P V run as block-scaled FP8 products with fp32 accumulation; the
+ * softmax is fp32, and P = exp(S - running max) <= 1 is rounded to E4M3 with
+ * the fixed block scale 2^-8 before O = P V (its row sum stays fp32).
+ */
+int32_t jfa_fwd_mx(const jfa_problem* prob, const jfa_plan_info* info,
+                   const int32_t* d_worker_ptr, const int32_t* d_tiles,
+                   const int32_t* d_sparse_ptr, const int32_t* d_sparse_idx,
+                   const int32_t* d_q_offsets, const int32_t* d_kv_offsets,
+                   const int32_t* d_block_offsets, int32_t num_blocks,
+                   const void* q_codes, const void* q_scales, const void* k_codes,
+                   const void* k_scales, const void* v_codes, const void* v_scales,
+                   void* o, float* lse, void* workspace, int64_t workspace_bytes, void* stream);
 
 /* A plan on the device: the sizes of jfa_plan_build's output and device
  * copies of its arrays (sparse_ptr / sparse_idx NULL when dense). The caller

@@ -33,7 +33,8 @@ JFA_PLAN_DYNAMIC = 16
 EXPORTS = (
     "jfa_abi_version", "jfa_status_string", "jfa_last_hip_error", "jfa_device_workers",
     "jfa_offsets_from_lengths", "jfa_plan_query", "jfa_plan_build", "jfa_fwd_workspace_bytes",
-    "jfa_fwd", "jfa_bwd_workspace_bytes", "jfa_bwd", "jfa_bwd_stages",
+    "jfa_fwd", "jfa_bwd_workspace_bytes", "jfa_bwd", "jfa_bwd_stages", "jfa_mx_block_offsets",
+    "jfa_mx_quantize_rows", "jfa_mx_quantize_v", "jfa_fwd_mx",
 )
 JFA_BWD_PREPROCESS = 1
 JFA_BWD_DKDV = 2
@@ -104,6 +105,10 @@ def _lib():
             "jfa_bwd_workspace_bytes": (i32, [prob, info, ctypes.POINTER(i64)]),
             "jfa_bwd": (i32, [prob, dplan, dplan] + [_P] * 14 + [i64, _P]),
             "jfa_bwd_stages": (i32, [i32, prob, dplan, dplan] + [_P] * 14 + [i64, _P]),
+            "jfa_mx_block_offsets": (i32, [_P, i32, _P]),
+            "jfa_mx_quantize_rows": (i32, [_P, i64, i32, i32, _P, _P, _P]),
+            "jfa_mx_quantize_v": (i32, [_P, _P, _P, i32, i32, i32, i32, _P, _P, _P]),
+            "jfa_fwd_mx": (i32, [prob, info] + [_P] * 7 + [i32] + [_P] * 9 + [i64, _P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -298,6 +303,46 @@ def jfa_bwd_stages(stages: int, prob: Problem, kv_plan: DevicePlan, dq_plan: Dev
                                  int(workspace_bytes), _stream(stream)), "jfa_bwd_stages")
 
 
+# ------------------------------------------------------------------ MXFP8
+
+def jfa_mx_block_offsets(kv_offsets) -> np.ndarray:
+    """First V scale block of each sequence (prefix sums of ceil(L_b / 32))."""
+    ko = _i32(kv_offsets)
+    out = np.zeros(len(ko), dtype=np.int32)
+    _check(_lib().jfa_mx_block_offsets(_np_ptr(ko), len(ko) - 1, _np_ptr(out)),
+           "jfa_mx_block_offsets")
+    return out
+
+
+def jfa_mx_quantize_rows(src, codes, scales, stream=None) -> None:
+    """bf16 [rows, H, D] -> E4M3 codes [rows, H, D] (uint8) and scales [H, rows, D/32]."""
+    rows, H, D = src.shape
+    _check(_lib().jfa_mx_quantize_rows(_dev_ptr(src), rows, H, D, _dev_ptr(codes), _dev_ptr(scales),
+                                       _stream(stream)), "jfa_mx_quantize_rows")
+
+
+def jfa_mx_quantize_v(v, kv_offsets, block_offsets, num_blocks, codes, scales, stream=None) -> None:
+    """bf16 V [T_k, H, D] -> codes [T_k, H, D] and scales [H, NB, D] (device offsets)."""
+    _, H, D = v.shape
+    _check(_lib().jfa_mx_quantize_v(_dev_ptr(v), _dev_ptr(kv_offsets), _dev_ptr(block_offsets),
+                                    kv_offsets.numel() - 1, H, D, int(num_blocks), _dev_ptr(codes),
+                                    _dev_ptr(scales), _stream(stream)), "jfa_mx_quantize_v")
+
+
+def jfa_fwd_mx(prob: Problem, plan: DevicePlan, q_offsets, kv_offsets, block_offsets, num_blocks,
+               qc, qs, kc, ks, vc, vs, o, lse, workspace=None, workspace_bytes: int = 0,
+               stream=None) -> None:
+    """Enqueue the MXFP8 forward (codes / scales as produced by the quantizers)."""
+    cp = prob.c()
+    _check(_lib().jfa_fwd_mx(ctypes.byref(cp), ctypes.byref(plan.info), _dev_ptr(plan.worker_ptr),
+                             _dev_ptr(plan.tiles), _dev_ptr(plan.sparse_ptr),
+                             _dev_ptr(plan.sparse_idx), _dev_ptr(q_offsets), _dev_ptr(kv_offsets),
+                             _dev_ptr(block_offsets), int(num_blocks), _dev_ptr(qc), _dev_ptr(qs),
+                             _dev_ptr(kc), _dev_ptr(ks), _dev_ptr(vc), _dev_ptr(vs), _dev_ptr(o),
+                             _dev_ptr(lse), _dev_ptr(workspace), int(workspace_bytes),
+                             _stream(stream)), "jfa_fwd_mx")
+
+
 # ------------------------------------------------------- convenience wrappers
 
 def default_workers(device: int = 0, per_cu: int = 1) -> int:
@@ -351,6 +396,38 @@ class JaggedAttention:
             lse = torch.empty((H, self.total_q), dtype=torch.float32, device=self.device)
         jfa_fwd(self.prob, self.fwd_plan, self.q_offsets, self.kv_offsets, q, k, v, o, lse,
                 self.fwd_workspace, self.fwd_ws_bytes)
+        return o, lse
+
+    def quantize_mx(self, q, k, v):
+        """MXFP8 encodings of bf16 q, k, v (device tensors) for forward_mx."""
+        import torch
+        if not hasattr(self, "v_block_offsets"):
+            boff = jfa_mx_block_offsets(self.kv_offsets.cpu().numpy())
+            self.v_num_blocks = int(boff[-1])
+            self.v_block_offsets = torch.from_numpy(boff).to(self.device)
+        H, D = self.prob.num_heads, self.prob.head_dim
+        u8 = dict(dtype=torch.uint8, device=self.device)
+        mxq = dict(qc=torch.empty(q.shape, **u8), qs=torch.empty((H, q.shape[0], D // 32), **u8),
+                   kc=torch.empty(k.shape, **u8), ks=torch.empty((H, k.shape[0], D // 32), **u8),
+                   vc=torch.empty(v.shape, **u8),
+                   vs=torch.empty((H, max(self.v_num_blocks, 1), D), **u8))
+        jfa_mx_quantize_rows(q, mxq["qc"], mxq["qs"])
+        jfa_mx_quantize_rows(k, mxq["kc"], mxq["ks"])
+        jfa_mx_quantize_v(v, self.kv_offsets, self.v_block_offsets, self.v_num_blocks, mxq["vc"],
+                          mxq["vs"])
+        return mxq
+
+    def forward_mx(self, mxq, o=None, lse=None):
+        """The MXFP8 forward on encodings from quantize_mx."""
+        import torch
+        H, D = self.prob.num_heads, self.prob.head_dim
+        if o is None:
+            o = torch.empty((self.total_q, H, D), dtype=torch.bfloat16, device=self.device)
+        if lse is None:
+            lse = torch.empty((H, self.total_q), dtype=torch.float32, device=self.device)
+        jfa_fwd_mx(self.prob, self.fwd_plan, self.q_offsets, self.kv_offsets, self.v_block_offsets,
+                   self.v_num_blocks, mxq["qc"], mxq["qs"], mxq["kc"], mxq["ks"], mxq["vc"],
+                   mxq["vs"], o, lse, self.fwd_workspace, self.fwd_ws_bytes)
         return o, lse
 
     def backward(self, q, k, v, o, lse, d_o, out=None, stages=JFA_BWD_ALL):

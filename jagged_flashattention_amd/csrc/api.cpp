@@ -115,11 +115,16 @@ int32_t jfa_fwd_workspace_bytes(const jfa_problem* prob, const jfa_plan_info* in
     return JFA_OK;
 }
 
-int32_t jfa_fwd(const jfa_problem* prob, const jfa_plan_info* info, const int32_t* d_worker_ptr,
-                const int32_t* d_tiles, const int32_t* d_sparse_ptr, const int32_t* d_sparse_idx,
-                const int32_t* d_q_offsets, const int32_t* d_kv_offsets, const void* q,
-                const void* k, const void* v, void* o, float* lse, void* workspace,
-                int64_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+// Validation and argument set-up shared by jfa_fwd and jfa_fwd_mx; returns
+// JFA_OK with *launch = false when there is nothing to do.
+static int32_t fwd_args(const jfa_problem* prob, const jfa_plan_info* info, const int32_t* d_worker_ptr,
+                        const int32_t* d_tiles, const int32_t* d_sparse_ptr,
+                        const int32_t* d_sparse_idx, const int32_t* d_q_offsets,
+                        const int32_t* d_kv_offsets, void* o, float* lse, void* workspace,
+                        int64_t workspace_bytes, jfa::FwdArgs& a, bool* launch) {
+    *launch = false;
     int32_t st = check_common(prob, info, JFA_PASS_FWD, d_worker_ptr, d_tiles, d_sparse_ptr,
                               d_sparse_idx, d_q_offsets, d_kv_offsets);
     if (st) return st;
@@ -130,22 +135,15 @@ int32_t jfa_fwd(const jfa_problem* prob, const jfa_plan_info* info, const int32_
         return JFA_ERR_WORKSPACE;
     if (info->num_tiles == 0) return JFA_OK;  // no output row exists
     const int64_t hd = (int64_t)prob->num_heads * prob->head_dim;
-    const int64_t q_rows = prob->broadcast_q ? prob->lq : info->total_q;
-    if (!tensor_ok(q, q_rows * hd) || !tensor_ok(k, info->total_kv * hd) ||
-        !tensor_ok(v, info->total_kv * hd) || !tensor_ok(o, (int64_t)info->total_q * hd))
-        return JFA_ERR_INVALID_ARG;
+    if (!tensor_ok(o, (int64_t)info->total_q * hd)) return JFA_ERR_INVALID_ARG;
     if (lse == nullptr || !aligned4(lse)) return JFA_ERR_INVALID_ARG;
-
-    jfa::FwdArgs a;
+    a = jfa::FwdArgs{};
     a.worker_ptr = d_worker_ptr;
     a.tiles = d_tiles;
     a.sp_ptr = d_sparse_ptr;
     a.sp_idx = d_sparse_idx;
     a.q_off = prob->broadcast_q ? nullptr : d_q_offsets;
     a.kv_off = d_kv_offsets;
-    a.q = static_cast<const uint16_t*>(q);
-    a.k = static_cast<const uint16_t*>(k);
-    a.v = static_cast<const uint16_t*>(v);
     a.o = static_cast<uint16_t*>(o);
     a.lse = lse;
     a.num_heads = prob->num_heads;
@@ -159,8 +157,106 @@ int32_t jfa_fwd(const jfa_problem* prob, const jfa_plan_info* info, const int32_
     a.win_right = bd.right;
     a.counter = need > 0 ? static_cast<int32_t*>(workspace) : nullptr;
     a.scale_log2 = prob->softmax_scale * 1.4426950408889634f;
+    a.q_rows = prob->broadcast_q ? prob->lq : info->total_q;
+    a.total_kv = info->total_kv;
+    *launch = true;
+    return JFA_OK;
+}
+
+extern "C" {
+
+int32_t jfa_fwd(const jfa_problem* prob, const jfa_plan_info* info, const int32_t* d_worker_ptr,
+                const int32_t* d_tiles, const int32_t* d_sparse_ptr, const int32_t* d_sparse_idx,
+                const int32_t* d_q_offsets, const int32_t* d_kv_offsets, const void* q,
+                const void* k, const void* v, void* o, float* lse, void* workspace,
+                int64_t workspace_bytes, void* stream) {
+    jfa::FwdArgs a;
+    bool launch = false;
+    int32_t st = fwd_args(prob, info, d_worker_ptr, d_tiles, d_sparse_ptr, d_sparse_idx, d_q_offsets,
+                          d_kv_offsets, o, lse, workspace, workspace_bytes, a, &launch);
+    if (st || !launch) return st;
+    const int64_t hd = (int64_t)prob->num_heads * prob->head_dim;
+    if (!tensor_ok(q, (int64_t)a.q_rows * hd) || !tensor_ok(k, info->total_kv * hd) ||
+        !tensor_ok(v, info->total_kv * hd))
+        return JFA_ERR_INVALID_ARG;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
     return hip_status(jfa::launch_fwd(a, prob->head_dim, mode_of(prob), prob->broadcast_q != 0,
                                       stream));
+}
+
+int32_t jfa_mx_block_offsets(const int32_t* h_kv_offsets, int32_t batch, int32_t* h_block_offsets) {
+    if (batch < 0 || h_kv_offsets == nullptr || h_block_offsets == nullptr) return JFA_ERR_INVALID_ARG;
+    int32_t st = jfa::check_offsets(h_kv_offsets, batch);
+    if (st) return st;
+    int64_t acc = 0;
+    h_block_offsets[0] = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+        acc += ((int64_t)h_kv_offsets[b + 1] - h_kv_offsets[b] + 31) / 32;
+        h_block_offsets[b + 1] = (int32_t)acc;
+    }
+    return JFA_OK;
+}
+
+int32_t jfa_mx_quantize_rows(const void* src, int64_t rows, int32_t num_heads, int32_t head_dim,
+                             void* codes, void* scales, void* stream) {
+    if (rows < 0 || num_heads < 1 || head_dim < 32 || head_dim % 32 != 0) return JFA_ERR_INVALID_ARG;
+    const int64_t n = rows * num_heads * head_dim;
+    if (n > 0 && (src == nullptr || codes == nullptr || scales == nullptr || !aligned16(src) ||
+                  !aligned16(codes)))
+        return JFA_ERR_INVALID_ARG;
+    return hip_status(jfa::launch_mx_quant_rows(static_cast<const uint16_t*>(src), rows, num_heads,
+                                                head_dim, static_cast<uint8_t*>(codes),
+                                                static_cast<uint8_t*>(scales), stream));
+}
+
+int32_t jfa_mx_quantize_v(const void* v, const int32_t* d_kv_offsets, const int32_t* d_block_offsets,
+                          int32_t batch, int32_t num_heads, int32_t head_dim, int32_t num_blocks,
+                          void* codes, void* scales, void* stream) {
+    if (batch < 0 || num_heads < 1 || head_dim < 32 || head_dim > 128 || head_dim % 32 != 0 ||
+        num_blocks < 0)
+        return JFA_ERR_INVALID_ARG;
+    if (batch > 0 && (d_kv_offsets == nullptr || d_block_offsets == nullptr)) return JFA_ERR_INVALID_ARG;
+    if (num_blocks > 0 && (v == nullptr || codes == nullptr || scales == nullptr))
+        return JFA_ERR_INVALID_ARG;
+    return hip_status(jfa::launch_mx_quant_v(static_cast<const uint16_t*>(v), d_kv_offsets,
+                                             d_block_offsets, batch, num_heads, head_dim, num_blocks,
+                                             static_cast<uint8_t*>(codes),
+                                             static_cast<uint8_t*>(scales), stream));
+}
+
+int32_t jfa_fwd_mx(const jfa_problem* prob, const jfa_plan_info* info, const int32_t* d_worker_ptr,
+                   const int32_t* d_tiles, const int32_t* d_sparse_ptr, const int32_t* d_sparse_idx,
+                   const int32_t* d_q_offsets, const int32_t* d_kv_offsets,
+                   const int32_t* d_block_offsets, int32_t num_blocks, const void* q_codes,
+                   const void* q_scales, const void* k_codes, const void* k_scales,
+                   const void* v_codes, const void* v_scales, void* o, float* lse, void* workspace,
+                   int64_t workspace_bytes, void* stream) {
+    int32_t st = jfa::check_problem(prob);
+    if (st) return st;
+    if (prob->head_dim != 128) return JFA_ERR_UNSUPPORTED;
+    jfa::FwdArgs a;
+    bool launch = false;
+    st = fwd_args(prob, info, d_worker_ptr, d_tiles, d_sparse_ptr, d_sparse_idx, d_q_offsets,
+                  d_kv_offsets, o, lse, workspace, workspace_bytes, a, &launch);
+    if (st || !launch) return st;
+    // one 32-key V block per 32 keys of each sequence: at least T_k / 32
+    if (num_blocks < (info->total_kv + 31) / 32 || d_block_offsets == nullptr) return JFA_ERR_INVALID_ARG;
+    const int64_t hd = (int64_t)prob->num_heads * prob->head_dim;
+    if (!tensor_ok(q_codes, (int64_t)a.q_rows * hd) || !tensor_ok(k_codes, info->total_kv * hd) ||
+        !tensor_ok(v_codes, info->total_kv * hd) || q_scales == nullptr || k_scales == nullptr ||
+        v_scales == nullptr || !aligned4(q_scales) || !aligned4(k_scales) || !aligned4(v_scales))
+        return JFA_ERR_INVALID_ARG;
+    a.q8 = static_cast<const uint8_t*>(q_codes);
+    a.k8 = static_cast<const uint8_t*>(k_codes);
+    a.v8 = static_cast<const uint8_t*>(v_codes);
+    a.q_sc = static_cast<const uint8_t*>(q_scales);
+    a.k_sc = static_cast<const uint8_t*>(k_scales);
+    a.v_sc = static_cast<const uint8_t*>(v_scales);
+    a.v_boff = d_block_offsets;
+    a.v_nb = num_blocks;
+    return hip_status(jfa::launch_fwd_mx(a, mode_of(prob), prob->broadcast_q != 0, stream));
 }
 
 int32_t jfa_bwd_workspace_bytes(const jfa_problem* prob, const jfa_plan_info* dq_info,

@@ -15,6 +15,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -43,6 +45,24 @@ __device__ __forceinline__ bf16x8 concat(bf16x4 lo, bf16x4 hi) {
 }
 
 // Value of x in lane l^32 combined with x: both halves end up with the pair.
+// MXFP8 product: acc += (A * 2^(sa-127)) (B * 2^(sb-127)) with E4M3 operands
+// of 64 along the contraction. Lane l (row or column l%32, half h = l/32)
+// holds 32 bytes: bytes 0-15 are 16 contraction slots of scale block 0,
+// bytes 16-31 16 slots of block 1 (which slot is which element is free as
+// long as A and B agree), and its scale byte is that of block h of its row.
+__device__ __forceinline__ f32x16 mfma_mx(const i32x8& a, const i32x8& b, int sa, int sb, const f32x16& c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// Four fp32 values / scale as E4M3 codes packed in one dword (value i in
+// byte i; round to nearest even; callers keep |value / scale| <= 448).
+__device__ __forceinline__ uint32_t pack4_fp8(float x0, float x1, float x2, float x3, float scale) {
+    s16x2 w = {0, 0};
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, x0, x1, scale, false);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, x2, x3, scale, true);
+    return __builtin_bit_cast(uint32_t, w);
+}
+
 __device__ __forceinline__ float pair_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));

@@ -46,7 +46,7 @@ constexpr int kReadAhead = 4;    // LDS operand reads kept in flight ahead of th
 constexpr int kStageRows = 16;   // O rows per wave per epilogue round
 
 
-template <int D>
+template <int D, bool MX>
 struct FwdLds {
     static constexpr int BLK = kFwdBlockN * D * 2;            // one K or V block
     static constexpr int K = 0;                                // kKSlots natural K blocks
@@ -59,9 +59,128 @@ struct FwdLds {
     static_assert(4 * OST_WAVE == BLK, "staging: 4 waves per released block");
 };
 
-template <int D, int MODE, bool BCAST>
+// MXFP8 (D = 128): E4M3 K/V blocks are half the size; their scales ride
+// along (K: 4 bytes per key, V: 2 x 128 bytes per 64-key block); V^T is made
+// by a byte transposition in LDS; O has a staging area of its own.
+template <int D>
+struct FwdLds<D, true> {
+    static constexpr int BLK = kFwdBlockN * D;                 // one E4M3 K, V or V^T block
+    static constexpr int SC = 256;                              // its scales
+    static constexpr int K = 0;                                 // kKSlots K blocks [64][128]
+    static constexpr int KS = K + kKSlots * BLK;                // kKSlots K scales [64][4]
+    static constexpr int V = KS + kKSlots * SC;                 // kVSlots V blocks [64][128]
+    static constexpr int VS = V + kVSlots * BLK;                // kKSlots V scales [2][128]
+    static constexpr int VT = VS + kKSlots * SC;                // 2 V^T blocks [128][64]
+    static constexpr int OST_WAVE = kStageRows * D * 2;
+    static constexpr int OST = VT + 2 * BLK;                    // O staging, kWaves areas
+    static constexpr int CLAIM = OST + kWaves * OST_WAVE;
+    static constexpr int QUEUE = CLAIM + 2 * 64 * 4;
+    static constexpr int BYTES = QUEUE + kWaves * 8 * 4;
+    static_assert(D == 128 && BLK == 64 * kThreads / 4, "one 16-byte copy per thread per block");
+};
+
+// ---- MXFP8 operands (D = 128, two 64-wide steps j along d). A 16-byte chunk
+// c of key r of a K block sits at chunk c ^ ((r >> 1) & 7) (the 16 lanes of a
+// read pass, 16 keys, cover all banks); chunk c of row d of a V^T block at
+// c ^ ((d >> 2) & 3).
+__device__ __forceinline__ int swz_k8(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz_vt8(int d) { return (d >> 2) & 3; }
+constexpr int kP8Scale = 127 - 8;   // E8M0 code of P's block scale 2^-8
+
+// S^T = K Q^T of a block's two 32-key tiles. Lane (key 32mb + lr, half hf),
+// step j: bytes 0-15 hold d 64j + 16hf .. +15 (scale block 2j), bytes 16-31
+// d 64j + 32 + 16hf .. +15 (block 2j + 1); the Q fragment uses the same
+// slots, and the lane gives the scale of d block 2j + hf.
+__device__ __forceinline__ void mx_scores(f32x16 (&acc)[2], const char* kb, const char* ksb,
+                                          const i32x8 (&qf)[2], const int (&qsc)[2], int lr, int hf) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        const int r = 32 * mb + lr;
+        const char* row = kb + r * 128;
+        const uint32_t ks = *(const uint32_t*)(ksb + 4 * r);
+        acc[mb] = f32x16{};
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const u32x4 lo = *(const u32x4*)(row + 16 * ((4 * j + hf) ^ swz_k8(r)));
+            const u32x4 hi = *(const u32x4*)(row + 16 * ((4 * j + 2 + hf) ^ swz_k8(r)));
+            const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                              (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            acc[mb] = mfma_mx(av, qf[j], (ks >> (8 * (2 * j + hf))) & 255, qsc[j], acc[mb]);
+        }
+    }
+}
+
+// P^T (probabilities already exponentiated, at most 1) as the B operand of
+// O^T += V^T P^T over a 64-key block (scale block kb = key tile kb), each
+// value divided by P's fixed scale 2^-8 and rounded to E4M3. Accumulator
+// register r of lane half h holds key 8(r/4) + 4h + r%4: packed four at a
+// time (dword g: keys 8g + 4h .. +3) and regrouped across the halves with two
+// lane-half swaps, so that half h holds keys 16h .. 16h+15 of each tile, as
+// dwords of keys 0-3, 8-11, 4-7, 12-15 (relative to 16h).
+__device__ __forceinline__ i32x8 mx_pack_p(const f32x16 (&p)[2]) {
+    i32x8 out;
+    const float sc = 1.0f / 256.0f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        uint32_t d[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            d[g] = pack4_fp8(p[mb][4 * g], p[mb][4 * g + 1], p[mb][4 * g + 2], p[mb][4 * g + 3], sc);
+        const auto r02 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+        const auto r13 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+        out[4 * mb + 0] = (int)r02[0];
+        out[4 * mb + 1] = (int)r13[0];
+        out[4 * mb + 2] = (int)r02[1];
+        out[4 * mb + 3] = (int)r13[1];
+    }
+    return out;
+}
+
+// O^T[d, qrow] += V^T[d, key] P^T[key, qrow]: lane (d = 32md + lr, half hf)
+// takes keys 16hf .. +15 (tile 0) and 32 + 16hf .. +15 (tile 1) of row d in
+// the dword order of mx_pack_p, and the scale of V block (d, 2n + hf).
+__device__ __forceinline__ void mx_pv(f32x16 (&oacc)[4], const i32x8& pb, const char* vtb,
+                                      const char* vsb, int lr, int hf) {
+#pragma unroll
+    for (int md = 0; md < 4; ++md) {
+        const int d = 32 * md + lr;
+        const char* row = vtb + d * 64;
+        const u32x4 lo = *(const u32x4*)(row + 16 * (hf ^ swz_vt8(d)));
+        const u32x4 hi = *(const u32x4*)(row + 16 * ((2 + hf) ^ swz_vt8(d)));
+        const i32x8 av = {(int)lo[0], (int)lo[2], (int)lo[1], (int)lo[3],
+                          (int)hi[0], (int)hi[2], (int)hi[1], (int)hi[3]};
+        const int vs = *(const uint8_t*)(vsb + hf * 128 + d);
+        oacc[md] = mfma_mx(av, pb, vs, kP8Scale, oacc[md]);
+    }
+}
+
+// V [64 keys][128 d] (E4M3) -> V^T [128 d][64 keys]: thread t transposes the
+// 4 x 4 byte tile of keys 4(t/32) .. +3 and d 4(t%32) .. +3 in registers.
+__device__ __forceinline__ void mx_transpose_v(const char* v, char* vt, int tid) {
+    const int b = tid & 31, aq = tid >> 5;
+    uint32_t r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = *(const uint32_t*)(v + (4 * aq + i) * 128 + 4 * b);
+    // byte i of column j = byte j of row i
+    const uint32_t lo01 = __builtin_amdgcn_perm(r[1], r[0], 0x05010400u);
+    const uint32_t hi01 = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);
+    const uint32_t lo23 = __builtin_amdgcn_perm(r[3], r[2], 0x05010400u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(r[3], r[2], 0x07030602u);
+    uint32_t c[4];
+    c[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+    c[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+    c[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+    c[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int d = 4 * b + j;
+        *(uint32_t*)(vt + d * 64 + 16 * ((aq >> 2) ^ swz_vt8(d)) + 4 * (aq & 3)) = c[j];
+    }
+}
+
+template <int D, int MODE, bool BCAST, bool MX>
 __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
-    using LY = FwdLds<D>;
+    using LY = FwdLds<D, MX>;
     __shared__ __attribute__((aligned(1024))) char smem[LY::BYTES];
     constexpr int KC = D / 16;              // 16-wide d chunks of S^T = K Q^T
     constexpr int MD = D / 32;              // 32-row d blocks of O^T
@@ -227,12 +346,37 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
         const int64_t base = (int64_t)LT.kv0 * rs + (int64_t)LT.h * D;
         char* kdst = smem + LY::K + (l_slot % kKSlots) * LY::BLK;
         char* vdst = smem + LY::V + (l_slot % kVSlots) * LY::BLK;
-#pragma unroll
-        for (int u = 0; u < LPW; ++u) {
-            const int key = min(kFwdBlockN * n + ld_row[u], LT.L - 1);
+        if constexpr (MX) {
+            // one 16-byte chunk of the K and of the V block per thread: key
+            // q/8, stored chunk q%8 (q = 64 wave + lane); the scales of the
+            // block's 64 keys (wave 0, a dword per key) and of V's two 32-key
+            // blocks (wave 1: lanes 0-31 block 2n, 32-63 block 2n+1, clamped
+            // to the sequence's last block)
+            const int q = 64 * wave + lane, r = q >> 3, cs = q & 7;
+            const int key = min(kFwdBlockN * n + r, LT.L - 1);
             const int64_t row = base + (int64_t)key * rs;
-            load_lds16(a.k + row + ld_gk[u], kdst + 1024 * (LPW * wave + u));
-            load_lds16(a.v + row + ld_gv[u], vdst + 1024 * (LPW * wave + u));
+            load_lds16((const uint16_t*)(a.k8 + row + 16 * (cs ^ swz_k8(r))), kdst + 1024 * wave);
+            load_lds16((const uint16_t*)(a.v8 + row + 16 * cs), vdst + 1024 * wave);
+            if (wave == 0) {
+                const int kk = min(kFwdBlockN * n + lane, LT.L - 1);
+                load_lds4(a.k_sc + ((int64_t)LT.h * a.total_kv + LT.kv0 + kk) * 4,
+                          smem + LY::KS + (l_slot % kKSlots) * LY::SC);
+            } else if (wave == 1) {
+                const int b0 = ld_uniform(a.v_boff + LT.b), nbk = ld_uniform(a.v_boff + LT.b + 1) - b0;
+                const int blk = min(2 * n + (lane >> 5), nbk - 1);
+                // (kKSlots deep like K: block s's scales are read at iteration s,
+                // after the V slot itself was recycled)
+                load_lds4(a.v_sc + ((int64_t)LT.h * a.v_nb + b0 + blk) * D + 4 * (lane & 31),
+                          smem + LY::VS + (l_slot % kKSlots) * LY::SC);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < LPW; ++u) {
+                const int key = min(kFwdBlockN * n + ld_row[u], LT.L - 1);
+                const int64_t row = base + (int64_t)key * rs;
+                load_lds16(a.k + row + ld_gk[u], kdst + 1024 * (LPW * wave + u));
+                load_lds16(a.v + row + ld_gv[u], vdst + 1024 * (LPW * wave + u));
+            }
         }
         ++l_slot;
         ++l_i;
@@ -249,9 +393,13 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
         for (int u = 0; u < TPW; ++u) *(bf16x4*)(dst + tr_dst[u]) = x[u];
     };
     auto transpose_v = [&](int s) {
-        bf16x4 x[TPW];
-        tr_read(s, x);
-        tr_write(s, x);
+        if constexpr (MX) {
+            mx_transpose_v(smem + LY::V + (s % kVSlots) * LY::BLK, smem + LY::VT + (s & 1) * LY::BLK, tid);
+        } else {
+            bf16x4 x[TPW];
+            tr_read(s, x);
+            tr_write(s, x);
+        }
     };
 
     // prologue: block 0 landed and transposed, blocks 1 .. kAhead-1 in flight
@@ -280,7 +428,22 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
         // row; a tile exists only when Lq >= 1, and a wave without rows skips
         // every block)
         bf16x8 qf[KC];
-        {
+        i32x8 qf8[2];   // MXFP8: the two 64-d steps (slots as in mx_scores)
+        int qsc[2];
+        if constexpr (MX) {
+            const int qr = q0 + min(qrow, Lq - 1);
+            const uint8_t* qp = a.q8 + (int64_t)qr * rs + (int64_t)T.h * D;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const u32x4 lo = *(const u32x4*)(qp + 64 * j + 16 * hf);
+                const u32x4 hi = *(const u32x4*)(qp + 64 * j + 32 + 16 * hf);
+                qf8[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            }
+            const uint32_t qs = *(const uint32_t*)(a.q_sc + ((int64_t)T.h * a.q_rows + qr) * 4);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) qsc[j] = (qs >> (8 * (2 * j + hf))) & 255;
+        } else {
             const int qr = min(qrow, Lq - 1);
             const uint16_t* qp = a.q + (int64_t)(q0 + qr) * rs + (int64_t)T.h * D + 8 * hf;
 #pragma unroll
@@ -338,8 +501,10 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
             // Block s+1 landed; in steady state the copies of block s+2 (the
             // wave's 2*LPW most recent vector memory operations) stay in flight.
             if (i > 0) {
-                if (l_slot == s + kAhead) wait_vmem_keep<2 * LPW>();
-                else wait_vmem();
+                if (l_slot != s + kAhead) wait_vmem();
+                else if (!MX) wait_vmem_keep<2 * LPW>();
+                else if (wave < 2) wait_vmem_keep<3>();   // MXFP8: K, V chunks (+ scales)
+                else wait_vmem_keep<2>();
             }
             publish();
             // every wave is past block s-1: its K slot and V^T buffer are free
@@ -353,8 +518,13 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
             block_flags<MODE>(T, i, n, row0, wave_rows, wave, skip, masked);
             if (!skip) {
                 f32x16 sc[2];
-                compute_s(sc, s);
-                pipeline_reads_mfma<2 * KC, kReadAhead>();
+                if constexpr (MX) {
+                    mx_scores(sc, smem + LY::K + (s % kKSlots) * LY::BLK,
+                              smem + LY::KS + (s % kKSlots) * LY::SC, qf8, qsc, lr, hf);
+                } else {
+                    compute_s(sc, s);
+                    pipeline_reads_mfma<2 * KC, kReadAhead>();
+                }
                 // masked tail: keys past the sequence (and, banded, outside the
                 // row's window [lo, lim]) -> -inf
                 if (masked) {
@@ -386,10 +556,26 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
                     for (int md = 0; md < MD; ++md) oacc[md] *= alpha;
                 }
                 float ls = 0.f;
-                bf16x8 pb[4];
-                exp_pack(sc, m_new, ls, pb);
-                l_run = l_run * alpha + ls;
-                pv(pb, s);
+                if constexpr (MX) {
+                    // P (fp32, at most 1; its row sum stays fp32) to E4M3
+#pragma unroll
+                    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const float p = __builtin_amdgcn_exp2f(fmaf(sc[mb][r], a.scale_log2, -m_new));
+                            ls += p;
+                            sc[mb][r] = p;
+                        }
+                    const i32x8 pb8 = mx_pack_p(sc);
+                    l_run = l_run * alpha + ls;
+                    mx_pv(oacc, pb8, smem + LY::VT + (s & 1) * LY::BLK,
+                          smem + LY::VS + (s % kKSlots) * LY::SC, lr, hf);
+                } else {
+                    bf16x8 pb[4];
+                    exp_pack(sc, m_new, ls, pb);
+                    l_run = l_run * alpha + ls;
+                    pv(pb, s);
+                }
             }
         }
 
@@ -402,8 +588,13 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
         const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
         __syncthreads();
         if (wave_rows) {
-            char* st = wave < 4 ? smem + LY::K + ((s + kKSlots - 1) % kKSlots) * LY::BLK + wave * LY::OST_WAVE
-                                : smem + LY::VT + ((s + 1) & 1) * LY::BLK + (wave - 4) * LY::OST_WAVE;
+            char* st;
+            if constexpr (MX) {
+                st = smem + LY::OST + wave * LY::OST_WAVE;
+            } else {
+                st = wave < 4 ? smem + LY::K + ((s + kKSlots - 1) % kKSlots) * LY::BLK + wave * LY::OST_WAVE
+                              : smem + LY::VT + ((s + 1) & 1) * LY::BLK + (wave - 4) * LY::OST_WAVE;
+            }
 #pragma unroll
             for (int rd = 0; rd < 32 / kStageRows; ++rd) {
                 if ((lr >> 4) == rd) {
@@ -449,19 +640,19 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
     }
 }
 
-template <int D, int MODE, bool BCAST>
+template <int D, int MODE, bool BCAST, bool MX = false>
 int32_t launch(const FwdArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((fwd_kernel<D, MODE, BCAST>), dim3(a.num_workers), dim3(kThreads), 0,
+    hipLaunchKernelGGL((fwd_kernel<D, MODE, BCAST, MX>), dim3(a.num_workers), dim3(kThreads), 0,
                        stream, a);
     return (int32_t)hipGetLastError();
 }
 
-template <int D>
+template <int D, bool MX = false>
 int32_t launch_d(const FwdArgs& a, Mode mode, bool bcast, hipStream_t s) {
-    if (mode == kCausal) return launch<D, kCausal, false>(a, s);
+    if (mode == kCausal) return launch<D, kCausal, false, MX>(a, s);
     if (mode == kSparse)
-        return bcast ? launch<D, kSparse, true>(a, s) : launch<D, kSparse, false>(a, s);
-    return bcast ? launch<D, kDense, true>(a, s) : launch<D, kDense, false>(a, s);
+        return bcast ? launch<D, kSparse, true, MX>(a, s) : launch<D, kSparse, false, MX>(a, s);
+    return bcast ? launch<D, kDense, true, MX>(a, s) : launch<D, kDense, false, MX>(a, s);
 }
 
 }  // namespace
@@ -470,6 +661,10 @@ int32_t launch_fwd(const FwdArgs& a, int32_t head_dim, Mode mode, bool broadcast
     hipStream_t s = (hipStream_t)stream;
     if (head_dim == 64) return launch_d<64>(a, mode, broadcast, s);
     return launch_d<128>(a, mode, broadcast, s);
+}
+
+int32_t launch_fwd_mx(const FwdArgs& a, Mode mode, bool broadcast, void* stream) {
+    return launch_d<128, true>(a, mode, broadcast, (hipStream_t)stream);
 }
 
 }  // namespace jfa

@@ -61,6 +61,17 @@ struct FwdArgs {
     int32_t win_left, win_right;   // banded mode: window bounds (-1: none)
     int32_t* counter;       // dynamic plan: [0] tiles claimed, [1] workgroups done; else null
     float scale_log2;       // softmax_scale * log2(e)
+    // MXFP8 forward only (q, k, v above unused): E4M3 codes and E8M0 scales
+    const uint8_t* q8;      // [q rows, H, D]
+    const uint8_t* k8;      // [T_k, H, D]
+    const uint8_t* v8;      // [T_k, H, D]
+    const uint8_t* q_sc;    // [H, q rows, D/32]
+    const uint8_t* k_sc;    // [H, T_k, D/32]
+    const uint8_t* v_sc;    // [H, NB, D]: 32-key blocks of each sequence
+    const int32_t* v_boff;  // [B+1]: first V scale block of each sequence
+    int32_t q_rows;         // lq (broadcast) or T_q
+    int32_t total_kv;
+    int32_t v_nb;           // NB
 };
 
 // Workspace of a dynamic forward plan (two int32 counters, padded).
@@ -136,9 +147,15 @@ struct DqReduceArgs {
 
 // Launchers (return a hipError_t value as int32).
 int32_t launch_fwd(const FwdArgs& a, int32_t head_dim, Mode mode, bool broadcast, void* stream);
+int32_t launch_fwd_mx(const FwdArgs& a, Mode mode, bool broadcast, void* stream);
 int32_t launch_bwd(const BwdArgs& a, int32_t head_dim, Mode mode, bool broadcast, int32_t stages,
                    void* stream);
 int32_t launch_dq(const DqArgs& a, int32_t head_dim, Mode mode, bool broadcast, void* stream);
 int32_t launch_dq_reduce(const DqReduceArgs& a, int32_t head_dim, void* stream);
+int32_t launch_mx_quant_rows(const uint16_t* src, int64_t rows, int32_t H, int32_t D, uint8_t* codes,
+                             uint8_t* scales, void* stream);
+int32_t launch_mx_quant_v(const uint16_t* v, const int32_t* kv_off, const int32_t* boff, int32_t B,
+                          int32_t H, int32_t D, int32_t nbt, uint8_t* codes, uint8_t* scales,
+                          void* stream);
 
 }  // namespace jfa

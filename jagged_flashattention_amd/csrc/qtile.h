@@ -68,6 +68,22 @@ __device__ __forceinline__ void load_lds16(const uint16_t* g, char* lds_wave_bas
         : "memory");
 }
 
+// Direct-to-LDS copy of 4 bytes per lane: lane l's dword at g lands at
+// lds_wave_base + 4 l (same conventions as load_lds16).
+__device__ __forceinline__ void load_lds4(const void* g, char* lds_wave_base) {
+    const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_wave_base;
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(g), "s"(lds)
+        : "memory");
+}
+
 // One tile of a Q-tile plan (wave-uniform): Q tile t of sequence b, head h,
 // visiting positions k0 .. k0+work-1 of the tile's block list (k0 > 0 only
 // for a chunk of a split broadcast-Q dQ tile). Banded mode: the list is the

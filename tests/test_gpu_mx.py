@@ -1,0 +1,176 @@
+"""MXFP8 variant on the GPU (through the C ABI) against the oracle.
+
+The encoders must equal the oracle's encoder bit for bit (integer codes and
+scales). The MXFP8 forward computes attention on the decoded Q, K, V; the
+only other rounding besides fp32 accumulation is P's own E4M3 rounding inside
+the kernel, so against the oracle's exact attention on the decoded inputs:
+
+  |O_gpu - O| <= sum_j max(2^-4 P_ij, 2^-18) |v_jd|  +  2^-8 |O|  +  1e-3
+
+per element (E4M3 rounds P, scaled by 2^8 and at most 256, to nearest even:
+relative error <= 2^-4 in its normal range, absolute <= 2^-10 * 2^-8 below
+it; the second term is O's bf16 rounding, the third fp32 accumulation), and
+LSE (fp32 softmax on exactly computed scores) within 1e-2.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention as A
+from oracle import mx as OMX
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import jagged_flashattention_amd as J  # noqa: E402
+from test_gpu_parity import SMALL_CASES, _custom, dev, problem_of  # noqa: E402
+
+
+def _u8(t):
+    return t.cpu().numpy().astype(np.uint8)
+
+
+def test_quantize_rows_bit_exact():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((300, 3, 128)).astype(np.float32)
+    x *= np.exp(rng.standard_normal((300, 3, 1)) * 4).astype(np.float32)
+    x[5, 1, :32] = 0.0
+    x[6, 2, 40] = -0.0
+    x[7, 0, :] = 1e-30                                  # below the normal range
+    bits = W.f32_to_bf16_bits(x)
+    src = dev(bits)
+    codes = torch.empty(src.shape, dtype=torch.uint8, device="cuda")
+    scales = torch.empty((3, 300, 4), dtype=torch.uint8, device="cuda")
+    J.jfa_mx_quantize_rows(src, codes, scales)
+    torch.cuda.synchronize()
+    oc, os_ = OMX.quantize_rows(W.bf16_bits_to_f32(bits).astype(np.float64))
+    assert np.array_equal(_u8(codes), oc)
+    assert np.array_equal(_u8(scales), os_)
+
+
+def test_quantize_v_bit_exact():
+    rng = np.random.default_rng(4)
+    lens = np.array([0, 1, 31, 32, 33, 100, 257, 0, 64])
+    off = W.offsets_of(lens)
+    v = rng.standard_normal((int(off[-1]), 2, 128)).astype(np.float32) * 3
+    v[40] *= 500.0
+    bits = W.f32_to_bf16_bits(v)
+    boff = J.jfa_mx_block_offsets(off)
+    assert np.array_equal(boff, OMX.mx_block_offsets(off))
+    nb = int(boff[-1])
+    src = dev(bits)
+    codes = torch.empty(src.shape, dtype=torch.uint8, device="cuda")
+    scales = torch.empty((2, nb, 128), dtype=torch.uint8, device="cuda")
+    J.jfa_mx_quantize_v(src, torch.from_numpy(off).cuda(), torch.from_numpy(boff).cuda(), nb,
+                        codes, scales)
+    torch.cuda.synchronize()
+    oc, os_ = OMX.quantize_v(W.bf16_bits_to_f32(bits).astype(np.float64), off)
+    assert np.array_equal(_u8(codes), oc)
+    assert np.array_equal(_u8(scales), os_)
+
+
+def _decoded(x):
+    """The oracle's decoding of the oracle's encoding of the bf16 inputs."""
+    q = W.bf16_bits_to_f32(x.q).astype(np.float64)
+    k = W.bf16_bits_to_f32(x.k).astype(np.float64)
+    v = W.bf16_bits_to_f32(x.v).astype(np.float64)
+    q = OMX.dequantize_rows(*OMX.quantize_rows(q))
+    k = OMX.dequantize_rows(*OMX.quantize_rows(k))
+    v = OMX.dequantize_v(*OMX.quantize_v(v, x.kv_offsets), x.kv_offsets)
+    return q, k, v
+
+
+def _check_mx(x, o_gpu, lse_gpu, seqs=None, heads=None):
+    w = x.workload
+    q, k, v = _decoded(x)
+    kw = dict(scale=w.scale, broadcast_q=w.broadcast_q, q_offsets=x.q_offsets, causal=w.causal,
+              block_mask=x.block_mask, window=w.window)
+    o, lse = A.forward(q, k, v, x.kv_offsets, seqs=seqs, heads=heads, **kw)
+    B = x.batch
+    total_err, n_el = 0.0, 0
+    for b in (range(B) if seqs is None else seqs):
+        k0, k1 = int(x.kv_offsets[b]), int(x.kv_offsets[b + 1])
+        if w.broadcast_q:
+            qs, os_ = slice(0, w.lq), slice(b * w.lq, (b + 1) * w.lq)
+        else:
+            qs = os_ = slice(int(x.q_offsets[b]), int(x.q_offsets[b + 1]))
+        n_rows = os_.stop - os_.start
+        if n_rows == 0:
+            continue
+        vis = A.visibility(n_rows, k1 - k0, causal=w.causal, window=w.window,
+                           mask_b=None if x.block_mask is None else x.block_mask[b])
+        for h in (range(w.heads) if heads is None else heads):
+            lse_ref = lse[h, os_]
+            fin = np.isfinite(lse_ref)
+            s = w.scale * (q[qs, h] @ k[k0:k1, h].T)
+            p = np.where(vis, np.exp(s - np.where(fin, lse_ref, 0.0)[:, None]), 0.0)
+            av = np.abs(v[k0:k1, h])
+            bound = (2.0 ** -4 * p @ av + 2.0 ** -18 * (vis.astype(float) @ av)
+                     + 2.0 ** -8 * np.abs(o[os_, h]) + 1e-3)
+            err = np.abs(o_gpu[os_, h] - o[os_, h])
+            assert np.all(err <= bound), (b, h, float((err - bound).max()))
+            total_err += err.sum()
+            n_el += err.size
+            assert np.array_equal(fin, np.isfinite(lse_gpu[h, os_]))
+            if fin.any():
+                assert np.abs(lse_gpu[h, os_][fin] - lse_ref[fin]).max() <= 1e-2, (b, h)
+    # and on average far inside that bound (a systematic error would not be)
+    assert total_err / max(n_el, 1) <= 1e-2
+
+
+def _run_mx(x, dynamic=True):
+    prob = problem_of(x)
+    att = J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask, fwd_dynamic=dynamic)
+    mxq = att.quantize_mx(dev(x.q), dev(x.k), dev(x.v))
+    H, D = prob.num_heads, prob.head_dim
+    o = torch.full((att.total_q, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((H, att.total_q), float("nan"), dtype=torch.float32, device="cuda")
+    att.forward_mx(mxq, o, lse)
+    torch.cuda.synchronize()
+    return (W.bf16_bits_to_f32(o.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64),
+            lse.cpu().numpy().astype(np.float64))
+
+
+MX_CASES = ["bcast_ragged_d128", "perseq_d128", "causal_d128", "sparse_d128", "window_band_d128",
+            "window_causal_d128", "cfg2_small", "cfg3_small", "cfg5_small"]
+
+
+@pytest.mark.parametrize("case", MX_CASES)
+def test_mx_forward_small(case):
+    print("case", case, flush=True)
+    x = SMALL_CASES[case]()
+    o, lse = _run_mx(x)
+    assert not np.isnan(o).any() and not np.isnan(lse).any()
+    _check_mx(x, o, lse)
+
+
+def test_mx_forward_static_plan_and_bitwise_repeat():
+    x = SMALL_CASES["cfg2_small"]()
+    o1, l1 = _run_mx(x, dynamic=False)
+    o2, l2 = _run_mx(x, dynamic=True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_mx_forward_full_size_sampled():
+    print("full-size GEM broadcast-Q, MXFP8", flush=True)
+    x = W.make_inputs(2)
+    o, lse = _run_mx(x)
+    assert not np.isnan(o).any() and not np.isnan(lse).any()
+    lens = x.lengths
+    seqs = sorted({int(np.argmax(lens)), int(np.argmin(lens)), 7})
+    _check_mx(x, o, lse, seqs=seqs, heads=[1])
+
+
+def test_mx_rejects_unsupported_head_dim():
+    x = SMALL_CASES["bcast_ragged_d64"]()
+    prob = problem_of(x)
+    att = J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask)
+    with pytest.raises(J.JfaError) as e:
+        mxq = att.quantize_mx(dev(x.q), dev(x.k), dev(x.v))
+        att.forward_mx(mxq)
+    assert e.value.status == J.JFA_ERR_UNSUPPORTED
