@@ -71,7 +71,8 @@ def work_model(x):
     fwd_bytes = q_rows * e + 2 * kv_read_rows * e + t_q * e + t_q * H * 4
     pre_bytes = 2 * t_q * e + t_q * H * 4
     dkdv_bytes = q_rows * e + 2 * kv_read_rows * e + t_q * e + 2 * t_q * H * 4 + 2 * t_k * e
-    dq_bytes = (q_rows * e + 2 * kv_read_rows * e + t_q * e + 2 * t_q * H * 4
+    # the dQ pass also forms delta: it reads O and writes delta
+    dq_bytes = (q_rows * e + 2 * kv_read_rows * e + 2 * t_q * e + 2 * t_q * H * 4
                 + q_rows * H * D * 4 + q_rows * e)
     reduce_bytes = q_rows * H * D * 4 + q_rows * e
     # FLOPs: the forward's two GEMMs; the backward's five (S, dP, dV, dK in the
@@ -211,7 +212,7 @@ def main():
     out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
                dq_accum=torch.empty(q.shape, dtype=torch.float32, device="cuda"),
                delta=torch.empty((H, att.total_q), dtype=torch.float32, device="cuda"))
-    stages = (J.JFA_BWD_PREPROCESS, J.JFA_BWD_DKDV, J.JFA_BWD_DQ, J.JFA_BWD_DQ_REDUCE)
+    stages = (J.JFA_BWD_DQ, J.JFA_BWD_DKDV, J.JFA_BWD_DQ_REDUCE)
     nev = len(stages) + 2
 
     def step(ev=None):
@@ -244,7 +245,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    names = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq", "bwd_dq_reduce")
+    names = ("fwd", "bwd_dq", "bwd_dkdv", "bwd_dq_reduce")
     per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in events])) for j, n in enumerate(names)}
 
     # the MXFP8 forward of the same problem (inputs encoded once, outside the
@@ -270,7 +271,7 @@ def main():
     value = flop / (ms_step * 1e-3) / 1e12
     wl_name = w.name
     fwd_tf = model["fwd_flop"] / (per["fwd"] * 1e-3) / 1e12
-    bwd_ms = per["bwd_pre"] + per["bwd_dkdv"] + per["bwd_dq"] + per["bwd_dq_reduce"]
+    bwd_ms = per["bwd_dq"] + per["bwd_dkdv"] + per["bwd_dq_reduce"]
     bwd_tf = model["bwd_flop"] / (bwd_ms * 1e-3) / 1e12
 
     kernels = {

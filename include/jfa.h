@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define JFA_ABI_VERSION 5
+#define JFA_ABI_VERSION 6
 
 /* status codes */
 #define JFA_OK                 0
@@ -285,16 +285,17 @@ int32_t jfa_bwd_workspace_bytes(const jfa_problem* prob, const jfa_plan_info* dq
  * Backward pass: dQ, dK, dV for the loss sum(dO * O), given the forward's O
  * and LSE. kv_plan is a BWD plan (KV tiles), dq_plan a DQ plan (Q tiles), both
  * for this problem and these offsets. Enqueues, in stream order:
- *   1. preprocess: delta = rowsum(dO * O), fp32 [H, T_q];
- *   2. dK/dV: KV-stationary persistent kernel over kv_plan, dK and dV
- *      accumulated per KV tile in registers and written as bf16;
- *   3. dQ: Q-stationary persistent kernel over dq_plan (the forward's tiles),
- *      dQ accumulated in registers while the K/V blocks stream past. With
- *      per-sequence Q each tile writes its rows of dq_accum (fp32) and dq
- *      (bf16). With broadcast Q, dQ sums over all sequences (theclarity.today,
- *      second paragraph): each dQ worker adds up its tiles, which all belong
- *      to one (head, Q tile) group, into one fp32 partial in the workspace;
- *   4. dQ reduce (broadcast Q only): the partials of each group are added in
+ *   1. dQ: Q-stationary persistent kernel over dq_plan (the forward's tiles),
+ *      dQ accumulated in registers while the K/V blocks stream past; each
+ *      tile also forms delta = rowsum(dO * O) (fp32 [H, T_q]) of its rows
+ *      and writes it out. With per-sequence Q each tile writes its rows of
+ *      dq_accum (fp32) and dq (bf16). With broadcast Q, dQ sums over all
+ *      sequences (theclarity.today, second paragraph): each dQ worker adds up
+ *      its tiles, which all belong to one (head, Q tile) group, into one fp32
+ *      partial in the workspace;
+ *   2. dK/dV: KV-stationary persistent kernel over kv_plan (reads delta), dK
+ *      and dV accumulated per KV tile in registers and written as bf16;
+ *   3. dQ reduce (broadcast Q only): the partials of each group are added in
  *      worker order into dq_accum (fp32 [lq, H, D]) and dq (bf16). The result
  *      does not depend on timing; no atomics are used anywhere.
  * dq_accum and delta are outputs too. workspace: jfa_bwd_workspace_bytes
@@ -310,16 +311,18 @@ int32_t jfa_bwd(const jfa_problem* prob, const jfa_device_plan* kv_plan,
 /*
  * The same backward, one stage at a time, for callers that interleave other
  * work or time each launch: `stages` is a bitwise OR of the JFA_BWD_* flags;
- * the selected launches are enqueued in stage order. Each stage expects the
- * outputs of the stages before it to be in place (delta for DKDV and DQ, the
- * dQ partials for DQ_REDUCE). Arguments are the same as jfa_bwd and are
+ * the selected launches are enqueued in flag order. Each stage expects the
+ * outputs of the stages before it to be in place (delta for DKDV, the dQ
+ * partials for DQ_REDUCE). Arguments are the same as jfa_bwd and are
  * validated the same way whatever the stages.
  */
-#define JFA_BWD_PREPROCESS 1   /* delta = rowsum(dO*O)                         */
-#define JFA_BWD_DKDV       2   /* dK, dV                                       */
-#define JFA_BWD_DQ         4   /* dQ (per-sequence Q) or dQ partials (broadcast) */
+#define JFA_BWD_PREPROCESS 1   /* delta = rowsum(dO*O) alone (not in ALL: the
+                                  DQ stage forms it too)                      */
+#define JFA_BWD_DQ         2   /* dQ (per-sequence Q) or dQ partials
+                                  (broadcast), and delta                      */
+#define JFA_BWD_DKDV       4   /* dK, dV                                       */
 #define JFA_BWD_DQ_REDUCE  8   /* broadcast Q: dq_accum, dq from the partials  */
-#define JFA_BWD_ALL        15
+#define JFA_BWD_ALL        14
 int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device_plan* kv_plan,
                        const jfa_device_plan* dq_plan, const int32_t* d_q_offsets,
                        const int32_t* d_kv_offsets, const void* q, const void* k, const void* v,

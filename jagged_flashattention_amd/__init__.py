@@ -37,10 +37,10 @@ EXPORTS = (
     "jfa_mx_quantize_rows", "jfa_mx_quantize_v", "jfa_fwd_mx",
 )
 JFA_BWD_PREPROCESS = 1
-JFA_BWD_DKDV = 2
-JFA_BWD_DQ = 4
+JFA_BWD_DQ = 2
+JFA_BWD_DKDV = 4
 JFA_BWD_DQ_REDUCE = 8
-JFA_BWD_ALL = 15
+JFA_BWD_ALL = 14
 
 
 class JfaProblem(ctypes.Structure):

@@ -285,7 +285,7 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device
                        const void* o, const float* lse, const void* d_o, void* dq, void* dk,
                        void* dv, float* dq_accum, float* delta, void* workspace,
                        int64_t workspace_bytes, void* stream) {
-    if (stages < 0 || stages > JFA_BWD_ALL) return JFA_ERR_INVALID_ARG;
+    if (stages < 0 || stages > (JFA_BWD_ALL | JFA_BWD_PREPROCESS)) return JFA_ERR_INVALID_ARG;
     int32_t st = check_plan(prob, kv_plan, JFA_PASS_BWD, d_q_offsets, d_kv_offsets);
     if (st) return st;
     st = check_plan(prob, dq_plan, JFA_PASS_DQ, d_q_offsets, d_kv_offsets);
@@ -337,9 +337,10 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device
     a.win_right = bd.right;
     a.scale = prob->softmax_scale;
     a.scale_log2 = prob->softmax_scale * 1.4426950408889634f;
-    st = hip_status(jfa::launch_bwd(a, prob->head_dim, mode, bcast,
-                                    stages & (JFA_BWD_PREPROCESS | JFA_BWD_DKDV), stream));
-    if (st) return st;
+    if (stages & JFA_BWD_PREPROCESS) {
+        st = hip_status(jfa::launch_bwd(a, prob->head_dim, mode, bcast, JFA_BWD_PREPROCESS, stream));
+        if (st) return st;
+    }
 
     if ((stages & JFA_BWD_DQ) && qi->num_tiles > 0) {
         jfa::DqArgs d;
@@ -353,6 +354,7 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device
         d.k = a.k;
         d.v = a.v;
         d.d_o = a.d_o;
+        d.o = a.o;
         d.lse = lse;
         d.delta = delta;
         d.dq = static_cast<uint16_t*>(dq);
@@ -369,6 +371,10 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device
         d.scale = prob->softmax_scale;
         d.scale_log2 = a.scale_log2;
         st = hip_status(jfa::launch_dq(d, prob->head_dim, mode, bcast, stream));
+        if (st) return st;
+    }
+    if (stages & JFA_BWD_DKDV) {
+        st = hip_status(jfa::launch_bwd(a, prob->head_dim, mode, bcast, JFA_BWD_DKDV, stream));
         if (st) return st;
     }
     if ((stages & JFA_BWD_DQ_REDUCE) && bcast) {

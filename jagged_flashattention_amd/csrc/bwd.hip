@@ -4,7 +4,9 @@
 //   1. preprocess: delta = rowsum(dO * O) in fp32 (the standard FlashAttention
 //      backward step; the pages only name the backward's persistent, tiled
 //      structure: "Meta's TLX Jagged Flash Attention Beats FA4 on Blackwell"
-//      (ainewsbites.com), section "Optimizations layered on top");
+//      (ainewsbites.com), section "Optimizations layered on top"). A stage of
+//      its own for callers that want delta alone: the full backward forms it
+//      inside the dQ pass, which runs first;
 //   2. dK/dV: one persistent workgroup of 8 waves per CU walking a KV-tile
 //      plan. A workgroup owns a 256-key KV tile (32 keys per wave, K in VGPRs
 //      as a B operand, V in LDS) and streams the 32-row Q/dO blocks that see

@@ -219,7 +219,22 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
             }
         }
         const float lse = a.lse[(int64_t)T.h * a.total_q + orow0 + qr];
-        const float dlt = a.delta[(int64_t)T.h * a.total_q + orow0 + qr];
+        // delta = rowsum(dO * O) of this lane's row (the standard FlashAttention
+        // backward quantity), from its half of d and the other half's lane;
+        // the tile's first chunk writes it out for the dK/dV pass
+        float dlt;
+        {
+            const uint16_t* op = a.o + (int64_t)(orow0 + qr) * rs + (int64_t)T.h * D + 8 * hf;
+            float part = 0.f;
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const bf16x8 of = load_bf16x8(op + 16 * kc);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) part = fmaf((float)df[kc][j], (float)of[j], part);
+            }
+            dlt = pair_sum(part);
+            if (hf == 0 && T.k0 == 0 && qrow < Lq) a.delta[(int64_t)T.h * a.total_q + orow0 + qrow] = dlt;
+        }
         // a row without visible keys (LSE = -inf) gets P = 0
         const float lse2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
         if (!BCAST) {
@@ -317,9 +332,10 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
             }
         }
     }
-    if (BCAST && t_begin < t_end) {
+    if (BCAST) {
         // this worker's partial sum over its tiles (all of one (head, Q tile)
-        // group): rows 0..255 of the tile, fp32
+        // group): rows 0..255 of the tile, fp32 (zeros for a worker without
+        // tiles, so that the reduce reads every partial unconditionally)
         __syncthreads();
         float* part = a.partial + (int64_t)w * kFwdBlockM * D;
         stage_out(s, [&](int r, int chunk, const f32x4& x) {
@@ -356,9 +372,7 @@ __global__ void __launch_bounds__(256) dq_reduce_kernel(DqReduceArgs a) {
         const int q0 = w0 + (nw * wave) / 4, q1 = w0 + (nw * (wave + 1)) / 4;
         const float* src = a.partial + (int64_t)(row % kFwdBlockM) * D + 4 * c4;
         if (a.worker_ptr != nullptr)   // null: the plan has no tiles, dQ = 0
-            for (int wk = q0; wk < q1; ++wk)
-                if (a.worker_ptr[wk + 1] > a.worker_ptr[wk])
-                    sum += *(const f32x4*)(src + (int64_t)wk * kFwdBlockM * D);
+            for (int wk = q0; wk < q1; ++wk) sum += *(const f32x4*)(src + (int64_t)wk * kFwdBlockM * D);
     }
     part[wave][lane] = sum;
     __syncthreads();

@@ -117,8 +117,9 @@ struct DqArgs {
     const uint16_t* k;
     const uint16_t* v;
     const uint16_t* d_o;
+    const uint16_t* o;       // the forward's output, for delta
     const float* lse;
-    const float* delta;
+    float* delta;            // written: rowsum(dO * O) of every row
     uint16_t* dq;            // per-sequence Q: bf16 [T_q, H, D]
     float* dq_accum;         // per-sequence Q: fp32 [T_q, H, D]
     float* partial;          // broadcast Q: fp32 [W][256][D] per-worker partial sums
