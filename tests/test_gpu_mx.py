@@ -53,19 +53,22 @@ def test_quantize_rows_bit_exact():
     assert np.array_equal(_u8(scales), os_)
 
 
-def test_quantize_v_bit_exact():
+@pytest.mark.parametrize("D", [32, 64, 96, 128])
+def test_quantize_v_bit_exact(D):
     rng = np.random.default_rng(4)
-    lens = np.array([0, 1, 31, 32, 33, 100, 257, 0, 64])
+    lens = np.array([0, 1, 31, 32, 33, 100, 257, 0, 64, 1000])
     off = W.offsets_of(lens)
-    v = rng.standard_normal((int(off[-1]), 2, 128)).astype(np.float32) * 3
+    v = rng.standard_normal((int(off[-1]), 2, D)).astype(np.float32) * 3
+    v *= np.exp(rng.standard_normal((1, 2, D)) * 2).astype(np.float32)   # column scales apart
     v[40] *= 500.0
+    v[518:550, 1, :5] = 0.0              # all-zero columns of the last sequence's first block
     bits = W.f32_to_bf16_bits(v)
     boff = J.jfa_mx_block_offsets(off)
     assert np.array_equal(boff, OMX.mx_block_offsets(off))
     nb = int(boff[-1])
     src = dev(bits)
     codes = torch.empty(src.shape, dtype=torch.uint8, device="cuda")
-    scales = torch.empty((2, nb, 128), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((2, nb, D), dtype=torch.uint8, device="cuda")
     J.jfa_mx_quantize_v(src, torch.from_numpy(off).cuda(), torch.from_numpy(boff).cuda(), nb,
                         codes, scales)
     torch.cuda.synchronize()
