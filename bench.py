@@ -1,8 +1,8 @@
 """Benchmark: jagged FlashAttention forward + backward on one MI355X.
 
 One step = the whole hot path over one batch of synthetic input: jfa_fwd
-(O, LSE) then the backward stages (delta preprocess, dK/dV kernel, dQ kernel,
-dQ reduce). Inputs are resident in HBM before timing starts. The default
+(O, LSE) then the backward stages (dQ kernel, which also forms delta =
+rowsum(dO*O); dK/dV kernel; dQ reduce). Inputs are resident in HBM before timing starts. The default
 workload is the GEM-shaped broadcast-Q one (B=256 sequences with lognormal
 lengths, H=4, D=128, one shared Q of 256 rows).
 
@@ -27,8 +27,10 @@ PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 METRIC = "JFA fwd+bwd TFLOP/s (bf16) and % of MFMA peak, jagged broadcast-Q"
 
 
-def work_model(x):
-    """Algorithmic FLOPs and bytes of one step (see the design notes)."""
+def work_model(x, dq_workers: int = 256):
+    """Algorithmic FLOPs and bytes of one step (see the design notes).
+    ``dq_workers``: workers of the dQ plan (broadcast Q: each writes one fp32
+    partial of a 256-row Q tile, which the reduce reads back)."""
     import numpy as np
     w = x.workload
     H, D = w.heads, w.head_dim
@@ -71,10 +73,15 @@ def work_model(x):
     fwd_bytes = q_rows * e + 2 * kv_read_rows * e + t_q * e + t_q * H * 4
     pre_bytes = 2 * t_q * e + t_q * H * 4
     dkdv_bytes = q_rows * e + 2 * kv_read_rows * e + t_q * e + 2 * t_q * H * 4 + 2 * t_k * e
-    # the dQ pass also forms delta: it reads O and writes delta
+    # the dQ pass also forms delta: it reads O and writes delta. Broadcast Q:
+    # it writes the workers' fp32 partials, which the reduce reads back
+    # before writing dq_accum (fp32) and dq; per-sequence Q: it writes those
+    # two itself
+    dq_out = q_rows * H * D * 4 + q_rows * e
+    partials = dq_workers * 256 * D * 4 if w.broadcast_q else 0
     dq_bytes = (q_rows * e + 2 * kv_read_rows * e + 2 * t_q * e + 2 * t_q * H * 4
-                + q_rows * H * D * 4 + q_rows * e)
-    reduce_bytes = q_rows * H * D * 4 + q_rows * e
+                + (partials if w.broadcast_q else dq_out))
+    reduce_bytes = partials + dq_out if w.broadcast_q else 0
     # FLOPs: the forward's two GEMMs; the backward's five (S, dP, dV, dK in the
     # dK/dV kernel, dQ in the dQ kernel; the dQ kernel's recomputation of S
     # and dP is not counted)
@@ -137,9 +144,10 @@ def cpu_baseline(x, budget_s: float):
                       "same workload, %.1f s" % (done, x.batch, w.heads, t_used)}
 
 
-def traffic_for(kernel: str, workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if
-    they were taken on the current kernel source; else None."""
+def counters_for(kernel: str, workload: str):
+    """The committed rocprofv3 counter summary of one kernel (HBM bytes and
+    MFMA busy cycles per launch), if it was taken on the current kernel
+    source; else None."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "%s.%s.traffic.txt" % (kernel, workload))
     if not os.path.exists(path):
@@ -155,7 +163,7 @@ def traffic_for(kernel: str, workload: str):
     digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
     if digest != kv.get("source_sha256_16"):
         return None
-    return float(kv["hbm_bytes_per_launch"])
+    return kv
 
 
 def main():
@@ -190,7 +198,6 @@ def main():
 
     x = W.make_inputs(args.workload)
     w = x.workload
-    model = work_model(x)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
     q, k, v, do = dev(x.q), dev(x.k), dev(x.v), dev(x.do)
     mq, mk = (x.block_mask.shape[1], x.block_mask.shape[2]) if x.block_mask is not None else (0, 0)
@@ -206,6 +213,7 @@ def main():
                             bwd_workers=cus * args.bwd_workers_per_cu,
                             fwd_dynamic=args.fwd_plan == "dynamic")
     plan_ms = (time.perf_counter() - t0) * 1e3
+    model = work_model(x, att.dq_plan.info.num_workers)
     H, D = w.heads, w.head_dim
     o = torch.empty((att.total_q, H, D), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((H, att.total_q), dtype=torch.float32, device="cuda")
@@ -264,8 +272,28 @@ def main():
             e1.record()
         torch.cuda.synchronize()
         mx_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in mev]))
+        # the encoding of bf16 Q, K, V into MXFP8, timed on its own
+        for e0, e1 in mev:
+            e0.record()
+            att.quantize_mx(q, k, v)
+            e1.record()
+        torch.cuda.synchronize()
+        qz_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in mev]))
         mx = {"fwd_ms": mx_ms, "fwd_tflops": model["fwd_flop"] / (mx_ms * 1e-3) / 1e12,
-              "pct_fp8_peak": 100.0 * model["fwd_flop"] / (mx_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS}
+              "pct_fp8_peak": 100.0 * model["fwd_flop"] / (mx_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
+              "encode_ms": qz_ms,
+              "fwd_with_encode_tflops": model["fwd_flop"] / ((mx_ms + qz_ms) * 1e-3) / 1e12}
+
+    # the standalone delta preprocess (not part of the step: the dQ kernel
+    # forms delta itself), timed alone for its HBM rate
+    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for e0, e1 in pev:
+        e0.record()
+        att.backward(q, k, v, o, lse, do, out, stages=J.JFA_BWD_PREPROCESS)
+        e1.record()
+    torch.cuda.synchronize()
+    pre_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in pev]))
 
     flop = model["fwd_flop"] + model["bwd_flop"]
     value = flop / (ms_step * 1e-3) / 1e12
@@ -290,7 +318,8 @@ def main():
         roof = {"bound": "hbm", "achieved": kbytes / t_s / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = traffic_for(dom, wl_name)
+    cnt = {n: counters_for(n, wl_name) for n in kernels}
+    roof["traffic"] = float(cnt[dom]["hbm_bytes_per_launch"]) if cnt[dom] else None
     roof["kernel"] = dom
     roof["avg_ms"] = per[dom]
     roof["algorithmic_flop"] = kflop
@@ -323,6 +352,12 @@ def main():
         "fwd_tflops": fwd_tf,
         "bwd_tflops": bwd_tf,
         "kernel_ms": per,
+        "hbm_gbps": {"bwd_dq_reduce": (model["reduce_bytes"] / (per["bwd_dq_reduce"] * 1e-3) / 1e9
+                                       if model["reduce_bytes"] else None),
+                     "bwd_preprocess_standalone": model["pre_bytes"] / (pre_ms * 1e-3) / 1e9},
+        "bwd_preprocess_standalone_ms": pre_ms,
+        "mfma_busy_pct_counters": {n: float(c["mfma_busy_pct"]) for n, c in cnt.items()
+                                   if c and "mfma_busy_pct" in c},
         "plan_host_ms": plan_ms,
         "roofline": roof,
     }
