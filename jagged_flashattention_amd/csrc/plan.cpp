@@ -8,7 +8,10 @@
 // The backward pass reuses it with KV tiles. The pages fix no tile size, work
 // measure, tie order or meaning of "zigzag"; the readings used here are:
 // work = inner-loop trip count of the tile, stable sort (ties keep (b,h,t)
-// order), snake deal (round r goes left-to-right when r is even, else
+// order) on the work (forward, dQ) or on the tile's estimated time on the
+// dK/dV kernel (backward: work * (kBwdBlockFixed + waves holding keys) +
+// kBwdTileFixed, so the partial last tile of a sequence does not count as a
+// full one), snake deal (round r goes left-to-right when r is even, else
 // right-to-left).
 // A dynamic forward plan keeps the same sort but deals only the first W
 // tiles (one per worker); the rest are claimed at run time, in sorted order,
@@ -25,6 +28,13 @@
 namespace jfa {
 
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// backward sort key: units of one wave's share of a Q block's products; a
+// block also costs kBwdBlockFixed of them in copies and barriers, a tile
+// boundary (K/V fetch, dK/dV stores) kBwdTileFixed (measured on the kernel)
+constexpr int64_t kBwdWaveKeys = 32;   // keys per wave: kBwdBlockN over the kernel's 8 waves
+constexpr int64_t kBwdBlockFixed = 4;
+constexpr int64_t kBwdTileFixed = 42;
 
 int32_t check_offsets(const int32_t* off, int32_t batch) {
     if (off == nullptr) return JFA_ERR_INVALID_ARG;
@@ -284,7 +294,17 @@ int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, co
     if (sparse && (sp_ptr == nullptr || (sp_idx == nullptr && sp_nnz > 0)))
         return JFA_ERR_INVALID_ARG;
 
-    // 3. stable sort by work, descending (within each group when grouped)
+    // 3. stable sort by the key, descending (within each group when grouped)
+    std::vector<int64_t> key(tiles.size());
+    for (size_t i = 0; i < tiles.size(); ++i) {
+        const Tile& t = tiles[i];
+        if (pass == JFA_PASS_BWD) {
+            const int64_t keys = std::min<int64_t>(bn, (int64_t)L.kv[t.b] - (int64_t)t.t * bn);
+            key[i] = (int64_t)t.work * (kBwdBlockFixed + cdiv(keys, kBwdWaveKeys)) + kBwdTileFixed;
+        } else {
+            key[i] = t.work;
+        }
+    }
     std::vector<int32_t> order(tiles.size());
     std::iota(order.begin(), order.end(), 0);
     auto group_of = [&](const Tile& t) -> int64_t {
@@ -293,7 +313,7 @@ int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, co
     std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t c) {
         const int64_t ga = group_of(tiles[a]), gc = group_of(tiles[c]);
         if (ga != gc) return ga < gc;
-        return tiles[a].work > tiles[c].work;
+        return key[a] > key[c];
     });
     if (dynamic) {   // the sorted list itself; worker w starts with tile w
         for (int32_t w = 0; w <= W; ++w) worker_ptr[w] = (int32_t)std::min<size_t>(w, order.size());

@@ -32,7 +32,16 @@ plainest readings, written out step by step here, are:
                    block imin // block_m
       block-sparse sum over the 128-row mask rows m kept by any mask column
                    of the tile of ceil((min(128(m+1), Lq_b) - 128m) / block_m)
- 3. Stable sort by work, descending (ties keep enumeration order).
+ 3. Stable sort by a sort key, descending (ties keep enumeration order).
+    forward: the work.
+    backward: the tile's estimated time on the dK/dV kernel, in units of
+    one wave's share of a Q block's matrix products:
+      key = work * (BWD_BLOCK_FIXED + ceil(keys / BWD_WAVE_KEYS)) + BWD_TILE_FIXED
+    with keys = min(block_n, Lk_b - t*block_n) the tile's keys (a wave holds
+    BWD_WAVE_KEYS of them; waves without keys idle), BWD_BLOCK_FIXED the
+    per-block copy and barrier time and BWD_TILE_FIXED the tile boundary
+    (fetch of K/V, store of dK/dV), both measured on the kernel. The work
+    alone would count the partial last tile of every sequence as a full one.
  4. Deal in snake order over W workers: sorted tile i goes to worker i mod W
     when floor(i / W) is even, else to W - 1 - (i mod W).
  5. Emit worker_ptr[W+1] and, per worker in increasing i, tiles[.,4] =
@@ -195,6 +204,18 @@ def _tile_work(pass_, b, t, lq_b, lk_b, *, block_m, block_n, causal, block_mask,
     return nqb
 
 
+# backward sort key constants (see step 3)
+BWD_WAVE_KEYS = 32
+BWD_BLOCK_FIXED = 4
+BWD_TILE_FIXED = 42
+
+
+def bwd_sort_key(work, t, lk_b, block_n):
+    """Step 3's backward sort key of KV tile t with the given work."""
+    keys = min(block_n, lk_b - t * block_n)
+    return work * (BWD_BLOCK_FIXED + cdiv(keys, BWD_WAVE_KEYS)) + BWD_TILE_FIXED
+
+
 def _snake(order_len, W):
     """Worker (0..W-1) of each position of a sorted list under the snake deal."""
     out = []
@@ -250,7 +271,7 @@ def plan(q_lens, kv_lens, num_heads, num_workers, pass_, *, block_m, block_n,
     W = int(num_workers)
     if W < 1:
         raise ValueError("need at least one worker")
-    tiles = []
+    tiles, keys = [], []
     for b in range(B):
         lq_b, lk_b = int(q_lens[b]), int(kv_lens[b])
         n_t = cdiv(lq_b, block_m) if pass_ == FWD else cdiv(lk_b, block_n)
@@ -259,7 +280,8 @@ def plan(q_lens, kv_lens, num_heads, num_workers, pass_, *, block_m, block_n,
                 w = _tile_work(pass_, b, t, lq_b, lk_b, block_m=block_m, block_n=block_n,
                                causal=causal, block_mask=block_mask, window=window)
                 tiles.append((b, h, t, w))
-    order = sorted(range(len(tiles)), key=lambda i: -tiles[i][3])   # stable
+                keys.append(w if pass_ == FWD else bwd_sort_key(w, t, lk_b, block_n))
+    order = sorted(range(len(tiles)), key=lambda i: -keys[i])   # stable
     if dynamic:
         if pass_ != FWD:
             raise ValueError("dynamic plans are forward plans")

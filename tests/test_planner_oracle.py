@@ -2,8 +2,9 @@
 
 The work of a tile is re-derived from the visibility rule itself (count the
 KV blocks / Q blocks holding at least one visible (query, key) pair), and the
-deal is checked for its defining properties: every tile exactly once, work
-non-increasing along the deal order, snake assignment over the workers.
+deal is checked for its defining properties: every tile exactly once, sort
+key (work; backward: the estimated time) non-increasing along the deal order,
+snake assignment over the workers.
 """
 import numpy as np
 import pytest
@@ -69,14 +70,22 @@ def test_plan_properties(name, qlens, kvlens, causal, mask, pass_, bm, bn, worke
         order.append(got[cursor[w]])
         cursor[w] += 1
     assert np.all(cursor == wp[1:])
-    works = [r[3] for r in order]
+    def key(r):
+        if pass_ == P.FWD:
+            return r[3]
+        # backward: work x (fixed per block + waves holding one of the tile's
+        # keys) + fixed per tile, the waves counted from the keys themselves
+        keys = min(bn, kvlens[r[0]] - r[2] * bn)
+        waves = len(set(k // P.BWD_WAVE_KEYS for k in range(keys)))
+        return r[3] * (P.BWD_BLOCK_FIXED + waves) + P.BWD_TILE_FIXED
+    works = [key(r) for r in order]
     assert all(works[i] >= works[i + 1] for i in range(n - 1))
-    # stable: equal work keeps (b, h, t) enumeration order
+    # stable: equal keys keep (b, h, t) enumeration order
     for i in range(n - 1):
         if works[i] == works[i + 1]:
             assert order[i][:3] < order[i + 1][:3]
     # balance: no worker exceeds the mean by more than one largest tile
-    loads = [sum(r[3] for r in got[wp[w]:wp[w + 1]]) for w in range(workers)]
+    loads = [sum(key(r) for r in got[wp[w]:wp[w + 1]]) for w in range(workers)]
     assert max(loads) <= sum(works) / workers + (max(works) if works else 0)
 
 
@@ -262,3 +271,14 @@ def test_band_plan_work_by_brute_force(window, causal, pass_, bm, bn):
         for t in range(n_t):
             w = _brute_work(pass_, b, t, L, L, bm, bn, causal, None, window=window)
             assert got[(b, 0, t)] == w, (b, t)
+
+
+def test_bwd_sort_key_puts_partial_tiles_after_full_ones():
+    """Equal work (2 Q blocks each), unequal keys: a full 256-key tile (8 waves
+    busy) sorts before a 100-key one (4 waves) and a 44-key one (2 waves):
+    keys 2*(4+8)+42 = 66, 2*(4+4)+42 = 58, 2*(4+2)+42 = 54."""
+    lens = [100, 256, 300]
+    wp, tiles = P.plan([64] * 3, lens, 1, 1, P.BWD, block_m=32, block_n=256)
+    assert [tuple(int(v) for v in r) for r in tiles] == [(1, 0, 0, 2), (2, 0, 0, 2),
+                                                         (0, 0, 0, 2), (2, 0, 1, 2)]
+    assert [P.bwd_sort_key(2, t, L, 256) for t, L in ((0, 256), (0, 100), (1, 300))] == [66, 58, 54]
