@@ -208,6 +208,34 @@ def test_zero_width_window_is_bitwise_v():
     assert g.dk.float().abs().max().item() <= 1e-5
 
 
+@pytest.mark.parametrize("case", ["bcast_ragged_d128", "perseq_d128", "causal_d64", "sparse_d128",
+                                  "cfg2_small"])
+def test_delta_of_dq_pass_and_standalone_stage(case):
+    """delta = rowsum(dO * O) of the GPU's own bf16 O and dO, formed by the dQ
+    pass (full backward) and by the standalone preprocess stage: both within
+    fp32 summation error (D terms, each rounded at most twice: 2 D 2^-24 of
+    the sum of |dO * O|) of the fp64 sum, for every row, empty sequences
+    included."""
+    print("case", case, flush=True)
+    x = SMALL_CASES[case]()
+    g = run_gpu(x)
+    H, D = x.workload.heads, x.workload.head_dim
+    o, do = host_f64(g.o), x.as_f64("do")
+    ref = np.einsum("rhd,rhd->hr", do, o)
+    bound = 2 * D * 2.0 ** -24 * np.einsum("rhd,rhd->hr", np.abs(do), np.abs(o)) + 1e-30
+    d_dq = g.delta.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(d_dq - ref) <= bound)
+    prob = problem_of(x)
+    att = J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask)
+    out = dict(dq=g.dq, dk=g.dk, dv=g.dv, dq_accum=g.dq_accum,
+               delta=torch.full((H, att.total_q), float("nan"), dtype=torch.float32, device="cuda"))
+    att.backward(dev(x.q), dev(x.k), dev(x.v), g.o, g.lse, dev(x.do), out,
+                 stages=J.JFA_BWD_PREPROCESS)
+    torch.cuda.synchronize()
+    d_pre = out["delta"].cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(d_pre - ref) <= bound)
+
+
 def test_zero_q_gives_mean_of_v():
     x = _custom("zeroq", broadcast=True, H=1, D=64, lengths=[7, 300], lq=40)
     x = dataclasses.replace(x, q=np.zeros_like(x.q))
