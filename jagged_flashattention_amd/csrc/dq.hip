@@ -371,8 +371,12 @@ __global__ void __launch_bounds__(256) dq_reduce_kernel(DqReduceArgs a) {
         const int nw = w1 - w0;
         const int q0 = w0 + (nw * wave) / 4, q1 = w0 + (nw * (wave + 1)) / 4;
         const float* src = a.partial + (int64_t)(row % kFwdBlockM) * D + 4 * c4;
-        if (a.worker_ptr != nullptr)   // null: the plan has no tiles, dQ = 0
+        // null worker_ptr: the plan has no tiles, dQ = 0. The loads of 8
+        // partials are issued before their adds (same order of addition)
+        if (a.worker_ptr != nullptr) {
+#pragma unroll 8
             for (int wk = q0; wk < q1; ++wk) sum += *(const f32x4*)(src + (int64_t)wk * kFwdBlockM * D);
+        }
     }
     part[wave][lane] = sum;
     __syncthreads();
