@@ -189,6 +189,10 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
         }
     };
 
+    // Q^T fragments of this lane's row; with a broadcast Q every tile of the
+    // worker has the same (head, Q tile), so they are loaded once
+    bf16x8 qf[KC];
+    int qf_h = -1, qf_t = -1;
     int s = 0;   // stream position of the consumer
     for (int ti = t_begin; ti < t_end; ++ti) {
         const TileInfo T = tile_info(ti);
@@ -208,14 +212,17 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
         // Q^T and dO^T fragments, LSE (exp2 domain) and delta of this lane's
         // row (rows past the sequence read its last row; their dQ is dropped)
         const int qr = min(qrow, Lq - 1);
-        bf16x8 qf[KC], df[KC];
+        bf16x8 df[KC];
         {
-            const uint16_t* qp = a.q + (int64_t)(q0 + qr) * rs + (int64_t)T.h * D + 8 * hf;
             const uint16_t* dp = a.d_o + (int64_t)(orow0 + qr) * rs + (int64_t)T.h * D + 8 * hf;
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                qf[kc] = load_bf16x8(qp + 16 * kc);
-                df[kc] = load_bf16x8(dp + 16 * kc);
+            for (int kc = 0; kc < KC; ++kc) df[kc] = load_bf16x8(dp + 16 * kc);
+            if (!BCAST || T.h != qf_h || T.t != qf_t) {
+                const uint16_t* qp = a.q + (int64_t)(q0 + qr) * rs + (int64_t)T.h * D + 8 * hf;
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) qf[kc] = load_bf16x8(qp + 16 * kc);
+                qf_h = T.h;
+                qf_t = T.t;
             }
         }
         const float lse = a.lse[(int64_t)T.h * a.total_q + orow0 + qr];
