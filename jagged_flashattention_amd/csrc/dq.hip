@@ -41,7 +41,9 @@ struct DqLds {
     static constexpr int K = 0;                         // kSlots natural K blocks
     static constexpr int V = K + kSlots * BLK;          // kSlots natural V blocks
     static constexpr int KT = V + kSlots * BLK;         // 2 K^T blocks [D][64]
-    static constexpr int BYTES = KT + 2 * BLK;
+    static constexpr int RW = 32 * D * 2;               // one wave's 32 dO rows (tile prologue)
+    static constexpr int STG = KT + 2 * BLK;            // stage areas of waves 4-7
+    static constexpr int BYTES = STG + 4 * RW;
     static constexpr int ST_WAVE = kStageRows * D * 4;  // fp32 staging of one wave
     static_assert(4 * ST_WAVE == BLK, "staging: 4 waves per released block");
 };
@@ -212,35 +214,87 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
         // Q^T and dO^T fragments, LSE (exp2 domain) and delta of this lane's
         // row (rows past the sequence read its last row; their dQ is dropped)
         const int qr = min(qrow, Lq - 1);
-        bf16x8 df[KC];
-        {
-            const uint16_t* dp = a.d_o + (int64_t)(orow0 + qr) * rs + (int64_t)T.h * D + 8 * hf;
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc) df[kc] = load_bf16x8(dp + 16 * kc);
-            if (!BCAST || T.h != qf_h || T.t != qf_t) {
-                const uint16_t* qp = a.q + (int64_t)(q0 + qr) * rs + (int64_t)T.h * D + 8 * hf;
-#pragma unroll
-                for (int kc = 0; kc < KC; ++kc) qf[kc] = load_bf16x8(qp + 16 * kc);
-                qf_h = T.h;
-                qf_t = T.t;
-            }
-        }
         const float lse = a.lse[(int64_t)T.h * a.total_q + orow0 + qr];
-        // delta = rowsum(dO * O) of this lane's row (the standard FlashAttention
-        // backward quantity), from its half of d and the other half's lane;
-        // the tile's first chunk writes it out for the dK/dV pass
+        // delta = rowsum(dO * O) of each row (the standard FlashAttention
+        // backward quantity); the tile's first chunk writes it out for the
+        // dK/dV pass
+        bf16x8 df[KC];
         float dlt;
-        {
+        if constexpr (BCAST) {
+            // dO and O of the wave's 32 rows, fetched with row-contiguous
+            // copies (row-strided dO^T fragment loads cost the vector memory
+            // unit one cache line per row and instruction): dO into the
+            // wave's stage area (the K or V slot of block s-1, free once every
+            // wave is past it, or the spare area), O into registers in the
+            // same layout. The dO^T fragments are then read from LDS, and
+            // delta is formed in the copy layout, summed over the lanes of a
+            // row and handed to the fragment lanes through LDS. (Per-sequence
+            // Q keeps the direct loads below: its extra live Q rows would
+            // spill.)
+            __syncthreads();
+            char* rg;
+            {
+                const int fs = (s + kSlots - 1) % kSlots;
+                rg = wave < 2 ? smem + LY::K + fs * LY::BLK + wave * LY::RW
+                     : wave < 4 ? smem + LY::V + fs * LY::BLK + (wave - 2) * LY::RW
+                                : smem + LY::STG + (wave - 4) * LY::RW;
+            }
+            constexpr int NI = 32 * CH / 64;   // 16-byte copies per lane
+            bf16x8 ov[NI];
+#pragma unroll
+            for (int u = 0; u < NI; ++u) {
+                const int p = 64 * u + lane, r = p / CH, cs = p % CH;
+                const int row = min(row0 + r, Lq - 1);
+                const int64_t g = (int64_t)(orow0 + row) * rs + (int64_t)T.h * D + 8 * (cs ^ swz_kv<D>(r));
+                load_lds16(a.d_o + g, rg + 1024 * u);
+                ov[u] = load_bf16x8(a.o + g);
+            }
+            wait_vmem();
+            wave_sync_lds();
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc)
+                df[kc] = *(const bf16x8*)(rg + lr * D * 2 + (((2 * kc + hf) ^ swz_kv<D>(lr)) << 4));
+            float dsum[NI];
+#pragma unroll
+            for (int u = 0; u < NI; ++u) {
+                const bf16x8 dd = *(const bf16x8*)(rg + 1024 * u + 16 * lane);
+                float part = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) part = fmaf((float)dd[j], (float)ov[u][j], part);
+#pragma unroll
+                for (int m = CH / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m);
+                dsum[u] = part;
+            }
+            wave_sync_lds();
+            float* dl = (float*)rg;   // delta of the wave's 32 rows
+            if (lane % CH == 0) {
+#pragma unroll
+                for (int u = 0; u < NI; ++u) dl[(64 * u + lane) / CH] = dsum[u];
+            }
+            wave_sync_lds();
+            dlt = dl[lr];
+        } else {
+            // this lane's half of d of its row, then the other half's lane
+            const uint16_t* dp = a.d_o + (int64_t)(orow0 + qr) * rs + (int64_t)T.h * D + 8 * hf;
             const uint16_t* op = a.o + (int64_t)(orow0 + qr) * rs + (int64_t)T.h * D + 8 * hf;
             float part = 0.f;
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
+                df[kc] = load_bf16x8(dp + 16 * kc);
                 const bf16x8 of = load_bf16x8(op + 16 * kc);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) part = fmaf((float)df[kc][j], (float)of[j], part);
             }
             dlt = pair_sum(part);
-            if (hf == 0 && T.k0 == 0 && qrow < Lq) a.delta[(int64_t)T.h * a.total_q + orow0 + qrow] = dlt;
+        }
+        if (hf == 0 && T.k0 == 0 && qrow < Lq) a.delta[(int64_t)T.h * a.total_q + orow0 + qrow] = dlt;
+        // Q^T fragments (with a broadcast Q: once per worker)
+        if (!BCAST || T.h != qf_h || T.t != qf_t) {
+            const uint16_t* qp = a.q + (int64_t)(q0 + qr) * rs + (int64_t)T.h * D + 8 * hf;
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) qf[kc] = load_bf16x8(qp + 16 * kc);
+            qf_h = T.h;
+            qf_t = T.t;
         }
         // a row without visible keys (LSE = -inf) gets P = 0
         const float lse2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
