@@ -250,6 +250,20 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
     if (t_begin < t_end) load_kv(tile_info(t_begin));
     wait_vmem();
     __syncthreads();
+    // This wave's 32 rows of a tile's K or V (row-contiguous direct-to-LDS
+    // copies) into its own V rows, the layout load_kv gives V
+    auto copy_rows = [&](const uint16_t* src, const KvTile& T) {
+        const int64_t kvrow0 = (int64_t)T.kv0 * rs + (int64_t)T.h * D;
+        const int lane_t = opaque(lane);
+#pragma unroll
+        for (int u = 0; u < VPW; ++u) {
+            const int p = 64 * (VPW * wave + u) + lane_t;
+            const int r = p / CH, cp = p % CH;
+            const int key = min(T.n * kBwdBlockN + r, T.L - 1);
+            load_lds16(src + kvrow0 + (int64_t)key * rs + 8 * (cp ^ swz_kv<D>(r)),
+                       smem + LY::V + 1024 * (VPW * wave + u));
+        }
+    };
 
     int s = 0;   // stream position of the consumer
     for (int ti = t_begin; ti < t_end; ++ti) {
@@ -381,12 +395,18 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
         }
 
         // ---- tile end. Every wave is done with V, with block s-1's ring slot
-        // and with its transposed buffer: the next tile's V tile and K rows are
-        // fetched right away, and dK = scale * (dK^T)^T and dV leave as bf16
-        // rows through the free slot (waves 4-7) and transposed buffer (waves
-        // 0-3), 16 keys per wave at a time, meanwhile.
+        // and with its transposed buffer. dK = scale * (dK^T)^T and dV leave as
+        // bf16 rows through the free slot (waves 4-7) and transposed buffer
+        // (waves 0-3), 16 keys per wave at a time. Meanwhile each wave fetches
+        // the next tile's K rows into its own V rows with row-contiguous
+        // copies (row-strided fragment loads cost the vector memory unit one
+        // cache line per key and instruction), reads its K fragments from
+        // there once dK is out, and then fetches the next V rows in their
+        // place while dV leaves.
         __syncthreads();
-        if (ti + 1 < t_end) load_kv(tile_info(ti + 1));
+        const bool has_next = ti + 1 < t_end;
+        const KvTile NT = has_next ? tile_info(ti + 1) : T;
+        if (has_next) copy_rows(a.k, NT);
         {
             const int64_t kvrow0 = (int64_t)T.kv0 * rs + (int64_t)T.h * D;
             char* st = wave < 4 ? smem + LY::T + ((s + 1) & 1) * LY::TBUF + wave * (16 * D * 2)
@@ -394,6 +414,16 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
             const int lane_e = opaque(lane), lr_e = lane_e & 31, hf_e = lane_e >> 5;
 #pragma unroll
             for (int pass = 0; pass < 4; ++pass) {   // dK keys 0-15, 16-31, then dV
+                if (pass == 2 && has_next) {
+                    wait_vmem();   // the K rows landed (and the dK stores are done)
+                    wave_sync_lds();
+#pragma unroll
+                    for (int kc = 0; kc < KC; ++kc)
+                        kf[kc] = __builtin_bit_cast(bf16x8, *(const u32x4*)(vb + row_off(kc)));
+                    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): read before overwritten
+                    wave_sync_lds();
+                    copy_rows(a.v, NT);
+                }
                 const int rd = pass & 1;
                 if ((lr_e >> 4) == rd) {
                     const int r = lr_e & 15;
