@@ -366,3 +366,41 @@ def test_full_size_sampled_parity(cfg):
         # and the bf16 dq is the rounding of the fp32 sum
         gdq16 = host_f64(g.dq)
         assert np.abs(gdq16 - gdq).max() <= 2 ** -8 * np.abs(gdq).max()
+
+
+def test_long_sequence_sampled():
+    """One sequence of 262,181 keys (1,025 KV tiles, a dQ tile cut into 257
+    chunks per (head, Q tile)) beside an empty, a one-key and a 4,999-key
+    sequence, with a ragged broadcast Q of 300 rows (two Q tiles): O, LSE,
+    dK, dV of the long sequence and the other sequences against the oracle,
+    rows of the batch-summed dQ too."""
+    print("long sequence", flush=True)
+    x = _custom("long", broadcast=True, H=2, D=128, lengths=[262181, 0, 1, 4999], lq=300, seed=5)
+    g = run_gpu(x, canary=True)
+    w = x.workload
+    go = g.o.view(torch.int16).cpu().numpy().view(np.uint16)
+    glse = g.lse.cpu().numpy()
+    gdk = g.dk.view(torch.int16).cpu().numpy().view(np.uint16)
+    gdv = g.dv.view(torch.int16).cpu().numpy().view(np.uint16)
+    gdq = g.dq_accum.cpu().numpy()
+    h = 1
+    for b in (0, 2, 3):
+        k0, k1 = int(x.kv_offsets[b]), int(x.kv_offsets[b + 1])
+        os_ = slice(b * w.lq, (b + 1) * w.lq)
+        q1, k1_, v1 = _head_f64(x.q, h), _head_f64(x.k, h, slice(k0, k1)), _head_f64(x.v, h, slice(k0, k1))
+        do1 = _head_f64(x.do, h, os_)
+        off = np.array([0, k1 - k0], dtype=np.int32)
+        kw = dict(scale=w.scale, broadcast_q=True)
+        o, lse = A.forward(q1, k1_, v1, off, **kw)
+        _, dk, dv, _ = A.backward(q1, k1_, v1, do1, off, **kw)
+        assert np.abs(W.bf16_bits_to_f32(go[os_, h]) - o[:, 0]).max() <= TOL_O, b
+        assert np.abs(glse[h, os_] - lse[0]).max() <= TOL_O, b
+        assert rel_err(W.bf16_bits_to_f32(gdk[k0:k1, h]), dk[:, 0]) <= TOL_GRAD, b
+        assert rel_err(W.bf16_bits_to_f32(gdv[k0:k1, h]), dv[:, 0]) <= TOL_GRAD, b
+    # the empty sequence: O = 0, LSE = -inf
+    os1 = slice(w.lq, 2 * w.lq)
+    assert not W.bf16_bits_to_f32(go[os1]).any() and np.all(glse[:, os1] == -np.inf)
+    rows = np.array([0, 1, 255, 256, 299])
+    ref = A.broadcast_dq_rows(_head_f64(x.q, h), _head_f64(x.k, h), _head_f64(x.v, h),
+                              _head_f64(x.do, h), x.kv_offsets, 0, rows, scale=w.scale)
+    assert rel_err(gdq[rows, h], ref) <= TOL_GRAD
