@@ -259,7 +259,6 @@ int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, co
     if (grouped) {
         if (G > INT32_MAX / 2) return JFA_ERR_INVALID_ARG;
         if ((int64_t)nqt * max_work > INT32_MAX) return JFA_ERR_INVALID_ARG;
-        W = (int32_t)std::max<int64_t>(W, G);
         std::vector<Tile> chunks;
         chunks.reserve(tiles.size());
         max_work = 0;
@@ -276,6 +275,14 @@ int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, co
         }
         if (chunks.size() > (size_t)(INT32_MAX / 4)) return JFA_ERR_INVALID_ARG;
         tiles.swap(chunks);
+        // W' = max(G, min(W, G * n)), n the largest chunk count of a group:
+        // no group gets more workers than it has chunks
+        if (G > 0) {
+            std::vector<int64_t> per_group((size_t)G, 0);
+            for (const Tile& t : tiles) ++per_group[(size_t)((int64_t)t.h * nqt + t.t % nqt)];
+            const int64_t n = *std::max_element(per_group.begin(), per_group.end());
+            W = (int32_t)std::max<int64_t>(G, std::min<int64_t>(W, G * n));
+        }
     }
     info->pass = pass_flags;
     info->num_workers = W;

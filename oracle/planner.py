@@ -61,7 +61,9 @@ tiles: (b, h, t) with the forward work.
  * broadcast Q: every Q tile t of head h gets the contributions of all
    sequences, summed over the batch ([clarity] second paragraph). Tiles are
    grouped by g = h * ceil(Lq / block_m) + t (G groups). The plan uses
-   W' = max(W, G) workers; group g owns the contiguous workers
+   W' = max(G, min(W, G * n)) workers, n the largest number of chunks
+   (below) of any group, so that no group gets more workers than it has
+   chunks to give them (W' = W when G = 0); group g owns the contiguous workers
    [floor(g W' / G), floor((g+1) W' / G)), and its tiles (b = 0..B-1) are
    stably sorted by work, descending, and dealt in snake order over them.
    Every worker thus sums one group only, into one per-worker partial.
@@ -236,11 +238,9 @@ def plan_dq(q_lens, kv_lens, num_heads, num_workers, *, broadcast_q, lq=0, block
     G = num_heads * nqt
     if int(num_workers) < 1:
         raise ValueError("need at least one worker")
-    W = max(int(num_workers), G)
-    per_worker = [[] for _ in range(W)]
+    groups = []
     for g in range(G):
         h, t = divmod(g, nqt)
-        w0, w1 = (g * W) // G, ((g + 1) * W) // G
         tiles = []
         for b in range(B):
             w = _tile_work(FWD, b, t, int(lq), int(kv_lens[b]), block_m=block_m,
@@ -251,6 +251,14 @@ def plan_dq(q_lens, kv_lens, num_heads, num_workers, *, broadcast_q, lq=0, block
                 length = w // n + (1 if c < w % n else 0)
                 tiles.append((b, h, t + nqt * k0, length))
                 k0 += length
+        groups.append(tiles)
+    W = int(num_workers)
+    if G > 0:
+        W = max(G, min(W, G * max(len(tl) for tl in groups)))
+    per_worker = [[] for _ in range(W)]
+    for g in range(G):
+        w0, w1 = (g * W) // G, ((g + 1) * W) // G
+        tiles = groups[g]
         order = sorted(range(len(tiles)), key=lambda i: -tiles[i][3])   # stable
         owner = _snake(len(order), w1 - w0)
         for i, ti in enumerate(order):

@@ -201,7 +201,11 @@ def test_dq_plan_grouped(workers, lq):
                           block_m=bm, block_n=bn)
     nqt = P.cdiv(lq, bm)
     G = H * nqt
-    Wp = max(workers, G)
+    # W' = max(G, min(W, G * n)), n the largest chunk count of a group (every
+    # group holds the same B sequences here, so all counts are equal)
+    n_g = sum(max(1, P.cdiv(_brute_work(P.FWD, b, 0, lq, int(lens[b]), bm, bn, False, None),
+                              P.DQ_CHUNK)) for b in range(11)) if G else 0
+    Wp = max(G, min(workers, G * n_g)) if G else workers
     assert len(wp) == Wp + 1
     got = [tuple(int(x) for x in r) for r in tiles]
     assert len(got) == len(set(got))
@@ -282,3 +286,20 @@ def test_bwd_sort_key_puts_partial_tiles_after_full_ones():
     assert [tuple(int(v) for v in r) for r in tiles] == [(1, 0, 0, 2), (2, 0, 0, 2),
                                                          (0, 0, 0, 2), (2, 0, 1, 2)]
     assert [P.bwd_sort_key(2, t, L, 256) for t, L in ((0, 256), (0, 100), (1, 300))] == [66, 58, 54]
+
+
+def test_dq_plan_workers_capped_by_chunks():
+    """A small broadcast-Q problem gets no more dQ workers than its groups
+    have chunks: 2 heads x 2 Q tiles, 3 sequences of one chunk each ->
+    W' = 4 * 3 = 12 of the 256 asked for; with more chunks than workers
+    per group, W' is the request (or G if larger)."""
+    wp, tiles = P.plan_dq([300] * 3, [10, 0, 64], 2, 256, broadcast_q=True, lq=300,
+                          block_m=256, block_n=64)
+    assert len(wp) == 13 and len(tiles) == 12
+    assert all(wp[w + 1] - wp[w] == 1 for w in range(12))
+    wp, _ = P.plan_dq([300] * 3, [5000, 4000, 64], 2, 8, broadcast_q=True, lq=300,
+                      block_m=256, block_n=64)
+    assert len(wp) == 9
+    wp, _ = P.plan_dq([300] * 3, [5000, 4000, 64], 2, 3, broadcast_q=True, lq=300,
+                      block_m=256, block_n=64)
+    assert len(wp) == 5
