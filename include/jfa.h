@@ -153,7 +153,8 @@ int32_t jfa_offsets_from_lengths(const int32_t* h_lengths, int32_t batch, int32_
  * DQ: the FWD tiles and work. With per-sequence Q the deal is the FWD deal.
  * With broadcast Q (every tile (b, h, t) adds into the same dQ rows of head
  * h), the G = H * ceil(lq/256) groups g = h * ceil(lq/256) + t get disjoint
- * worker ranges [g W'/G, (g+1) W'/G) of W' = max(W, G) workers, and each
+ * worker ranges [g W'/G, (g+1) W'/G) of W' = max(G, min(W, G n)) workers (n the
+ * largest number of chunks, below, of any group; W' = W when G = 0), and each
  * group's tiles are sorted and snake-dealt over its own range, so that every
  * worker sums one group only (one partial per worker). Since those partials
  * are summed anyway, a broadcast-Q DQ tile of more than 16 blocks is first

@@ -248,7 +248,8 @@ int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, co
     }
 
     // dQ pass with broadcast Q: tiles grouped by (head, Q tile); group g owns
-    // the workers [g W' / G, (g+1) W' / G) of W' = max(W, G) workers. A tile
+    // the workers [g W' / G, (g+1) W' / G) of W' = max(G, min(W, G n)) workers
+    // (n: the largest chunk count of a group, counted below). A tile
     // of w > kDqChunkBlocks blocks is split into n = ceil(w / kDqChunkBlocks)
     // chunks of consecutive list positions, the first (w mod n) one block
     // longer; a chunk starting at position k0 is stored with t + nqt * k0 in
