@@ -403,10 +403,16 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
         // cache line per key and instruction), reads its K fragments from
         // there once dK is out, and then fetches the next V rows in their
         // place while dV leaves.
+        // (The banded mode keeps the direct K loads: the staged form spills
+        // there.)
         __syncthreads();
+        constexpr bool kStageK = MODE != kCausal;
         const bool has_next = ti + 1 < t_end;
         const KvTile NT = has_next ? tile_info(ti + 1) : T;
-        if (has_next) copy_rows(a.k, NT);
+        if (has_next) {
+            if (kStageK) copy_rows(a.k, NT);
+            else load_kv(NT);
+        }
         {
             const int64_t kvrow0 = (int64_t)T.kv0 * rs + (int64_t)T.h * D;
             char* st = wave < 4 ? smem + LY::T + ((s + 1) & 1) * LY::TBUF + wave * (16 * D * 2)
@@ -414,7 +420,7 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
             const int lane_e = opaque(lane), lr_e = lane_e & 31, hf_e = lane_e >> 5;
 #pragma unroll
             for (int pass = 0; pass < 4; ++pass) {   // dK keys 0-15, 16-31, then dV
-                if (pass == 2 && has_next) {
+                if (kStageK && pass == 2 && has_next) {
                     wait_vmem();   // the K rows landed (and the dK stores are done)
                     wave_sync_lds();
 #pragma unroll
