@@ -81,65 +81,74 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* __restr
     scales[((int64_t)h * rows + row) * nb + blk] = (uint8_t)(e + 127);
 }
 
-// One workgroup per (sequence, head). Thread (j, g) encodes d = 8g .. 8g+7 of
-// the sequence's 32-key blocks j, j+16, ...: it holds the block's 32 rows of
-// those 8 d in registers, takes the 8 column maxima, and writes 8 bytes of
-// codes per row and the 8 scale codes. Codes [T_k, H, D], scales [H, NB, D].
-constexpr int kVThreads = 256;
-__global__ void __launch_bounds__(kVThreads) quant_v_kernel(const uint16_t* __restrict__ v,
-                                                            const int32_t* __restrict__ kv_off,
-                                                            const int32_t* __restrict__ boff, int32_t H,
-                                                            int32_t D, int32_t nbt, uint8_t* __restrict__ codes,
-                                                            uint8_t* __restrict__ scales) {
-    const int b = blockIdx.x / H, h = blockIdx.x % H;
-    const int groups = D / 8, slots = kVThreads / groups;
-    const int g = threadIdx.x % groups, j = threadIdx.x / groups;
-    if (j >= slots) return;
-    const int k0 = kv_off[b], L = kv_off[b + 1] - k0, b0 = boff[b];
+// One thread per (32-key block j of the batch, head h, 8 columns g): it finds
+// its sequence by binary search over the block offsets, holds the block's
+// 32 rows of its 8 columns in registers, takes the column maxima, and writes
+// 8 bytes of codes per row and the 8 scale codes. Consecutive threads take
+// consecutive columns, then heads, so a wave reads whole key rows. Codes
+// [T_k, H, D], scales [H, NB, D].
+__global__ void __launch_bounds__(256) quant_v_kernel(const uint16_t* __restrict__ v,
+                                                      const int32_t* __restrict__ kv_off,
+                                                      const int32_t* __restrict__ boff, int32_t B, int32_t H,
+                                                      int32_t D, int32_t nbt, uint8_t* __restrict__ codes,
+                                                      uint8_t* __restrict__ scales) {
+    const int groups = D / 8;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)nbt * H * groups) return;
+    const int g = (int)(idx % groups);
+    const int h = (int)((idx / groups) % H);
+    const int j = (int)(idx / ((int64_t)groups * H));
+    // the last sequence b with boff[b] <= j (its blocks [boff[b], boff[b+1]) hold j)
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (boff[mid] <= j) lo = mid;
+        else hi = mid - 1;
+    }
+    const int b = lo, blk = j - boff[b];
+    const int k0 = kv_off[b], L = kv_off[b + 1] - k0;
+    const int n = min(32, L - 32 * blk);
     const int64_t rs = (int64_t)H * D;
-    for (int blk = j; 32 * blk < L; blk += slots) {
-        const int n = min(32, L - 32 * blk);
-        const int64_t base = (int64_t)(k0 + 32 * blk) * rs + (int64_t)h * D + 8 * g;
-        u32x4 x[32];
+    const int64_t base = (int64_t)(k0 + 32 * blk) * rs + (int64_t)h * D + 8 * g;
+    u32x4 x[32];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) x[i] = i < n ? *(const u32x4*)(v + base + i * rs) : u32x4{0, 0, 0, 0};
-        // column maxima of |x| on the bf16 bits (sign cleared; bf16 magnitudes
-        // order like their bit patterns)
-        uint32_t m[4] = {0, 0, 0, 0};
+    for (int i = 0; i < 32; ++i) x[i] = i < n ? *(const u32x4*)(v + base + i * rs) : u32x4{0, 0, 0, 0};
+    // column maxima of |x| on the bf16 bits (sign cleared; bf16 magnitudes
+    // order like their bit patterns)
+    uint32_t m[4] = {0, 0, 0, 0};
 #pragma unroll
-        for (int i = 0; i < 32; ++i)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint32_t a = x[i][c] & 0x7FFF7FFFu;
-                m[c] = max(m[c] & 0xFFFFu, a & 0xFFFFu) | (max(m[c] >> 16, a >> 16) << 16);
-            }
-        int e[8];
+    for (int i = 0; i < 32; ++i)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            e[2 * c] = block_exp(bf16_to_f32((uint16_t)(m[c] & 0xFFFF)));
-            e[2 * c + 1] = block_exp(bf16_to_f32((uint16_t)(m[c] >> 16)));
+            const uint32_t a = x[i][c] & 0x7FFF7FFFu;
+            m[c] = max(m[c] & 0xFFFFu, a & 0xFFFFu) | (max(m[c] >> 16, a >> 16) << 16);
         }
+    int e[8];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            if (i < n) {
-                uint32_t w[2];
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const uint32_t lo = x[i][2 * q], hi = x[i][2 * q + 1];
-                    int p = pack2_e<false>(bf16_to_f32((uint16_t)(lo & 0xFFFF)), bf16_to_f32((uint16_t)(lo >> 16)),
-                                           e[4 * q], e[4 * q + 1], 0);
-                    p = pack2_e<true>(bf16_to_f32((uint16_t)(hi & 0xFFFF)), bf16_to_f32((uint16_t)(hi >> 16)),
-                                      e[4 * q + 2], e[4 * q + 3], p);
-                    w[q] = (uint32_t)p;
-                }
-                *(uint2*)(codes + base + i * rs) = make_uint2(w[0], w[1]);
-            }
-        }
-        uint32_t sc[2] = {0, 0};
-#pragma unroll
-        for (int c = 0; c < 8; ++c) sc[c >> 2] |= (uint32_t)(e[c] + 127) << (8 * (c & 3));
-        *(uint2*)(scales + ((int64_t)h * nbt + b0 + blk) * D + 8 * g) = make_uint2(sc[0], sc[1]);
+    for (int c = 0; c < 4; ++c) {
+        e[2 * c] = block_exp(bf16_to_f32((uint16_t)(m[c] & 0xFFFF)));
+        e[2 * c + 1] = block_exp(bf16_to_f32((uint16_t)(m[c] >> 16)));
     }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        if (i < n) {
+            uint32_t w[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const uint32_t lo_ = x[i][2 * q], hi_ = x[i][2 * q + 1];
+                int p = pack2_e<false>(bf16_to_f32((uint16_t)(lo_ & 0xFFFF)), bf16_to_f32((uint16_t)(lo_ >> 16)),
+                                       e[4 * q], e[4 * q + 1], 0);
+                p = pack2_e<true>(bf16_to_f32((uint16_t)(hi_ & 0xFFFF)), bf16_to_f32((uint16_t)(hi_ >> 16)),
+                                  e[4 * q + 2], e[4 * q + 3], p);
+                w[q] = (uint32_t)p;
+            }
+            *(uint2*)(codes + base + i * rs) = make_uint2(w[0], w[1]);
+        }
+    }
+    uint32_t sc[2] = {0, 0};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) sc[c >> 2] |= (uint32_t)(e[c] + 127) << (8 * (c & 3));
+    *(uint2*)(scales + ((int64_t)h * nbt + j) * D + 8 * g) = make_uint2(sc[0], sc[1]);
 }
 
 }  // namespace
@@ -156,9 +165,10 @@ int32_t launch_mx_quant_rows(const uint16_t* src, int64_t rows, int32_t H, int32
 int32_t launch_mx_quant_v(const uint16_t* v, const int32_t* kv_off, const int32_t* boff, int32_t B,
                           int32_t H, int32_t D, int32_t nbt, uint8_t* codes, uint8_t* scales,
                           void* stream) {
-    if (B == 0) return 0;
-    hipLaunchKernelGGL(quant_v_kernel, dim3((unsigned)(B * H)), dim3(kVThreads), 0, (hipStream_t)stream, v,
-                       kv_off, boff, H, D, nbt, codes, scales);
+    const int64_t n = (int64_t)nbt * H * (D / 8);
+    if (B == 0 || n == 0) return 0;
+    hipLaunchKernelGGL(quant_v_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, v,
+                       kv_off, boff, B, H, D, nbt, codes, scales);
     return (int32_t)hipGetLastError();
 }
 
