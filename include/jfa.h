@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define JFA_ABI_VERSION 6
+#define JFA_ABI_VERSION 7
 
 /* status codes */
 #define JFA_OK                 0
@@ -330,6 +330,51 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device
                        const void* o, const float* lse, const void* d_o,
                        void* dq, void* dk, void* dv, float* dq_accum, float* delta,
                        void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * MXFP8 dQ pass ("TLX porta l'attenzione jagged su Blackwell" (ai-radar.it),
+ * section "The turning point": the MXFP8 version of the kernel; its backward,
+ * here the dQ pass): the JFA_BWD_DQ stage with its three products as
+ * block-scaled FP8 MFMAs (head_dim 128):
+ *   S  = Q K^T    Q and K encoded along d (the MXFP8 forward's encodings),
+ *   dP = dO V^T   dO and V encoded along d (jfa_mx_quantize_rows),
+ *   dQ += dS K    K encoded along the keys of its sequence in 32-key blocks
+ *                 (jfa_mx_quantize_v applied to K), and dS = P (dP - delta)
+ *                 rounded to E4M3 on the fly with one E8M0 scale per (query
+ *                 row, 32-key block): the smallest power of two 2^e with
+ *                 max|dS| / 2^e <= 448, so no value is clamped (a block below
+ *                 2^-100 is sent as zeros).
+ * P = exp(S - LSE) and dS are fp32; delta = rowsum(dO * O) is formed from the
+ * bf16 dO and O and written out, as by JFA_BWD_DQ. Outputs as JFA_BWD_DQ:
+ * per-sequence Q: dq and dq_accum; broadcast Q: the per-worker partials in
+ * the workspace (same size as jfa_bwd's), which jfa_bwd_stages with
+ * JFA_BWD_DQ_REDUCE turns into dq_accum and dq. The dK/dV pass stays bf16
+ * (jfa_bwd_stages with JFA_BWD_DKDV after this call, which needs delta).
+ * Layouts: codes [rows, H, D] and scales [H, rows, D/32] for the operands
+ * encoded along d (rows: lq or T_q for Q, T_k for K and V, T_q for dO); K
+ * along keys: codes [T_k, H, D], scales [H, NB, D] with the blocks of
+ * sequence b starting at d_key_block_offsets[b] (device copy of
+ * jfa_mx_block_offsets' output, NB = num_key_blocks). Scale arrays 4-byte
+ * aligned, codes 16-byte aligned; the caller owns everything.
+ */
+typedef struct jfa_mx_bwd_operands {
+    const void* q_codes;
+    const void* q_scales;
+    const void* k_codes;
+    const void* k_scales;
+    const void* v_codes;
+    const void* v_scales;
+    const void* do_codes;
+    const void* do_scales;
+    const void* kk_codes;     /* K along keys */
+    const void* kk_scales;
+} jfa_mx_bwd_operands;
+int32_t jfa_bwd_dq_mx(const jfa_problem* prob, const jfa_device_plan* dq_plan,
+                      const int32_t* d_q_offsets, const int32_t* d_kv_offsets,
+                      const int32_t* d_key_block_offsets, int32_t num_key_blocks,
+                      const void* o, const float* lse, const void* d_o,
+                      const jfa_mx_bwd_operands* ops, void* dq, float* dq_accum, float* delta,
+                      void* workspace, int64_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -34,7 +34,7 @@ EXPORTS = (
     "jfa_abi_version", "jfa_status_string", "jfa_last_hip_error", "jfa_device_workers",
     "jfa_offsets_from_lengths", "jfa_plan_query", "jfa_plan_build", "jfa_fwd_workspace_bytes",
     "jfa_fwd", "jfa_bwd_workspace_bytes", "jfa_bwd", "jfa_bwd_stages", "jfa_mx_block_offsets",
-    "jfa_mx_quantize_rows", "jfa_mx_quantize_v", "jfa_fwd_mx",
+    "jfa_mx_quantize_rows", "jfa_mx_quantize_v", "jfa_fwd_mx", "jfa_bwd_dq_mx",
 )
 JFA_BWD_PREPROCESS = 1
 JFA_BWD_DQ = 2
@@ -65,6 +65,12 @@ class JfaDevicePlan(ctypes.Structure):
     _fields_ = [("info", ctypes.POINTER(JfaPlanInfo)), ("worker_ptr", ctypes.c_void_p),
                 ("tiles", ctypes.c_void_p), ("sparse_ptr", ctypes.c_void_p),
                 ("sparse_idx", ctypes.c_void_p)]
+
+
+class JfaMxBwdOperands(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "q_codes", "q_scales", "k_codes", "k_scales", "v_codes", "v_scales", "do_codes",
+        "do_scales", "kk_codes", "kk_scales")]
 
 
 class JfaError(RuntimeError):
@@ -109,6 +115,8 @@ def _lib():
             "jfa_mx_quantize_rows": (i32, [_P, i64, i32, i32, _P, _P, _P]),
             "jfa_mx_quantize_v": (i32, [_P, _P, _P, i32, i32, i32, i32, _P, _P, _P]),
             "jfa_fwd_mx": (i32, [prob, info] + [_P] * 7 + [i32] + [_P] * 9 + [i64, _P]),
+            "jfa_bwd_dq_mx": (i32, [prob, dplan, _P, _P, _P, i32, _P, _P, _P,
+                                    ctypes.POINTER(JfaMxBwdOperands), _P, _P, _P, _P, i64, _P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -305,6 +313,23 @@ def jfa_bwd_stages(stages: int, prob: Problem, kv_plan: DevicePlan, dq_plan: Dev
 
 # ------------------------------------------------------------------ MXFP8
 
+def jfa_bwd_dq_mx(prob: Problem, dq_plan: DevicePlan, q_offsets, kv_offsets, key_block_offsets,
+                  num_key_blocks, o, lse, d_o, ops: dict, dq, dq_accum, delta, workspace=None,
+                  workspace_bytes: int = 0, stream=None) -> None:
+    """Enqueue the MXFP8 dQ pass (operands: qc/qs, kc/ks, vdc/vds, doc/dos,
+    kkc/kks device tensors as produced by JaggedAttention.quantize_mx_bwd)."""
+    cp = prob.c()
+    qp = _c_plan(dq_plan)
+    mo = JfaMxBwdOperands(*[_dev_ptr(ops[n]) for n in (
+        "qc", "qs", "kc", "ks", "vdc", "vds", "doc", "dos", "kkc", "kks")])
+    _check(_lib().jfa_bwd_dq_mx(ctypes.byref(cp), ctypes.byref(qp), _dev_ptr(q_offsets),
+                                _dev_ptr(kv_offsets), _dev_ptr(key_block_offsets),
+                                int(num_key_blocks), _dev_ptr(o), _dev_ptr(lse), _dev_ptr(d_o),
+                                ctypes.byref(mo), _dev_ptr(dq), _dev_ptr(dq_accum), _dev_ptr(delta),
+                                _dev_ptr(workspace), int(workspace_bytes), _stream(stream)),
+           "jfa_bwd_dq_mx")
+
+
 def jfa_mx_block_offsets(kv_offsets) -> np.ndarray:
     """First V scale block of each sequence (prefix sums of ceil(L_b / 32))."""
     ko = _i32(kv_offsets)
@@ -429,6 +454,42 @@ class JaggedAttention:
                    self.v_num_blocks, mxq["qc"], mxq["qs"], mxq["kc"], mxq["ks"], mxq["vc"],
                    mxq["vs"], o, lse, self.fwd_workspace, self.fwd_ws_bytes)
         return o, lse
+
+    def quantize_mx_bwd(self, mxq, k, v, d_o):
+        """The further MXFP8 encodings of the MXFP8 dQ pass: V and dO along d,
+        K along the keys of its sequence (added to quantize_mx's dict)."""
+        import torch
+        H, D = self.prob.num_heads, self.prob.head_dim
+        u8 = dict(dtype=torch.uint8, device=self.device)
+        ops = dict(mxq)
+        ops.update(vdc=torch.empty(v.shape, **u8), vds=torch.empty((H, v.shape[0], D // 32), **u8),
+                   doc=torch.empty(d_o.shape, **u8),
+                   dos=torch.empty((H, d_o.shape[0], D // 32), **u8),
+                   kkc=torch.empty(k.shape, **u8),
+                   kks=torch.empty((H, max(self.v_num_blocks, 1), D), **u8))
+        jfa_mx_quantize_rows(v, ops["vdc"], ops["vds"])
+        jfa_mx_quantize_rows(d_o, ops["doc"], ops["dos"])
+        jfa_mx_quantize_v(k, self.kv_offsets, self.v_block_offsets, self.v_num_blocks, ops["kkc"],
+                          ops["kks"])
+        return ops
+
+    def backward_mx(self, q, k, v, o, lse, d_o, ops, out=None, stages=JFA_BWD_ALL):
+        """Backward with the MXFP8 dQ pass (in place of JFA_BWD_DQ) and the
+        bf16 dK/dV pass and dQ reduce, for the stages selected."""
+        import torch
+        if out is None:
+            out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+                       dq_accum=torch.empty(q.shape, dtype=torch.float32, device=self.device),
+                       delta=torch.empty((self.prob.num_heads, self.total_q), dtype=torch.float32,
+                                         device=self.device))
+        if stages & JFA_BWD_DQ:
+            jfa_bwd_dq_mx(self.prob, self.dq_plan, self.q_offsets, self.kv_offsets,
+                          self.v_block_offsets, self.v_num_blocks, o, lse, d_o, ops, out["dq"],
+                          out["dq_accum"], out["delta"], self.workspace, self.ws_bytes)
+        rest = stages & ~JFA_BWD_DQ
+        if rest:
+            self.backward(q, k, v, o, lse, d_o, out, stages=rest)
+        return out
 
     def backward(self, q, k, v, o, lse, d_o, out=None, stages=JFA_BWD_ALL):
         import torch

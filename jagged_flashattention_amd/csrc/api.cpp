@@ -394,6 +394,78 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device
     return JFA_OK;
 }
 
+int32_t jfa_bwd_dq_mx(const jfa_problem* prob, const jfa_device_plan* dq_plan,
+                      const int32_t* d_q_offsets, const int32_t* d_kv_offsets,
+                      const int32_t* d_key_block_offsets, int32_t num_key_blocks, const void* o,
+                      const float* lse, const void* d_o, const jfa_mx_bwd_operands* ops, void* dq,
+                      float* dq_accum, float* delta, void* workspace, int64_t workspace_bytes,
+                      void* stream) {
+    int32_t st = check_plan(prob, dq_plan, JFA_PASS_DQ, d_q_offsets, d_kv_offsets);
+    if (st) return st;
+    if (prob->head_dim != 128) return JFA_ERR_UNSUPPORTED;
+    const jfa_plan_info* qi = dq_plan->info;
+    int64_t need = 0;
+    st = jfa_bwd_workspace_bytes(prob, qi, &need);
+    if (st) return st;
+    if (workspace_bytes < need || (need > 0 && (workspace == nullptr || !aligned16(workspace))))
+        return JFA_ERR_WORKSPACE;
+    const bool bcast = prob->broadcast_q != 0;
+    const int64_t hd = (int64_t)prob->num_heads * prob->head_dim;
+    const int64_t q_rows = bcast ? prob->lq : qi->total_q;
+    if (ops == nullptr || d_key_block_offsets == nullptr || num_key_blocks < (qi->total_kv + 31) / 32)
+        return JFA_ERR_INVALID_ARG;
+    if (!tensor_ok(o, qi->total_q * hd) || !tensor_ok(d_o, qi->total_q * hd) || lse == nullptr ||
+        delta == nullptr || !tensor_ok(ops->q_codes, q_rows * hd) ||
+        !tensor_ok(ops->k_codes, qi->total_kv * hd) || !tensor_ok(ops->v_codes, qi->total_kv * hd) ||
+        !tensor_ok(ops->do_codes, qi->total_q * hd) || !tensor_ok(ops->kk_codes, qi->total_kv * hd))
+        return JFA_ERR_INVALID_ARG;
+    const void* scs[5] = {ops->q_scales, ops->k_scales, ops->v_scales, ops->do_scales, ops->kk_scales};
+    for (const void* p : scs)
+        if (p == nullptr || !aligned4(p)) return JFA_ERR_INVALID_ARG;
+    if (!bcast && (!tensor_ok(dq, qi->total_q * hd) || dq_accum == nullptr)) return JFA_ERR_INVALID_ARG;
+    if (qi->num_tiles == 0) return JFA_OK;
+    const jfa::Band bd = jfa::band_of(prob);
+    jfa::DqArgs d{};
+    d.worker_ptr = dq_plan->worker_ptr;
+    d.tiles = dq_plan->tiles;
+    d.sp_ptr = dq_plan->sparse_ptr;
+    d.sp_idx = dq_plan->sparse_idx;
+    d.q_off = bcast ? nullptr : d_q_offsets;
+    d.kv_off = d_kv_offsets;
+    d.d_o = static_cast<const uint16_t*>(d_o);
+    d.o = static_cast<const uint16_t*>(o);
+    d.lse = lse;
+    d.delta = delta;
+    d.dq = static_cast<uint16_t*>(dq);
+    d.dq_accum = dq_accum;
+    d.partial = static_cast<float*>(workspace);
+    d.chunk_div = bcast ? (prob->lq + jfa::kFwdBlockM - 1) / jfa::kFwdBlockM : 0;
+    d.win_left = bd.left;
+    d.win_right = bd.right;
+    d.num_heads = prob->num_heads;
+    d.lq = prob->lq;
+    d.total_q = qi->total_q;
+    d.mask_q_blocks = prob->mask_q_blocks;
+    d.num_workers = qi->num_workers;
+    d.scale = prob->softmax_scale;
+    d.scale_log2 = prob->softmax_scale * 1.4426950408889634f;
+    d.q8 = static_cast<const uint8_t*>(ops->q_codes);
+    d.q_sc = static_cast<const uint8_t*>(ops->q_scales);
+    d.k8 = static_cast<const uint8_t*>(ops->k_codes);
+    d.k_sc = static_cast<const uint8_t*>(ops->k_scales);
+    d.v8 = static_cast<const uint8_t*>(ops->v_codes);
+    d.v_sc = static_cast<const uint8_t*>(ops->v_scales);
+    d.do8 = static_cast<const uint8_t*>(ops->do_codes);
+    d.do_sc = static_cast<const uint8_t*>(ops->do_scales);
+    d.kk8 = static_cast<const uint8_t*>(ops->kk_codes);
+    d.kk_sc = static_cast<const uint8_t*>(ops->kk_scales);
+    d.kk_boff = d_key_block_offsets;
+    d.kk_nb = num_key_blocks;
+    d.q_rows = (int32_t)q_rows;
+    d.total_kv = qi->total_kv;
+    return hip_status(jfa::launch_dq_mx(d, mode_of(prob), bcast, stream));
+}
+
 int32_t jfa_bwd(const jfa_problem* prob, const jfa_device_plan* kv_plan,
                 const jfa_device_plan* dq_plan, const int32_t* d_q_offsets,
                 const int32_t* d_kv_offsets, const void* q, const void* k, const void* v,

@@ -132,6 +132,21 @@ struct DqArgs {
     int32_t num_workers;
     float scale;
     float scale_log2;
+    // MXFP8 dQ pass (head_dim 128): E4M3 codes and E8M0 scale codes
+    const uint8_t* q8;       // Q along d: [q_rows, H, D], scales [H, q_rows, D/32]
+    const uint8_t* q_sc;
+    const uint8_t* k8;       // K along d: [T_k, H, D], scales [H, T_k, D/32]
+    const uint8_t* k_sc;
+    const uint8_t* v8;       // V along d: [T_k, H, D], scales [H, T_k, D/32]
+    const uint8_t* v_sc;
+    const uint8_t* do8;      // dO along d: [T_q, H, D], scales [H, T_q, D/32]
+    const uint8_t* do_sc;
+    const uint8_t* kk8;      // K along keys: [T_k, H, D], scales [H, NB, D]
+    const uint8_t* kk_sc;
+    const int32_t* kk_boff;  // first 32-key block of each sequence [B+1]
+    int32_t kk_nb;           // NB
+    int32_t q_rows;
+    int32_t total_kv;
 };
 
 // Deterministic sum of the broadcast-Q dQ partials of each (head, Q tile)
@@ -153,6 +168,7 @@ int32_t launch_bwd(const BwdArgs& a, int32_t head_dim, Mode mode, bool broadcast
                    void* stream);
 int32_t launch_dq(const DqArgs& a, int32_t head_dim, Mode mode, bool broadcast, void* stream);
 int32_t launch_dq_reduce(const DqReduceArgs& a, int32_t head_dim, void* stream);
+int32_t launch_dq_mx(const DqArgs& a, Mode mode, bool broadcast, void* stream);
 int32_t launch_mx_quant_rows(const uint16_t* src, int64_t rows, int32_t H, int32_t D, uint8_t* codes,
                              uint8_t* scales, void* stream);
 int32_t launch_mx_quant_v(const uint16_t* v, const int32_t* kv_off, const int32_t* boff, int32_t B,

@@ -148,3 +148,57 @@ def dequantize_v(codes, scales, kv_offsets):
             s = np.ldexp(1.0, scales[:, boff[b] + j, :].astype(np.int64) - E8M0_BIAS)   # [H, D]
             out[s0:s1] *= s[None]
     return out
+
+
+def dq_mx(q_d, k_d, v_d, do_d, k_keys, do, o, lse, kv_offsets, *, scale, broadcast_q,
+          q_offsets=None, causal=False, block_mask=None, window=None):
+    """What the MXFP8 dQ pass computes, with dS kept exact (the kernel rounds
+    it to E4M3 per (row, 32-key tile); tests bound that rounding).
+
+    Per sequence and head, with every operand float64 and already decoded:
+      S     = scale * q_d k_d^T          (Q and K encoded along d)
+      P     = exp(S - lse) on visible keys, 0 elsewhere (lse given: the
+              forward's)
+      delta = rowsum(do * o)             (the bf16 dO and O)
+      dP    = do_d v_d^T                 (dO and V encoded along d)
+      dS    = P (dP - delta)
+      dQ   += scale * dS k_keys          (K encoded along keys)
+    the broadcast dQ summing over sequences. Returns (dq, delta, abs_sum,
+    floor_sum): abs_sum = scale * |dS| |k_keys| and floor_sum = scale *
+    max_j |dS_ij| * sum_j |k_keys_j| (per sequence), the two terms a bound on
+    dS's rounding needs."""
+    import oracle.attention as A
+    B = len(kv_offsets) - 1
+    H = k_d.shape[1]
+    if broadcast_q:
+        lq = q_d.shape[0]
+        t_q = B * lq
+    else:
+        t_q = int(q_offsets[-1])
+    dq = np.zeros(q_d.shape)
+    abs_sum = np.zeros(q_d.shape)
+    floor_sum = np.zeros(q_d.shape)
+    delta = np.zeros((H, t_q))
+    for b in range(B):
+        k0, k1 = int(kv_offsets[b]), int(kv_offsets[b + 1])
+        if broadcast_q:
+            qs, os_ = slice(0, lq), slice(b * lq, (b + 1) * lq)
+        else:
+            qs = os_ = slice(int(q_offsets[b]), int(q_offsets[b + 1]))
+        n_rows = qs.stop - qs.start
+        vis = A.visibility(n_rows, k1 - k0, causal=causal, window=window,
+                           mask_b=None if block_mask is None else block_mask[b])
+        for h in range(H):
+            lse_b = lse[h, os_]
+            fin = np.isfinite(lse_b)
+            s = scale * (q_d[qs, h] @ k_d[k0:k1, h].T)
+            p = np.where(vis & fin[:, None], np.exp(s - np.where(fin, lse_b, 0.0)[:, None]), 0.0)
+            dl = np.sum(do[os_, h] * o[os_, h], axis=1)
+            ds = p * (do_d[os_, h] @ v_d[k0:k1, h].T - dl[:, None])
+            kk = k_keys[k0:k1, h]
+            dq[qs, h] += scale * (ds @ kk)
+            abs_sum[qs, h] += scale * (np.abs(ds) @ np.abs(kk))
+            amax = np.abs(ds).max(axis=1, initial=0.0)
+            floor_sum[qs, h] += scale * amax[:, None] * np.abs(kk).sum(axis=0)[None, :]
+            delta[h, os_] = dl
+    return dq, delta, abs_sum, floor_sum

@@ -28,7 +28,7 @@ if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
 import jagged_flashattention_amd as J  # noqa: E402
-from test_gpu_parity import SMALL_CASES, _custom, dev, problem_of  # noqa: E402
+from test_gpu_parity import SMALL_CASES, _custom, dev, host_f64, problem_of  # noqa: E402
 
 
 def _u8(t):
@@ -177,3 +177,70 @@ def test_mx_rejects_unsupported_head_dim():
         mxq = att.quantize_mx(dev(x.q), dev(x.k), dev(x.v))
         att.forward_mx(mxq)
     assert e.value.status == J.JFA_ERR_UNSUPPORTED
+
+
+MXB_CASES = ["bcast_ragged_d128", "perseq_d128", "causal_d128", "sparse_d128", "window_band_d128",
+             "cfg2_small", "cfg3_small", "cfg5_small"]
+
+
+def _f64(bits):
+    return W.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+@pytest.mark.parametrize("case", MXB_CASES)
+def test_mx_dq_pass(case):
+    """The MXFP8 dQ pass against the oracle's definition of it (exact dS) on
+    the oracle's own O and LSE: the GPU rounds dS to E4M3 with one scale per
+    (row, 32-key tile) 2^e, the smallest power of two with max|dS| / 2^e <=
+    448 (so 2^e <= max|dS| 2^-7 and nothing is clamped); per element
+
+      |dQ_gpu - dQ| <= scale sum_j (2^-4 |dS_ij| + 2^-17 max_j' |dS_ij'|) |k_jd|
+                       + 1e-4 scale sum_j |dS_ij| |k_jd| + 1e-6
+
+    (half an E4M3 step: relative 2^-4 in the normal range, at most 2^-10 2^e
+    below it; and fp32 sums), and delta within fp32 summation error."""
+    print("case", case, flush=True)
+    x = SMALL_CASES[case]()
+    w = x.workload
+    off = x.kv_offsets
+    qf, kf, vf, dof = _f64(x.q), _f64(x.k), _f64(x.v), _f64(x.do)
+    q_d = OMX.dequantize_rows(*OMX.quantize_rows(qf))
+    k_d = OMX.dequantize_rows(*OMX.quantize_rows(kf))
+    v_d = OMX.dequantize_rows(*OMX.quantize_rows(vf))
+    do_d = OMX.dequantize_rows(*OMX.quantize_rows(dof))
+    k_keys = OMX.dequantize_v(*OMX.quantize_v(kf, off), off)
+    v_keys = OMX.dequantize_v(*OMX.quantize_v(vf, off), off)
+    kw = dict(scale=w.scale, broadcast_q=w.broadcast_q, q_offsets=x.q_offsets, causal=w.causal,
+              block_mask=x.block_mask, window=w.window)
+    # the forward's O (bf16) and LSE: the oracle's attention on the MXFP8
+    # forward's operands
+    o, lse = A.forward(q_d, k_d, v_keys, off, **kw)
+    o_bits = W.f32_to_bf16_bits(o.astype(np.float32))
+    o_bf = _f64(o_bits)
+    dq, delta, abs_sum, floor_sum = OMX.dq_mx(q_d, k_d, v_d, do_d, k_keys, dof, o_bf, lse, off, **kw)
+
+    prob = problem_of(x)
+    att = J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask)
+    qg, kg, vg, dog = dev(x.q), dev(x.k), dev(x.v), dev(x.do)
+    mxq = att.quantize_mx(qg, kg, vg)
+    ops = att.quantize_mx_bwd(mxq, kg, vg, dog)
+    H, D = prob.num_heads, prob.head_dim
+    out = dict(dq=torch.full(qg.shape, float("nan"), dtype=torch.bfloat16, device="cuda"),
+               dk=torch.empty_like(kg), dv=torch.empty_like(vg),
+               dq_accum=torch.full(qg.shape, float("nan"), dtype=torch.float32, device="cuda"),
+               delta=torch.full((H, att.total_q), float("nan"), dtype=torch.float32, device="cuda"))
+    att.backward_mx(qg, kg, vg, dev(o_bits), torch.from_numpy(lse.astype(np.float32)).cuda(), dog, ops,
+                    out, stages=J.JFA_BWD_DQ | J.JFA_BWD_DQ_REDUCE)
+    torch.cuda.synchronize()
+    gdq = out["dq_accum"].cpu().numpy().astype(np.float64)
+    gdelta = out["delta"].cpu().numpy().astype(np.float64)
+    assert not np.isnan(gdq).any() and not np.isnan(gdelta).any()
+    bound = 2.0 ** -4 * abs_sum + 2.0 ** -17 * floor_sum + 1e-4 * abs_sum + 1e-6
+    err = np.abs(gdq - dq)
+    assert np.all(err <= bound), float((err - bound).max())
+    # and on average far inside it
+    assert err.mean() <= 0.25 * bound.mean()
+    dbound = 2 * D * 2.0 ** -24 * np.einsum("rhd,rhd->hr", np.abs(dof), np.abs(o_bf)) + 1e-30
+    assert np.all(np.abs(gdelta - delta) <= dbound)
+    # the bf16 dq is the rounding of the fp32 sum
+    assert np.abs(host_f64(out["dq"]) - gdq).max() <= 2 ** -8 * np.abs(gdq).max() + 1e-30

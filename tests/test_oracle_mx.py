@@ -100,3 +100,38 @@ def test_quantize_v_blocks_stay_inside_sequences():
     # the scaled-up key did not coarsen sequence 1's first block
     assert np.abs(y[33:38] - v[33:38]).max() <= 2.0 ** -4 * np.abs(v[33:38]).max() * 2
     assert np.abs(y[32] - v[32]).max() <= 2.0 ** -4 * np.abs(v[32]).max() * 2
+
+
+def _small(broadcast):
+    import workloads as W
+    rng = np.random.default_rng(7)
+    lens = np.array([5, 0, 70, 33])
+    off = W.offsets_of(lens)
+    H, D = 2, 64
+    k = rng.standard_normal((off[-1], H, D))
+    v = rng.standard_normal((off[-1], H, D))
+    if broadcast:
+        q = rng.standard_normal((9, H, D))
+        do = rng.standard_normal((9 * len(lens), H, D))
+        return q, k, v, do, off, None
+    q = rng.standard_normal((off[-1], H, D))
+    do = rng.standard_normal((off[-1], H, D))
+    return q, k, v, do, off, off
+
+
+@pytest.mark.parametrize("broadcast", [True, False])
+def test_dq_mx_without_quantisation_is_the_attention_gradient(broadcast):
+    """With every encoding the identity (the operands undecoded) and the
+    forward's own O and LSE, the MXFP8 dQ definition is the attention dQ and
+    delta of oracle.attention.backward; dQ is linear in the K used for its
+    last product and blind to it in S."""
+    from oracle import attention as A
+    q, k, v, do, off, qoff = _small(broadcast)
+    kw = dict(scale=0.125, broadcast_q=broadcast, q_offsets=qoff, causal=not broadcast)
+    o, lse = A.forward(q, k, v, off, **kw)
+    dq_ref, _, _, delta_ref = A.backward(q, k, v, do, off, **kw)
+    dq, delta, abs_sum, floor_sum = mx.dq_mx(q, k, v, do, k, do, o, lse, off, **kw)
+    assert np.allclose(dq, dq_ref, rtol=0, atol=1e-12) and np.allclose(delta, delta_ref, atol=1e-12)
+    assert np.all(abs_sum >= np.abs(dq) - 1e-12) and np.all(floor_sum >= 0)
+    dq2, _, _, _ = mx.dq_mx(q, k, v, do, 2 * k, do, o, lse, off, **kw)
+    assert np.allclose(dq2, 2 * dq, rtol=0, atol=1e-12)
