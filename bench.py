@@ -175,7 +175,7 @@ def main():
     ap.add_argument("--fwd-workers-per-cu", type=int, default=1)
     ap.add_argument("--bwd-workers-per-cu", type=int, default=1)
     ap.add_argument("--mx", type=int, default=1,
-                    help="also time the MXFP8 forward on the same inputs (head_dim 128; 0: skip)")
+                    help="also time the MXFP8 forward and dQ pass on the same inputs (head_dim 128; 0: skip)")
     ap.add_argument("--fwd-plan", choices=("dynamic", "static"), default="dynamic",
                     help="forward tiles claimed at run time from the sorted list, or the "
                          "static snake deal")
@@ -283,6 +283,32 @@ def main():
               "pct_fp8_peak": 100.0 * model["fwd_flop"] / (mx_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
               "encode_ms": qz_ms,
               "fwd_with_encode_tflops": model["fwd_flop"] / ((mx_ms + qz_ms) * 1e-3) / 1e12}
+        # the MXFP8 dQ pass (the backward's other encodings made once, outside
+        # the timed loop), timed alone; then the step with both MXFP8 passes in
+        # place of their bf16 ones
+        ops = att.quantize_mx_bwd(mxq, k, v, do)
+        for _ in range(args.warmup):
+            att.backward_mx(q, k, v, o, lse, do, ops, out, stages=J.JFA_BWD_DQ)
+        torch.cuda.synchronize()
+        for e0, e1 in mev:
+            e0.record()
+            att.backward_mx(q, k, v, o, lse, do, ops, out, stages=J.JFA_BWD_DQ)
+            e1.record()
+        torch.cuda.synchronize()
+        mdq_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in mev]))
+        for e0, e1 in mev:
+            e0.record()
+            att.quantize_mx_bwd(mxq, k, v, do)
+            e1.record()
+        torch.cuda.synchronize()
+        qzb_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in mev]))
+        mixed_ms = mx_ms + mdq_ms + per["bwd_dkdv"] + per["bwd_dq_reduce"]
+        mx.update({"dq_ms": mdq_ms, "dq_vs_bf16_dq": per["bwd_dq"] / mdq_ms,
+                   "dq_issued_tflops": 3 * model["dq_flop"] / (mdq_ms * 1e-3) / 1e12,
+                   "encode_bwd_ms": qzb_ms,
+                   "step_mx_fwd_mx_dq_ms": mixed_ms,
+                   "step_mx_fwd_mx_dq_tflops": (model["fwd_flop"] + model["bwd_flop"])
+                   / (mixed_ms * 1e-3) / 1e12})
 
     # the standalone delta preprocess (not part of the step: the dQ kernel
     # forms delta itself), timed alone for its HBM rate
@@ -362,7 +388,7 @@ def main():
         "roofline": roof,
     }
     if mx is not None:
-        res["mxfp8_forward"] = mx
+        res["mxfp8"] = mx
     if args.cpu_budget > 0:
         res["cpu_baseline"] = cpu_baseline(x, args.cpu_budget)
     print(json.dumps(res))
