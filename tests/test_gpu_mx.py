@@ -244,3 +244,58 @@ def test_mx_dq_pass(case):
     assert np.all(np.abs(gdelta - delta) <= dbound)
     # the bf16 dq is the rounding of the fp32 sum
     assert np.abs(host_f64(out["dq"]) - gdq).max() <= 2 ** -8 * np.abs(gdq).max() + 1e-30
+
+
+def test_mx_dq_pass_full_size_one_head():
+    """The MXFP8 dQ pass on the full GEM-shaped broadcast-Q workload, in the
+    launch configuration the benchmark times, checked on head 1 (every row:
+    the broadcast dQ sums over all sequences) against the oracle with the
+    bound of test_mx_dq_pass. The other heads get O = 0 and LSE = 30 (their
+    P is negligible); they are computed but not checked."""
+    print("full-size GEM broadcast-Q, MXFP8 dQ pass, head 1", flush=True)
+    x = W.make_inputs(2)
+    w = x.workload
+    off = x.kv_offsets
+    h = 1
+    one = lambda a: _f64(a)[:, h:h + 1]
+    qf, kf, vf, dof = one(x.q), one(x.k), one(x.v), one(x.do)
+    q_d = OMX.dequantize_rows(*OMX.quantize_rows(qf))
+    k_d = OMX.dequantize_rows(*OMX.quantize_rows(kf))
+    v_d = OMX.dequantize_rows(*OMX.quantize_rows(vf))
+    do_d = OMX.dequantize_rows(*OMX.quantize_rows(dof))
+    k_keys = OMX.dequantize_v(*OMX.quantize_v(kf, off), off)
+    v_keys = OMX.dequantize_v(*OMX.quantize_v(vf, off), off)
+    kw = dict(scale=w.scale, broadcast_q=True, q_offsets=None, causal=False)
+    o, lse = A.forward(q_d, k_d, v_keys, off, **kw)
+    o_bits = W.f32_to_bf16_bits(o.astype(np.float32))
+    o_bf = _f64(o_bits)
+    dq, delta, abs_sum, floor_sum = OMX.dq_mx(q_d, k_d, v_d, do_d, k_keys, dof, o_bf, lse, off, **kw)
+
+    prob = problem_of(x)
+    cus = J.jfa_device_workers(0)
+    att = J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask, fwd_workers=cus,
+                            bwd_workers=cus)
+    qg, kg, vg, dog = dev(x.q), dev(x.k), dev(x.v), dev(x.do)
+    H, D = prob.num_heads, prob.head_dim
+    o_all = np.zeros((att.total_q, H, D), dtype=np.uint16)
+    o_all[:, h] = o_bits[:, 0]
+    lse_all = np.full((H, att.total_q), 30.0, dtype=np.float32)
+    lse_all[h] = lse[0]
+    mxq = att.quantize_mx(qg, kg, vg)
+    ops = att.quantize_mx_bwd(mxq, kg, vg, dog)
+    out = dict(dq=torch.empty_like(qg), dk=torch.empty_like(kg), dv=torch.empty_like(vg),
+               dq_accum=torch.full(qg.shape, float("nan"), dtype=torch.float32, device="cuda"),
+               delta=torch.full((H, att.total_q), float("nan"), dtype=torch.float32, device="cuda"))
+    att.backward_mx(qg, kg, vg, dev(o_all), torch.from_numpy(lse_all).cuda(), dog, ops, out,
+                    stages=J.JFA_BWD_DQ | J.JFA_BWD_DQ_REDUCE)
+    torch.cuda.synchronize()
+    gdq = out["dq_accum"].cpu().numpy().astype(np.float64)
+    assert not np.isnan(gdq).any()
+    gdq = gdq[:, h:h + 1]
+    gdelta = out["delta"].cpu().numpy().astype(np.float64)[h:h + 1]
+    bound = 2.0 ** -4 * abs_sum + 2.0 ** -17 * floor_sum + 1e-4 * abs_sum + 1e-6
+    err = np.abs(gdq - dq)
+    assert np.all(err <= bound), float((err - bound).max())
+    assert err.mean() <= 0.25 * bound.mean()
+    dbound = 2 * D * 2.0 ** -24 * np.einsum("rhd,rhd->hr", np.abs(dof), np.abs(o_bf)) + 1e-30
+    assert np.all(np.abs(gdelta - delta) <= dbound)
