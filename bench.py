@@ -170,7 +170,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=2, help="1..6 (2: GEM-shaped broadcast-Q; 6: sliding window)")
     ap.add_argument("--fwd-workers-per-cu", type=int, default=1)
     ap.add_argument("--bwd-workers-per-cu", type=int, default=1)
@@ -179,6 +179,9 @@ def main():
     ap.add_argument("--fwd-plan", choices=("dynamic", "static"), default="dynamic",
                     help="forward tiles claimed at run time from the sorted list, or the "
                          "static snake deal")
+    ap.add_argument("--ablation", type=int, default=1,
+                    help="also time the kernels with the natural (unsorted, round-robin) plans "
+                         "and with the other forward plan (0: skip)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle CPU work for the baseline (0: skip)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -199,7 +202,12 @@ def main():
     x = W.make_inputs(args.workload)
     w = x.workload
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
-    q, k, v, do = dev(x.q), dev(x.k), dev(x.v), dev(x.do)
+    # two resident copies of the inputs (and outputs), used by alternate
+    # steps, so that no step finds the previous step's tensors in L2 or the
+    # MALL (the GEM workload's K and V alone exceed the 256 MiB MALL, the
+    # others fit in it)
+    sets = [tuple(dev(a) for a in (x.q, x.k, x.v, x.do)) for _ in range(2)]
+    q, k, v, do = sets[0]
     mq, mk = (x.block_mask.shape[1], x.block_mask.shape[2]) if x.block_mask is not None else (0, 0)
     prob = J.Problem(batch=x.batch, num_heads=w.heads, head_dim=w.head_dim,
                      broadcast_q=w.broadcast_q, lq=w.lq if w.broadcast_q else 0, causal=w.causal,
@@ -215,22 +223,27 @@ def main():
     plan_ms = (time.perf_counter() - t0) * 1e3
     model = work_model(x, att.dq_plan.info.num_workers)
     H, D = w.heads, w.head_dim
-    o = torch.empty((att.total_q, H, D), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((H, att.total_q), dtype=torch.float32, device="cuda")
-    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
-               dq_accum=torch.empty(q.shape, dtype=torch.float32, device="cuda"),
-               delta=torch.empty((H, att.total_q), dtype=torch.float32, device="cuda"))
+    def outputs():
+        return (torch.empty((att.total_q, H, D), dtype=torch.bfloat16, device="cuda"),
+                torch.empty((H, att.total_q), dtype=torch.float32, device="cuda"),
+                dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+                     dq_accum=torch.empty(q.shape, dtype=torch.float32, device="cuda"),
+                     delta=torch.empty((H, att.total_q), dtype=torch.float32, device="cuda")))
+    outs = [outputs() for _ in range(2)]
+    o, lse, out = outs[0]
     stages = (J.JFA_BWD_DQ, J.JFA_BWD_DKDV, J.JFA_BWD_DQ_REDUCE)
     nev = len(stages) + 2
 
-    def step(ev=None):
+    def step(ev=None, i=0, a=att):
+        qi, ki, vi, doi = sets[i % 2]
+        oi, lsei, outi = outs[i % 2]
         if ev is not None:
             ev[0].record()
-        att.forward(q, k, v, o, lse)
-        for i, s in enumerate(stages):
+        a.forward(qi, ki, vi, oi, lsei)
+        for j, st in enumerate(stages):
             if ev is not None:
-                ev[1 + i].record()
-            att.backward(q, k, v, o, lse, do, out, stages=s)
+                ev[1 + j].record()
+            a.backward(qi, ki, vi, oi, lsei, doi, outi, stages=st)
         if ev is not None:
             ev[-1].record()
 
@@ -242,43 +255,57 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
     names = ("fwd", "bwd_dq", "bwd_dkdv", "bwd_dq_reduce")
-    per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in events])) for j, n in enumerate(names)}
+    # The side measurements (plan ablation, MXFP8 passes, standalone delta)
+    # run first, the headline steps last: a GPU that has just come out of idle
+    # runs below its sustained clock for tens of milliseconds.
 
-    # the MXFP8 forward of the same problem (inputs encoded once, outside the
-    # timed loop; same plan), timed alone with HIP events
+    # plan ablation (the sort and zigzag deal against the unsorted
+    # round-robin plan, and the static zigzag forward against the dynamic
+    # one): the same steps with other plans, per-kernel medians
+    def timed_kernels(a):
+        for i in range(args.warmup):
+            step(i=i, a=a)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            step(ev[i], i, a)
+        torch.cuda.synchronize()
+        return {n: float(np.median([e[j].elapsed_time(e[j + 1]) for e in ev]))
+                for j, n in enumerate(names)}
+    ablation = None
+    if args.ablation:
+        kw = dict(fwd_workers=cus * args.fwd_workers_per_cu, bwd_workers=cus * args.bwd_workers_per_cu)
+        nat = timed_kernels(J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask,
+                                              natural_plans=True, **kw))
+        stat = timed_kernels(J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask,
+                                               fwd_dynamic=args.fwd_plan != "dynamic", **kw))
+        ablation = {"kernel_ms_natural_plans": nat,
+                    ("fwd_ms_static_zigzag" if args.fwd_plan == "dynamic" else "fwd_ms_dynamic"):
+                    stat["fwd"]}
+
+    def time_alone(fn):
+        """Median over the timed steps of fn(i) (i alternates the two input
+        sets), recorded with HIP events around each call, after the warm-up."""
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for i, (e0, e1) in enumerate(ev):
+            e0.record()
+            fn(i)
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+    # the MXFP8 forward of the same problem (inputs encoded once per input
+    # set, outside the timed loop; same plan), timed alone
     mx = None
     if args.mx and D == 128:
-        mxq = att.quantize_mx(q, k, v)
-        for _ in range(args.warmup):
-            att.forward_mx(mxq, o, lse)
-        torch.cuda.synchronize()
-        mev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-        for e0, e1 in mev:
-            e0.record()
-            att.forward_mx(mxq, o, lse)
-            e1.record()
-        torch.cuda.synchronize()
-        mx_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in mev]))
+        mxqs = [att.quantize_mx(*sets[i][:3]) for i in range(2)]
+        mx_ms = time_alone(lambda i: att.forward_mx(mxqs[i % 2], outs[i % 2][0], outs[i % 2][1]))
         # the encoding of bf16 Q, K, V into MXFP8, timed on its own
-        for e0, e1 in mev:
-            e0.record()
-            att.quantize_mx(q, k, v)
-            e1.record()
-        torch.cuda.synchronize()
-        qz_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in mev]))
+        qz_ms = time_alone(lambda i: att.quantize_mx(*sets[i % 2][:3]))
         mx = {"fwd_ms": mx_ms, "fwd_tflops": model["fwd_flop"] / (mx_ms * 1e-3) / 1e12,
               "pct_fp8_peak": 100.0 * model["fwd_flop"] / (mx_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
               "encode_ms": qz_ms,
@@ -286,40 +313,55 @@ def main():
         # the MXFP8 dQ pass (the backward's other encodings made once, outside
         # the timed loop), timed alone; then the step with both MXFP8 passes in
         # place of their bf16 ones
-        ops = att.quantize_mx_bwd(mxq, k, v, do)
-        for _ in range(args.warmup):
-            att.backward_mx(q, k, v, o, lse, do, ops, out, stages=J.JFA_BWD_DQ)
-        torch.cuda.synchronize()
-        for e0, e1 in mev:
-            e0.record()
-            att.backward_mx(q, k, v, o, lse, do, ops, out, stages=J.JFA_BWD_DQ)
-            e1.record()
-        torch.cuda.synchronize()
-        mdq_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in mev]))
-        for e0, e1 in mev:
-            e0.record()
-            att.quantize_mx_bwd(mxq, k, v, do)
-            e1.record()
-        torch.cuda.synchronize()
-        qzb_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in mev]))
-        mixed_ms = mx_ms + mdq_ms + per["bwd_dkdv"] + per["bwd_dq_reduce"]
-        mx.update({"dq_ms": mdq_ms, "dq_vs_bf16_dq": per["bwd_dq"] / mdq_ms,
+        opss = [att.quantize_mx_bwd(mxqs[i], sets[i][1], sets[i][2], sets[i][3]) for i in range(2)]
+
+        def mx_dq(i):
+            qi, ki, vi, doi = sets[i % 2]
+            oi, lsei, outi = outs[i % 2]
+            att.backward_mx(qi, ki, vi, oi, lsei, doi, opss[i % 2], outi, stages=J.JFA_BWD_DQ)
+        mdq_ms = time_alone(mx_dq)
+        qzb_ms = time_alone(lambda i: att.quantize_mx_bwd(mxqs[i % 2], *sets[i % 2][1:]))
+        mx.update({"dq_ms": mdq_ms,
                    "dq_issued_tflops": 3 * model["dq_flop"] / (mdq_ms * 1e-3) / 1e12,
-                   "encode_bwd_ms": qzb_ms,
-                   "step_mx_fwd_mx_dq_ms": mixed_ms,
-                   "step_mx_fwd_mx_dq_tflops": (model["fwd_flop"] + model["bwd_flop"])
-                   / (mixed_ms * 1e-3) / 1e12})
+                   "encode_bwd_ms": qzb_ms})
 
     # the standalone delta preprocess (not part of the step: the dQ kernel
     # forms delta itself), timed alone for its HBM rate
-    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for e0, e1 in pev:
-        e0.record()
-        att.backward(q, k, v, o, lse, do, out, stages=J.JFA_BWD_PREPROCESS)
-        e1.record()
+    def pre(i):
+        qi, ki, vi, doi = sets[i % 2]
+        oi, lsei, outi = outs[i % 2]
+        att.backward(qi, ki, vi, oi, lsei, doi, outi, stages=J.JFA_BWD_PREPROCESS)
+    pre_ms = time_alone(pre)
+
+    for i in range(args.warmup):
+        step(i=i)
     torch.cuda.synchronize()
-    pre_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in pev]))
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i], i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    names = ("fwd", "bwd_dq", "bwd_dkdv", "bwd_dq_reduce")
+    # per-kernel: the median over the timed steps
+    per = {n: float(np.median([e[j].elapsed_time(e[j + 1]) for e in events]))
+           for j, n in enumerate(names)}
+    per_mean = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in events]))
+                for j, n in enumerate(names)}
+
+    if ablation is not None:
+        nat = ablation["kernel_ms_natural_plans"]
+        ablation["fwd_speedup_sorted_vs_natural"] = nat["fwd"] / per["fwd"]
+        ablation["bwd_speedup_sorted_vs_natural"] = (sum(nat[n] for n in names[1:])
+                                                     / sum(per[n] for n in names[1:]))
+    if mx is not None:
+        mixed_ms = mx["fwd_ms"] + mx["dq_ms"] + per["bwd_dkdv"] + per["bwd_dq_reduce"]
+        mx.update({"dq_vs_bf16_dq": per["bwd_dq"] / mx["dq_ms"],
+                   "step_mx_fwd_mx_dq_ms": mixed_ms,
+                   "step_mx_fwd_mx_dq_tflops": (model["fwd_flop"] + model["bwd_flop"])
+                   / (mixed_ms * 1e-3) / 1e12})
 
     flop = model["fwd_flop"] + model["bwd_flop"]
     value = flop / (ms_step * 1e-3) / 1e12
@@ -336,7 +378,7 @@ def main():
     dom = max(kernels, key=lambda n: per[n])
     _, kflop, kbytes = kernels[dom]
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    t_s = per[dom] * 1e-3
+    t_s = per_mean[dom] * 1e-3   # the average launch, as rocprofv3's statistics give it
     if kflop / kbytes >= ridge:
         roof = {"bound": "mfma", "achieved": kflop / t_s / 1e12, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s"}
@@ -347,7 +389,7 @@ def main():
     cnt = {n: counters_for(n, wl_name) for n in kernels}
     roof["traffic"] = float(cnt[dom]["hbm_bytes_per_launch"]) if cnt[dom] else None
     roof["kernel"] = dom
-    roof["avg_ms"] = per[dom]
+    roof["avg_ms"] = per_mean[dom]
     roof["algorithmic_flop"] = kflop
     roof["algorithmic_bytes"] = kbytes
 
@@ -378,6 +420,7 @@ def main():
         "fwd_tflops": fwd_tf,
         "bwd_tflops": bwd_tf,
         "kernel_ms": per,
+        "kernel_ms_mean": per_mean,
         "hbm_gbps": {"bwd_dq_reduce": (model["reduce_bytes"] / (per["bwd_dq_reduce"] * 1e-3) / 1e9
                                        if model["reduce_bytes"] else None),
                      "bwd_preprocess_standalone": model["pre_bytes"] / (pre_ms * 1e-3) / 1e9},
@@ -389,6 +432,8 @@ def main():
     }
     if mx is not None:
         res["mxfp8"] = mx
+    if ablation is not None:
+        res["plan_ablation"] = ablation
     if args.cpu_budget > 0:
         res["cpu_baseline"] = cpu_baseline(x, args.cpu_budget)
     print(json.dumps(res))

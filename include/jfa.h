@@ -78,6 +78,9 @@ extern "C" {
 #define JFA_PASS_DQ 2   /* Q-stationary dQ pass of the backward */
 /* OR'ed into a FWD pass: a plan for dynamic tile fetch (see the planner) */
 #define JFA_PLAN_DYNAMIC 16
+/* OR'ed into any pass (not with JFA_PLAN_DYNAMIC): the unsorted ablation
+   plan, tiles in enumeration order dealt round-robin (see the planner) */
+#define JFA_PLAN_NATURAL 32
 
 /* Problem description shared by the planner, jfa_fwd and jfa_bwd. */
 typedef struct jfa_problem {
@@ -171,6 +174,14 @@ int32_t jfa_offsets_from_lengths(const int32_t* h_lengths, int32_t batch, int32_
  * h_worker_ptr[w] = min(w, N): worker w starts with sorted tile w, and later
  * tiles W, W+1, ... go, one at a time and in order, to whichever worker asks
  * first (a device counter, see jfa_fwd). Only the forward has this mode.
+ *
+ * pass | JFA_PLAN_NATURAL: the baseline the sort and zigzag deal are measured
+ * against (the pages credit them with about a fifth of the forward's speed;
+ * bites, "Optimizations layered on top"): no sort, tiles in enumeration
+ * order (b, h, t) dealt round-robin, enumerated tile i to worker i mod W
+ * (broadcast-Q DQ: within each group's workers, the groups and chunks as
+ * above). info->pass does not record the flag: the plan has the layout of a
+ * static plan of its pass and is used like one.
  *
  * h_q_offsets: int32 [B+1], NULL in broadcast mode. h_kv_offsets: int32 [B+1].
  * h_block_mask: NULL when mask_q_blocks = mask_kv_blocks = 0.

@@ -29,6 +29,7 @@ JFA_PASS_FWD = 0
 JFA_PASS_BWD = 1
 JFA_PASS_DQ = 2
 JFA_PLAN_DYNAMIC = 16
+JFA_PLAN_NATURAL = 32
 
 EXPORTS = (
     "jfa_abi_version", "jfa_status_string", "jfa_last_hip_error", "jfa_device_workers",
@@ -384,18 +385,22 @@ class JaggedAttention:
 
     def __init__(self, prob: Problem, kv_offsets, q_offsets=None, block_mask=None,
                  fwd_workers: Optional[int] = None, bwd_workers: Optional[int] = None,
-                 dq_workers: Optional[int] = None, fwd_dynamic: bool = True, device="cuda"):
+                 dq_workers: Optional[int] = None, fwd_dynamic: bool = True,
+                 natural_plans: bool = False, device="cuda"):
+        """natural_plans: the unsorted round-robin plans (the ablation
+        baseline) for all three passes; the forward is then static."""
         import torch
         self.prob = prob
         self.device = device
         cus = jfa_device_workers(torch.device(device).index or 0)
-        fwd_pass = JFA_PASS_FWD | (JFA_PLAN_DYNAMIC if fwd_dynamic else 0)
+        nat = JFA_PLAN_NATURAL if natural_plans else 0
+        fwd_pass = JFA_PASS_FWD | (JFA_PLAN_DYNAMIC if fwd_dynamic and not natural_plans else nat)
         self.fwd_plan_host = jfa_plan_build(prob, q_offsets, kv_offsets, block_mask,
                                             fwd_pass, fwd_workers or cus)
         self.bwd_plan_host = jfa_plan_build(prob, q_offsets, kv_offsets, block_mask,
-                                            JFA_PASS_BWD, bwd_workers or cus)
+                                            JFA_PASS_BWD | nat, bwd_workers or cus)
         self.dq_plan_host = jfa_plan_build(prob, q_offsets, kv_offsets, block_mask,
-                                           JFA_PASS_DQ, dq_workers or cus)
+                                           JFA_PASS_DQ | nat, dq_workers or cus)
         self.fwd_plan = to_device(self.fwd_plan_host, device)
         self.bwd_plan = to_device(self.bwd_plan_host, device)
         self.dq_plan = to_device(self.dq_plan_host, device)

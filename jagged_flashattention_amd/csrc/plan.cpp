@@ -18,6 +18,8 @@
 // through a device counter: the counterpart of the cluster launch control the
 // pages pair with the host sort (same page, sections "What TLX changes" and
 // "Optimizations layered on top").
+// A natural plan (the ablation baseline for the sort and the deal) skips the
+// sort and deals the tiles in enumeration order round-robin.
 #include "internal.h"
 
 #include <algorithm>
@@ -190,10 +192,11 @@ int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, co
     int32_t st = check_problem(p);
     if (st) return st;
     const bool dynamic = (pass_flags & JFA_PLAN_DYNAMIC) != 0;
-    const int32_t pass = pass_flags & ~JFA_PLAN_DYNAMIC;
+    const bool natural = (pass_flags & JFA_PLAN_NATURAL) != 0;
+    const int32_t pass = pass_flags & ~(JFA_PLAN_DYNAMIC | JFA_PLAN_NATURAL);
     if (pass != JFA_PASS_FWD && pass != JFA_PASS_BWD && pass != JFA_PASS_DQ)
         return JFA_ERR_INVALID_ARG;
-    if (dynamic && pass != JFA_PASS_FWD) return JFA_ERR_INVALID_ARG;
+    if (dynamic && (pass != JFA_PASS_FWD || natural)) return JFA_ERR_INVALID_ARG;
     if (W < 1) return JFA_ERR_INVALID_ARG;
     // Q-tile passes (forward, dQ) enumerate Q tiles; the backward KV tiles
     const bool qtiles = pass != JFA_PASS_BWD;
@@ -285,7 +288,7 @@ int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, co
             W = (int32_t)std::max<int64_t>(G, std::min<int64_t>(W, G * n));
         }
     }
-    info->pass = pass_flags;
+    info->pass = pass_flags & ~JFA_PLAN_NATURAL;   // laid out as the static plan of its pass
     info->num_workers = W;
     info->num_tiles = (int32_t)tiles.size();
     info->block_m = bm;
@@ -321,7 +324,7 @@ int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, co
     std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t c) {
         const int64_t ga = group_of(tiles[a]), gc = group_of(tiles[c]);
         if (ga != gc) return ga < gc;
-        return key[a] > key[c];
+        return !natural && key[a] > key[c];   // natural: enumeration order
     });
     if (dynamic) {   // the sorted list itself; worker w starts with tile w
         for (int32_t w = 0; w <= W; ++w) worker_ptr[w] = (int32_t)std::min<size_t>(w, order.size());
@@ -346,7 +349,7 @@ int32_t plan_impl(const jfa_problem* p, const int32_t* qo, const int32_t* ko, co
         for (size_t k = i; k < e; ++k) {
             const size_t j = k - i;
             const int32_t pos = (int32_t)(j % nw);
-            const int32_t w = w0 + (((j / nw) % 2 == 0) ? pos : nw - 1 - pos);
+            const int32_t w = w0 + ((natural || (j / nw) % 2 == 0) ? pos : nw - 1 - pos);
             owner[k] = w;
             ++count[w];
         }

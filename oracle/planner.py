@@ -74,6 +74,13 @@ tiles: (b, h, t) with the forward work.
    sort; a chunk starting at position k0 is stored as (b, h, t + nqt * k0,
    length) with nqt = ceil(Lq / block_m).
 
+Natural plan (the ablation baseline). The pages credit the sort and the
+zigzag deal with about a fifth of the forward's speed ([bites] section
+"Optimizations layered on top"); the plan they are measured against skips
+both: steps 1-2 as above, no sort, and enumerated tile i goes to worker
+i mod W (broadcast-Q dQ pass: the groups, W' and chunks as above, each
+group's tiles in their (b, chunk) order dealt round-robin over its workers).
+
 Block-sparse lists ([radar] section "The turning point": the block-sparse
 variant only adds iteration over the selected blocks). The mask is uint8
 [B, NQ, NK] over 128-row Q tiles x 128-key blocks, shared by all heads.
@@ -227,12 +234,18 @@ def _snake(order_len, W):
     return out
 
 
+def _round_robin(order_len, W):
+    """Worker of each position of a list under the natural plan's deal."""
+    return [i % W for i in range(order_len)]
+
+
 def plan_dq(q_lens, kv_lens, num_heads, num_workers, *, broadcast_q, lq=0, block_m, block_n,
-            causal=False, block_mask=None, window=None):
+            causal=False, block_mask=None, window=None, natural=False):
     """dQ pass. Returns (worker_ptr int32 [W'+1], tiles int32 [N, 4])."""
     if not broadcast_q:
         return plan(q_lens, kv_lens, num_heads, num_workers, FWD, block_m=block_m,
-                    block_n=block_n, causal=causal, block_mask=block_mask, window=window)
+                    block_n=block_n, causal=causal, block_mask=block_mask, window=window,
+                    natural=natural)
     B = len(kv_lens)
     nqt = cdiv(int(lq), block_m)
     G = num_heads * nqt
@@ -259,8 +272,12 @@ def plan_dq(q_lens, kv_lens, num_heads, num_workers, *, broadcast_q, lq=0, block
     for g in range(G):
         w0, w1 = (g * W) // G, ((g + 1) * W) // G
         tiles = groups[g]
-        order = sorted(range(len(tiles)), key=lambda i: -tiles[i][3])   # stable
-        owner = _snake(len(order), w1 - w0)
+        if natural:
+            order = list(range(len(tiles)))
+            owner = _round_robin(len(order), w1 - w0)
+        else:
+            order = sorted(range(len(tiles)), key=lambda i: -tiles[i][3])   # stable
+            owner = _snake(len(order), w1 - w0)
         for i, ti in enumerate(order):
             per_worker[w0 + owner[i]].append(tiles[ti])
     worker_ptr = [0]
@@ -273,7 +290,7 @@ def plan_dq(q_lens, kv_lens, num_heads, num_workers, *, broadcast_q, lq=0, block
 
 
 def plan(q_lens, kv_lens, num_heads, num_workers, pass_, *, block_m, block_n,
-         causal=False, block_mask=None, dynamic=False, window=None):
+         causal=False, block_mask=None, dynamic=False, window=None, natural=False):
     """Returns (worker_ptr int32 [W+1], tiles int32 [N, 4])."""
     B = len(kv_lens)
     W = int(num_workers)
@@ -289,13 +306,20 @@ def plan(q_lens, kv_lens, num_heads, num_workers, pass_, *, block_m, block_n,
                                causal=causal, block_mask=block_mask, window=window)
                 tiles.append((b, h, t, w))
                 keys.append(w if pass_ == FWD else bwd_sort_key(w, t, lk_b, block_n))
-    order = sorted(range(len(tiles)), key=lambda i: -keys[i])   # stable
+    if natural:
+        if dynamic:
+            raise ValueError("a natural plan is static")
+        order = list(range(len(tiles)))
+        owner = _round_robin(len(order), W)
+    else:
+        order = sorted(range(len(tiles)), key=lambda i: -keys[i])   # stable
     if dynamic:
         if pass_ != FWD:
             raise ValueError("dynamic plans are forward plans")
         worker_ptr = np.array([min(w, len(order)) for w in range(W + 1)], dtype=np.int32)
         return worker_ptr, np.array([tiles[i] for i in order], dtype=np.int32).reshape(-1, 4)
-    owner = _snake(len(order), W)
+    if not natural:
+        owner = _snake(len(order), W)
     per_worker = [[] for _ in range(W)]
     for i, ti in enumerate(order):
         per_worker[owner[i]].append(tiles[ti])

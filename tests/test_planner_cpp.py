@@ -182,3 +182,37 @@ def test_cpp_band_plans_equal_oracle():
         wp, tiles = OP.plan_dq(lens, lens, 2, W_, broadcast_q=False, block_m=FWD_BM,
                                block_n=FWD_BN, causal=causal, window=window)
         assert np.array_equal(hp.tiles, tiles), (trial, "dq")
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+@pytest.mark.parametrize("workers", [1, 7, 256])
+def test_cpp_natural_plan_equals_oracle(cfg, workers):
+    """The unsorted round-robin ablation plans, bit for bit, every pass."""
+    w, lens, mask = _lengths_only(cfg)
+    kv_off = W.offsets_of(lens)
+    q_off = None if w.broadcast_q else kv_off
+    mq, mk = (mask.shape[1], mask.shape[2]) if mask is not None else (0, 0)
+    prob = J.Problem(batch=w.batch, num_heads=w.heads, head_dim=w.head_dim,
+                     broadcast_q=w.broadcast_q, lq=w.lq if w.broadcast_q else 0, causal=w.causal,
+                     mask_q_blocks=mq, mask_kv_blocks=mk, softmax_scale=w.scale)
+    q_lens = [w.lq] * w.batch if w.broadcast_q else lens
+    for pass_, bm, bn in ((OP.FWD, FWD_BM, FWD_BN), (OP.BWD, BWD_BM, BWD_BN)):
+        hp = J.jfa_plan_build(prob, q_off, kv_off, mask, pass_ | J.JFA_PLAN_NATURAL, workers)
+        wp, tiles = OP.plan(q_lens, lens, w.heads, workers, pass_, block_m=bm, block_n=bn,
+                            causal=w.causal, block_mask=mask, natural=True)
+        assert hp.info.pass_ == pass_
+        assert np.array_equal(hp.worker_ptr, wp) and np.array_equal(hp.tiles, tiles), pass_
+    hp = J.jfa_plan_build(prob, q_off, kv_off, mask, J.JFA_PASS_DQ | J.JFA_PLAN_NATURAL, workers)
+    wp, tiles = OP.plan_dq(q_lens, lens, w.heads, workers, broadcast_q=w.broadcast_q, lq=w.lq,
+                           block_m=FWD_BM, block_n=FWD_BN, causal=w.causal, block_mask=mask,
+                           natural=True)
+    assert hp.info.pass_ == J.JFA_PASS_DQ
+    assert np.array_equal(hp.worker_ptr, wp) and np.array_equal(hp.tiles, tiles)
+
+
+def test_cpp_natural_plan_is_static():
+    prob = J.Problem(2, 1, 64, True, lq=8, softmax_scale=0.1)
+    with pytest.raises(J.JfaError) as e:
+        J.jfa_plan_build(prob, None, [0, 3, 5], None,
+                         J.JFA_PASS_FWD | J.JFA_PLAN_DYNAMIC | J.JFA_PLAN_NATURAL, 4)
+    assert e.value.status == J.JFA_ERR_INVALID_ARG

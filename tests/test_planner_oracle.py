@@ -303,3 +303,52 @@ def test_dq_plan_workers_capped_by_chunks():
     wp, _ = P.plan_dq([300] * 3, [5000, 4000, 64], 2, 3, broadcast_q=True, lq=300,
                       block_m=256, block_n=64)
     assert len(wp) == 5
+
+
+@pytest.mark.parametrize("name,qlens,kvlens,causal,mask", _cases())
+@pytest.mark.parametrize("pass_,bm,bn", [(P.FWD, 256, 64), (P.BWD, 32, 256)])
+@pytest.mark.parametrize("workers", [1, 7, 255])
+def test_natural_plan_by_enumeration(name, qlens, kvlens, causal, mask, pass_, bm, bn, workers):
+    """The natural (ablation) plan: the tiles enumerated by nested loops over
+    (b, h, t) with their brute-force work, tile i on worker i mod W, each
+    worker's list in enumeration order."""
+    H = 2
+    wp, tiles = P.plan(qlens, kvlens, H, workers, pass_, block_m=bm, block_n=bn,
+                       causal=causal, block_mask=mask, natural=True)
+    enum = []
+    for b in range(len(kvlens)):
+        n_t = P.cdiv(qlens[b], bm) if pass_ == P.FWD else P.cdiv(kvlens[b], bn)
+        for h in range(H):
+            for t in range(n_t):
+                enum.append((b, h, t, _brute_work(pass_, b, t, qlens[b], kvlens[b], bm, bn,
+                                                  causal, mask)))
+    for w in range(workers):
+        got = [tuple(int(x) for x in r) for r in tiles[wp[w]:wp[w + 1]]]
+        assert got == enum[w::workers]
+    # the same tiles as the sorted plan
+    _, sorted_tiles = P.plan(qlens, kvlens, H, workers, pass_, block_m=bm, block_n=bn,
+                             causal=causal, block_mask=mask)
+    assert sorted(map(tuple, tiles.tolist())) == sorted(map(tuple, sorted_tiles.tolist()))
+
+
+def test_natural_dq_plan_keeps_groups():
+    """Broadcast-Q natural dQ plan: the sorted plan's groups, workers and
+    chunks, each group's chunks in (b, chunk) order dealt round-robin."""
+    lens = [40, 3000, 700, 0, 1500]
+    wp_s, t_s = P.plan_dq([300] * 5, lens, 2, 16, broadcast_q=True, lq=300, block_m=256,
+                          block_n=64)
+    wp, t = P.plan_dq([300] * 5, lens, 2, 16, broadcast_q=True, lq=300, block_m=256,
+                      block_n=64, natural=True)
+    assert len(wp) == len(wp_s)
+    W_ = len(wp) - 1
+    G = 2 * 2
+    nqt = 2
+    for g in range(G):
+        h, tq = divmod(g, nqt)
+        w0, w1 = g * W_ // G, (g + 1) * W_ // G
+        chunks = [tuple(int(x) for x in r) for r in t_s.tolist()
+                  if r[1] == h and r[2] % nqt == tq]
+        chunks.sort(key=lambda r: (r[0], r[2] // nqt))       # (b, chunk) order
+        for j, w in enumerate(range(w0, w1)):
+            got = [tuple(int(x) for x in r) for r in t[wp[w]:wp[w + 1]]]
+            assert got == chunks[j::w1 - w0]
