@@ -196,3 +196,42 @@ def test_bwd_validation_returns_before_launch():
     assert _call_bwd(prob, kv, dq, need, ws=None) == J.JFA_ERR_WORKSPACE
     assert _call_bwd(prob, kv, dq, need, dk=_FakeTensor(0x1004)) == J.JFA_ERR_INVALID_ARG
     assert _call_bwd(_prob(lq=9), kv, dq, need) == J.JFA_ERR_PLAN_MISMATCH
+
+
+def _call_dq_mx(prob, dq, ws_bytes, nkb=1, ops=True, **over):
+    t = _FakeTensor(0x1000)
+    f = lambda x: None if x is None else ctypes.c_void_p(x.data_ptr())
+    args = dict(o=t, lse=t, d_o=t, dq=t, dq_accum=t, delta=t, ws=t, kbo=t)
+    args.update(over)
+    sc = dict(q_scales=0x1000, k_scales=0x1000, v_scales=0x1000, do_scales=0x1000, kk_scales=0x1000)
+    sc.update({k: v for k, v in over.items() if k.endswith("_scales")})
+    mx = J.JfaMxBwdOperands(q_codes=0x1000, k_codes=0x1000, v_codes=0x1000, do_codes=0x1000,
+                            kk_codes=0x1000, **sc)
+    plan = J.JfaDevicePlan(ctypes.pointer(dq.info), 0x1000, 0x1000, None, None)
+    cp = prob.c()
+    return J._lib().jfa_bwd_dq_mx(ctypes.byref(cp), ctypes.byref(plan), None,
+                                  ctypes.c_void_p(0x1000), f(args["kbo"]), nkb, f(args["o"]),
+                                  f(args["lse"]), f(args["d_o"]),
+                                  ctypes.byref(mx) if ops else None, f(args["dq"]),
+                                  f(args["dq_accum"]), f(args["delta"]), f(args["ws"]), ws_bytes,
+                                  None)
+
+
+def test_bwd_dq_mx_validation_returns_before_launch():
+    prob = _prob(head_dim=128)
+    dq = J.jfa_plan_build(prob, None, [0, 3, 5], None, J.JFA_PASS_DQ, 4)
+    kv = J.jfa_plan_build(prob, None, [0, 3, 5], None, J.JFA_PASS_BWD, 4)
+    need = J.jfa_bwd_workspace_bytes(prob, dq.info)
+    # two sequences of 3 and 2 keys: one 32-key block each
+    assert _call_dq_mx(prob, kv, need, nkb=2) == J.JFA_ERR_PLAN_MISMATCH      # not a DQ plan
+    assert _call_dq_mx(prob, dq, need - 1, nkb=2) == J.JFA_ERR_WORKSPACE
+    assert _call_dq_mx(prob, dq, need, nkb=2, ws=None) == J.JFA_ERR_WORKSPACE
+    assert _call_dq_mx(prob, dq, need, nkb=2, ops=False) == J.JFA_ERR_INVALID_ARG
+    assert _call_dq_mx(prob, dq, need, nkb=0) == J.JFA_ERR_INVALID_ARG      # too few key blocks
+    assert _call_dq_mx(prob, dq, need, nkb=2, kbo=None) == J.JFA_ERR_INVALID_ARG
+    assert _call_dq_mx(prob, dq, need, nkb=2, kk_scales=0x1002) == J.JFA_ERR_INVALID_ARG  # unaligned
+    assert _call_dq_mx(prob, dq, need, nkb=2, d_o=_FakeTensor(0x1004)) == J.JFA_ERR_INVALID_ARG
+    assert _call_dq_mx(prob, dq, need, nkb=2, delta=None) == J.JFA_ERR_INVALID_ARG
+    p64 = _prob(head_dim=64)
+    dq64 = J.jfa_plan_build(p64, None, [0, 3, 5], None, J.JFA_PASS_DQ, 4)
+    assert _call_dq_mx(p64, dq64, J.jfa_bwd_workspace_bytes(p64, dq64.info), nkb=2) == J.JFA_ERR_UNSUPPORTED
