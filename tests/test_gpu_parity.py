@@ -368,6 +368,59 @@ def test_full_size_sampled_parity(cfg):
         assert np.abs(gdq16 - gdq).max() <= 2 ** -8 * np.abs(gdq).max()
 
 
+def test_element_offsets_beyond_int32():
+    """A first sequence of 4,198,400 keys (H=4, D=128: K and V hold more than
+    2^31 elements, 4.3 GB each) puts every later sequence past element 2^31,
+    so any 32-bit element index would wrap. Its keys are 1,025 copies of one
+    random 4,096-key block and its dO rows are zero (so its dK, dV and its
+    share of the batch-summed dQ are exactly zero); the three later sequences
+    are random. Checked against the oracle: O and LSE of two rows of the long
+    sequence, O, LSE, dK, dV of the later sequences, every row of dQ."""
+    print("element offsets beyond 2^31", flush=True)
+    H, D, lq, blk, reps = 4, 128, 256, 4096, 1025
+    base = _custom("i32", broadcast=True, H=H, D=D, lengths=[blk, 1000, 37, 300], lq=lq, seed=9)
+    big = blk * reps
+    assert big * H * D > 2 ** 31
+    lens = np.array([big, 1000, 37, 300], dtype=np.int32)
+    tile_rows = lambda a: np.concatenate([np.tile(a[:blk], (reps, 1, 1)), a[blk:]])
+    do = base.do.copy()
+    do[:lq] = 0
+    x = dataclasses.replace(base, lengths=lens, kv_offsets=W.offsets_of(lens), k=tile_rows(base.k),
+                            v=tile_rows(base.v), do=do)
+    g = run_gpu(x, canary=True)
+    w = x.workload
+    off = x.kv_offsets
+    # the long sequence: no gradient
+    for t in (g.dk, g.dv):
+        assert float(t[:big].abs().amax()) == 0.0
+    go = g.o.view(torch.int16).cpu().numpy().view(np.uint16)
+    glse = g.lse.cpu().numpy()
+    gdk = g.dk[big:].view(torch.int16).cpu().numpy().view(np.uint16)
+    gdv = g.dv[big:].view(torch.int16).cpu().numpy().view(np.uint16)
+    gdq = g.dq_accum.cpu().numpy()
+    kw = dict(scale=w.scale, broadcast_q=True)
+    h = 1
+    rows = [0, lq - 1]
+    q_rows = _head_f64(x.q, h)[rows]
+    o0, lse0 = A.forward(q_rows, _head_f64(x.k, h, slice(0, big)), _head_f64(x.v, h, slice(0, big)),
+                         np.array([0, big], dtype=np.int32), **kw)
+    assert np.abs(W.bf16_bits_to_f32(go[rows, h]) - o0[:, 0]).max() <= TOL_O
+    assert np.abs(glse[h, rows] - lse0[0]).max() <= TOL_O
+    # the later sequences, as a batch of their own (broadcast dQ sums them)
+    sub = np.array([0, 1000, 1037, 1337], dtype=np.int32)
+    q_all = x.as_f64("q")
+    k_s = W.bf16_bits_to_f32(x.k[big:]).astype(np.float64)
+    v_s = W.bf16_bits_to_f32(x.v[big:]).astype(np.float64)
+    do_s = W.bf16_bits_to_f32(x.do[lq:]).astype(np.float64)
+    o, lse = A.forward(q_all, k_s, v_s, sub, **kw)
+    dq, dk, dv, _ = A.backward(q_all, k_s, v_s, do_s, sub, **kw)
+    assert np.abs(W.bf16_bits_to_f32(go[lq:]) - o).max() <= TOL_O
+    assert np.abs(glse[:, lq:] - lse).max() <= TOL_O
+    assert rel_err(W.bf16_bits_to_f32(gdk), dk) <= TOL_GRAD
+    assert rel_err(W.bf16_bits_to_f32(gdv), dv) <= TOL_GRAD
+    assert rel_err(gdq, dq) <= TOL_GRAD
+
+
 def test_long_sequence_sampled():
     """One sequence of 262,181 keys (1,025 KV tiles, a dQ tile cut into 257
     chunks per (head, Q tile)) beside an empty, a one-key and a 4,999-key
