@@ -299,3 +299,65 @@ def test_mx_dq_pass_full_size_one_head():
     assert err.mean() <= 0.25 * bound.mean()
     dbound = 2 * D * 2.0 ** -24 * np.einsum("rhd,rhd->hr", np.abs(dof), np.abs(o_bf)) + 1e-30
     assert np.all(np.abs(gdelta - delta) <= dbound)
+
+
+def test_mx_element_offsets_beyond_int32():
+    """The MXFP8 encoders, forward and dQ pass on a batch whose K and V hold
+    more than 2^31 elements (a first sequence of 4,198,400 keys with zero dO
+    rows, then three random sequences that start past element 2^31). The
+    later sequences' O, LSE and the batch-summed dQ (to which the first
+    sequence adds exactly nothing) against the oracle on the later
+    sequences' own encodings (an MX block never spans two rows or two
+    sequences), with the bounds of test_mx_forward_small and
+    test_mx_dq_pass."""
+    from test_gpu_parity import beyond_int32_inputs
+    print("MXFP8, element offsets beyond 2^31", flush=True)
+    x, big, later = beyond_int32_inputs()
+    w = x.workload
+    H, D, lq = w.heads, w.head_dim, w.lq
+    sub = dataclasses.replace(x, lengths=np.array(later, dtype=np.int32),
+                              kv_offsets=W.offsets_of(np.array(later)), k=x.k[big:], v=x.v[big:],
+                              do=x.do[lq:])
+    prob = problem_of(x)
+    att = J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask)
+    qg, kg, vg, dog = dev(x.q), dev(x.k), dev(x.v), dev(x.do)
+    mxq = att.quantize_mx(qg, kg, vg)
+    o = torch.full((att.total_q, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((H, att.total_q), float("nan"), dtype=torch.float32, device="cuda")
+    att.forward_mx(mxq, o, lse)
+    torch.cuda.synchronize()
+    o_h = W.bf16_bits_to_f32(o[lq:].view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    _check_mx(sub, o_h, lse[:, lq:].cpu().numpy().astype(np.float64))
+
+    # the dQ pass on the oracle's O and LSE of the later sequences (the first
+    # sequence's rows get O = 0, LSE = 0: with dO = 0 its dS is zero anyway)
+    off = sub.kv_offsets
+    qf, kf, vf, dof = _f64(sub.q), _f64(sub.k), _f64(sub.v), _f64(sub.do)
+    q_d = OMX.dequantize_rows(*OMX.quantize_rows(qf))
+    k_d = OMX.dequantize_rows(*OMX.quantize_rows(kf))
+    v_d = OMX.dequantize_rows(*OMX.quantize_rows(vf))
+    do_d = OMX.dequantize_rows(*OMX.quantize_rows(dof))
+    k_keys = OMX.dequantize_v(*OMX.quantize_v(kf, off), off)
+    v_keys = OMX.dequantize_v(*OMX.quantize_v(vf, off), off)
+    kw = dict(scale=w.scale, broadcast_q=True)
+    o_r, lse_r = A.forward(q_d, k_d, v_keys, off, **kw)
+    o_bits = W.f32_to_bf16_bits(o_r.astype(np.float32))
+    dq, _, abs_sum, floor_sum = OMX.dq_mx(q_d, k_d, v_d, do_d, k_keys, dof, _f64(o_bits), lse_r, off,
+                                          **kw)
+    o_all = np.zeros((att.total_q, H, D), dtype=np.uint16)
+    o_all[lq:] = o_bits
+    lse_all = np.zeros((H, att.total_q), dtype=np.float32)
+    lse_all[:, lq:] = lse_r
+    ops = att.quantize_mx_bwd(mxq, kg, vg, dog)
+    out = dict(dq=torch.empty_like(qg), dk=torch.empty_like(kg), dv=torch.empty_like(vg),
+               dq_accum=torch.full(qg.shape, float("nan"), dtype=torch.float32, device="cuda"),
+               delta=torch.full((H, att.total_q), float("nan"), dtype=torch.float32, device="cuda"))
+    att.backward_mx(qg, kg, vg, dev(o_all), torch.from_numpy(lse_all).cuda(), dog, ops, out,
+                    stages=J.JFA_BWD_DQ | J.JFA_BWD_DQ_REDUCE)
+    torch.cuda.synchronize()
+    gdq = out["dq_accum"].cpu().numpy().astype(np.float64)
+    assert not np.isnan(gdq).any()
+    bound = 2.0 ** -4 * abs_sum + 2.0 ** -17 * floor_sum + 1e-4 * abs_sum + 1e-6
+    err = np.abs(gdq - dq)
+    assert np.all(err <= bound), float((err - bound).max())
+    assert err.mean() <= 0.25 * bound.mean()

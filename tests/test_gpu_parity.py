@@ -368,6 +368,25 @@ def test_full_size_sampled_parity(cfg):
         assert np.abs(gdq16 - gdq).max() <= 2 ** -8 * np.abs(gdq).max()
 
 
+def beyond_int32_inputs():
+    """Broadcast Q (H=4, D=128, 256 rows) over a first sequence of 4,198,400
+    keys (1,025 copies of one random 4,096-key block; its dO rows zero) and
+    three random ones that start past element 2^31 of K and V. Returns
+    (inputs, length of the first sequence, lengths of the others)."""
+    H, D, lq, blk, reps = 4, 128, 256, 4096, 1025
+    later = [1000, 37, 300]
+    base = _custom("i32", broadcast=True, H=H, D=D, lengths=[blk] + later, lq=lq, seed=9)
+    big = blk * reps
+    assert big * H * D > 2 ** 31
+    lens = np.array([big] + later, dtype=np.int32)
+    tile_rows = lambda a: np.concatenate([np.tile(a[:blk], (reps, 1, 1)), a[blk:]])
+    do = base.do.copy()
+    do[:lq] = 0
+    x = dataclasses.replace(base, lengths=lens, kv_offsets=W.offsets_of(lens), k=tile_rows(base.k),
+                            v=tile_rows(base.v), do=do)
+    return x, big, later
+
+
 def test_element_offsets_beyond_int32():
     """A first sequence of 4,198,400 keys (H=4, D=128: K and V hold more than
     2^31 elements, 4.3 GB each) puts every later sequence past element 2^31,
@@ -377,16 +396,8 @@ def test_element_offsets_beyond_int32():
     are random. Checked against the oracle: O and LSE of two rows of the long
     sequence, O, LSE, dK, dV of the later sequences, every row of dQ."""
     print("element offsets beyond 2^31", flush=True)
-    H, D, lq, blk, reps = 4, 128, 256, 4096, 1025
-    base = _custom("i32", broadcast=True, H=H, D=D, lengths=[blk, 1000, 37, 300], lq=lq, seed=9)
-    big = blk * reps
-    assert big * H * D > 2 ** 31
-    lens = np.array([big, 1000, 37, 300], dtype=np.int32)
-    tile_rows = lambda a: np.concatenate([np.tile(a[:blk], (reps, 1, 1)), a[blk:]])
-    do = base.do.copy()
-    do[:lq] = 0
-    x = dataclasses.replace(base, lengths=lens, kv_offsets=W.offsets_of(lens), k=tile_rows(base.k),
-                            v=tile_rows(base.v), do=do)
+    x, big, later = beyond_int32_inputs()
+    H, D, lq = x.workload.heads, x.workload.head_dim, x.workload.lq
     g = run_gpu(x, canary=True)
     w = x.workload
     off = x.kv_offsets
@@ -407,7 +418,7 @@ def test_element_offsets_beyond_int32():
     assert np.abs(W.bf16_bits_to_f32(go[rows, h]) - o0[:, 0]).max() <= TOL_O
     assert np.abs(glse[h, rows] - lse0[0]).max() <= TOL_O
     # the later sequences, as a batch of their own (broadcast dQ sums them)
-    sub = np.array([0, 1000, 1037, 1337], dtype=np.int32)
+    sub = W.offsets_of(np.array(later))
     q_all = x.as_f64("q")
     k_s = W.bf16_bits_to_f32(x.k[big:]).astype(np.float64)
     v_s = W.bf16_bits_to_f32(x.v[big:]).astype(np.float64)
