@@ -333,13 +333,11 @@ __global__ void __launch_bounds__(kThreads, 1) dq_mx_kernel(DqArgs a) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) sc[mb][r] = 0.f;
                 } else {
+                    // (|dS| <= max <= 448 * 2^e: nothing to clamp)
                     int e = (int)((__float_as_uint(amax) >> 23) & 255) - 127 - 8;
                     if (amax > 448.0f * __uint_as_float((uint32_t)(e + 127) << 23)) ++e;
                     sce[mb] = e;
                     scl[mb] = __uint_as_float((uint32_t)(e + 127) << 23);
-                    const float lim = 448.0f * scl[mb];
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) sc[mb][r] = fminf(fmaxf(sc[mb][r], -lim), lim);
                 }
             }
             const i32x8 ds8 = mx_pack_scaled(sc, scl);
