@@ -417,6 +417,29 @@ class JaggedAttention:
         self.fwd_workspace = (torch.zeros(self.fwd_ws_bytes, dtype=torch.uint8, device=device)
                               if self.fwd_ws_bytes else None)
 
+    def _expect(self, **named):
+        """Raise ValueError unless every given tensor is a contiguous CUDA
+        tensor of its expected shape and dtype (the kernels take raw pointers:
+        a mismatch would read or write out of bounds)."""
+        import torch
+        H, D = self.prob.num_heads, self.prob.head_dim
+        q_rows = self.prob.lq if self.prob.broadcast_q else self.total_q
+        bf, f32 = torch.bfloat16, torch.float32
+        want = {"q": ((q_rows, H, D), bf), "k": ((self.total_kv, H, D), bf),
+                "v": ((self.total_kv, H, D), bf), "o": ((self.total_q, H, D), bf),
+                "d_o": ((self.total_q, H, D), bf), "lse": ((H, self.total_q), f32),
+                "dq": ((q_rows, H, D), bf), "dk": ((self.total_kv, H, D), bf),
+                "dv": ((self.total_kv, H, D), bf), "dq_accum": ((q_rows, H, D), f32),
+                "delta": ((H, self.total_q), f32)}
+        for name, t in named.items():
+            shape, dtype = want[name]
+            if not isinstance(t, torch.Tensor) or not t.is_cuda:
+                raise ValueError("%s: a CUDA tensor is needed" % name)
+            if t.dtype != dtype or tuple(t.shape) != shape or not t.is_contiguous():
+                raise ValueError("%s: expected a contiguous %s tensor of shape %s, got %s %s%s"
+                                 % (name, dtype, shape, t.dtype, tuple(t.shape),
+                                    "" if t.is_contiguous() else " (not contiguous)"))
+
     def forward(self, q, k, v, o=None, lse=None):
         import torch
         H, D = self.prob.num_heads, self.prob.head_dim
@@ -424,6 +447,7 @@ class JaggedAttention:
             o = torch.empty((self.total_q, H, D), dtype=torch.bfloat16, device=self.device)
         if lse is None:
             lse = torch.empty((H, self.total_q), dtype=torch.float32, device=self.device)
+        self._expect(q=q, k=k, v=v, o=o, lse=lse)
         jfa_fwd(self.prob, self.fwd_plan, self.q_offsets, self.kv_offsets, q, k, v, o, lse,
                 self.fwd_workspace, self.fwd_ws_bytes)
         return o, lse
@@ -435,6 +459,7 @@ class JaggedAttention:
             boff = jfa_mx_block_offsets(self.kv_offsets.cpu().numpy())
             self.v_num_blocks = int(boff[-1])
             self.v_block_offsets = torch.from_numpy(boff).to(self.device)
+        self._expect(q=q, k=k, v=v)
         H, D = self.prob.num_heads, self.prob.head_dim
         u8 = dict(dtype=torch.uint8, device=self.device)
         mxq = dict(qc=torch.empty(q.shape, **u8), qs=torch.empty((H, q.shape[0], D // 32), **u8),
@@ -455,6 +480,7 @@ class JaggedAttention:
             o = torch.empty((self.total_q, H, D), dtype=torch.bfloat16, device=self.device)
         if lse is None:
             lse = torch.empty((H, self.total_q), dtype=torch.float32, device=self.device)
+        self._expect(o=o, lse=lse)
         jfa_fwd_mx(self.prob, self.fwd_plan, self.q_offsets, self.kv_offsets, self.v_block_offsets,
                    self.v_num_blocks, mxq["qc"], mxq["qs"], mxq["kc"], mxq["ks"], mxq["vc"],
                    mxq["vs"], o, lse, self.fwd_workspace, self.fwd_ws_bytes)
@@ -464,6 +490,7 @@ class JaggedAttention:
         """The further MXFP8 encodings of the MXFP8 dQ pass: V and dO along d,
         K along the keys of its sequence (added to quantize_mx's dict)."""
         import torch
+        self._expect(k=k, v=v, d_o=d_o)
         H, D = self.prob.num_heads, self.prob.head_dim
         u8 = dict(dtype=torch.uint8, device=self.device)
         ops = dict(mxq)
@@ -488,6 +515,8 @@ class JaggedAttention:
                        delta=torch.empty((self.prob.num_heads, self.total_q), dtype=torch.float32,
                                          device=self.device))
         if stages & JFA_BWD_DQ:
+            self._expect(o=o, lse=lse, d_o=d_o, dq=out["dq"], dq_accum=out["dq_accum"],
+                         delta=out["delta"])
             jfa_bwd_dq_mx(self.prob, self.dq_plan, self.q_offsets, self.kv_offsets,
                           self.v_block_offsets, self.v_num_blocks, o, lse, d_o, ops, out["dq"],
                           out["dq_accum"], out["delta"], self.workspace, self.ws_bytes)
@@ -503,6 +532,8 @@ class JaggedAttention:
                        dq_accum=torch.empty(q.shape, dtype=torch.float32, device=self.device),
                        delta=torch.empty((self.prob.num_heads, self.total_q), dtype=torch.float32,
                                          device=self.device))
+        self._expect(q=q, k=k, v=v, o=o, lse=lse, d_o=d_o,
+                     **{n: out[n] for n in ("dq", "dk", "dv", "dq_accum", "delta")})
         jfa_bwd_stages(stages, self.prob, self.bwd_plan, self.dq_plan, self.q_offsets,
                        self.kv_offsets, q, k, v, o, lse, d_o, out["dq"], out["dk"], out["dv"],
                        out["dq_accum"], out["delta"], self.workspace, self.ws_bytes)

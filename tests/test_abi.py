@@ -235,3 +235,38 @@ def test_bwd_dq_mx_validation_returns_before_launch():
     p64 = _prob(head_dim=64)
     dq64 = J.jfa_plan_build(p64, None, [0, 3, 5], None, J.JFA_PASS_DQ, 4)
     assert _call_dq_mx(p64, dq64, J.jfa_bwd_workspace_bytes(p64, dq64.info), nkb=2) == J.JFA_ERR_UNSUPPORTED
+
+
+def test_jagged_attention_rejects_mismatched_tensors(monkeypatch):
+    """The high-level wrapper checks every tensor before anything reaches the
+    kernels (raw pointers: a wrong shape, dtype or layout would be read out of
+    bounds). Runs without a GPU: the checks come first, so CPU tensors are
+    refused as well."""
+    torch = pytest.importorskip("torch")
+    prob = _prob(head_dim=64, lq=8)
+    att = J.JaggedAttention.__new__(J.JaggedAttention)
+    att.prob, att.total_q, att.total_kv = prob, 16, 5
+    good = dict(q=(8, 1, 64), k=(5, 1, 64), v=(5, 1, 64), o=(16, 1, 64), d_o=(16, 1, 64))
+
+    class T:   # stands in for a CUDA tensor (shape, dtype, layout only)
+        def __init__(self, shape, dtype=torch.bfloat16, contiguous=True):
+            self.shape, self.dtype, self._c = shape, dtype, contiguous
+            self.is_cuda = True
+
+        def is_contiguous(self):
+            return self._c
+    monkeypatch.setattr(torch, "Tensor", T)
+    att._expect(**{n: T(s) for n, s in good.items()}, lse=T((1, 16), torch.float32))
+    for bad in (dict(q=T((16, 1, 64))),                       # per-sequence shape, broadcast problem
+                dict(k=T((5, 1, 64), torch.float16)),          # wrong dtype
+                dict(v=T((5, 1, 64), contiguous=False)),       # a view
+                dict(lse=T((1, 16))),                          # bf16 LSE
+                dict(delta=T((16, 1), torch.float32))):        # transposed
+        with pytest.raises(ValueError):
+            att._expect(**bad)
+    class Host(T):
+        def __init__(self, shape):
+            super().__init__(shape)
+            self.is_cuda = False
+    with pytest.raises(ValueError):
+        att._expect(o=Host((16, 1, 64)))
