@@ -427,6 +427,10 @@ def main():
         "bwd_preprocess_standalone_ms": pre_ms,
         "mfma_busy_pct_counters": {n: float(c["mfma_busy_pct"]) for n, c in cnt.items()
                                    if c and "mfma_busy_pct" in c},
+        # achieved shader clock: GRBM_GUI_ACTIVE per launch (summed over the
+        # 8 XCDs, from the committed counter run) over this run's mean launch
+        "clock_ghz_counters": {n: float(c["grbm_gui_active"]) / 8 / (per_mean[n] * 1e-3) / 1e9
+                               for n, c in cnt.items() if c and "grbm_gui_active" in c},
         "plan_host_ms": plan_ms,
         "roofline": roof,
     }
