@@ -468,3 +468,31 @@ def test_long_sequence_sampled():
     ref = A.broadcast_dq_rows(_head_f64(x.q, h), _head_f64(x.k, h), _head_f64(x.v, h),
                               _head_f64(x.do, h), x.kv_offsets, 0, rows, scale=w.scale)
     assert rel_err(gdq[rows, h], ref) <= TOL_GRAD
+
+
+@pytest.mark.parametrize("kind", ["empty_batch", "all_empty_sequences", "perseq_all_empty"])
+def test_degenerate_batches(kind):
+    """No sequence at all (B = 0, a broadcast Q of 7 rows), three empty
+    sequences under a broadcast Q of 5 rows, and per-sequence Q with empty Q
+    and KV everywhere: every kernel either launches nothing or writes the
+    defined values (O = 0, LSE = -inf, delta = 0, dQ = 0; the oracle's
+    reading of rows without a visible key), and no canary survives."""
+    print("degenerate batch", kind, flush=True)
+    if kind == "empty_batch":
+        x = _custom("e0", broadcast=True, H=2, D=64, lengths=[], lq=7)
+    elif kind == "all_empty_sequences":
+        x = _custom("e1", broadcast=True, H=2, D=128, lengths=[0, 0, 0], lq=5)
+    else:
+        x = _custom("e2", broadcast=False, H=2, D=64, lengths=[0, 0], q_lengths=[0, 0])
+    g = run_gpu(x, canary=True)
+    o, lse, dq, dk, dv, delta = oracle_full(x)
+    go = host_f64(g.o)
+    assert go.shape == o.shape and np.array_equal(go, np.zeros_like(go))
+    glse = g.lse.cpu().numpy()
+    assert glse.shape == lse.shape and np.all(glse == -np.inf) and np.all(lse == -np.inf)
+    for got, ref in ((g.dq_accum.cpu().numpy(), dq), (host_f64(g.dq), dq)):
+        assert got.shape == ref.shape and np.array_equal(got, np.zeros_like(got))
+        assert np.array_equal(ref, np.zeros_like(ref))
+    assert g.dk.numel() == 0 and g.dv.numel() == 0
+    if x.t_q > 0:
+        assert np.array_equal(g.delta.cpu().numpy(), np.zeros((x.workload.heads, x.t_q)))
