@@ -245,7 +245,8 @@ int32_t jfa_fwd(const jfa_problem* prob, const jfa_plan_info* info,
  * clamped. Layouts: Q codes [q rows, H, D] with scales [H, q rows, D/32]
  * (q rows = lq when broadcast, else T_q); K codes [T_k, H, D] with scales
  * [H, T_k, D/32]; V codes [T_k, H, D] with scales [H, NB, D], the blocks of
- * sequence b starting at block_offsets[b] and NB = block_offsets[B].
+ * sequence b starting at block_offsets[b] and NB = block_offsets[B]. Codes
+ * are 16-byte aligned, scales 4-byte aligned; an empty array may be NULL.
  */
 /* block_offsets[0] = 0, block_offsets[b+1] = block_offsets[b] + ceil(L_b/32)
  * for the lengths given by h_kv_offsets [B+1] (host arrays). */
@@ -366,7 +367,8 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device
  * along keys: codes [T_k, H, D], scales [H, NB, D] with the blocks of
  * sequence b starting at d_key_block_offsets[b] (device copy of
  * jfa_mx_block_offsets' output, NB = num_key_blocks). Scale arrays 4-byte
- * aligned, codes 16-byte aligned; the caller owns everything.
+ * aligned, codes 16-byte aligned (either may be NULL when it is empty); the
+ * caller owns everything.
  */
 typedef struct jfa_mx_bwd_operands {
     const void* q_codes;

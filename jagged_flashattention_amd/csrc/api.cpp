@@ -69,6 +69,12 @@ bool tensor_ok(const void* ptr, int64_t elems) {
     return ptr != nullptr && aligned16(ptr);
 }
 
+// E8M0 scale arrays (read a dword at a time): may be NULL when empty
+bool scales_ok(const void* ptr, int64_t bytes) {
+    if (bytes == 0) return true;
+    return ptr != nullptr && aligned4(ptr);
+}
+
 }  // namespace
 
 extern "C" {
@@ -244,9 +250,11 @@ int32_t jfa_fwd_mx(const jfa_problem* prob, const jfa_plan_info* info, const int
     // one 32-key V block per 32 keys of each sequence: at least T_k / 32
     if (num_blocks < (info->total_kv + 31) / 32 || d_block_offsets == nullptr) return JFA_ERR_INVALID_ARG;
     const int64_t hd = (int64_t)prob->num_heads * prob->head_dim;
+    const int64_t H = prob->num_heads, nbd = prob->head_dim / 32;
     if (!tensor_ok(q_codes, (int64_t)a.q_rows * hd) || !tensor_ok(k_codes, info->total_kv * hd) ||
-        !tensor_ok(v_codes, info->total_kv * hd) || q_scales == nullptr || k_scales == nullptr ||
-        v_scales == nullptr || !aligned4(q_scales) || !aligned4(k_scales) || !aligned4(v_scales))
+        !tensor_ok(v_codes, info->total_kv * hd) || !scales_ok(q_scales, H * a.q_rows * nbd) ||
+        !scales_ok(k_scales, H * info->total_kv * nbd) ||
+        !scales_ok(v_scales, H * (int64_t)num_blocks * prob->head_dim))
         return JFA_ERR_INVALID_ARG;
     a.q8 = static_cast<const uint8_t*>(q_codes);
     a.k8 = static_cast<const uint8_t*>(k_codes);
@@ -419,9 +427,12 @@ int32_t jfa_bwd_dq_mx(const jfa_problem* prob, const jfa_device_plan* dq_plan,
         !tensor_ok(ops->k_codes, qi->total_kv * hd) || !tensor_ok(ops->v_codes, qi->total_kv * hd) ||
         !tensor_ok(ops->do_codes, qi->total_q * hd) || !tensor_ok(ops->kk_codes, qi->total_kv * hd))
         return JFA_ERR_INVALID_ARG;
-    const void* scs[5] = {ops->q_scales, ops->k_scales, ops->v_scales, ops->do_scales, ops->kk_scales};
-    for (const void* p : scs)
-        if (p == nullptr || !aligned4(p)) return JFA_ERR_INVALID_ARG;
+    const int64_t H = prob->num_heads, nbd = prob->head_dim / 32;
+    if (!scales_ok(ops->q_scales, H * q_rows * nbd) || !scales_ok(ops->k_scales, H * qi->total_kv * nbd) ||
+        !scales_ok(ops->v_scales, H * qi->total_kv * nbd) ||
+        !scales_ok(ops->do_scales, H * qi->total_q * nbd) ||
+        !scales_ok(ops->kk_scales, H * (int64_t)num_key_blocks * prob->head_dim))
+        return JFA_ERR_INVALID_ARG;
     if (!bcast && (!tensor_ok(dq, qi->total_q * hd) || dq_accum == nullptr)) return JFA_ERR_INVALID_ARG;
     if (qi->num_tiles == 0) return JFA_OK;
     const jfa::Band bd = jfa::band_of(prob);

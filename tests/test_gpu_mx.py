@@ -361,3 +361,29 @@ def test_mx_element_offsets_beyond_int32():
     err = np.abs(gdq - dq)
     assert np.all(err <= bound), float((err - bound).max())
     assert err.mean() <= 0.25 * bound.mean()
+
+
+def test_mx_only_empty_sequences():
+    """Three empty sequences under a broadcast Q of 5 rows through the MXFP8
+    encoders, forward and dQ pass: O = 0, LSE = -inf, delta = 0, dQ = 0 (rows
+    without a visible key), no canary left."""
+    x = _custom("me", broadcast=True, H=2, D=128, lengths=[0, 0, 0], lq=5)
+    prob = problem_of(x)
+    att = J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask)
+    qg, kg, vg, dog = dev(x.q), dev(x.k), dev(x.v), dev(x.do)
+    H, D = prob.num_heads, prob.head_dim
+    mxq = att.quantize_mx(qg, kg, vg)
+    o = torch.full((att.total_q, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((H, att.total_q), float("nan"), dtype=torch.float32, device="cuda")
+    att.forward_mx(mxq, o, lse)
+    ops = att.quantize_mx_bwd(mxq, kg, vg, dog)
+    out = dict(dq=torch.full(qg.shape, float("nan"), dtype=torch.bfloat16, device="cuda"),
+               dk=torch.empty_like(kg), dv=torch.empty_like(vg),
+               dq_accum=torch.full(qg.shape, float("nan"), dtype=torch.float32, device="cuda"),
+               delta=torch.full((H, att.total_q), float("nan"), dtype=torch.float32, device="cuda"))
+    att.backward_mx(qg, kg, vg, o, lse, dog, ops, out, stages=J.JFA_BWD_DQ | J.JFA_BWD_DQ_REDUCE)
+    torch.cuda.synchronize()
+    assert float(o.float().abs().max()) == 0.0
+    assert bool(torch.all(lse == float("-inf")))
+    assert float(out["dq_accum"].abs().max()) == 0.0 and float(out["dq"].float().abs().max()) == 0.0
+    assert float(out["delta"].abs().max()) == 0.0
