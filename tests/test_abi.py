@@ -270,3 +270,15 @@ def test_jagged_attention_rejects_mismatched_tensors(monkeypatch):
             self.is_cuda = False
     with pytest.raises(ValueError):
         att._expect(o=Host((16, 1, 64)))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark runs on one GPU: asked for more it says so and exits
+    with status 2 before touching a device."""
+    import subprocess
+    import sys
+    root = __import__("os").path.dirname(__import__("os").path.dirname(__file__))
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=root,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
