@@ -177,8 +177,8 @@ def main():
     ap.add_argument("--mx", type=int, default=1,
                     help="also time the MXFP8 forward and dQ pass on the same inputs (head_dim 128; 0: skip)")
     ap.add_argument("--fwd-plan", choices=("dynamic", "static"), default="dynamic",
-                    help="forward tiles claimed at run time from the sorted list, or the "
-                         "static snake deal")
+                    help="forward tiles claimed at run time from the sorted list (when there "
+                         "are more tiles than workers), or the static snake deal")
     ap.add_argument("--ablation", type=int, default=1,
                     help="also time the kernels with the natural (unsorted, round-robin) plans "
                          "and with the other forward plan (0: skip)")
@@ -219,7 +219,7 @@ def main():
     att = J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask,
                             fwd_workers=cus * args.fwd_workers_per_cu,
                             bwd_workers=cus * args.bwd_workers_per_cu,
-                            fwd_dynamic=args.fwd_plan == "dynamic")
+                            fwd_dynamic=None if args.fwd_plan == "dynamic" else False)
     plan_ms = (time.perf_counter() - t0) * 1e3
     model = work_model(x, att.dq_plan.info.num_workers)
     H, D = w.heads, w.head_dim
@@ -413,7 +413,8 @@ def main():
                    "lengths": w.lengths, "seed": w.seed, "total_kv": model["t_k"],
                    "total_q": model["t_q"],
                    "fwd_workers": att.fwd_plan.info.num_workers,
-                   "fwd_plan": args.fwd_plan,
+                   "fwd_plan": ("dynamic" if att.fwd_plan.info.pass_ & J.JFA_PLAN_DYNAMIC
+                                else "static"),
                    "bwd_workers": att.bwd_plan.info.num_workers,
                    "dq_workers": att.dq_plan.info.num_workers},
         "pct_mfma_peak": 100.0 * value / PEAK_BF16_TFLOPS,

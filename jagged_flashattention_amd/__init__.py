@@ -385,15 +385,23 @@ class JaggedAttention:
 
     def __init__(self, prob: Problem, kv_offsets, q_offsets=None, block_mask=None,
                  fwd_workers: Optional[int] = None, bwd_workers: Optional[int] = None,
-                 dq_workers: Optional[int] = None, fwd_dynamic: bool = True,
+                 dq_workers: Optional[int] = None, fwd_dynamic: Optional[bool] = None,
                  natural_plans: bool = False, device="cuda"):
-        """natural_plans: the unsorted round-robin plans (the ablation
-        baseline) for all three passes; the forward is then static."""
+        """fwd_dynamic: True claims forward tiles at run time, False deals
+        them statically, None (default) claims them only when there are more
+        tiles than workers (with no more, each worker has at most one tile
+        and the claims would only cost their atomics). natural_plans: the
+        unsorted round-robin plans (the ablation baseline) for all three
+        passes; the forward is then static."""
         import torch
         self.prob = prob
         self.device = device
         cus = jfa_device_workers(torch.device(device).index or 0)
         nat = JFA_PLAN_NATURAL if natural_plans else 0
+        if fwd_dynamic is None and not natural_plans:
+            qi = jfa_plan_query(prob, q_offsets, kv_offsets, block_mask, JFA_PASS_FWD,
+                                fwd_workers or cus)
+            fwd_dynamic = qi.num_tiles > qi.num_workers
         fwd_pass = JFA_PASS_FWD | (JFA_PLAN_DYNAMIC if fwd_dynamic and not natural_plans else nat)
         self.fwd_plan_host = jfa_plan_build(prob, q_offsets, kv_offsets, block_mask,
                                             fwd_pass, fwd_workers or cus)
