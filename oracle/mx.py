@@ -32,6 +32,14 @@ quantisation happens inside the kernel, in whichever order its online softmax
 visits the keys; the oracle keeps P exact and the tests bound the difference
 (every P element is rounded to E4M3 with a relative error of at most 2^-4,
 or, below E4M3's normal range, an absolute error of at most 2^-18).
+
+The same page reports the MXFP8 version's backward at parity on dense shapes
+without describing it. ``dq_mx`` is the plainest reading for the dQ pass:
+every product of the FlashAttention dQ computation on MXFP8 operands, each
+encoded along that product's contraction dimension (Q, K, dO, V along d for
+S and dP; K along the keys of its sequence for dQ = dS K), with delta from
+the bf16 dO and O. The kernel rounds dS to E4M3 on the fly; the oracle keeps
+it exact and the tests bound the rounding.
 """
 from __future__ import annotations
 
@@ -152,8 +160,10 @@ def dequantize_v(codes, scales, kv_offsets):
 
 def dq_mx(q_d, k_d, v_d, do_d, k_keys, do, o, lse, kv_offsets, *, scale, broadcast_q,
           q_offsets=None, causal=False, block_mask=None, window=None):
-    """What the MXFP8 dQ pass computes, with dS kept exact (the kernel rounds
-    it to E4M3 per (row, 32-key tile); tests bound that rounding).
+    """What the MXFP8 dQ pass computes ([radar] section "The turning point":
+    the MXFP8 version's backward; the reading is in the module header), with
+    dS kept exact (the kernel rounds it to E4M3 per (row, 32-key tile);
+    tests bound that rounding).
 
     Per sequence and head, with every operand float64 and already decoded:
       S     = scale * q_d k_d^T          (Q and K encoded along d)
