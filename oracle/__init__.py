@@ -6,8 +6,11 @@ benchmark's CPU-baseline leg use it. It shares no code with the HIP library.
 
 Modules
   attention  exact attention forward/backward, evaluated per sequence and head
-  planner    the host tile plan (sort by KV work, zigzag deal) and the
-             block-sparse row/column lists, as integer reference
+  planner    the host tile plan (sort by KV work, zigzag deal, the natural
+             ablation plan) and the block-sparse row/column lists, as
+             integer reference
+  mx         the MXFP8 encoding (OCP E4M3 elements, E8M0 block scales) and
+             the MXFP8 dQ pass on decoded operands
 
 Every function states the passage it follows. All three pages used are about
 the same kernel:
