@@ -93,8 +93,23 @@ def work_model(x, dq_workers: int = 256):
 
 def cpu_baseline(x, budget_s: float):
     """The fp64 oracle (as it stands) on the first sequences of the same
-    workload until ``budget_s`` seconds of CPU work are spent."""
-    from threadpoolctl import threadpool_info
+    workload until ``budget_s`` seconds of CPU work are spent, its BLAS
+    threads pinned to the host cores this process may use (the CPU set of
+    the process, capped by OMP_NUM_THREADS where that is set)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    import numpy as np
+    threads = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        threads = min(threads, int(os.environ["OMP_NUM_THREADS"]))
+    with threadpool_limits(limits=threads, user_api="blas"):
+        used = max([p.get("num_threads", 1) for p in threadpool_info()
+                    if p.get("user_api") == "blas"] or [1])
+        res = _oracle_sample(x, budget_s)
+    res["cores"] = used
+    return res
+
+
+def _oracle_sample(x, budget_s: float):
     import numpy as np
     from oracle import attention as A
     import workloads as W
@@ -137,9 +152,7 @@ def cpu_baseline(x, budget_s: float):
         done += 1
         if t_used >= budget_s:
             break
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                   if p.get("internal_api") in ("openblas", "mkl", "blis")] or [1])
-    return {"value": flop / t_used / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": flop / t_used / 1e12, "unit": "TFLOP/s", "cores": None, "kind": "oracle",
             "sample": "fp64 oracle fwd+bwd of the first %d of %d sequences (all %d heads) of the "
                       "same workload, %.1f s" % (done, x.batch, w.heads, t_used)}
 
@@ -157,13 +170,38 @@ def counters_for(kernel: str, workload: str):
         if "=" in line and not line.startswith("#"):
             a, b = line.split("=", 1)
             kv[a.strip()] = b.strip()
-    src = os.path.join(ROOT, "jagged_flashattention_amd", "csrc", kv.get("source", ""))
-    if not os.path.exists(src):
-        return None
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if digest != kv.get("source_sha256_16"):
+    digest = source_digest(kv.get("source", ""))
+    if digest is None or digest != kv.get("source_sha256_16"):
         return None
     return kv
+
+
+def source_digest(name: str):
+    """sha256 (first 16 hex digits) of a kernel source together with every
+    header it includes from the library's own directories (transitively), so
+    that a change to shared inner-loop code also marks a counter summary
+    stale; None if the source does not exist."""
+    import hashlib
+    import re
+    dirs = [os.path.join(ROOT, "jagged_flashattention_amd", "csrc"), os.path.join(ROOT, "include")]
+    first = os.path.join(dirs[0], name)
+    if not name or not os.path.exists(first):
+        return None
+    seen, todo, h = [], [first], hashlib.sha256()
+    while todo:
+        path = todo.pop(0)
+        if path in seen:
+            continue
+        seen.append(path)
+        text = open(path, "rb").read()
+        h.update(os.path.basename(path).encode() + b"\0" + text)
+        for inc in re.findall(rb'^\s*#\s*include\s+"([^"]+)"', text, re.M):
+            for d in dirs:
+                cand = os.path.join(d, inc.decode())
+                if os.path.exists(cand):
+                    todo.append(cand)
+                    break
+    return h.hexdigest()[:16]
 
 
 def main():
@@ -215,12 +253,17 @@ def main():
                      window_left=-1 if w.window is None or w.window[0] is None else w.window[0],
                      window_right=-1 if w.window is None or w.window[1] is None else w.window[1])
     cus = J.jfa_device_workers(0)
-    t0 = time.perf_counter()
-    att = J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask,
-                            fwd_workers=cus * args.fwd_workers_per_cu,
-                            bwd_workers=cus * args.bwd_workers_per_cu,
-                            fwd_dynamic=None if args.fwd_plan == "dynamic" else False)
-    plan_ms = (time.perf_counter() - t0) * 1e3
+    mk_att = lambda: J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask,
+                                       fwd_workers=cus * args.fwd_workers_per_cu,
+                                       bwd_workers=cus * args.bwd_workers_per_cu,
+                                       fwd_dynamic=None if args.fwd_plan == "dynamic" else False)
+    att = mk_att()
+    # host planning: the three plans on the CPU, then their one copy to the
+    # device (median of a few re-plans; the first also pays for warm-up)
+    replans = [mk_att() for _ in range(5)]
+    plan_ms = {"planner_ms": float(np.median([a.planner_ms for a in replans])),
+               "upload_ms": float(np.median([a.upload_ms for a in replans]))}
+    del replans
     model = work_model(x, att.dq_plan.info.num_workers)
     H, D = w.heads, w.head_dim
     def outputs():

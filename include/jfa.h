@@ -16,8 +16,9 @@
  * Visible keys: every key of the row's own sequence; with causal=1 only keys
  * j <= i (local indices); with a sliding window only keys
  * i - window_left <= j <= i + window_right (the pages name sliding-window
- * attention among the variants the kernel serves, theclarity.today second
- * paragraph, without defining it: this band is the usual meaning; causal is
+ * attention among the variants the kernel serves, theclarity.today fourth
+ * paragraph and ainewsbites.com section "Why attention in GEM needed a
+ * rewrite", without defining it: this band is the usual meaning; causal is
  * the band with no left bound and right bound 0); with a block mask only keys
  * whose 128-key block is kept for the row's 128-row Q tile ("TLX porta
  * l'attenzione jagged su Blackwell" (ai-radar.it), section "The turning

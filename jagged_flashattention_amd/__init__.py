@@ -10,6 +10,7 @@ from __future__ import annotations
 import ctypes
 import dataclasses
 import os
+import time
 from typing import Optional
 
 import numpy as np
@@ -251,6 +252,39 @@ def to_device(plan: HostPlan, device="cuda") -> DevicePlan:
                       f(plan.sparse_ptr), f(plan.sparse_idx))
 
 
+def upload_int32(arrays, device="cuda"):
+    """Device copies of several host int32 arrays (None stays None) made by
+    one host-to-device copy of their concatenation: views into one device
+    buffer, each starting on a 16-byte boundary."""
+    import torch
+    parts, starts, n = [], [], 0
+    for a in arrays:
+        if a is None:
+            starts.append(None)
+            continue
+        a = np.ascontiguousarray(a, dtype=np.int32).reshape(-1)
+        starts.append((n, a.size))
+        parts.append((n, a))
+        n += -(-max(a.size, 1) // 4) * 4
+    host = np.zeros(max(n, 4), dtype=np.int32)
+    for off, a in parts:
+        host[off:off + a.size] = a
+    dev = torch.from_numpy(host).to(device)
+    return [None if st is None else dev[st[0]:st[0] + st[1]] for st in starts]
+
+
+def plans_to_device(plans, extra=(), device="cuda"):
+    """DevicePlans of several host plans plus device copies of the ``extra``
+    int32 arrays, all from one host-to-device copy."""
+    arrays = []
+    for p in plans:
+        arrays += [p.worker_ptr, p.tiles.reshape(-1), p.sparse_ptr, p.sparse_idx]
+    arrays += list(extra)
+    dev = upload_int32(arrays, device)
+    out = [DevicePlan(p.info, *dev[4 * i:4 * i + 4]) for i, p in enumerate(plans)]
+    return out, dev[4 * len(plans):]
+
+
 def jfa_fwd_workspace_bytes(prob: Problem, info: JfaPlanInfo) -> int:
     """Device scratch bytes jfa_fwd needs for a FWD plan (the counter of a
     dynamic plan)."""
@@ -293,7 +327,8 @@ def _c_plan(plan: DevicePlan) -> JfaDevicePlan:
 def jfa_bwd(prob: Problem, kv_plan: DevicePlan, dq_plan: DevicePlan, q_offsets, kv_offsets, q, k,
             v, o, lse, d_o, dq, dk, dv, dq_accum, delta, workspace=None,
             workspace_bytes: int = 0, stream=None) -> None:
-    """Enqueue the whole backward (preprocess, dK/dV, dQ, dQ reduce) on ``stream``."""
+    """Enqueue the whole backward on ``stream``: the dQ pass (which also forms
+    delta = rowsum(dO * O)), dK/dV, and with a broadcast Q the dQ reduce."""
     jfa_bwd_stages(JFA_BWD_ALL, prob, kv_plan, dq_plan, q_offsets, kv_offsets, q, k, v, o, lse,
                    d_o, dq, dk, dv, dq_accum, delta, workspace, workspace_bytes, stream)
 
@@ -403,17 +438,23 @@ class JaggedAttention:
                                 fwd_workers or cus)
             fwd_dynamic = qi.num_tiles > qi.num_workers
         fwd_pass = JFA_PASS_FWD | (JFA_PLAN_DYNAMIC if fwd_dynamic and not natural_plans else nat)
+        t0 = time.perf_counter()
         self.fwd_plan_host = jfa_plan_build(prob, q_offsets, kv_offsets, block_mask,
                                             fwd_pass, fwd_workers or cus)
         self.bwd_plan_host = jfa_plan_build(prob, q_offsets, kv_offsets, block_mask,
                                             JFA_PASS_BWD | nat, bwd_workers or cus)
         self.dq_plan_host = jfa_plan_build(prob, q_offsets, kv_offsets, block_mask,
                                            JFA_PASS_DQ | nat, dq_workers or cus)
-        self.fwd_plan = to_device(self.fwd_plan_host, device)
-        self.bwd_plan = to_device(self.bwd_plan_host, device)
-        self.dq_plan = to_device(self.dq_plan_host, device)
-        self.kv_offsets = torch.from_numpy(_i32(kv_offsets)).to(device)
-        self.q_offsets = None if q_offsets is None else torch.from_numpy(_i32(q_offsets)).to(device)
+        t1 = time.perf_counter()
+        # the three plans and the offsets reach the device in one copy
+        (self.fwd_plan, self.bwd_plan, self.dq_plan), (self.kv_offsets, self.q_offsets) = \
+            plans_to_device([self.fwd_plan_host, self.bwd_plan_host, self.dq_plan_host],
+                            [kv_offsets, q_offsets], device)
+        if torch.device(device).type == "cuda":
+            torch.cuda.synchronize(device)
+        t2 = time.perf_counter()
+        self.planner_ms = (t1 - t0) * 1e3     # the host planner, three passes
+        self.upload_ms = (t2 - t1) * 1e3      # packing and the host-to-device copy
         self.total_q = self.fwd_plan.info.total_q
         self.total_kv = self.fwd_plan.info.total_kv
         self.ws_bytes = jfa_bwd_workspace_bytes(prob, self.dq_plan.info)

@@ -30,8 +30,8 @@ whose 128-key block is kept for the row's 128-row Q tile ([radar] section "The
 turning point": the block-sparse variant iterates only over selected blocks);
 with a sliding window (left, right) only keys i - left <= j <= i + right, a
 bound being None when absent (the pages name sliding-window attention as one
-of the variants the kernel serves -- [clarity] second paragraph, [bites] "Why
-attention in GEM needed a rewrite" -- without defining it; this band of local
+of the variants the kernel serves -- [clarity] fourth paragraph, [bites] "Why
+attention in GEM needed a rewrite", [radar] introduction -- without defining it; this band of local
 indices is the usual meaning, and causal is the band (None, 0)).
 A row with no visible key has O = 0, LSE = -inf and contributes no gradient.
 

@@ -27,6 +27,29 @@ def _brute_work(pass_, b, t, lq_b, lk_b, bm, bn, causal, mask, window=None):
     return len(set(int(i) // bm for i in rows))
 
 
+def _simulated_bwd_cost(r, qlens, kvlens, bm, bn, causal, mask, window=None):
+    """The backward tile's cost under the plan's cost model, by walking it:
+    the Q blocks the tile visits are found from the visibility rule (blocks
+    holding a row that sees one of the tile's keys), and each visited block
+    costs BWD_BLOCK_FIXED plus one unit per wave (BWD_WAVE_KEYS consecutive
+    keys of the tile) that holds at least one key inside the sequence; the
+    tile adds BWD_TILE_FIXED. The record's work field is not used."""
+    b, _, t, _ = (int(v) for v in r)
+    lq_b, lk_b = int(qlens[b]), int(kvlens[b])
+    keys = np.arange(t * bn, min((t + 1) * bn, lk_b))
+    mask_b = None if mask is None else mask[b]
+    vis = A.visibility(lq_b, lk_b, causal=causal, mask_b=mask_b, window=window)[:, keys]
+    blocks = sorted(set(int(i) // bm for i in np.nonzero(vis.any(axis=1))[0]))
+    cost = P.BWD_TILE_FIXED
+    for _ in blocks:
+        cost += P.BWD_BLOCK_FIXED
+        for wave in range(bn // P.BWD_WAVE_KEYS):
+            lo = t * bn + wave * P.BWD_WAVE_KEYS
+            if any(lo <= int(k) < lo + P.BWD_WAVE_KEYS for k in keys):
+                cost += 1
+    return cost
+
+
 def _cases():
     rng = np.random.default_rng(0)
     lens = rng.integers(1, 700, size=9)
@@ -73,11 +96,7 @@ def test_plan_properties(name, qlens, kvlens, causal, mask, pass_, bm, bn, worke
     def key(r):
         if pass_ == P.FWD:
             return r[3]
-        # backward: work x (fixed per block + waves holding one of the tile's
-        # keys) + fixed per tile, the waves counted from the keys themselves
-        keys = min(bn, kvlens[r[0]] - r[2] * bn)
-        waves = len(set(k // P.BWD_WAVE_KEYS for k in range(keys)))
-        return r[3] * (P.BWD_BLOCK_FIXED + waves) + P.BWD_TILE_FIXED
+        return _simulated_bwd_cost(r, qlens, kvlens, bm, bn, causal, mask)
     works = [key(r) for r in order]
     assert all(works[i] >= works[i + 1] for i in range(n - 1))
     # stable: equal keys keep (b, h, t) enumeration order
