@@ -345,6 +345,29 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device
                        void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * jfa_bwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. The
+ * same backward with the same arguments except the workspace, which is a
+ * scratch area of JFA_NOALLOC_SCRATCH_BYTES inside the library itself, one
+ * per GPU (each GPU the library runs on holds it until the process ends);
+ * the call allocates and frees nothing. Returns JFA_ERR_WORKSPACE, before
+ * anything is launched, when the DQ plan needs more than that
+ * (jfa_bwd_workspace_bytes: with a broadcast Q, 256 * head_dim * 4 bytes per
+ * dQ worker, i.e. at most 256 dQ workers at head_dim 128 and 512 at 64;
+ * per-sequence Q needs none). Nothing in the area has to start at zero: every
+ * dQ worker writes its whole partial before the reduce reads it. Every call
+ * on one GPU uses the same area, which keeps the last call's contents: two
+ * calls whose work overlaps in time on one GPU (streams not ordered by
+ * events) race on it, so order them.
+ */
+#define JFA_NOALLOC_SCRATCH_BYTES (32 << 20)
+int32_t jfa_bwd_noalloc(const jfa_problem* prob, const jfa_device_plan* kv_plan,
+                        const jfa_device_plan* dq_plan, const int32_t* d_q_offsets,
+                        const int32_t* d_kv_offsets, const void* q, const void* k, const void* v,
+                        const void* o, const float* lse, const void* d_o,
+                        void* dq, void* dk, void* dv, float* dq_accum, float* delta, void* stream);
+
+/*
  * MXFP8 dQ pass ("TLX porta l'attenzione jagged su Blackwell" (ai-radar.it),
  * section "The turning point": the MXFP8 version of the kernel; its backward,
  * here the dQ pass): the JFA_BWD_DQ stage with its three products as

@@ -37,6 +37,7 @@ EXPORTS = (
     "jfa_offsets_from_lengths", "jfa_plan_query", "jfa_plan_build", "jfa_fwd_workspace_bytes",
     "jfa_fwd", "jfa_bwd_workspace_bytes", "jfa_bwd", "jfa_bwd_stages", "jfa_mx_block_offsets",
     "jfa_mx_quantize_rows", "jfa_mx_quantize_v", "jfa_fwd_mx", "jfa_bwd_dq_mx",
+    "jfa_bwd_noalloc",
 )
 JFA_BWD_PREPROCESS = 1
 JFA_BWD_DQ = 2
@@ -113,6 +114,7 @@ def _lib():
             "jfa_bwd_workspace_bytes": (i32, [prob, info, ctypes.POINTER(i64)]),
             "jfa_bwd": (i32, [prob, dplan, dplan] + [_P] * 14 + [i64, _P]),
             "jfa_bwd_stages": (i32, [i32, prob, dplan, dplan] + [_P] * 14 + [i64, _P]),
+            "jfa_bwd_noalloc": (i32, [prob, dplan, dplan] + [_P] * 14),
             "jfa_mx_block_offsets": (i32, [_P, i32, _P]),
             "jfa_mx_quantize_rows": (i32, [_P, i64, i32, i32, _P, _P, _P]),
             "jfa_mx_quantize_v": (i32, [_P, _P, _P, i32, i32, i32, i32, _P, _P, _P]),
@@ -345,6 +347,24 @@ def jfa_bwd_stages(stages: int, prob: Problem, kv_plan: DevicePlan, dq_plan: Dev
                                  _dev_ptr(d_o), _dev_ptr(dq), _dev_ptr(dk), _dev_ptr(dv),
                                  _dev_ptr(dq_accum), _dev_ptr(delta), _dev_ptr(workspace),
                                  int(workspace_bytes), _stream(stream)), "jfa_bwd_stages")
+
+
+JFA_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def jfa_bwd_noalloc(prob: Problem, kv_plan: DevicePlan, dq_plan: DevicePlan, q_offsets,
+                    kv_offsets, q, k, v, o, lse, d_o, dq, dk, dv, dq_accum, delta,
+                    stream=None) -> None:
+    """The whole backward like jfa_bwd, with the library's own scratch area
+    in place of a workspace (nothing is allocated by the call)."""
+    cp = prob.c()
+    kp, qp = _c_plan(kv_plan), _c_plan(dq_plan)
+    _check(_lib().jfa_bwd_noalloc(ctypes.byref(cp), ctypes.byref(kp), ctypes.byref(qp),
+                                  _dev_ptr(q_offsets), _dev_ptr(kv_offsets), _dev_ptr(q),
+                                  _dev_ptr(k), _dev_ptr(v), _dev_ptr(o), _dev_ptr(lse),
+                                  _dev_ptr(d_o), _dev_ptr(dq), _dev_ptr(dk), _dev_ptr(dv),
+                                  _dev_ptr(dq_accum), _dev_ptr(delta), _stream(stream)),
+           "jfa_bwd_noalloc")
 
 
 # ------------------------------------------------------------------ MXFP8

@@ -282,3 +282,25 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_bwd_noalloc_rejects_plans_beyond_its_scratch():
+    """jfa_bwd_noalloc returns JFA_ERR_WORKSPACE, before touching the GPU,
+    for a DQ plan whose partials exceed the library's scratch area: a
+    broadcast Q of 16 heads x 8,192 rows has 512 (head, Q tile) groups, so
+    512 dQ workers x 256 x 128 x 4 bytes = 64 MiB > 32 MiB."""
+    prob = J.Problem(batch=2, num_heads=16, head_dim=128, broadcast_q=True, lq=8192,
+                     softmax_scale=0.088)
+    kv = J.jfa_plan_build(prob, None, [0, 3, 5], None, J.JFA_PASS_BWD, 256)
+    dq = J.jfa_plan_build(prob, None, [0, 3, 5], None, J.JFA_PASS_DQ, 256)
+    assert J.jfa_bwd_workspace_bytes(prob, dq.info) == 64 << 20 > J.JFA_NOALLOC_SCRATCH_BYTES
+    plans = [J.JfaDevicePlan(ctypes.pointer(p.info), 0x1000, 0x1000, None, None) for p in (kv, dq)]
+    cp = prob.c()
+    t = ctypes.c_void_p(0x1000)
+    st = J._lib().jfa_bwd_noalloc(ctypes.byref(cp), ctypes.byref(plans[0]), ctypes.byref(plans[1]),
+                                  None, t, *([t] * 11), None)
+    assert st == J.JFA_ERR_WORKSPACE
+    # a DQ plan of the wrong pass is refused the same way as by jfa_bwd
+    st = J._lib().jfa_bwd_noalloc(ctypes.byref(cp), ctypes.byref(plans[0]), ctypes.byref(plans[0]),
+                                  None, t, *([t] * 11), None)
+    assert st == J.JFA_ERR_PLAN_MISMATCH
