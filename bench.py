@@ -368,6 +368,27 @@ def main():
                    "dq_issued_tflops": 3 * model["dq_flop"] / (mdq_ms * 1e-3) / 1e12,
                    "encode_bwd_ms": qzb_ms})
 
+    # the two second stages of the broadcast-Q dQ reduction, each timed alone
+    # on the same inputs: the per-worker partials plus the fixed-order reduce
+    # (the step's scheme), and fp32 atomic adds into the zeroed dq_accum plus
+    # the bf16 conversion
+    def stage(st):
+        def f(i):
+            qi, ki, vi, doi = sets[i % 2]
+            oi, lsei, outi = outs[i % 2]
+            att.backward(qi, ki, vi, oi, lsei, doi, outi, stages=st)
+        return f
+    dq_scheme = None
+    if w.broadcast_q:
+        at = J.JFA_BWD_DQ_ATOMIC
+        red = (time_alone(stage(J.JFA_BWD_DQ)), time_alone(stage(J.JFA_BWD_DQ_REDUCE)))
+        ato = (time_alone(stage(J.JFA_BWD_DQ | at)), time_alone(stage(J.JFA_BWD_DQ_REDUCE | at)))
+        dq_scheme = {"partials_reduce": {"dq_ms": red[0], "reduce_ms": red[1], "total_ms": sum(red)},
+                     "atomic": {"dq_ms": ato[0], "convert_ms": ato[1], "total_ms": sum(ato)}}
+        # leave the step's outputs as the step's scheme makes them
+        for i in range(2):
+            stage(J.JFA_BWD_DQ | J.JFA_BWD_DQ_REDUCE)(i)
+
     # the standalone delta preprocess (not part of the step: the dQ kernel
     # forms delta itself), timed alone for its HBM rate
     def pre(i):
@@ -482,6 +503,8 @@ def main():
         res["mxfp8"] = mx
     if ablation is not None:
         res["plan_ablation"] = ablation
+    if dq_scheme is not None:
+        res["dq_reduction_schemes"] = dq_scheme
     if args.cpu_budget > 0:
         res["cpu_baseline"] = cpu_baseline(x, args.cpu_budget)
     print(json.dumps(res))

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define JFA_ABI_VERSION 7
+#define JFA_ABI_VERSION 8
 
 /* status codes */
 #define JFA_OK                 0
@@ -337,6 +337,17 @@ int32_t jfa_bwd(const jfa_problem* prob, const jfa_device_plan* kv_plan,
 #define JFA_BWD_DKDV       4   /* dK, dV                                       */
 #define JFA_BWD_DQ_REDUCE  8   /* broadcast Q: dq_accum, dq from the partials  */
 #define JFA_BWD_ALL        14
+/* Modifier of the broadcast-Q dQ reduction (no effect with per-sequence Q):
+ * the second of the two stages the pages describe for the batch-summed dQ
+ * ("Meta's TLX Jagged Flash Attention Beats FA4 on Blackwell"
+ * (ainewsbites.com), section "Optimizations layered on top") done by fp32
+ * atomic adds instead of a fixed-order reduce. With JFA_BWD_DQ the stage
+ * first zeroes dq_accum, then each dQ worker adds its sum over its tiles into
+ * dq_accum with device-scope fp32 atomic adds (no partials are written);
+ * with JFA_BWD_DQ_REDUCE the stage only rounds dq_accum to dq (bf16). The sum
+ * then depends on the order in which the adds land: not bitwise reproducible
+ * from run to run. The workspace is still validated but not used. */
+#define JFA_BWD_DQ_ATOMIC 16
 int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device_plan* kv_plan,
                        const jfa_device_plan* dq_plan, const int32_t* d_q_offsets,
                        const int32_t* d_kv_offsets, const void* q, const void* k, const void* v,

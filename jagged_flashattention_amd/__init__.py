@@ -44,6 +44,7 @@ JFA_BWD_DQ = 2
 JFA_BWD_DKDV = 4
 JFA_BWD_DQ_REDUCE = 8
 JFA_BWD_ALL = 14
+JFA_BWD_DQ_ATOMIC = 16
 
 
 class JfaProblem(ctypes.Structure):

@@ -324,7 +324,8 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device
                        const void* o, const float* lse, const void* d_o, void* dq, void* dk,
                        void* dv, float* dq_accum, float* delta, void* workspace,
                        int64_t workspace_bytes, void* stream) {
-    if (stages < 0 || stages > (JFA_BWD_ALL | JFA_BWD_PREPROCESS)) return JFA_ERR_INVALID_ARG;
+    if (stages < 0 || stages > (JFA_BWD_ALL | JFA_BWD_PREPROCESS | JFA_BWD_DQ_ATOMIC))
+        return JFA_ERR_INVALID_ARG;
     int32_t st = check_plan(prob, kv_plan, JFA_PASS_BWD, d_q_offsets, d_kv_offsets);
     if (st) return st;
     st = check_plan(prob, dq_plan, JFA_PASS_DQ, d_q_offsets, d_kv_offsets);
@@ -349,6 +350,7 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device
     if (tq == 0 && q_rows == 0 && tk == 0) return JFA_OK;
     const jfa::Mode mode = mode_of(prob);
     const bool bcast = prob->broadcast_q != 0;
+    const bool atomic = bcast && (stages & JFA_BWD_DQ_ATOMIC) != 0;
 
     jfa::BwdArgs a;
     a.worker_ptr = kv_plan->worker_ptr;
@@ -381,6 +383,10 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device
         if (st) return st;
     }
 
+    if ((stages & JFA_BWD_DQ) && atomic) {
+        st = hip_status(jfa::launch_dq_zero(dq_accum, q_rows * hd, stream));
+        if (st) return st;
+    }
     if ((stages & JFA_BWD_DQ) && qi->num_tiles > 0) {
         jfa::DqArgs d;
         d.worker_ptr = dq_plan->worker_ptr;
@@ -409,14 +415,17 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device
         d.num_workers = qi->num_workers;
         d.scale = prob->softmax_scale;
         d.scale_log2 = a.scale_log2;
-        st = hip_status(jfa::launch_dq(d, prob->head_dim, mode, bcast, stream));
+        st = hip_status(jfa::launch_dq(d, prob->head_dim, mode, bcast, atomic, stream));
         if (st) return st;
     }
     if (stages & JFA_BWD_DKDV) {
         st = hip_status(jfa::launch_bwd(a, prob->head_dim, mode, bcast, JFA_BWD_DKDV, stream));
         if (st) return st;
     }
-    if ((stages & JFA_BWD_DQ_REDUCE) && bcast) {
+    if ((stages & JFA_BWD_DQ_REDUCE) && atomic) {
+        st = hip_status(jfa::launch_dq_convert(dq_accum, static_cast<uint16_t*>(dq), q_rows * hd, stream));
+        if (st) return st;
+    } else if ((stages & JFA_BWD_DQ_REDUCE) && bcast) {
         jfa::DqReduceArgs r;
         r.worker_ptr = dq_plan->worker_ptr;
         r.partial = static_cast<const float*>(workspace);

@@ -16,13 +16,17 @@
 //     a worker range of its own; each worker sums its tiles in registers
 //     (stage 1) and writes one fp32 partial; a reduce kernel adds the partials
 //     of each group in worker order (stage 2), so the result does not depend
-//     on timing.
+//     on timing. The alternative second stage (ATOMIC): each worker adds its
+//     sum into the zeroed dq_accum with fp32 atomic adds, and a last kernel
+//     rounds dq_accum to bf16.
 // Per 64-key block and wave (32 query rows, one per lane column):
 //   S^T  = K Q^T        A = K rows from LDS,   B = Q^T (VGPRs)
 //   dP^T = V dO^T       A = V rows from LDS,   B = dO^T (VGPRs)
 //   P^T  = exp2(S^T * scale*log2e - LSE*log2e), dS^T = P^T (dP^T - delta)
 //   dQ^T += K^T dS^T    A = K^T from LDS (keys in sigma order), B = dS^T
 // K^T is made once per block from the natural K tile by transposed LDS reads.
+#include <algorithm>
+
 #include "qtile.h"
 
 namespace jfa {
@@ -48,7 +52,7 @@ struct DqLds {
     static_assert(4 * ST_WAVE == BLK, "staging: 4 waves per released block");
 };
 
-template <int D, int MODE, bool BCAST>
+template <int D, int MODE, bool BCAST, bool ATOMIC>
 __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
     using LY = DqLds<D>;
     __shared__ __attribute__((aligned(1024))) char smem[LY::BYTES];
@@ -393,7 +397,25 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
             }
         }
     }
-    if (BCAST) {
+    if (BCAST && ATOMIC) {
+        // this worker's sum over its tiles (all of one (head, Q tile) group)
+        // added into dq_accum, element by element, with fp32 atomic adds (a
+        // worker without tiles adds nothing)
+        __syncthreads();
+        if (t_begin < t_end) {
+            const TileInfo T0 = tile_info(t_begin);
+            float* acc0 = a.dq_accum + (int64_t)T0.h * D;
+            stage_out(s, [&](int r, int chunk, const f32x4& x) {
+                const int row = T0.t * kFwdBlockM + r;
+                if (row < a.lq) {
+                    float* p = acc0 + (int64_t)row * H * D + 4 * chunk;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        __hip_atomic_fetch_add(p + j, x[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            });
+        }
+    } else if (BCAST) {
         // this worker's partial sum over its tiles (all of one (head, Q tile)
         // group): rows 0..255 of the tile, fp32 (zeros for a worker without
         // tiles, so that the reduce reads every partial unconditionally)
@@ -448,26 +470,62 @@ __global__ void __launch_bounds__(256) dq_reduce_kernel(DqReduceArgs a) {
     }
 }
 
-template <int D, int MODE, bool BCAST>
+// dq_accum = 0 (the atomic reduction adds into it)
+__global__ void __launch_bounds__(256) dq_zero_kernel(float* __restrict__ acc, int64_t n4) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+        ((f32x4*)acc)[i] = f32x4{};
+}
+
+// dq = bf16(dq_accum), 4 elements per thread
+__global__ void __launch_bounds__(256) dq_convert_kernel(const float* __restrict__ acc,
+                                                          uint16_t* __restrict__ dq, int64_t n4) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+        ((bf16x4*)dq)[i] = to_bf16x4(((const f32x4*)acc)[i]);
+}
+
+template <int D, int MODE, bool BCAST, bool ATOMIC = false>
 int32_t launch(const DqArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((dq_kernel<D, MODE, BCAST>), dim3(a.num_workers), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((dq_kernel<D, MODE, BCAST, ATOMIC>), dim3(a.num_workers), dim3(kThreads), 0,
+                       stream, a);
     return (int32_t)hipGetLastError();
 }
 
 template <int D>
-int32_t launch_d(const DqArgs& a, Mode mode, bool bcast, hipStream_t s) {
+int32_t launch_d(const DqArgs& a, Mode mode, bool bcast, bool atomic, hipStream_t s) {
     if (mode == kCausal) return launch<D, kCausal, false>(a, s);
-    if (mode == kSparse)
-        return bcast ? launch<D, kSparse, true>(a, s) : launch<D, kSparse, false>(a, s);
-    return bcast ? launch<D, kDense, true>(a, s) : launch<D, kDense, false>(a, s);
+    if (mode == kSparse) {
+        if (!bcast) return launch<D, kSparse, false>(a, s);
+        return atomic ? launch<D, kSparse, true, true>(a, s) : launch<D, kSparse, true>(a, s);
+    }
+    if (!bcast) return launch<D, kDense, false>(a, s);
+    return atomic ? launch<D, kDense, true, true>(a, s) : launch<D, kDense, true>(a, s);
 }
+
+int grid_for(int64_t n4) { return (int)std::max<int64_t>(1, std::min<int64_t>((n4 + 255) / 256, 2048)); }
 
 }  // namespace
 
-int32_t launch_dq(const DqArgs& a, int32_t head_dim, Mode mode, bool broadcast, void* stream) {
+int32_t launch_dq(const DqArgs& a, int32_t head_dim, Mode mode, bool broadcast, bool atomic,
+                  void* stream) {
     hipStream_t s = (hipStream_t)stream;
-    if (head_dim == 64) return launch_d<64>(a, mode, broadcast, s);
-    return launch_d<128>(a, mode, broadcast, s);
+    if (head_dim == 64) return launch_d<64>(a, mode, broadcast, atomic, s);
+    return launch_d<128>(a, mode, broadcast, atomic, s);
+}
+
+int32_t launch_dq_zero(float* dq_accum, int64_t n, void* stream) {
+    if (n == 0) return 0;
+    hipLaunchKernelGGL(dq_zero_kernel, dim3(grid_for(n / 4)), dim3(256), 0, (hipStream_t)stream,
+                       dq_accum, n / 4);
+    return (int32_t)hipGetLastError();
+}
+
+int32_t launch_dq_convert(const float* dq_accum, uint16_t* dq, int64_t n, void* stream) {
+    if (n == 0) return 0;
+    hipLaunchKernelGGL(dq_convert_kernel, dim3(grid_for(n / 4)), dim3(256), 0, (hipStream_t)stream,
+                       dq_accum, dq, n / 4);
+    return (int32_t)hipGetLastError();
 }
 
 int32_t launch_dq_reduce(const DqReduceArgs& a, int32_t head_dim, void* stream) {

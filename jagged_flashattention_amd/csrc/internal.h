@@ -166,8 +166,13 @@ int32_t launch_fwd(const FwdArgs& a, int32_t head_dim, Mode mode, bool broadcast
 int32_t launch_fwd_mx(const FwdArgs& a, Mode mode, bool broadcast, void* stream);
 int32_t launch_bwd(const BwdArgs& a, int32_t head_dim, Mode mode, bool broadcast, int32_t stages,
                    void* stream);
-int32_t launch_dq(const DqArgs& a, int32_t head_dim, Mode mode, bool broadcast, void* stream);
+int32_t launch_dq(const DqArgs& a, int32_t head_dim, Mode mode, bool broadcast, bool atomic,
+                  void* stream);
 int32_t launch_dq_reduce(const DqReduceArgs& a, int32_t head_dim, void* stream);
+// broadcast Q, atomic reduction: dq_accum = 0 before the dQ pass, then
+// dq = bf16(dq_accum) after it (n = lq * H * D elements)
+int32_t launch_dq_zero(float* dq_accum, int64_t n, void* stream);
+int32_t launch_dq_convert(const float* dq_accum, uint16_t* dq, int64_t n, void* stream);
 int32_t launch_dq_mx(const DqArgs& a, Mode mode, bool broadcast, void* stream);
 int32_t launch_mx_quant_rows(const uint16_t* src, int64_t rows, int32_t H, int32_t D, uint8_t* codes,
                              uint8_t* scales, void* stream);

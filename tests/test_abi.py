@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert J.jfa_abi_version() == 7
+    assert J.jfa_abi_version() == 8
     for st in range(-7, 1):
         assert J.jfa_status_string(st) not in ("", "unknown status")
     assert J.jfa_status_string(-99) == "unknown status"
@@ -304,3 +304,32 @@ def test_bwd_noalloc_rejects_plans_beyond_its_scratch():
     st = J._lib().jfa_bwd_noalloc(ctypes.byref(cp), ctypes.byref(plans[0]), ctypes.byref(plans[0]),
                                   None, t, *([t] * 11), None)
     assert st == J.JFA_ERR_PLAN_MISMATCH
+
+
+def test_bwd_stage_flags_validated_before_launch():
+    """The stage mask accepts the JFA_BWD_* flags and the atomic dQ modifier,
+    and refuses any other bit before launching anything."""
+    prob = _prob()
+    kv = J.jfa_plan_build(prob, None, [0, 3, 5], None, J.JFA_PASS_BWD, 4)
+    dq = J.jfa_plan_build(prob, None, [0, 3, 5], None, J.JFA_PASS_DQ, 4)
+    need = J.jfa_bwd_workspace_bytes(prob, dq.info)
+    t = _FakeTensor(0x1000)
+    f = lambda x: ctypes.c_void_p(x.data_ptr())
+    plans = [J.JfaDevicePlan(ctypes.pointer(p.info), 0x1000, 0x1000, None, None) for p in (kv, dq)]
+    cp = prob.c()
+
+    def call(stages, **over):
+        args = [t] * 11
+        return J._lib().jfa_bwd_stages(stages, ctypes.byref(cp), ctypes.byref(plans[0]),
+                                       ctypes.byref(plans[1]), None, ctypes.c_void_p(0x1000),
+                                       *[f(x) for x in args], f(t), need, None)
+    for bad in (-1, 32, 64, J.JFA_BWD_ALL | 32):
+        assert call(bad) == J.JFA_ERR_INVALID_ARG, bad
+    # a valid mask gets past the flag check to the next validation step (a
+    # misaligned dq_accum here), so nothing is launched in this test
+    args = [t] * 11
+    args[9] = _FakeTensor(0x1004)
+    st = J._lib().jfa_bwd_stages(J.JFA_BWD_ALL | J.JFA_BWD_DQ_ATOMIC, ctypes.byref(cp),
+                                 ctypes.byref(plans[0]), ctypes.byref(plans[1]), None,
+                                 ctypes.c_void_p(0x1000), *[f(x) for x in args], f(t), need, None)
+    assert st == J.JFA_ERR_INVALID_ARG

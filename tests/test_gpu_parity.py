@@ -405,6 +405,42 @@ def test_full_size(cfg, part):
             assert rel_err(gdq[:, h], dq[:, 0]) <= TOL_GRAD, (b, h)
 
 
+@pytest.mark.parametrize("case", ["bcast_ragged_d128", "bcast_ragged_d64", "sparse_d128",
+                                  "bcast_long_d64", "cfg2_small", "perseq_d128"])
+def test_atomic_dq_reduction(case):
+    """The atomic second stage of the broadcast-Q dQ reduction
+    (JFA_BWD_DQ_ATOMIC): dq_accum against the oracle and within fp32 summation
+    error of the fixed-order reduce (only the order of the fp32 adds differs),
+    dq the bf16 rounding of it; dK, dV and delta do not depend on the dQ
+    scheme (bit for bit). With per-sequence Q the flag changes nothing."""
+    print("case", case, flush=True)
+    x = SMALL_CASES[case]()
+    ref = run_gpu(x)
+    prob = problem_of(x)
+    att = J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask)
+    q, k, v, do = dev(x.q), dev(x.k), dev(x.v), dev(x.do)
+    H = prob.num_heads
+    out = dict(dq=torch.full_like(q, float("nan")), dk=torch.full_like(k, float("nan")),
+               dv=torch.full_like(v, float("nan")),
+               dq_accum=torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda"),
+               delta=torch.full((H, att.total_q), float("nan"), dtype=torch.float32, device="cuda"))
+    for _ in range(2):   # the stage zeroes dq_accum itself: a second run adds nothing twice
+        att.backward(q, k, v, ref.o, ref.lse, do, out, stages=J.JFA_BWD_ALL | J.JFA_BWD_DQ_ATOMIC)
+    torch.cuda.synchronize()
+    for name in ("dk", "dv", "delta"):
+        assert torch.equal(_bits(out[name]), _bits(getattr(ref, name))), name
+    if not prob.broadcast_q:
+        for name in ("dq", "dq_accum"):
+            assert torch.equal(_bits(out[name]), _bits(getattr(ref, name))), name
+        return
+    got, base = out["dq_accum"].double(), ref.dq_accum.double()
+    assert not torch.isnan(got).any()
+    assert float((got - base).abs().max()) <= 1e-5 * max(1.0, float(base.abs().max()))
+    assert torch.equal(_bits(out["dq"]), _bits(out["dq_accum"].to(torch.bfloat16)))
+    _, _, dq, _, _, _ = oracle_full(x)
+    assert rel_err(got.cpu().numpy(), dq) <= TOL_GRAD
+
+
 def beyond_int32_inputs():
     """Broadcast Q (H=4, D=128, 256 rows) over a first sequence of 4,198,400
     keys (1,025 copies of one random 4,096-key block; its dO rows zero) and
