@@ -34,12 +34,16 @@ visits the keys; the oracle keeps P exact and the tests bound the difference
 or, below E4M3's normal range, an absolute error of at most 2^-18).
 
 The same page reports the MXFP8 version's backward at parity on dense shapes
-without describing it. ``dq_mx`` is the plainest reading for the dQ pass:
+without describing it. ``dq_mx`` and ``dkdv_mx`` are the plainest reading
+for its two passes. ``dq_mx``, the dQ pass:
 every product of the FlashAttention dQ computation on MXFP8 operands, each
 encoded along that product's contraction dimension (Q, K, dO, V along d for
 S and dP; K along the keys of its sequence for dQ = dS K), with delta from
 the bf16 dO and O. The kernel rounds dS to E4M3 on the fly; the oracle keeps
-it exact and the tests bound the rounding.
+it exact and the tests bound the rounding. ``dkdv_mx``, the dK/dV pass: the
+same S and dP, then dV = P^T dO and dK = dS^T Q with Q and dO encoded along
+their rows (32-row blocks of one sequence, never spanning two, as V along
+keys: ``quantize_v`` with row offsets); the kernel rounds P and dS to E4M3.
 """
 from __future__ import annotations
 
@@ -212,3 +216,66 @@ def dq_mx(q_d, k_d, v_d, do_d, k_keys, do, o, lse, kv_offsets, *, scale, broadca
             floor_sum[qs, h] += scale * amax[:, None] * np.abs(kk).sum(axis=0)[None, :]
             delta[h, os_] = dl
     return dq, delta, abs_sum, floor_sum
+
+
+def dkdv_mx(q_d, k_d, v_d, do_d, q_r, do_r, do, o, lse, kv_offsets, *, scale, broadcast_q,
+            q_offsets=None, causal=False, block_mask=None, window=None):
+    """What the MXFP8 dK/dV pass computes ([radar] section "The turning point":
+    the MXFP8 version's backward; the reading is in the module header and
+    below), with P and dS kept exact (the kernel rounds P to E4M3 with the
+    fixed block scale 2^-8 and dS with one scale per (key, 32-row block);
+    tests bound that rounding).
+
+    Every product of the FlashAttention dK/dV computation on MXFP8 operands,
+    each encoded along that product's contraction dimension: Q, K, dO, V
+    along d for S and dP; Q and dO along their rows (32-row blocks of one
+    sequence, as V is encoded along keys for the forward) for dK = dS^T Q and
+    dV = P^T dO. Per sequence and head, every operand float64 and decoded:
+      S     = scale * q_d k_d^T
+      P     = exp(S - lse) on visible keys, 0 elsewhere (lse given: the forward's)
+      delta = rowsum(do * o)             (the bf16 dO and O)
+      dP    = do_d v_d^T
+      dS    = P (dP - delta)
+      dV    = P^T do_r
+      dK    = scale * dS^T q_r
+    Returns (dk, dv, dv_p_abs, dv_p_floor, dk_abs, dk_floor): dv_p_abs =
+    P^T |do_r| and dv_p_floor = vis^T |do_r| (the terms of P's rounding bound),
+    dk_abs = scale |dS|^T |q_r| and dk_floor = scale * (max_i |dS_ij|) *
+    sum_i |q_r_i| per key (those of dS's)."""
+    import oracle.attention as A
+    B = len(kv_offsets) - 1
+    T_k, H, D = k_d.shape
+    dk = np.zeros((T_k, H, D))
+    dv = np.zeros((T_k, H, D))
+    dv_p_abs = np.zeros((T_k, H, D))
+    dv_p_floor = np.zeros((T_k, H, D))
+    dk_abs = np.zeros((T_k, H, D))
+    dk_floor = np.zeros((T_k, H, D))
+    lq = q_d.shape[0] if broadcast_q else None
+    for b in range(B):
+        k0, k1 = int(kv_offsets[b]), int(kv_offsets[b + 1])
+        if broadcast_q:
+            qs, os_ = slice(0, lq), slice(b * lq, (b + 1) * lq)
+        else:
+            qs = os_ = slice(int(q_offsets[b]), int(q_offsets[b + 1]))
+        n_rows = qs.stop - qs.start
+        if n_rows == 0 or k1 == k0:
+            continue
+        vis = A.visibility(n_rows, k1 - k0, causal=causal, window=window,
+                           mask_b=None if block_mask is None else block_mask[b])
+        for h in range(H):
+            lse_b = lse[h, os_]
+            fin = np.isfinite(lse_b)
+            visf = vis & fin[:, None]
+            s = scale * (q_d[qs, h] @ k_d[k0:k1, h].T)
+            p = np.where(visf, np.exp(s - np.where(fin, lse_b, 0.0)[:, None]), 0.0)
+            dl = np.sum(do[os_, h] * o[os_, h], axis=1)
+            ds = p * (do_d[os_, h] @ v_d[k0:k1, h].T - dl[:, None])
+            dv[k0:k1, h] = p.T @ do_r[os_, h]
+            dk[k0:k1, h] = scale * (ds.T @ q_r[qs, h])
+            dv_p_abs[k0:k1, h] = p.T @ np.abs(do_r[os_, h])
+            dv_p_floor[k0:k1, h] = visf.astype(np.float64).T @ np.abs(do_r[os_, h])
+            dk_abs[k0:k1, h] = scale * (np.abs(ds).T @ np.abs(q_r[qs, h]))
+            amax = np.abs(ds).max(axis=0, initial=0.0)
+            dk_floor[k0:k1, h] = scale * amax[:, None] * np.abs(q_r[qs, h]).sum(axis=0)[None, :]
+    return dk, dv, dv_p_abs, dv_p_floor, dk_abs, dk_floor

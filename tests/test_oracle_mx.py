@@ -135,3 +135,24 @@ def test_dq_mx_without_quantisation_is_the_attention_gradient(broadcast):
     assert np.all(abs_sum >= np.abs(dq) - 1e-12) and np.all(floor_sum >= 0)
     dq2, _, _, _ = mx.dq_mx(q, k, v, do, 2 * k, do, o, lse, off, **kw)
     assert np.allclose(dq2, 2 * dq, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("broadcast", [True, False])
+def test_dkdv_mx_without_quantisation_is_the_attention_gradient(broadcast):
+    """With every encoding the identity and the forward's own O and LSE, the
+    MXFP8 dK/dV definition is the attention dK and dV of
+    oracle.attention.backward; dV is linear in the dO of its product and
+    blind to the Q of dK's, and dK the other way round (which pins which
+    encoding each product takes); the rounding-bound terms dominate |dK|,
+    |dV|."""
+    from oracle import attention as A
+    q, k, v, do, off, qoff = _small(broadcast)
+    kw = dict(scale=0.125, broadcast_q=broadcast, q_offsets=qoff, causal=not broadcast)
+    o, lse = A.forward(q, k, v, off, **kw)
+    _, dk_ref, dv_ref, _ = A.backward(q, k, v, do, off, **kw)
+    dk, dv, pa, pf, ka, kf = mx.dkdv_mx(q, k, v, do, q, do, do, o, lse, off, **kw)
+    assert np.allclose(dk, dk_ref, rtol=0, atol=1e-12) and np.allclose(dv, dv_ref, rtol=0, atol=1e-12)
+    assert np.all(pa >= np.abs(dv) - 1e-12) and np.all(pf >= pa - 1e-12)
+    assert np.all(ka >= np.abs(dk) - 1e-12) and np.all(kf >= 0)
+    dk2, dv2, *_ = mx.dkdv_mx(q, k, v, do, 3 * q, 2 * do, do, o, lse, off, **kw)
+    assert np.allclose(dv2, 2 * dv, rtol=0, atol=1e-12) and np.allclose(dk2, 3 * dk, rtol=0, atol=1e-12)
