@@ -364,9 +364,22 @@ def main():
             att.backward_mx(qi, ki, vi, oi, lsei, doi, opss[i % 2], outi, stages=J.JFA_BWD_DQ)
         mdq_ms = time_alone(mx_dq)
         qzb_ms = time_alone(lambda i: att.quantize_mx_bwd(mxqs[i % 2], *sets[i % 2][1:]))
+        # the MXFP8 dK/dV pass (Q and dO also encoded along their rows, once,
+        # outside the timed loop), timed alone
+        opsk = [att.quantize_mx_dkdv(opss[i], sets[i][0], sets[i][3]) for i in range(2)]
+
+        def mx_dkdv(i):
+            qi, ki, vi, doi = sets[i % 2]
+            oi, lsei, outi = outs[i % 2]
+            att.backward_mx(qi, ki, vi, oi, lsei, doi, opsk[i % 2], outi, stages=J.JFA_BWD_DKDV)
+        mdkdv_ms = time_alone(mx_dkdv)
+        qzk_ms = time_alone(lambda i: att.quantize_mx_dkdv(opss[i % 2], sets[i % 2][0], sets[i % 2][3]))
         mx.update({"dq_ms": mdq_ms,
                    "dq_issued_tflops": 3 * model["dq_flop"] / (mdq_ms * 1e-3) / 1e12,
-                   "encode_bwd_ms": qzb_ms})
+                   "encode_bwd_ms": qzb_ms,
+                   "dkdv_ms": mdkdv_ms,
+                   "dkdv_tflops": model["dkdv_flop"] / (mdkdv_ms * 1e-3) / 1e12,
+                   "encode_dkdv_rows_ms": qzk_ms})
 
     # the two second stages of the broadcast-Q dQ reduction, each timed alone
     # on the same inputs: the per-worker partials plus the fixed-order reduce
@@ -422,10 +435,14 @@ def main():
                                                      / sum(per[n] for n in names[1:]))
     if mx is not None:
         mixed_ms = mx["fwd_ms"] + mx["dq_ms"] + per["bwd_dkdv"] + per["bwd_dq_reduce"]
+        all_ms = mx["fwd_ms"] + mx["dq_ms"] + mx["dkdv_ms"] + per["bwd_dq_reduce"]
         mx.update({"dq_vs_bf16_dq": per["bwd_dq"] / mx["dq_ms"],
+                   "dkdv_vs_bf16_dkdv": per["bwd_dkdv"] / mx["dkdv_ms"],
                    "step_mx_fwd_mx_dq_ms": mixed_ms,
                    "step_mx_fwd_mx_dq_tflops": (model["fwd_flop"] + model["bwd_flop"])
-                   / (mixed_ms * 1e-3) / 1e12})
+                   / (mixed_ms * 1e-3) / 1e12,
+                   "step_all_mx_ms": all_ms,
+                   "step_all_mx_tflops": (model["fwd_flop"] + model["bwd_flop"]) / (all_ms * 1e-3) / 1e12})
 
     flop = model["fwd_flop"] + model["bwd_flop"]
     value = flop / (ms_step * 1e-3) / 1e12

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define JFA_ABI_VERSION 8
+#define JFA_ABI_VERSION 9
 
 /* status codes */
 #define JFA_OK                 0
@@ -423,6 +423,55 @@ int32_t jfa_bwd_dq_mx(const jfa_problem* prob, const jfa_device_plan* dq_plan,
                       const void* o, const float* lse, const void* d_o,
                       const jfa_mx_bwd_operands* ops, void* dq, float* dq_accum, float* delta,
                       void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * MXFP8 dK/dV pass ("TLX porta l'attenzione jagged su Blackwell" (ai-radar.it),
+ * section "The turning point": the MXFP8 version of the kernel; its backward,
+ * here the dK/dV pass): the JFA_BWD_DKDV stage with its four products as
+ * block-scaled FP8 MFMAs (head_dim 128):
+ *   S  = Q K^T    Q and K encoded along d (the MXFP8 forward's encodings),
+ *   dP = dO V^T   dO and V encoded along d (jfa_mx_quantize_rows),
+ *   dV = P^T dO   dO encoded along its rows in 32-row blocks of one sequence
+ *                 (jfa_mx_quantize_v applied to dO with the row offsets of
+ *                 the sequences: b*lq with a broadcast Q, else q_offsets);
+ *                 P = exp(S - LSE) <= 1 rounded to E4M3 on the fly with the
+ *                 fixed block scale 2^-8,
+ *   dK = scale dS^T Q   Q encoded along its rows (jfa_mx_quantize_v applied
+ *                 to Q with offsets [0, lq] for a broadcast Q, else
+ *                 q_offsets); dS = P (dP - delta) rounded to E4M3 on the fly
+ *                 with one E8M0 scale per (key, 32-row block): the smallest
+ *                 power of two 2^e with max|dS| / 2^e <= 448, so nothing is
+ *                 clamped (a block below 2^-100 is sent as zeros).
+ * P, dS and the dK/dV accumulators are fp32; dk and dv are written as bf16
+ * [T_k, H, D]. lse is the forward's, delta = rowsum(dO * O) (written by the
+ * dQ pass, bf16 or MXFP8, or by JFA_BWD_PREPROCESS). kv_plan is a BWD plan.
+ * Along-rows layouts: codes [rows, H, D], scales [H, NB, D] with the blocks
+ * of sequence b starting at d_*_row_block_offsets[b] (device copies of
+ * jfa_mx_block_offsets' output for those row offsets; the Q one is not read
+ * with a broadcast Q, whose blocks are those of its lq rows). Scale arrays
+ * 4-byte aligned, codes 16-byte aligned (either may be NULL when empty); the
+ * caller owns everything.
+ */
+typedef struct jfa_mx_dkdv_operands {
+    const void* q_codes;      /* Q along d */
+    const void* q_scales;
+    const void* k_codes;      /* K along d */
+    const void* k_scales;
+    const void* v_codes;      /* V along d */
+    const void* v_scales;
+    const void* do_codes;     /* dO along d */
+    const void* do_scales;
+    const void* qr_codes;     /* Q along its rows */
+    const void* qr_scales;
+    const void* dor_codes;    /* dO along its rows */
+    const void* dor_scales;
+} jfa_mx_dkdv_operands;
+int32_t jfa_bwd_dkdv_mx(const jfa_problem* prob, const jfa_device_plan* kv_plan,
+                        const int32_t* d_q_offsets, const int32_t* d_kv_offsets,
+                        const int32_t* d_q_row_block_offsets, int32_t num_q_row_blocks,
+                        const int32_t* d_do_row_block_offsets, int32_t num_do_row_blocks,
+                        const float* lse, const float* delta, const jfa_mx_dkdv_operands* ops,
+                        void* dk, void* dv, void* stream);
 
 #ifdef __cplusplus
 }

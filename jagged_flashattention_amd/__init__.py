@@ -37,7 +37,7 @@ EXPORTS = (
     "jfa_offsets_from_lengths", "jfa_plan_query", "jfa_plan_build", "jfa_fwd_workspace_bytes",
     "jfa_fwd", "jfa_bwd_workspace_bytes", "jfa_bwd", "jfa_bwd_stages", "jfa_mx_block_offsets",
     "jfa_mx_quantize_rows", "jfa_mx_quantize_v", "jfa_fwd_mx", "jfa_bwd_dq_mx",
-    "jfa_bwd_noalloc",
+    "jfa_bwd_noalloc", "jfa_bwd_dkdv_mx",
 )
 JFA_BWD_PREPROCESS = 1
 JFA_BWD_DQ = 2
@@ -75,6 +75,12 @@ class JfaMxBwdOperands(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "q_codes", "q_scales", "k_codes", "k_scales", "v_codes", "v_scales", "do_codes",
         "do_scales", "kk_codes", "kk_scales")]
+
+
+class JfaMxDkdvOperands(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "q_codes", "q_scales", "k_codes", "k_scales", "v_codes", "v_scales", "do_codes",
+        "do_scales", "qr_codes", "qr_scales", "dor_codes", "dor_scales")]
 
 
 class JfaError(RuntimeError):
@@ -116,6 +122,8 @@ def _lib():
             "jfa_bwd": (i32, [prob, dplan, dplan] + [_P] * 14 + [i64, _P]),
             "jfa_bwd_stages": (i32, [i32, prob, dplan, dplan] + [_P] * 14 + [i64, _P]),
             "jfa_bwd_noalloc": (i32, [prob, dplan, dplan] + [_P] * 14),
+            "jfa_bwd_dkdv_mx": (i32, [prob, dplan, _P, _P, _P, i32, _P, i32, _P, _P,
+                                      ctypes.POINTER(JfaMxDkdvOperands), _P, _P, _P]),
             "jfa_mx_block_offsets": (i32, [_P, i32, _P]),
             "jfa_mx_quantize_rows": (i32, [_P, i64, i32, i32, _P, _P, _P]),
             "jfa_mx_quantize_v": (i32, [_P, _P, _P, i32, i32, i32, i32, _P, _P, _P]),
@@ -387,6 +395,24 @@ def jfa_bwd_dq_mx(prob: Problem, dq_plan: DevicePlan, q_offsets, kv_offsets, key
            "jfa_bwd_dq_mx")
 
 
+def jfa_bwd_dkdv_mx(prob: Problem, kv_plan: DevicePlan, q_offsets, kv_offsets, q_row_block_offsets,
+                    num_q_row_blocks, do_row_block_offsets, num_do_row_blocks, lse, delta,
+                    ops: dict, dk, dv, stream=None) -> None:
+    """Enqueue the MXFP8 dK/dV pass (operands: qc/qs, kc/ks, vdc/vds, doc/dos
+    along d, qrc/qrs, dorc/dors along rows, as produced by
+    JaggedAttention.quantize_mx_dkdv)."""
+    cp = prob.c()
+    kp = _c_plan(kv_plan)
+    mo = JfaMxDkdvOperands(*[_dev_ptr(ops[n]) for n in (
+        "qc", "qs", "kc", "ks", "vdc", "vds", "doc", "dos", "qrc", "qrs", "dorc", "dors")])
+    _check(_lib().jfa_bwd_dkdv_mx(ctypes.byref(cp), ctypes.byref(kp), _dev_ptr(q_offsets),
+                                  _dev_ptr(kv_offsets), _dev_ptr(q_row_block_offsets),
+                                  int(num_q_row_blocks), _dev_ptr(do_row_block_offsets),
+                                  int(num_do_row_blocks), _dev_ptr(lse), _dev_ptr(delta),
+                                  ctypes.byref(mo), _dev_ptr(dk), _dev_ptr(dv), _stream(stream)),
+           "jfa_bwd_dkdv_mx")
+
+
 def jfa_mx_block_offsets(kv_offsets) -> np.ndarray:
     """First V scale block of each sequence (prefix sums of ceil(L_b / 32))."""
     ko = _i32(kv_offsets)
@@ -575,24 +601,65 @@ class JaggedAttention:
                           ops["kks"])
         return ops
 
+    def quantize_mx_dkdv(self, ops, q, d_o):
+        """The further MXFP8 encodings of the MXFP8 dK/dV pass: Q and dO along
+        their rows, in 32-row blocks of one sequence (added to
+        quantize_mx_bwd's dict)."""
+        import torch
+        self._expect(q=q, d_o=d_o)
+        H, D = self.prob.num_heads, self.prob.head_dim
+        if not hasattr(self, "q_row_boff"):
+            B = self.kv_offsets.numel() - 1
+            if self.prob.broadcast_q:
+                q_rows_off = np.array([0, self.prob.lq], dtype=np.int32)
+                do_rows_off = (np.arange(B + 1) * self.prob.lq).astype(np.int32)
+            else:
+                q_rows_off = do_rows_off = self.q_offsets.cpu().numpy()
+            qb, db = jfa_mx_block_offsets(q_rows_off), jfa_mx_block_offsets(do_rows_off)
+            self.q_row_nb, self.do_row_nb = int(qb[-1]), int(db[-1])
+            (self.q_rows_off, self.do_rows_off, self.q_row_boff, self.do_row_boff) = upload_int32(
+                [q_rows_off, do_rows_off, qb, db], self.device)
+        u8 = dict(dtype=torch.uint8, device=self.device)
+        out = dict(ops)
+        out.update(qrc=torch.empty(q.shape, **u8), qrs=torch.empty((H, max(self.q_row_nb, 1), D), **u8),
+                   dorc=torch.empty(d_o.shape, **u8),
+                   dors=torch.empty((H, max(self.do_row_nb, 1), D), **u8))
+        jfa_mx_quantize_v(q, self.q_rows_off, self.q_row_boff, self.q_row_nb, out["qrc"], out["qrs"])
+        jfa_mx_quantize_v(d_o, self.do_rows_off, self.do_row_boff, self.do_row_nb, out["dorc"],
+                          out["dors"])
+        return out
+
     def backward_mx(self, q, k, v, o, lse, d_o, ops, out=None, stages=JFA_BWD_ALL):
-        """Backward with the MXFP8 dQ pass (in place of JFA_BWD_DQ) and the
-        bf16 dK/dV pass and dQ reduce, for the stages selected."""
+        """Backward with the MXFP8 dQ pass (in place of JFA_BWD_DQ) and, when
+        ops holds the along-rows encodings of quantize_mx_dkdv, the MXFP8
+        dK/dV pass (in place of JFA_BWD_DKDV); the other selected stages are
+        the bf16 ones."""
         import torch
         if out is None:
             out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
                        dq_accum=torch.empty(q.shape, dtype=torch.float32, device=self.device),
                        delta=torch.empty((self.prob.num_heads, self.total_q), dtype=torch.float32,
                                          device=self.device))
+        # in the order of jfa_bwd_stages: delta alone, dQ, dK/dV, dQ reduce
+        if stages & JFA_BWD_PREPROCESS:
+            self.backward(q, k, v, o, lse, d_o, out, stages=JFA_BWD_PREPROCESS)
         if stages & JFA_BWD_DQ:
             self._expect(o=o, lse=lse, d_o=d_o, dq=out["dq"], dq_accum=out["dq_accum"],
                          delta=out["delta"])
             jfa_bwd_dq_mx(self.prob, self.dq_plan, self.q_offsets, self.kv_offsets,
                           self.v_block_offsets, self.v_num_blocks, o, lse, d_o, ops, out["dq"],
                           out["dq_accum"], out["delta"], self.workspace, self.ws_bytes)
-        rest = stages & ~JFA_BWD_DQ
-        if rest:
-            self.backward(q, k, v, o, lse, d_o, out, stages=rest)
+        if stages & JFA_BWD_DKDV:
+            if "qrc" in ops:
+                self._expect(lse=lse, delta=out["delta"], dk=out["dk"], dv=out["dv"])
+                jfa_bwd_dkdv_mx(self.prob, self.bwd_plan, self.q_offsets, self.kv_offsets,
+                                self.q_row_boff, self.q_row_nb, self.do_row_boff, self.do_row_nb,
+                                lse, out["delta"], ops, out["dk"], out["dv"])
+            else:
+                self.backward(q, k, v, o, lse, d_o, out, stages=JFA_BWD_DKDV)
+        # (the MXFP8 dQ pass writes per-worker partials: the fixed-order reduce)
+        if stages & JFA_BWD_DQ_REDUCE:
+            self.backward(q, k, v, o, lse, d_o, out, stages=JFA_BWD_DQ_REDUCE)
         return out
 
     def backward(self, q, k, v, o, lse, d_o, out=None, stages=JFA_BWD_ALL):

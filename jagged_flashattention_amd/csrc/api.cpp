@@ -352,7 +352,7 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device
     const bool bcast = prob->broadcast_q != 0;
     const bool atomic = bcast && (stages & JFA_BWD_DQ_ATOMIC) != 0;
 
-    jfa::BwdArgs a;
+    jfa::BwdArgs a{};
     a.worker_ptr = kv_plan->worker_ptr;
     a.tiles = kv_plan->tiles;
     a.sp_ptr = kv_plan->sparse_ptr;
@@ -515,6 +515,83 @@ int32_t jfa_bwd_dq_mx(const jfa_problem* prob, const jfa_device_plan* dq_plan,
     d.q_rows = (int32_t)q_rows;
     d.total_kv = qi->total_kv;
     return hip_status(jfa::launch_dq_mx(d, mode_of(prob), bcast, stream));
+}
+
+int32_t jfa_bwd_dkdv_mx(const jfa_problem* prob, const jfa_device_plan* kv_plan,
+                        const int32_t* d_q_offsets, const int32_t* d_kv_offsets,
+                        const int32_t* d_q_row_block_offsets, int32_t num_q_row_blocks,
+                        const int32_t* d_do_row_block_offsets, int32_t num_do_row_blocks,
+                        const float* lse, const float* delta, const jfa_mx_dkdv_operands* ops,
+                        void* dk, void* dv, void* stream) {
+    int32_t st = check_plan(prob, kv_plan, JFA_PASS_BWD, d_q_offsets, d_kv_offsets);
+    if (st) return st;
+    if (prob->head_dim != 128) return JFA_ERR_UNSUPPORTED;
+    const jfa_plan_info* ki = kv_plan->info;
+    const bool bcast = prob->broadcast_q != 0;
+    const int64_t hd = (int64_t)prob->num_heads * prob->head_dim;
+    const int64_t q_rows = bcast ? prob->lq : ki->total_q;
+    const int64_t tq = ki->total_q, tk = ki->total_kv;
+    if (ops == nullptr || num_q_row_blocks < 0 || num_do_row_blocks < 0) return JFA_ERR_INVALID_ARG;
+    // one 32-row block per 32 rows of each sequence: at least rows / 32
+    if (num_q_row_blocks < (q_rows + 31) / 32 || num_do_row_blocks < (tq + 31) / 32)
+        return JFA_ERR_INVALID_ARG;
+    if (ki->num_tiles > 0 && (d_do_row_block_offsets == nullptr ||
+                              (!bcast && d_q_row_block_offsets == nullptr)))
+        return JFA_ERR_INVALID_ARG;
+    if (!tensor_ok(dk, tk * hd) || !tensor_ok(dv, tk * hd) || !tensor_ok(ops->q_codes, q_rows * hd) ||
+        !tensor_ok(ops->k_codes, tk * hd) || !tensor_ok(ops->v_codes, tk * hd) ||
+        !tensor_ok(ops->do_codes, tq * hd) || !tensor_ok(ops->qr_codes, q_rows * hd) ||
+        !tensor_ok(ops->dor_codes, tq * hd))
+        return JFA_ERR_INVALID_ARG;
+    const int64_t H = prob->num_heads, nbd = prob->head_dim / 32;
+    if (!scales_ok(ops->q_scales, H * q_rows * nbd) || !scales_ok(ops->k_scales, H * tk * nbd) ||
+        !scales_ok(ops->v_scales, H * tk * nbd) || !scales_ok(ops->do_scales, H * tq * nbd) ||
+        !scales_ok(ops->qr_scales, H * (int64_t)num_q_row_blocks * prob->head_dim) ||
+        !scales_ok(ops->dor_scales, H * (int64_t)num_do_row_blocks * prob->head_dim))
+        return JFA_ERR_INVALID_ARG;
+    if (tq > 0 && (lse == nullptr || delta == nullptr || !aligned4(lse) || !aligned4(delta)))
+        return JFA_ERR_INVALID_ARG;
+    if (ki->num_tiles == 0) return JFA_OK;
+    const jfa::Band bd = jfa::band_of(prob);
+    jfa::BwdArgs a{};
+    a.worker_ptr = kv_plan->worker_ptr;
+    a.tiles = kv_plan->tiles;
+    a.sp_ptr = kv_plan->sparse_ptr;
+    a.sp_idx = kv_plan->sparse_idx;
+    a.q_off = bcast ? nullptr : d_q_offsets;
+    a.kv_off = d_kv_offsets;
+    a.lse = lse;
+    a.delta = const_cast<float*>(delta);
+    a.dk = static_cast<uint16_t*>(dk);
+    a.dv = static_cast<uint16_t*>(dv);
+    a.num_heads = prob->num_heads;
+    a.lq = prob->lq;
+    a.total_q = ki->total_q;
+    a.mask_kv_blocks = prob->mask_kv_blocks;
+    a.num_workers = ki->num_workers;
+    a.win_left = bd.left;
+    a.win_right = bd.right;
+    a.scale = prob->softmax_scale;
+    a.scale_log2 = prob->softmax_scale * 1.4426950408889634f;
+    a.q8 = static_cast<const uint8_t*>(ops->q_codes);
+    a.q_sc = static_cast<const uint8_t*>(ops->q_scales);
+    a.k8 = static_cast<const uint8_t*>(ops->k_codes);
+    a.k_sc = static_cast<const uint8_t*>(ops->k_scales);
+    a.v8 = static_cast<const uint8_t*>(ops->v_codes);
+    a.v_sc = static_cast<const uint8_t*>(ops->v_scales);
+    a.do8 = static_cast<const uint8_t*>(ops->do_codes);
+    a.do_sc = static_cast<const uint8_t*>(ops->do_scales);
+    a.qr8 = static_cast<const uint8_t*>(ops->qr_codes);
+    a.qr_sc = static_cast<const uint8_t*>(ops->qr_scales);
+    a.dor8 = static_cast<const uint8_t*>(ops->dor_codes);
+    a.dor_sc = static_cast<const uint8_t*>(ops->dor_scales);
+    a.qr_boff = d_q_row_block_offsets;
+    a.dor_boff = d_do_row_block_offsets;
+    a.qr_nb = num_q_row_blocks;
+    a.dor_nb = num_do_row_blocks;
+    a.q_rows = (int32_t)q_rows;
+    a.total_kv = ki->total_kv;
+    return hip_status(jfa::launch_dkdv_mx(a, mode_of(prob), bcast, stream));
 }
 
 int32_t jfa_bwd_noalloc(const jfa_problem* prob, const jfa_device_plan* kv_plan,

@@ -103,6 +103,24 @@ struct BwdArgs {
     int32_t win_left, win_right;   // banded mode: window bounds (-1: none)
     float scale;
     float scale_log2;
+    // MXFP8 dK/dV pass (head_dim 128): E4M3 codes and E8M0 scale codes
+    const uint8_t* q8;       // Q along d: [q_rows, H, D], scales [H, q_rows, D/32]
+    const uint8_t* q_sc;
+    const uint8_t* k8;       // K along d: [T_k, H, D], scales [H, T_k, D/32]
+    const uint8_t* k_sc;
+    const uint8_t* v8;       // V along d: [T_k, H, D], scales [H, T_k, D/32]
+    const uint8_t* v_sc;
+    const uint8_t* do8;      // dO along d: [T_q, H, D], scales [H, T_q, D/32]
+    const uint8_t* do_sc;
+    const uint8_t* qr8;      // Q along its rows: [q_rows, H, D], scales [H, qr_nb, D]
+    const uint8_t* qr_sc;
+    const uint8_t* dor8;     // dO along its rows: [T_q, H, D], scales [H, dor_nb, D]
+    const uint8_t* dor_sc;
+    const int32_t* qr_boff;  // first 32-row Q block of each sequence [B+1] (per-sequence Q)
+    const int32_t* dor_boff; // first 32-row dO block of each sequence [B+1]
+    int32_t qr_nb, dor_nb;
+    int32_t q_rows;
+    int32_t total_kv;
 };
 
 // Q-stationary dQ pass of the backward (JFA_PASS_DQ plan).
@@ -174,6 +192,7 @@ int32_t launch_dq_reduce(const DqReduceArgs& a, int32_t head_dim, void* stream);
 int32_t launch_dq_zero(float* dq_accum, int64_t n, void* stream);
 int32_t launch_dq_convert(const float* dq_accum, uint16_t* dq, int64_t n, void* stream);
 int32_t launch_dq_mx(const DqArgs& a, Mode mode, bool broadcast, void* stream);
+int32_t launch_dkdv_mx(const BwdArgs& a, Mode mode, bool broadcast, void* stream);
 int32_t launch_mx_quant_rows(const uint16_t* src, int64_t rows, int32_t H, int32_t D, uint8_t* codes,
                              uint8_t* scales, void* stream);
 int32_t launch_mx_quant_v(const uint16_t* v, const int32_t* kv_off, const int32_t* boff, int32_t B,

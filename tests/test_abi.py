@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert J.jfa_abi_version() == 8
+    assert J.jfa_abi_version() == 9
     for st in range(-7, 1):
         assert J.jfa_status_string(st) not in ("", "unknown status")
     assert J.jfa_status_string(-99) == "unknown status"

@@ -387,3 +387,111 @@ def test_mx_only_empty_sequences():
     assert bool(torch.all(lse == float("-inf")))
     assert float(out["dq_accum"].abs().max()) == 0.0 and float(out["dq"].float().abs().max()) == 0.0
     assert float(out["delta"].abs().max()) == 0.0
+
+
+MXKV_CASES = ["bcast_ragged_d128", "perseq_d128", "causal_d128", "sparse_d128", "window_band_d128",
+              "window_causal_d128", "cfg2_small", "cfg3_small", "cfg5_small"]
+
+
+def _row_offsets(x):
+    """Offsets of the Q rows and of the dO rows of each sequence (the
+    along-rows encodings' block boundaries)."""
+    w = x.workload
+    if w.broadcast_q:
+        return np.array([0, w.lq], dtype=np.int32), (np.arange(x.batch + 1) * w.lq).astype(np.int32)
+    return x.q_offsets, x.q_offsets
+
+
+def _mx_dkdv_case(x, heads=None):
+    """The oracle's MXFP8 dK/dV (and its bound terms) and the GPU's, on the
+    oracle's own O and LSE of the MXFP8 forward operands; delta from the
+    standalone preprocess of the same bf16 O and dO. With ``heads`` only those
+    heads carry the case (the others get O = 0, LSE = 30: P negligible)."""
+    w = x.workload
+    off = x.kv_offsets
+    hs = list(range(w.heads)) if heads is None else heads
+    sel = lambda a: _f64(a)[:, hs]
+    qf, kf, vf, dof = sel(x.q), sel(x.k), sel(x.v), sel(x.do)
+    q_d = OMX.dequantize_rows(*OMX.quantize_rows(qf))
+    k_d = OMX.dequantize_rows(*OMX.quantize_rows(kf))
+    v_d = OMX.dequantize_rows(*OMX.quantize_rows(vf))
+    do_d = OMX.dequantize_rows(*OMX.quantize_rows(dof))
+    v_keys = OMX.dequantize_v(*OMX.quantize_v(vf, off), off)
+    q_off_rows, do_off_rows = _row_offsets(x)
+    q_r = OMX.dequantize_v(*OMX.quantize_v(qf, q_off_rows), q_off_rows)
+    do_r = OMX.dequantize_v(*OMX.quantize_v(dof, do_off_rows), do_off_rows)
+    kw = dict(scale=w.scale, broadcast_q=w.broadcast_q, q_offsets=x.q_offsets, causal=w.causal,
+              block_mask=x.block_mask, window=w.window)
+    o, lse = A.forward(q_d, k_d, v_keys, off, **kw)
+    o_bits = W.f32_to_bf16_bits(o.astype(np.float32))
+    ref = OMX.dkdv_mx(q_d, k_d, v_d, do_d, q_r, do_r, dof, _f64(o_bits), lse, off, **kw)
+
+    prob = problem_of(x)
+    cus = J.jfa_device_workers(0)
+    att = J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask, fwd_workers=cus,
+                            bwd_workers=cus)
+    qg, kg, vg, dog = dev(x.q), dev(x.k), dev(x.v), dev(x.do)
+    H, D = prob.num_heads, prob.head_dim
+    o_all = np.zeros((att.total_q, H, D), dtype=np.uint16)
+    o_all[:, hs] = o_bits
+    lse_all = np.full((H, att.total_q), 30.0, dtype=np.float32)
+    lse_all[hs] = lse
+    mxq = att.quantize_mx(qg, kg, vg)
+    ops = att.quantize_mx_dkdv(att.quantize_mx_bwd(mxq, kg, vg, dog), qg, dog)
+    out = dict(dq=torch.empty_like(qg), dk=torch.full_like(kg, float("nan")),
+               dv=torch.full_like(vg, float("nan")),
+               dq_accum=torch.empty(qg.shape, dtype=torch.float32, device="cuda"),
+               delta=torch.full((H, att.total_q), float("nan"), dtype=torch.float32, device="cuda"))
+    att.backward_mx(qg, kg, vg, dev(o_all), torch.from_numpy(lse_all).cuda(), dog, ops, out,
+                    stages=J.JFA_BWD_PREPROCESS | J.JFA_BWD_DKDV)
+    torch.cuda.synchronize()
+    return ref, host_f64(out["dk"])[:, hs], host_f64(out["dv"])[:, hs]
+
+
+def _check_mx_dkdv(ref, gdk, gdv):
+    """Against the oracle's exact-P, exact-dS values, per element:
+      |dV_gpu - dV| <= 2^-4 P^T|dO_r| + 2^-18 vis^T|dO_r| + 2^-8 |dV| + 1e-4 P^T|dO_r| + 1e-6
+      |dK_gpu - dK| <= 2^-4 scale|dS|^T|Q_r| + 2^-17 scale max|dS| sum|Q_r| + 2^-8 |dK|
+                        + 1e-4 scale|dS|^T|Q_r| + 1e-6
+    (P, at most 1, scaled by 2^8 and rounded to E4M3: relative 2^-4 in its
+    normal range, 2^-10 2^-8 below it; dS with its (key, 32-row block) scale
+    2^e <= max|dS| 2^-7: relative 2^-4, at most 2^-10 2^e below; the bf16
+    rounding of dK, dV; fp32 sums), and on average far inside that."""
+    dk, dv, pa, pf, ka, kf = ref
+    assert not np.isnan(gdk).any() and not np.isnan(gdv).any()
+    bv = 2.0 ** -4 * pa + 2.0 ** -18 * pf + 2.0 ** -8 * np.abs(dv) + 1e-4 * pa + 1e-6
+    bk = 2.0 ** -4 * ka + 2.0 ** -17 * kf + 2.0 ** -8 * np.abs(dk) + 1e-4 * ka + 1e-6
+    ev, ek = np.abs(gdv - dv), np.abs(gdk - dk)
+    assert np.all(ev <= bv), ("dV", float((ev - bv).max()))
+    assert np.all(ek <= bk), ("dK", float((ek - bk).max()))
+    assert ev.mean() <= 0.25 * bv.mean() and ek.mean() <= 0.25 * bk.mean()
+
+
+@pytest.mark.parametrize("case", MXKV_CASES)
+def test_mx_dkdv_pass(case):
+    """The MXFP8 dK/dV pass against the oracle's definition of it."""
+    print("case", case, flush=True)
+    x = SMALL_CASES[case]()
+    _check_mx_dkdv(*_mx_dkdv_case(x))
+
+
+def test_mx_dkdv_pass_full_size_one_head():
+    """The MXFP8 dK/dV pass on the full GEM-shaped broadcast-Q workload, in
+    the launch configuration the benchmark times, checked on every key of
+    head 1 against the oracle with the bounds of test_mx_dkdv_pass."""
+    print("full-size GEM broadcast-Q, MXFP8 dK/dV pass, head 1", flush=True)
+    x = W.make_inputs(2)
+    _check_mx_dkdv(*_mx_dkdv_case(x, heads=[1]))
+
+
+def test_mx_dkdv_rejects_unsupported_head_dim_and_missing_encodings():
+    x = SMALL_CASES["bcast_ragged_d64"]()
+    prob = problem_of(x)
+    att = J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask)
+    t = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    ops = {n: t for n in ("qc", "qs", "kc", "ks", "vdc", "vds", "doc", "dos", "qrc", "qrs", "dorc", "dors")}
+    lse = torch.zeros((prob.num_heads, att.total_q), dtype=torch.float32, device="cuda")
+    with pytest.raises(J.JfaError) as e:
+        J.jfa_bwd_dkdv_mx(prob, att.bwd_plan, None, att.kv_offsets, att.kv_offsets, 64,
+                          att.kv_offsets, 64, lse, lse, ops, t, t)
+    assert e.value.status == J.JFA_ERR_UNSUPPORTED
