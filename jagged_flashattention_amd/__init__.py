@@ -16,7 +16,9 @@ from typing import Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libjfa.so")
+# JFA_LIBRARY names another build of the same library to load instead (the
+# host-check build that the CPU tests run under the sanitizers).
+LIB_PATH = os.environ.get("JFA_LIBRARY") or os.path.join(_HERE, "libjfa.so")
 
 JFA_OK = 0
 JFA_ERR_INVALID_ARG = -1

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libjfa.so")
-SOURCES = ["plan.cpp", "api.cpp", "fwd.hip", "bwd.hip", "bwd_mx.hip", "dq.hip", "dq_mx.hip", "mx.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "noalloc.hip", "fwd.hip", "bwd.hip", "bwd_mx.hip", "dq.hip", "dq_mx.hip", "mx.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are disabled for all device code (ordinary float code is

@@ -1,18 +1,10 @@
 // C ABI entry points: argument validation and kernel launches on the caller's
 // stream. Nothing here allocates device memory or synchronises.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <cmath>
-#include <mutex>
 
 #include "internal.h"
-
-// Workspace of jfa_bwd_noalloc: a scratch area in the library's own device
-// memory (each GPU gets its copy when the code object is loaded there), so
-// that the call allocates nothing. In host code `scratch` is only a
-// host-side stand-in: kernels get the device address that
-// hipGetSymbolAddress gives for the current device (noalloc_scratch below).
-static __device__ __align__(256) char scratch[JFA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -69,29 +61,6 @@ int32_t check_common(const jfa_problem* p, const jfa_plan_info* info, int32_t pa
     if (info->num_tiles > 0 && d_kv_offsets == nullptr) return JFA_ERR_INVALID_ARG;
     if (info->num_tiles > 0 && !p->broadcast_q && d_q_offsets == nullptr)
         return JFA_ERR_INVALID_ARG;
-    return JFA_OK;
-}
-
-// Device address of `scratch` on the current device, looked up once per
-// device (with that device current) and kept.
-constexpr int kMaxDevices = 64;
-std::mutex g_scratch_mu;
-void* g_scratch_ptr[kMaxDevices] = {};
-
-int32_t noalloc_scratch(void** out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_status((int32_t)e);
-    if (dev < 0 || dev >= kMaxDevices) return JFA_ERR_INVALID_ARG;
-    std::lock_guard<std::mutex> lock(g_scratch_mu);
-    if (g_scratch_ptr[dev] == nullptr) {
-        void* p = nullptr;
-        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-        if (e != hipSuccess) return hip_status((int32_t)e);
-        if (p == nullptr || !aligned16(p)) return JFA_ERR_HIP;
-        g_scratch_ptr[dev] = p;
-    }
-    *out = g_scratch_ptr[dev];
     return JFA_OK;
 }
 
@@ -606,8 +575,9 @@ int32_t jfa_bwd_noalloc(const jfa_problem* prob, const jfa_device_plan* kv_plan,
     if (need > (int64_t)JFA_NOALLOC_SCRATCH_BYTES) return JFA_ERR_WORKSPACE;
     void* ws = nullptr;
     if (need > 0) {
-        st = noalloc_scratch(&ws);
+        st = hip_status(jfa::noalloc_scratch(&ws));
         if (st) return st;
+        if (ws == nullptr || !aligned16(ws)) return JFA_ERR_HIP;
     }
     return jfa_bwd_stages(JFA_BWD_ALL, prob, kv_plan, dq_plan, d_q_offsets, d_kv_offsets, q, k, v,
                           o, lse, d_o, dq, dk, dv, dq_accum, delta, ws, need, stream);

@@ -195,6 +195,10 @@ int32_t launch_dq_mx(const DqArgs& a, Mode mode, bool broadcast, void* stream);
 int32_t launch_dkdv_mx(const BwdArgs& a, Mode mode, bool broadcast, void* stream);
 int32_t launch_mx_quant_rows(const uint16_t* src, int64_t rows, int32_t H, int32_t D, uint8_t* codes,
                              uint8_t* scales, void* stream);
+// Device address, on the current device, of the library's own scratch area
+// of JFA_NOALLOC_SCRATCH_BYTES (the workspace of jfa_bwd_noalloc): looked up
+// once per device and kept. Returns a hipError_t value as int32.
+int32_t noalloc_scratch(void** out);
 int32_t launch_mx_quant_v(const uint16_t* v, const int32_t* kv_off, const int32_t* boff, int32_t B,
                           int32_t H, int32_t D, int32_t nbt, uint8_t* codes, uint8_t* scales,
                           void* stream);
