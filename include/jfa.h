@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define JFA_ABI_VERSION 9
+#define JFA_ABI_VERSION 10
 
 /* status codes */
 #define JFA_OK                 0
@@ -395,8 +395,9 @@ int32_t jfa_bwd_noalloc(const jfa_problem* prob, const jfa_device_plan* kv_plan,
  * bf16 dO and O and written out, as by JFA_BWD_DQ. Outputs as JFA_BWD_DQ:
  * per-sequence Q: dq and dq_accum; broadcast Q: the per-worker partials in
  * the workspace (same size as jfa_bwd's), which jfa_bwd_stages with
- * JFA_BWD_DQ_REDUCE turns into dq_accum and dq. The dK/dV pass stays bf16
- * (jfa_bwd_stages with JFA_BWD_DKDV after this call, which needs delta).
+ * JFA_BWD_DQ_REDUCE turns into dq_accum and dq. The dK/dV pass comes after
+ * this call, which writes the delta it needs: bf16 (jfa_bwd_stages with
+ * JFA_BWD_DKDV) or MXFP8 (jfa_bwd_dkdv_mx).
  * Layouts: codes [rows, H, D] and scales [H, rows, D/32] for the operands
  * encoded along d (rows: lq or T_q for Q, T_k for K and V, T_q for dO); K
  * along keys: codes [T_k, H, D], scales [H, NB, D] with the blocks of
@@ -472,6 +473,31 @@ int32_t jfa_bwd_dkdv_mx(const jfa_problem* prob, const jfa_device_plan* kv_plan,
                         const int32_t* d_do_row_block_offsets, int32_t num_do_row_blocks,
                         const float* lse, const float* delta, const jfa_mx_dkdv_operands* ops,
                         void* dk, void* dv, void* stream);
+
+/*
+ * Executed-tile log, for checking the kernels' walk over their plans (debug
+ * builds of the library only, libjfa_debug.so; the product library returns
+ * JFA_ERR_UNSUPPORTED and logs nothing). While set, every launch of the bf16
+ * forward, dK/dV and dQ kernels (jfa_fwd, jfa_bwd, jfa_bwd_stages,
+ * jfa_bwd_noalloc) has each worker record, in the order it takes them, the
+ * tiles it executes: worker w's area starts at int32 index
+ * w * (8 + 8 * records_per_worker) of d_log; area[0] = the number of tiles
+ * the worker took, and tile n (n < records_per_worker) is the 8 int32 at
+ * area + 8 + 8 n:
+ *   {pass (0 forward, 1 dK/dV, 2 dQ), worker, b, h, t, work, blocks, flags}
+ * with (b, h, t, work) the plan's record (the dQ pass's t as in its plan),
+ * blocks = the worker's blocks streamed so far at the tile's end (-1 for the
+ * forward, which logs a tile when its loader takes it) and flags the
+ * indices checked against the problem: 1 b outside the batch, 2 h outside
+ * the heads, 4 t outside the sequence's tiles. d_log: device memory, 16-byte
+ * aligned, of at least num_workers * (8 + 8 * records_per_worker) int32 for
+ * every launch made while it is set, owned by the caller, who zeroes the
+ * area before a launch whose log it reads (each launch writes over the
+ * last); launches that log must not overlap in time. NULL turns the log
+ * off. The setting is process-wide. The debug build waits for its log
+ * stores after each record, so it runs slower than the product library.
+ */
+int32_t jfa_debug_tile_log(int32_t* d_log, int32_t records_per_worker);
 
 #ifdef __cplusplus
 }

@@ -7,6 +7,7 @@ not built, every call raises -- there is no fallback path.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import dataclasses
 import os
@@ -19,6 +20,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # JFA_LIBRARY names another build of the same library to load instead (the
 # host-check build that the CPU tests run under the sanitizers).
 LIB_PATH = os.environ.get("JFA_LIBRARY") or os.path.join(_HERE, "libjfa.so")
+# the same library with the executed-tile log compiled in (jfa_debug_tile_log)
+DEBUG_LIB_PATH = os.path.join(_HERE, "libjfa_debug.so")
 
 JFA_OK = 0
 JFA_ERR_INVALID_ARG = -1
@@ -39,7 +42,7 @@ EXPORTS = (
     "jfa_offsets_from_lengths", "jfa_plan_query", "jfa_plan_build", "jfa_fwd_workspace_bytes",
     "jfa_fwd", "jfa_bwd_workspace_bytes", "jfa_bwd", "jfa_bwd_stages", "jfa_mx_block_offsets",
     "jfa_mx_quantize_rows", "jfa_mx_quantize_v", "jfa_fwd_mx", "jfa_bwd_dq_mx",
-    "jfa_bwd_noalloc", "jfa_bwd_dkdv_mx",
+    "jfa_bwd_noalloc", "jfa_bwd_dkdv_mx", "jfa_debug_tile_log",
 )
 JFA_BWD_PREPROCESS = 1
 JFA_BWD_DQ = 2
@@ -103,42 +106,62 @@ _I32P = ctypes.POINTER(ctypes.c_int32)
 def _lib():
     global _LIB
     if _LIB is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError("libjfa.so is not built (run jagged_flashattention_amd/build.py); "
-                               "there is no fallback implementation")
-        lib = ctypes.CDLL(LIB_PATH)
-        i32, i64 = ctypes.c_int32, ctypes.c_int64
-        prob, info = ctypes.POINTER(JfaProblem), ctypes.POINTER(JfaPlanInfo)
-        dplan = ctypes.POINTER(JfaDevicePlan)
-        sig = {
-            "jfa_abi_version": (i32, []),
-            "jfa_status_string": (ctypes.c_char_p, [i32]),
-            "jfa_last_hip_error": (i32, []),
-            "jfa_device_workers": (i32, [i32, _I32P]),
-            "jfa_offsets_from_lengths": (i32, [_P, i32, _P]),
-            "jfa_plan_query": (i32, [prob, _P, _P, _P, i32, i32, info]),
-            "jfa_plan_build": (i32, [prob, _P, _P, _P, i32, i32, info, _P, _P, _P, _P]),
-            "jfa_fwd_workspace_bytes": (i32, [prob, info, ctypes.POINTER(i64)]),
-            "jfa_fwd": (i32, [prob, info] + [_P] * 12 + [i64, _P]),
-            "jfa_bwd_workspace_bytes": (i32, [prob, info, ctypes.POINTER(i64)]),
-            "jfa_bwd": (i32, [prob, dplan, dplan] + [_P] * 14 + [i64, _P]),
-            "jfa_bwd_stages": (i32, [i32, prob, dplan, dplan] + [_P] * 14 + [i64, _P]),
-            "jfa_bwd_noalloc": (i32, [prob, dplan, dplan] + [_P] * 14),
-            "jfa_bwd_dkdv_mx": (i32, [prob, dplan, _P, _P, _P, i32, _P, i32, _P, _P,
-                                      ctypes.POINTER(JfaMxDkdvOperands), _P, _P, _P]),
-            "jfa_mx_block_offsets": (i32, [_P, i32, _P]),
-            "jfa_mx_quantize_rows": (i32, [_P, i64, i32, i32, _P, _P, _P]),
-            "jfa_mx_quantize_v": (i32, [_P, _P, _P, i32, i32, i32, i32, _P, _P, _P]),
-            "jfa_fwd_mx": (i32, [prob, info] + [_P] * 7 + [i32] + [_P] * 9 + [i64, _P]),
-            "jfa_bwd_dq_mx": (i32, [prob, dplan, _P, _P, _P, i32, _P, _P, _P,
-                                    ctypes.POINTER(JfaMxBwdOperands), _P, _P, _P, _P, i64, _P]),
-        }
-        for name, (res, args) in sig.items():
-            fn = getattr(lib, name)
-            fn.restype = res
-            fn.argtypes = args
-        _LIB = lib
+        _LIB = load_library(LIB_PATH)
     return _LIB
+
+
+def load_library(path):
+    """A ctypes handle of a build of the library at ``path`` with every
+    entry point's signature set."""
+    if not os.path.exists(path):
+        raise RuntimeError("%s is not built (run jagged_flashattention_amd/build.py); "
+                           "there is no fallback implementation" % os.path.basename(path))
+    lib = ctypes.CDLL(path)
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    prob, info = ctypes.POINTER(JfaProblem), ctypes.POINTER(JfaPlanInfo)
+    dplan = ctypes.POINTER(JfaDevicePlan)
+    sig = {
+        "jfa_abi_version": (i32, []),
+        "jfa_status_string": (ctypes.c_char_p, [i32]),
+        "jfa_last_hip_error": (i32, []),
+        "jfa_device_workers": (i32, [i32, _I32P]),
+        "jfa_offsets_from_lengths": (i32, [_P, i32, _P]),
+        "jfa_plan_query": (i32, [prob, _P, _P, _P, i32, i32, info]),
+        "jfa_plan_build": (i32, [prob, _P, _P, _P, i32, i32, info, _P, _P, _P, _P]),
+        "jfa_fwd_workspace_bytes": (i32, [prob, info, ctypes.POINTER(i64)]),
+        "jfa_fwd": (i32, [prob, info] + [_P] * 12 + [i64, _P]),
+        "jfa_bwd_workspace_bytes": (i32, [prob, info, ctypes.POINTER(i64)]),
+        "jfa_bwd": (i32, [prob, dplan, dplan] + [_P] * 14 + [i64, _P]),
+        "jfa_bwd_stages": (i32, [i32, prob, dplan, dplan] + [_P] * 14 + [i64, _P]),
+        "jfa_bwd_noalloc": (i32, [prob, dplan, dplan] + [_P] * 14),
+        "jfa_bwd_dkdv_mx": (i32, [prob, dplan, _P, _P, _P, i32, _P, i32, _P, _P,
+                                  ctypes.POINTER(JfaMxDkdvOperands), _P, _P, _P]),
+        "jfa_mx_block_offsets": (i32, [_P, i32, _P]),
+        "jfa_mx_quantize_rows": (i32, [_P, i64, i32, i32, _P, _P, _P]),
+        "jfa_mx_quantize_v": (i32, [_P, _P, _P, i32, i32, i32, i32, _P, _P, _P]),
+        "jfa_fwd_mx": (i32, [prob, info] + [_P] * 7 + [i32] + [_P] * 9 + [i64, _P]),
+        "jfa_bwd_dq_mx": (i32, [prob, dplan, _P, _P, _P, i32, _P, _P, _P,
+                                ctypes.POINTER(JfaMxBwdOperands), _P, _P, _P, _P, i64, _P]),
+        "jfa_debug_tile_log": (i32, [_P, i32]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+@contextlib.contextmanager
+def using_library(lib):
+    """Route every call of this module to ``lib`` (a load_library handle,
+    e.g. of the debug build) inside the block."""
+    global _LIB
+    old = _LIB
+    _LIB = lib
+    try:
+        yield lib
+    finally:
+        _LIB = old
 
 
 def _check(status: int, where: str):
@@ -413,6 +436,24 @@ def jfa_bwd_dkdv_mx(prob: Problem, kv_plan: DevicePlan, q_offsets, kv_offsets, q
                                   int(num_do_row_blocks), _dev_ptr(lse), _dev_ptr(delta),
                                   ctypes.byref(mo), _dev_ptr(dk), _dev_ptr(dv), _stream(stream)),
            "jfa_bwd_dkdv_mx")
+
+
+def jfa_debug_tile_log(log, records_per_worker: int) -> None:
+    """Set (a device int32 tensor) or clear (None) the executed-tile log of
+    the debug build; the product library raises JfaError (unsupported)."""
+    _check(_lib().jfa_debug_tile_log(_dev_ptr(log), int(records_per_worker)), "jfa_debug_tile_log")
+
+
+def read_tile_log(log, num_workers: int, records_per_worker: int):
+    """The records of an executed-tile log as a list per worker of int32
+    [n, 8] arrays (pass, worker, b, h, t, work, blocks, flags), plus the
+    number of tiles each worker took."""
+    a = log.cpu().numpy().reshape(-1)[:num_workers * (8 + 8 * records_per_worker)]
+    a = a.reshape(num_workers, 8 + 8 * records_per_worker)
+    counts = a[:, 0].copy()
+    recs = [a[w, 8:].reshape(records_per_worker, 8)[:min(int(counts[w]), records_per_worker)]
+            for w in range(num_workers)]
+    return recs, counts
 
 
 def jfa_mx_block_offsets(kv_offsets) -> np.ndarray:

@@ -2,11 +2,18 @@
 // stream. Nothing here allocates device memory or synchronises.
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
 #include <cmath>
 
 #include "internal.h"
 
 namespace {
+
+#ifdef JFA_TILE_LOG
+constexpr bool kTileLogBuild = true;
+#else
+constexpr bool kTileLogBuild = false;
+#endif
 
 thread_local int32_t g_last_hip_error = 0;
 
@@ -73,6 +80,17 @@ bool tensor_ok(const void* ptr, int64_t elems) {
 bool scales_ok(const void* ptr, int64_t bytes) {
     if (bytes == 0) return true;
     return ptr != nullptr && aligned4(ptr);
+}
+
+// Executed-tile log of debug builds: where the kernels write it (null: off).
+std::atomic<int32_t*> g_tile_log{nullptr};
+std::atomic<int32_t> g_tile_log_cap{0};
+
+template <typename Args>
+void set_debug_fields(Args& a, int32_t batch) {
+    a.batch = batch;
+    a.tile_log = kTileLogBuild ? g_tile_log.load() : nullptr;
+    a.tile_log_cap = g_tile_log_cap.load();
 }
 
 }  // namespace
@@ -165,6 +183,7 @@ static int32_t fwd_args(const jfa_problem* prob, const jfa_plan_info* info, cons
     a.scale_log2 = prob->softmax_scale * 1.4426950408889634f;
     a.q_rows = prob->broadcast_q ? prob->lq : info->total_q;
     a.total_kv = info->total_kv;
+    set_debug_fields(a, prob->batch);
     *launch = true;
     return JFA_OK;
 }
@@ -322,6 +341,7 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device
     const bool atomic = bcast && (stages & JFA_BWD_DQ_ATOMIC) != 0;
 
     jfa::BwdArgs a{};
+    set_debug_fields(a, prob->batch);
     a.worker_ptr = kv_plan->worker_ptr;
     a.tiles = kv_plan->tiles;
     a.sp_ptr = kv_plan->sparse_ptr;
@@ -357,7 +377,7 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device
         if (st) return st;
     }
     if ((stages & JFA_BWD_DQ) && qi->num_tiles > 0) {
-        jfa::DqArgs d;
+        jfa::DqArgs d{};
         d.worker_ptr = dq_plan->worker_ptr;
         d.tiles = dq_plan->tiles;
         d.sp_ptr = dq_plan->sparse_ptr;
@@ -384,6 +404,7 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device
         d.num_workers = qi->num_workers;
         d.scale = prob->softmax_scale;
         d.scale_log2 = a.scale_log2;
+        set_debug_fields(d, prob->batch);
         st = hip_status(jfa::launch_dq(d, prob->head_dim, mode, bcast, atomic, stream));
         if (st) return st;
     }
@@ -483,6 +504,7 @@ int32_t jfa_bwd_dq_mx(const jfa_problem* prob, const jfa_device_plan* dq_plan,
     d.kk_nb = num_key_blocks;
     d.q_rows = (int32_t)q_rows;
     d.total_kv = qi->total_kv;
+    set_debug_fields(d, prob->batch);
     return hip_status(jfa::launch_dq_mx(d, mode_of(prob), bcast, stream));
 }
 
@@ -523,6 +545,7 @@ int32_t jfa_bwd_dkdv_mx(const jfa_problem* prob, const jfa_device_plan* kv_plan,
     if (ki->num_tiles == 0) return JFA_OK;
     const jfa::Band bd = jfa::band_of(prob);
     jfa::BwdArgs a{};
+    set_debug_fields(a, prob->batch);
     a.worker_ptr = kv_plan->worker_ptr;
     a.tiles = kv_plan->tiles;
     a.sp_ptr = kv_plan->sparse_ptr;
@@ -592,6 +615,14 @@ int32_t jfa_bwd(const jfa_problem* prob, const jfa_device_plan* kv_plan,
     return jfa_bwd_stages(JFA_BWD_ALL, prob, kv_plan, dq_plan, d_q_offsets, d_kv_offsets, q, k, v,
                           o, lse, d_o, dq, dk, dv, dq_accum, delta, workspace, workspace_bytes,
                           stream);
+}
+
+int32_t jfa_debug_tile_log(int32_t* d_log, int32_t records_per_worker) {
+    if (!kTileLogBuild) return JFA_ERR_UNSUPPORTED;
+    if (d_log != nullptr && (records_per_worker < 0 || !aligned16(d_log))) return JFA_ERR_INVALID_ARG;
+    g_tile_log_cap.store(d_log != nullptr ? records_per_worker : 0);
+    g_tile_log.store(d_log);
+    return JFA_OK;
 }
 
 }  // extern "C"

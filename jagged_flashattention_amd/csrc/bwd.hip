@@ -406,6 +406,12 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
         // (The banded mode keeps the direct K loads: the staged form spills
         // there.)
         __syncthreads();
+        if (kTileLog && a.tile_log != nullptr) {
+            const int fl = (T.b < 0 || T.b >= a.batch ? kLogBadBatch : 0) |
+                           (T.h < 0 || T.h >= H ? kLogBadHead : 0) |
+                           (T.n < 0 || T.n * kBwdBlockN >= T.L ? kLogBadTile : 0);
+            tile_log(a.tile_log, a.tile_log_cap, ti - t_begin, {1, w, T.b, T.h, T.n, T.work, s, fl});
+        }
         constexpr bool kStageK = MODE != kCausal;
         const bool has_next = ti + 1 < t_end;
         const KvTile NT = has_next ? tile_info(ti + 1) : T;

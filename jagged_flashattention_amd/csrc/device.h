@@ -93,6 +93,42 @@ __device__ __forceinline__ void wait_vmem_keep() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Executed-tile log of debug builds (compiled with JFA_TILE_LOG; nothing
+// otherwise). Thread 0 of worker w's workgroup writes the n-th tile the
+// worker takes as record n of its area, log + w * (8 + 8 cap): area[0] is
+// the number of tiles taken so far (n + 1), record n is the 8 int32 at
+// area + 8 + 8 n (records past cap are counted, not stored). The wave then
+// waits for the stores, so the kernel's counted waits on its own copies
+// still see only those copies.
+struct TileLogRec {
+    int pass, worker, b, h, t, work, blocks, flags;
+};
+__device__ __forceinline__ void tile_log(int32_t* log, int cap, int n, const TileLogRec& r) {
+#ifdef JFA_TILE_LOG
+    if (log != nullptr) {
+        if (threadIdx.x == 0) {
+            int32_t* area = log + (int64_t)r.worker * (8 + 8 * (int64_t)cap);
+            if (n < cap) {
+                int4* rec = (int4*)(area + 8 + 8 * (int64_t)n);
+                rec[0] = make_int4(r.pass, r.worker, r.b, r.h);
+                rec[1] = make_int4(r.t, r.work, r.blocks, r.flags);
+            }
+            area[0] = n + 1;
+        }
+        wait_vmem();
+    }
+#else
+    (void)log, (void)cap, (void)n, (void)r;
+#endif
+}
+#ifdef JFA_TILE_LOG
+constexpr bool kTileLog = true;
+#else
+constexpr bool kTileLog = false;
+#endif
+// flag bits of a record: the plan's indices checked against the problem
+constexpr int kLogBadBatch = 1, kLogBadHead = 2, kLogBadTile = 4, kLogBadStream = 8;
+
 // Scheduling hint for a run of N LDS operand reads each feeding one MFMA:
 // issue the first A reads, then alternate one MFMA with one more read, then
 // the last A MFMAs. Without it the scheduler keeps a single read in flight

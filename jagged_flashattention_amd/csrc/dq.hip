@@ -396,6 +396,13 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
                 });
             }
         }
+        if (kTileLog && a.tile_log != nullptr) {
+            const int fl = (T.b < 0 || T.b >= a.batch ? kLogBadBatch : 0) |
+                           (T.h < 0 || T.h >= H ? kLogBadHead : 0) |
+                           (T.t < 0 || T.k0 < 0 || T.t * kFwdBlockM >= Lq ? kLogBadTile : 0);
+            tile_log(a.tile_log, a.tile_log_cap, ti - t_begin,
+                     {2, w, T.b, T.h, T.t + a.chunk_div * T.k0, T.work, s, fl});
+        }
     }
     if (BCAST && ATOMIC) {
         // this worker's sum over its tiles (all of one (head, Q tile) group)

@@ -210,6 +210,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
     bool l_end = false;
     TileInfo LT;
     LT.work = 0;
+    int log_n = 0;   // tiles taken (executed-tile log)
     auto advance = [&]() {   // to the next tile with blocks, or the end
         while (!l_end && l_i >= LT.work) {
             int nt;
@@ -227,6 +228,14 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
             l_ti = nt;
             l_i = 0;
             LT = tile_info(nt);
+            if (kTileLog && a.tile_log != nullptr) {
+                int lq0, lLq, lrow0;
+                rows_of(LT, lq0, lLq, lrow0);
+                const int fl = (LT.b < 0 || LT.b >= a.batch ? kLogBadBatch : 0) |
+                               (LT.h < 0 || LT.h >= a.num_heads ? kLogBadHead : 0) |
+                               (LT.t < 0 || LT.t * kFwdBlockM >= lLq ? kLogBadTile : 0);
+                tile_log(a.tile_log, a.tile_log_cap, log_n++, {0, w, LT.b, LT.h, LT.t, LT.work, -1, fl});
+            }
             if (LT.work == 0) {
                 zero_rows(LT);
             } else {

@@ -72,6 +72,10 @@ struct FwdArgs {
     int32_t q_rows;         // lq (broadcast) or T_q
     int32_t total_kv;
     int32_t v_nb;           // NB
+    // executed-tile log of debug builds (see tile_log in device.h)
+    int32_t batch;
+    int32_t* tile_log;       // null: off
+    int32_t tile_log_cap;    // records per worker
 };
 
 // Workspace of a dynamic forward plan (two int32 counters, padded).
@@ -121,6 +125,10 @@ struct BwdArgs {
     int32_t qr_nb, dor_nb;
     int32_t q_rows;
     int32_t total_kv;
+    // executed-tile log of debug builds (see tile_log in device.h)
+    int32_t batch;
+    int32_t* tile_log;       // null: off
+    int32_t tile_log_cap;    // records per worker
 };
 
 // Q-stationary dQ pass of the backward (JFA_PASS_DQ plan).
@@ -165,6 +173,10 @@ struct DqArgs {
     int32_t kk_nb;           // NB
     int32_t q_rows;
     int32_t total_kv;
+    // executed-tile log of debug builds (see tile_log in device.h)
+    int32_t batch;
+    int32_t* tile_log;       // null: off
+    int32_t tile_log_cap;    // records per worker
 };
 
 // Deterministic sum of the broadcast-Q dQ partials of each (head, Q tile)

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert J.jfa_abi_version() == 9
+    assert J.jfa_abi_version() == 10
     for st in range(-7, 1):
         assert J.jfa_status_string(st) not in ("", "unknown status")
     assert J.jfa_status_string(-99) == "unknown status"
@@ -333,3 +333,16 @@ def test_bwd_stage_flags_validated_before_launch():
                                  ctypes.byref(plans[0]), ctypes.byref(plans[1]), None,
                                  ctypes.c_void_p(0x1000), *[f(x) for x in args], f(t), need, None)
     assert st == J.JFA_ERR_INVALID_ARG
+
+
+def test_tile_log_is_debug_only():
+    """The product library has no executed-tile log; the debug build takes a
+    16-byte-aligned log or NULL (argument checks only: nothing launches)."""
+    with pytest.raises(J.JfaError) as e:
+        J.jfa_debug_tile_log(None, 0)
+    assert e.value.status == J.JFA_ERR_UNSUPPORTED
+    dbg = J.load_library(J.DEBUG_LIB_PATH)
+    assert dbg.jfa_abi_version() == J.jfa_abi_version()
+    assert dbg.jfa_debug_tile_log(ctypes.c_void_p(0x1008), 4) == J.JFA_ERR_INVALID_ARG
+    assert dbg.jfa_debug_tile_log(ctypes.c_void_p(0x1000), -1) == J.JFA_ERR_INVALID_ARG
+    assert dbg.jfa_debug_tile_log(None, 0) == J.JFA_OK
