@@ -4,7 +4,11 @@
 
 #include <atomic>
 #include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
 
+#include "hostlog.h"
 #include "internal.h"
 
 namespace {
@@ -94,6 +98,38 @@ void set_debug_fields(Args& a, int32_t batch) {
 }
 
 }  // namespace
+
+namespace jfa {
+
+bool log_enabled() {
+    static const bool on = [] {
+        const char* e = std::getenv("JFA_LOG");
+        return e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0;
+    }();
+    return on;
+}
+
+void log_line(const char* what, const jfa_problem* p, const jfa_plan_info* info, int32_t extra,
+              int32_t status, double host_us) {
+    char buf[512];
+    int n = std::snprintf(buf, sizeof buf, "jfa: %s", what);
+    if (p != nullptr && n > 0 && n < (int)sizeof buf)
+        n += std::snprintf(buf + n, sizeof buf - n, " B=%d H=%d D=%d %s lq=%d causal=%d window=[%d,%d] mask=%dx%d",
+                           p->batch, p->num_heads, p->head_dim, p->broadcast_q ? "broadcast-q" : "per-seq-q",
+                           p->lq, p->causal, p->window_left, p->window_right, p->mask_q_blocks,
+                           p->mask_kv_blocks);
+    // a planner call's info is its output: only meaningful when it succeeded
+    const bool info_out = std::strncmp(what, "jfa_plan", 8) == 0;
+    if (info != nullptr && (status == JFA_OK || !info_out) && n > 0 && n < (int)sizeof buf)
+        n += std::snprintf(buf + n, sizeof buf - n, " pass=%d workers=%d tiles=%d work=%lld",
+                           info->pass, info->num_workers, info->num_tiles, (long long)info->total_work);
+    if (n > 0 && n < (int)sizeof buf)
+        std::snprintf(buf + n, sizeof buf - n, " arg=%d -> %s (%d) %.1f us host\n", extra,
+                      jfa_status_string(status), status, host_us);
+    std::fputs(buf, stderr);
+}
+
+}  // namespace jfa
 
 extern "C" {
 
@@ -195,20 +231,22 @@ int32_t jfa_fwd(const jfa_problem* prob, const jfa_plan_info* info, const int32_
                 const int32_t* d_q_offsets, const int32_t* d_kv_offsets, const void* q,
                 const void* k, const void* v, void* o, float* lse, void* workspace,
                 int64_t workspace_bytes, void* stream) {
-    jfa::FwdArgs a;
-    bool launch = false;
-    int32_t st = fwd_args(prob, info, d_worker_ptr, d_tiles, d_sparse_ptr, d_sparse_idx, d_q_offsets,
-                          d_kv_offsets, o, lse, workspace, workspace_bytes, a, &launch);
-    if (st || !launch) return st;
-    const int64_t hd = (int64_t)prob->num_heads * prob->head_dim;
-    if (!tensor_ok(q, (int64_t)a.q_rows * hd) || !tensor_ok(k, info->total_kv * hd) ||
-        !tensor_ok(v, info->total_kv * hd))
-        return JFA_ERR_INVALID_ARG;
-    a.q = static_cast<const uint16_t*>(q);
-    a.k = static_cast<const uint16_t*>(k);
-    a.v = static_cast<const uint16_t*>(v);
-    return hip_status(jfa::launch_fwd(a, prob->head_dim, mode_of(prob), prob->broadcast_q != 0,
-                                      stream));
+    return jfa::logged("jfa_fwd", prob, info, 0, [&]() -> int32_t {
+        jfa::FwdArgs a;
+        bool launch = false;
+        int32_t st = fwd_args(prob, info, d_worker_ptr, d_tiles, d_sparse_ptr, d_sparse_idx, d_q_offsets,
+                              d_kv_offsets, o, lse, workspace, workspace_bytes, a, &launch);
+        if (st || !launch) return st;
+        const int64_t hd = (int64_t)prob->num_heads * prob->head_dim;
+        if (!tensor_ok(q, (int64_t)a.q_rows * hd) || !tensor_ok(k, info->total_kv * hd) ||
+            !tensor_ok(v, info->total_kv * hd))
+            return JFA_ERR_INVALID_ARG;
+        a.q = static_cast<const uint16_t*>(q);
+        a.k = static_cast<const uint16_t*>(k);
+        a.v = static_cast<const uint16_t*>(v);
+        return hip_status(jfa::launch_fwd(a, prob->head_dim, mode_of(prob), prob->broadcast_q != 0,
+                                          stream));
+    });
 }
 
 int32_t jfa_mx_block_offsets(const int32_t* h_kv_offsets, int32_t batch, int32_t* h_block_offsets) {
@@ -258,32 +296,34 @@ int32_t jfa_fwd_mx(const jfa_problem* prob, const jfa_plan_info* info, const int
                    const void* q_scales, const void* k_codes, const void* k_scales,
                    const void* v_codes, const void* v_scales, void* o, float* lse, void* workspace,
                    int64_t workspace_bytes, void* stream) {
-    int32_t st = jfa::check_problem(prob);
-    if (st) return st;
-    if (prob->head_dim != 128) return JFA_ERR_UNSUPPORTED;
-    jfa::FwdArgs a;
-    bool launch = false;
-    st = fwd_args(prob, info, d_worker_ptr, d_tiles, d_sparse_ptr, d_sparse_idx, d_q_offsets,
-                  d_kv_offsets, o, lse, workspace, workspace_bytes, a, &launch);
-    if (st || !launch) return st;
-    // one 32-key V block per 32 keys of each sequence: at least T_k / 32
-    if (num_blocks < (info->total_kv + 31) / 32 || d_block_offsets == nullptr) return JFA_ERR_INVALID_ARG;
-    const int64_t hd = (int64_t)prob->num_heads * prob->head_dim;
-    const int64_t H = prob->num_heads, nbd = prob->head_dim / 32;
-    if (!tensor_ok(q_codes, (int64_t)a.q_rows * hd) || !tensor_ok(k_codes, info->total_kv * hd) ||
-        !tensor_ok(v_codes, info->total_kv * hd) || !scales_ok(q_scales, H * a.q_rows * nbd) ||
-        !scales_ok(k_scales, H * info->total_kv * nbd) ||
-        !scales_ok(v_scales, H * (int64_t)num_blocks * prob->head_dim))
-        return JFA_ERR_INVALID_ARG;
-    a.q8 = static_cast<const uint8_t*>(q_codes);
-    a.k8 = static_cast<const uint8_t*>(k_codes);
-    a.v8 = static_cast<const uint8_t*>(v_codes);
-    a.q_sc = static_cast<const uint8_t*>(q_scales);
-    a.k_sc = static_cast<const uint8_t*>(k_scales);
-    a.v_sc = static_cast<const uint8_t*>(v_scales);
-    a.v_boff = d_block_offsets;
-    a.v_nb = num_blocks;
-    return hip_status(jfa::launch_fwd_mx(a, mode_of(prob), prob->broadcast_q != 0, stream));
+    return jfa::logged("jfa_fwd_mx", prob, info, 0, [&]() -> int32_t {
+        int32_t st = jfa::check_problem(prob);
+        if (st) return st;
+        if (prob->head_dim != 128) return JFA_ERR_UNSUPPORTED;
+        jfa::FwdArgs a;
+        bool launch = false;
+        st = fwd_args(prob, info, d_worker_ptr, d_tiles, d_sparse_ptr, d_sparse_idx, d_q_offsets,
+                      d_kv_offsets, o, lse, workspace, workspace_bytes, a, &launch);
+        if (st || !launch) return st;
+        // one 32-key V block per 32 keys of each sequence: at least T_k / 32
+        if (num_blocks < (info->total_kv + 31) / 32 || d_block_offsets == nullptr) return JFA_ERR_INVALID_ARG;
+        const int64_t hd = (int64_t)prob->num_heads * prob->head_dim;
+        const int64_t H = prob->num_heads, nbd = prob->head_dim / 32;
+        if (!tensor_ok(q_codes, (int64_t)a.q_rows * hd) || !tensor_ok(k_codes, info->total_kv * hd) ||
+            !tensor_ok(v_codes, info->total_kv * hd) || !scales_ok(q_scales, H * a.q_rows * nbd) ||
+            !scales_ok(k_scales, H * info->total_kv * nbd) ||
+            !scales_ok(v_scales, H * (int64_t)num_blocks * prob->head_dim))
+            return JFA_ERR_INVALID_ARG;
+        a.q8 = static_cast<const uint8_t*>(q_codes);
+        a.k8 = static_cast<const uint8_t*>(k_codes);
+        a.v8 = static_cast<const uint8_t*>(v_codes);
+        a.q_sc = static_cast<const uint8_t*>(q_scales);
+        a.k_sc = static_cast<const uint8_t*>(k_scales);
+        a.v_sc = static_cast<const uint8_t*>(v_scales);
+        a.v_boff = d_block_offsets;
+        a.v_nb = num_blocks;
+        return hip_status(jfa::launch_fwd_mx(a, mode_of(prob), prob->broadcast_q != 0, stream));
+    });
 }
 
 int32_t jfa_bwd_workspace_bytes(const jfa_problem* prob, const jfa_plan_info* dq_info,
@@ -312,71 +352,163 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device
                        const void* o, const float* lse, const void* d_o, void* dq, void* dk,
                        void* dv, float* dq_accum, float* delta, void* workspace,
                        int64_t workspace_bytes, void* stream) {
-    if (stages < 0 || stages > (JFA_BWD_ALL | JFA_BWD_PREPROCESS | JFA_BWD_DQ_ATOMIC))
-        return JFA_ERR_INVALID_ARG;
-    int32_t st = check_plan(prob, kv_plan, JFA_PASS_BWD, d_q_offsets, d_kv_offsets);
-    if (st) return st;
-    st = check_plan(prob, dq_plan, JFA_PASS_DQ, d_q_offsets, d_kv_offsets);
-    if (st) return st;
-    const jfa_plan_info* ki = kv_plan->info;
-    const jfa_plan_info* qi = dq_plan->info;
-    if (ki->total_q != qi->total_q || ki->total_kv != qi->total_kv) return JFA_ERR_PLAN_MISMATCH;
-    int64_t need = 0;
-    st = jfa_bwd_workspace_bytes(prob, qi, &need);
-    if (st) return st;
-    if (workspace_bytes < need || (need > 0 && (workspace == nullptr || !aligned16(workspace))))
-        return JFA_ERR_WORKSPACE;
-    const int64_t hd = (int64_t)prob->num_heads * prob->head_dim;
-    const int64_t q_rows = prob->broadcast_q ? prob->lq : ki->total_q;
-    const int64_t tq = ki->total_q, tk = ki->total_kv;
-    if (!tensor_ok(q, q_rows * hd) || !tensor_ok(k, tk * hd) || !tensor_ok(v, tk * hd) ||
-        !tensor_ok(o, tq * hd) || !tensor_ok(d_o, tq * hd) || !tensor_ok(dq, q_rows * hd) ||
-        !tensor_ok(dk, tk * hd) || !tensor_ok(dv, tk * hd) || !tensor_ok(dq_accum, q_rows * hd))
-        return JFA_ERR_INVALID_ARG;
-    if (tq > 0 && (lse == nullptr || delta == nullptr || !aligned4(lse) || !aligned4(delta)))
-        return JFA_ERR_INVALID_ARG;
-    if (tq == 0 && q_rows == 0 && tk == 0) return JFA_OK;
-    const jfa::Mode mode = mode_of(prob);
-    const bool bcast = prob->broadcast_q != 0;
-    const bool atomic = bcast && (stages & JFA_BWD_DQ_ATOMIC) != 0;
-
-    jfa::BwdArgs a{};
-    set_debug_fields(a, prob->batch);
-    a.worker_ptr = kv_plan->worker_ptr;
-    a.tiles = kv_plan->tiles;
-    a.sp_ptr = kv_plan->sparse_ptr;
-    a.sp_idx = kv_plan->sparse_idx;
-    a.q_off = bcast ? nullptr : d_q_offsets;
-    a.kv_off = d_kv_offsets;
-    a.q = static_cast<const uint16_t*>(q);
-    a.k = static_cast<const uint16_t*>(k);
-    a.v = static_cast<const uint16_t*>(v);
-    a.o = static_cast<const uint16_t*>(o);
-    a.lse = lse;
-    a.d_o = static_cast<const uint16_t*>(d_o);
-    a.dk = static_cast<uint16_t*>(dk);
-    a.dv = static_cast<uint16_t*>(dv);
-    a.delta = delta;
-    a.num_heads = prob->num_heads;
-    a.lq = prob->lq;
-    a.total_q = ki->total_q;
-    a.mask_kv_blocks = prob->mask_kv_blocks;
-    a.num_workers = ki->num_tiles > 0 ? ki->num_workers : 0;  // 0: no dK/dV launch
-    const jfa::Band bd = jfa::band_of(prob);
-    a.win_left = bd.left;
-    a.win_right = bd.right;
-    a.scale = prob->softmax_scale;
-    a.scale_log2 = prob->softmax_scale * 1.4426950408889634f;
-    if (stages & JFA_BWD_PREPROCESS) {
-        st = hip_status(jfa::launch_bwd(a, prob->head_dim, mode, bcast, JFA_BWD_PREPROCESS, stream));
+    return jfa::logged("jfa_bwd_stages", prob, kv_plan != nullptr ? kv_plan->info : nullptr, stages, [&]() -> int32_t {
+        if (stages < 0 || stages > (JFA_BWD_ALL | JFA_BWD_PREPROCESS | JFA_BWD_DQ_ATOMIC))
+            return JFA_ERR_INVALID_ARG;
+        int32_t st = check_plan(prob, kv_plan, JFA_PASS_BWD, d_q_offsets, d_kv_offsets);
         if (st) return st;
-    }
-
-    if ((stages & JFA_BWD_DQ) && atomic) {
-        st = hip_status(jfa::launch_dq_zero(dq_accum, q_rows * hd, stream));
+        st = check_plan(prob, dq_plan, JFA_PASS_DQ, d_q_offsets, d_kv_offsets);
         if (st) return st;
-    }
-    if ((stages & JFA_BWD_DQ) && qi->num_tiles > 0) {
+        const jfa_plan_info* ki = kv_plan->info;
+        const jfa_plan_info* qi = dq_plan->info;
+        if (ki->total_q != qi->total_q || ki->total_kv != qi->total_kv) return JFA_ERR_PLAN_MISMATCH;
+        int64_t need = 0;
+        st = jfa_bwd_workspace_bytes(prob, qi, &need);
+        if (st) return st;
+        if (workspace_bytes < need || (need > 0 && (workspace == nullptr || !aligned16(workspace))))
+            return JFA_ERR_WORKSPACE;
+        const int64_t hd = (int64_t)prob->num_heads * prob->head_dim;
+        const int64_t q_rows = prob->broadcast_q ? prob->lq : ki->total_q;
+        const int64_t tq = ki->total_q, tk = ki->total_kv;
+        if (!tensor_ok(q, q_rows * hd) || !tensor_ok(k, tk * hd) || !tensor_ok(v, tk * hd) ||
+            !tensor_ok(o, tq * hd) || !tensor_ok(d_o, tq * hd) || !tensor_ok(dq, q_rows * hd) ||
+            !tensor_ok(dk, tk * hd) || !tensor_ok(dv, tk * hd) || !tensor_ok(dq_accum, q_rows * hd))
+            return JFA_ERR_INVALID_ARG;
+        if (tq > 0 && (lse == nullptr || delta == nullptr || !aligned4(lse) || !aligned4(delta)))
+            return JFA_ERR_INVALID_ARG;
+        if (tq == 0 && q_rows == 0 && tk == 0) return JFA_OK;
+        const jfa::Mode mode = mode_of(prob);
+        const bool bcast = prob->broadcast_q != 0;
+        const bool atomic = bcast && (stages & JFA_BWD_DQ_ATOMIC) != 0;
+
+        jfa::BwdArgs a{};
+        set_debug_fields(a, prob->batch);
+        a.worker_ptr = kv_plan->worker_ptr;
+        a.tiles = kv_plan->tiles;
+        a.sp_ptr = kv_plan->sparse_ptr;
+        a.sp_idx = kv_plan->sparse_idx;
+        a.q_off = bcast ? nullptr : d_q_offsets;
+        a.kv_off = d_kv_offsets;
+        a.q = static_cast<const uint16_t*>(q);
+        a.k = static_cast<const uint16_t*>(k);
+        a.v = static_cast<const uint16_t*>(v);
+        a.o = static_cast<const uint16_t*>(o);
+        a.lse = lse;
+        a.d_o = static_cast<const uint16_t*>(d_o);
+        a.dk = static_cast<uint16_t*>(dk);
+        a.dv = static_cast<uint16_t*>(dv);
+        a.delta = delta;
+        a.num_heads = prob->num_heads;
+        a.lq = prob->lq;
+        a.total_q = ki->total_q;
+        a.mask_kv_blocks = prob->mask_kv_blocks;
+        a.num_workers = ki->num_tiles > 0 ? ki->num_workers : 0;  // 0: no dK/dV launch
+        const jfa::Band bd = jfa::band_of(prob);
+        a.win_left = bd.left;
+        a.win_right = bd.right;
+        a.scale = prob->softmax_scale;
+        a.scale_log2 = prob->softmax_scale * 1.4426950408889634f;
+        if (stages & JFA_BWD_PREPROCESS) {
+            st = hip_status(jfa::launch_bwd(a, prob->head_dim, mode, bcast, JFA_BWD_PREPROCESS, stream));
+            if (st) return st;
+        }
+
+        if ((stages & JFA_BWD_DQ) && atomic) {
+            st = hip_status(jfa::launch_dq_zero(dq_accum, q_rows * hd, stream));
+            if (st) return st;
+        }
+        if ((stages & JFA_BWD_DQ) && qi->num_tiles > 0) {
+            jfa::DqArgs d{};
+            d.worker_ptr = dq_plan->worker_ptr;
+            d.tiles = dq_plan->tiles;
+            d.sp_ptr = dq_plan->sparse_ptr;
+            d.sp_idx = dq_plan->sparse_idx;
+            d.q_off = bcast ? nullptr : d_q_offsets;
+            d.kv_off = d_kv_offsets;
+            d.q = a.q;
+            d.k = a.k;
+            d.v = a.v;
+            d.d_o = a.d_o;
+            d.o = a.o;
+            d.lse = lse;
+            d.delta = delta;
+            d.dq = static_cast<uint16_t*>(dq);
+            d.dq_accum = dq_accum;
+            d.partial = static_cast<float*>(workspace);
+            d.chunk_div = bcast ? (prob->lq + jfa::kFwdBlockM - 1) / jfa::kFwdBlockM : 0;
+            d.win_left = bd.left;
+            d.win_right = bd.right;
+            d.num_heads = prob->num_heads;
+            d.lq = prob->lq;
+            d.total_q = qi->total_q;
+            d.mask_q_blocks = prob->mask_q_blocks;
+            d.num_workers = qi->num_workers;
+            d.scale = prob->softmax_scale;
+            d.scale_log2 = a.scale_log2;
+            set_debug_fields(d, prob->batch);
+            st = hip_status(jfa::launch_dq(d, prob->head_dim, mode, bcast, atomic, stream));
+            if (st) return st;
+        }
+        if (stages & JFA_BWD_DKDV) {
+            st = hip_status(jfa::launch_bwd(a, prob->head_dim, mode, bcast, JFA_BWD_DKDV, stream));
+            if (st) return st;
+        }
+        if ((stages & JFA_BWD_DQ_REDUCE) && atomic) {
+            st = hip_status(jfa::launch_dq_convert(dq_accum, static_cast<uint16_t*>(dq), q_rows * hd, stream));
+            if (st) return st;
+        } else if ((stages & JFA_BWD_DQ_REDUCE) && bcast) {
+            jfa::DqReduceArgs r;
+            r.worker_ptr = dq_plan->worker_ptr;
+            r.partial = static_cast<const float*>(workspace);
+            r.dq_accum = dq_accum;
+            r.dq = static_cast<uint16_t*>(dq);
+            r.num_heads = prob->num_heads;
+            r.lq = prob->lq;
+            r.num_workers = qi->num_workers;
+            if (qi->num_tiles > 0 && r.worker_ptr == nullptr) return JFA_ERR_INVALID_ARG;
+            if (qi->num_tiles == 0) r.worker_ptr = nullptr;
+            st = hip_status(jfa::launch_dq_reduce(r, prob->head_dim, stream));
+            if (st) return st;
+        }
+        return JFA_OK;
+    });
+}
+
+int32_t jfa_bwd_dq_mx(const jfa_problem* prob, const jfa_device_plan* dq_plan,
+                      const int32_t* d_q_offsets, const int32_t* d_kv_offsets,
+                      const int32_t* d_key_block_offsets, int32_t num_key_blocks, const void* o,
+                      const float* lse, const void* d_o, const jfa_mx_bwd_operands* ops, void* dq,
+                      float* dq_accum, float* delta, void* workspace, int64_t workspace_bytes,
+                      void* stream) {
+    return jfa::logged("jfa_bwd_dq_mx", prob, dq_plan != nullptr ? dq_plan->info : nullptr, 0, [&]() -> int32_t {
+        int32_t st = check_plan(prob, dq_plan, JFA_PASS_DQ, d_q_offsets, d_kv_offsets);
+        if (st) return st;
+        if (prob->head_dim != 128) return JFA_ERR_UNSUPPORTED;
+        const jfa_plan_info* qi = dq_plan->info;
+        int64_t need = 0;
+        st = jfa_bwd_workspace_bytes(prob, qi, &need);
+        if (st) return st;
+        if (workspace_bytes < need || (need > 0 && (workspace == nullptr || !aligned16(workspace))))
+            return JFA_ERR_WORKSPACE;
+        const bool bcast = prob->broadcast_q != 0;
+        const int64_t hd = (int64_t)prob->num_heads * prob->head_dim;
+        const int64_t q_rows = bcast ? prob->lq : qi->total_q;
+        if (ops == nullptr || d_key_block_offsets == nullptr || num_key_blocks < (qi->total_kv + 31) / 32)
+            return JFA_ERR_INVALID_ARG;
+        if (!tensor_ok(o, qi->total_q * hd) || !tensor_ok(d_o, qi->total_q * hd) || lse == nullptr ||
+            delta == nullptr || !tensor_ok(ops->q_codes, q_rows * hd) ||
+            !tensor_ok(ops->k_codes, qi->total_kv * hd) || !tensor_ok(ops->v_codes, qi->total_kv * hd) ||
+            !tensor_ok(ops->do_codes, qi->total_q * hd) || !tensor_ok(ops->kk_codes, qi->total_kv * hd))
+            return JFA_ERR_INVALID_ARG;
+        const int64_t H = prob->num_heads, nbd = prob->head_dim / 32;
+        if (!scales_ok(ops->q_scales, H * q_rows * nbd) || !scales_ok(ops->k_scales, H * qi->total_kv * nbd) ||
+            !scales_ok(ops->v_scales, H * qi->total_kv * nbd) ||
+            !scales_ok(ops->do_scales, H * qi->total_q * nbd) ||
+            !scales_ok(ops->kk_scales, H * (int64_t)num_key_blocks * prob->head_dim))
+            return JFA_ERR_INVALID_ARG;
+        if (!bcast && (!tensor_ok(dq, qi->total_q * hd) || dq_accum == nullptr)) return JFA_ERR_INVALID_ARG;
+        if (qi->num_tiles == 0) return JFA_OK;
+        const jfa::Band bd = jfa::band_of(prob);
         jfa::DqArgs d{};
         d.worker_ptr = dq_plan->worker_ptr;
         d.tiles = dq_plan->tiles;
@@ -384,11 +516,8 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device
         d.sp_idx = dq_plan->sparse_idx;
         d.q_off = bcast ? nullptr : d_q_offsets;
         d.kv_off = d_kv_offsets;
-        d.q = a.q;
-        d.k = a.k;
-        d.v = a.v;
-        d.d_o = a.d_o;
-        d.o = a.o;
+        d.d_o = static_cast<const uint16_t*>(d_o);
+        d.o = static_cast<const uint16_t*>(o);
         d.lse = lse;
         d.delta = delta;
         d.dq = static_cast<uint16_t*>(dq);
@@ -403,109 +532,24 @@ int32_t jfa_bwd_stages(int32_t stages, const jfa_problem* prob, const jfa_device
         d.mask_q_blocks = prob->mask_q_blocks;
         d.num_workers = qi->num_workers;
         d.scale = prob->softmax_scale;
-        d.scale_log2 = a.scale_log2;
+        d.scale_log2 = prob->softmax_scale * 1.4426950408889634f;
+        d.q8 = static_cast<const uint8_t*>(ops->q_codes);
+        d.q_sc = static_cast<const uint8_t*>(ops->q_scales);
+        d.k8 = static_cast<const uint8_t*>(ops->k_codes);
+        d.k_sc = static_cast<const uint8_t*>(ops->k_scales);
+        d.v8 = static_cast<const uint8_t*>(ops->v_codes);
+        d.v_sc = static_cast<const uint8_t*>(ops->v_scales);
+        d.do8 = static_cast<const uint8_t*>(ops->do_codes);
+        d.do_sc = static_cast<const uint8_t*>(ops->do_scales);
+        d.kk8 = static_cast<const uint8_t*>(ops->kk_codes);
+        d.kk_sc = static_cast<const uint8_t*>(ops->kk_scales);
+        d.kk_boff = d_key_block_offsets;
+        d.kk_nb = num_key_blocks;
+        d.q_rows = (int32_t)q_rows;
+        d.total_kv = qi->total_kv;
         set_debug_fields(d, prob->batch);
-        st = hip_status(jfa::launch_dq(d, prob->head_dim, mode, bcast, atomic, stream));
-        if (st) return st;
-    }
-    if (stages & JFA_BWD_DKDV) {
-        st = hip_status(jfa::launch_bwd(a, prob->head_dim, mode, bcast, JFA_BWD_DKDV, stream));
-        if (st) return st;
-    }
-    if ((stages & JFA_BWD_DQ_REDUCE) && atomic) {
-        st = hip_status(jfa::launch_dq_convert(dq_accum, static_cast<uint16_t*>(dq), q_rows * hd, stream));
-        if (st) return st;
-    } else if ((stages & JFA_BWD_DQ_REDUCE) && bcast) {
-        jfa::DqReduceArgs r;
-        r.worker_ptr = dq_plan->worker_ptr;
-        r.partial = static_cast<const float*>(workspace);
-        r.dq_accum = dq_accum;
-        r.dq = static_cast<uint16_t*>(dq);
-        r.num_heads = prob->num_heads;
-        r.lq = prob->lq;
-        r.num_workers = qi->num_workers;
-        if (qi->num_tiles > 0 && r.worker_ptr == nullptr) return JFA_ERR_INVALID_ARG;
-        if (qi->num_tiles == 0) r.worker_ptr = nullptr;
-        st = hip_status(jfa::launch_dq_reduce(r, prob->head_dim, stream));
-        if (st) return st;
-    }
-    return JFA_OK;
-}
-
-int32_t jfa_bwd_dq_mx(const jfa_problem* prob, const jfa_device_plan* dq_plan,
-                      const int32_t* d_q_offsets, const int32_t* d_kv_offsets,
-                      const int32_t* d_key_block_offsets, int32_t num_key_blocks, const void* o,
-                      const float* lse, const void* d_o, const jfa_mx_bwd_operands* ops, void* dq,
-                      float* dq_accum, float* delta, void* workspace, int64_t workspace_bytes,
-                      void* stream) {
-    int32_t st = check_plan(prob, dq_plan, JFA_PASS_DQ, d_q_offsets, d_kv_offsets);
-    if (st) return st;
-    if (prob->head_dim != 128) return JFA_ERR_UNSUPPORTED;
-    const jfa_plan_info* qi = dq_plan->info;
-    int64_t need = 0;
-    st = jfa_bwd_workspace_bytes(prob, qi, &need);
-    if (st) return st;
-    if (workspace_bytes < need || (need > 0 && (workspace == nullptr || !aligned16(workspace))))
-        return JFA_ERR_WORKSPACE;
-    const bool bcast = prob->broadcast_q != 0;
-    const int64_t hd = (int64_t)prob->num_heads * prob->head_dim;
-    const int64_t q_rows = bcast ? prob->lq : qi->total_q;
-    if (ops == nullptr || d_key_block_offsets == nullptr || num_key_blocks < (qi->total_kv + 31) / 32)
-        return JFA_ERR_INVALID_ARG;
-    if (!tensor_ok(o, qi->total_q * hd) || !tensor_ok(d_o, qi->total_q * hd) || lse == nullptr ||
-        delta == nullptr || !tensor_ok(ops->q_codes, q_rows * hd) ||
-        !tensor_ok(ops->k_codes, qi->total_kv * hd) || !tensor_ok(ops->v_codes, qi->total_kv * hd) ||
-        !tensor_ok(ops->do_codes, qi->total_q * hd) || !tensor_ok(ops->kk_codes, qi->total_kv * hd))
-        return JFA_ERR_INVALID_ARG;
-    const int64_t H = prob->num_heads, nbd = prob->head_dim / 32;
-    if (!scales_ok(ops->q_scales, H * q_rows * nbd) || !scales_ok(ops->k_scales, H * qi->total_kv * nbd) ||
-        !scales_ok(ops->v_scales, H * qi->total_kv * nbd) ||
-        !scales_ok(ops->do_scales, H * qi->total_q * nbd) ||
-        !scales_ok(ops->kk_scales, H * (int64_t)num_key_blocks * prob->head_dim))
-        return JFA_ERR_INVALID_ARG;
-    if (!bcast && (!tensor_ok(dq, qi->total_q * hd) || dq_accum == nullptr)) return JFA_ERR_INVALID_ARG;
-    if (qi->num_tiles == 0) return JFA_OK;
-    const jfa::Band bd = jfa::band_of(prob);
-    jfa::DqArgs d{};
-    d.worker_ptr = dq_plan->worker_ptr;
-    d.tiles = dq_plan->tiles;
-    d.sp_ptr = dq_plan->sparse_ptr;
-    d.sp_idx = dq_plan->sparse_idx;
-    d.q_off = bcast ? nullptr : d_q_offsets;
-    d.kv_off = d_kv_offsets;
-    d.d_o = static_cast<const uint16_t*>(d_o);
-    d.o = static_cast<const uint16_t*>(o);
-    d.lse = lse;
-    d.delta = delta;
-    d.dq = static_cast<uint16_t*>(dq);
-    d.dq_accum = dq_accum;
-    d.partial = static_cast<float*>(workspace);
-    d.chunk_div = bcast ? (prob->lq + jfa::kFwdBlockM - 1) / jfa::kFwdBlockM : 0;
-    d.win_left = bd.left;
-    d.win_right = bd.right;
-    d.num_heads = prob->num_heads;
-    d.lq = prob->lq;
-    d.total_q = qi->total_q;
-    d.mask_q_blocks = prob->mask_q_blocks;
-    d.num_workers = qi->num_workers;
-    d.scale = prob->softmax_scale;
-    d.scale_log2 = prob->softmax_scale * 1.4426950408889634f;
-    d.q8 = static_cast<const uint8_t*>(ops->q_codes);
-    d.q_sc = static_cast<const uint8_t*>(ops->q_scales);
-    d.k8 = static_cast<const uint8_t*>(ops->k_codes);
-    d.k_sc = static_cast<const uint8_t*>(ops->k_scales);
-    d.v8 = static_cast<const uint8_t*>(ops->v_codes);
-    d.v_sc = static_cast<const uint8_t*>(ops->v_scales);
-    d.do8 = static_cast<const uint8_t*>(ops->do_codes);
-    d.do_sc = static_cast<const uint8_t*>(ops->do_scales);
-    d.kk8 = static_cast<const uint8_t*>(ops->kk_codes);
-    d.kk_sc = static_cast<const uint8_t*>(ops->kk_scales);
-    d.kk_boff = d_key_block_offsets;
-    d.kk_nb = num_key_blocks;
-    d.q_rows = (int32_t)q_rows;
-    d.total_kv = qi->total_kv;
-    set_debug_fields(d, prob->batch);
-    return hip_status(jfa::launch_dq_mx(d, mode_of(prob), bcast, stream));
+        return hip_status(jfa::launch_dq_mx(d, mode_of(prob), bcast, stream));
+    });
 }
 
 int32_t jfa_bwd_dkdv_mx(const jfa_problem* prob, const jfa_device_plan* kv_plan,
@@ -514,76 +558,78 @@ int32_t jfa_bwd_dkdv_mx(const jfa_problem* prob, const jfa_device_plan* kv_plan,
                         const int32_t* d_do_row_block_offsets, int32_t num_do_row_blocks,
                         const float* lse, const float* delta, const jfa_mx_dkdv_operands* ops,
                         void* dk, void* dv, void* stream) {
-    int32_t st = check_plan(prob, kv_plan, JFA_PASS_BWD, d_q_offsets, d_kv_offsets);
-    if (st) return st;
-    if (prob->head_dim != 128) return JFA_ERR_UNSUPPORTED;
-    const jfa_plan_info* ki = kv_plan->info;
-    const bool bcast = prob->broadcast_q != 0;
-    const int64_t hd = (int64_t)prob->num_heads * prob->head_dim;
-    const int64_t q_rows = bcast ? prob->lq : ki->total_q;
-    const int64_t tq = ki->total_q, tk = ki->total_kv;
-    if (ops == nullptr || num_q_row_blocks < 0 || num_do_row_blocks < 0) return JFA_ERR_INVALID_ARG;
-    // one 32-row block per 32 rows of each sequence: at least rows / 32
-    if (num_q_row_blocks < (q_rows + 31) / 32 || num_do_row_blocks < (tq + 31) / 32)
-        return JFA_ERR_INVALID_ARG;
-    if (ki->num_tiles > 0 && (d_do_row_block_offsets == nullptr ||
-                              (!bcast && d_q_row_block_offsets == nullptr)))
-        return JFA_ERR_INVALID_ARG;
-    if (!tensor_ok(dk, tk * hd) || !tensor_ok(dv, tk * hd) || !tensor_ok(ops->q_codes, q_rows * hd) ||
-        !tensor_ok(ops->k_codes, tk * hd) || !tensor_ok(ops->v_codes, tk * hd) ||
-        !tensor_ok(ops->do_codes, tq * hd) || !tensor_ok(ops->qr_codes, q_rows * hd) ||
-        !tensor_ok(ops->dor_codes, tq * hd))
-        return JFA_ERR_INVALID_ARG;
-    const int64_t H = prob->num_heads, nbd = prob->head_dim / 32;
-    if (!scales_ok(ops->q_scales, H * q_rows * nbd) || !scales_ok(ops->k_scales, H * tk * nbd) ||
-        !scales_ok(ops->v_scales, H * tk * nbd) || !scales_ok(ops->do_scales, H * tq * nbd) ||
-        !scales_ok(ops->qr_scales, H * (int64_t)num_q_row_blocks * prob->head_dim) ||
-        !scales_ok(ops->dor_scales, H * (int64_t)num_do_row_blocks * prob->head_dim))
-        return JFA_ERR_INVALID_ARG;
-    if (tq > 0 && (lse == nullptr || delta == nullptr || !aligned4(lse) || !aligned4(delta)))
-        return JFA_ERR_INVALID_ARG;
-    if (ki->num_tiles == 0) return JFA_OK;
-    const jfa::Band bd = jfa::band_of(prob);
-    jfa::BwdArgs a{};
-    set_debug_fields(a, prob->batch);
-    a.worker_ptr = kv_plan->worker_ptr;
-    a.tiles = kv_plan->tiles;
-    a.sp_ptr = kv_plan->sparse_ptr;
-    a.sp_idx = kv_plan->sparse_idx;
-    a.q_off = bcast ? nullptr : d_q_offsets;
-    a.kv_off = d_kv_offsets;
-    a.lse = lse;
-    a.delta = const_cast<float*>(delta);
-    a.dk = static_cast<uint16_t*>(dk);
-    a.dv = static_cast<uint16_t*>(dv);
-    a.num_heads = prob->num_heads;
-    a.lq = prob->lq;
-    a.total_q = ki->total_q;
-    a.mask_kv_blocks = prob->mask_kv_blocks;
-    a.num_workers = ki->num_workers;
-    a.win_left = bd.left;
-    a.win_right = bd.right;
-    a.scale = prob->softmax_scale;
-    a.scale_log2 = prob->softmax_scale * 1.4426950408889634f;
-    a.q8 = static_cast<const uint8_t*>(ops->q_codes);
-    a.q_sc = static_cast<const uint8_t*>(ops->q_scales);
-    a.k8 = static_cast<const uint8_t*>(ops->k_codes);
-    a.k_sc = static_cast<const uint8_t*>(ops->k_scales);
-    a.v8 = static_cast<const uint8_t*>(ops->v_codes);
-    a.v_sc = static_cast<const uint8_t*>(ops->v_scales);
-    a.do8 = static_cast<const uint8_t*>(ops->do_codes);
-    a.do_sc = static_cast<const uint8_t*>(ops->do_scales);
-    a.qr8 = static_cast<const uint8_t*>(ops->qr_codes);
-    a.qr_sc = static_cast<const uint8_t*>(ops->qr_scales);
-    a.dor8 = static_cast<const uint8_t*>(ops->dor_codes);
-    a.dor_sc = static_cast<const uint8_t*>(ops->dor_scales);
-    a.qr_boff = d_q_row_block_offsets;
-    a.dor_boff = d_do_row_block_offsets;
-    a.qr_nb = num_q_row_blocks;
-    a.dor_nb = num_do_row_blocks;
-    a.q_rows = (int32_t)q_rows;
-    a.total_kv = ki->total_kv;
-    return hip_status(jfa::launch_dkdv_mx(a, mode_of(prob), bcast, stream));
+    return jfa::logged("jfa_bwd_dkdv_mx", prob, kv_plan != nullptr ? kv_plan->info : nullptr, 0, [&]() -> int32_t {
+        int32_t st = check_plan(prob, kv_plan, JFA_PASS_BWD, d_q_offsets, d_kv_offsets);
+        if (st) return st;
+        if (prob->head_dim != 128) return JFA_ERR_UNSUPPORTED;
+        const jfa_plan_info* ki = kv_plan->info;
+        const bool bcast = prob->broadcast_q != 0;
+        const int64_t hd = (int64_t)prob->num_heads * prob->head_dim;
+        const int64_t q_rows = bcast ? prob->lq : ki->total_q;
+        const int64_t tq = ki->total_q, tk = ki->total_kv;
+        if (ops == nullptr || num_q_row_blocks < 0 || num_do_row_blocks < 0) return JFA_ERR_INVALID_ARG;
+        // one 32-row block per 32 rows of each sequence: at least rows / 32
+        if (num_q_row_blocks < (q_rows + 31) / 32 || num_do_row_blocks < (tq + 31) / 32)
+            return JFA_ERR_INVALID_ARG;
+        if (ki->num_tiles > 0 && (d_do_row_block_offsets == nullptr ||
+                                  (!bcast && d_q_row_block_offsets == nullptr)))
+            return JFA_ERR_INVALID_ARG;
+        if (!tensor_ok(dk, tk * hd) || !tensor_ok(dv, tk * hd) || !tensor_ok(ops->q_codes, q_rows * hd) ||
+            !tensor_ok(ops->k_codes, tk * hd) || !tensor_ok(ops->v_codes, tk * hd) ||
+            !tensor_ok(ops->do_codes, tq * hd) || !tensor_ok(ops->qr_codes, q_rows * hd) ||
+            !tensor_ok(ops->dor_codes, tq * hd))
+            return JFA_ERR_INVALID_ARG;
+        const int64_t H = prob->num_heads, nbd = prob->head_dim / 32;
+        if (!scales_ok(ops->q_scales, H * q_rows * nbd) || !scales_ok(ops->k_scales, H * tk * nbd) ||
+            !scales_ok(ops->v_scales, H * tk * nbd) || !scales_ok(ops->do_scales, H * tq * nbd) ||
+            !scales_ok(ops->qr_scales, H * (int64_t)num_q_row_blocks * prob->head_dim) ||
+            !scales_ok(ops->dor_scales, H * (int64_t)num_do_row_blocks * prob->head_dim))
+            return JFA_ERR_INVALID_ARG;
+        if (tq > 0 && (lse == nullptr || delta == nullptr || !aligned4(lse) || !aligned4(delta)))
+            return JFA_ERR_INVALID_ARG;
+        if (ki->num_tiles == 0) return JFA_OK;
+        const jfa::Band bd = jfa::band_of(prob);
+        jfa::BwdArgs a{};
+        set_debug_fields(a, prob->batch);
+        a.worker_ptr = kv_plan->worker_ptr;
+        a.tiles = kv_plan->tiles;
+        a.sp_ptr = kv_plan->sparse_ptr;
+        a.sp_idx = kv_plan->sparse_idx;
+        a.q_off = bcast ? nullptr : d_q_offsets;
+        a.kv_off = d_kv_offsets;
+        a.lse = lse;
+        a.delta = const_cast<float*>(delta);
+        a.dk = static_cast<uint16_t*>(dk);
+        a.dv = static_cast<uint16_t*>(dv);
+        a.num_heads = prob->num_heads;
+        a.lq = prob->lq;
+        a.total_q = ki->total_q;
+        a.mask_kv_blocks = prob->mask_kv_blocks;
+        a.num_workers = ki->num_workers;
+        a.win_left = bd.left;
+        a.win_right = bd.right;
+        a.scale = prob->softmax_scale;
+        a.scale_log2 = prob->softmax_scale * 1.4426950408889634f;
+        a.q8 = static_cast<const uint8_t*>(ops->q_codes);
+        a.q_sc = static_cast<const uint8_t*>(ops->q_scales);
+        a.k8 = static_cast<const uint8_t*>(ops->k_codes);
+        a.k_sc = static_cast<const uint8_t*>(ops->k_scales);
+        a.v8 = static_cast<const uint8_t*>(ops->v_codes);
+        a.v_sc = static_cast<const uint8_t*>(ops->v_scales);
+        a.do8 = static_cast<const uint8_t*>(ops->do_codes);
+        a.do_sc = static_cast<const uint8_t*>(ops->do_scales);
+        a.qr8 = static_cast<const uint8_t*>(ops->qr_codes);
+        a.qr_sc = static_cast<const uint8_t*>(ops->qr_scales);
+        a.dor8 = static_cast<const uint8_t*>(ops->dor_codes);
+        a.dor_sc = static_cast<const uint8_t*>(ops->dor_scales);
+        a.qr_boff = d_q_row_block_offsets;
+        a.dor_boff = d_do_row_block_offsets;
+        a.qr_nb = num_q_row_blocks;
+        a.dor_nb = num_do_row_blocks;
+        a.q_rows = (int32_t)q_rows;
+        a.total_kv = ki->total_kv;
+        return hip_status(jfa::launch_dkdv_mx(a, mode_of(prob), bcast, stream));
+    });
 }
 
 int32_t jfa_bwd_noalloc(const jfa_problem* prob, const jfa_device_plan* kv_plan,

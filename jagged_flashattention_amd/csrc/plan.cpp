@@ -20,6 +20,7 @@
 // "Optimizations layered on top").
 // A natural plan (the ablation baseline for the sort and the deal) skips the
 // sort and deals the tiles in enumeration order round-robin.
+#include "hostlog.h"
 #include "internal.h"
 
 #include <algorithm>
@@ -422,16 +423,20 @@ int32_t jfa_offsets_from_lengths(const int32_t* h_lengths, int32_t batch, int32_
 int32_t jfa_plan_query(const jfa_problem* prob, const int32_t* h_q_offsets,
                        const int32_t* h_kv_offsets, const uint8_t* h_block_mask, int32_t pass,
                        int32_t num_workers, jfa_plan_info* info) {
-    return jfa::plan_impl(prob, h_q_offsets, h_kv_offsets, h_block_mask, pass, num_workers, info,
-                          nullptr, nullptr, nullptr, nullptr, false);
+    return jfa::logged("jfa_plan_query", prob, info, pass, [&]() -> int32_t {
+        return jfa::plan_impl(prob, h_q_offsets, h_kv_offsets, h_block_mask, pass, num_workers, info,
+                              nullptr, nullptr, nullptr, nullptr, false);
+    });
 }
 
 int32_t jfa_plan_build(const jfa_problem* prob, const int32_t* h_q_offsets,
                        const int32_t* h_kv_offsets, const uint8_t* h_block_mask, int32_t pass,
                        int32_t num_workers, jfa_plan_info* info, int32_t* h_worker_ptr,
                        int32_t* h_tiles, int32_t* h_sparse_ptr, int32_t* h_sparse_idx) {
-    return jfa::plan_impl(prob, h_q_offsets, h_kv_offsets, h_block_mask, pass, num_workers, info,
-                          h_worker_ptr, h_tiles, h_sparse_ptr, h_sparse_idx, true);
+    return jfa::logged("jfa_plan_build", prob, info, pass, [&]() -> int32_t {
+        return jfa::plan_impl(prob, h_q_offsets, h_kv_offsets, h_block_mask, pass, num_workers, info,
+                              h_worker_ptr, h_tiles, h_sparse_ptr, h_sparse_idx, true);
+    });
 }
 
 }  // extern "C"

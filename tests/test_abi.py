@@ -346,3 +346,28 @@ def test_tile_log_is_debug_only():
     assert dbg.jfa_debug_tile_log(ctypes.c_void_p(0x1008), 4) == J.JFA_ERR_INVALID_ARG
     assert dbg.jfa_debug_tile_log(ctypes.c_void_p(0x1000), -1) == J.JFA_ERR_INVALID_ARG
     assert dbg.jfa_debug_tile_log(None, 0) == J.JFA_OK
+
+
+def test_jfa_log_writes_one_line_per_call():
+    """JFA_LOG=1: each planner / entry point call writes one line to stderr
+    with its name, the problem and its status; unset: nothing."""
+    import subprocess
+    import sys
+    code = ("import jagged_flashattention_amd as J\n"
+            "p = J.Problem(batch=2, num_heads=1, head_dim=64, broadcast_q=True, lq=8, softmax_scale=0.125)\n"
+            "J.jfa_plan_build(p, None, [0, 3, 5], None, J.JFA_PASS_BWD, 4)\n"
+            "try:\n"
+            "    J.jfa_plan_build(p, None, [0, 3, 2], None, J.JFA_PASS_FWD, 4)\n"
+            "except J.JfaError:\n"
+            "    pass\n")
+    env = dict(os.environ, JFA_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    lines = [l for l in r.stderr.splitlines() if l.startswith("jfa: ")]
+    assert len(lines) == 3, r.stderr                       # query + build, then the failing query
+    assert "jfa_plan_query" in lines[0] and "jfa_plan_build" in lines[1]
+    assert "B=2 H=1 D=64" in lines[1] and "pass=1" in lines[1] and "-> ok (0)" in lines[1]
+    assert "-> bad offsets" in lines[2] and "(-2)" in lines[2] and "workers=" not in lines[2]
+    env["JFA_LOG"] = "0"
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True)
+    assert r.returncode == 0 and "jfa: " not in r.stderr
