@@ -24,9 +24,14 @@
 //     so a lane owns one query row and row max / row sum stay in-lane), fp32
 //     online softmax in the exp2 domain (rescale skipped while no row max
 //     moves), O^T += V^T P^T with P^T straight from the accumulators;
-//   - a bulk path without mask arithmetic and a masked tail (partial last
-//     block, causal diagonal); blocks a wave's rows cannot see (causal, or
-//     dropped by its block-sparse mask row) are skipped by that wave;
+//   - the peel is per block, not per loop: scalar flags computed for each
+//     block send it down the bulk path (no mask arithmetic) or the masked
+//     tail path (partial last block, causal diagonal) with a wave-uniform
+//     branch, and blocks a wave's rows cannot see (causal, or dropped by its
+//     block-sparse mask row) are skipped by that wave. The block body is
+//     compiled once: two copies of it (a bulk loop and a tail loop) would
+//     double the kernel's largest code region for the few scalar
+//     instructions the flags cost;
 //   - O leaves through a per-wave LDS staging area (in the K slot and V^T
 //     buffer the tile's last block has released) as whole 16-byte-per-lane
 //     rows, so each store instruction writes 4 full rows.
