@@ -22,8 +22,10 @@
 //     accumulator registers hold them, once per block for all 8 waves;
 //   - per wave: S^T = K Q^T (32x32x16 bf16 MFMA, Q in VGPRs as the B operand,
 //     so a lane owns one query row and row max / row sum stay in-lane), fp32
-//     online softmax in the exp2 domain (rescale skipped while no row max
-//     moves), O^T += V^T P^T with P^T straight from the accumulators;
+//     online softmax in the exp2 domain (bf16: the running max moves, and
+//     O^T is rescaled, only when a row's max rises by more than 2^8; MXFP8:
+//     whenever it rises), O^T += V^T P^T with P^T straight from the
+//     accumulators;
 //   - the peel is per block, not per loop: scalar flags computed for each
 //     block send it down the bulk path (no mask arithmetic) or the masked
 //     tail path (partial last block, causal diagonal) with a wave-uniform
@@ -43,6 +45,12 @@
 
 namespace jfa {
 namespace {
+
+// bf16 forward: the online softmax's running max is moved only when a block
+// raises some row's max by more than this (exp2 domain), so P <= 2^8: exact
+// after the final O / l, safe in bf16 and fp32, and the O^T rescale runs
+// about once per tile instead of on most blocks.
+constexpr float kMaxSlack = 8.0f;
 
 using namespace qtile;
 using namespace mxops;
@@ -465,15 +473,17 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
                     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[mb][r]);
                 // running max in the exp2 domain of the scaled scores
                 mx = pair_max(mx) * a.scale_log2;
-                const float m_new = fmaxf(m_run, mx);
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-                m_run = m_new;
-                if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-                    for (int md = 0; md < MD; ++md) oacc[md] *= alpha;
-                }
                 float ls = 0.f;
                 if constexpr (MX) {
+                    // P is encoded with the fixed scale of a value <= 1: the
+                    // running max follows every rise
+                    const float m_new = fmaxf(m_run, mx);
+                    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                    m_run = m_new;
+                    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+                        for (int md = 0; md < MD; ++md) oacc[md] *= alpha;
+                    }
                     // P (fp32, at most 1; its row sum stays fp32) to E4M3
 #pragma unroll
                     for (int mb = 0; mb < 2; ++mb)
@@ -488,9 +498,21 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
                     mx_pv(oacc, pb8, smem + LY::VT + (s & 1) * LY::BLK,
                           smem + LY::VS + (s % kKSlots) * LY::SC, kP8Scale, lr, hf);
                 } else {
+                    // The running max moves (and O^T and l are rescaled) only
+                    // when some row's block max rises more than kMaxSlack above
+                    // it; otherwise P = exp2(s - m_run) <= 2^kMaxSlack is kept
+                    // against the stale max, which O / l cancels exactly
+                    if (__builtin_amdgcn_ballot_w64(mx > m_run + kMaxSlack) != 0) {
+                        const float m_new = fmaxf(m_run, mx);
+                        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                        m_run = m_new;
+#pragma unroll
+                        for (int md = 0; md < MD; ++md) oacc[md] *= alpha;
+                        l_run *= alpha;
+                    }
                     bf16x8 pb[4];
-                    exp_pack(sc, m_new, ls, pb);
-                    l_run = l_run * alpha + ls;
+                    exp_pack(sc, m_run, ls, pb);
+                    l_run += ls;
                     pv(pb, s);
                 }
             }
