@@ -192,7 +192,7 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
             float* rv = (float*)(smem + LY::RING + (s % kSlots) * LY::SLOT + LY::ROWV);
             float x;
             if (hf == 0) x = (!pend_in || pend_v == -INFINITY) ? INFINITY : pend_v * kLog2e;
-            else x = pend_in ? pend_v : 0.f;
+            else x = pend_in ? -pend_v : 0.f;   // -delta: the dP accumulators start there
             rv[lane] = x;
         }
     };
@@ -314,7 +314,14 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
             const char* qt = smem + LY::T + (s & 1) * LY::TBUF;
             const char* dt = qt + LY::QB;
 
-            f32x16 sc = f32x16{}, dp = f32x16{};
+            // dP accumulates onto -delta (row values), so it ends as dP - delta
+            f32x16 sc = f32x16{}, dp;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 d4 = *(const f32x4*)(rv + 32 + 8 * g + 4 * hf);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dp[4 * g + j] = d4[j];
+            }
             {
                 bf16x8 qa[KC], da[KC], vf[KC];
 #pragma unroll
@@ -352,7 +359,6 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
             for (int g = 0; g < 4; ++g) {
                 const int row = 8 * g + 4 * hf;
                 const f32x4 l4 = *(const f32x4*)(rv + row);
-                const f32x4 d4 = *(const f32x4*)(rv + 32 + row);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     float p = __builtin_amdgcn_exp2f(fmaf(sc[4 * g + j], a.scale_log2, -l4[j]));
@@ -361,7 +367,7 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
                         if (c < c_lo || c > c_hi) p = 0.f;
                     }
                     sc[4 * g + j] = p;
-                    dp[4 * g + j] = p * (dp[4 * g + j] - d4[j]);
+                    dp[4 * g + j] = p * dp[4 * g + j];
                 }
             }
             bf16x8 pb[2], sb[2];
