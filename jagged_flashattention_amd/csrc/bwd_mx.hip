@@ -381,9 +381,9 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_mx_kernel(BwdArgs a) {
                 const u32x4 dt = *(const u32x4*)(trow + 16 * ((2 + hf) ^ swz_vt8(d)));
                 const int qrs = hf ? 127 : *(const uint8_t*)(sl + LY::QRS + d);
                 const int drs = hf ? 127 : *(const uint8_t*)(sl + LY::DRS + d);
-                dv_acc[md] = mfma_mx(i32x8{(int)dt[0], (int)dt[2], (int)dt[1], (int)dt[3], 0, 0, 0, 0}, pb8,
+                dv_acc[md] = mfma_mx(i32x8{(int)dt[0], (int)dt[1], (int)dt[2], (int)dt[3], 0, 0, 0, 0}, pb8,
                                      drs, pcode, dv_acc[md]);
-                dk_acc[md] = mfma_mx(i32x8{(int)qt[0], (int)qt[2], (int)qt[1], (int)qt[3], 0, 0, 0, 0}, sb8,
+                dk_acc[md] = mfma_mx(i32x8{(int)qt[0], (int)qt[1], (int)qt[2], (int)qt[3], 0, 0, 0, 0}, sb8,
                                      qrs, scode, dk_acc[md]);
             }
             // reads one d block ahead of the products

@@ -98,8 +98,8 @@ __device__ __forceinline__ void mx_pv(f32x16 (&oacc)[4], const i32x8& pb, const 
         const char* row = vtb + d * 64;
         const u32x4 lo = *(const u32x4*)(row + 16 * (hf ^ swz_vt8(d)));
         const u32x4 hi = *(const u32x4*)(row + 16 * ((2 + hf) ^ swz_vt8(d)));
-        const i32x8 av = {(int)lo[0], (int)lo[2], (int)lo[1], (int)lo[3],
-                          (int)hi[0], (int)hi[2], (int)hi[1], (int)hi[3]};
+        const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         const int vs = *(const uint8_t*)(vsb + hf * 128 + d);
         oacc[md] = mfma_mx(av, pb, vs, bsc, oacc[md]);
     }
@@ -107,6 +107,9 @@ __device__ __forceinline__ void mx_pv(f32x16 (&oacc)[4], const i32x8& pb, const 
 
 // V [64 keys][128 d] (E4M3) -> V^T [128 d][64 keys]: thread t transposes the
 // 4 x 4 byte tile of keys 4(t/32) .. +3 and d 4(t%32) .. +3 in registers.
+// Within each 16-key chunk of a V^T row the four 4-key dwords are stored in
+// the order keys 0-3, 8-11, 4-7, 12-15 (relative to the chunk): the dword
+// order of the packed P^T operand, so a chunk read is an A operand as is.
 __device__ __forceinline__ void mx_transpose_v(const char* v, char* vt, int tid) {
     const int b = tid & 31, aq = tid >> 5;
     uint32_t r[4];
@@ -125,7 +128,8 @@ __device__ __forceinline__ void mx_transpose_v(const char* v, char* vt, int tid)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int d = 4 * b + j;
-        *(uint32_t*)(vt + d * 64 + 16 * ((aq >> 2) ^ swz_vt8(d)) + 4 * (aq & 3)) = c[j];
+        const int g = aq & 3, pos = g == 1 ? 2 : g == 2 ? 1 : g;   // dword order 0, 2, 1, 3
+        *(uint32_t*)(vt + d * 64 + 16 * ((aq >> 2) ^ swz_vt8(d)) + 4 * pos) = c[j];
     }
 }
 
