@@ -175,26 +175,27 @@ __device__ __forceinline__ T ld_uniform(const T* p) {
 
 // Atomic increment of *p by lane 0 alone (the exec mask is narrowed inside
 // the asm, so the surrounding code stays free of lane-divergent branches),
-// returning the old value in lane 0. The value arrives asynchronously: the
-// compiler does not track it, so it must not be read before an s_waitcnt
-// that covers this atomic (vmcnt(0), or vmcnt(N) with N vector memory
-// operations issued after it); async_value_ready() marks that point.
-__device__ __forceinline__ int atomic_inc_lane0_async(int* p) {
+// returning the old value in lane 0. The asm waits for the value (vmcnt(0):
+// this also waits for the wave's earlier vector memory operations). It has
+// to: the compiler takes an asm output as ready when the asm ends, and may
+// copy or spill the register right there, before any later wait, which
+// would read it before the atomic has written it. (A compiler-visible
+// atomic is tracked correctly but, restricted to one lane, turns the
+// loader's wave-uniform state into per-lane state in the generated code.)
+__device__ __forceinline__ int atomic_inc_lane0(int* p) {
     int r;
     uint64_t saved;
     asm volatile(
         "s_mov_b64 %1, exec\n\t"
         "s_mov_b64 exec, 1\n\t"
         "global_atomic_add %0, %2, %3, off sc0\n\t"
+        "s_waitcnt vmcnt(0)\n\t"
         "s_mov_b64 exec, %1"
         : "=&v"(r), "=&s"(saved)
         : "v"(p), "v"(1)
         : "memory");
     return r;
 }
-// Orders the first read of an atomic_inc_lane0_async value after the asm
-// wait that precedes this call.
-__device__ __forceinline__ void async_value_ready(int& v) { asm volatile("" : "+v"(v)::"memory"); }
 
 // Persistent worker of this workgroup. Workgroup ids are dealt round-robin to
 // the 8 XCDs; mapping consecutive workers to the same XCD puts tiles dealt

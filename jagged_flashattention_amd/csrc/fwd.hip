@@ -172,24 +172,20 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
     int q_head = 0, q_tail = 0;          // consumer queue cursors (wave-uniform)
     int l_next = dynamic && t_begin < t_end ? t_begin : -1;   // tile after the loader's
     bool l_have = dynamic;               // l_next is known
-    bool l_claiming = false;             // a claim is in flight
+    bool l_claiming = false;             // a claim is made and not yet received
     int n_claims = 0;                    // claims received (parity picks the LDS slot)
     int claim_ret = 0;                   // wave 0, lane 0: the counter's old value
     auto claim = [&]() {
-        // One atomic, by lane 0 of wave 0, whose value is first read after
-        // the next wait for the copies issued after it (see publish), so its
-        // latency hides behind the iteration's work.
-        if (wave == 0) claim_ret = atomic_inc_lane0_async(a.counter);
+        // One atomic, by lane 0 of wave 0, waited for at once (see
+        // atomic_inc_lane0): the other waves go on meanwhile.
+        if (wave == 0) claim_ret = atomic_inc_lane0(a.counter);
         l_claiming = true;
     };
     // wave 0 puts a claimed value in LDS before a barrier; every wave reads it
     // (lane 0's) after that barrier. Two slots: a slot is rewritten only after
     // the barrier that follows its read.
     auto publish = [&]() {
-        if (l_claiming && wave == 0) {
-            async_value_ready(claim_ret);
-            claim_lds[64 * (n_claims & 1) + lane] = claim_ret;
-        }
+        if (l_claiming && wave == 0) claim_lds[64 * (n_claims & 1) + lane] = claim_ret;
     };
     auto receive = [&]() {
         if (l_claiming) {
@@ -202,7 +198,6 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
     };
     auto claim_now = [&]() {   // the next tile is needed before the next barrier
         if (!l_claiming) claim();
-        if (wave == 0) wait_vmem();
         publish();
         __syncthreads();
         receive();
@@ -265,7 +260,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
         if (l_i >= LT.work) advance();
         if (l_end) return;
         // the last block of the loader's tile: claim the tile after it now,
-        // ahead of the copies (a later wait for the copies covers the claim)
+        // ahead of the copies
         if (dynamic && l_i == LT.work - 1 && !l_have && !l_claiming) claim();
         const int n = seq_block(LT, l_i);
         const int64_t base = (int64_t)LT.kv0 * rs + (int64_t)LT.h * D;
