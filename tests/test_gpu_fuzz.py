@@ -1,0 +1,70 @@
+"""Seeded random problems through the whole HIP path against the oracle: every
+output (O, LSE, dQ, dK, dV, dq_accum, delta) of every sequence and head,
+outputs NaN-filled before the run. Each seed draws one problem of a random
+kind (broadcast Q, per-sequence Q with its own lengths, causal, sliding
+window, block-sparse with a broadcast or per-sequence Q), head_dim 64 or 128,
+1-3 heads, ragged lengths (0, 1 and tile sizes +-1 among them), and random
+worker counts for the three plans and a static or dynamic forward. Sizes are
+kept so that the fp64 oracle finishes in about a second per problem."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from test_gpu_parity import _custom, check_all, run_gpu  # noqa: E402
+
+N_CASES = 160
+EDGE = [0, 1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+
+
+def _lengths(rng, n, hi):
+    pick = rng.random(n) < 0.5
+    return [int(rng.choice(EDGE)) if p else int(rng.integers(0, hi)) for p in pick]
+
+
+def _problem(seed):
+    rng = np.random.default_rng(7000 + seed)
+    kind = str(rng.choice(["bcast", "perseq", "causal", "window", "sparse", "sparse_self"]))
+    H = int(rng.integers(1, 4))
+    D = int(rng.choice([64, 128]))
+    B = int(rng.integers(1, 7))
+    kw = dict(H=H, D=D, seed=100 + seed)
+    if kind == "bcast":
+        x = _custom("fz", broadcast=True, lengths=_lengths(rng, B, 600),
+                    lq=int(rng.choice([1, 31, 100, 256, 257, 300])), **kw)
+    elif kind == "perseq":
+        x = _custom("fz", broadcast=False, lengths=_lengths(rng, B, 500),
+                    q_lengths=_lengths(rng, B, 400), **kw)
+    elif kind == "causal":
+        x = _custom("fz", broadcast=False, lengths=_lengths(rng, B, 700), causal=True, **kw)
+    elif kind == "window":
+        left = None if rng.random() < 0.2 else int(rng.integers(0, 400))
+        right = 0 if rng.random() < 0.4 else (None if rng.random() < 0.2 else int(rng.integers(0, 200)))
+        if left is None and right is None:
+            right = 0
+        x = _custom("fz", broadcast=False, lengths=_lengths(rng, B, 700),
+                    causal=right == 0, window=(left, None if right == 0 else right), **kw)
+    elif kind == "sparse":
+        x = _custom("fz", broadcast=True, lengths=_lengths(rng, B, 800),
+                    lq=int(rng.choice([1, 100, 256, 257, 400])), mask_seed=int(rng.integers(0, 1000)),
+                    **kw)
+    else:
+        x = _custom("fz", broadcast=False, lengths=_lengths(rng, B, 600),
+                    mask_seed=int(rng.integers(0, 1000)), **kw)
+    plan = dict(fwd_workers=int(rng.choice([1, 3, 17, 256, 700])),
+                bwd_workers=int(rng.choice([1, 5, 64, 256])),
+                dq_workers=int(rng.choice([1, 7, 256, 600])),
+                fwd_dynamic=bool(rng.random() < 0.7))
+    return kind, x, plan
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_problem_matches_oracle(seed):
+    kind, x, plan = _problem(seed)
+    print("fuzz seed", seed, kind, "lengths", list(x.lengths), "H", x.workload.heads,
+          "D", x.workload.head_dim, plan, flush=True)
+    check_all(x, run_gpu(x, canary=True, **plan))
