@@ -38,8 +38,11 @@
 //     buffer the tile's last block has released) as whole 16-byte-per-lane
 //     rows, so each store instruction writes 4 full rows.
 // Every LDS tile is XOR-swizzled at 16-byte granularity so that the MFMA
-// operand reads, the transposed reads and the V^T writes are free of bank
-// conflicts (64 banks x 4 bytes).
+// operand reads and the transposed reads are free of bank conflicts (reads
+// see 64 banks x 4 bytes). The 8-byte V^T writes are not: writes are served
+// 16 lanes at a time over 32 banks, and the 16 lanes of a write group hold
+// one key position of 16 rows; the conflict-free form (lanes i and i + 16
+// joined into 16-byte writes) measured slower.
 #include "mxops.h"
 #include "qtile.h"
 

@@ -18,7 +18,8 @@ constexpr int kThreads = 64 * kWaves;
 static_assert(kFwdBlockM == 32 * kWaves && kFwdBlockN == 64, "Q-tile geometry");
 
 // 16-byte chunk swizzles of LDS tiles (stored chunk = chunk XOR f(row)),
-// chosen for 64 banks x 4 bytes:
+// chosen for LDS reads (64 banks x 4 bytes, 16 lanes per cycle for 16-byte
+// reads, 32 for 8-byte ones):
 //  - swz_k: rows read as 32x32x16 MFMA A operands (16 lanes = 16 rows, one
 //    16-byte chunk each);
 //  - swz_v: rows read by transposed reads (a 16-lane group reads 4 rows x 32
