@@ -178,9 +178,13 @@ def dq_mx(q_d, k_d, v_d, do_d, k_keys, do, o, lse, kv_offsets, *, scale, broadca
       dS    = P (dP - delta)
       dQ   += scale * dS k_keys          (K encoded along keys)
     the broadcast dQ summing over sequences. Returns (dq, delta, abs_sum,
-    floor_sum): abs_sum = scale * |dS| |k_keys| and floor_sum = scale *
-    max_j |dS_ij| * sum_j |k_keys_j| (per sequence), the two terms a bound on
-    dS's rounding needs."""
+    floor_sum, acc_sum): abs_sum = scale * |dS| |k_keys| and floor_sum =
+    scale * max_j |dS_ij| * sum_j |k_keys_j| (per sequence), the two terms a
+    bound on dS's rounding needs, and acc_sum = scale * (P (|do_d| |v_d|^T +
+    sum_d |do o|)) |k_keys|, the magnitudes that dP and delta sum over d: a
+    kernel forms both as fp32 sums of D terms, whose error (up to D 2^-24
+    times these magnitudes) is not relative to dS = P (dP - delta) itself
+    and dominates it where dP and delta nearly cancel."""
     import oracle.attention as A
     B = len(kv_offsets) - 1
     H = k_d.shape[1]
@@ -192,6 +196,7 @@ def dq_mx(q_d, k_d, v_d, do_d, k_keys, do, o, lse, kv_offsets, *, scale, broadca
     dq = np.zeros(q_d.shape)
     abs_sum = np.zeros(q_d.shape)
     floor_sum = np.zeros(q_d.shape)
+    acc_sum = np.zeros(q_d.shape)
     delta = np.zeros((H, t_q))
     for b in range(B):
         k0, k1 = int(kv_offsets[b]), int(kv_offsets[b + 1])
@@ -214,8 +219,10 @@ def dq_mx(q_d, k_d, v_d, do_d, k_keys, do, o, lse, kv_offsets, *, scale, broadca
             abs_sum[qs, h] += scale * (np.abs(ds) @ np.abs(kk))
             amax = np.abs(ds).max(axis=1, initial=0.0)
             floor_sum[qs, h] += scale * amax[:, None] * np.abs(kk).sum(axis=0)[None, :]
+            mag = np.abs(do_d[os_, h]) @ np.abs(v_d[k0:k1, h]).T + np.sum(np.abs(do[os_, h] * o[os_, h]), axis=1)[:, None]
+            acc_sum[qs, h] += scale * ((p * mag) @ np.abs(kk))
             delta[h, os_] = dl
-    return dq, delta, abs_sum, floor_sum
+    return dq, delta, abs_sum, floor_sum, acc_sum
 
 
 def dkdv_mx(q_d, k_d, v_d, do_d, q_r, do_r, do, o, lse, kv_offsets, *, scale, broadcast_q,
@@ -238,10 +245,12 @@ def dkdv_mx(q_d, k_d, v_d, do_d, q_r, do_r, do, o, lse, kv_offsets, *, scale, br
       dS    = P (dP - delta)
       dV    = P^T do_r
       dK    = scale * dS^T q_r
-    Returns (dk, dv, dv_p_abs, dv_p_floor, dk_abs, dk_floor): dv_p_abs =
-    P^T |do_r| and dv_p_floor = vis^T |do_r| (the terms of P's rounding bound),
-    dk_abs = scale |dS|^T |q_r| and dk_floor = scale * (max_i |dS_ij|) *
-    sum_i |q_r_i| per key (those of dS's)."""
+    Returns (dk, dv, dv_p_abs, dv_p_floor, dk_abs, dk_floor, dk_acc): dv_p_abs
+    = P^T |do_r| and dv_p_floor = vis^T |do_r| (the terms of P's rounding
+    bound), dk_abs = scale |dS|^T |q_r| and dk_floor = scale * (max_i |dS_ij|)
+    * sum_i |q_r_i| per key (those of dS's), and dk_acc = scale * (P (|do_d|
+    |v_d|^T + sum_d |do o|))^T |q_r|, the magnitudes behind the fp32 sums
+    that form dP and delta (as for dq_mx's acc_sum)."""
     import oracle.attention as A
     B = len(kv_offsets) - 1
     T_k, H, D = k_d.shape
@@ -251,6 +260,7 @@ def dkdv_mx(q_d, k_d, v_d, do_d, q_r, do_r, do, o, lse, kv_offsets, *, scale, br
     dv_p_floor = np.zeros((T_k, H, D))
     dk_abs = np.zeros((T_k, H, D))
     dk_floor = np.zeros((T_k, H, D))
+    dk_acc = np.zeros((T_k, H, D))
     lq = q_d.shape[0] if broadcast_q else None
     for b in range(B):
         k0, k1 = int(kv_offsets[b]), int(kv_offsets[b + 1])
@@ -278,4 +288,6 @@ def dkdv_mx(q_d, k_d, v_d, do_d, q_r, do_r, do, o, lse, kv_offsets, *, scale, br
             dk_abs[k0:k1, h] = scale * (np.abs(ds).T @ np.abs(q_r[qs, h]))
             amax = np.abs(ds).max(axis=0, initial=0.0)
             dk_floor[k0:k1, h] = scale * amax[:, None] * np.abs(q_r[qs, h]).sum(axis=0)[None, :]
-    return dk, dv, dv_p_abs, dv_p_floor, dk_abs, dk_floor
+            mag = np.abs(do_d[os_, h]) @ np.abs(v_d[k0:k1, h]).T + np.sum(np.abs(do[os_, h] * o[os_, h]), axis=1)[:, None]
+            dk_acc[k0:k1, h] = scale * ((p * mag).T @ np.abs(q_r[qs, h]))
+    return dk, dv, dv_p_abs, dv_p_floor, dk_abs, dk_floor, dk_acc

@@ -26,11 +26,11 @@ def _lengths(rng, n, hi):
     return [int(rng.choice(EDGE)) if p else int(rng.integers(0, hi)) for p in pick]
 
 
-def _problem(seed):
+def _problem(seed, head_dims=(64, 128)):
     rng = np.random.default_rng(7000 + seed)
     kind = str(rng.choice(["bcast", "perseq", "causal", "window", "sparse", "sparse_self"]))
     H = int(rng.integers(1, 4))
-    D = int(rng.choice([64, 128]))
+    D = int(rng.choice(list(head_dims)))
     B = int(rng.integers(1, 7))
     kw = dict(H=H, D=D, seed=100 + seed)
     if kind == "bcast":

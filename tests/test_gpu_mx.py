@@ -195,12 +195,22 @@ def test_mx_dq_pass(case):
     448 (so 2^e <= max|dS| 2^-7 and nothing is clamped); per element
 
       |dQ_gpu - dQ| <= scale sum_j (2^-4 |dS_ij| + 2^-17 max_j' |dS_ij'|) |k_jd|
-                       + 1e-4 scale sum_j |dS_ij| |k_jd| + 1e-6
+                       + 1e-4 scale sum_j |dS_ij| |k_jd|
+                       + 2^-17 scale sum_j P_ij (sum_d |do_id v_jd| + sum_d |do_id o_id|) |k_jd|
+                       + 1e-6
 
     (half an E4M3 step: relative 2^-4 in the normal range, at most 2^-10 2^e
-    below it; and fp32 sums), and delta within fp32 summation error."""
+    below it; fp32 sums; and the fp32 sums of D = 128 terms that form dP and
+    delta, within D 2^-24 = 2^-17 of the magnitudes summed, which is not
+    relative to dS = P (dP - delta): where dP and delta nearly cancel it is
+    the largest term), and delta within fp32 summation error."""
     print("case", case, flush=True)
-    x = SMALL_CASES[case]()
+    _check_mx_dq(SMALL_CASES[case]())
+
+
+def _check_mx_dq(x, mean_frac=0.25):
+    """The check of test_mx_dq_pass on the instance x (mean_frac: see
+    _check_mx_dkdv)."""
     w = x.workload
     off = x.kv_offsets
     qf, kf, vf, dof = _f64(x.q), _f64(x.k), _f64(x.v), _f64(x.do)
@@ -217,7 +227,7 @@ def test_mx_dq_pass(case):
     o, lse = A.forward(q_d, k_d, v_keys, off, **kw)
     o_bits = W.f32_to_bf16_bits(o.astype(np.float32))
     o_bf = _f64(o_bits)
-    dq, delta, abs_sum, floor_sum = OMX.dq_mx(q_d, k_d, v_d, do_d, k_keys, dof, o_bf, lse, off, **kw)
+    dq, delta, abs_sum, floor_sum, acc_sum = OMX.dq_mx(q_d, k_d, v_d, do_d, k_keys, dof, o_bf, lse, off, **kw)
 
     prob = problem_of(x)
     att = J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask)
@@ -235,11 +245,11 @@ def test_mx_dq_pass(case):
     gdq = out["dq_accum"].cpu().numpy().astype(np.float64)
     gdelta = out["delta"].cpu().numpy().astype(np.float64)
     assert not np.isnan(gdq).any() and not np.isnan(gdelta).any()
-    bound = 2.0 ** -4 * abs_sum + 2.0 ** -17 * floor_sum + 1e-4 * abs_sum + 1e-6
+    bound = 2.0 ** -4 * abs_sum + 2.0 ** -17 * floor_sum + 1e-4 * abs_sum + 2.0 ** -17 * acc_sum + 1e-6
     err = np.abs(gdq - dq)
     assert np.all(err <= bound), float((err - bound).max())
     # and on average far inside it
-    assert err.mean() <= 0.25 * bound.mean()
+    assert err.mean() <= mean_frac * bound.mean()
     dbound = 2 * D * 2.0 ** -24 * np.einsum("rhd,rhd->hr", np.abs(dof), np.abs(o_bf)) + 1e-30
     assert np.all(np.abs(gdelta - delta) <= dbound)
     # the bf16 dq is the rounding of the fp32 sum
@@ -269,7 +279,7 @@ def test_mx_dq_pass_full_size_one_head():
     o, lse = A.forward(q_d, k_d, v_keys, off, **kw)
     o_bits = W.f32_to_bf16_bits(o.astype(np.float32))
     o_bf = _f64(o_bits)
-    dq, delta, abs_sum, floor_sum = OMX.dq_mx(q_d, k_d, v_d, do_d, k_keys, dof, o_bf, lse, off, **kw)
+    dq, delta, abs_sum, floor_sum, acc_sum = OMX.dq_mx(q_d, k_d, v_d, do_d, k_keys, dof, o_bf, lse, off, **kw)
 
     prob = problem_of(x)
     cus = J.jfa_device_workers(0)
@@ -293,7 +303,7 @@ def test_mx_dq_pass_full_size_one_head():
     assert not np.isnan(gdq).any()
     gdq = gdq[:, h:h + 1]
     gdelta = out["delta"].cpu().numpy().astype(np.float64)[h:h + 1]
-    bound = 2.0 ** -4 * abs_sum + 2.0 ** -17 * floor_sum + 1e-4 * abs_sum + 1e-6
+    bound = 2.0 ** -4 * abs_sum + 2.0 ** -17 * floor_sum + 1e-4 * abs_sum + 2.0 ** -17 * acc_sum + 1e-6
     err = np.abs(gdq - dq)
     assert np.all(err <= bound), float((err - bound).max())
     assert err.mean() <= 0.25 * bound.mean()
@@ -342,7 +352,7 @@ def test_mx_element_offsets_beyond_int32():
     kw = dict(scale=w.scale, broadcast_q=True)
     o_r, lse_r = A.forward(q_d, k_d, v_keys, off, **kw)
     o_bits = W.f32_to_bf16_bits(o_r.astype(np.float32))
-    dq, _, abs_sum, floor_sum = OMX.dq_mx(q_d, k_d, v_d, do_d, k_keys, dof, _f64(o_bits), lse_r, off,
+    dq, _, abs_sum, floor_sum, acc_sum = OMX.dq_mx(q_d, k_d, v_d, do_d, k_keys, dof, _f64(o_bits), lse_r, off,
                                           **kw)
     o_all = np.zeros((att.total_q, H, D), dtype=np.uint16)
     o_all[lq:] = o_bits
@@ -357,7 +367,7 @@ def test_mx_element_offsets_beyond_int32():
     torch.cuda.synchronize()
     gdq = out["dq_accum"].cpu().numpy().astype(np.float64)
     assert not np.isnan(gdq).any()
-    bound = 2.0 ** -4 * abs_sum + 2.0 ** -17 * floor_sum + 1e-4 * abs_sum + 1e-6
+    bound = 2.0 ** -4 * abs_sum + 2.0 ** -17 * floor_sum + 1e-4 * abs_sum + 2.0 ** -17 * acc_sum + 1e-6
     err = np.abs(gdq - dq)
     assert np.all(err <= bound), float((err - bound).max())
     assert err.mean() <= 0.25 * bound.mean()
@@ -448,23 +458,31 @@ def _mx_dkdv_case(x, heads=None):
     return ref, host_f64(out["dk"])[:, hs], host_f64(out["dv"])[:, hs]
 
 
-def _check_mx_dkdv(ref, gdk, gdv):
+def _check_mx_dkdv(ref, gdk, gdv, mean_frac=0.25):
     """Against the oracle's exact-P, exact-dS values, per element:
       |dV_gpu - dV| <= 2^-4 P^T|dO_r| + 2^-18 vis^T|dO_r| + 2^-8 |dV| + 1e-4 P^T|dO_r| + 1e-6
       |dK_gpu - dK| <= 2^-4 scale|dS|^T|Q_r| + 2^-17 scale max|dS| sum|Q_r| + 2^-8 |dK|
-                        + 1e-4 scale|dS|^T|Q_r| + 1e-6
+                        + 1e-4 scale|dS|^T|Q_r|
+                        + 2^-17 scale (P (|dO||V|^T + sum_d |dO O|))^T |Q_r| + 1e-6
     (P, at most 1, scaled by 2^8 and rounded to E4M3: relative 2^-4 in its
     normal range, 2^-10 2^-8 below it; dS with its (key, 32-row block) scale
     2^e <= max|dS| 2^-7: relative 2^-4, at most 2^-10 2^e below; the bf16
-    rounding of dK, dV; fp32 sums), and on average far inside that."""
-    dk, dv, pa, pf, ka, kf = ref
+    rounding of dK, dV; fp32 sums; the fp32 sums of D = 128 terms that form
+    dP and delta, as for the dQ pass), and on average inside mean_frac of it.
+    A systematic error would not be: unbiased round-to-nearest leaves a mean
+    error of at most half its worst case (error uniform within half a step),
+    and sums over many terms partly cancel, hence 0.25 on these cases; where
+    an element is a single rounded term (a broadcast Q of one row: dV_j =
+    P_1j dO_1) the mean reaches about 0.35, so random problems use 0.5."""
+    dk, dv, pa, pf, ka, kf, kacc = ref
     assert not np.isnan(gdk).any() and not np.isnan(gdv).any()
     bv = 2.0 ** -4 * pa + 2.0 ** -18 * pf + 2.0 ** -8 * np.abs(dv) + 1e-4 * pa + 1e-6
-    bk = 2.0 ** -4 * ka + 2.0 ** -17 * kf + 2.0 ** -8 * np.abs(dk) + 1e-4 * ka + 1e-6
+    bk = (2.0 ** -4 * ka + 2.0 ** -17 * kf + 2.0 ** -8 * np.abs(dk) + 1e-4 * ka
+          + 2.0 ** -17 * kacc + 1e-6)
     ev, ek = np.abs(gdv - dv), np.abs(gdk - dk)
     assert np.all(ev <= bv), ("dV", float((ev - bv).max()))
     assert np.all(ek <= bk), ("dK", float((ek - bk).max()))
-    assert ev.mean() <= 0.25 * bv.mean() and ek.mean() <= 0.25 * bk.mean()
+    assert ev.mean() <= mean_frac * bv.mean() and ek.mean() <= mean_frac * bk.mean()
 
 
 @pytest.mark.parametrize("case", MXKV_CASES)

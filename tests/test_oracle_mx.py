@@ -130,10 +130,13 @@ def test_dq_mx_without_quantisation_is_the_attention_gradient(broadcast):
     kw = dict(scale=0.125, broadcast_q=broadcast, q_offsets=qoff, causal=not broadcast)
     o, lse = A.forward(q, k, v, off, **kw)
     dq_ref, _, _, delta_ref = A.backward(q, k, v, do, off, **kw)
-    dq, delta, abs_sum, floor_sum = mx.dq_mx(q, k, v, do, k, do, o, lse, off, **kw)
+    dq, delta, abs_sum, floor_sum, acc_sum = mx.dq_mx(q, k, v, do, k, do, o, lse, off, **kw)
     assert np.allclose(dq, dq_ref, rtol=0, atol=1e-12) and np.allclose(delta, delta_ref, atol=1e-12)
     assert np.all(abs_sum >= np.abs(dq) - 1e-12) and np.all(floor_sum >= 0)
-    dq2, _, _, _ = mx.dq_mx(q, k, v, do, 2 * k, do, o, lse, off, **kw)
+    # |dP - delta| <= sum_d |do v| + sum_d |do o|, so the accumulation term
+    # dominates the one of dS itself
+    assert np.all(acc_sum >= abs_sum - 1e-12)
+    dq2, *_ = mx.dq_mx(q, k, v, do, 2 * k, do, o, lse, off, **kw)
     assert np.allclose(dq2, 2 * dq, rtol=0, atol=1e-12)
 
 
@@ -150,9 +153,9 @@ def test_dkdv_mx_without_quantisation_is_the_attention_gradient(broadcast):
     kw = dict(scale=0.125, broadcast_q=broadcast, q_offsets=qoff, causal=not broadcast)
     o, lse = A.forward(q, k, v, off, **kw)
     _, dk_ref, dv_ref, _ = A.backward(q, k, v, do, off, **kw)
-    dk, dv, pa, pf, ka, kf = mx.dkdv_mx(q, k, v, do, q, do, do, o, lse, off, **kw)
+    dk, dv, pa, pf, ka, kf, kacc = mx.dkdv_mx(q, k, v, do, q, do, do, o, lse, off, **kw)
     assert np.allclose(dk, dk_ref, rtol=0, atol=1e-12) and np.allclose(dv, dv_ref, rtol=0, atol=1e-12)
     assert np.all(pa >= np.abs(dv) - 1e-12) and np.all(pf >= pa - 1e-12)
-    assert np.all(ka >= np.abs(dk) - 1e-12) and np.all(kf >= 0)
+    assert np.all(ka >= np.abs(dk) - 1e-12) and np.all(kf >= 0) and np.all(kacc >= ka - 1e-12)
     dk2, dv2, *_ = mx.dkdv_mx(q, k, v, do, 3 * q, 2 * do, do, o, lse, off, **kw)
     assert np.allclose(dv2, 2 * dv, rtol=0, atol=1e-12) and np.allclose(dk2, 3 * dk, rtol=0, atol=1e-12)
