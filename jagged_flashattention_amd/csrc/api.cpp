@@ -495,8 +495,11 @@ int32_t jfa_bwd_dq_mx(const jfa_problem* prob, const jfa_device_plan* dq_plan,
         const int64_t q_rows = bcast ? prob->lq : qi->total_q;
         if (ops == nullptr || d_key_block_offsets == nullptr || num_key_blocks < (qi->total_kv + 31) / 32)
             return JFA_ERR_INVALID_ARG;
-        if (!tensor_ok(o, qi->total_q * hd) || !tensor_ok(d_o, qi->total_q * hd) || lse == nullptr ||
-            delta == nullptr || !tensor_ok(ops->q_codes, q_rows * hd) ||
+        // (no query row at all: O, dO, LSE, delta and dQ may be empty)
+        if (qi->total_q > 0 && (lse == nullptr || delta == nullptr || !aligned4(lse) || !aligned4(delta)))
+            return JFA_ERR_INVALID_ARG;
+        if (!tensor_ok(o, qi->total_q * hd) || !tensor_ok(d_o, qi->total_q * hd) ||
+            !tensor_ok(ops->q_codes, q_rows * hd) ||
             !tensor_ok(ops->k_codes, qi->total_kv * hd) || !tensor_ok(ops->v_codes, qi->total_kv * hd) ||
             !tensor_ok(ops->do_codes, qi->total_q * hd) || !tensor_ok(ops->kk_codes, qi->total_kv * hd))
             return JFA_ERR_INVALID_ARG;
@@ -506,7 +509,8 @@ int32_t jfa_bwd_dq_mx(const jfa_problem* prob, const jfa_device_plan* dq_plan,
             !scales_ok(ops->do_scales, H * qi->total_q * nbd) ||
             !scales_ok(ops->kk_scales, H * (int64_t)num_key_blocks * prob->head_dim))
             return JFA_ERR_INVALID_ARG;
-        if (!bcast && (!tensor_ok(dq, qi->total_q * hd) || dq_accum == nullptr)) return JFA_ERR_INVALID_ARG;
+        if (!bcast && (!tensor_ok(dq, qi->total_q * hd) || (qi->total_q > 0 && dq_accum == nullptr)))
+            return JFA_ERR_INVALID_ARG;
         if (qi->num_tiles == 0) return JFA_OK;
         const jfa::Band bd = jfa::band_of(prob);
         jfa::DqArgs d{};

@@ -198,7 +198,7 @@ def test_bwd_validation_returns_before_launch():
     assert _call_bwd(_prob(lq=9), kv, dq, need) == J.JFA_ERR_PLAN_MISMATCH
 
 
-def _call_dq_mx(prob, dq, ws_bytes, nkb=1, ops=True, **over):
+def _call_dq_mx(prob, dq_plan, ws_bytes, nkb=1, ops=True, **over):
     t = _FakeTensor(0x1000)
     f = lambda x: None if x is None else ctypes.c_void_p(x.data_ptr())
     args = dict(o=t, lse=t, d_o=t, dq=t, dq_accum=t, delta=t, ws=t, kbo=t)
@@ -207,7 +207,7 @@ def _call_dq_mx(prob, dq, ws_bytes, nkb=1, ops=True, **over):
     sc.update({k: v for k, v in over.items() if k.endswith("_scales")})
     mx = J.JfaMxBwdOperands(q_codes=0x1000, k_codes=0x1000, v_codes=0x1000, do_codes=0x1000,
                             kk_codes=0x1000, **sc)
-    plan = J.JfaDevicePlan(ctypes.pointer(dq.info), 0x1000, 0x1000, None, None)
+    plan = J.JfaDevicePlan(ctypes.pointer(dq_plan.info), 0x1000, 0x1000, None, None)
     cp = prob.c()
     return J._lib().jfa_bwd_dq_mx(ctypes.byref(cp), ctypes.byref(plan), None,
                                   ctypes.c_void_p(0x1000), f(args["kbo"]), nkb, f(args["o"]),
@@ -235,6 +235,18 @@ def test_bwd_dq_mx_validation_returns_before_launch():
     p64 = _prob(head_dim=64)
     dq64 = J.jfa_plan_build(p64, None, [0, 3, 5], None, J.JFA_PASS_DQ, 4)
     assert _call_dq_mx(p64, dq64, J.jfa_bwd_workspace_bytes(p64, dq64.info), nkb=2) == J.JFA_ERR_UNSUPPORTED
+
+
+def test_bwd_dq_mx_accepts_a_problem_without_query_rows():
+    """Per-sequence Q whose sequences all have 0 rows: O, dO, LSE, delta and
+    dQ are empty (null pointers, as empty tensors give) and the call does
+    nothing (it used to refuse the null LSE)."""
+    prob = _prob(head_dim=128, broadcast_q=False, lq=0)
+    dq = J.jfa_plan_build(prob, [0, 0, 0], [0, 3, 5], None, J.JFA_PASS_DQ, 4)
+    assert dq.info.total_q == 0 and dq.info.num_tiles == 0
+    need = J.jfa_bwd_workspace_bytes(prob, dq.info)
+    assert _call_dq_mx(prob, dq, need, nkb=2, o=None, lse=None, d_o=None, dq=None, dq_accum=None,
+                       delta=None) == J.JFA_OK
 
 
 def test_jagged_attention_rejects_mismatched_tensors(monkeypatch):

@@ -17,7 +17,7 @@ if not torch.cuda.is_available():
 
 from test_gpu_parity import _custom, check_all, run_gpu  # noqa: E402
 
-N_CASES = 160
+N_CASES = 400
 EDGE = [0, 1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
 
 

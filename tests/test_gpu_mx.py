@@ -249,11 +249,13 @@ def _check_mx_dq(x, mean_frac=0.25):
     err = np.abs(gdq - dq)
     assert np.all(err <= bound), float((err - bound).max())
     # and on average far inside it
-    assert err.mean() <= mean_frac * bound.mean()
+    if mean_frac is not None and err.size:
+        assert err.mean() <= mean_frac * bound.mean(), ("mean", float(err.mean() / bound.mean()))
     dbound = 2 * D * 2.0 ** -24 * np.einsum("rhd,rhd->hr", np.abs(dof), np.abs(o_bf)) + 1e-30
-    assert np.all(np.abs(gdelta - delta) <= dbound)
+    assert np.all(np.abs(gdelta - delta) <= dbound), ("delta", float(np.max(np.abs(gdelta - delta) - dbound, initial=0)))
     # the bf16 dq is the rounding of the fp32 sum
-    assert np.abs(host_f64(out["dq"]) - gdq).max() <= 2 ** -8 * np.abs(gdq).max() + 1e-30
+    e16 = float(np.max(np.abs(host_f64(out["dq"]) - gdq), initial=0.0))
+    assert e16 <= 2 ** -8 * float(np.max(np.abs(gdq), initial=0.0)) + 1e-30, ("bf16 dq", e16)
 
 
 def test_mx_dq_pass_full_size_one_head():
@@ -473,16 +475,22 @@ def _check_mx_dkdv(ref, gdk, gdv, mean_frac=0.25):
     error of at most half its worst case (error uniform within half a step),
     and sums over many terms partly cancel, hence 0.25 on these cases; where
     an element is a single rounded term (a broadcast Q of one row: dV_j =
-    P_1j dO_1) the mean reaches about 0.35, so random problems use 0.5."""
+    P_1j dO_1) the mean reaches about 0.35, so random problems use 0.5; and
+    where only a few rounded terms make up every element (a handful of rows
+    or keys) the mean says nothing: mean_frac None skips it."""
     dk, dv, pa, pf, ka, kf, kacc = ref
     assert not np.isnan(gdk).any() and not np.isnan(gdv).any()
     bv = 2.0 ** -4 * pa + 2.0 ** -18 * pf + 2.0 ** -8 * np.abs(dv) + 1e-4 * pa + 1e-6
     bk = (2.0 ** -4 * ka + 2.0 ** -17 * kf + 2.0 ** -8 * np.abs(dk) + 1e-4 * ka
           + 2.0 ** -17 * kacc + 1e-6)
     ev, ek = np.abs(gdv - dv), np.abs(gdk - dk)
+    if not ev.size:   # no key at all
+        return
     assert np.all(ev <= bv), ("dV", float((ev - bv).max()))
     assert np.all(ek <= bk), ("dK", float((ek - bk).max()))
-    assert ev.mean() <= mean_frac * bv.mean() and ek.mean() <= mean_frac * bk.mean()
+    if mean_frac is not None:
+        assert ev.mean() <= mean_frac * bv.mean() and ek.mean() <= mean_frac * bk.mean(), (
+            "mean", float(ev.mean() / bv.mean()), float(ek.mean() / bk.mean()))
 
 
 @pytest.mark.parametrize("case", MXKV_CASES)

@@ -29,6 +29,15 @@ TOL_O = 1e-2
 TOL_GRAD = 2e-2
 
 
+def o_err_ok(got, ref):
+    """|O_gpu - O| <= TOL_O + 2^-8 |O| element-wise. O is bf16 by contract: a
+    correctly rounded bf16 value lies within half a unit in its last place,
+    at most 2^-8 |O|, of the exact one, which alone exceeds 1e-2 once |O| >
+    2.56 (rows that see one or a few keys, O close to one N(0,1) V row). The
+    1e-2 applies on top of that output rounding."""
+    return bool(np.all(np.abs(got - ref) <= TOL_O + 2.0 ** -8 * np.abs(ref)))
+
+
 def dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
@@ -101,8 +110,14 @@ def oracle_full(x):
 
 
 def rel_err(got, ref):
+    if ref.size == 0:   # e.g. no query rows at all
+        return 0.0
     scale = np.abs(ref).max()
     return np.abs(got - ref).max() / (scale if scale > 0 else 1.0)
+
+
+def _max_abs(a):
+    return float(np.abs(a).max()) if a.size else 0.0
 
 
 def check_all(x, g):
@@ -111,16 +126,17 @@ def check_all(x, g):
     assert not np.isnan(go).any() and not np.isnan(glse).any()
     fin = np.isfinite(lse)
     assert np.array_equal(fin, np.isfinite(glse)), "rows without keys must give LSE=-inf"
-    assert np.abs(go - o).max() <= TOL_O
+    assert o_err_ok(go, o), ("o", _max_abs(go - o))
     if fin.any():
-        assert np.abs(glse[fin] - lse[fin]).max() <= TOL_O
+        assert _max_abs(glse[fin] - lse[fin]) <= TOL_O, ("lse", _max_abs(glse[fin] - lse[fin]))
     gdq, gdk, gdv = host_f64(g.dq), host_f64(g.dk), host_f64(g.dv)
     for name, got, ref in (("dq", gdq, dq), ("dk", gdk, dk), ("dv", gdv, dv)):
         assert not np.isnan(got).any(), name
         assert rel_err(got, ref) <= TOL_GRAD, (name, rel_err(got, ref))
-    assert rel_err(g.dq_accum.cpu().numpy().astype(np.float64), dq) <= TOL_GRAD
+    e = rel_err(g.dq_accum.cpu().numpy().astype(np.float64), dq)
+    assert e <= TOL_GRAD, ("dq_accum", e)
     gdelta = g.delta.cpu().numpy()
-    assert np.abs(gdelta - delta).max() <= 2e-2 * max(1.0, np.abs(delta).max())
+    assert _max_abs(gdelta - delta) <= 2e-2 * max(1.0, _max_abs(delta)), ("delta", _max_abs(gdelta - delta))
 
 
 def _custom(name, *, broadcast, H, D, lengths, lq=0, causal=False, mask_seed=None, seed=11,
@@ -243,8 +259,8 @@ def test_zero_q_gives_mean_of_v():
     g = run_gpu(x)
     o = host_f64(g.o)
     v = W.bf16_bits_to_f32(x.v).astype(np.float64)
-    assert np.abs(o[:40] - v[0:7].mean(axis=0)).max() <= TOL_O
-    assert np.abs(o[40:] - v[7:307].mean(axis=0)).max() <= TOL_O
+    assert o_err_ok(o[:40], np.broadcast_to(v[0:7].mean(axis=0), o[:40].shape))
+    assert o_err_ok(o[40:], np.broadcast_to(v[7:307].mean(axis=0), o[40:].shape))
     lse = g.lse.cpu().numpy()
     np.testing.assert_allclose(lse[0, :40], np.log(7), atol=1e-5)
     np.testing.assert_allclose(lse[0, 40:], np.log(300), atol=1e-5)
@@ -397,7 +413,7 @@ def test_full_size(cfg, part):
         do1 = _head_f64(x.do, h, os_)
         o, lse = A.forward(q1, k1_, v1, off, **kw)
         dq, dk, dv, _ = A.backward(q1, k1_, v1, do1, off, **kw)
-        assert np.abs(W.bf16_bits_to_f32(go[:, h]) - o[:, 0]).max() <= TOL_O, (b, h)
+        assert o_err_ok(W.bf16_bits_to_f32(go[:, h]), o[:, 0]), (b, h)
         assert np.abs(glse[h] - lse[0]).max() <= TOL_O, (b, h)
         assert rel_err(W.bf16_bits_to_f32(gdk[:, h]), dk[:, 0]) <= TOL_GRAD, (b, h)
         assert rel_err(W.bf16_bits_to_f32(gdv[:, h]), dv[:, 0]) <= TOL_GRAD, (b, h)
@@ -488,7 +504,7 @@ def test_element_offsets_beyond_int32():
     q_rows = _head_f64(x.q, h)[rows]
     o0, lse0 = A.forward(q_rows, _head_f64(x.k, h, slice(0, big)), _head_f64(x.v, h, slice(0, big)),
                          np.array([0, big], dtype=np.int32), **kw)
-    assert np.abs(W.bf16_bits_to_f32(go[rows, h]) - o0[:, 0]).max() <= TOL_O
+    assert o_err_ok(W.bf16_bits_to_f32(go[rows, h]), o0[:, 0])
     assert np.abs(glse[h, rows] - lse0[0]).max() <= TOL_O
     # the later sequences, as a batch of their own (broadcast dQ sums them)
     sub = W.offsets_of(np.array(later))
@@ -498,7 +514,7 @@ def test_element_offsets_beyond_int32():
     do_s = W.bf16_bits_to_f32(x.do[lq:]).astype(np.float64)
     o, lse = A.forward(q_all, k_s, v_s, sub, **kw)
     dq, dk, dv, _ = A.backward(q_all, k_s, v_s, do_s, sub, **kw)
-    assert np.abs(W.bf16_bits_to_f32(go[lq:]) - o).max() <= TOL_O
+    assert o_err_ok(W.bf16_bits_to_f32(go[lq:]), o)
     assert np.abs(glse[:, lq:] - lse).max() <= TOL_O
     assert rel_err(W.bf16_bits_to_f32(gdk), dk) <= TOL_GRAD
     assert rel_err(W.bf16_bits_to_f32(gdv), dv) <= TOL_GRAD
@@ -530,7 +546,7 @@ def test_long_sequence_sampled():
         kw = dict(scale=w.scale, broadcast_q=True)
         o, lse = A.forward(q1, k1_, v1, off, **kw)
         _, dk, dv, _ = A.backward(q1, k1_, v1, do1, off, **kw)
-        assert np.abs(W.bf16_bits_to_f32(go[os_, h]) - o[:, 0]).max() <= TOL_O, b
+        assert o_err_ok(W.bf16_bits_to_f32(go[os_, h]), o[:, 0]), b
         assert np.abs(glse[h, os_] - lse[0]).max() <= TOL_O, b
         assert rel_err(W.bf16_bits_to_f32(gdk[k0:k1, h]), dk[:, 0]) <= TOL_GRAD, b
         assert rel_err(W.bf16_bits_to_f32(gdv[k0:k1, h]), dv[:, 0]) <= TOL_GRAD, b
