@@ -129,19 +129,20 @@ constexpr bool kTileLog = false;
 // flag bits of a record: the plan's indices checked against the problem
 constexpr int kLogBadBatch = 1, kLogBadHead = 2, kLogBadTile = 4, kLogBadStream = 8;
 
-// Scheduling hint for a run of N LDS operand reads each feeding one MFMA:
-// issue the first A reads, then alternate one MFMA with one more read, then
-// the last A MFMAs. Without it the scheduler keeps a single read in flight
-// and every MFMA waits out a full LDS latency. Only orders the reads and
-// MFMAs of the current scheduling region; other instructions move freely.
-template <int N, int A>
+// Scheduling hint for a run of N MFMAs each fed by R LDS operand reads:
+// issue the reads of the first A MFMAs, then alternate one MFMA with the
+// reads of one more, then the last A MFMAs. Without it the scheduler keeps a
+// single read in flight and every MFMA waits out a full LDS latency. Only
+// orders the reads and MFMAs of the current scheduling region; other
+// instructions move freely.
+template <int N, int A, int R = 1>
 __device__ __forceinline__ void pipeline_reads_mfma() {
     constexpr int kMfma = 0x008, kDsRead = 0x100;
-    __builtin_amdgcn_sched_group_barrier(kDsRead, A, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, A * R, 0);
 #pragma unroll
     for (int j = 0; j < N - A; ++j) {
         __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, R, 0);
     }
     __builtin_amdgcn_sched_group_barrier(kMfma, A, 0);
 }

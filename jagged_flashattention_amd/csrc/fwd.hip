@@ -14,12 +14,14 @@
 //     rows (for a broadcast Q of 256 rows: every K/V row is read once);
 //   - the worker's blocks form one stream across its tiles: K and V of block
 //     j+3 are copied global -> LDS with direct-to-LDS loads while block j is
-//     computed (4-slot K ring, 3-slot V ring; a block's copies get two
-//     iterations to land), so the copy costs no VGPRs and no LDS store
-//     instructions, and tile boundaries do not drain the pipe;
-//   - V of block j+1 is transposed LDS -> LDS with transposed LDS reads
-//     (ds_read_b64_tr_b16) into V^T with keys in the order the P^T
-//     accumulator registers hold them, once per block for all 8 waves;
+//     computed (4-slot K and V rings; a block's copies get two iterations to
+//     land), so the copy costs no VGPRs and no LDS store instructions, and
+//     tile boundaries do not drain the pipe;
+//   - the V^T operands of O^T += V^T P^T come straight from the natural V
+//     block through transposed LDS reads (ds_read_b64_tr_b16): each 16-lane
+//     group reads the 4 key rows that the lane's P^T registers hold, in
+//     their order, so no transposed copy of V is made (MXFP8 makes one, by a
+//     byte transposition of block j+1 at block j);
 //   - per wave: S^T = K Q^T (32x32x16 bf16 MFMA, Q in VGPRs as the B operand,
 //     so a lane owns one query row and row max / row sum stay in-lane), fp32
 //     online softmax in the exp2 domain (bf16: the running max moves, and
@@ -34,15 +36,13 @@
 //     compiled once: two copies of it (a bulk loop and a tail loop) would
 //     double the kernel's largest code region for the few scalar
 //     instructions the flags cost;
-//   - O leaves through a per-wave LDS staging area (in the K slot and V^T
-//     buffer the tile's last block has released) as whole 16-byte-per-lane
-//     rows, so each store instruction writes 4 full rows.
+//   - O leaves through a per-wave LDS staging area (in the K and V slots the
+//     tile's last block has released) as whole 16-byte-per-lane rows, so
+//     each store instruction writes 4 full rows.
 // Every LDS tile is XOR-swizzled at 16-byte granularity so that the MFMA
 // operand reads and the transposed reads are free of bank conflicts (reads
-// see 64 banks x 4 bytes). The 8-byte V^T writes are not: writes are served
-// 16 lanes at a time over 32 banks, and the 16 lanes of a write group hold
-// one key position of 16 rows; the conflict-free form (lanes i and i + 16
-// joined into 16-byte writes) measured slower.
+// see 64 banks x 4 bytes; a half wave's transposed reads cover 4 rows x 64
+// bytes).
 #include "mxops.h"
 #include "qtile.h"
 
@@ -59,18 +59,17 @@ using namespace qtile;
 using namespace mxops;
 constexpr int kAhead = 3;        // block j+kAhead is copied while block j is computed
 constexpr int kKSlots = kAhead + 1;   // K ring: blocks j .. j+kAhead
-constexpr int kVSlots = kAhead;       // V ring: blocks j+1 .. j+kAhead (j+1 is transposed at j)
 constexpr int kReadAhead = 4;    // LDS operand reads kept in flight ahead of the MFMAs
 constexpr int kStageRows = 16;   // O rows per wave per epilogue round
 
 
 template <int D, bool MX>
 struct FwdLds {
+    static constexpr int VSLOTS = kAhead + 1;                  // V ring: blocks j .. j+kAhead
     static constexpr int BLK = kFwdBlockN * D * 2;            // one K or V block
-    static constexpr int K = 0;                                // kKSlots natural K blocks
-    static constexpr int V = K + kKSlots * BLK;                // kVSlots natural V blocks
-    static constexpr int VT = V + kVSlots * BLK;               // 2 V^T blocks [D][64]
-    static constexpr int CLAIM = VT + 2 * BLK;                 // int [2][64]: claimed tiles
+    static constexpr int K = 0;                                // kKSlots K blocks
+    static constexpr int V = K + kKSlots * BLK;                // VSLOTS V blocks
+    static constexpr int CLAIM = V + VSLOTS * BLK;             // int [2][64]: claimed tiles
     static constexpr int QUEUE = CLAIM + 2 * 64 * 4;           // int [kWaves][8]: tile queues
     static constexpr int BYTES = QUEUE + kWaves * 8 * 4;
     static constexpr int OST_WAVE = kStageRows * D * 2;        // O staging of one wave
@@ -79,15 +78,17 @@ struct FwdLds {
 
 // MXFP8 (D = 128): E4M3 K/V blocks are half the size; their scales ride
 // along (K: 4 bytes per key, V: 2 x 128 bytes per 64-key block); V^T is made
-// by a byte transposition in LDS; O has a staging area of its own.
+// by a byte transposition in LDS (block j+1 at block j, so the V ring holds
+// blocks j+1 .. j+kAhead); O has a staging area of its own.
 template <int D>
 struct FwdLds<D, true> {
+    static constexpr int VSLOTS = kAhead;
     static constexpr int BLK = kFwdBlockN * D;                 // one E4M3 K, V or V^T block
     static constexpr int SC = 256;                              // its scales
     static constexpr int K = 0;                                 // kKSlots K blocks [64][128]
     static constexpr int KS = K + kKSlots * BLK;                // kKSlots K scales [64][4]
-    static constexpr int V = KS + kKSlots * SC;                 // kVSlots V blocks [64][128]
-    static constexpr int VS = V + kVSlots * BLK;                // kKSlots V scales [2][128]
+    static constexpr int V = KS + kKSlots * SC;                 // VSLOTS V blocks [64][128]
+    static constexpr int VS = V + VSLOTS * BLK;                 // kKSlots V scales [2][128]
     static constexpr int VT = VS + kKSlots * SC;                // 2 V^T blocks [128][64]
     static constexpr int OST_WAVE = kStageRows * D * 2;
     static constexpr int OST = VT + 2 * BLK;                    // O staging, kWaves areas
@@ -100,12 +101,12 @@ struct FwdLds<D, true> {
 template <int D, int MODE, bool BCAST, bool MX>
 __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
     using LY = FwdLds<D, MX>;
+    constexpr int kVSlots = LY::VSLOTS;
     __shared__ __attribute__((aligned(1024))) char smem[LY::BYTES];
     constexpr int KC = D / 16;              // 16-wide d chunks of S^T = K Q^T
     constexpr int MD = D / 32;              // 32-row d blocks of O^T
     constexpr int CH = D / 8;               // 16-byte chunks per K/V row
     constexpr int LPW = (kFwdBlockN * CH) / (64 * kWaves);   // K (and V) loads per wave per block
-    constexpr int TPW = (kFwdBlockN * D) / (256 * kWaves);   // transposed reads per wave per block
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -122,20 +123,31 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
         const int r = p / CH, cp = p % CH;
         ld_row[u] = r;
         ld_gk[u] = 8 * (cp ^ swz_k<D>(r));
-        ld_gv[u] = 8 * (cp ^ swz_v<D>(r));
+        ld_gv[u] = 8 * (cp ^ swz_vo<D>(r));
     }
-    // transposition V -> V^T: this lane's read and write addresses per read u
-    int tr_src[TPW], tr_dst[TPW];
-    transpose_offsets<D, TPW>(wave, lane, [](int r) { return swz_v<D>(r); }, tr_src, tr_dst);
     // S^T operand: K row 32mb + lr, chunk 2kc + hf (swz_k(32mb + lr) == swz_k(lr))
     int k_off[KC];
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) k_off[kc] = lr * D * 2 + (((2 * kc + hf) ^ swz_k<D>(lr)) << 4);
-    // O^T operand: V^T row 32md + lr, 16-key chunk c -> stored chunk 2c + hf
-    // (swz_t(32md + lr) == swz_t(lr))
-    int vt_off[4];
+    // O^T operand V^T[32md + lr][keys of chunk c in sigma order], read from
+    // the natural V block by two transposed reads: read t of this lane's
+    // 16-lane group (d span 32md + 16g .. +15) takes rows 16c + 8t + 4hf + e,
+    // e = 0..3 (lanes 4e .. 4e+3 address row e, 8 bytes each), so the lane
+    // gets keys 16c + 8t + 4hf + 0..3 of its d: with t = 0, 1 the keys its
+    // P^T B operand holds (registers 0-3 and 8-11 of a lane half's column).
+    // The swizzle depends on the row modulo 16 only, so chunk c is an
+    // immediate offset of 16 rows.
+    int vo_off[2][MD];
+    {
+        const int n16 = lane & 15, e = n16 >> 2, cq = n16 & 3, g = (lane >> 4) & 1;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) vt_off[c] = lr * 128 + (((2 * c + hf) ^ swz_t(lr)) << 4);
+        for (int t = 0; t < 2; ++t) {
+            const int r = 8 * t + 4 * hf + e;
+#pragma unroll
+            for (int md = 0; md < MD; ++md)
+                vo_off[t][md] = r * D * 2 + (((4 * md + 2 * g + (cq >> 1)) ^ swz_vo<D>(r)) << 4) + 8 * (cq & 1);
+        }
+    }
 
     const int w = worker_id(a.num_workers);
     const int t_begin = ld_uniform(a.worker_ptr + w), t_end = ld_uniform(a.worker_ptr + w + 1);
@@ -304,28 +316,14 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
         ++l_slot;
         ++l_i;
     };
-    // V (natural, slot s % kVSlots) -> V^T (buffer s % 2)
-    auto tr_read = [&](int s, bf16x4 (&x)[TPW]) {
-        const char* src = smem + LY::V + (s % kVSlots) * LY::BLK;
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) x[u] = lds_read_tr((const uint16_t*)(src + tr_src[u]));
-    };
-    auto tr_write = [&](int s, const bf16x4 (&x)[TPW]) {
-        char* dst = smem + LY::VT + (s & 1) * LY::BLK;
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) *(bf16x4*)(dst + tr_dst[u]) = x[u];
-    };
+    // MXFP8: V (natural, slot s % kVSlots) -> V^T (buffer s % 2)
     auto transpose_v = [&](int s) {
-        if constexpr (MX) {
+        if constexpr (MX)
             mx_transpose_v(smem + LY::V + (s % kVSlots) * LY::BLK, smem + LY::VT + (s & 1) * LY::BLK, tid);
-        } else {
-            bf16x4 x[TPW];
-            tr_read(s, x);
-            tr_write(s, x);
-        }
     };
 
-    // prologue: block 0 landed and transposed, blocks 1 .. kAhead-1 in flight
+    // prologue: block 0 landed (MXFP8: and transposed), blocks 1 .. kAhead-1
+    // in flight
     l_issue();
     if (l_slot > 0) {
         wait_vmem();
@@ -408,16 +406,19 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
                 pb[c] = to_bf16x8(x);
             }
         };
-        // O^T[d, qrow] += V^T[d, key] P^T[key, qrow] (V^T buffer of stream position p)
+        // O^T[d, qrow] += V^T[d, key] P^T[key, qrow] (V slot of stream position p)
         auto pv = [&](const bf16x8 (&pb)[4], int p) {
-            const char* vtb = smem + LY::VT + (p & 1) * LY::BLK;
+            const char* vb = smem + LY::V + (p % kVSlots) * LY::BLK;
             bf16x8 vf[4 * MD];
 #pragma unroll
-            for (int j = 0; j < 4 * MD; ++j)
-                vf[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(vtb + 32 * 128 * (j >> 2) + vt_off[j & 3]));
+            for (int j = 0; j < 4 * MD; ++j) {
+                const char* rows = vb + 16 * D * 2 * (j & 3);
+                vf[j] = concat(lds_read_tr((const uint16_t*)(rows + vo_off[0][j >> 2])),
+                               lds_read_tr((const uint16_t*)(rows + vo_off[1][j >> 2])));
+            }
 #pragma unroll
             for (int j = 0; j < 4 * MD; ++j) oacc[j >> 2] = mfma32(vf[j], pb[j & 3], oacc[j >> 2]);
-            pipeline_reads_mfma<4 * MD, kReadAhead>();
+            pipeline_reads_mfma<4 * MD, kReadAhead, 2>();
         };
 
         for (int i = 0; i < T.work; ++i, ++s) {
@@ -430,11 +431,12 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
                 else wait_vmem_keep<2>();
             }
             publish();
-            // every wave is past block s-1: its K slot and V^T buffer are free
+            // every wave is past block s-1: its K and V slots (MXFP8: its
+            // V^T buffer) are free
             __syncthreads();
             receive();
             l_issue();                                // block s+kAhead
-            if (l_slot > s + 1) transpose_v(s + 1);   // V^T of block s+1
+            if (MX && l_slot > s + 1) transpose_v(s + 1);   // MXFP8: V^T of block s+1
 
             const int n = seq_block(T, i);
             bool skip, masked;
@@ -519,8 +521,9 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
         // ---- epilogue: O = O^T / l through this wave's staging area, LSE.
         // The staging areas are the K slot of block s-1 (no copy in flight
         // targets it: those are blocks s .. s+kAhead-1) for waves 0-3 and the
-        // V^T buffer of block s-1 for waves 4-7, free once every wave is past
+        // V slot of block s-1 for waves 4-7, free once every wave is past
         // block s-1; both are next written after the next iteration's barrier.
+        // (MXFP8 has staging of its own.)
         const float l_tot = pair_sum(l_run);
         const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
         __syncthreads();
@@ -530,7 +533,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
                 st = smem + LY::OST + wave * LY::OST_WAVE;
             } else {
                 st = wave < 4 ? smem + LY::K + ((s + kKSlots - 1) % kKSlots) * LY::BLK + wave * LY::OST_WAVE
-                              : smem + LY::VT + ((s + 1) & 1) * LY::BLK + (wave - 4) * LY::OST_WAVE;
+                              : smem + LY::V + ((s + kVSlots - 1) % kVSlots) * LY::BLK + (wave - 4) * LY::OST_WAVE;
             }
 #pragma unroll
             for (int rd = 0; rd < 32 / kStageRows; ++rd) {

@@ -25,7 +25,10 @@ static_assert(kFwdBlockM == 32 * kWaves && kFwdBlockN == 64, "Q-tile geometry");
 //  - swz_v: rows read by transposed reads (a 16-lane group reads 4 rows x 32
 //    bytes; the two groups of a half wave read rows r and r + 8);
 //  - swz_kv: both uses at once (swz_v plus bit 2 of the row);
-//  - swz_t: [d][64 keys] transposed tiles (128-byte rows) read as A operands.
+//  - swz_t: [d][64 keys] transposed tiles (128-byte rows) read as A operands;
+//  - swz_vo: rows read by transposed reads as 32x32x16 A operands with d on
+//    the lanes (a half wave reads 4 consecutive rows x 64 bytes: the 4 rows
+//    of a quad must land in different 64-byte quarters of the bank space).
 template <int D>
 __device__ __forceinline__ int swz_k(int r) {
     return D == 128 ? (r & 15) : ((r >> 1) & 7);
@@ -39,6 +42,10 @@ __device__ __forceinline__ int swz_kv(int r) {
     return swz_v<D>(r) + ((r >> 2) & 1);
 }
 __device__ __forceinline__ int swz_t(int d) { return (d >> 1) & 7; }
+template <int D>
+__device__ __forceinline__ int swz_vo(int r) {
+    return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
 
 // position of key q (within its group of 16) in sigma order 0-3, 8-11, 4-7,
 // 12-15: the order in which a 32x32 accumulator column holds its 16 rows
