@@ -12,8 +12,7 @@
 //      as a B operand, V in LDS) and streams the 32-row Q/dO blocks that see
 //      it. The worker's blocks form one stream across its tiles: Q and dO of
 //      block j+2 are copied global -> LDS with direct-to-LDS loads while block
-//      j is computed, and Q^T, dO^T of block j+1 are made LDS -> LDS with
-//      transposed reads. dK and dV stay in registers for the whole tile and
+//      j is computed. dK and dV stay in registers for the whole tile and
 //      leave as whole rows through LDS.
 //
 // Per Q block and wave (keys on lanes, query rows in registers):
@@ -21,8 +20,10 @@
 //   P   = exp2(S*scale*log2e - LSE*log2e)
 //   dP  = dO V^T         A = dO rows from LDS,   B = V rows from LDS
 //   dS  = P * (dP - delta)
-//   dV^T += dO^T P       A = dO^T from LDS (rows in sigma order), B = P
-//   dK^T += Q^T dS       A = Q^T from LDS (rows in sigma order),  B = dS
+//   dV^T += dO^T P       A = dO^T: transposed reads of the dO rows, B = P
+//   dK^T += Q^T dS       A = Q^T: transposed reads of the Q rows,  B = dS
+// (a transposed read of a 16-lane group takes the 4 rows that the lane's P or
+// dS registers hold, in their order, so no transposed copy is made)
 #include <climits>
 
 #include "qtile.h"
@@ -43,16 +44,12 @@ struct DkdvLds {
     static constexpr int ROWV = 2 * QB;                       // LSE*log2e [32], delta [32] fp32
     static constexpr int SLOT = 2 * QB + 512;                 // Q, dO, row values
     static constexpr int RING = 0;                            // kSlots slots
-    static constexpr int T = RING + kSlots * SLOT;            // 2 x (Q^T, dO^T) [D][32]
-    static constexpr int TBUF = 2 * QB;
-    static constexpr int V = T + 2 * TBUF;                    // V tile [256][D] (epilogue staging)
+    static constexpr int ST = RING + kSlots * SLOT;           // epilogue staging, waves 0-3
+    static constexpr int ST_WAVE = 16 * D * 2;                // 16 rows of one wave
+    static constexpr int V = ST + 4 * ST_WAVE;                // V tile [256][D]
     static constexpr int BYTES = V + kBwdBlockN * D * 2;
-    static constexpr int ST_WAVE = 32 * D * 2;                // staging of one wave: 32 rows
-    static_assert(kWaves * ST_WAVE == kBwdBlockN * D * 2, "staging fits the V tile");
+    static_assert(4 * ST_WAVE <= SLOT, "waves 4-7 stage in a released ring slot");
 };
-
-// [D][32] transposed tiles (64-byte rows): stored chunk = chunk ^ ((d >> 2) & 3)
-__device__ __forceinline__ int swz_t32(int d) { return (d >> 2) & 3; }
 
 template <int D, int MODE, bool BCAST>
 __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
@@ -63,8 +60,7 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
     constexpr int CH = D / 8;               // 16-byte chunks per row
     constexpr int QPW = (2 * kBwdBlockM * CH) / (64 * kWaves);   // Q + dO copies per wave per block
     constexpr int VPW = (kBwdBlockN * CH) / (64 * kWaves);       // V copies per wave per tile
-    constexpr int TPW = (kBwdBlockM * D) / (256 * kWaves);       // transposed reads per wave per tensor
-    static_assert(QPW >= 1 && TPW >= 1, "copy split");
+    static_assert(QPW >= 1, "copy split");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -73,31 +69,29 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
     const int64_t rs = (int64_t)H * D;
 
     constexpr int QH = (kBwdBlockM * CH) / 64;   // copies per tensor (Q or dO) per block
-    // transposition [32 rows][D] -> [D][32] with rows in sigma order: per
-    // read u, a 16-lane group reads 4 rows x 16 d; the two groups of a half
-    // wave read row quads kq and kq + 2
-    int tr_src[TPW], tr_dst[TPW];
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-        const int P = 2 * (TPW * wave + u) + (lane >> 5);
-        const int dg = P >> 2, sq = (P >> 1) & 1, z = P & 1;
-        const int kq = 4 * sq + z + 2 * ((lane >> 4) & 1);
-        const int n16 = lane & 15, e = n16 >> 2, c = n16 & 3;
-        const int r = 4 * kq + e;
-        tr_src[u] = r * D * 2 + (((2 * dg + (c >> 1)) ^ swz_kv<D>(r)) << 4) + 8 * (c & 1);
-        const int d = 16 * dg + n16, pos = sigma_pos(4 * kq);
-        tr_dst[u] = d * 64 + (((pos >> 3) ^ swz_t32(d)) << 4) + 2 * (pos & 7);
-    }
     // A operands: Q / dO row lr, chunk 2kc + hf; the V rows (B operand) of
     // this wave's keys use the same pattern 32 rows further per wave
     // (2kc + hf) ^ x = 2 (kc ^ x/2) + ((hf ^ x) & 1): one base and one XOR mask
-    const int ro_x = swz_kv<D>(lr);
+    const int ro_x = swz_vo<D>(lr);
     const int ro_base = lr * D * 2 + (((hf ^ ro_x) & 1) << 4), ro_xh = ro_x >> 1;
     auto row_off = [&](int kc) { return ro_base + ((kc ^ ro_xh) << 5); };
-    // Q^T / dO^T row 32md + lr, 16-row chunk c (stored chunk 2c + hf)
-    int t_off[2];
+    // Q^T / dO^T [32md + lr][rows of chunk c in sigma order] by two
+    // transposed reads of the natural rows: read t of this lane's 16-lane
+    // group (d span 32md + 16g .. +15) takes rows 16c + 8t + 4hf + e, e =
+    // 0..3, the rows this lane's P / dS registers 0-3 (t = 0) and 8-11
+    // (t = 1) of chunk c hold. The swizzle depends on the row modulo 16 only,
+    // so chunk c (and dO's place after Q in the slot) is an immediate offset.
+    int to_off[2][MD];
+    {
+        const int n16 = lane & 15, e = n16 >> 2, cq = n16 & 3, g = (lane >> 4) & 1;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) t_off[c] = lr * 64 + (((2 * c + hf) ^ swz_t32(lr)) << 4);
+        for (int t = 0; t < 2; ++t) {
+            const int r = 8 * t + 4 * hf + e;
+#pragma unroll
+            for (int md = 0; md < MD; ++md)
+                to_off[t][md] = r * D * 2 + (((4 * md + 2 * g + (cq >> 1)) ^ swz_vo<D>(r)) << 4) + 8 * (cq & 1);
+        }
+    }
 
     const int w = worker_id(a.num_workers);
     const int t_begin = ld_uniform(a.worker_ptr + w), t_end = ld_uniform(a.worker_ptr + w + 1);
@@ -171,7 +165,7 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
             const int p = 64 * (g % QH) + lane;
             const int r = p / CH, cp = p % CH;
             const int qi = min(kBwdBlockM * rb + r, LT.Lq - 1);
-            const int64_t off = hq + 8 * (cp ^ swz_kv<D>(r));
+            const int64_t off = hq + 8 * (cp ^ swz_vo<D>(r));
             const uint16_t* src = is_do ? a.d_o + (int64_t)(LT.orow0 + qi) * rs + off
                                         : a.q + (int64_t)(LT.q0 + qi) * rs + off;
             load_lds16(src, dst + (is_do ? LY::QB : 0) + 1024 * (g % QH));
@@ -196,22 +190,6 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
             rv[lane] = x;
         }
     };
-    // Q and dO of block s (slot s % kSlots) -> Q^T, dO^T (buffer s % 2)
-    auto transpose_q = [&](int s) {
-        const char* src = smem + LY::RING + (s % kSlots) * LY::SLOT;
-        char* dst = smem + LY::T + (s & 1) * LY::TBUF;
-        bf16x4 x[2 * TPW];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int u = 0; u < TPW; ++u)
-                x[TPW * t + u] = lds_read_tr((const uint16_t*)(src + t * LY::QB + tr_src[u]));
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int u = 0; u < TPW; ++u) *(bf16x4*)(dst + t * LY::QB + tr_dst[u]) = x[TPW * t + u];
-    };
-
     if (t_begin < t_end) {
         LT = tile_info(t_begin);
         l_settle();
@@ -223,7 +201,6 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
         wait_vmem();
         __syncthreads();
         put_rowvals(0);
-        transpose_q(0);
         l_issue();
     }
 
@@ -239,7 +216,7 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
             const int p = 64 * (VPW * wave + u) + lane_t;
             const int r = p / CH, cp = p % CH;
             const int key = min(T.n * kBwdBlockN + r, T.L - 1);
-            load_lds16(a.v + kvrow0 + (int64_t)key * rs + 8 * (cp ^ swz_kv<D>(r)),
+            load_lds16(a.v + kvrow0 + (int64_t)key * rs + 8 * (cp ^ swz_vo<D>(r)),
                        smem + LY::V + 1024 * (VPW * wave + u));
         }
         const int key = min(T.n * kBwdBlockN + 32 * wave + (lane_t & 31), T.L - 1);
@@ -260,7 +237,7 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
             const int p = 64 * (VPW * wave + u) + lane_t;
             const int r = p / CH, cp = p % CH;
             const int key = min(T.n * kBwdBlockN + r, T.L - 1);
-            load_lds16(src + kvrow0 + (int64_t)key * rs + 8 * (cp ^ swz_kv<D>(r)),
+            load_lds16(src + kvrow0 + (int64_t)key * rs + 8 * (cp ^ swz_vo<D>(r)),
                        smem + LY::V + 1024 * (VPW * wave + u));
         }
     };
@@ -280,15 +257,11 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
 
         for (int i = 0; i < T.work; ++i, ++s) {
             if (i > 0) wait_vmem();   // block s+1 landed (the only copies in flight)
-            // every wave is past block s-1: its slot and transposed buffer are free
+            // every wave is past block s-1: its slot is free
             __syncthreads();
-            // (past the end of the stream these two work on stale, unread data)
+            // (past the end of the stream this works on stale, unread data)
             put_rowvals(s + 1);
             l_issue();                               // block s+kAhead
-            // Q^T, dO^T of block s+1: here, or (dense) behind the S/dP MFMAs,
-            // where the extra live registers still fit
-            constexpr bool kLateTranspose = MODE == kDense;
-            if (!kLateTranspose) transpose_q(s + 1);
 
             const int rb = q_block(T, i);
             bool skip = !wave_keys, masked = false;
@@ -304,15 +277,10 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
             } else if (MODE == kSparse) {
                 skip = skip || !((ld_uniform(T.sp + (i >> 2)) >> (wave >> 2)) & 1);
             }
-            if (skip) {
-                if (kLateTranspose) transpose_q(s + 1);
-                continue;
-            }
+            if (skip) continue;
             const char* qb = smem + LY::RING + (s % kSlots) * LY::SLOT;
             const char* db = qb + LY::QB;
             const float* rv = (const float*)(qb + LY::ROWV);
-            const char* qt = smem + LY::T + (s & 1) * LY::TBUF;
-            const char* dt = qt + LY::QB;
 
             // dP accumulates onto -delta (row values), so it ends as dP - delta
             f32x16 sc = f32x16{}, dp;
@@ -344,7 +312,6 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             }
-            if (kLateTranspose) transpose_q(s + 1);
             // P and dS; register r is query row 32rb + 8(r/4) + 4hf + r%4, the
             // column this lane's key 32wave + lr (tile-local). Banded: with
             // c = 8(r/4) + r%4, key - row = base - c, visible iff
@@ -384,26 +351,33 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
             }
             // dV^T += dO^T P ; dK^T += Q^T dS over the block's 32 rows
             {
+                // (one address per (t, md), shared by Q and dO)
+                const uint32_t lq = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)qb;
+                uint32_t ta[2][MD];
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int md = 0; md < MD; ++md) ta[t][md] = lq + to_off[t][md];
                 bf16x8 dta[2 * MD], qta[2 * MD];
 #pragma unroll
                 for (int j = 0; j < 2 * MD; ++j) {
-                    const int o = 32 * 64 * (j >> 1) + t_off[j & 1];
-                    dta[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(dt + o));
-                    qta[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qt + o));
+                    const int o = 16 * D * 2 * (j & 1);
+                    dta[j] = concat(lds_read_tr_at(ta[0][j >> 1], LY::QB + o), lds_read_tr_at(ta[1][j >> 1], LY::QB + o));
+                    qta[j] = concat(lds_read_tr_at(ta[0][j >> 1], o), lds_read_tr_at(ta[1][j >> 1], o));
                 }
 #pragma unroll
                 for (int j = 0; j < 2 * MD; ++j) {
                     dv_acc[j >> 1] = mfma32(dta[j], pb[j & 1], dv_acc[j >> 1]);
                     dk_acc[j >> 1] = mfma32(qta[j], sb[j & 1], dk_acc[j >> 1]);
                 }
-                pipeline_reads_mfma<4 * MD, kReadAhead>();
+                pipeline_reads_mfma<4 * MD, kReadAhead, 2>();
             }
         }
 
-        // ---- tile end. Every wave is done with V, with block s-1's ring slot
-        // and with its transposed buffer. dK = scale * (dK^T)^T and dV leave as
-        // bf16 rows through the free slot (waves 4-7) and transposed buffer
-        // (waves 0-3), 16 keys per wave at a time. Meanwhile each wave fetches
+        // ---- tile end. Every wave is done with V and with block s-1's ring
+        // slot. dK = scale * (dK^T)^T and dV leave as bf16 rows through the
+        // free slot (waves 4-7) and the staging area (waves 0-3), 16 keys per
+        // wave at a time. Meanwhile each wave fetches
         // the next tile's K rows into its own V rows with row-contiguous
         // copies (row-strided fragment loads cost the vector memory unit one
         // cache line per key and instruction), reads its K fragments from
@@ -427,8 +401,8 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
         }
         {
             const int64_t kvrow0 = (int64_t)T.kv0 * rs + (int64_t)T.h * D;
-            char* st = wave < 4 ? smem + LY::T + ((s + 1) & 1) * LY::TBUF + wave * (16 * D * 2)
-                                : smem + LY::RING + ((s + kSlots - 1) % kSlots) * LY::SLOT + (wave - 4) * (16 * D * 2);
+            char* st = wave < 4 ? smem + LY::ST + wave * LY::ST_WAVE
+                                : smem + LY::RING + ((s + kSlots - 1) % kSlots) * LY::SLOT + (wave - 4) * LY::ST_WAVE;
             const int lane_e = opaque(lane), lr_e = lane_e & 31, hf_e = lane_e >> 5;
 #pragma unroll
             for (int pass = 0; pass < 4; ++pass) {   // dK keys 0-15, 16-31, then dV

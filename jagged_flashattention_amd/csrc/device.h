@@ -39,6 +39,13 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t* p) {
     s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
     return __builtin_bit_cast(bf16x4, v);
 }
+// The same read at LDS byte address a + imm (imm a compile-time constant, so
+// that it becomes the instruction's offset field).
+__device__ __forceinline__ bf16x4 lds_read_tr_at(uint32_t a, int imm) {
+    typedef __attribute__((address_space(3))) char lds_char;
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_char*)(uintptr_t)a + imm));
+    return __builtin_bit_cast(bf16x4, v);
+}
 
 __device__ __forceinline__ bf16x8 concat(bf16x4 lo, bf16x4 hi) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
