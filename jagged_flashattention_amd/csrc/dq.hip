@@ -23,8 +23,9 @@
 //   S^T  = K Q^T        A = K rows from LDS,   B = Q^T (VGPRs)
 //   dP^T = V dO^T       A = V rows from LDS,   B = dO^T (VGPRs)
 //   P^T  = exp2(S^T * scale*log2e - LSE*log2e), dS^T = P^T (dP^T - delta)
-//   dQ^T += K^T dS^T    A = K^T from LDS (keys in sigma order), B = dS^T
-// K^T is made once per block from the natural K tile by transposed LDS reads.
+//   dQ^T += K^T dS^T    A = K^T: transposed reads of the K rows, B = dS^T
+// (a transposed read of a 16-lane group takes the 4 keys that the lane's dS^T
+// registers hold, in their order, so no transposed copy of K is made).
 #include <algorithm>
 
 #include "qtile.h"
@@ -44,9 +45,8 @@ struct DqLds {
     static constexpr int BLK = kFwdBlockN * D * 2;     // one K or V block (bf16)
     static constexpr int K = 0;                         // kSlots natural K blocks
     static constexpr int V = K + kSlots * BLK;          // kSlots natural V blocks
-    static constexpr int KT = V + kSlots * BLK;         // 2 K^T blocks [D][64]
     static constexpr int RW = 32 * D * 2;               // one wave's 32 dO rows (tile prologue)
-    static constexpr int STG = KT + 2 * BLK;            // stage areas of waves 4-7
+    static constexpr int STG = V + kSlots * BLK;        // stage areas of waves 4-7
     static constexpr int BYTES = STG + 4 * RW;
     static constexpr int ST_WAVE = kStageRows * D * 4;  // fp32 staging of one wave
     static_assert(4 * ST_WAVE == BLK, "staging: 4 waves per released block");
@@ -61,7 +61,6 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
     constexpr int CH = D / 8;               // 16-byte chunks per K/V row
     constexpr int CH4 = D / 4;              // 16-byte chunks per fp32 dQ row
     constexpr int LPW = (kFwdBlockN * CH) / (64 * kWaves);   // K (and V) copies per wave per block
-    constexpr int TPW = (kFwdBlockN * D) / (256 * kWaves);   // transposed reads per wave per block
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -79,18 +78,30 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
         const int p = 64 * (LPW * wave + u) + lane;
         const int r = p / CH, cp = p % CH;
         ld_row[u] = r;
-        ld_g[u] = 8 * (cp ^ swz_kv<D>(r));
+        ld_g[u] = 8 * (cp ^ swz_vo<D>(r));
     }
-    int tr_src[TPW], tr_dst[TPW];
-    transpose_offsets<D, TPW>(wave, lane, [](int r) { return swz_kv<D>(r); }, tr_src, tr_dst);
-    // A operands: K / V row 32mb + lr, chunk 2kc + hf (swz_kv depends on the
-    // row's low 4 bits only); K^T row 32md + lr, 16-key chunk c
+    // A operands: K / V row 32mb + lr, chunk 2kc + hf (swz_vo depends on the
+    // row's low 4 bits only)
     int kv_off[KC];
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) kv_off[kc] = lr * D * 2 + (((2 * kc + hf) ^ swz_kv<D>(lr)) << 4);
-    int kt_off[4];
+    for (int kc = 0; kc < KC; ++kc) kv_off[kc] = lr * D * 2 + (((2 * kc + hf) ^ swz_vo<D>(lr)) << 4);
+    // K^T[32md + lr][keys of 16-key chunk c in sigma order] by two transposed
+    // reads of the natural K rows: read t of this lane's 16-lane group (d
+    // span 32md + 16g .. +15) takes keys 16c + 8t + 4hf + e, e = 0..3, the
+    // keys this lane's dS^T registers 0-3 (t = 0) and 8-11 (t = 1) of chunk c
+    // hold. The swizzle depends on the row modulo 16 only, so chunk c is an
+    // immediate offset of 16 rows.
+    int kt_off[2][MD];
+    {
+        const int n16 = lane & 15, e = n16 >> 2, cq = n16 & 3, g = (lane >> 4) & 1;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) kt_off[c] = lr * 128 + (((2 * c + hf) ^ swz_t(lr)) << 4);
+        for (int t = 0; t < 2; ++t) {
+            const int r = 8 * t + 4 * hf + e;
+#pragma unroll
+            for (int md = 0; md < MD; ++md)
+                kt_off[t][md] = r * D * 2 + (((4 * md + 2 * g + (cq >> 1)) ^ swz_vo<D>(r)) << 4) + 8 * (cq & 1);
+        }
+    }
 
     const int w = worker_id(a.num_workers);
     const int t_begin = ld_uniform(a.worker_ptr + w), t_end = ld_uniform(a.worker_ptr + w + 1);
@@ -130,28 +141,16 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
         ++l_i;
         l_settle();
     };
-    // K (natural, slot s % kSlots) -> K^T (buffer s % 2)
-    auto transpose_k = [&](int s) {
-        const char* src = smem + LY::K + (s % kSlots) * LY::BLK;
-        char* dst = smem + LY::KT + (s & 1) * LY::BLK;
-        bf16x4 x[TPW];
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) x[u] = lds_read_tr((const uint16_t*)(src + tr_src[u]));
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) *(bf16x4*)(dst + tr_dst[u]) = x[u];
-    };
-
     if (t_begin < t_end) {
         LT = tile_info(t_begin);
         l_settle();
     }
     int total = 0;   // stream length
     for (int ti = t_begin; ti < t_end; ++ti) total += ld_uniform(a.tiles + 4 * ti + 3);
-    if (total > 0) {   // block 0 landed and transposed, block 1 in flight
+    if (total > 0) {   // block 0 landed, block 1 in flight
         l_issue();
         wait_vmem();
         __syncthreads();
-        transpose_k(0);
         l_issue();
     }
 
@@ -249,7 +248,7 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
             for (int u = 0; u < NI; ++u) {
                 const int p = 64 * u + lane, r = p / CH, cs = p % CH;
                 const int row = min(row0 + r, Lq - 1);
-                const int64_t g = (int64_t)(orow0 + row) * rs + (int64_t)T.h * D + 8 * (cs ^ swz_kv<D>(r));
+                const int64_t g = (int64_t)(orow0 + row) * rs + (int64_t)T.h * D + 8 * (cs ^ swz_vo<D>(r));
                 load_lds16(a.d_o + g, rg + 1024 * u);
                 ov[u] = load_bf16x8(a.o + g);
             }
@@ -257,7 +256,7 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
             wave_sync_lds();
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc)
-                df[kc] = *(const bf16x8*)(rg + lr * D * 2 + (((2 * kc + hf) ^ swz_kv<D>(lr)) << 4));
+                df[kc] = *(const bf16x8*)(rg + lr * D * 2 + (((2 * kc + hf) ^ swz_vo<D>(lr)) << 4));
             float dsum[NI];
 #pragma unroll
             for (int u = 0; u < NI; ++u) {
@@ -312,10 +311,9 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
 
         for (int i = 0; i < T.work; ++i, ++s) {
             if (i > 0) wait_vmem();   // block s+1 landed (the only copies in flight)
-            // every wave is past block s-1: its slots and K^T buffer are free
+            // every wave is past block s-1: its slots are free
             __syncthreads();
             l_issue();                              // block s+kAhead
-            if (s + 1 < total) transpose_k(s + 1);  // K^T of block s+1
 
             const int n = seq_block<MODE>(T, T.k0 + i);
             bool skip, masked;
@@ -323,7 +321,6 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
             if (skip) continue;
             const char* kb = smem + LY::K + (s % kSlots) * LY::BLK;
             const char* vb = smem + LY::V + (s % kSlots) * LY::BLK;
-            const char* ktb = smem + LY::KT + (s & 1) * LY::BLK;
             // the block in two halves of 32 keys (hb)
 #pragma unroll
             for (int hb = 0; hb < 2; ++hb) {
@@ -371,12 +368,14 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
                 {
                     bf16x8 kt[2 * MD];
 #pragma unroll
-                    for (int j = 0; j < 2 * MD; ++j)
-                        kt[j] = __builtin_bit_cast(
-                            bf16x8, *(const u32x4*)(ktb + 32 * 128 * (j >> 1) + kt_off[2 * hb + (j & 1)]));
+                    for (int j = 0; j < 2 * MD; ++j) {
+                        const char* rows = kb + 16 * D * 2 * (2 * hb + (j & 1));
+                        kt[j] = concat(lds_read_tr((const uint16_t*)(rows + kt_off[0][j >> 1])),
+                                       lds_read_tr((const uint16_t*)(rows + kt_off[1][j >> 1])));
+                    }
 #pragma unroll
                     for (int j = 0; j < 2 * MD; ++j) acc[j >> 1] = mfma32(kt[j], db[j & 1], acc[j >> 1]);
-                    pipeline_reads_mfma<2 * MD, kReadAhead>();
+                    pipeline_reads_mfma<2 * MD, kReadAhead, 2>();
                 }
             }
         }
