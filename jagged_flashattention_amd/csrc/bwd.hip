@@ -72,26 +72,14 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
     // A operands: Q / dO row lr, chunk 2kc + hf; the V rows (B operand) of
     // this wave's keys use the same pattern 32 rows further per wave
     // (2kc + hf) ^ x = 2 (kc ^ x/2) + ((hf ^ x) & 1): one base and one XOR mask
-    const int ro_x = swz_vo<D>(lr);
+    const int ro_x = swz_rt<D>(lr);
     const int ro_base = lr * D * 2 + (((hf ^ ro_x) & 1) << 4), ro_xh = ro_x >> 1;
     auto row_off = [&](int kc) { return ro_base + ((kc ^ ro_xh) << 5); };
-    // Q^T / dO^T [32md + lr][rows of chunk c in sigma order] by two
-    // transposed reads of the natural rows: read t of this lane's 16-lane
-    // group (d span 32md + 16g .. +15) takes rows 16c + 8t + 4hf + e, e =
-    // 0..3, the rows this lane's P / dS registers 0-3 (t = 0) and 8-11
-    // (t = 1) of chunk c hold. The swizzle depends on the row modulo 16 only,
-    // so chunk c (and dO's place after Q in the slot) is an immediate offset.
+    // Q^T / dO^T [32md + lr][rows of chunk c, in P's and dS's order]: two
+    // transposed reads of the natural rows (chunk c and dO's place after Q in
+    // the slot are immediate offsets)
     int to_off[2][MD];
-    {
-        const int n16 = lane & 15, e = n16 >> 2, cq = n16 & 3, g = (lane >> 4) & 1;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int r = 8 * t + 4 * hf + e;
-#pragma unroll
-            for (int md = 0; md < MD; ++md)
-                to_off[t][md] = r * D * 2 + (((4 * md + 2 * g + (cq >> 1)) ^ swz_vo<D>(r)) << 4) + 8 * (cq & 1);
-        }
-    }
+    tr_operand_offsets<D>(lane, to_off);
 
     const int w = worker_id(a.num_workers);
     const int t_begin = ld_uniform(a.worker_ptr + w), t_end = ld_uniform(a.worker_ptr + w + 1);
@@ -165,7 +153,7 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
             const int p = 64 * (g % QH) + lane;
             const int r = p / CH, cp = p % CH;
             const int qi = min(kBwdBlockM * rb + r, LT.Lq - 1);
-            const int64_t off = hq + 8 * (cp ^ swz_vo<D>(r));
+            const int64_t off = hq + 8 * (cp ^ swz_rt<D>(r));
             const uint16_t* src = is_do ? a.d_o + (int64_t)(LT.orow0 + qi) * rs + off
                                         : a.q + (int64_t)(LT.q0 + qi) * rs + off;
             load_lds16(src, dst + (is_do ? LY::QB : 0) + 1024 * (g % QH));
@@ -216,7 +204,7 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
             const int p = 64 * (VPW * wave + u) + lane_t;
             const int r = p / CH, cp = p % CH;
             const int key = min(T.n * kBwdBlockN + r, T.L - 1);
-            load_lds16(a.v + kvrow0 + (int64_t)key * rs + 8 * (cp ^ swz_vo<D>(r)),
+            load_lds16(a.v + kvrow0 + (int64_t)key * rs + 8 * (cp ^ swz_rt<D>(r)),
                        smem + LY::V + 1024 * (VPW * wave + u));
         }
         const int key = min(T.n * kBwdBlockN + 32 * wave + (lane_t & 31), T.L - 1);
@@ -237,7 +225,7 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
             const int p = 64 * (VPW * wave + u) + lane_t;
             const int r = p / CH, cp = p % CH;
             const int key = min(T.n * kBwdBlockN + r, T.L - 1);
-            load_lds16(src + kvrow0 + (int64_t)key * rs + 8 * (cp ^ swz_vo<D>(r)),
+            load_lds16(src + kvrow0 + (int64_t)key * rs + 8 * (cp ^ swz_rt<D>(r)),
                        smem + LY::V + 1024 * (VPW * wave + u));
         }
     };

@@ -70,7 +70,7 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
 
     // direct-to-LDS copy: copy u of this wave fills chunk positions
     // 64 (LPW wave + u) + lane of a block: key r, stored chunk cp. K and V
-    // share the swizzle that serves both the operand reads and the
+    // share the swizzle that serves both the operand reads and (K) the
     // transposed reads.
     int ld_row[LPW], ld_g[LPW];
 #pragma unroll
@@ -78,30 +78,17 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
         const int p = 64 * (LPW * wave + u) + lane;
         const int r = p / CH, cp = p % CH;
         ld_row[u] = r;
-        ld_g[u] = 8 * (cp ^ swz_vo<D>(r));
+        ld_g[u] = 8 * (cp ^ swz_rt<D>(r));
     }
-    // A operands: K / V row 32mb + lr, chunk 2kc + hf (swz_vo depends on the
+    // A operands: K / V row 32mb + lr, chunk 2kc + hf (swz_rt depends on the
     // row's low 4 bits only)
     int kv_off[KC];
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) kv_off[kc] = lr * D * 2 + (((2 * kc + hf) ^ swz_vo<D>(lr)) << 4);
-    // K^T[32md + lr][keys of 16-key chunk c in sigma order] by two transposed
-    // reads of the natural K rows: read t of this lane's 16-lane group (d
-    // span 32md + 16g .. +15) takes keys 16c + 8t + 4hf + e, e = 0..3, the
-    // keys this lane's dS^T registers 0-3 (t = 0) and 8-11 (t = 1) of chunk c
-    // hold. The swizzle depends on the row modulo 16 only, so chunk c is an
-    // immediate offset of 16 rows.
+    for (int kc = 0; kc < KC; ++kc) kv_off[kc] = lr * D * 2 + (((2 * kc + hf) ^ swz_rt<D>(lr)) << 4);
+    // K^T[32md + lr][keys of 16-key chunk c, in dS^T's order]: two transposed
+    // reads of the natural K rows
     int kt_off[2][MD];
-    {
-        const int n16 = lane & 15, e = n16 >> 2, cq = n16 & 3, g = (lane >> 4) & 1;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int r = 8 * t + 4 * hf + e;
-#pragma unroll
-            for (int md = 0; md < MD; ++md)
-                kt_off[t][md] = r * D * 2 + (((4 * md + 2 * g + (cq >> 1)) ^ swz_vo<D>(r)) << 4) + 8 * (cq & 1);
-        }
-    }
+    tr_operand_offsets<D>(lane, kt_off);
 
     const int w = worker_id(a.num_workers);
     const int t_begin = ld_uniform(a.worker_ptr + w), t_end = ld_uniform(a.worker_ptr + w + 1);
@@ -248,7 +235,7 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
             for (int u = 0; u < NI; ++u) {
                 const int p = 64 * u + lane, r = p / CH, cs = p % CH;
                 const int row = min(row0 + r, Lq - 1);
-                const int64_t g = (int64_t)(orow0 + row) * rs + (int64_t)T.h * D + 8 * (cs ^ swz_vo<D>(r));
+                const int64_t g = (int64_t)(orow0 + row) * rs + (int64_t)T.h * D + 8 * (cs ^ swz_rt<D>(r));
                 load_lds16(a.d_o + g, rg + 1024 * u);
                 ov[u] = load_bf16x8(a.o + g);
             }
@@ -256,7 +243,7 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
             wave_sync_lds();
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc)
-                df[kc] = *(const bf16x8*)(rg + lr * D * 2 + (((2 * kc + hf) ^ swz_vo<D>(lr)) << 4));
+                df[kc] = *(const bf16x8*)(rg + lr * D * 2 + (((2 * kc + hf) ^ swz_rt<D>(lr)) << 4));
             float dsum[NI];
 #pragma unroll
             for (int u = 0; u < NI; ++u) {

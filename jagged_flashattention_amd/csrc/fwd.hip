@@ -123,31 +123,16 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
         const int r = p / CH, cp = p % CH;
         ld_row[u] = r;
         ld_gk[u] = 8 * (cp ^ swz_k<D>(r));
-        ld_gv[u] = 8 * (cp ^ swz_vo<D>(r));
+        ld_gv[u] = 8 * (cp ^ swz_rt<D>(r));
     }
     // S^T operand: K row 32mb + lr, chunk 2kc + hf (swz_k(32mb + lr) == swz_k(lr))
     int k_off[KC];
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) k_off[kc] = lr * D * 2 + (((2 * kc + hf) ^ swz_k<D>(lr)) << 4);
-    // O^T operand V^T[32md + lr][keys of chunk c in sigma order], read from
-    // the natural V block by two transposed reads: read t of this lane's
-    // 16-lane group (d span 32md + 16g .. +15) takes rows 16c + 8t + 4hf + e,
-    // e = 0..3 (lanes 4e .. 4e+3 address row e, 8 bytes each), so the lane
-    // gets keys 16c + 8t + 4hf + 0..3 of its d: with t = 0, 1 the keys its
-    // P^T B operand holds (registers 0-3 and 8-11 of a lane half's column).
-    // The swizzle depends on the row modulo 16 only, so chunk c is an
-    // immediate offset of 16 rows.
+    // O^T operand V^T[32md + lr][keys of chunk c, in P^T's order]: two
+    // transposed reads of the natural V block
     int vo_off[2][MD];
-    {
-        const int n16 = lane & 15, e = n16 >> 2, cq = n16 & 3, g = (lane >> 4) & 1;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int r = 8 * t + 4 * hf + e;
-#pragma unroll
-            for (int md = 0; md < MD; ++md)
-                vo_off[t][md] = r * D * 2 + (((4 * md + 2 * g + (cq >> 1)) ^ swz_vo<D>(r)) << 4) + 8 * (cq & 1);
-        }
-    }
+    tr_operand_offsets<D>(lane, vo_off);
 
     const int w = worker_id(a.num_workers);
     const int t_begin = ld_uniform(a.worker_ptr + w), t_end = ld_uniform(a.worker_ptr + w + 1);

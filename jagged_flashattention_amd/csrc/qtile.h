@@ -22,38 +22,40 @@ static_assert(kFwdBlockM == 32 * kWaves && kFwdBlockN == 64, "Q-tile geometry");
 // reads, 32 for 8-byte ones):
 //  - swz_k: rows read as 32x32x16 MFMA A operands (16 lanes = 16 rows, one
 //    16-byte chunk each);
-//  - swz_v: rows read by transposed reads (a 16-lane group reads 4 rows x 32
-//    bytes; the two groups of a half wave read rows r and r + 8);
-//  - swz_kv: both uses at once (swz_v plus bit 2 of the row);
-//  - swz_t: [d][64 keys] transposed tiles (128-byte rows) read as A operands;
-//  - swz_vo: rows read by transposed reads as 32x32x16 A operands with d on
-//    the lanes (a half wave reads 4 consecutive rows x 64 bytes: the 4 rows
-//    of a quad must land in different 64-byte quarters of the bank space).
+//  - swz_rt: rows read that way and also by the transposed reads of
+//    tr_operand_offsets (a half wave reads 4 consecutive rows x 64 bytes):
+//    a bijection on every 16 rows, with rows 4q .. 4q+3 in different
+//    64-byte quarters of the bank space (D = 128: row mod 4 in bits 2-3; D =
+//    64, two rows per 256 bytes: rows 4q and 4q + 2 differ in bit 2).
 template <int D>
 __device__ __forceinline__ int swz_k(int r) {
     return D == 128 ? (r & 15) : ((r >> 1) & 7);
 }
 template <int D>
-__device__ __forceinline__ int swz_v(int r) {
-    return D == 128 ? 2 * ((r & 3) + 4 * ((r >> 3) & 1)) : 2 * (((r >> 1) & 1) + 2 * ((r >> 3) & 1));
-}
-template <int D>
-__device__ __forceinline__ int swz_kv(int r) {
-    return swz_v<D>(r) + ((r >> 2) & 1);
-}
-__device__ __forceinline__ int swz_t(int d) { return (d >> 1) & 7; }
-template <int D>
-__device__ __forceinline__ int swz_vo(int r) {
+__device__ __forceinline__ int swz_rt(int r) {
     return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 
-// position of key q (within its group of 16) in sigma order 0-3, 8-11, 4-7,
-// 12-15: the order in which a 32x32 accumulator column holds its 16 rows
-// once they are fed back as a B operand (register r of lane half h holds row
-// 8(r/4) + 4h + r%4)
-__device__ __forceinline__ int sigma_pos(int q) {
-    const int g = (q >> 2) & 3;
-    return (q & ~15) | (((g >> 1) | ((g & 1) << 1)) << 2) | (q & 3);
+// Offsets (within a tile of natural [rows][D] bf16 rows swizzled by swz_rt)
+// of the transposed reads (ds_read_b64_tr_b16) that give the 32x32x16 A
+// operand X^T[32md + lr][16 rows of chunk c] of a product whose B operand is
+// an accumulator fed back: register r of lane half h holds row 8(r/4) + 4h +
+// r%4 of its 32, so B's 8 values of chunk c in half h are rows 16c + 4h +
+// {0-3, 8-11}, and A must hold the same rows in the same order. Read t (t =
+// 0, 1) of this lane's 16-lane group (d span 32md + 16g .. +15) addresses
+// rows 16c + 8t + 4h + e, e = 0..3 (lanes 4e .. 4e+3 point at row e, 8
+// bytes each); the lane receives its own d at those 4 rows. The swizzle
+// depends on the row modulo 16 only, so chunk c adds an immediate 16c rows.
+template <int D>
+__device__ __forceinline__ void tr_operand_offsets(int lane, int (&off)[2][D / 32]) {
+    const int n16 = lane & 15, e = n16 >> 2, cq = n16 & 3, g = (lane >> 4) & 1, h = lane >> 5;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int r = 8 * t + 4 * h + e;
+#pragma unroll
+        for (int md = 0; md < D / 32; ++md)
+            off[t][md] = r * D * 2 + (((4 * md + 2 * g + (cq >> 1)) ^ swz_rt<D>(r)) << 4) + 8 * (cq & 1);
+    }
 }
 
 // Direct-to-LDS copy of 16 bytes per lane: lane l's bytes at g land at
@@ -150,26 +152,6 @@ __device__ __forceinline__ void block_flags(const TileInfo& T, int i, int n, int
     } else {
         masked = kFwdBlockN * (n + 1) > T.L;
         if (MODE == kSparse) skip = skip || !((ld_uniform(T.sp + (i >> 1)) >> (wave >> 2)) & 1);
-    }
-}
-
-// Addresses of the transposition of a natural [64 keys][D] tile into a
-// [D][64] tile with keys in sigma order, by 16-lane transposed reads: per read
-// u of this wave, the source offset (rows swizzled by SWZ) and the
-// destination offset (rows swizzled by swz_t).
-template <int D, int TPW, typename SWZ>
-__device__ __forceinline__ void transpose_offsets(int wave, int lane, SWZ swz, int (&src)[TPW],
-                                                  int (&dst)[TPW]) {
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-        const int P = 2 * (TPW * wave + u) + (lane >> 5);
-        const int dg = P >> 3, s = (P >> 1) & 3, z = P & 1;
-        const int kq = 4 * s + z + 2 * ((lane >> 4) & 1);   // key quad of this 16-lane group
-        const int n16 = lane & 15, e = n16 >> 2, c = n16 & 3;
-        const int r = 4 * kq + e;
-        src[u] = r * D * 2 + (((2 * dg + (c >> 1)) ^ swz(r)) << 4) + 8 * (c & 1);
-        const int d = 16 * dg + n16, pos = sigma_pos(4 * kq);
-        dst[u] = d * 128 + (((pos >> 3) ^ swz_t(d)) << 4) + 2 * (pos & 7);
     }
 }
 
