@@ -44,11 +44,10 @@ struct DkdvLds {
     static constexpr int ROWV = 2 * QB;                       // LSE*log2e [32], delta [32] fp32
     static constexpr int SLOT = 2 * QB + 512;                 // Q, dO, row values
     static constexpr int RING = 0;                            // kSlots slots
-    static constexpr int ST = RING + kSlots * SLOT;           // epilogue staging, waves 0-3
+    static constexpr int ST = RING + kSlots * SLOT;           // epilogue staging, one area per wave
     static constexpr int ST_WAVE = 16 * D * 2;                // 16 rows of one wave
-    static constexpr int V = ST + 4 * ST_WAVE;                // V tile [256][D]
+    static constexpr int V = ST + kWaves * ST_WAVE;           // V tile [256][D]
     static constexpr int BYTES = V + kBwdBlockN * D * 2;
-    static_assert(4 * ST_WAVE <= SLOT, "waves 4-7 stage in a released ring slot");
 };
 
 template <int D, int MODE, bool BCAST>
@@ -362,18 +361,18 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
             }
         }
 
-        // ---- tile end. Every wave is done with V and with block s-1's ring
-        // slot. dK = scale * (dK^T)^T and dV leave as bf16 rows through the
-        // free slot (waves 4-7) and the staging area (waves 0-3), 16 keys per
-        // wave at a time. Meanwhile each wave fetches
-        // the next tile's K rows into its own V rows with row-contiguous
-        // copies (row-strided fragment loads cost the vector memory unit one
-        // cache line per key and instruction), reads its K fragments from
-        // there once dK is out, and then fetches the next V rows in their
-        // place while dV leaves.
+        // ---- tile end, wave by wave: a wave's V rows, K rows and staging area
+        // are its own, so no workgroup barrier is needed here (the next
+        // block's barrier orders the ring). dK = scale * (dK^T)^T and dV leave
+        // as bf16 rows through the wave's staging area, 16 keys at a time.
+        // Meanwhile the wave fetches the next tile's K rows into its own V
+        // rows with row-contiguous copies (row-strided fragment loads cost the
+        // vector memory unit one cache line per key and instruction; the V
+        // reads of its last block were consumed by its dP products), reads
+        // its K fragments from there once dK is out, and then fetches the
+        // next V rows in their place while dV leaves.
         // (The banded mode keeps the direct K loads: the staged form spills
         // there.)
-        __syncthreads();
         if (kTileLog && a.tile_log != nullptr) {
             const int fl = (T.b < 0 || T.b >= a.batch ? kLogBadBatch : 0) |
                            (T.h < 0 || T.h >= H ? kLogBadHead : 0) |
@@ -389,8 +388,7 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
         }
         {
             const int64_t kvrow0 = (int64_t)T.kv0 * rs + (int64_t)T.h * D;
-            char* st = wave < 4 ? smem + LY::ST + wave * LY::ST_WAVE
-                                : smem + LY::RING + ((s + kSlots - 1) % kSlots) * LY::SLOT + (wave - 4) * LY::ST_WAVE;
+            char* st = smem + LY::ST + wave * LY::ST_WAVE;
             const int lane_e = opaque(lane), lr_e = lane_e & 31, hf_e = lane_e >> 5;
 #pragma unroll
             for (int pass = 0; pass < 4; ++pass) {   // dK keys 0-15, 16-31, then dV
@@ -433,9 +431,8 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
                 wave_sync_lds();
             }
         }
-        // the next tile's V and K landed (and this tile's stores are done)
+        // this wave's next V and K rows landed (and its stores are done)
         wait_vmem();
-        __syncthreads();
     }
 }
 
