@@ -46,10 +46,10 @@ struct DqLds {
     static constexpr int K = 0;                         // kSlots natural K blocks
     static constexpr int V = K + kSlots * BLK;          // kSlots natural V blocks
     static constexpr int RW = 32 * D * 2;               // one wave's 32 dO rows (tile prologue)
-    static constexpr int STG = V + kSlots * BLK;        // stage areas of waves 4-7
-    static constexpr int BYTES = STG + 4 * RW;
+    static constexpr int STG = V + kSlots * BLK;        // a stage area per wave
+    static constexpr int BYTES = STG + kWaves * RW;
     static constexpr int ST_WAVE = kStageRows * D * 4;  // fp32 staging of one wave
-    static_assert(4 * ST_WAVE == BLK, "staging: 4 waves per released block");
+    static_assert(ST_WAVE <= RW, "dQ staging fits the wave's stage area");
 };
 
 template <int D, int MODE, bool BCAST, bool ATOMIC>
@@ -147,13 +147,11 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
 #pragma unroll
     for (int md = 0; md < MD; ++md) acc[md] = f32x16{};
 
-    // fp32 rows of scale * dQ through this wave's staging area (in the K or V
-    // slot of block s-1, free once every wave is past that block), handed to
-    // store(row, chunk, value) as 16-byte chunks: 4 rows x 256 bytes per
-    // instruction
-    auto stage_out = [&](int s_next, auto store) {
-        char* st = wave < 4 ? smem + LY::K + ((s_next + kSlots - 1) % kSlots) * LY::BLK + wave * LY::ST_WAVE
-                            : smem + LY::V + ((s_next + kSlots - 1) % kSlots) * LY::BLK + (wave - 4) * LY::ST_WAVE;
+    // fp32 rows of scale * dQ through this wave's own stage area (no
+    // workgroup barrier needed), handed to store(row, chunk, value) as
+    // 16-byte chunks: 4 rows x 256 bytes per instruction
+    auto stage_out = [&](auto store) {
+        char* st = smem + LY::STG + wave * LY::RW;
 #pragma unroll
         for (int rd = 0; rd < 32 / kStageRows; ++rd) {
             if ((lr >> 3) == rd) {
@@ -214,21 +212,12 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
             // dO and O of the wave's 32 rows, fetched with row-contiguous
             // copies (row-strided dO^T fragment loads cost the vector memory
             // unit one cache line per row and instruction): dO into the
-            // wave's stage area (the K or V slot of block s-1, free once every
-            // wave is past it, or the spare area), O into registers in the
-            // same layout. The dO^T fragments are then read from LDS, and
+            // wave's own stage area, O into registers in the same layout. The dO^T fragments are then read from LDS, and
             // delta is formed in the copy layout, summed over the lanes of a
             // row and handed to the fragment lanes through LDS. (Per-sequence
             // Q keeps the direct loads below: its extra live Q rows would
             // spill.)
-            __syncthreads();
-            char* rg;
-            {
-                const int fs = (s + kSlots - 1) % kSlots;
-                rg = wave < 2 ? smem + LY::K + fs * LY::BLK + wave * LY::RW
-                     : wave < 4 ? smem + LY::V + fs * LY::BLK + (wave - 2) * LY::RW
-                                : smem + LY::STG + (wave - 4) * LY::RW;
-            }
+            char* rg = smem + LY::STG + wave * LY::RW;
             constexpr int NI = 32 * CH / 64;   // 16-byte copies per lane
             bf16x8 ov[NI];
 #pragma unroll
@@ -369,10 +358,9 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
 
         if (!BCAST) {
             // dQ rows of this tile: dq_accum (fp32) and dq (bf16)
-            __syncthreads();
             if (wave_rows) {
                 const int64_t base = (int64_t)T.h * D;
-                stage_out(s, [&](int r, int chunk, const f32x4& x) {
+                stage_out([&](int r, int chunk, const f32x4& x) {
                     const int row = T.t * kFwdBlockM + r;
                     if (row < Lq) {
                         const int64_t g = (int64_t)(q0 + row) * rs + base + 4 * chunk;
@@ -394,11 +382,10 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
         // this worker's sum over its tiles (all of one (head, Q tile) group)
         // added into dq_accum, element by element, with fp32 atomic adds (a
         // worker without tiles adds nothing)
-        __syncthreads();
         if (t_begin < t_end) {
             const TileInfo T0 = tile_info(t_begin);
             float* acc0 = a.dq_accum + (int64_t)T0.h * D;
-            stage_out(s, [&](int r, int chunk, const f32x4& x) {
+            stage_out([&](int r, int chunk, const f32x4& x) {
                 const int row = T0.t * kFwdBlockM + r;
                 if (row < a.lq) {
                     float* p = acc0 + (int64_t)row * H * D + 4 * chunk;
@@ -412,9 +399,8 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
         // this worker's partial sum over its tiles (all of one (head, Q tile)
         // group): rows 0..255 of the tile, fp32 (zeros for a worker without
         // tiles, so that the reduce reads every partial unconditionally)
-        __syncthreads();
         float* part = a.partial + (int64_t)w * kFwdBlockM * D;
-        stage_out(s, [&](int r, int chunk, const f32x4& x) {
+        stage_out([&](int r, int chunk, const f32x4& x) {
             *(f32x4*)(part + (int64_t)r * D + 4 * chunk) = x;
         });
     }
