@@ -77,21 +77,20 @@ struct FwdLds {
 };
 
 // MXFP8 (D = 128): E4M3 K/V blocks are half the size; their scales ride
-// along (K: 4 bytes per key, V: 2 x 128 bytes per 64-key block); V^T is made
-// by a byte transposition in LDS (block j+1 at block j, so the V ring holds
-// blocks j+1 .. j+kAhead); O has a staging area of its own.
+// along (K: 4 bytes per key, V: 2 x 128 bytes per 64-key block); the V^T
+// operands are byte-transposed reads of the natural V block; O has a staging
+// area of its own.
 template <int D>
 struct FwdLds<D, true> {
-    static constexpr int VSLOTS = kAhead;
-    static constexpr int BLK = kFwdBlockN * D;                 // one E4M3 K, V or V^T block
+    static constexpr int VSLOTS = kAhead + 1;
+    static constexpr int BLK = kFwdBlockN * D;                 // one E4M3 K or V block
     static constexpr int SC = 256;                              // its scales
     static constexpr int K = 0;                                 // kKSlots K blocks [64][128]
     static constexpr int KS = K + kKSlots * BLK;                // kKSlots K scales [64][4]
     static constexpr int V = KS + kKSlots * SC;                 // VSLOTS V blocks [64][128]
     static constexpr int VS = V + VSLOTS * BLK;                 // kKSlots V scales [2][128]
-    static constexpr int VT = VS + kKSlots * SC;                // 2 V^T blocks [128][64]
     static constexpr int OST_WAVE = kStageRows * D * 2;
-    static constexpr int OST = VT + 2 * BLK;                    // O staging, kWaves areas
+    static constexpr int OST = VS + kKSlots * SC;               // O staging, kWaves areas
     static constexpr int CLAIM = OST + kWaves * OST_WAVE;
     static constexpr int QUEUE = CLAIM + 2 * 64 * 4;
     static constexpr int BYTES = QUEUE + kWaves * 8 * 4;
@@ -276,7 +275,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
             const int key = min(kFwdBlockN * n + r, LT.L - 1);
             const int64_t row = base + (int64_t)key * rs;
             load_lds16((const uint16_t*)(a.k8 + row + 16 * (cs ^ swz_k8(r))), kdst + 1024 * wave);
-            load_lds16((const uint16_t*)(a.v8 + row + 16 * cs), vdst + 1024 * wave);
+            load_lds16((const uint16_t*)(a.v8 + row + 16 * (cs ^ swz_v8(r))), vdst + 1024 * wave);
             if (wave == 0) {
                 const int kk = min(kFwdBlockN * n + lane, LT.L - 1);
                 load_lds4(a.k_sc + ((int64_t)LT.h * a.total_kv + LT.kv0 + kk) * 4,
@@ -301,19 +300,15 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
         ++l_slot;
         ++l_i;
     };
-    // MXFP8: V (natural, slot s % kVSlots) -> V^T (buffer s % 2)
-    auto transpose_v = [&](int s) {
-        if constexpr (MX)
-            mx_transpose_v(smem + LY::V + (s % kVSlots) * LY::BLK, smem + LY::VT + (s & 1) * LY::BLK, tid);
-    };
+    // MXFP8: this lane's offsets of the byte-transposed V^T reads
+    int mx_vo[4];
+    if constexpr (MX) mx_tr_offsets(lane, mx_vo);
 
-    // prologue: block 0 landed (MXFP8: and transposed), blocks 1 .. kAhead-1
-    // in flight
+    // prologue: block 0 landed, blocks 1 .. kAhead-1 in flight
     l_issue();
     if (l_slot > 0) {
         wait_vmem();
         __syncthreads();
-        transpose_v(0);
 #pragma unroll
         for (int k = 1; k < kAhead; ++k) l_issue();
     }
@@ -416,12 +411,10 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
                 else wait_vmem_keep<2>();
             }
             publish();
-            // every wave is past block s-1: its K and V slots (MXFP8: its
-            // V^T buffer) are free
+            // every wave is past block s-1: its K and V slots are free
             __syncthreads();
             receive();
             l_issue();                                // block s+kAhead
-            if (MX && l_slot > s + 1) transpose_v(s + 1);   // MXFP8: V^T of block s+1
 
             const int n = seq_block(T, i);
             bool skip, masked;
@@ -480,7 +473,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
                         }
                     const i32x8 pb8 = mx_pack_p(sc);
                     l_run = l_run * alpha + ls;
-                    mx_pv(oacc, pb8, smem + LY::VT + (s & 1) * LY::BLK,
+                    mx_pv_tr(oacc, pb8, smem + LY::V + (s % kVSlots) * LY::BLK, mx_vo,
                           smem + LY::VS + (s % kKSlots) * LY::SC, kP8Scale, lr, hf);
                 } else {
                     // The running max moves (and O^T and l are rescaled) only

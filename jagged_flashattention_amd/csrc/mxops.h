@@ -14,6 +14,11 @@ namespace mxops {
 // c ^ ((d >> 2) & 3).
 __device__ __forceinline__ int swz_k8(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int swz_vt8(int d) { return (d >> 2) & 3; }
+// A natural [64 keys][128 d] block read by mx_pv_tr: chunk c of key r at
+// c ^ swz_v8(r). A half wave's transposed reads take 8 keys x 32 bytes
+// (keys 16h + 0-3 and 8-11, or 4-7 and 12-15); the even (odd) keys among them
+// then sit in 4 different 32-byte spans of a 256-byte bank period.
+__device__ __forceinline__ int swz_v8(int r) { return 2 * ((r >> 1) & 1) + 4 * ((r >> 3) & 1); }
 constexpr int kP8Scale = 127 - 8;   // E8M0 code of P's block scale 2^-8
 
 // S^T = K Q^T of a block's two 32-key tiles. Lane (key 32mb + lr, half hf),
@@ -100,6 +105,41 @@ __device__ __forceinline__ void mx_pv(f32x16 (&oacc)[4], const i32x8& pb, const 
         const u32x4 hi = *(const u32x4*)(row + 16 * ((2 + hf) ^ swz_vt8(d)));
         const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                           (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        const int vs = *(const uint8_t*)(vsb + hf * 128 + d);
+        oacc[md] = mfma_mx(av, pb, vs, bsc, oacc[md]);
+    }
+}
+
+// mx_pv with the V^T operands read straight from the natural V block (keys
+// swizzled by swz_v8) by byte-transposed reads (ds_read_b64_tr_b8: lanes 2e,
+// 2e+1 of a 16-lane group address row e, 8 bytes each, and lane i receives
+// byte i of the 8 rows). Lane (d = 32md + lr, half hf) needs keys 16hf +
+// (0-3, 8-11, 4-7, 12-15) and the same + 32: four reads of 8 keys, at rows
+// 16hf + (0-3, 8-11) + {0, 4, 32, 36}. vo[md] is this lane's offset of the
+// first read (mx_tr_offsets); the others add 4, 32 and 36 rows.
+__device__ __forceinline__ void mx_tr_offsets(int lane, int (&vo)[4]) {
+    const int n16 = lane & 15, e = n16 >> 1, g = (lane >> 4) & 1, hf = lane >> 5;
+    const int r = 16 * hf + (e < 4 ? e : e + 4);
+#pragma unroll
+    for (int md = 0; md < 4; ++md) vo[md] = r * 128 + (((2 * md + g) ^ swz_v8(r)) << 4) + 8 * (n16 & 1);
+}
+__device__ __forceinline__ void mx_pv_tr(f32x16 (&oacc)[4], const i32x8& pb, const char* vb,
+                                         const int (&vo)[4], const char* vsb, int bsc, int lr, int hf) {
+    typedef int v2i32 __attribute__((vector_size(8)));
+    typedef __attribute__((address_space(3))) v2i32 lds_v2i32;
+    typedef __attribute__((address_space(3))) const char lds_char;
+    const uint32_t base = (uint32_t)(uintptr_t)(lds_char*)vb;
+#pragma unroll
+    for (int md = 0; md < 4; ++md) {
+        const int d = 32 * md + lr;
+        v2i32 x[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            constexpr int rows[4] = {0, 4, 32, 36};
+            x[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (lds_v2i32*)((lds_char*)(uintptr_t)(base + vo[md]) + 128 * rows[t]));
+        }
+        const i32x8 av = {x[0][0], x[0][1], x[1][0], x[1][1], x[2][0], x[2][1], x[3][0], x[3][1]};
         const int vs = *(const uint8_t*)(vsb + hf * 128 + d);
         oacc[md] = mfma_mx(av, pb, vs, bsc, oacc[md]);
     }
