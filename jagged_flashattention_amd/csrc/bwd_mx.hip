@@ -22,8 +22,9 @@
 //                     is clamped
 // A 32-row block fills one of the two 32-element scale blocks of the 64-long
 // contraction of the scaled MFMA; the other is zero. The dO^T and Q^T
-// operands are made once per block for all waves by a byte transposition in
-// LDS. P = exp2(S c - LSE c) and dS = P (dP - delta) stay fp32; dK and dV
+// operands are byte-transposed LDS reads (ds_read_b64_tr_b8) of the Q and dO
+// blocks encoded along rows, which the slot holds back to back as one 64-row
+// block (Q rows, then dO rows), swizzled by swz_v8. P = exp2(S c - LSE c) and dS = P (dP - delta) stay fp32; dK and dV
 // accumulate in fp32 and leave as bf16.
 #include <climits>
 
@@ -57,9 +58,7 @@ struct DkdvMxLds {
     static constexpr int ROWV = DRS + 128;           // LSE*log2e [32], delta [32] fp32
     static constexpr int SLOT = ROWV + 256;
     static constexpr int RING = 0;
-    static constexpr int T = RING + kSlots * SLOT;   // 2 x [128 d][64]: Q^T | dO^T columns
-    static constexpr int TBUF = 2 * QB;
-    static constexpr int V = T + 2 * TBUF;           // V tile along d [256][128] (swz_k8);
+    static constexpr int V = RING + kSlots * SLOT;   // V tile along d [256][128] (swz_k8);
     static constexpr int VS = V + kBwdBlockN * D;    // it stages dK/dV at a tile end
     static constexpr int K = VS + kBwdBlockN * 4;    // K tile along d [256][128] (swz_k8)
     static constexpr int KS = K + kBwdBlockN * D;
@@ -166,8 +165,8 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_mx_kernel(BwdArgs a) {
             const uint8_t* src;
             if (tensor == 0) src = a.q8 + (int64_t)(LT.q0 + qi) * rs + hq + 16 * (pos ^ swz_k8(r));
             else if (tensor == 1) src = a.do8 + (int64_t)(LT.orow0 + qi) * rs + hq + 16 * (pos ^ swz_k8(r));
-            else if (tensor == 2) src = a.qr8 + (int64_t)(LT.q0 + qi) * rs + hq + 16 * pos;
-            else src = a.dor8 + (int64_t)(LT.orow0 + qi) * rs + hq + 16 * pos;
+            else if (tensor == 2) src = a.qr8 + (int64_t)(LT.q0 + qi) * rs + hq + 16 * (pos ^ swz_v8(r));
+            else src = a.dor8 + (int64_t)(LT.orow0 + qi) * rs + hq + 16 * (pos ^ swz_v8(r));
             load_lds16((const uint16_t*)src, dst + LY::QB * tensor + 1024 * (wave & 3));
         }
         if (wave == 0) {
@@ -199,10 +198,8 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_mx_kernel(BwdArgs a) {
             rv[lane] = x;
         }
     };
-    // Q and dO along rows of block s -> [128 d][64]: columns 0-31 Q^T, 32-63 dO^T
-    auto transpose_q = [&](int s) {
-        mx_transpose_v(smem + LY::RING + (s % kSlots) * LY::SLOT + LY::QR, smem + LY::T + (s & 1) * LY::TBUF, tid);
-    };
+    int tr_vo[4];   // this lane's offsets of the byte-transposed Q^T / dO^T reads
+    mx_tr_offsets(lane, tr_vo);
 
     if (t_begin < t_end) {
         LT = tile_info(t_begin);
@@ -215,7 +212,6 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_mx_kernel(BwdArgs a) {
         wait_vmem();
         __syncthreads();
         put_rowvals(0);
-        transpose_q(0);
         l_issue();
     }
 
@@ -257,12 +253,11 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_mx_kernel(BwdArgs a) {
 
         for (int i = 0; i < T.work; ++i, ++s) {
             wait_vmem();   // block s+1 landed (the only copies in flight)
-            // every wave is past block s-1: its slot and transposed buffer are free
+            // every wave is past block s-1: its slot is free
             __syncthreads();
-            // (past the end of the stream these two work on stale, unread data)
+            // (past the end of the stream this works on stale, unread data)
             put_rowvals(s + 1);
             l_issue();                               // block s+kAhead
-            transpose_q(s + 1);
 
             const int rb = q_block(T, i);
             bool skip = !wave_keys, masked = false;
@@ -277,7 +272,6 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_mx_kernel(BwdArgs a) {
             }
             if (skip) continue;
             const char* sl = smem + LY::RING + (s % kSlots) * LY::SLOT;
-            const char* tb = smem + LY::T + (s & 1) * LY::TBUF;
 
             // S = Q K^T and dP = dO V^T: A = the block's rows along d (lane =
             // row lr), B = this lane's key along d; the lane gives the scale
@@ -371,27 +365,27 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_mx_kernel(BwdArgs a) {
             const int scode = hf ? 127 : dcode;
             __builtin_amdgcn_sched_barrier(0);
             // dV^T[d, key] += dO^T[d, rows] P[rows, key]; dK^T += Q^T dS: A
-            // row d of the transposed block (dO^T columns 32-63, Q^T 0-31),
-            // rows 16hf .. 16hf+15 in the dword order of pack_col
+            // = rows 16hf .. 16hf+15 of the Q (dO) block at d, in the dword
+            // order of pack_col, by two byte-transposed reads each (rows
+            // 16hf + (0-3, 8-11), then + 4; dO 32 rows further)
+            const uint32_t qrb = lds_addr(sl + LY::QR);
 #pragma unroll
             for (int md = 0; md < MD; ++md) {
                 const int d = 32 * md + lr;
-                const char* trow = tb + d * 64;
-                const u32x4 qt = *(const u32x4*)(trow + 16 * (hf ^ swz_vt8(d)));
-                const u32x4 dt = *(const u32x4*)(trow + 16 * ((2 + hf) ^ swz_vt8(d)));
+                const uint32_t ta = qrb + tr_vo[md];
+                const i32x2 q0 = lds_read_tr8_at(ta, 0), q1 = lds_read_tr8_at(ta, 4 * 128);
+                const i32x2 d0 = lds_read_tr8_at(ta, 32 * 128), d1 = lds_read_tr8_at(ta, 36 * 128);
                 const int qrs = hf ? 127 : *(const uint8_t*)(sl + LY::QRS + d);
                 const int drs = hf ? 127 : *(const uint8_t*)(sl + LY::DRS + d);
-                dv_acc[md] = mfma_mx(i32x8{(int)dt[0], (int)dt[1], (int)dt[2], (int)dt[3], 0, 0, 0, 0}, pb8,
-                                     drs, pcode, dv_acc[md]);
-                dk_acc[md] = mfma_mx(i32x8{(int)qt[0], (int)qt[1], (int)qt[2], (int)qt[3], 0, 0, 0, 0}, sb8,
-                                     qrs, scode, dk_acc[md]);
+                dv_acc[md] = mfma_mx(i32x8{d0[0], d0[1], d1[0], d1[1], 0, 0, 0, 0}, pb8, drs, pcode, dv_acc[md]);
+                dk_acc[md] = mfma_mx(i32x8{q0[0], q0[1], q1[0], q1[1], 0, 0, 0, 0}, sb8, qrs, scode, dk_acc[md]);
             }
             // reads one d block ahead of the products
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
 #pragma unroll
             for (int md = 1; md < MD; ++md) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         }

@@ -46,6 +46,15 @@ __device__ __forceinline__ bf16x4 lds_read_tr_at(uint32_t a, int imm) {
     s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_char*)(uintptr_t)a + imm));
     return __builtin_bit_cast(bf16x4, v);
 }
+// Byte-transposed LDS read (ds_read_b64_tr_b8) at LDS byte address a + imm:
+// lanes 2e, 2e+1 of each 16-lane group address row e of an 8-row block, 8
+// bytes each, and lane i receives byte i of the 8 rows (row e in byte e).
+typedef int i32x2 __attribute__((vector_size(8)));
+__device__ __forceinline__ i32x2 lds_read_tr8_at(uint32_t a, int imm) {
+    typedef __attribute__((address_space(3))) char lds_char;
+    typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)((lds_char*)(uintptr_t)a + imm));
+}
 
 __device__ __forceinline__ bf16x8 concat(bf16x4 lo, bf16x4 hi) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);

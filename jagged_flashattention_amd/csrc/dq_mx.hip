@@ -12,7 +12,8 @@
 //   S^T  = K Q^T     K and Q encoded along d
 //   dP^T = V dO^T    V and dO encoded along d
 //   dQ^T += K^T dS^T K encoded along the keys of its sequence (32-key blocks,
-//                    as V is for the MXFP8 forward), transposed in LDS; dS^T
+//                    as V is for the MXFP8 forward), its K^T operands
+//                    byte-transposed LDS reads of the natural rows; dS^T
 //                    quantised on the fly with one scale per (row, 32-key
 //                    tile): the smallest power of two 2^e with max|dS| / 2^e
 //                    <= 448, so that no value is clamped (the encoders' rule
@@ -42,11 +43,10 @@ struct DqMxLds {
     static constexpr int KS = K + kMxSlots * BLK;       // K scales: a dword per key
     static constexpr int V = KS + kMxSlots * SC;        // V along d (as K)
     static constexpr int VS = V + kMxSlots * BLK;       // V scales: a dword per key
-    static constexpr int KK = VS + kMxSlots * SC;       // K along keys: natural rows
+    static constexpr int KK = VS + kMxSlots * SC;       // K along keys (rows swizzled by swz_v8)
     static constexpr int KKS = KK + kMxSlots * BLK;     // its scales [2 blocks][128 d]
-    static constexpr int KT = KKS + kMxSlots * SC;      // 2 K^T blocks [128][64]
     static constexpr int RW = 32 * D * 2;               // one wave's 32 bf16 rows
-    static constexpr int STG = KT + 2 * BLK;            // per-wave stage areas
+    static constexpr int STG = KKS + kMxSlots * SC;     // per-wave stage areas
     static constexpr int BYTES = STG + kWaves * RW;
     static_assert(BLK == 16 * kThreads, "one 16-byte copy per thread per block and tensor");
     static_assert(kMxStageRows * D * 4 <= RW, "epilogue staging fits a wave's area");
@@ -101,7 +101,7 @@ __global__ void __launch_bounds__(kThreads, 1) dq_mx_kernel(DqArgs a) {
         const int64_t row = base + (int64_t)key * rs;
         load_lds16((const uint16_t*)(a.k8 + row + 16 * (cs ^ swz_k8(r))), smem + LY::K + sl * LY::BLK + 1024 * wave);
         load_lds16((const uint16_t*)(a.v8 + row + 16 * (cs ^ swz_k8(r))), smem + LY::V + sl * LY::BLK + 1024 * wave);
-        load_lds16((const uint16_t*)(a.kk8 + row + 16 * cs), smem + LY::KK + sl * LY::BLK + 1024 * wave);
+        load_lds16((const uint16_t*)(a.kk8 + row + 16 * (cs ^ swz_v8(r))), smem + LY::KK + sl * LY::BLK + 1024 * wave);
         if (wave < 2) {
             const int kk = min(kFwdBlockN * n + lane, LT.L - 1);
             const uint8_t* src = wave == 0 ? a.k_sc : a.v_sc;
@@ -117,9 +117,8 @@ __global__ void __launch_bounds__(kThreads, 1) dq_mx_kernel(DqArgs a) {
         ++l_i;
         l_settle();
     };
-    auto transpose_k = [&](int s) {   // K along keys (slot s) -> K^T (buffer s % 2)
-        mx_transpose_v(smem + LY::KK + (s % kMxSlots) * LY::BLK, smem + LY::KT + (s & 1) * LY::BLK, tid);
-    };
+    int kt_vo[4];   // this lane's offsets of the byte-transposed K^T reads
+    mx_tr_offsets(lane, kt_vo);
 
     if (t_begin < t_end) {
         LT = tile_info(t_begin);
@@ -127,11 +126,10 @@ __global__ void __launch_bounds__(kThreads, 1) dq_mx_kernel(DqArgs a) {
     }
     int total = 0;   // stream length
     for (int ti = t_begin; ti < t_end; ++ti) total += ld_uniform(a.tiles + 4 * ti + 3);
-    if (total > 0) {   // block 0 landed and transposed, block 1 in flight
+    if (total > 0) {   // block 0 landed, block 1 in flight
         l_issue();
         wait_vmem();
         __syncthreads();
-        transpose_k(0);
         l_issue();
     }
 
@@ -280,10 +278,9 @@ __global__ void __launch_bounds__(kThreads, 1) dq_mx_kernel(DqArgs a) {
 
         for (int i = 0; i < T.work; ++i, ++s) {
             if (i > 0) wait_vmem();   // block s+1 landed (the only copies in flight)
-            // every wave is past block s-1: its slots and K^T buffer are free
+            // every wave is past block s-1: its slots are free
             __syncthreads();
             l_issue();                              // block s+kMxAhead
-            if (s + 1 < total) transpose_k(s + 1);  // K^T of block s+1
 
             const int n = seq_block<MODE>(T, T.k0 + i);
             bool skip, masked;
@@ -343,7 +340,7 @@ __global__ void __launch_bounds__(kThreads, 1) dq_mx_kernel(DqArgs a) {
             const i32x8 ds8 = mx_pack_scaled(sc, scl);
             // dQ^T[d, row] += K^T[d, key] dS^T[key, row]; this lane gives the
             // scale of tile hf of its row
-            mx_pv(acc, ds8, smem + LY::KT + (s & 1) * LY::BLK, smem + LY::KKS + sl * LY::SC,
+            mx_pv_tr(acc, ds8, smem + LY::KK + sl * LY::BLK, kt_vo, smem + LY::KKS + sl * LY::SC,
                   (hf ? sce[1] : sce[0]) + 127, lr, hf);
         }
 

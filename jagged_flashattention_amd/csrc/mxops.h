@@ -1,4 +1,4 @@
-// MXFP8 operand helpers shared by the MXFP8 forward and the MXFP8 dQ pass
+// MXFP8 operand helpers shared by the MXFP8 forward, dQ and dK/dV passes
 // (gfx950 scaled MFMA v_mfma_scale_f32_32x32x64_f8f6f4 with OCP E4M3 data and
 // E8M0 block scales; D = 128).
 #pragma once
@@ -10,10 +10,8 @@ namespace mxops {
 
 // ---- MXFP8 operands (D = 128, two 64-wide steps j along d). A 16-byte chunk
 // c of key r of a K block sits at chunk c ^ ((r >> 1) & 7) (the 16 lanes of a
-// read pass, 16 keys, cover all banks); chunk c of row d of a V^T block at
-// c ^ ((d >> 2) & 3).
+// read pass, 16 keys, cover all banks).
 __device__ __forceinline__ int swz_k8(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int swz_vt8(int d) { return (d >> 2) & 3; }
 // A natural [64 keys][128 d] block read by mx_pv_tr: chunk c of key r at
 // c ^ swz_v8(r). A half wave's transposed reads take 8 keys x 32 bytes
 // (keys 16h + 0-3 and 8-11, or 4-7 and 12-15); the even (odd) keys among them
@@ -91,27 +89,12 @@ __device__ __forceinline__ i32x8 mx_pack_scaled(const f32x16 (&x)[2], const floa
     return out;
 }
 
-// O^T[d, qrow] += V^T[d, key] P^T[key, qrow]: lane (d = 32md + lr, half hf)
-// takes keys 16hf .. +15 (tile 0) and 32 + 16hf .. +15 (tile 1) of row d in
-// the dword order of mx_pack_p, and the scale of V block (d, 2n + hf); bsc
-// is the E8M0 scale of this lane's P^T block (block hf of its row).
-__device__ __forceinline__ void mx_pv(f32x16 (&oacc)[4], const i32x8& pb, const char* vtb,
-                                      const char* vsb, int bsc, int lr, int hf) {
-#pragma unroll
-    for (int md = 0; md < 4; ++md) {
-        const int d = 32 * md + lr;
-        const char* row = vtb + d * 64;
-        const u32x4 lo = *(const u32x4*)(row + 16 * (hf ^ swz_vt8(d)));
-        const u32x4 hi = *(const u32x4*)(row + 16 * ((2 + hf) ^ swz_vt8(d)));
-        const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        const int vs = *(const uint8_t*)(vsb + hf * 128 + d);
-        oacc[md] = mfma_mx(av, pb, vs, bsc, oacc[md]);
-    }
-}
-
-// mx_pv with the V^T operands read straight from the natural V block (keys
-// swizzled by swz_v8) by byte-transposed reads (ds_read_b64_tr_b8: lanes 2e,
+// O^T[d, qrow] += V^T[d, key] P^T[key, qrow] over a 64-key block, P^T packed
+// by mx_pack_p (lane half hf: keys 16hf .. +15 of each 32-key tile, dwords
+// of keys 0-3, 8-11, 4-7, 12-15), V's scale that of block (d, 2n + hf); bsc
+// is the E8M0 scale of this lane's P^T block. The V^T operands are read
+// straight from the natural V block (keys swizzled by swz_v8) by
+// byte-transposed reads (ds_read_b64_tr_b8: lanes 2e,
 // 2e+1 of a 16-lane group address row e, 8 bytes each, and lane i receives
 // byte i of the 8 rows). Lane (d = 32md + lr, half hf) needs keys 16hf +
 // (0-3, 8-11, 4-7, 12-15) and the same + 32: four reads of 8 keys, at rows
@@ -123,53 +106,21 @@ __device__ __forceinline__ void mx_tr_offsets(int lane, int (&vo)[4]) {
 #pragma unroll
     for (int md = 0; md < 4; ++md) vo[md] = r * 128 + (((2 * md + g) ^ swz_v8(r)) << 4) + 8 * (n16 & 1);
 }
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
 __device__ __forceinline__ void mx_pv_tr(f32x16 (&oacc)[4], const i32x8& pb, const char* vb,
                                          const int (&vo)[4], const char* vsb, int bsc, int lr, int hf) {
-    typedef int v2i32 __attribute__((vector_size(8)));
-    typedef __attribute__((address_space(3))) v2i32 lds_v2i32;
-    typedef __attribute__((address_space(3))) const char lds_char;
-    const uint32_t base = (uint32_t)(uintptr_t)(lds_char*)vb;
+    const uint32_t base = lds_addr(vb);
 #pragma unroll
     for (int md = 0; md < 4; ++md) {
         const int d = 32 * md + lr;
-        v2i32 x[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            constexpr int rows[4] = {0, 4, 32, 36};
-            x[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (lds_v2i32*)((lds_char*)(uintptr_t)(base + vo[md]) + 128 * rows[t]));
-        }
-        const i32x8 av = {x[0][0], x[0][1], x[1][0], x[1][1], x[2][0], x[2][1], x[3][0], x[3][1]};
+        const uint32_t a = base + vo[md];
+        const i32x2 x0 = lds_read_tr8_at(a, 0), x1 = lds_read_tr8_at(a, 4 * 128);
+        const i32x2 x2 = lds_read_tr8_at(a, 32 * 128), x3 = lds_read_tr8_at(a, 36 * 128);
+        const i32x8 av = {x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
         const int vs = *(const uint8_t*)(vsb + hf * 128 + d);
         oacc[md] = mfma_mx(av, pb, vs, bsc, oacc[md]);
-    }
-}
-
-// V [64 keys][128 d] (E4M3) -> V^T [128 d][64 keys]: thread t transposes the
-// 4 x 4 byte tile of keys 4(t/32) .. +3 and d 4(t%32) .. +3 in registers.
-// Within each 16-key chunk of a V^T row the four 4-key dwords are stored in
-// the order keys 0-3, 8-11, 4-7, 12-15 (relative to the chunk): the dword
-// order of the packed P^T operand, so a chunk read is an A operand as is.
-__device__ __forceinline__ void mx_transpose_v(const char* v, char* vt, int tid) {
-    const int b = tid & 31, aq = tid >> 5;
-    uint32_t r[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = *(const uint32_t*)(v + (4 * aq + i) * 128 + 4 * b);
-    // byte i of column j = byte j of row i
-    const uint32_t lo01 = __builtin_amdgcn_perm(r[1], r[0], 0x05010400u);
-    const uint32_t hi01 = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);
-    const uint32_t lo23 = __builtin_amdgcn_perm(r[3], r[2], 0x05010400u);
-    const uint32_t hi23 = __builtin_amdgcn_perm(r[3], r[2], 0x07030602u);
-    uint32_t c[4];
-    c[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
-    c[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
-    c[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
-    c[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int d = 4 * b + j;
-        const int g = aq & 3, pos = g == 1 ? 2 : g == 2 ? 1 : g;   // dword order 0, 2, 1, 3
-        *(uint32_t*)(vt + d * 64 + 16 * ((aq >> 2) ^ swz_vt8(d)) + 4 * pos) = c[j];
     }
 }
 
