@@ -45,8 +45,8 @@ struct DkdvMxLds {
     static constexpr int D = 128;
     static constexpr int QB = kBwdBlockM * D;       // one E4M3 block [32][128]
     // ring slot: Q and dO along d (rows swizzled by swz_k8), Q and dO along
-    // rows (natural, back to back: the [64][128] input of the transposition),
-    // their scales, the block's row values
+    // rows (back to back, one [64][128] block read by byte-transposed reads,
+    // rows swizzled by swz_v8), their scales, the block's row values
     static constexpr int QD = 0;
     static constexpr int DD = QD + QB;
     static constexpr int QR = DD + QB;

@@ -20,8 +20,8 @@
 //   - the V^T operands of O^T += V^T P^T come straight from the natural V
 //     block through transposed LDS reads (ds_read_b64_tr_b16): each 16-lane
 //     group reads the 4 key rows that the lane's P^T registers hold, in
-//     their order, so no transposed copy of V is made (MXFP8 makes one, by a
-//     byte transposition of block j+1 at block j);
+//     their order, so no transposed copy of V is made (MXFP8 reads its E4M3
+//     V^T operands the same way with byte-transposed reads);
 //   - per wave: S^T = K Q^T (32x32x16 bf16 MFMA, Q in VGPRs as the B operand,
 //     so a lane owns one query row and row max / row sum stay in-lane), fp32
 //     online softmax in the exp2 domain (bf16: the running max moves, and
