@@ -176,14 +176,40 @@ def counters_for(kernel: str, workload: str):
     return kv
 
 
-def source_digest(name: str):
+def code_only(text: bytes) -> bytes:
+    """C/C++ source without its comments, trailing blanks and empty lines
+    (string and character literals kept as they are)."""
+    out, i, n = bytearray(), 0, len(text)
+    while i < n:
+        c = text[i:i + 1]
+        if c in (b'"', b"'"):
+            j = i + 1
+            while j < n and text[j:j + 1] != c:
+                j += 2 if text[j:j + 1] == b"\\" else 1
+            out += text[i:j + 1]
+            i = j + 1
+        elif text.startswith(b"//", i):
+            while i < n and text[i:i + 1] != b"\n":
+                i += 1
+        elif text.startswith(b"/*", i):
+            j = text.find(b"*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out += c
+            i += 1
+    lines = [ln.rstrip() for ln in bytes(out).split(b"\n")]
+    return b"\n".join(ln for ln in lines if ln)
+
+
+def source_digest(name: str, root: str = ROOT):
     """sha256 (first 16 hex digits) of a kernel source together with every
-    header it includes from the library's own directories (transitively), so
-    that a change to shared inner-loop code also marks a counter summary
-    stale; None if the source does not exist."""
+    header it includes from the library's own directories (transitively),
+    comments left out, so that a change to the code, shared inner-loop code
+    included, marks a counter summary stale and a change to a comment does
+    not; None if the source does not exist."""
     import hashlib
     import re
-    dirs = [os.path.join(ROOT, "jagged_flashattention_amd", "csrc"), os.path.join(ROOT, "include")]
+    dirs = [os.path.join(root, "jagged_flashattention_amd", "csrc"), os.path.join(root, "include")]
     first = os.path.join(dirs[0], name)
     if not name or not os.path.exists(first):
         return None
@@ -194,7 +220,7 @@ def source_digest(name: str):
             continue
         seen.append(path)
         text = open(path, "rb").read()
-        h.update(os.path.basename(path).encode() + b"\0" + text)
+        h.update(os.path.basename(path).encode() + b"\0" + code_only(text))
         for inc in re.findall(rb'^\s*#\s*include\s+"([^"]+)"', text, re.M):
             for d in dirs:
                 cand = os.path.join(d, inc.decode())
