@@ -177,36 +177,44 @@ def counters_for(kernel: str, workload: str):
 
 
 def code_only(text: bytes) -> bytes:
-    """C/C++ source without its comments, trailing blanks and empty lines
-    (string and character literals kept as they are)."""
-    out, i, n = bytearray(), 0, len(text)
-    while i < n:
-        c = text[i:i + 1]
-        if c in (b'"', b"'"):
-            j = i + 1
-            while j < n and text[j:j + 1] != c:
-                j += 2 if text[j:j + 1] == b"\\" else 1
-            out += text[i:j + 1]
-            i = j + 1
-        elif text.startswith(b"//", i):
-            while i < n and text[i:i + 1] != b"\n":
+    """C/C++ source without its comments, every run of white space (line
+    breaks included) outside string and character literals made one blank:
+    what stays is the code's token stream."""
+    def scan(t, on_comment, on_space):
+        out, i, n = bytearray(), 0, len(t)
+        while i < n:
+            c = t[i:i + 1]
+            if c in (b'"', b"'"):
+                j = i + 1
+                while j < n and t[j:j + 1] != c:
+                    j += 2 if t[j:j + 1] == b"\\" else 1
+                out += t[i:j + 1]
+                i = j + 1
+            elif on_comment and t.startswith(b"//", i):
+                while i < n and t[i:i + 1] != b"\n":
+                    i += 1
+                out += b" "
+            elif on_comment and t.startswith(b"/*", i):
+                j = t.find(b"*/", i + 2)
+                i = n if j < 0 else j + 2
+                out += b" "
+            elif on_space and c.isspace():
+                while i < n and t[i:i + 1].isspace():
+                    i += 1
+                out += b" "
+            else:
+                out += c
                 i += 1
-        elif text.startswith(b"/*", i):
-            j = text.find(b"*/", i + 2)
-            i = n if j < 0 else j + 2
-        else:
-            out += c
-            i += 1
-    lines = [ln.rstrip() for ln in bytes(out).split(b"\n")]
-    return b"\n".join(ln for ln in lines if ln)
+        return bytes(out)
+    return scan(scan(text, True, False), False, True).strip()
 
 
 def source_digest(name: str, root: str = ROOT):
     """sha256 (first 16 hex digits) of a kernel source together with every
     header it includes from the library's own directories (transitively),
     comments left out, so that a change to the code, shared inner-loop code
-    included, marks a counter summary stale and a change to a comment does
-    not; None if the source does not exist."""
+    included, marks a counter summary stale and a change to a comment or to
+    the layout of the text does not; None if the source does not exist."""
     import hashlib
     import re
     dirs = [os.path.join(root, "jagged_flashattention_amd", "csrc"), os.path.join(root, "include")]

@@ -349,7 +349,8 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
 #pragma unroll
                 for (int j = 0; j < 2 * MD; ++j) {
                     const int o = 16 * D * 2 * (j & 1);
-                    dta[j] = concat(lds_read_tr_at(ta[0][j >> 1], LY::QB + o), lds_read_tr_at(ta[1][j >> 1], LY::QB + o));
+                    dta[j] = concat(lds_read_tr_at(ta[0][j >> 1], LY::QB + o),
+                                    lds_read_tr_at(ta[1][j >> 1], LY::QB + o));
                     qta[j] = concat(lds_read_tr_at(ta[0][j >> 1], o), lds_read_tr_at(ta[1][j >> 1], o));
                 }
 #pragma unroll

@@ -212,11 +212,11 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
             // dO and O of the wave's 32 rows, fetched with row-contiguous
             // copies (row-strided dO^T fragment loads cost the vector memory
             // unit one cache line per row and instruction): dO into the
-            // wave's own stage area, O into registers in the same layout. The dO^T fragments are then read from LDS, and
-            // delta is formed in the copy layout, summed over the lanes of a
-            // row and handed to the fragment lanes through LDS. (Per-sequence
-            // Q keeps the direct loads below: its extra live Q rows would
-            // spill.)
+            // wave's own stage area, O into registers in the same layout.
+            // The dO^T fragments are then read from LDS, and delta is formed
+            // in the copy layout, summed over the lanes of a row and handed
+            // to the fragment lanes through LDS. (Per-sequence Q keeps the
+            // direct loads below: its extra live Q rows would spill.)
             char* rg = smem + LY::STG + wave * LY::RW;
             constexpr int NI = 32 * CH / 64;   // 16-byte copies per lane
             bf16x8 ov[NI];

@@ -1,7 +1,7 @@
 """The counter summaries under profiles/ are tied to the kernel code they
 were measured on by a digest of the source and the library headers it
-includes, comments left out: a code change marks a summary stale, a comment
-change does not (CPU only)."""
+includes, comments and layout left out: a code change marks a summary
+stale, a comment or a line break does not (CPU only)."""
 import os
 import shutil
 
@@ -11,7 +11,7 @@ import bench
 def test_code_only_drops_comments_and_keeps_literals():
     src = (b'int a = 1;  // note\n/* block\n   comment */\n\nconst char* s = "x // y /* z */";\n'
            b"char q = '\"'; int b = 2; // trailing\n")
-    assert bench.code_only(src) == b'int a = 1;\nconst char* s = "x // y /* z */";\nchar q = \'"\'; int b = 2;'
+    assert bench.code_only(src) == b'int a = 1; const char* s = "x // y /* z */"; char q = \'"\'; int b = 2;'
 
 
 def _tree(tmp_path):
@@ -28,7 +28,8 @@ def test_digest_follows_code_not_comments(tmp_path):
     assert base == bench.source_digest("bwd.hip")
     hdr = os.path.join(root, "jagged_flashattention_amd", "csrc", "qtile.h")
     text = open(hdr).read()
-    open(hdr, "w").write("// a new comment line\n" + text.replace("namespace qtile {", "namespace qtile {  // here"))
+    open(hdr, "w").write("// a new comment line\n" + text.replace("namespace qtile {", "namespace qtile {  // here")
+                         .replace("constexpr int kWaves = 8;", "constexpr  int\n    kWaves = 8;"))
     assert bench.source_digest("bwd.hip", root) == base
     # a code change in an included header marks every kernel using it stale
     open(hdr, "w").write(text.replace("constexpr int kWaves = 8;", "constexpr int kWaves = 4;"))
