@@ -134,11 +134,15 @@ def forward_rows(q, k, v, kv_offsets, b, h, rows, *, scale, broadcast_q, q_offse
 
 
 def backward(q, k, v, do, kv_offsets, *, scale, broadcast_q, q_offsets=None, causal=False,
-             block_mask=None, seqs=None, heads=None, window=None):
+             block_mask=None, seqs=None, heads=None, window=None, o=None):
     """dQ (shape of q), dK, dV [T_k,H,D] and delta [H,T_q], all float64.
 
     With ``seqs`` given, only those sequences contribute (their dK/dV rows are
-    exact; a broadcast dQ is then the partial sum over ``seqs``)."""
+    exact; a broadcast dQ is then the partial sum over ``seqs``). ``o`` is the
+    forward output as a backward receives it ([T_q,H,D], e.g. as stored in
+    bf16): delta_i = <dO_i, o_i> is formed from it, everything else from the
+    exact softmax; by default it is the exact O, and the result the exact
+    gradients."""
     B, lq, t_q = _problem(q, kv_offsets, q_offsets, broadcast_q)
     H, D = k.shape[1], k.shape[2]
     dq = np.zeros(q.shape)
@@ -154,7 +158,7 @@ def backward(q, k, v, do, kv_offsets, *, scale, broadcast_q, q_offsets=None, cau
         for h in (range(H) if heads is None else heads):
             qb, kb, vb, dob = q[qs, h, :], k[ks, h, :], v[ks, h, :], do[os_, h, :]
             _, p = _softmax_stats(scale * (qb @ kb.T), vis)
-            ob = p @ vb
+            ob = p @ vb if o is None else o[os_, h, :]
             dl = np.sum(dob * ob, axis=1)
             dp = dob @ vb.T
             ds = p * (dp - dl[:, None])
@@ -163,6 +167,41 @@ def backward(q, k, v, do, kv_offsets, *, scale, broadcast_q, q_offsets=None, cau
             dv[ks, h, :] = p.T @ dob
             delta[h, os_] = dl
     return dq, dk, dv, delta
+
+
+def delta_slack(q, k, v, do, kv_offsets, *, scale, broadcast_q, q_offsets=None, causal=False,
+                block_mask=None, window=None):
+    """Element-wise bounds (dQ, dK; float64, shapes of q and k) on how far
+    the gradients move when delta_i = <dO_i, o_i> is formed from O as the
+    forward stores it rather than from the exact O.
+
+    O is stored in bf16 (the layout the pages fix for the kernel's tensors)
+    and a kernel forms it from probabilities rounded to bf16 for its matrix
+    products, so an element of the stored O may be off by up to 2^-9 sum_j
+    p_ij |v_jd| (the rounded probabilities) plus 2^-9 |o_id| (the rounding of
+    O itself); both are taken at 2^-8 here. Then |d delta_i| <= eps_i =
+    sum_d |dO_id| * 2^-8 (sum_j p_ij |v_jd| + |o_id|), dS_ij moves by
+    p_ij d delta_i, and so dq_i by at most scale * eps_i * sum_j p_ij |k_j|
+    and dk_j by at most scale * sum_i p_ij eps_i |q_i| (summed over the batch
+    for a broadcast Q, as dQ is). Where dP_ij - delta_i nearly cancels this
+    is the larger part of the gradients' error. Test infrastructure only."""
+    B, lq, t_q = _problem(q, kv_offsets, q_offsets, broadcast_q)
+    H = k.shape[1]
+    sq = np.zeros(q.shape)
+    sk = np.zeros(k.shape)
+    for b in range(B):
+        qs, os_ = _q_rows(b, kv_offsets, q_offsets, lq, broadcast_q)
+        ks = slice(int(kv_offsets[b]), int(kv_offsets[b + 1]))
+        vis = visibility(qs.stop - qs.start, ks.stop - ks.start, causal=causal, window=window,
+                         mask_b=None if block_mask is None else block_mask[b])
+        for h in range(H):
+            qb, kb, vb, dob = q[qs, h, :], k[ks, h, :], v[ks, h, :], do[os_, h, :]
+            _, p = _softmax_stats(scale * (qb @ kb.T), vis)
+            ob = p @ vb
+            eps = 2.0 ** -8 * np.sum(np.abs(dob) * (p @ np.abs(vb) + np.abs(ob)), axis=1)
+            sq[qs, h, :] += scale * eps[:, None] * (p @ np.abs(kb))
+            sk[ks, h, :] = scale * ((p * eps[:, None]).T @ np.abs(qb))
+    return sq, sk
 
 
 def broadcast_dq_rows(q, k, v, do, kv_offsets, h, rows, *, scale, block_mask=None):

@@ -1,6 +1,7 @@
 """Seeded random problems through the whole HIP path against the oracle: every
 output (O, LSE, dQ, dK, dV, dq_accum, delta) of every sequence and head,
-outputs NaN-filled before the run. Each seed draws one problem of a random
+outputs NaN-filled before the run; then the backward alone, fed the oracle's
+O as stored (bf16) and its LSE, against the oracle's backward on that O. Each seed draws one problem of a random
 kind (broadcast Q, per-sequence Q with its own lengths, causal, sliding
 window, block-sparse with a broadcast or per-sequence Q), head_dim 64 or 128,
 1-3 heads, ragged lengths (0, 1 and tile sizes +-1 among them), and random
@@ -15,7 +16,7 @@ torch = pytest.importorskip("torch")
 if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
-from test_gpu_parity import _custom, check_all, run_gpu  # noqa: E402
+from test_gpu_parity import _custom, check_all, check_bwd_given_o, run_gpu  # noqa: E402
 
 N_CASES = 400
 EDGE = [0, 1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
@@ -62,9 +63,12 @@ def _problem(seed, head_dims=(64, 128)):
     return kind, x, plan
 
 
-@pytest.mark.parametrize("seed", range(N_CASES))
+# 1862: one query row over six keys, where dP - delta nearly cancels and the
+# stored O's rounding carried by delta is the larger part of the dQ error
+@pytest.mark.parametrize("seed", list(range(N_CASES)) + [1862])
 def test_random_problem_matches_oracle(seed):
     kind, x, plan = _problem(seed)
     print("fuzz seed", seed, kind, "lengths", list(x.lengths), "H", x.workload.heads,
           "D", x.workload.head_dim, plan, flush=True)
     check_all(x, run_gpu(x, canary=True, **plan))
+    check_bwd_given_o(x, **plan)

@@ -120,8 +120,21 @@ def _max_abs(a):
     return float(np.abs(a).max()) if a.size else 0.0
 
 
+def oracle_kw(x):
+    w = x.workload
+    return dict(scale=w.scale, broadcast_q=w.broadcast_q, q_offsets=x.q_offsets, causal=w.causal,
+                block_mask=x.block_mask, window=w.window)
+
+
 def check_all(x, g):
+    """The whole path (the GPU backward fed the GPU forward's O and LSE)
+    against the exact oracle. dQ and dK may also move by what forming delta
+    from the stored bf16 O costs (oracle.attention.delta_slack), on top of the
+    gradient tolerance; check_bwd_given_o holds the backward alone to the
+    gradient tolerance with that effect taken out."""
     o, lse, dq, dk, dv, delta = oracle_full(x)
+    q64, k64, v64, do64 = (x.as_f64(n) for n in ("q", "k", "v", "do"))
+    sq, sk = A.delta_slack(q64, k64, v64, do64, x.kv_offsets, **oracle_kw(x))
     go, glse = host_f64(g.o), g.lse.cpu().numpy().astype(np.float64)
     assert not np.isnan(go).any() and not np.isnan(glse).any()
     fin = np.isfinite(lse)
@@ -130,12 +143,54 @@ def check_all(x, g):
     if fin.any():
         assert _max_abs(glse[fin] - lse[fin]) <= TOL_O, ("lse", _max_abs(glse[fin] - lse[fin]))
     gdq, gdk, gdv = host_f64(g.dq), host_f64(g.dk), host_f64(g.dv)
-    for name, got, ref in (("dq", gdq, dq), ("dk", gdk, dk), ("dv", gdv, dv)):
+    gacc = g.dq_accum.cpu().numpy().astype(np.float64)
+    for name, got, ref, slack in (("dq", gdq, dq, sq), ("dk", gdk, dk, sk), ("dv", gdv, dv, 0.0),
+                                  ("dq_accum", gacc, dq, sq)):
+        assert not np.isnan(got).any(), name
+        allowed = TOL_GRAD * _max_abs(ref) + slack
+        assert np.all(np.abs(got - ref) <= allowed), (name, rel_err(got, ref))
+    gdelta = g.delta.cpu().numpy()
+    assert _max_abs(gdelta - delta) <= 2e-2 * max(1.0, _max_abs(delta)), ("delta", _max_abs(gdelta - delta))
+
+
+def run_gpu_bwd_given(x, o_bits, lse32, bwd_workers=None, dq_workers=None, canary=True, **_):
+    """The GPU backward alone, fed O (bf16 bits) and LSE (float32) from the
+    caller."""
+    att = J.JaggedAttention(problem_of(x), x.kv_offsets, x.q_offsets, x.block_mask,
+                            bwd_workers=bwd_workers, dq_workers=dq_workers)
+    q, k, v, do, o = dev(x.q), dev(x.k), dev(x.v), dev(x.do), dev(o_bits)
+    lse = torch.from_numpy(np.ascontiguousarray(lse32, dtype=np.float32)).cuda()
+    H = x.workload.heads
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               dq_accum=torch.empty(q.shape, dtype=torch.float32, device="cuda"),
+               delta=torch.empty((H, att.total_q), dtype=torch.float32, device="cuda"))
+    if canary:
+        for t in out.values():
+            t.fill_(float("nan"))
+    att.backward(q, k, v, o, lse, do, out)
+    torch.cuda.synchronize()
+    return out
+
+
+def check_bwd_given_o(x, **plan):
+    """The GPU backward fed the oracle's O rounded to bf16 (as the forward
+    stores it) and its LSE in float32, against the oracle's backward that
+    forms delta from that same O: dQ, dK, dV, dq_accum and delta to the
+    gradient tolerance, with nothing added for the stored O."""
+    q64, k64, v64, do64 = (x.as_f64(n) for n in ("q", "k", "v", "do"))
+    kw = oracle_kw(x)
+    o, lse = A.forward(q64, k64, v64, x.kv_offsets, **kw)
+    o_bits = W.f32_to_bf16_bits(o.astype(np.float32))
+    o_st = W.bf16_bits_to_f32(o_bits).astype(np.float64)
+    dq, dk, dv, delta = A.backward(q64, k64, v64, do64, x.kv_offsets, o=o_st, **kw)
+    out = run_gpu_bwd_given(x, o_bits, lse.astype(np.float32), **plan)
+    for name, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
+        got = host_f64(out[name])
         assert not np.isnan(got).any(), name
         assert rel_err(got, ref) <= TOL_GRAD, (name, rel_err(got, ref))
-    e = rel_err(g.dq_accum.cpu().numpy().astype(np.float64), dq)
+    e = rel_err(out["dq_accum"].cpu().numpy().astype(np.float64), dq)
     assert e <= TOL_GRAD, ("dq_accum", e)
-    gdelta = g.delta.cpu().numpy()
+    gdelta = out["delta"].cpu().numpy()
     assert _max_abs(gdelta - delta) <= 2e-2 * max(1.0, _max_abs(delta)), ("delta", _max_abs(gdelta - delta))
 
 
@@ -201,6 +256,7 @@ def test_small_parity(case):
     print("case", case, flush=True)
     x = SMALL_CASES[case]()
     check_all(x, run_gpu(x))
+    check_bwd_given_o(x)
 
 
 def test_one_key_sequence_is_bitwise_v_row():
