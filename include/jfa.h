@@ -65,9 +65,10 @@ extern "C" {
 #define JFA_OK                 0
 #define JFA_ERR_INVALID_ARG   -1  /* null/misaligned pointer, bad size or flag */
 #define JFA_ERR_BAD_OFFSETS   -2  /* offsets[0] != 0, decreasing, or overflow   */
-#define JFA_ERR_UNSUPPORTED   -3  /* head_dim not 64/128, causal or window with
-                                     broadcast Q or with unequal Q/KV lengths,
-                                     mask with causal or window               */
+#define JFA_ERR_UNSUPPORTED   -3  /* head_dim not 64/128, num_heads > 32768,
+                                     causal or window with broadcast Q or with
+                                     unequal Q/KV lengths, mask with causal or
+                                     window                                   */
 #define JFA_ERR_PLAN_MISMATCH -4  /* plan built for another pass/problem      */
 #define JFA_ERR_WORKSPACE     -5  /* workspace too small                       */
 #define JFA_ERR_HIP           -6  /* a HIP call failed: see jfa_last_hip_error */
@@ -86,7 +87,9 @@ extern "C" {
 /* Problem description shared by the planner, jfa_fwd and jfa_bwd. */
 typedef struct jfa_problem {
     int32_t batch;          /* B >= 0 sequences                                */
-    int32_t num_heads;      /* H >= 1                                          */
+    int32_t num_heads;      /* 1 <= H <= 32768 (a token row of H*D bf16 stays
+                               below 2^24 bytes: the kernels address a block's
+                               rows with 24-bit multiples of it)               */
     int32_t head_dim;       /* D, 64 or 128                                    */
     int32_t broadcast_q;    /* 1: one dense Q [lq,H,D] shared by all sequences */
     int32_t lq;             /* rows of the shared Q (broadcast_q only), >= 0   */

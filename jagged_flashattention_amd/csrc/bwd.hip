@@ -66,6 +66,9 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
     const int lr = lane & 31, hf = lane >> 5;
     const int H = a.num_heads;
     const int64_t rs = (int64_t)H * D;
+    // row stride in bytes, below 2^24 (H bounded by the planner): a block's
+    // rows are 24-bit multiples of it from its first row
+    const uint32_t rs_b = (uint32_t)rs * 2;
 
     constexpr int QH = (kBwdBlockM * CH) / 64;   // copies per tensor (Q or dO) per block
     // A operands: Q / dO row lr, chunk 2kc + hf; the V rows (B operand) of
@@ -141,7 +144,12 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
         if (l_ti >= t_end) return;
         const int rb = q_block(LT, l_i);
         char* dst = smem + LY::RING + (l_slot % kSlots) * LY::SLOT;
+        // the block's first Q and dO rows (wave-uniform); a partial last
+        // block moves its rows past the sequence back onto the last row
         const int64_t hq = (int64_t)LT.h * D;
+        const uint16_t* qb0 = a.q + (int64_t)(LT.q0 + kBwdBlockM * rb) * rs + hq;
+        const uint16_t* db0 = a.d_o + (int64_t)(LT.orow0 + kBwdBlockM * rb) * rs + hq;
+        const int last = LT.Lq - 1 - kBwdBlockM * rb;
         // copy u of this wave is copy g = QPW*wave + u of the block (first
         // half Q, second half dO) and fills chunk positions 64 (g mod QH) +
         // lane: row r, stored chunk cp (g and the tensor are wave-uniform)
@@ -151,11 +159,8 @@ __global__ void __launch_bounds__(kThreads, 1) dkdv_kernel(BwdArgs a) {
             const bool is_do = g >= QH;
             const int p = 64 * (g % QH) + lane;
             const int r = p / CH, cp = p % CH;
-            const int qi = min(kBwdBlockM * rb + r, LT.Lq - 1);
-            const int64_t off = hq + 8 * (cp ^ swz_rt<D>(r));
-            const uint16_t* src = is_do ? a.d_o + (int64_t)(LT.orow0 + qi) * rs + off
-                                        : a.q + (int64_t)(LT.q0 + qi) * rs + off;
-            load_lds16(src, dst + (is_do ? LY::QB : 0) + 1024 * (g % QH));
+            const uint32_t off = __umul24((uint32_t)min(r, last), rs_b) + 16 * (cp ^ swz_rt<D>(r));
+            load_lds16_s(is_do ? db0 : qb0, off, dst + (is_do ? LY::QB : 0) + 1024 * (g % QH));
         }
         if (wave == 0) {
             const int row = kBwdBlockM * rb + lr;

@@ -72,13 +72,17 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
     // 64 (LPW wave + u) + lane of a block: key r, stored chunk cp. K and V
     // share the swizzle that serves both the operand reads and (K) the
     // transposed reads.
-    int ld_row[LPW], ld_g[LPW];
+    // The lane's byte offset from the block's first key row (32 bits: at
+    // most 64 rows of H*D*2 bytes, H bounded by the planner).
+    const uint32_t rs_b = (uint32_t)rs * 2;
+    int ld_row[LPW];
+    uint32_t ld_o[LPW];
 #pragma unroll
     for (int u = 0; u < LPW; ++u) {
         const int p = 64 * (LPW * wave + u) + lane;
         const int r = p / CH, cp = p % CH;
         ld_row[u] = r;
-        ld_g[u] = 8 * (cp ^ swz_rt<D>(r));
+        ld_o[u] = r * rs_b + 16 * (cp ^ swz_rt<D>(r));
     }
     // A operands: K / V row 32mb + lr, chunk 2kc + hf (swz_rt depends on the
     // row's low 4 bits only)
@@ -114,15 +118,20 @@ __global__ void __launch_bounds__(kThreads, 1) dq_kernel(DqArgs a) {
     auto l_issue = [&]() {
         if (l_ti >= t_end) return;
         const int n = seq_block<MODE>(LT, LT.k0 + l_i);
-        const int64_t base = (int64_t)LT.kv0 * rs + (int64_t)LT.h * D;
         char* kdst = smem + LY::K + (l_slot % kSlots) * LY::BLK;
         char* vdst = smem + LY::V + (l_slot % kSlots) * LY::BLK;
+        // the block's first key row (wave-uniform); a partial last block
+        // moves its rows past the sequence back onto the last row
+        const int64_t blk0 = (int64_t)(LT.kv0 + kFwdBlockN * n) * rs + (int64_t)LT.h * D;
+        const uint16_t* kb = a.k + blk0;
+        const uint16_t* vb = a.v + blk0;
+        const int last = LT.L - 1 - kFwdBlockN * n;
 #pragma unroll
         for (int u = 0; u < LPW; ++u) {
-            const int key = min(kFwdBlockN * n + ld_row[u], LT.L - 1);
-            const int64_t row = base + (int64_t)key * rs + ld_g[u];
-            load_lds16(a.k + row, kdst + 1024 * (LPW * wave + u));
-            load_lds16(a.v + row, vdst + 1024 * (LPW * wave + u));
+            uint32_t back = 0;
+            if (last < kFwdBlockN - 1) back = (uint32_t)max(ld_row[u] - last, 0) * rs_b;
+            load_lds16_s(kb, ld_o[u] - back, kdst + 1024 * (LPW * wave + u));
+            load_lds16_s(vb, ld_o[u] - back, vdst + 1024 * (LPW * wave + u));
         }
         ++l_slot;
         ++l_i;

@@ -114,15 +114,19 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
     const int64_t rs = (int64_t)H * D;
 
     // direct-to-LDS copy: load u of this wave fills chunk positions 64u'+lane
-    // (u' = LPW*wave + u) of a block, i.e. key r, stored chunk cp
-    int ld_row[LPW], ld_gk[LPW], ld_gv[LPW];
+    // (u' = LPW*wave + u) of a block, i.e. key r, stored chunk cp; the lane's
+    // byte offsets from the block's first key row (K and V swizzles; rows
+    // fit 32 bits: at most 64 rows of H*D*2 bytes, H bounded by the planner)
+    const uint32_t rs_b = (uint32_t)rs * 2;
+    int ld_row[LPW];
+    uint32_t ld_ok[LPW], ld_ov[LPW];
 #pragma unroll
     for (int u = 0; u < LPW; ++u) {
         const int p = 64 * (LPW * wave + u) + lane;
         const int r = p / CH, cp = p % CH;
         ld_row[u] = r;
-        ld_gk[u] = 8 * (cp ^ swz_k<D>(r));
-        ld_gv[u] = 8 * (cp ^ swz_rt<D>(r));
+        ld_ok[u] = r * rs_b + 16 * (cp ^ swz_k<D>(r));
+        ld_ov[u] = r * rs_b + 16 * (cp ^ swz_rt<D>(r));
     }
     // S^T operand: K row 32mb + lr, chunk 2kc + hf (swz_k(32mb + lr) == swz_k(lr))
     int k_off[KC];
@@ -289,12 +293,18 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
                           smem + LY::VS + (l_slot % kKSlots) * LY::SC);
             }
         } else {
+            // the block's first key row (wave-uniform); a partial last block
+            // moves its rows past the sequence back onto the last row
+            const int64_t blk0 = base + (int64_t)(kFwdBlockN * n) * rs;
+            const uint16_t* kb = a.k + blk0;
+            const uint16_t* vb = a.v + blk0;
+            const int last = LT.L - 1 - kFwdBlockN * n;
 #pragma unroll
             for (int u = 0; u < LPW; ++u) {
-                const int key = min(kFwdBlockN * n + ld_row[u], LT.L - 1);
-                const int64_t row = base + (int64_t)key * rs;
-                load_lds16(a.k + row + ld_gk[u], kdst + 1024 * (LPW * wave + u));
-                load_lds16(a.v + row + ld_gv[u], vdst + 1024 * (LPW * wave + u));
+                uint32_t back = 0;
+                if (last < kFwdBlockN - 1) back = (uint32_t)max(ld_row[u] - last, 0) * rs_b;
+                load_lds16_s(kb, ld_ok[u] - back, kdst + 1024 * (LPW * wave + u));
+                load_lds16_s(vb, ld_ov[u] - back, vdst + 1024 * (LPW * wave + u));
             }
         }
         ++l_slot;

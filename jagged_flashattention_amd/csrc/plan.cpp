@@ -53,6 +53,9 @@ int32_t check_problem(const jfa_problem* p) {
     if (p->broadcast_q != 0 && p->broadcast_q != 1) return JFA_ERR_INVALID_ARG;
     if (p->causal != 0 && p->causal != 1) return JFA_ERR_INVALID_ARG;
     if (p->head_dim != 64 && p->head_dim != 128) return JFA_ERR_UNSUPPORTED;
+    // a token row (H*D bf16) below 2^24 bytes: the kernels address the rows
+    // of a block as 24-bit multiples of it from the block's first row
+    if (p->num_heads > 32768) return JFA_ERR_UNSUPPORTED;
     // finite and positive (the kernels take the row max before scaling)
     if (!(p->softmax_scale > 0.0f) || p->softmax_scale > 3.0e38f) return JFA_ERR_INVALID_ARG;
     if (p->window_left < -1 || p->window_right < -1) return JFA_ERR_INVALID_ARG;

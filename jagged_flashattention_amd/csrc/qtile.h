@@ -78,6 +78,23 @@ __device__ __forceinline__ void load_lds16(const uint16_t* g, char* lds_wave_bas
         : "memory");
 }
 
+// The same copy from sbase + voff bytes: sbase wave-uniform (an SGPR pair,
+// the scalar-base form of the instruction), voff this lane's 32-bit byte
+// offset, so the lane's address costs no 64-bit vector arithmetic.
+__device__ __forceinline__ void load_lds16_s(const void* sbase, uint32_t voff, char* lds_wave_base) {
+    const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_wave_base;
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(lds)
+        : "memory");
+}
+
 // Direct-to-LDS copy of 4 bytes per lane: lane l's dword at g lands at
 // lds_wave_base + 4 l (same conventions as load_lds16).
 __device__ __forceinline__ void load_lds4(const void* g, char* lds_wave_base) {

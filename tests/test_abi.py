@@ -57,6 +57,7 @@ def _prob(**kw):
 
 @pytest.mark.parametrize("kw,qoff,kvoff,mask,status", [
     (dict(head_dim=96), None, [0, 3, 5], None, J.JFA_ERR_UNSUPPORTED),
+    (dict(num_heads=32769), None, [0, 3, 5], None, J.JFA_ERR_UNSUPPORTED),
     (dict(causal=True), None, [0, 3, 5], None, J.JFA_ERR_UNSUPPORTED),
     (dict(), None, [1, 3, 5], None, J.JFA_ERR_BAD_OFFSETS),
     (dict(), None, [0, 3, 2], None, J.JFA_ERR_BAD_OFFSETS),
