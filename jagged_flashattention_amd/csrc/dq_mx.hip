@@ -95,13 +95,14 @@ __global__ void __launch_bounds__(kThreads, 1) dq_mx_kernel(DqArgs a) {
         if (l_ti >= t_end) return;
         const int n = seq_block<MODE>(LT, LT.k0 + l_i);
         const int sl = l_slot % kMxSlots;
-        const int64_t base = (int64_t)LT.kv0 * rs + (int64_t)LT.h * D;
+        // (from the block's first key row, a wave-uniform base; E4M3 rows are
+        // rs bytes, below 2^24)
+        const int64_t blk0 = (int64_t)(LT.kv0 + kFwdBlockN * n) * rs + (int64_t)LT.h * D;
         const int q = 64 * wave + lane, r = q >> 3, cs = q & 7;
-        const int key = min(kFwdBlockN * n + r, LT.L - 1);
-        const int64_t row = base + (int64_t)key * rs;
-        load_lds16((const uint16_t*)(a.k8 + row + 16 * (cs ^ swz_k8(r))), smem + LY::K + sl * LY::BLK + 1024 * wave);
-        load_lds16((const uint16_t*)(a.v8 + row + 16 * (cs ^ swz_k8(r))), smem + LY::V + sl * LY::BLK + 1024 * wave);
-        load_lds16((const uint16_t*)(a.kk8 + row + 16 * (cs ^ swz_v8(r))), smem + LY::KK + sl * LY::BLK + 1024 * wave);
+        const uint32_t ro = __umul24((uint32_t)min(r, LT.L - 1 - kFwdBlockN * n), (uint32_t)rs);
+        load_lds16_s(a.k8 + blk0, ro + 16 * (cs ^ swz_k8(r)), smem + LY::K + sl * LY::BLK + 1024 * wave);
+        load_lds16_s(a.v8 + blk0, ro + 16 * (cs ^ swz_k8(r)), smem + LY::V + sl * LY::BLK + 1024 * wave);
+        load_lds16_s(a.kk8 + blk0, ro + 16 * (cs ^ swz_v8(r)), smem + LY::KK + sl * LY::BLK + 1024 * wave);
         if (wave < 2) {
             const int kk = min(kFwdBlockN * n + lane, LT.L - 1);
             const uint8_t* src = wave == 0 ? a.k_sc : a.v_sc;
