@@ -339,26 +339,44 @@ def main():
 
     # plan ablation (the sort and zigzag deal against the unsorted
     # round-robin plan, and the static zigzag forward against the dynamic
-    # one): the same steps with other plans, per-kernel medians
-    def timed_kernels(a):
-        for i in range(args.warmup):
-            step(i=i, a=a)
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
-        for i in range(args.steps):
-            step(ev[i], i, a)
-        torch.cuda.synchronize()
-        return {n: float(np.median([e[j].elapsed_time(e[j + 1]) for e in ev]))
-                for j, n in enumerate(names)}
+    # one): the same steps with other plans. The plans take turns, round by
+    # round (the order reversed every other round), so that a clock that
+    # drifts while the GPU warms up or heats up weighs on each plan alike;
+    # per-kernel medians over every round's steps.
+    def timed_rounds(atts, rounds=4):
+        for a in atts:
+            for i in range(args.warmup):
+                step(i=i, a=a)
+        samples = [{n: [] for n in names} for _ in atts]
+        for r in range(rounds):
+            order = list(range(len(atts)))
+            if r % 2:
+                order.reverse()
+            for k in order:
+                ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+                      for _ in range(args.steps)]
+                for i in range(args.steps):
+                    step(ev[i], i, atts[k])
+                torch.cuda.synchronize()
+                for j, n in enumerate(names):
+                    samples[k][n] += [e[j].elapsed_time(e[j + 1]) for e in ev]
+        return [{n: float(np.median(v)) for n, v in smp.items()} for smp in samples]
     ablation = None
     if args.ablation:
         kw = dict(fwd_workers=cus * args.fwd_workers_per_cu, bwd_workers=cus * args.bwd_workers_per_cu)
-        nat = timed_kernels(J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask,
-                                              natural_plans=True, **kw))
-        stat = timed_kernels(J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask,
-                                               fwd_dynamic=args.fwd_plan != "dynamic", **kw))
-        ablation = {"kernel_ms_natural_plans": nat,
+        srt, nat, stat = timed_rounds([
+            att,
+            J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask,
+                              natural_plans=True, **kw),
+            J.JaggedAttention(prob, x.kv_offsets, x.q_offsets, x.block_mask,
+                              fwd_dynamic=args.fwd_plan != "dynamic", **kw)])
+        ablation = {"kernel_ms_sorted_plans": srt, "kernel_ms_natural_plans": nat,
                     ("fwd_ms_static_zigzag" if args.fwd_plan == "dynamic" else "fwd_ms_dynamic"):
-                    stat["fwd"]}
+                    stat["fwd"],
+                    "fwd_speedup_sorted_vs_natural": nat["fwd"] / srt["fwd"],
+                    "bwd_speedup_sorted_vs_natural": (sum(nat[n] for n in names[1:])
+                                                      / sum(srt[n] for n in names[1:])),
+                    "dkdv_speedup_sorted_vs_natural": nat["bwd_dkdv"] / srt["bwd_dkdv"]}
 
     def time_alone(fn):
         """Median over the timed steps of fn(i) (i alternates the two input
@@ -468,11 +486,6 @@ def main():
     per_mean = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in events]))
                 for j, n in enumerate(names)}
 
-    if ablation is not None:
-        nat = ablation["kernel_ms_natural_plans"]
-        ablation["fwd_speedup_sorted_vs_natural"] = nat["fwd"] / per["fwd"]
-        ablation["bwd_speedup_sorted_vs_natural"] = (sum(nat[n] for n in names[1:])
-                                                     / sum(per[n] for n in names[1:]))
     if mx is not None:
         mixed_ms = mx["fwd_ms"] + mx["dq_ms"] + per["bwd_dkdv"] + per["bwd_dq_reduce"]
         all_ms = mx["fwd_ms"] + mx["dq_ms"] + mx["dkdv_ms"] + per["bwd_dq_reduce"]
